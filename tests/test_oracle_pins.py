@@ -1,0 +1,378 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+Each test ties an oracle function to something other than itself: a worked
+example printed on a page, a closed form, an exact identity checked by
+enumeration, a Monte-Carlo law with a stated tolerance, or a library routine
+that computes the same quantity in a special case.  A plausible slip in the
+oracle (a dropped term, a flipped comparison, a wrong index or an off-by-one
+anchor) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand_simplex(rng, V, zeros=0):
+    p = rng.random(V) + 0.05
+    if zeros:
+        p[rng.choice(V, zeros, replace=False)] = 0.0
+    return p / p.sum()
+
+
+def _logits_from_probs(p):
+    with np.errstate(divide="ignore"):
+        return np.log(p).astype(np.float64)
+
+
+# ----------------------------------------------------------------- bf16 decode
+
+def test_bf16_decode_matches_torch_for_every_bit_pattern(orc):
+    torch = pytest.importorskip("torch")
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = orc.decode_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+# ----------------------------------------------------------------- worked example
+
+def test_worked_example_acceptance_probabilities(orc):
+    g = _load_golden("worked_example_acceptance.json")
+    for case in g["cases"]:
+        a = orc.accept_prob(case["p_target"], case["q_draft"])
+        assert abs(a - case["accept_prob"]) <= case["printed_tolerance"] + 1e-15, case
+
+
+def test_worked_example_through_full_verify_v2(orc):
+    """V=2: the draft proposes token 0 with q=0.9.  Target p(0)=0.95 keeps it for
+    every u; target p(0)=0.1 keeps it for u < 1/9 and otherwise resamples the
+    target's preferred token 1."""
+    g = _load_golden("worked_example_acceptance.json")
+    us = (np.arange(9000, dtype=np.float32) + 0.5) / 9000  # evenly spread uniforms in (0,1)
+    for case in g["cases"]:
+        p0, q0 = case["p_target"], case["q_draft"]
+        pt = np.array([p0, 1 - p0])
+        qd = np.array([q0, 1 - q0])
+        B = us.size
+        # k=1: target has rows for position 0 and the bonus position 1
+        target = np.tile(np.stack([_logits_from_probs(pt), _logits_from_probs(pt)])[None], (B, 1, 1))
+        draft = np.tile(_logits_from_probs(qd)[None, None], (B, 1, 1))
+        tokens = np.zeros((B, 1), np.int32)
+        u = np.stack([us, np.full(B, 0.5, np.float32)], axis=1).astype(np.float32)
+        r = orc.verify(target.astype(np.float32), draft.astype(np.float32), tokens, u, 1.0)
+        frac = r.accepted_len.mean()
+        assert abs(frac - case["accept_prob"]) <= case["printed_tolerance"] + 2e-4, (case, frac)
+        rejected = r.accepted_len == 0
+        if rejected.any():
+            # the residual max(0, p - q) is one-hot on token 1: every resample is 1
+            assert np.all(r.out_tokens[rejected, 0] == 1)
+            assert np.all(r.out_tokens[rejected, 1] == -1)
+        acc = ~rejected
+        assert np.all(r.out_tokens[acc, 0] == 0)
+
+
+# ----------------------------------------------------------------- closed forms
+
+def test_acceptance_rate_equals_one_minus_total_variation(orc):
+    """x ~ q, kept w.p. min(1,p/q): E[kept] = sum_x min(p(x), q(x)) = 1 - TV(p,q)."""
+    rng = np.random.default_rng(7)
+    for trial in range(4):
+        V = 6
+        p = _rand_simplex(rng, V, zeros=trial % 2)
+        q = _rand_simplex(rng, V, zeros=(trial // 2) % 2)
+        B = 200_000
+        x = rng.choice(V, size=B, p=q).astype(np.int32)[:, None]
+        u = rng.random((B, 2), dtype=np.float32)
+        lt = np.tile(np.stack([_logits_from_probs(p)] * 2)[None], (B, 1, 1)).astype(np.float32)
+        ld = np.tile(_logits_from_probs(q)[None, None], (B, 1, 1)).astype(np.float32)
+        r = orc.verify(lt, ld, x, u, 1.0)
+        frac = r.accepted_len.mean()
+        expect = np.minimum(p, q).sum()
+        assert abs(expect - (1 - 0.5 * np.abs(p - q).sum())) < 1e-12
+        sigma = math.sqrt(expect * (1 - expect) / B)
+        assert abs(frac - expect) < 5 * sigma + 1e-6, (trial, frac, expect)
+
+
+def test_residual_mass_is_total_variation(orc):
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        V = int(rng.integers(2, 40))
+        p, q = _rand_simplex(rng, V, zeros=1), _rand_simplex(rng, V)
+        w = orc.residual(p, q)
+        assert np.all(w >= 0)
+        assert abs(w.sum() - 0.5 * np.abs(p - q).sum()) < 1e-12
+        assert abs(w.sum() - (1 - np.minimum(p, q).sum())) < 1e-12
+
+
+def test_losslessness_by_exact_enumeration(orc):
+    """P(out = y) = q(y) a(y) + (1 - sum_x q(x) a(x)) w(y)/sum(w) equals p(y),
+    a = accept_prob, w = residual: the output token is distributed as the target."""
+    rng = np.random.default_rng(11)
+    for V in range(2, 7):
+        for _ in range(40):
+            p = _rand_simplex(rng, V, zeros=int(rng.integers(0, V - 1)))
+            q = _rand_simplex(rng, V, zeros=int(rng.integers(0, V - 1)))
+            a = np.array([orc.accept_prob(p[y], q[y]) for y in range(V)])
+            kept = q * a
+            reject_mass = 1.0 - kept.sum()
+            w = orc.residual(p, q)
+            out = kept + (reject_mass * w / w.sum() if w.sum() > 0 else 0.0)
+            assert np.allclose(out, p, atol=1e-12, rtol=0), (p, q, out)
+
+
+def test_losslessness_chi_square_full_sampler(orc):
+    """Monte Carlo through the whole batched path at V=8, k=3: among trials that
+    reach position j, out[j] ~ p_j; P(accepted_len >= j) = prod_{i<j} alpha_i."""
+    rng = np.random.default_rng(2024)
+    V, k, B = 8, 3, 200_000
+    P = np.stack([_rand_simplex(rng, V, zeros=1) for _ in range(k + 1)])
+    Q = np.stack([_rand_simplex(rng, V, zeros=1 if i == 1 else 0) for i in range(k)])
+    lt = np.tile(_logits_from_probs(P)[None], (B, 1, 1)).astype(np.float32)
+    ld = np.tile(_logits_from_probs(Q)[None], (B, 1, 1)).astype(np.float32)
+    # the fp32 logits round the probabilities; use the exactly decoded ones
+    P = np.stack([orc.softmax(lt[0, i].astype(np.float64), 1.0)[0] for i in range(k + 1)])
+    Q = np.stack([orc.softmax(ld[0, i].astype(np.float64), 1.0)[0] for i in range(k)])
+    x = np.stack([rng.choice(V, size=B, p=Q[i]) for i in range(k)], axis=1).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    r = orc.verify(lt, ld, x, u, 1.0)
+    L = r.accepted_len
+    alpha = np.minimum(P[:k], Q).sum(axis=1)
+    pvals = []
+    for j in range(k + 1):
+        reach = L >= j
+        n = int(reach.sum())
+        expect_reach = float(np.prod(alpha[:j]))
+        sigma = math.sqrt(expect_reach * (1 - expect_reach) / B) if 0 < expect_reach < 1 else 0
+        assert abs(n / B - expect_reach) < 5 * sigma + 1e-9, (j, n / B, expect_reach)
+        counts = np.bincount(r.out_tokens[reach, j], minlength=V)
+        support = P[j] > 0
+        assert counts[~support].sum() == 0  # zero-probability tokens never emitted
+        pvals.append(stats.chisquare(counts[support], n * P[j][support] / P[j][support].sum()).pvalue)
+    assert min(pvals) > 1e-4 / len(pvals), pvals
+
+
+# ----------------------------------------------------------------- special cases
+
+def test_identical_draft_and_target_always_accepts(orc):
+    rng = np.random.default_rng(5)
+    B, k, V = 512, 5, 50
+    lt = (3 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+    ld = lt[:, :k].copy()
+    x = rng.integers(0, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    r = orc.verify(lt, ld, x, u, 0.7)
+    assert np.all(r.accepted_len == k)
+    assert np.array_equal(r.out_tokens[:, :k], x)
+
+
+def test_onehot_draft_acceptance_is_target_prob(orc):
+    """q = indicator of x: kept iff u < p(x); residual is p with x removed."""
+    rng = np.random.default_rng(9)
+    B, k, V = 4000, 1, 5
+    lt = (2 * rng.standard_normal((1, k + 1, V))).astype(np.float32)
+    lt = np.tile(lt, (B, 1, 1))
+    x = np.full((B, 1), 2, np.int32)
+    u = rng.random((B, 2), dtype=np.float32)
+    r = orc.verify(lt, None, x, u, 1.0, onehot=True)
+    p0 = orc.softmax(lt[0, 0].astype(np.float64), 1.0)[0]
+    assert np.array_equal(r.accepted_len == 1, u[:, 0].astype(np.float64) < p0[2])
+    assert np.allclose(r.probs[:, 0, 0], p0[2], rtol=1e-15)
+    assert np.all(r.probs[:, 0, 1] == 1.0)
+    rej = r.accepted_len == 0
+    # resampled token never equals the rejected draft token, and follows the
+    # library inverse CDF of p with x zeroed
+    w = p0.copy()
+    w[2] = 0.0
+    cdf = np.cumsum(w)
+    expect = np.searchsorted(cdf, u[rej, 1].astype(np.float64) * cdf[-1], side="right")
+    assert np.array_equal(r.out_tokens[rej, 0], expect)
+    assert not np.any(r.out_tokens[rej, 0] == 2)
+
+
+def test_greedy_matches_numpy_argmax_with_ties(orc):
+    rng = np.random.default_rng(13)
+    B, k, V = 300, 4, 64
+    # coarse values make ties common; numpy.argmax returns the first maximum
+    lt = rng.integers(-4, 5, (B, k + 1, V)).astype(np.float32)
+    g = np.argmax(lt, axis=2)
+    x = np.where(rng.random((B, k)) < 0.7, g[:, :k], rng.integers(0, V, (B, k))).astype(np.int32)
+    r = orc.verify(lt, None, x, None, 0.0)
+    for b in range(B):
+        mism = np.nonzero(x[b] != g[b, :k])[0]
+        rr = int(mism[0]) if mism.size else k
+        assert r.accepted_len[b] == rr
+        assert list(r.out_tokens[b, :rr]) == list(x[b, :rr])
+        assert r.out_tokens[b, rr] == g[b, rr]
+        assert np.all(r.out_tokens[b, rr + 1:] == -1)
+        assert np.array_equal(r.target_mz[b, :, 1], g[b])
+
+
+def test_greedy_matches_numpy_argmax_bf16(orc):
+    import workloads
+
+    rng = np.random.default_rng(17)
+    B, k, V = 50, 3, 3001
+    bits = workloads.round_to_bf16_bits((4 * rng.standard_normal((B, k + 1, V))).astype(np.float32))
+    vals = workloads.bf16_bits_to_f32(bits)
+    g = np.argmax(vals, axis=2)
+    x = g[:, :k].astype(np.int32).copy()
+    x[::3, 1] = (x[::3, 1] + 1) % V
+    r = orc.verify(bits, None, x, None, 0.0)
+    assert np.array_equal(r.target_mz[:, :, 1].astype(np.int64), g)
+
+
+def test_inverse_cdf_matches_searchsorted(orc):
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        V = int(rng.integers(1, 200))
+        w = rng.random(V) * (rng.random(V) < 0.7)
+        if w.sum() == 0:
+            w[int(rng.integers(0, V))] = 1.0
+        u = float(rng.random(dtype=np.float32))
+        y, margin = orc.inverse_cdf(w, u)
+        cdf = np.cumsum(w)
+        assert y == int(np.searchsorted(cdf, u * cdf[-1], side="right"))
+        assert w[y] > 0
+        assert margin >= 0
+
+
+def test_inverse_cdf_never_picks_zero_weight_even_at_u_near_one(orc):
+    w = np.array([0.0, 0.3, 0.0, 0.7, 0.0, 0.0])
+    for u in [0.0, 0.2999, 0.3, 0.5, 0.9999999]:
+        y, _ = orc.inverse_cdf(w, u)
+        assert w[y] > 0
+
+
+def test_softmax_matches_scipy(orc):
+    rng = np.random.default_rng(23)
+    for T in [1.0, 0.6, 0.01, 3.0]:
+        l = 4 * rng.standard_normal(1000)
+        l[::97] = -np.inf
+        p, m, z = orc.softmax(l, T)
+        assert np.allclose(p, special.softmax(l / T), rtol=1e-13, atol=0)
+        assert abs(m + math.log(z) - special.logsumexp(l / T)) < 1e-12 * max(1.0, abs(m))
+        assert m == np.max(l) / T
+        assert np.all(p[::97] == 0)
+
+
+def test_neg_inf_logits_are_never_emitted(orc):
+    rng = np.random.default_rng(29)
+    B, k, V = 2000, 2, 12
+    lt = rng.standard_normal((B, k + 1, V)).astype(np.float32)
+    ld = rng.standard_normal((B, k, V)).astype(np.float32)
+    lt[:, :, 5:9] = -np.inf
+    x = rng.integers(0, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    r = orc.verify(lt, ld, x, u, 1.0)
+    for b in range(B):
+        L = r.accepted_len[b]
+        assert not (5 <= r.out_tokens[b, L] < 9)
+
+
+def test_invalid_token_flags_sequence(orc):
+    rng = np.random.default_rng(31)
+    B, k, V = 3, 3, 10
+    lt = rng.standard_normal((B, k + 1, V)).astype(np.float32)
+    ld = rng.standard_normal((B, k, V)).astype(np.float32)
+    x = rng.integers(0, V, (B, k)).astype(np.int32)
+    x[1, 2] = V
+    x[2, 0] = -1
+    u = rng.random((B, k + 1), dtype=np.float32)
+    r = orc.verify(lt, ld, x, u, 1.0)
+    assert r.accepted_len[0] >= 0
+    assert list(r.accepted_len[1:]) == [-1, -1]
+    assert np.all(r.out_tokens[1:] == -1)
+
+
+def test_temperature_scales_logits(orc):
+    """softmax(l/T) at T is the T=1 softmax of l/T: the same verify result."""
+    rng = np.random.default_rng(37)
+    B, k, V, T = 64, 4, 300, 0.6
+    lt = (4 * rng.standard_normal((B, k + 1, V))).astype(np.float64)
+    ld = lt[:, :k] + 0.3 * rng.standard_normal((B, k, V))
+    # choose T and logits so that l/T is exactly representable
+    T = 0.5
+    x = rng.integers(0, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    a = orc.verify(lt.astype(np.float32), ld.astype(np.float32), x, u, T)
+    b = orc.verify((lt / T).astype(np.float32), (ld / T).astype(np.float32), x, u, 1.0)
+    np.testing.assert_array_equal(a.accepted_len, b.accepted_len)
+    np.testing.assert_array_equal(a.out_tokens, b.out_tokens)
+
+
+# ----------------------------------------------------------------- VAT
+
+def _vat_inputs_with_reject_at(rs, k, V=4):
+    """Blocks whose proposed token has p/q = 0.5 at every position; u = 0 keeps
+    it, u = 0.9 rejects it.  Block n is built to reject first at rs[n]."""
+    N = len(rs)
+    p = np.array([0.2, 0.3, 0.25, 0.25])
+    q = np.array([0.4, 0.2, 0.2, 0.2])
+    lt = np.tile(_logits_from_probs(p)[None, None], (N, k, 1)).astype(np.float32)
+    ld = np.tile(_logits_from_probs(q)[None, None], (N, k, 1)).astype(np.float32)
+    x = np.zeros((N, k), np.int32)
+    u = np.zeros((N, k), np.float32)
+    for n, r in enumerate(rs):
+        if r < k:
+            u[n, r] = 0.9
+            u[n, r + 1:] = np.linspace(0, 0.99, k - r - 1)
+    return lt, ld, x, u
+
+
+def test_vat_weighting_prose_examples(orc):
+    g = _load_golden("vat_weighting_examples.json")
+    decay = g["decay"]
+    for case in g["cases"]:
+        k, r = case["k"], case["first_reject"]
+        lt, ld, x, u = _vat_inputs_with_reject_at([r], k)
+        res = orc.vat_labels(lt, ld, x, u, 1.0, decay)
+        assert res.first_reject[0] == r
+        assert int(res.accept_mask[0].sum()) == case["accept_mask_ones"]
+        assert np.all(res.accept_mask[0, :r] == 1) and np.all(res.accept_mask[0, r:] == 0)
+        full = case["full_weight_positions"]
+        assert np.all(res.weights[0, full] == 1.0)
+        anchor = case["decay_anchor"]
+        for i in range(anchor, k):
+            assert res.weights[0, i] == pytest.approx(decay ** (i - anchor), rel=1e-15)
+        if r == 0:
+            # the fixed curve decaying from the first position: 0.8^(j-1), j 1-based
+            j = np.arange(1, k + 1)
+            assert np.allclose(res.weights[0], decay ** (j - 1), rtol=1e-15)
+
+
+def test_vat_hard_cut_is_zero_decay(orc):
+    k = 8
+    lt, ld, x, u = _vat_inputs_with_reject_at([3], k)
+    res = orc.vat_labels(lt, ld, x, u, 1.0, 0.0)
+    assert list(res.weights[0]) == [1, 1, 1, 1, 0, 0, 0, 0]
+
+
+def test_vat_labels_follow_inference_rule(orc):
+    """The simulated verification is the inference-time rule: first_reject equals
+    the accepted length of batched verification on the same rows and uniforms."""
+    rng = np.random.default_rng(41)
+    N, k, V = 400, 6, 40
+    lt = (2 * rng.standard_normal((N, k + 1, V))).astype(np.float32)
+    ld = (lt[:, :k] + 0.8 * rng.standard_normal((N, k, V))).astype(np.float32)
+    x = rng.integers(0, V, (N, k)).astype(np.int32)
+    u = rng.random((N, k + 1), dtype=np.float32)
+    v = orc.verify(lt, ld, x, u, 0.8)
+    t = orc.vat_labels(np.ascontiguousarray(lt[:, :k]), ld, x, np.ascontiguousarray(u[:, :k]), 0.8, 0.8)
+    np.testing.assert_array_equal(v.accepted_len, t.first_reject)
+    np.testing.assert_array_equal(t.accept_mask.sum(axis=1), t.first_reject)
+    g = orc.verify(lt, None, x, None, 0.0)
+    tg = orc.vat_labels(np.ascontiguousarray(lt[:, :k]), None, x, None, 0.0, 0.8)
+    np.testing.assert_array_equal(g.accepted_len, tg.first_reject)

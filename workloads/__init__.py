@@ -1,0 +1,196 @@
+"""Seeded synthetic workloads for batched speculative-sampling verification.
+
+The parity tests feed the same arrays to the HIP library and to the fp64
+oracle, and the bench times the library on them.  This module holds none of
+the verification arithmetic (no softmax, acceptance test, residual or
+sampler): it draws Gaussian logits, rounds them to bfloat16, draws the draft
+tokens (exponential race over the draft logits, i.e. the Gumbel-max trick, an
+argmax, or an n-gram-style coin), and draws the host uniforms.
+
+Every sequence (or VAT block) ``b`` is generated from its own PCG64 streams,
+keyed by ``(seed, stream, b)``, so any subset of sequences of a configuration
+can be regenerated on its own, bit for bit, and a reduced-batch variant holds
+exactly the first sequences of the full one.
+
+Workloads (shapes and value distributions as stated for each configuration;
+logits stand in for the output of a target/draft forward, since the
+verification step only ever sees logits):
+
+=============  ======================================================================
+tiny           B=4, k=4, V=1000, fp32, T=1; t = 3z, d = t + 0.3z', x ~ softmax(d/T)
+selfdraft      B=128, k=5, V=151936, bf16, T=1; t = 4z, d = t + 0.1z', x ~ softmax(d/T)
+ngram_tail     B=8, k=16, V=151936, bf16 target, one-hot draft, T=1; t = 5z;
+               x = argmax t w.p. 0.9, else uniform over [0, V)
+grpo           B=320, k=7, V=151936, bf16, T=0.6; t = 4z, d = t + 0.2z', x ~ softmax(d/T)
+grpo_greedy    same logits as grpo, T=0; x = argmax d (lowest id)
+vat            N=2048 blocks, k=16, V=128256, fp32, T=1, decay 0.8; t = 4z, d = t + 0.25z',
+               x ~ softmax(d/T); target has k rows per block (no bonus row)
+=============  ======================================================================
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["Config", "Workload", "CONFIGS", "get_config", "generate", "round_to_bf16_bits",
+           "bf16_bits_to_f32"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    kind: str            # "verify" or "vat"
+    B: int               # sequences (verify) or draft blocks (vat)
+    k: int               # draft positions
+    V: int               # vocabulary
+    dtype: str           # "f32" or "bf16"
+    T: float             # temperature (0 = greedy)
+    sigma_t: float       # target logits = sigma_t * N(0,1)
+    sigma_d: Optional[float]  # draft logits = target + sigma_d * N(0,1); None = one-hot draft
+    draft_mode: str      # "sample" | "argmax" | "ngram"
+    seed_logits: int
+    seed_draft: int = 1
+    seed_u: int = 0
+    decay: float = 0.8   # vat only
+    ngram_hit: float = 0.9  # ngram only: probability that x is the target argmax
+
+    @property
+    def onehot(self) -> bool:
+        return self.sigma_d is None
+
+    @property
+    def target_rows_per_seq(self) -> int:
+        return self.k + 1 if self.kind == "verify" else self.k
+
+    @property
+    def n_uniforms(self) -> int:
+        return self.k + 1 if self.kind == "verify" else self.k
+
+    @property
+    def reads_draft(self) -> bool:
+        return (not self.onehot) and self.T != 0.0
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def algorithmic_bytes(self) -> int:
+        """Every logit the path needs, read once (tokens/uniforms/outputs excluded)."""
+        rows = self.B * self.target_rows_per_seq
+        if self.reads_draft:
+            rows += self.B * self.k
+        return rows * self.V * self.elem_bytes
+
+    def positions(self) -> int:
+        return self.B * self.k
+
+    def scaled(self, **changes) -> "Config":
+        return dataclasses.replace(self, **changes)
+
+
+CONFIGS = {
+    "tiny": Config("tiny", "verify", 4, 4, 1000, "f32", 1.0, 3.0, 0.3, "sample", 100),
+    "selfdraft": Config("selfdraft", "verify", 128, 5, 151936, "bf16", 1.0, 4.0, 0.1, "sample", 200),
+    "ngram_tail": Config("ngram_tail", "verify", 8, 16, 151936, "bf16", 1.0, 5.0, None, "ngram", 300),
+    "grpo": Config("grpo", "verify", 320, 7, 151936, "bf16", 0.6, 4.0, 0.2, "sample", 400),
+    "grpo_greedy": Config("grpo_greedy", "verify", 320, 7, 151936, "bf16", 0.0, 4.0, 0.2, "argmax", 400),
+    "vat": Config("vat", "vat", 2048, 16, 128256, "f32", 1.0, 4.0, 0.25, "sample", 500),
+}
+
+
+def get_config(name: str) -> Config:
+    return CONFIGS[name]
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Workload:
+    config: Config
+    lo: int                       # first sequence index held
+    target: np.ndarray            # [n][rows][V] float32 or uint16 (bf16 bits)
+    draft: Optional[np.ndarray]   # [n][k][V] or None (one-hot)
+    tokens: np.ndarray            # [n][k] int32
+    uniforms: np.ndarray          # [n][k+1] (verify) or [n][k] (vat) float32
+
+    @property
+    def n(self) -> int:
+        return self.tokens.shape[0]
+
+
+def _rng(*key) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(v) for v in key])))
+
+
+def _as_values(stored: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(stored) if stored.dtype == np.uint16 else stored
+
+
+def _one_sequence(cfg: Config, b: int, target_out, draft_out, tokens_out, u_out, i: int) -> None:
+    rows_t = cfg.target_rows_per_seq
+    z = _rng(cfg.seed_logits, 0, b).standard_normal((rows_t, cfg.V), dtype=np.float32)
+    t = (np.float32(cfg.sigma_t) * z).astype(np.float32)
+    t_st = round_to_bf16_bits(t) if cfg.dtype == "bf16" else t
+    target_out[i] = t_st
+    d_st = None
+    if not cfg.onehot:
+        zd = _rng(cfg.seed_logits, 1, b).standard_normal((cfg.k, cfg.V), dtype=np.float32)
+        d = (t[: cfg.k] + np.float32(cfg.sigma_d) * zd).astype(np.float32)
+        d_st = round_to_bf16_bits(d) if cfg.dtype == "bf16" else d
+        if draft_out is not None:
+            draft_out[i] = d_st
+    rx = _rng(cfg.seed_draft, b)
+    if cfg.draft_mode == "sample":
+        # Exponential race (Gumbel-max): argmax_y d(y)/T - log E(y), E ~ Exp(1),
+        # picks y with probability proportional to exp(d(y)/T).
+        dv = _as_values(d_st).astype(np.float64)
+        e = rx.standard_exponential((cfg.k, cfg.V))
+        tokens_out[i] = np.argmax(dv / cfg.T - np.log(e), axis=1)
+    elif cfg.draft_mode == "argmax":
+        tokens_out[i] = np.argmax(_as_values(d_st), axis=1)
+    elif cfg.draft_mode == "ngram":
+        hit = rx.random(cfg.k) < cfg.ngram_hit
+        other = rx.integers(0, cfg.V, size=cfg.k)
+        best = np.argmax(_as_values(t_st)[: cfg.k], axis=1)
+        tokens_out[i] = np.where(hit, best, other)
+    else:
+        raise ValueError(cfg.draft_mode)
+    u_out[i] = _rng(cfg.seed_u, b).random(cfg.n_uniforms, dtype=np.float32)
+
+
+def generate(cfg: Config, lo: int = 0, hi: Optional[int] = None, workers: Optional[int] = None,
+             with_draft: bool = True) -> Workload:
+    """Generate sequences [lo, hi) of ``cfg`` (all of them by default)."""
+    hi = cfg.B if hi is None else hi
+    assert 0 <= lo <= hi <= cfg.B
+    n = hi - lo
+    st_dtype = np.uint16 if cfg.dtype == "bf16" else np.float32
+    target = np.empty((n, cfg.target_rows_per_seq, cfg.V), dtype=st_dtype)
+    draft = None
+    if with_draft and not cfg.onehot:
+        draft = np.empty((n, cfg.k, cfg.V), dtype=st_dtype)
+    tokens = np.empty((n, cfg.k), dtype=np.int32)
+    u = np.empty((n, cfg.n_uniforms), dtype=np.float32)
+    if workers is None:
+        workers = max(1, min(16, os.cpu_count() or 1))
+    jobs = [(cfg, lo + i, target, draft, tokens, u, i) for i in range(n)]
+    if workers == 1 or n <= 1:
+        for j in jobs:
+            _one_sequence(*j)
+    else:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda j: _one_sequence(*j), jobs))
+    return Workload(cfg, lo, target, draft, tokens, u)
