@@ -1,0 +1,211 @@
+"""Throughput of batched speculative-sampling verification on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload selfdraft] [--gpus 1]
+
+One step = one sv_verify call (every kernel of the path) over one batch of
+synthetic logits already resident in HBM.  The default workload is the
+quantized-self-drafter batch: B=128 sequences, k=5 draft positions,
+V=151936, bf16 target and draft logits, T=1.  Prints ONE JSON line.
+
+  value        verified draft positions per second = B*k*K / wall time of K
+               steps (synchronised on both sides)
+  roofline     the row-statistics kernel (the one that streams every logit):
+               algorithmic bytes per launch / its mean duration, measured live
+               with HIP events recorded on the launch stream around each launch
+  cpu_baseline the fp64 oracle on a bounded sample of the same workload on
+               the host (single thread)
+
+Inputs rotate through enough copies that each timed sweep touches more than
+twice the 256 MB last-level (MALL) cache, so the figures are HBM figures.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 2**20
+METRIC = "verified draft positions/sec + achieved HBM GB/s (V=151936 bf16, k=5..16)"
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the probe slots of the verify descriptor take them)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError("hipEventCreate failed: %d" % rc)
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        self.hip.hipEventSynchronize(ctypes.c_void_p(b))
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("sv_kernels.hip", "sv_launch.h"):
+        with open(os.path.join(ROOT, "speculative_decoding_verification_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, wl, seconds: float):
+    """The oracle as it is (plain fp64 C, one thread) over whole sequences of
+    the same workload until `seconds` of CPU work have elapsed."""
+    import oracle
+
+    done = 0
+    t0 = time.perf_counter()
+    step = 4
+    while True:
+        lo = done % wl.n
+        hi = min(wl.n, lo + step)
+        d = wl.draft[lo:hi] if wl.draft is not None else None
+        oracle.verify(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, onehot=cfg.onehot)
+        done += hi - lo
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * cfg.k / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": "%d whole sequences (%d positions) of the %s workload, fp64 C oracle, 1 thread, %.1f s"
+                      % (done, done * cfg.k, cfg.name, dt),
+            "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="selfdraft",
+                    choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "tiny"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU; --gpus %d is not supported (the path shards by sequence "
+              "with no exchange, so N GPUs would each run this single-GPU step)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+
+    import speculative_decoding_verification_amd as sv
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no HIP device", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    cfg = workloads.get_config(args.workload)
+    print("bench: generating %s (B=%d k=%d V=%d %s T=%g)" % (cfg.name, cfg.B, cfg.k, cfg.V, cfg.dtype, cfg.T),
+          file=sys.stderr, flush=True)
+    wl = workloads.generate(cfg)
+    in_bytes = cfg.algorithmic_bytes()
+    copies = max(1, math.ceil(2 * MALL_BYTES / in_bytes))
+    sets = [workloads.to_device(wl, dev) for _ in range(copies)]
+    ev = HipEvents()
+    n_launch = args.warmup + args.steps
+    probes = [(ev.create(), ev.create()) for _ in range(n_launch)]
+    verifiers = []
+    for i in range(n_launch):
+        t, d, x, u = sets[i % copies]
+        verifiers.append(sv.Verifier(t, d, x, u, cfg.T, onehot=cfg.onehot, probe=probes[i]))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    print("bench: %d copies of %.1f MB, %d warmup + %d timed steps" % (copies, in_bytes / 1e6, args.warmup,
+                                                                        args.steps), file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        verifiers[i](stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_launch):
+        verifiers[i](stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    k1_ms = [ev.elapsed_ms(*probes[i]) for i in range(args.warmup, n_launch)]
+    k1_ms.sort()
+    k1_mean = sum(k1_ms) / len(k1_ms)
+    ms_per_step = elapsed * 1e3 / args.steps
+    positions = cfg.positions() * args.steps
+    value = positions / elapsed
+    kernel = "k_row_argmax" if cfg.T == 0.0 else "k_row_stats"
+    achieved = in_bytes / (k1_mean * 1e-3) / 1e9
+    acc = verifiers[-1].accepted_len.float().mean().item()
+    for a, b in probes:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
+                   "logits": cfg.dtype, "temperature": cfg.T, "draft": "one-hot" if cfg.onehot else "logits",
+                   "input_copies_rotated": copies},
+        "hbm_gbps_whole_step": in_bytes / (ms_per_step * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(kernel, cfg.name),
+                     "algorithmic_bytes_per_launch": in_bytes, "mean_launch_us": k1_mean * 1e3,
+                     "median_launch_us": k1_ms[len(k1_ms) // 2] * 1e3},
+        "mean_accepted_len": acc,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,199 @@
+/*
+ * specverify.h -- C ABI of libspecverify: batched lossless speculative-sampling
+ * verification and verification-aware-training (VAT) labels on MI355X (gfx950).
+ *
+ * What the operations compute (sources: page title, then section):
+ *
+ *  sv_verify   -- "AI 开始抄自己的作业——而且抄得理直气壮" (NgramRL essay,
+ *                 zhichai.net), section "投机解码：让草稿先跑，考官殿后":
+ *                 for each sequence the draft proposes k tokens x_0..x_{k-1};
+ *                 one target forward gives k+1 next-token distributions; token
+ *                 x_i is kept with probability min(1, p_i(x_i)/q_i(x_i)); the
+ *                 chain stops at the first rejection r, where the target
+ *                 supplies one token drawn from the residual max(0, p_r - q_r)
+ *                 renormalised; if all k are kept the target supplies a bonus
+ *                 token from its last distribution p_k.  Same page, section
+ *                 "考官坐镇：为什么抄作业不算作弊": the result is distributed
+ *                 exactly as sampling from the target alone.
+ *                 "NgramRL：用Rollout历史加速RL后训练的推测解码新方案"
+ *                 (kongchang.com), section "自适应 fan-out 预取": the outcome
+ *                 of one step is (accepted length j, target-supplied token b),
+ *                 here (accepted_len[b], out_tokens[b][accepted_len[b]]).
+ *
+ *  sv_vat_labels -- "让AI草稿模型学会“照镜子”：训练时就知道自己会不会被打回"
+ *                 (VAT write-up), section "VAT怎么把“验收规则”塞进训练里":
+ *                 training runs the same acceptance rule on each draft block
+ *                 and labels every position from the first rejection on as
+ *                 rejected; section "第二件事，改权重分配的锚点": positions
+ *                 before the first rejection r get weight 1 and the decay
+ *                 curve restarts at r (weight decay^(i-r) for i >= r).
+ *
+ * Readings this library takes where the pages leave a step open:
+ *  - p = softmax(target_logits / T), q = softmax(draft_logits / T), one T;
+ *  - acceptance: x_i is kept iff u[b][i] * q_i(x_i) < p_i(x_i);
+ *  - the single draw uses u[b][k] and inverts the cumulative weight in
+ *    ascending token id: smallest y with C(y) > u * C(V-1);
+ *  - T == 0 is greedy: the target's choice g_i is the first (lowest-id)
+ *    maximum of the raw logits; x_i is kept iff x_i == g_i; the target's token
+ *    is g_r; uniforms and draft logits are not read;
+ *  - one-hot drafts (SV_DRAFT_ONEHOT): q_i is the indicator of x_i, so x_i is
+ *    kept iff u < p_i(x_i) and the residual is p_r with x_r removed;
+ *  - positions of out_tokens after accepted_len are -1.
+ *
+ * Conventions shared by every entry point:
+ *  - Shapes are row-major with the vocabulary contiguous.  Logits are either
+ *    IEEE binary32 (SV_F32) or bfloat16 (SV_BF16, the top half of binary32).
+ *  - Ownership: every array is caller-owned DEVICE memory on the current HIP
+ *    device; the descriptor and the size out-parameter are host memory.  The
+ *    library allocates nothing and keeps no state between calls.
+ *  - Asynchrony: compute entry points enqueue kernels on `stream` and return;
+ *    outputs are valid once the stream reaches that point.
+ *  - Errors: arguments are checked on the host before anything is enqueued;
+ *    on any error nothing is launched and no output or workspace byte is
+ *    touched.  A failed launch returns SV_ERR_HIP (a workspace used by a call
+ *    that returned SV_ERR_HIP must be zero-filled again before reuse).
+ *  - Data checks done on the device: a sequence (block) holding a draft token
+ *    outside [0, V) is flagged (accepted_len = -1 / first_reject = -1, its
+ *    out_tokens -1, mask 0, weights 0) and never indexes memory with that
+ *    token.  Uniforms outside [0,1), NaN logits or rows that are all -inf
+ *    give unspecified (but in-bounds) results.
+ *  - Workspace: query its size, allocate it on the device, zero-fill it once
+ *    before first use; every call that returns SV_OK leaves it ready for the
+ *    next call.  Calls that use the same workspace must not overlap in time.
+ *  - Determinism: results are bitwise reproducible for identical inputs (no
+ *    floating-point atomics; fixed reduction orders).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+#define SV_MAX_DRAFT 64 /* k is limited to one 64-lane wavefront */
+
+typedef enum sv_status {
+    SV_OK = 0,
+    SV_ERR_NULL_ARG = 1,          /* a required pointer is NULL */
+    SV_ERR_BAD_SHAPE = 2,         /* batch < 0, k outside [1,64], vocab < 1, or size overflow */
+    SV_ERR_BAD_DTYPE = 3,         /* dtype not SV_F32 / SV_BF16 */
+    SV_ERR_BAD_TEMPERATURE = 4,   /* T not 0 and not a finite value >= 1e-4 */
+    SV_ERR_BAD_DRAFT_KIND = 5,    /* draft_kind not SV_DRAFT_LOGITS / SV_DRAFT_ONEHOT */
+    SV_ERR_WORKSPACE_TOO_SMALL = 6,
+    SV_ERR_BAD_DECAY = 7,         /* VAT decay not in [0, 1] */
+    SV_ERR_HIP = 8                /* a kernel launch or event record failed */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+typedef enum sv_draft_kind { SV_DRAFT_LOGITS = 0, SV_DRAFT_ONEHOT = 1 } sv_draft_kind;
+
+/* Shape and options of one sv_verify call.
+ * probe_start / probe_stop: optional instrumentation (NULL to skip).  When both
+ * are non-NULL they are recorded on `stream` immediately before and after the
+ * row-statistics kernel, the kernel that streams the logits. */
+typedef struct sv_verify_desc {
+    int32_t batch;       /* B >= 0 sequences (0: nothing to do) */
+    int32_t num_draft;   /* k in [1, 64] */
+    int32_t vocab;       /* V >= 1 */
+    int32_t dtype;       /* sv_dtype of both logit arrays */
+    int32_t draft_kind;  /* sv_draft_kind */
+    float temperature;   /* T: 0 (greedy) or finite >= 1e-4 */
+    hipEvent_t probe_start;
+    hipEvent_t probe_stop;
+} sv_verify_desc;
+
+/* Shape and options of one sv_vat_labels call (probe events as above). */
+typedef struct sv_vat_desc {
+    int32_t blocks;      /* N >= 0 draft blocks */
+    int32_t num_draft;   /* k in [1, 64] positions per block */
+    int32_t vocab;       /* V >= 1 */
+    int32_t dtype;       /* sv_dtype */
+    float temperature;   /* T: 0 (greedy labels) or finite >= 1e-4 */
+    float decay;         /* weight decay per position after the first rejection, in [0,1] */
+    hipEvent_t probe_start;
+    hipEvent_t probe_stop;
+} sv_vat_desc;
+
+/* Returns SV_ABI_VERSION of the built library. */
+int sv_abi_version(void);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* sv_status_str(int status);
+
+/* Workspace bytes sv_verify needs for `desc` (host out-parameter `bytes`).
+ * Errors: SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE, SV_ERR_BAD_DTYPE,
+ * SV_ERR_BAD_TEMPERATURE, SV_ERR_BAD_DRAFT_KIND. */
+sv_status sv_verify_workspace_size(const sv_verify_desc* desc, size_t* bytes);
+
+/*
+ * Batched verification.  Source: NgramRL essay, section "投机解码：让草稿先跑，
+ * 考官殿后" (acceptance rule, truncation, residual / bonus token); NgramRL
+ * summary, section "自适应 fan-out 预取" (outcome pair).
+ *
+ *  target_logits  device, [B][k+1][V] dtype: target logits at positions 0..k
+ *  draft_logits   device, [B][k][V] dtype; read only when draft_kind is
+ *                 SV_DRAFT_LOGITS and T > 0 (may be NULL otherwise)
+ *  draft_tokens   device, [B][k] int32: proposed tokens, expected in [0, V)
+ *  uniforms       device, [B][k+1] float32 in [0,1): column i < k drives test i,
+ *                 column k the single residual / bonus draw; unused (may be
+ *                 NULL) at T == 0
+ *  accepted_len   device out, [B] int32 in [0, k] (-1: invalid token)
+ *  out_tokens     device out, [B][k+1] int32: x_0..x_{r-1}, then the target's
+ *                 token at r, then -1
+ *  probs_out      device out or NULL, [B][k][2] float32: (p_i(x_i), q_i(x_i))
+ *                 for every position (T == 0: ([x_i == g_i], 1))
+ *  row_stats_out  device out or NULL, [B(k+1) + B k][2] float32, target rows
+ *                 then draft rows (one-hot or T == 0: target rows only):
+ *                 (m, Z) with m = max_y l(y)/T and Z = sum_y exp(l(y)/T - m);
+ *                 at T == 0: (max_y l(y), first argmax as a float)
+ *  workspace      device, >= sv_verify_workspace_size bytes, zero-filled once
+ *  stream         HIP stream the kernels are enqueued on (0 = null stream)
+ *
+ * Errors (nothing launched): SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE,
+ * SV_ERR_BAD_DTYPE, SV_ERR_BAD_TEMPERATURE, SV_ERR_BAD_DRAFT_KIND,
+ * SV_ERR_WORKSPACE_TOO_SMALL.  Launch failure: SV_ERR_HIP.
+ */
+sv_status sv_verify(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len,
+                    int32_t* out_tokens, float* probs_out, float* row_stats_out, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes sv_vat_labels needs for `desc`.  Errors as for
+ * sv_verify_workspace_size, plus SV_ERR_BAD_DECAY. */
+sv_status sv_vat_workspace_size(const sv_vat_desc* desc, size_t* bytes);
+
+/*
+ * VAT labels.  Source: VAT write-up, sections "VAT怎么把“验收规则”塞进训练里"
+ * (simulated verification, labels) and "第二件事，改权重分配的锚点" (weights).
+ *
+ *  target_logits  device, [N][k][V] dtype: target logits at the k drafted
+ *                 positions of each block (no bonus row)
+ *  draft_logits   device, [N][k][V] dtype (unused, may be NULL, at T == 0)
+ *  draft_tokens   device, [N][k] int32
+ *  uniforms       device, [N][k] float32 in [0,1) (unused at T == 0)
+ *  accept_mask    device out, [N][k] uint8: 1 before the first rejection, else 0
+ *  first_reject   device out, [N] int32: r in [0,k], k = no rejection (-1: invalid token)
+ *  weights        device out, [N][k] float32: 1 for i < r, decay^(i-r) for i >= r
+ *  probs_out      device out or NULL, [N][k][2] float32 (p_i(x_i), q_i(x_i))
+ *  row_stats_out  device out or NULL, [N k + N k][2] float32, as for sv_verify
+ *  workspace, workspace_bytes, stream: as for sv_verify
+ *
+ * Errors as for sv_verify, plus SV_ERR_BAD_DECAY.
+ */
+sv_status sv_vat_labels(const sv_vat_desc* desc, const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms, uint8_t* accept_mask,
+                        int32_t* first_reject, float* weights, float* probs_out, float* row_stats_out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

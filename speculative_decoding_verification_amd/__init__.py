@@ -1,0 +1,290 @@
+"""Python binding of libspecverify (batched speculative-sampling verification on MI355X).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch supplies device memory (tensors) and the stream (the current
+torch stream of the tensors' device).  There is no CPU fallback: if the
+library is not built, importing works but every call raises.
+
+    from speculative_decoding_verification_amd import verify, vat_labels
+    acc, out = verify(target, draft, tokens, uniforms, temperature=1.0)
+
+Names follow the C ABI in ``include/specverify.h``: ``sv_verify`` ->
+:func:`verify`, ``sv_vat_labels`` -> :func:`vat_labels`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+__all__ = ["verify", "vat_labels", "Verifier", "VatLabeler", "SVError", "library_path", "load_library",
+           "SV_F32", "SV_BF16", "SV_DRAFT_LOGITS", "SV_DRAFT_ONEHOT", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_F32, SV_BF16 = 0, 1
+SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT = 0, 1
+STATUS = {0: "SV_OK", 1: "SV_ERR_NULL_ARG", 2: "SV_ERR_BAD_SHAPE", 3: "SV_ERR_BAD_DTYPE",
+          4: "SV_ERR_BAD_TEMPERATURE", 5: "SV_ERR_BAD_DRAFT_KIND", 6: "SV_ERR_WORKSPACE_TOO_SMALL",
+          7: "SV_ERR_BAD_DECAY", 8: "SV_ERR_HIP"}
+
+EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_size", "sv_verify",
+                    "sv_vat_workspace_size", "sv_vat_labels")
+
+
+class SVError(RuntimeError):
+    def __init__(self, status: int, where: str, lib=None):
+        self.status = status
+        msg = STATUS.get(status, "status %d" % status)
+        if lib is not None:
+            msg = lib.sv_status_str(status).decode()
+        super().__init__("%s: %s" % (where, msg))
+
+
+class VerifyDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("draft_kind", ctypes.c_int32), ("temperature", ctypes.c_float),
+                ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+
+
+class VatDesc(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float), ("decay", ctypes.c_float),
+                ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Loads libspecverify.so (built in-tree).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libspecverify.so is not built (%s); run "
+                           "`python -m speculative_decoding_verification_amd.build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.sv_abi_version.restype = ctypes.c_int
+    lib.sv_abi_version.argtypes = []
+    lib.sv_status_str.restype = ctypes.c_char_p
+    lib.sv_status_str.argtypes = [ctypes.c_int]
+    lib.sv_verify_workspace_size.restype = ctypes.c_int
+    lib.sv_verify_workspace_size.argtypes = [ctypes.POINTER(VerifyDesc), ctypes.POINTER(sz)]
+    lib.sv_verify.restype = ctypes.c_int
+    lib.sv_verify.argtypes = [ctypes.POINTER(VerifyDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sv_vat_workspace_size.restype = ctypes.c_int
+    lib.sv_vat_workspace_size.argtypes = [ctypes.POINTER(VatDesc), ctypes.POINTER(sz)]
+    lib.sv_vat_labels.restype = ctypes.c_int
+    lib.sv_vat_labels.argtypes = [ctypes.POINTER(VatDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError("logits must be torch.float32 or torch.bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(name, t, device, dtype=None, shape=None):
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+class _Workspace:
+    """Per-device zero-filled workspace, grown on demand (the library allocates nothing)."""
+
+    def __init__(self):
+        self._buf = {}
+
+    def get(self, device, nbytes: int):
+        torch = _torch()
+        buf = self._buf.get(device)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._buf[device] = buf
+        return buf
+
+
+_WS = _Workspace()
+
+
+def _stream_handle(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+class VerifyOutput(NamedTuple):
+    accepted_len: "object"
+    out_tokens: "object"
+    probs: "object"
+    row_stats: "object"
+
+
+class Verifier:
+    """A prepared sv_verify call: descriptor, outputs and workspace built once,
+    so that repeated calls (bench loops, decode steps) only cross ctypes."""
+
+    def __init__(self, target, draft, draft_tokens, uniforms, temperature: float, *, onehot: bool = False,
+                 return_probs: bool = False, return_row_stats: bool = False, workspace=None, probe=None):
+        torch = _torch()
+        lib = load_library()
+        if target.dim() != 3:
+            raise ValueError("target must be [B][k+1][V]")
+        B, kp1, V = (int(s) for s in target.shape)
+        k = kp1 - 1
+        device = target.device
+        dt = _dtype_code(target)
+        _check_dev("target", target, device)
+        greedy = float(temperature) == 0.0
+        uses_draft = (not onehot) and not greedy
+        if uses_draft:
+            if draft is None:
+                raise ValueError("draft logits are required unless onehot or temperature == 0")
+            _check_dev("draft", draft, device, target.dtype, (B, k, V))
+        else:
+            draft = None
+        _check_dev("draft_tokens", draft_tokens, device, torch.int32, (B, k))
+        if not greedy:
+            if uniforms is None:
+                raise ValueError("uniforms are required unless temperature == 0")
+            _check_dev("uniforms", uniforms, device, torch.float32, (B, k + 1))
+        else:
+            uniforms = None
+        self.desc = VerifyDesc(B, k, V, dt, SV_DRAFT_ONEHOT if onehot else SV_DRAFT_LOGITS, float(temperature),
+                               None, None)
+        if probe is not None:
+            self.desc.probe_start, self.desc.probe_stop = probe
+        nbytes = ctypes.c_size_t()
+        st = lib.sv_verify_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
+        if st:
+            raise SVError(st, "sv_verify_workspace_size", lib)
+        if workspace is None:
+            workspace = _WS.get(device, nbytes.value)
+        elif workspace.numel() * workspace.element_size() < nbytes.value:
+            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+        self.accepted_len = torch.empty(B, dtype=torch.int32, device=device)
+        self.out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
+        self.probs = torch.empty((B, k, 2), dtype=torch.float32, device=device) if return_probs else None
+        rows = B * (k + 1) + (B * k if uses_draft else 0)
+        self.row_stats = torch.empty((rows, 2), dtype=torch.float32, device=device) if return_row_stats else None
+        self._keep = (target, draft, draft_tokens, uniforms, workspace)
+        self._lib = lib
+        self._device = device
+        self._args = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                      _ptr(self.accepted_len), _ptr(self.out_tokens), _ptr(self.probs), _ptr(self.row_stats),
+                      workspace.data_ptr(), workspace.numel() * workspace.element_size())
+
+    def __call__(self, stream: Optional[int] = None) -> VerifyOutput:
+        s = _stream_handle(self._device) if stream is None else stream
+        st = self._lib.sv_verify(*self._args, s)
+        if st:
+            raise SVError(st, "sv_verify", self._lib)
+        return VerifyOutput(self.accepted_len, self.out_tokens, self.probs, self.row_stats)
+
+
+def verify(target, draft, draft_tokens, uniforms, temperature: float, *, onehot: bool = False,
+           return_probs: bool = False, return_row_stats: bool = False, workspace=None) -> VerifyOutput:
+    """sv_verify on torch tensors (all on one HIP device, contiguous).
+
+    target [B][k+1][V] bf16/fp32; draft [B][k][V] same dtype (ignored when
+    onehot or temperature == 0); draft_tokens [B][k] int32; uniforms [B][k+1]
+    float32 (ignored at temperature 0).  Returns (accepted_len [B],
+    out_tokens [B][k+1], probs [B][k][2] or None, row_stats or None).
+    """
+    return Verifier(target, draft, draft_tokens, uniforms, temperature, onehot=onehot, return_probs=return_probs,
+                    return_row_stats=return_row_stats, workspace=workspace)()
+
+
+class VatOutput(NamedTuple):
+    accept_mask: "object"
+    first_reject: "object"
+    weights: "object"
+    probs: "object"
+    row_stats: "object"
+
+
+class VatLabeler:
+    """A prepared sv_vat_labels call (see :class:`Verifier`)."""
+
+    def __init__(self, target, draft, draft_tokens, uniforms, temperature: float, decay: float, *,
+                 return_probs: bool = False, return_row_stats: bool = False, workspace=None, probe=None):
+        torch = _torch()
+        lib = load_library()
+        if target.dim() != 3:
+            raise ValueError("target must be [N][k][V]")
+        N, k, V = (int(s) for s in target.shape)
+        device = target.device
+        dt = _dtype_code(target)
+        _check_dev("target", target, device)
+        greedy = float(temperature) == 0.0
+        if not greedy:
+            if draft is None or uniforms is None:
+                raise ValueError("draft logits and uniforms are required unless temperature == 0")
+            _check_dev("draft", draft, device, target.dtype, (N, k, V))
+            _check_dev("uniforms", uniforms, device, torch.float32, (N, k))
+        else:
+            draft, uniforms = None, None
+        _check_dev("draft_tokens", draft_tokens, device, torch.int32, (N, k))
+        self.desc = VatDesc(N, k, V, dt, float(temperature), float(decay), None, None)
+        if probe is not None:
+            self.desc.probe_start, self.desc.probe_stop = probe
+        nbytes = ctypes.c_size_t()
+        st = lib.sv_vat_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
+        if st:
+            raise SVError(st, "sv_vat_workspace_size", lib)
+        if workspace is None:
+            workspace = _WS.get(device, nbytes.value)
+        elif workspace.numel() * workspace.element_size() < nbytes.value:
+            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+        self.accept_mask = torch.empty((N, k), dtype=torch.uint8, device=device)
+        self.first_reject = torch.empty(N, dtype=torch.int32, device=device)
+        self.weights = torch.empty((N, k), dtype=torch.float32, device=device)
+        self.probs = torch.empty((N, k, 2), dtype=torch.float32, device=device) if return_probs else None
+        rows = N * k * (1 if greedy else 2)
+        self.row_stats = torch.empty((rows, 2), dtype=torch.float32, device=device) if return_row_stats else None
+        self._keep = (target, draft, draft_tokens, uniforms, workspace)
+        self._lib = lib
+        self._device = device
+        self._args = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                      _ptr(self.accept_mask), _ptr(self.first_reject), _ptr(self.weights), _ptr(self.probs),
+                      _ptr(self.row_stats), workspace.data_ptr(), workspace.numel() * workspace.element_size())
+
+    def __call__(self, stream: Optional[int] = None) -> VatOutput:
+        s = _stream_handle(self._device) if stream is None else stream
+        st = self._lib.sv_vat_labels(*self._args, s)
+        if st:
+            raise SVError(st, "sv_vat_labels", self._lib)
+        return VatOutput(self.accept_mask, self.first_reject, self.weights, self.probs, self.row_stats)
+
+
+def vat_labels(target, draft, draft_tokens, uniforms, temperature: float, decay: float = 0.8, *,
+               return_probs: bool = False, return_row_stats: bool = False, workspace=None) -> VatOutput:
+    """sv_vat_labels on torch tensors: target/draft [N][k][V], tokens/uniforms [N][k]."""
+    return VatLabeler(target, draft, draft_tokens, uniforms, temperature, decay, return_probs=return_probs,
+                      return_row_stats=return_row_stats, workspace=workspace)()

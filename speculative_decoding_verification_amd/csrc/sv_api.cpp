@@ -1,0 +1,219 @@
+// C ABI of libspecverify: host-side argument checks, workspace planning and
+// dispatch to the gfx950 kernels.  Every check runs before anything is
+// enqueued, so an error return leaves all outputs and the workspace untouched.
+#include <cmath>
+#include <cstdint>
+
+#include "sv_launch.h"
+#include "specverify.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int64_t kMaxVocab = int64_t{1} << 24;
+constexpr float kMinTemperature = 1e-4f;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool temperature_ok(float t) { return t == 0.f || (std::isfinite(t) && t >= kMinTemperature); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Shape {
+    int64_t batch, k, vocab;
+    int elem_bytes;
+    int64_t target_rows_per_seq;
+    int64_t rows_t, rows_d;
+    int64_t chunk, chunks;
+    bool greedy, onehot, vat;
+};
+
+// Shared checks of both entry points.  `draft_kind` is SV_DRAFT_LOGITS for VAT.
+sv_status check_shape(int32_t batch, int32_t k, int32_t vocab, int32_t dtype, int32_t draft_kind,
+                      float temperature, bool vat, Shape* s) {
+    if (batch < 0 || k < 1 || k > SV_MAX_DRAFT || vocab < 1 || vocab > kMaxVocab) return SV_ERR_BAD_SHAPE;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_BAD_DTYPE;
+    if (!temperature_ok(temperature)) return SV_ERR_BAD_TEMPERATURE;
+    if (draft_kind != SV_DRAFT_LOGITS && draft_kind != SV_DRAFT_ONEHOT) return SV_ERR_BAD_DRAFT_KIND;
+    s->batch = batch;
+    s->k = k;
+    s->vocab = vocab;
+    s->elem_bytes = dtype == SV_BF16 ? 2 : 4;
+    s->greedy = temperature == 0.f;
+    s->onehot = draft_kind == SV_DRAFT_ONEHOT;
+    s->vat = vat;
+    s->target_rows_per_seq = vat ? k : k + 1;
+    s->rows_t = s->batch * s->target_rows_per_seq;
+    s->rows_d = (s->greedy || s->onehot) ? 0 : s->batch * k;
+    s->chunk = chunk_elems(s->elem_bytes);
+    s->chunks = ceil_div(vocab, s->chunk);
+    // Byte offsets of the largest logit array must fit in int64.
+    const double bytes = static_cast<double>(s->rows_t + s->batch * k) * vocab * s->elem_bytes;
+    if (bytes > 4.0e18) return SV_ERR_BAD_SHAPE;
+    return SV_OK;
+}
+
+size_t workspace_bytes_for(const Shape& s) {
+    return workspace_layout(s.rows_t + s.rows_d, s.batch, s.chunks).total;
+}
+
+void fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
+    pl->batch = static_cast<int32_t>(s.batch);
+    pl->k = static_cast<int32_t>(s.k);
+    pl->vocab = static_cast<int32_t>(s.vocab);
+    pl->elem_bytes = s.elem_bytes;
+    pl->target_rows_per_seq = static_cast<int32_t>(s.target_rows_per_seq);
+    pl->chunks = static_cast<int32_t>(s.chunks);
+    pl->chunk = static_cast<int32_t>(s.chunk);
+    pl->rows_t = s.rows_t;
+    pl->rows_d = s.rows_d;
+    pl->greedy = s.greedy;
+    pl->onehot = s.onehot;
+    pl->vat = s.vat;
+    pl->temperature = temperature;
+    pl->c2 = s.greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+    pl->decay = decay;
+}
+
+void carve_workspace(const Shape& s, void* ws, Plan* pl) {
+    const WorkspaceLayout L = workspace_layout(s.rows_t + s.rows_d, s.batch, s.chunks);
+    char* base = static_cast<char*>(ws);
+    pl->partials = reinterpret_cast<float2*>(base + L.partials);
+    pl->row_mz = reinterpret_cast<float2*>(base + L.row_mz);
+    pl->seq = reinterpret_cast<SeqState*>(base + L.seq);
+    pl->resid = reinterpret_cast<float*>(base + L.resid);
+}
+
+}  // namespace
+
+WorkspaceLayout workspace_layout(int64_t rows, int64_t batch, int64_t chunks) {
+    WorkspaceLayout L;
+    size_t off = 0;
+    L.partials = off;
+    off = align_up(off + static_cast<size_t>(rows * chunks) * sizeof(float2));
+    L.row_mz = off;
+    off = align_up(off + static_cast<size_t>(rows) * sizeof(float2));
+    L.seq = off;
+    off = align_up(off + static_cast<size_t>(batch) * sizeof(SeqState));
+    L.resid = off;
+    off = align_up(off + static_cast<size_t>(batch * chunks) * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+}  // namespace sv
+
+extern "C" {
+
+int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char* sv_status_str(int status) {
+    switch (status) {
+        case SV_OK: return "SV_OK";
+        case SV_ERR_NULL_ARG: return "SV_ERR_NULL_ARG: a required pointer is NULL";
+        case SV_ERR_BAD_SHAPE: return "SV_ERR_BAD_SHAPE: batch < 0, k outside [1,64], vocab outside [1,2^24] or size overflow";
+        case SV_ERR_BAD_DTYPE: return "SV_ERR_BAD_DTYPE: dtype must be SV_F32 or SV_BF16";
+        case SV_ERR_BAD_TEMPERATURE: return "SV_ERR_BAD_TEMPERATURE: temperature must be 0 or finite and >= 1e-4";
+        case SV_ERR_BAD_DRAFT_KIND: return "SV_ERR_BAD_DRAFT_KIND: draft_kind must be SV_DRAFT_LOGITS or SV_DRAFT_ONEHOT";
+        case SV_ERR_WORKSPACE_TOO_SMALL: return "SV_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the size query";
+        case SV_ERR_BAD_DECAY: return "SV_ERR_BAD_DECAY: decay must be in [0, 1]";
+        case SV_ERR_HIP: return "SV_ERR_HIP: a HIP launch or event record failed";
+        default: return "unknown status";
+    }
+}
+
+sv_status sv_verify_workspace_size(const sv_verify_desc* desc, size_t* bytes) {
+    if (!desc || !bytes) return SV_ERR_NULL_ARG;
+    sv::Shape s;
+    const sv_status st = sv::check_shape(desc->batch, desc->num_draft, desc->vocab, desc->dtype, desc->draft_kind,
+                                         desc->temperature, false, &s);
+    if (st != SV_OK) return st;
+    *bytes = sv::workspace_bytes_for(s);
+    return SV_OK;
+}
+
+sv_status sv_verify(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len, int32_t* out_tokens,
+                    float* probs_out, float* row_stats_out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+    if (!desc) return SV_ERR_NULL_ARG;
+    sv::Shape s;
+    sv_status st = sv::check_shape(desc->batch, desc->num_draft, desc->vocab, desc->dtype, desc->draft_kind,
+                                   desc->temperature, false, &s);
+    if (st != SV_OK) return st;
+    if (s.batch == 0) return SV_OK;
+    if (!target_logits || !draft_tokens || !accepted_len || !out_tokens) return SV_ERR_NULL_ARG;
+    if (!s.greedy && !uniforms) return SV_ERR_NULL_ARG;
+    if (s.rows_d && !draft_logits) return SV_ERR_NULL_ARG;
+    const size_t need = sv::workspace_bytes_for(s);
+    if (!workspace) return SV_ERR_NULL_ARG;
+    if (workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
+
+    sv::Plan pl{};
+    sv::fill_plan(s, desc->temperature, 0.f, &pl);
+    pl.vec = (s.vocab * s.elem_bytes) % 16 == 0 && sv::aligned16(target_logits) &&
+             (!s.rows_d || sv::aligned16(draft_logits));
+    pl.target = target_logits;
+    pl.draft = s.rows_d ? draft_logits : nullptr;
+    pl.tokens = draft_tokens;
+    pl.uniforms = uniforms;
+    pl.accepted_len = accepted_len;
+    pl.out_tokens = out_tokens;
+    pl.probs_out = probs_out;
+    pl.row_stats_out = row_stats_out;
+    sv::carve_workspace(s, workspace, &pl);
+    const hipError_t e = sv::launch_path(pl, stream, desc->probe_start, desc->probe_stop);
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status sv_vat_workspace_size(const sv_vat_desc* desc, size_t* bytes) {
+    if (!desc || !bytes) return SV_ERR_NULL_ARG;
+    sv::Shape s;
+    const sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
+                                         desc->temperature, true, &s);
+    if (st != SV_OK) return st;
+    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
+    *bytes = sv::workspace_bytes_for(s);
+    return SV_OK;
+}
+
+sv_status sv_vat_labels(const sv_vat_desc* desc, const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms, uint8_t* accept_mask,
+                        int32_t* first_reject, float* weights, float* probs_out, float* row_stats_out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!desc) return SV_ERR_NULL_ARG;
+    sv::Shape s;
+    sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
+                                   desc->temperature, true, &s);
+    if (st != SV_OK) return st;
+    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
+    if (s.batch == 0) return SV_OK;
+    if (!target_logits || !draft_tokens || !accept_mask || !first_reject || !weights) return SV_ERR_NULL_ARG;
+    if (!s.greedy && (!uniforms || !draft_logits)) return SV_ERR_NULL_ARG;
+    const size_t need = sv::workspace_bytes_for(s);
+    if (!workspace) return SV_ERR_NULL_ARG;
+    if (workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
+
+    sv::Plan pl{};
+    sv::fill_plan(s, desc->temperature, desc->decay, &pl);
+    pl.vec = (s.vocab * s.elem_bytes) % 16 == 0 && sv::aligned16(target_logits) &&
+             (!s.rows_d || sv::aligned16(draft_logits));
+    pl.target = target_logits;
+    pl.draft = s.rows_d ? draft_logits : nullptr;
+    pl.tokens = draft_tokens;
+    pl.uniforms = uniforms;
+    pl.mask = accept_mask;
+    pl.first_reject = first_reject;
+    pl.weights = weights;
+    pl.probs_out = probs_out;
+    pl.row_stats_out = row_stats_out;
+    sv::carve_workspace(s, workspace, &pl);
+    const hipError_t e = sv::launch_path(pl, stream, desc->probe_start, desc->probe_stop);
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"

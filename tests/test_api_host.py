@@ -1,0 +1,214 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before anything is
+enqueued, leaving outputs untouched.  No call here reaches a kernel launch."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import speculative_decoding_verification_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.library_path()):
+        pytest.fail("libspecverify.so is not built; run __graft_entry__.build()")
+    return sv.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_bound_symbols():
+    assert _declared_functions() == sorted(sv.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen("nm -D --defined-only %s" % sv.library_path()).read()
+    for name in _declared_functions():
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_abi_version_and_status_strings(lib):
+    hdr = open(HEADER).read()
+    ver = int(re.search(r"#define SV_ABI_VERSION (\d+)", hdr).group(1))
+    assert lib.sv_abi_version() == ver
+    for code, name in sv.STATUS.items():
+        assert lib.sv_status_str(code).decode().startswith(name)
+    assert lib.sv_status_str(12345).decode() == "unknown status"
+
+
+def test_status_codes_match_header():
+    hdr = open(HEADER).read()
+    for code, name in sv.STATUS.items():
+        m = re.search(r"\b%s = (\d+)" % name, hdr)
+        assert m and int(m.group(1)) == code, name
+
+
+def _vdesc(B=2, k=3, V=1000, dtype=sv.SV_F32, kind=sv.SV_DRAFT_LOGITS, T=1.0):
+    return sv.VerifyDesc(B, k, V, dtype, kind, T, None, None)
+
+
+def _wsize(lib, d):
+    n = ctypes.c_size_t(0)
+    st = lib.sv_verify_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", -1, 2), ("num_draft", 0, 2), ("num_draft", 65, 2), ("vocab", 0, 2), ("vocab", (1 << 24) + 1, 2),
+    ("dtype", 2, 3), ("dtype", -1, 3), ("temperature", -1.0, 4), ("temperature", float("nan"), 4),
+    ("temperature", float("inf"), 4), ("temperature", 1e-5, 4), ("draft_kind", 2, 5),
+])
+def test_workspace_size_rejects_bad_desc(lib, field, value, status):
+    d = _vdesc()
+    setattr(d, field, value)
+    st, _ = _wsize(lib, d)
+    assert st == status
+
+
+def test_workspace_size_null_args(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.sv_verify_workspace_size(None, ctypes.byref(n)) == 1
+    d = _vdesc()
+    assert lib.sv_verify_workspace_size(ctypes.byref(d), None) == 1
+
+
+def test_workspace_size_grows_with_problem(lib):
+    sizes = []
+    for B in (1, 8, 64):
+        st, n = _wsize(lib, _vdesc(B=B, V=151936, dtype=sv.SV_BF16))
+        assert st == 0
+        sizes.append(n)
+    assert sizes[0] < sizes[1] < sizes[2]
+    assert all(s % 256 == 0 for s in sizes)
+    # one-hot and greedy read no draft rows: smaller workspace
+    _, n_logits = _wsize(lib, _vdesc(B=8, V=151936, dtype=sv.SV_BF16))
+    _, n_onehot = _wsize(lib, _vdesc(B=8, V=151936, dtype=sv.SV_BF16, kind=sv.SV_DRAFT_ONEHOT))
+    _, n_greedy = _wsize(lib, _vdesc(B=8, V=151936, dtype=sv.SV_BF16, T=0.0))
+    assert n_onehot < n_logits and n_greedy == n_onehot
+
+
+class _HostBufs:
+    """Host buffers passed where device pointers go.  Only used on error paths,
+    where the library must return before touching them (checked)."""
+
+    def __init__(self, B=2, k=3, V=1000):
+        self.target = np.zeros(B * (k + 1) * V, np.float32)
+        self.draft = np.zeros(B * k * V, np.float32)
+        self.tokens = np.zeros(B * k, np.int32)
+        self.u = np.zeros(B * (k + 1), np.float32)
+        self.acc = np.full(B, 777, np.int32)
+        self.out = np.full(B * (k + 1), 777, np.int32)
+        self.probs = np.full(B * k * 2, 777, np.float32)
+        self.ws = np.full(1 << 16, 0xAB, np.uint8)
+
+    def p(self, a):
+        return None if a is None else a.ctypes.data
+
+    def untouched(self):
+        return (np.all(self.acc == 777) and np.all(self.out == 777) and np.all(self.probs == 777)
+                and np.all(self.ws == 0xAB))
+
+
+def _call_verify(lib, d, h, **over):
+    args = dict(target=h.target, draft=h.draft, tokens=h.tokens, u=h.u, acc=h.acc, out=h.out, probs=h.probs,
+                stats=None, ws=h.ws, ws_bytes=h.ws.nbytes)
+    args.update(over)
+    return lib.sv_verify(ctypes.byref(d) if d is not None else None, h.p(args["target"]), h.p(args["draft"]),
+                         h.p(args["tokens"]), h.p(args["u"]), h.p(args["acc"]), h.p(args["out"]),
+                         h.p(args["probs"]), h.p(args["stats"]), h.p(args["ws"]), args["ws_bytes"], None)
+
+
+def test_verify_null_and_shape_errors_leave_outputs_untouched(lib):
+    h = _HostBufs()
+    assert _call_verify(lib, None, h) == 1
+    assert _call_verify(lib, _vdesc(), h, target=None) == 1
+    assert _call_verify(lib, _vdesc(), h, tokens=None) == 1
+    assert _call_verify(lib, _vdesc(), h, acc=None) == 1
+    assert _call_verify(lib, _vdesc(), h, out=None) == 1
+    assert _call_verify(lib, _vdesc(), h, u=None) == 1            # T > 0 needs uniforms
+    assert _call_verify(lib, _vdesc(), h, draft=None) == 1        # draft logits needed
+    assert _call_verify(lib, _vdesc(), h, ws=None) == 1
+    d = _vdesc()
+    d.num_draft = 70
+    assert _call_verify(lib, d, h) == 2
+    d = _vdesc(T=-0.5)
+    assert _call_verify(lib, d, h) == 4
+    d = _vdesc(dtype=7)
+    assert _call_verify(lib, d, h) == 3
+    assert h.untouched()
+
+
+def test_verify_workspace_too_small(lib):
+    h = _HostBufs()
+    d = _vdesc()
+    st, need = _wsize(lib, d)
+    assert st == 0 and need > 16
+    assert _call_verify(lib, d, h, ws_bytes=need - 1) == 6
+    # one-hot drafts need no draft logits: the missing pointer is not an error,
+    # the workspace is (nothing is launched either way)
+    d1 = _vdesc(kind=sv.SV_DRAFT_ONEHOT)
+    assert _call_verify(lib, d1, h, draft=None, ws_bytes=8) == 6
+    # greedy needs neither uniforms nor draft logits
+    d0 = _vdesc(T=0.0)
+    assert _call_verify(lib, d0, h, draft=None, u=None, ws_bytes=8) == 6
+    assert h.untouched()
+
+
+def test_verify_empty_batch_is_a_noop(lib):
+    d = _vdesc(B=0)
+    assert lib.sv_verify(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None) == 0
+
+
+def _vat_desc(N=2, k=3, V=1000, dtype=sv.SV_F32, T=1.0, decay=0.8):
+    return sv.VatDesc(N, k, V, dtype, T, decay, None, None)
+
+
+@pytest.mark.parametrize("decay", [-0.1, 1.5, float("nan")])
+def test_vat_bad_decay(lib, decay):
+    n = ctypes.c_size_t()
+    d = _vat_desc(decay=decay)
+    assert lib.sv_vat_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 7
+    h = _HostBufs()
+    mask = np.full(6, 7, np.uint8)
+    fr = np.full(2, 7, np.int32)
+    w = np.full(6, 7, np.float32)
+    st = lib.sv_vat_labels(ctypes.byref(d), h.p(h.target), h.p(h.draft), h.p(h.tokens), h.p(h.u), h.p(mask),
+                           h.p(fr), h.p(w), None, None, h.p(h.ws), h.ws.nbytes, None)
+    assert st == 7
+    assert np.all(mask == 7) and np.all(fr == 7) and np.all(w == 7) and h.untouched()
+
+
+def test_vat_null_and_workspace_errors(lib):
+    h = _HostBufs()
+    mask = np.full(6, 7, np.uint8)
+    fr = np.full(2, 7, np.int32)
+    w = np.full(6, 7, np.float32)
+    d = _vat_desc()
+
+    def call(**o):
+        a = dict(t=h.target, dr=h.draft, x=h.tokens, u=h.u, m=mask, f=fr, w=w, ws=h.ws, n=h.ws.nbytes)
+        a.update(o)
+        return lib.sv_vat_labels(ctypes.byref(d), h.p(a["t"]), h.p(a["dr"]), h.p(a["x"]), h.p(a["u"]),
+                                 h.p(a["m"]), h.p(a["f"]), h.p(a["w"]), None, None, h.p(a["ws"]), a["n"], None)
+
+    assert call(t=None) == 1
+    assert call(dr=None) == 1
+    assert call(u=None) == 1
+    assert call(m=None) == 1
+    assert call(f=None) == 1
+    assert call(w=None) == 1
+    assert call(n=8) == 6
+    assert np.all(mask == 7) and np.all(fr == 7) and np.all(w == 7) and h.untouched()

@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases span several 8 KiB chunks and a ragged last chunk (V = 151936 is
+37.09 bf16 chunks); the full-size cases are the five workloads at their
+stated sizes, checked on every sequence where the oracle is fast and on a
+sample otherwise.  Tolerances and ambiguity bands are described in parity.py.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import compare_vat, compare_verify, check_row_stats, run_vat_gpu, run_verify_gpu, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import speculative_decoding_verification_amd as sv
+
+    sv.load_library()  # fails loudly if the library is not built
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _verify_case(wl, dev, T=None, onehot=None, seq_index=None):
+    cfg = wl.config
+    T = cfg.T if T is None else T
+    oh = cfg.onehot if onehot is None else onehot
+    _say("case verify %s B=%d k=%d V=%d %s T=%g onehot=%s" % (cfg.name, wl.n, cfg.k, cfg.V, cfg.dtype, T, oh))
+    gpu = run_verify_gpu(wl, dev, temperature=T, onehot=oh)
+    if seq_index is None:
+        orc = oracle.verify(wl.target, wl.draft, wl.tokens, wl.uniforms, T, onehot=oh)
+        check_row_stats(gpu["row_stats"], orc.target_mz, orc.draft_mz, T == 0.0, not oh and T != 0.0)
+        rep = compare_verify(gpu, orc, cfg.k, cfg.V, T == 0.0)
+    else:
+        idx = np.asarray(seq_index)
+        sub_d = wl.draft[idx] if wl.draft is not None else None
+        orc = oracle.verify(wl.target[idx], sub_d, wl.tokens[idx], wl.uniforms[idx], T, onehot=oh)
+        gsub = {k: v[idx] for k, v in gpu.items() if k != "row_stats"}
+        rows_per = cfg.k + 1
+        st_t = gpu["row_stats"][: wl.n * rows_per].reshape(wl.n, rows_per, 2)[idx].reshape(-1, 2)
+        st = st_t
+        if not oh and T != 0.0:
+            st_d = gpu["row_stats"][wl.n * rows_per:].reshape(wl.n, cfg.k, 2)[idx].reshape(-1, 2)
+            st = np.concatenate([st_t, st_d])
+        check_row_stats(st, orc.target_mz, orc.draft_mz, T == 0.0, not oh and T != 0.0)
+        rep = compare_verify(gsub, orc, cfg.k, cfg.V, T == 0.0)
+    _say("  parity ok:", rep)
+    return gpu, rep
+
+
+# ------------------------------------------------------------------ small cases
+
+@pytest.mark.parametrize("name,changes", [
+    ("tiny", {}),
+    ("selfdraft", {"B": 8}),
+    ("ngram_tail", {}),
+    ("grpo", {"B": 6}),
+    ("grpo_greedy", {"B": 16}),
+])
+def test_workloads_reduced(dev, name, changes):
+    cfg = workloads.get_config(name).scaled(**changes)
+    _verify_case(workloads.generate(cfg), dev)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_vat_reduced(dev, T):
+    cfg = workloads.get_config("vat").scaled(B=12, T=T)
+    wl = workloads.generate(cfg)
+    _say("case vat N=12 T=%g" % T)
+    gpu = run_vat_gpu(wl, dev)
+    orc = oracle.vat_labels(wl.target, wl.draft, wl.tokens, wl.uniforms, T, cfg.decay)
+    check_row_stats(gpu["row_stats"], orc.target_mz, orc.draft_mz, T == 0.0, T != 0.0)
+    _say("  parity ok:", compare_vat(gpu, orc, cfg.k, cfg.decay, T == 0.0))
+
+
+def _custom(B, k, V, dtype, T, sigma_t=3.0, sigma_d=0.5, mode="sample", onehot=False, seed=900):
+    return workloads.Config("custom", "verify", B, k, V, dtype, T, sigma_t, None if onehot else sigma_d,
+                            mode if not onehot else "ngram", seed)
+
+
+@pytest.mark.parametrize("B,k,V,dtype,T,onehot", [
+    (5, 3, 1001, "bf16", 1.0, False),     # rows not 16-byte aligned: scalar loads
+    (50, 2, 7, "f32", 1.0, False),        # V smaller than a vector
+    (64, 1, 4096, "bf16", 1.0, False),    # exactly one chunk
+    (3, 64, 5000, "f32", 0.8, False),     # k = 64: a full wavefront of positions
+    (1, 16, 151936, "bf16", 1.0, False),  # B = 1
+    (4, 5, 8200, "bf16", 0.01, False),    # sharp temperature, ragged 8-logit last chunk
+    (6, 4, 3000, "f32", 1.0, True),       # one-hot draft, fp32
+    (6, 4, 1001, "bf16", 1.0, True),      # one-hot draft, unaligned rows
+    (20, 4, 2048, "f32", 0.0, False),     # greedy fp32, exactly one chunk
+    (9, 3, 1001, "bf16", 0.0, False),     # greedy unaligned
+])
+def test_edge_shapes(dev, B, k, V, dtype, T, onehot):
+    cfg = _custom(B, k, V, dtype, T, onehot=onehot, mode="argmax" if T == 0 else "sample")
+    _verify_case(workloads.generate(cfg), dev)
+
+
+def test_neg_inf_logits_and_greedy_ties(dev):
+    rng = np.random.default_rng(77)
+    B, k, V = 12, 4, 9000
+    # coarse integer logits: many exact ties for the maximum; -inf blocks
+    t = rng.integers(-3, 4, (B, k + 1, V)).astype(np.float32)
+    t[:, :, 4096:6000] = -np.inf
+    t[:, :, 7000:] = -np.inf
+    d = t[:, :k] + rng.integers(-1, 2, (B, k, V)).astype(np.float32)
+    bits_t = workloads.round_to_bf16_bits(t)
+    bits_d = workloads.round_to_bf16_bits(d)
+    g = np.argmax(t, axis=2)
+    x = np.where(rng.random((B, k)) < 0.6, g[:, :k], rng.integers(0, 4096, (B, k))).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    cfg = _custom(B, k, V, "bf16", 1.0)
+    wl = workloads.Workload(cfg, 0, bits_t, bits_d, x, u)
+    _verify_case(wl, dev, T=0.0)
+    gpu, _ = _verify_case(wl, dev, T=1.0)
+    outs = gpu["out_tokens"][np.arange(B), np.maximum(gpu["accepted_len"], 0)]
+    assert not np.any(((outs >= 4096) & (outs < 6000)) | (outs >= 7000))
+
+
+def test_invalid_tokens_flag_sequence(dev):
+    cfg = _custom(6, 3, 2000, "f32", 1.0)
+    wl = workloads.generate(cfg)
+    wl.tokens[1, 2] = 2000
+    wl.tokens[4, 0] = -7
+    gpu, _ = _verify_case(wl, dev)
+    assert list(gpu["accepted_len"][[1, 4]]) == [-1, -1]
+    gpu0, _ = _verify_case(wl, dev, T=0.0)
+    assert list(gpu0["accepted_len"][[1, 4]]) == [-1, -1]
+
+
+def test_determinism_bitwise(dev):
+    cfg = workloads.get_config("grpo").scaled(B=16)
+    wl = workloads.generate(cfg)
+    runs = [run_verify_gpu(wl, dev) for _ in range(3)]
+    for r in runs[1:]:
+        for key in runs[0]:
+            assert np.array_equal(runs[0][key].view(np.uint8), r[key].view(np.uint8)), key
+
+
+def test_gpu_losslessness_chi_square(dev):
+    """The HIP sampler's outputs follow the target: V=8, k=3, 200k sequences."""
+    from scipy import stats
+
+    import speculative_decoding_verification_amd as sv
+    import torch
+
+    rng = np.random.default_rng(4242)
+    V, k, B = 8, 3, 200_000
+
+    def simplex(z=0):
+        p = rng.random(V) + 0.05
+        if z:
+            p[rng.choice(V, z, replace=False)] = 0
+        return p / p.sum()
+
+    with np.errstate(divide="ignore"):
+        lt1 = np.log(np.stack([simplex(1) for _ in range(k + 1)])).astype(np.float32)
+        ld1 = np.log(np.stack([simplex(i == 1) for i in range(k)])).astype(np.float32)
+    P = np.stack([oracle.softmax(lt1[i].astype(np.float64), 1.0)[0] for i in range(k + 1)])
+    Q = np.stack([oracle.softmax(ld1[i].astype(np.float64), 1.0)[0] for i in range(k)])
+    x = np.stack([rng.choice(V, size=B, p=Q[i]) for i in range(k)], axis=1).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    _say("case chi-square V=8 k=3 B=200000")
+    t = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(lt1, (B, k + 1, V)))).to(dev)
+    d = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(ld1, (B, k, V)))).to(dev)
+    res = sv.verify(t, d, to_torch(x, dev), to_torch(u, dev), 1.0)
+    L = res.accepted_len.cpu().numpy()
+    out = res.out_tokens.cpu().numpy()
+    alpha = np.minimum(P[:k], Q).sum(axis=1)
+    pv = []
+    for j in range(k + 1):
+        reach = L >= j
+        n = int(reach.sum())
+        er = float(np.prod(alpha[:j]))
+        sig = np.sqrt(er * (1 - er) / B) if 0 < er < 1 else 0
+        assert abs(n / B - er) < 5 * sig + 1e-9, (j, n / B, er)
+        c = np.bincount(out[reach, j], minlength=V)
+        sup = P[j] > 0
+        assert c[~sup].sum() == 0
+        pv.append(stats.chisquare(c[sup], n * P[j][sup] / P[j][sup].sum()).pvalue)
+    _say("  chi-square p-values", pv)
+    assert min(pv) > 1e-4 / len(pv)
+
+
+# ------------------------------------------------------------------ full sizes
+
+def test_full_selfdraft_all_sequences(dev):
+    wl = workloads.generate(workloads.get_config("selfdraft"))
+    _verify_case(wl, dev)
+
+
+def test_full_ngram_tail(dev):
+    wl = workloads.generate(workloads.get_config("ngram_tail"))
+    _verify_case(wl, dev)
+
+
+def test_full_grpo_sampled(dev):
+    cfg = workloads.get_config("grpo")
+    wl = workloads.generate(cfg)
+    idx = np.random.default_rng(1).choice(cfg.B, 40, replace=False)
+    idx.sort()
+    _verify_case(wl, dev, seq_index=idx)
+
+
+def test_full_grpo_greedy_all_sequences(dev):
+    cfg = workloads.get_config("grpo_greedy")
+    wl = workloads.generate(cfg, with_draft=True)
+    _verify_case(wl, dev)
+
+
+def test_full_vat_sampled(dev):
+    import speculative_decoding_verification_amd as sv
+    import torch
+
+    cfg = workloads.get_config("vat")
+    _say("case vat full N=2048 k=16 V=128256 f32 (33.6 GB, device-generated)")
+    t, d, x, u = workloads.generate_on_device(cfg, dev)
+    res = sv.vat_labels(t, d, x, u, cfg.T, cfg.decay, return_probs=True)
+    torch.cuda.synchronize()
+    fr = res.first_reject.cpu().numpy()
+    mask = res.accept_mask.cpu().numpy()
+    w = res.weights.cpu().numpy()
+    i = np.arange(cfg.k)
+    # every block: labels and weights follow its first rejection
+    assert np.all((fr >= 0) & (fr <= cfg.k))
+    assert np.array_equal(mask, (i[None, :] < fr[:, None]).astype(np.uint8))
+    want = np.where(i[None, :] < fr[:, None], 1.0, cfg.decay ** np.maximum(i[None, :] - fr[:, None], 0))
+    assert np.allclose(w, want, rtol=2e-7, atol=0)
+    idx = np.random.default_rng(5).choice(cfg.B, 24, replace=False)
+    idx.sort()
+    ti = torch.as_tensor(idx, device=dev)
+    tl = t.index_select(0, ti).cpu().numpy()
+    dl = d.index_select(0, ti).cpu().numpy()
+    xs = x.index_select(0, ti).cpu().numpy()
+    us = u.index_select(0, ti).cpu().numpy()
+    orc = oracle.vat_labels(tl, dl, xs, us, cfg.T, cfg.decay)
+    gpu = {"first_reject": fr[idx], "accept_mask": mask[idx], "weights": w[idx],
+           "probs": res.probs.cpu().numpy()[idx]}
+    rep = compare_vat(gpu, orc, cfg.k, cfg.decay, False)
+    _say("  parity ok:", rep, "mean first_reject", fr.mean())
+    del t, d, x, u, res
+    torch.cuda.empty_cache()

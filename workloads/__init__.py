@@ -36,8 +36,8 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Config", "Workload", "CONFIGS", "get_config", "generate", "round_to_bf16_bits",
-           "bf16_bits_to_f32"]
+__all__ = ["Config", "Workload", "CONFIGS", "get_config", "generate", "generate_on_device", "to_device",
+           "round_to_bf16_bits", "bf16_bits_to_f32"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -194,3 +194,63 @@ def generate(cfg: Config, lo: int = 0, hi: Optional[int] = None, workers: Option
         with ThreadPoolExecutor(workers) as ex:
             list(ex.map(lambda j: _one_sequence(*j), jobs))
     return Workload(cfg, lo, target, draft, tokens, u)
+
+
+def generate_on_device(cfg: Config, device, slab: int = 64):
+    """Device-side variant for workloads too large to draw on the host (the
+    33.6 GB VAT case): the same distributions drawn by torch's generator on
+    `device`, seeded per slab of `slab` sequences as (seed_logits, slab index).
+    Returns torch tensors (target, draft, tokens, uniforms); a checker copies
+    the sequences it samples back to the host and hands the oracle those bytes.
+    """
+    import torch
+
+    rows_t = cfg.target_rows_per_seq
+    st = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    target = torch.empty((cfg.B, rows_t, cfg.V), dtype=st, device=device)
+    draft = None if cfg.onehot else torch.empty((cfg.B, cfg.k, cfg.V), dtype=st, device=device)
+    tokens = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device=device)
+    uniforms = torch.empty((cfg.B, cfg.n_uniforms), dtype=torch.float32, device=device)
+    for s0 in range(0, cfg.B, slab):
+        s1 = min(cfg.B, s0 + slab)
+        g = torch.Generator(device=device)
+        g.manual_seed(int(cfg.seed_logits) * 1_000_003 + s0 // slab)
+        t = cfg.sigma_t * torch.randn((s1 - s0, rows_t, cfg.V), generator=g, device=device, dtype=torch.float32)
+        target[s0:s1] = t.to(st)
+        if draft is not None:
+            d = t[:, : cfg.k] + cfg.sigma_d * torch.randn((s1 - s0, cfg.k, cfg.V), generator=g, device=device,
+                                                           dtype=torch.float32)
+            draft[s0:s1] = d.to(st)
+            dv = draft[s0:s1].float()
+            if cfg.draft_mode == "sample":
+                # fp64 draws: an Exp(1) draw of exactly 0 (which would always win
+                # the race) has probability 2^-53 instead of 2^-24.
+                e = torch.empty(dv.shape, dtype=torch.float64, device=device).exponential_(generator=g)
+                tokens[s0:s1] = torch.argmax(dv.double() / cfg.T - torch.log(e), dim=2).to(torch.int32)
+                del e
+            elif cfg.draft_mode == "argmax":
+                tokens[s0:s1] = torch.argmax(dv, dim=2).to(torch.int32)
+            else:
+                raise ValueError(cfg.draft_mode)
+            del d, dv
+        else:
+            raise ValueError("device generation covers draft-logit workloads only")
+        uniforms[s0:s1] = torch.rand((s1 - s0, cfg.n_uniforms), generator=g, device=device, dtype=torch.float32)
+        del t
+    return target, draft, tokens, uniforms
+
+
+def to_device(wl: Workload, device):
+    """Copies a host workload to `device` as torch tensors (bf16 bits become
+    torch.bfloat16).  Returns (target, draft or None, tokens, uniforms)."""
+    import torch
+
+    def up(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(a).to(device)
+
+    return up(wl.target), up(wl.draft), up(wl.tokens), up(wl.uniforms)
