@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 2**20
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 METRIC = "verified draft positions/sec + achieved HBM GB/s (V=151936 bf16, k=5..16)"
 
 
@@ -43,14 +44,16 @@ class HipEvents:
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self):
+        # No system-scope fence at record time: the probes only timestamp the
+        # launch stream and should disturb it as little as possible.
         ev = ctypes.c_void_p()
-        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE)
         if rc != 0:
             raise RuntimeError("hipEventCreate failed: %d" % rc)
         return ev.value

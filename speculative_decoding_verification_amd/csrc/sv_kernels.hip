@@ -37,6 +37,8 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
 __device__ __forceinline__ const char* row_base(const void* p, int64_t row, int64_t V, int eb) {
     return static_cast<const char*>(p) + (row * V) * eb;
 }
@@ -162,6 +164,15 @@ __device__ __forceinline__ void wave_argmax(float& best, int& idx) {
     }
 }
 
+// Scale of a row with max m: returns mc = m*c2 rounded, and sets corr so that
+// exp2(fma(l, c2, -mc)) * corr == exp2((l - m) * c2) up to one rounding of the
+// exponent (corr = exp2(-(m*c2 - mc)), the rounding error of mc being exact).
+__device__ __forceinline__ float row_scale(float m, float c2, float& corr) {
+    const float mc = m * c2;
+    corr = exp2_hw(-fmaf(m, c2, -mc));
+    return mc;
+}
+
 // Merges (m, s) pairs where s = sum exp2((l - m) * c2) over disjoint sets.
 __device__ __forceinline__ void wave_merge_ms(float& m, float& s, float c2) {
     const float M = wave_max(m);
@@ -231,7 +242,11 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(const void* target, const 
 
     float s = 0.f;
     if (m != neg_inf()) {
+        // fma(v, c2, -mc) = (v - m) * c2 + dlt, rounded once, where
+        // dlt = m*c2 - mc is the (exactly representable) rounding error of
+        // mc: a factor exp2(dlt) common to the whole chunk, removed below.
         const float mc = m * c2;
+        const float dlt = fmaf(m, c2, -mc);
         float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
         for (int e = 0; e < Chunk<EB>::kPerLane; e += 4) {
@@ -240,7 +255,7 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(const void* target, const 
             a2 += exp2_hw(fmaf(v[e + 2], c2, -mc));
             a3 += exp2_hw(fmaf(v[e + 3], c2, -mc));
         }
-        s = (a0 + a1) + (a2 + a3);
+        s = ((a0 + a1) + (a2 + a3)) * exp2_hw(-dlt);
     }
     s = wave_sum(s);
     if (lane == 0) partials[item] = make_float2(m, s);
@@ -278,10 +293,12 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(const void* target, int64
 
 // ------------------------------------------------------------------ kernel 2
 
+// log2 of p(x) = exp((l(x) - m)/T) / Z for a row with statistics (m, Z).
 template <int EB>
-__device__ __forceinline__ float prob_of(const void* logits, int64_t row, int64_t V, int x, float2 mz, float c2) {
+__device__ __forceinline__ float log2_prob_of(const void* logits, int64_t row, int64_t V, int x, float2 mz,
+                                              float c2) {
     const float l = Elem<EB>::at(row_base(logits, row, V, EB), x);
-    return exp2_hw(fmaf(l, c2, -(mz.x * c2))) / mz.y;
+    return (l - mz.x) * c2 - log2_hw(mz.y);
 }
 
 template <int EB>
@@ -361,10 +378,16 @@ __global__ __launch_bounds__(kBlock) void k_accept(Plan pl) {
             p = keep ? 1.f : 0.f;
             q = 1.f;
         } else {
-            p = prob_of<EB>(pl.target, trow, V, x, s_mz[i], c2);
-            q = pl.onehot ? 1.f : prob_of<EB>(pl.draft, static_cast<int64_t>(b) * k + i, V, x, s_mz[n_t + i], c2);
+            // The test u*q < p, taken in the log2 domain so that probabilities
+            // below the fp32 range still decide correctly (log2(0) = -inf).
+            const float lp = log2_prob_of<EB>(pl.target, trow, V, x, s_mz[i], c2);
+            const float lq = pl.onehot ? 0.f
+                                       : log2_prob_of<EB>(pl.draft, static_cast<int64_t>(b) * k + i, V, x,
+                                                          s_mz[n_t + i], c2);
             const float u = pl.uniforms[static_cast<int64_t>(b) * n_u + i];
-            keep = u * q < p;
+            keep = log2_hw(u) + lq < lp;
+            p = exp2_hw(lp);
+            q = exp2_hw(lq);
         }
     }
     const uint64_t kept = __ballot(keep);
@@ -381,7 +404,11 @@ __global__ __launch_bounds__(kBlock) void k_accept(Plan pl) {
         if (active) {
             const int64_t o = static_cast<int64_t>(b) * k + i;
             pl.mask[o] = static_cast<uint8_t>(!invalid && i < r);
-            pl.weights[o] = invalid ? 0.f : (i < r ? 1.f : powf(pl.decay, static_cast<float>(i - r)));
+            // decay^(i-r) in fp64, rounded once to fp32
+            pl.weights[o] = invalid ? 0.f
+                                    : (i < r ? 1.f
+                                             : static_cast<float>(pow(static_cast<double>(pl.decay),
+                                                                      static_cast<double>(i - r))));
         }
         if (lane == 0) pl.first_reject[b] = r;
         return;
@@ -424,11 +451,12 @@ struct ResidW {
 
 __device__ __forceinline__ ResidW make_resid_w(float2 mzt, float2 mzd, float c2) {
     ResidW w;
+    float ct, cd;
     w.c2 = c2;
-    w.mt = mzt.x * c2;
-    w.izt = 1.f / mzt.y;
-    w.md = mzd.x * c2;
-    w.izd = 1.f / mzd.y;
+    w.mt = row_scale(mzt.x, c2, ct);
+    w.izt = ct / mzt.y;
+    w.md = row_scale(mzd.x, c2, cd);
+    w.izd = cd / mzd.y;
     return w;
 }
 
@@ -467,7 +495,8 @@ struct DrawRow {
     int mode;        // kModeBonus (plain target row), kModeOneHot, kModeResidual
     const char* rt;  // target row
     const char* rd;  // draft row (residual only)
-    float c2, mt;    // mt = row max * c2 (bonus / one-hot)
+    float c2, mt;    // mt = row max * c2 rounded (bonus / one-hot)
+    float corr;      // exact correction of that rounding (see row_scale)
     int excl;        // one-hot: excluded token, else -1
     ResidW rw;
 };
@@ -476,7 +505,7 @@ template <int EB>
 __device__ __forceinline__ float draw_weight(const DrawRow& d, int64_t y) {
     if (d.mode == kModeResidual) return d.rw(Elem<EB>::at(d.rt, y), Elem<EB>::at(d.rd, y));
     if (y == d.excl) return 0.f;
-    return exp2_hw(fmaf(Elem<EB>::at(d.rt, y), d.c2, -d.mt));
+    return exp2_hw(fmaf(Elem<EB>::at(d.rt, y), d.c2, -d.mt)) * d.corr;
 }
 
 // Chunk masses of a plain target row from its k_row_stats partials, in the
@@ -525,7 +554,7 @@ __global__ __launch_bounds__(kBlock) void k_sample(Plan pl) {
     d.rt = row_base(pl.target, trow, V, EB);
     d.rd = nullptr;
     float2 mzt = pl.row_mz[trow];
-    d.mt = mzt.x * c2;
+    d.mt = row_scale(mzt.x, c2, d.corr);
     if (st.mode == kModeResidual) {
         const int64_t drow = static_cast<int64_t>(b) * k + r;
         d.rd = row_base(pl.draft, drow, V, EB);

@@ -17,6 +17,9 @@ import numpy as np
 
 BAND = 1e-5
 RTOL = 1e-5
+# fp32 outputs cannot hold probabilities below the smallest normal float (the
+# hardware exp2 flushes subnormal results): an absolute floor for p(x), q(x).
+FLT_MIN = float(np.finfo(np.float32).tiny)
 
 
 def to_torch(a, device):
@@ -76,9 +79,13 @@ def _assert_close(name, got, want, rtol=RTOL, atol=0.0):
 
 
 def check_row_stats(gpu_stats, orc_t_mz, orc_d_mz, greedy, rows_d_present):
+    """Rows of sequences the oracle flags for an invalid token carry NaN there
+    and are not compared (the library still reports their statistics)."""
     t = orc_t_mz.reshape(-1, 2)
     nt = t.shape[0]
     g_t = gpu_stats[:nt]
+    keep = ~np.isnan(t[:, 0])
+    t, g_t = t[keep], g_t[keep]
     if greedy:
         assert np.array_equal(g_t[:, 0].astype(np.float64), t[:, 0]), "greedy row max differs"
         assert np.array_equal(g_t[:, 1].astype(np.int64), t[:, 1].astype(np.int64)), "greedy argmax differs"
@@ -88,6 +95,8 @@ def check_row_stats(gpu_stats, orc_t_mz, orc_d_mz, greedy, rows_d_present):
     if rows_d_present:
         d = orc_d_mz.reshape(-1, 2)
         g_d = gpu_stats[nt:nt + d.shape[0]]
+        keep = ~np.isnan(d[:, 0])
+        d, g_d = d[keep], g_d[keep]
         _assert_close("draft m", g_d[:, 0], d[:, 0], atol=1e-6)
         _assert_close("draft Z", g_d[:, 1], d[:, 1])
 
@@ -104,8 +113,8 @@ def compare_verify(gpu, orc, k, V, greedy, seq_index=None):
     if greedy:
         assert np.array_equal(pg.astype(np.float64), po), "greedy probs differ"
     else:
-        _assert_close("p(x)", pg[..., 0], po[..., 0])
-        _assert_close("q(x)", pg[..., 1], po[..., 1])
+        _assert_close("p(x)", pg[..., 0], po[..., 0], atol=FLT_MIN)
+        _assert_close("q(x)", pg[..., 1], po[..., 1], atol=FLT_MIN)
     amb_accept = 0
     amb_sample = 0
     for j, b in enumerate(rows):
@@ -137,6 +146,8 @@ def compare_verify(gpu, orc, k, V, greedy, seq_index=None):
 
 
 def compare_vat(gpu, orc, k, decay, greedy, blk_index=None):
+    """`orc` must have been run with the fp32 value of decay the C ABI receives."""
+    decay = float(np.float32(decay))
     fr_g = gpu["first_reject"]
     N = fr_g.shape[0]
     rows = np.arange(N) if blk_index is None else blk_index
@@ -146,8 +157,8 @@ def compare_vat(gpu, orc, k, decay, greedy, blk_index=None):
     if greedy:
         assert np.array_equal(pg.astype(np.float64), po)
     else:
-        _assert_close("p(x)", pg[..., 0], po[..., 0])
-        _assert_close("q(x)", pg[..., 1], po[..., 1])
+        _assert_close("p(x)", pg[..., 0], po[..., 0], atol=FLT_MIN)
+        _assert_close("q(x)", pg[..., 1], po[..., 1], atol=FLT_MIN)
     amb = 0
     i = np.arange(k)
     for j, n in enumerate(rows):
@@ -159,7 +170,7 @@ def compare_vat(gpu, orc, k, decay, greedy, blk_index=None):
         # labels and weights follow the GPU's own r exactly (closed form)
         assert np.array_equal(gpu["accept_mask"][j], (i < rg).astype(np.uint8)), n
         want_w = np.where(i < rg, 1.0, np.power(float(decay), np.maximum(i - rg, 0).astype(np.float64)))
-        _assert_close("weights", gpu["weights"][j], want_w, rtol=2e-7, atol=0.0)
+        _assert_close("weights", gpu["weights"][j], want_w, rtol=1e-7, atol=0.0)
         tested = range(min(ro + 1, k))
         a = [p for p in tested if abs(orc.accept_margin[n, p]) < BAND]
         if a and not greedy:
@@ -167,6 +178,6 @@ def compare_vat(gpu, orc, k, decay, greedy, blk_index=None):
             assert rg >= a[0]
             continue
         assert rg == ro, ("first_reject", int(n), rg, ro)
-        _assert_close("weights vs oracle", gpu["weights"][j], orc.weights[n], rtol=2e-7)
+        _assert_close("weights vs oracle", gpu["weights"][j], orc.weights[n], rtol=1e-7)
         assert np.array_equal(gpu["accept_mask"][j], orc.accept_mask[n])
     return {"blocks": len(rows), "ambiguous_accept": amb}
