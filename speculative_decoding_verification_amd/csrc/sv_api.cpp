@@ -1,6 +1,8 @@
 // C ABI of libspecverify: host-side argument checks, workspace planning and
 // dispatch to the gfx950 kernels.  Every check runs before anything is
 // enqueued, so an error return leaves all outputs and the workspace untouched.
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -22,6 +24,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool temperature_ok(float t) { return t == 0.f || (std::isfinite(t) && t >= kMinTemperature); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tag of this call's hand-off words (see kTagFirst): consecutive calls get
+// consecutive tags, so words left by an earlier call never match.
+uint32_t next_tag() {
+    static std::atomic<uint32_t> calls{0};
+    return kTagFirst + calls.fetch_add(1u, std::memory_order_relaxed) % kTagCount;
+}
 
 struct Shape {
     int64_t batch, k, vocab;
@@ -69,6 +78,11 @@ void fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
     pl->target_rows_per_seq = static_cast<int32_t>(s.target_rows_per_seq);
     pl->chunks = static_cast<int32_t>(s.chunks);
     pl->chunk = static_cast<int32_t>(s.chunk);
+    pl->rows_per_seq = static_cast<int32_t>(s.target_rows_per_seq + (s.rows_d ? s.k : 0));
+    pl->wg_per_seq_a = static_cast<int32_t>(ceil_div(static_cast<int64_t>(pl->rows_per_seq) * s.chunks, kWavesPerBlock));
+    pl->wg_per_seq_b = static_cast<int32_t>(ceil_div(s.chunks, kWavesPerBlock));
+    pl->lag_a = static_cast<int32_t>(std::min<int64_t>(s.batch, ceil_div(kResidentBlocks, pl->wg_per_seq_a)));
+    pl->lag_b = static_cast<int32_t>(std::min<int64_t>(s.batch, ceil_div(kResidentBlocks, pl->wg_per_seq_b)));
     pl->rows_t = s.rows_t;
     pl->rows_d = s.rows_d;
     pl->greedy = s.greedy;
@@ -82,10 +96,11 @@ void fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
 void carve_workspace(const Shape& s, void* ws, Plan* pl) {
     const WorkspaceLayout L = workspace_layout(s.rows_t + s.rows_d, s.batch, s.chunks);
     char* base = static_cast<char*>(ws);
-    pl->partials = reinterpret_cast<float2*>(base + L.partials);
+    pl->partials = reinterpret_cast<uint64_t*>(base + L.partials);
+    pl->resid = reinterpret_cast<uint64_t*>(base + L.resid);
     pl->row_mz = reinterpret_cast<float2*>(base + L.row_mz);
-    pl->seq = reinterpret_cast<SeqState*>(base + L.seq);
-    pl->resid = reinterpret_cast<float*>(base + L.resid);
+    pl->jobs = reinterpret_cast<ResidJob*>(base + L.jobs);
+    pl->tag = next_tag();
 }
 
 }  // namespace
@@ -94,13 +109,13 @@ WorkspaceLayout workspace_layout(int64_t rows, int64_t batch, int64_t chunks) {
     WorkspaceLayout L;
     size_t off = 0;
     L.partials = off;
-    off = align_up(off + static_cast<size_t>(rows * chunks) * sizeof(float2));
+    off = align_up(off + static_cast<size_t>(rows * chunks) * 2 * sizeof(uint64_t));
+    L.resid = off;
+    off = align_up(off + static_cast<size_t>(batch * chunks) * sizeof(uint64_t));
     L.row_mz = off;
     off = align_up(off + static_cast<size_t>(rows) * sizeof(float2));
-    L.seq = off;
-    off = align_up(off + static_cast<size_t>(batch) * sizeof(SeqState));
-    L.resid = off;
-    off = align_up(off + static_cast<size_t>(batch * chunks) * sizeof(float));
+    L.jobs = off;
+    off = align_up(off + static_cast<size_t>(batch) * sizeof(ResidJob));
     L.total = off;
     return L;
 }

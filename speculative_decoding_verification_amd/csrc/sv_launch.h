@@ -28,16 +28,21 @@ enum SampleMode : int32_t {
     kModeResidual = 3  // draft logits rejected at r: draw from max(0, p_r - q_r)
 };
 
-struct SeqState {
-    int32_t r;     // first rejection (k if none), -1 invalid
+// What the finisher of a sequence leaves for the residual kernel.
+struct ResidJob {
+    int32_t r;     // first rejection (k if none), -1 invalid, -2 timed out
     int32_t mode;  // SampleMode
-    int32_t x_r;   // draft token at r (one-hot exclusion)
+    float u;       // the uniform of the draw
     int32_t pad;
+    float2 mzt;    // (max, Z) of target row r
+    float2 mzd;    // (max, Z) of draft row r
 };
 
-// Everything the kernels of one call need.  Row numbering: target rows
-// 0 .. rows_t-1 (sequence b, position i -> b*target_rows_per_seq + i), then
-// draft rows rows_t .. rows_t+rows_d-1 (b, i -> rows_t + b*k + i).
+// Everything the kernels of one call need.  Global row numbering (row_mz,
+// row_stats_out): target rows 0 .. rows_t-1 (sequence b, position i ->
+// b*target_rows_per_seq + i), then draft rows rows_t .. rows_t+rows_d-1
+// (b, i -> rows_t + b*k + i).  Within a sequence, local row j < n_t is target
+// position j and j >= n_t is draft position j - n_t.
 struct Plan {
     int32_t batch;            // B (verify) or N (VAT)
     int32_t k;
@@ -46,6 +51,12 @@ struct Plan {
     int32_t target_rows_per_seq;  // k+1 (verify) or k (VAT)
     int32_t chunks;           // P = ceil(V / chunk)
     int32_t chunk;            // elements per chunk
+    int32_t rows_per_seq;     // R_s = target_rows_per_seq + (k if draft logits are read)
+    int32_t wg_per_seq_a;     // worker blocks per sequence of the streaming kernel
+    int32_t wg_per_seq_b;     // worker blocks per sequence of the residual kernel
+    int32_t lag_a;            // finisher of sequence b follows the workers of sequence b + lag
+    int32_t lag_b;
+    uint32_t tag;             // this call's tag of hand-off words
     int64_t rows_t;
     int64_t rows_d;           // 0 for one-hot drafts and T == 0
     bool vec;                 // 16-byte loads allowed (aligned rows)
@@ -70,14 +81,31 @@ struct Plan {
     float* row_stats_out;
 
     // workspace regions
-    float2* partials;         // [rows][P]
-    float2* row_mz;           // [rows]
-    SeqState* seq;            // [B]
-    float* resid;             // [B][P]
+    uint64_t* partials;       // [B][R_s][P][2] tagged words (m, s) or (max, index)
+    uint64_t* resid;          // [B][P] tagged residual masses
+    float2* row_mz;           // [rows] (max, Z) or (max, argmax)
+    ResidJob* jobs;           // [B]
 };
 
+// Blocks the GPU keeps resident at once (256 CUs x ~5 workgroups of 256
+// threads): the lag, in blocks, between a sequence's worker blocks and its
+// finisher block.
+constexpr int64_t kResidentBlocks = 1280;
+
+// Values handed between blocks inside a kernel travel as 64-bit words: 32
+// data bits and a 32-bit tag that is unique to the call.  Tags are
+// signalling-NaN bit patterns (0x7f800001 .. 0x7fbfffff); data words never
+// hold one (NaN data is written as the canonical quiet NaN, and integers are
+// below 2^24).  A reader polls until every word it needs carries its call's
+// tag, so no slot ever needs clearing.
+constexpr uint32_t kTagFirst = 0x7f800001u;
+constexpr uint32_t kTagCount = 0x3fffffu;
+
+// Staging capacity of a finisher block in LDS: 32-bit words of partials.
+constexpr int kStageWords = 4096;
+
 struct WorkspaceLayout {
-    size_t partials, row_mz, seq, resid, total;
+    size_t partials, resid, row_mz, jobs, total;
 };
 
 WorkspaceLayout workspace_layout(int64_t rows, int64_t batch, int64_t chunks);
