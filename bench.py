@@ -2,21 +2,31 @@
 
     python bench.py [--steps K] [--warmup W] [--workload selfdraft] [--gpus 1]
 
-One step = one sv_verify call (every kernel of the path) over one batch of
-synthetic logits already resident in HBM.  The default workload is the
+One step = one sv_verify call (sv_vat_labels for --workload vat) over one
+batch of synthetic logits already resident in HBM; the call is the whole path
+(one launch of the task-grid kernel k_verify).  The default workload is the
 quantized-self-drafter batch: B=128 sequences, k=5 draft positions,
 V=151936, bf16 target and draft logits, T=1.  Prints ONE JSON line.
 
   value        verified draft positions per second = B*k*K / wall time of K
-               steps (synchronised on both sides)
-  roofline     the row-statistics kernel (the one that streams every logit):
-               algorithmic bytes per launch / its mean duration, measured live
-               with HIP events recorded on the launch stream around each launch
+               steps (synchronised on both sides); VAT: labelled positions
+  roofline     k_verify: algorithmic bytes per launch (every logit the path
+               needs, read once) / its mean duration, measured live with HIP
+               events recorded on the launch stream around each launch;
+               `traffic` = HBM bytes per launch from committed rocprofv3
+               FETCH_SIZE/WRITE_SIZE counters when they were taken on the
+               current kernel source, else null
   cpu_baseline the fp64 oracle on a bounded sample of the same workload on
                the host (single thread)
 
 Inputs rotate through enough copies that each timed sweep touches more than
 twice the 256 MB last-level (MALL) cache, so the figures are HBM figures.
+
+    python bench.py --copy-probe [--steps K]
+
+runs K plain device-to-device copies of 1 GiB (torch's copy kernel) and
+nothing else: the known-size reference that scales rocprofv3's FETCH_SIZE and
+WRITE_SIZE counters to bytes.
 """
 from __future__ import annotations
 
@@ -91,27 +101,65 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, wl, seconds: float):
-    """The oracle as it is (plain fp64 C, one thread) over whole sequences of
-    the same workload until `seconds` of CPU work have elapsed."""
+def cpu_baseline(cfg, seconds: float):
+    """The oracle as it is (plain fp64 C, one thread) over whole sequences (VAT:
+    blocks) of the same workload until `seconds` of CPU work have elapsed; the
+    sample is drawn on the host by the same seeded generator."""
     import oracle
+    import workloads
 
+    n_sample = min(cfg.B, 32 if cfg.kind == "verify" else 4)
+    wl = workloads.generate(cfg, 0, n_sample)
     done = 0
     t0 = time.perf_counter()
-    step = 4
+    step = 4 if cfg.kind == "verify" else 1
     while True:
-        lo = done % wl.n
-        hi = min(wl.n, lo + step)
+        lo = done % n_sample
+        hi = min(n_sample, lo + step)
         d = wl.draft[lo:hi] if wl.draft is not None else None
-        oracle.verify(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, onehot=cfg.onehot)
+        if cfg.kind == "vat":
+            oracle.vat_labels(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, cfg.decay)
+        else:
+            oracle.verify(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, onehot=cfg.onehot)
         done += hi - lo
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    what = "blocks" if cfg.kind == "vat" else "sequences"
     return {"value": done * cfg.k / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": "%d whole sequences (%d positions) of the %s workload, fp64 C oracle, 1 thread, %.1f s"
-                      % (done, done * cfg.k, cfg.name, dt),
+            "sample": "%d whole %s (%d positions; cycling over the first %d) of the %s workload, fp64 C oracle, "
+                      "1 thread, %.1f s" % (done, what, done * cfg.k, n_sample, cfg.name, dt),
             "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+
+
+def copy_probe(steps: int) -> int:
+    import torch
+
+    dev = torch.device("cuda:0")
+    n = 2**30 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": steps + 1,
+                      "us_per_copy": dt * 1e6, "gbps_read_plus_write": 2 * n * 4 / dt / 1e9}), flush=True)
+    return 0
+
+
+def _launchers(cfg, sets, probes, sv, n_launch):
+    out = []
+    for i in range(n_launch):
+        t, d, x, u = sets[i % len(sets)]
+        if cfg.kind == "vat":
+            out.append(sv.VatLabeler(t, d, x, u, cfg.T, cfg.decay, probe=probes[i]))
+        else:
+            out.append(sv.Verifier(t, d, x, u, cfg.T, onehot=cfg.onehot, probe=probes[i]))
+    return out
 
 
 def main(argv=None):
@@ -120,9 +168,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="selfdraft",
-                    choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "tiny"])
+                    choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -132,37 +181,44 @@ def main(argv=None):
 
     import torch
 
-    import speculative_decoding_verification_amd as sv
-    import workloads
-
     if not torch.cuda.is_available():
         print("bench.py: no HIP device", file=sys.stderr)
         return 1
+    if args.copy_probe:
+        return copy_probe(args.steps)
+
+    import speculative_decoding_verification_amd as sv
+    import workloads
+
     dev = torch.device("cuda:0")
     cfg = workloads.get_config(args.workload)
     print("bench: generating %s (B=%d k=%d V=%d %s T=%g)" % (cfg.name, cfg.B, cfg.k, cfg.V, cfg.dtype, cfg.T),
           file=sys.stderr, flush=True)
-    wl = workloads.generate(cfg)
     in_bytes = cfg.algorithmic_bytes()
     copies = max(1, math.ceil(2 * MALL_BYTES / in_bytes))
-    sets = [workloads.to_device(wl, dev) for _ in range(copies)]
+    if cfg.kind == "vat":
+        # 33.6 GB: drawn on the device (same distributions, torch's generator)
+        sets = [workloads.generate_on_device(cfg, dev)]
+        for _ in range(copies - 1):
+            sets.append(tuple(a.clone() for a in sets[0]))
+    else:
+        wl = workloads.generate(cfg)
+        sets = [workloads.to_device(wl, dev) for _ in range(copies)]
+        del wl
     ev = HipEvents()
     n_launch = args.warmup + args.steps
     probes = [(ev.create(), ev.create()) for _ in range(n_launch)]
-    verifiers = []
-    for i in range(n_launch):
-        t, d, x, u = sets[i % copies]
-        verifiers.append(sv.Verifier(t, d, x, u, cfg.T, onehot=cfg.onehot, probe=probes[i]))
+    calls = _launchers(cfg, sets, probes, sv, n_launch)
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     print("bench: %d copies of %.1f MB, %d warmup + %d timed steps" % (copies, in_bytes / 1e6, args.warmup,
                                                                         args.steps), file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        verifiers[i](stream)
+        calls[i](stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, n_launch):
-        verifiers[i](stream)
+        calls[i](stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -172,12 +228,19 @@ def main(argv=None):
     ms_per_step = elapsed * 1e3 / args.steps
     positions = cfg.positions() * args.steps
     value = positions / elapsed
-    kernel = "k_row_argmax" if cfg.T == 0.0 else "k_row_stats"
+    kernel = "k_verify"
     achieved = in_bytes / (k1_mean * 1e-3) / 1e9
-    acc = verifiers[-1].accepted_len.float().mean().item()
+    last = calls[-1]
+    if cfg.kind == "vat":
+        fr = last.first_reject.float()
+        extra = {"mean_first_reject": fr.mean().item(), "timeouts": int((fr == -2).sum().item())}
+    else:
+        acc = last.accepted_len.float()
+        extra = {"mean_accepted_len": acc.mean().item(), "timeouts": int((acc == -2).sum().item())}
     for a, b in probes:
         ev.destroy(a)
         ev.destroy(b)
+    del calls, sets
 
     res = {
         "metric": METRIC,
@@ -190,7 +253,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
                    "logits": cfg.dtype, "temperature": cfg.T, "draft": "one-hot" if cfg.onehot else "logits",
@@ -201,11 +264,13 @@ def main(argv=None):
                      "traffic": measured_traffic(kernel, cfg.name),
                      "algorithmic_bytes_per_launch": in_bytes, "mean_launch_us": k1_mean * 1e3,
                      "median_launch_us": k1_ms[len(k1_ms) // 2] * 1e3},
-        "mean_accepted_len": acc,
     }
+    res.update(extra)
+    if cfg.kind == "vat":
+        res["config"]["decay"] = cfg.decay
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
 

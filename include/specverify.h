@@ -52,6 +52,12 @@
  *    on any error nothing is launched and no output or workspace byte is
  *    touched.  A failed launch returns SV_ERR_HIP (a workspace used by a call
  *    that returned SV_ERR_HIP must be zero-filled again before reuse).
+ *  - Inside one call, blocks hand partial results to later blocks of the same
+ *    grid through the workspace and wait for them with a bounded poll (about
+ *    one second).  If a wait runs out (it cannot while the device dispatches
+ *    blocks in grid order, as gfx950 does), the sequence (block) is reported
+ *    with accepted_len = -2 / first_reject = -2, out_tokens -1, mask 0 and
+ *    weights 0; the kernel still ends normally.
  *  - Data checks done on the device: a sequence (block) holding a draft token
  *    outside [0, V) is flagged (accepted_len = -1 / first_reject = -1, its
  *    out_tokens -1, mask 0, weights 0) and never indexes memory with that
@@ -59,7 +65,10 @@
  *    give unspecified (but in-bounds) results.
  *  - Workspace: query its size, allocate it on the device, zero-fill it once
  *    before first use; every call that returns SV_OK leaves it ready for the
- *    next call.  Calls that use the same workspace must not overlap in time.
+ *    next call (each call tags what it writes with a fresh 32-bit call
+ *    number, so nothing needs clearing; the numbers repeat only after 2^32 - 1
+ *    calls in one process).  Calls that use the same workspace must not
+ *    overlap in time.
  *  - Determinism: results are bitwise reproducible for identical inputs (no
  *    floating-point atomics; fixed reduction orders).
  */
@@ -144,7 +153,8 @@ sv_status sv_verify_workspace_size(const sv_verify_desc* desc, size_t* bytes);
  *  uniforms       device, [B][k+1] float32 in [0,1): column i < k drives test i,
  *                 column k the single residual / bonus draw; unused (may be
  *                 NULL) at T == 0
- *  accepted_len   device out, [B] int32 in [0, k] (-1: invalid token)
+ *  accepted_len   device out, [B] int32 in [0, k] (-1: invalid token, -2: wait
+ *                 timed out)
  *  out_tokens     device out, [B][k+1] int32: x_0..x_{r-1}, then the target's
  *                 token at r, then -1
  *  probs_out      device out or NULL, [B][k][2] float32: (p_i(x_i), q_i(x_i))
@@ -179,7 +189,8 @@ sv_status sv_vat_workspace_size(const sv_vat_desc* desc, size_t* bytes);
  *  draft_tokens   device, [N][k] int32
  *  uniforms       device, [N][k] float32 in [0,1) (unused at T == 0)
  *  accept_mask    device out, [N][k] uint8: 1 before the first rejection, else 0
- *  first_reject   device out, [N] int32: r in [0,k], k = no rejection (-1: invalid token)
+ *  first_reject   device out, [N] int32: r in [0,k], k = no rejection (-1: invalid
+ *                 token, -2: wait timed out)
  *  weights        device out, [N][k] float32: 1 for i < r, decay^(i-r) for i >= r
  *  probs_out      device out or NULL, [N][k][2] float32 (p_i(x_i), q_i(x_i))
  *  row_stats_out  device out or NULL, [N k + N k][2] float32, as for sv_verify

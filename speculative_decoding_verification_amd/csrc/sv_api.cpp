@@ -78,11 +78,29 @@ void fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
     pl->target_rows_per_seq = static_cast<int32_t>(s.target_rows_per_seq);
     pl->chunks = static_cast<int32_t>(s.chunks);
     pl->chunk = static_cast<int32_t>(s.chunk);
-    pl->rows_per_seq = static_cast<int32_t>(s.target_rows_per_seq + (s.rows_d ? s.k : 0));
-    pl->wg_per_seq_a = static_cast<int32_t>(ceil_div(static_cast<int64_t>(pl->rows_per_seq) * s.chunks, kWavesPerBlock));
-    pl->wg_per_seq_b = static_cast<int32_t>(ceil_div(s.chunks, kWavesPerBlock));
-    pl->lag_a = static_cast<int32_t>(std::min<int64_t>(s.batch, ceil_div(kResidentBlocks, pl->wg_per_seq_a)));
-    pl->lag_b = static_cast<int32_t>(std::min<int64_t>(s.batch, ceil_div(kResidentBlocks, pl->wg_per_seq_b)));
+    pl->dec_rows = static_cast<int32_t>(s.k + (s.rows_d ? s.k : 0));
+    pl->has_bonus = !s.vat;
+    pl->has_resid = !s.vat && !s.greedy && !s.onehot;
+    pl->rows_per_seq = pl->dec_rows + (pl->has_bonus ? 1 : 0);
+    pl->nc_dec = kChunksPerWave;
+    pl->nc_res = kChunksPerWaveResid;
+    const int64_t per_block_dec = static_cast<int64_t>(kWavesPerBlock) * pl->nc_dec;
+    const int64_t per_block_res = static_cast<int64_t>(kWavesPerBlock) * pl->nc_res;
+    pl->w_dec = static_cast<int32_t>(ceil_div(static_cast<int64_t>(pl->dec_rows) * s.chunks, per_block_dec));
+    pl->w_res = pl->has_resid ? static_cast<int32_t>(ceil_div(s.chunks, per_block_res)) : 0;
+    pl->w_bonus = pl->has_bonus ? static_cast<int32_t>(ceil_div(s.chunks, per_block_dec)) : 0;
+    // Lags, in groups, chosen so that a finisher is dispatched about when what
+    // it waits for is done: a residency (the lifetime of a worker block) after
+    // its workers; residual workers half a residency after the decision; the
+    // residual finisher half a residency after its workers.
+    const int64_t group_a = pl->w_dec + 1 + (pl->has_resid ? pl->w_res + 1 : 0);
+    const auto lag = [&](int64_t blocks, int64_t group) {
+        return static_cast<int32_t>(std::min<int64_t>(s.batch, ceil_div(blocks, group)));
+    };
+    pl->lag_a = lag(kResidentBlocks, group_a);
+    pl->lag_r = pl->has_resid ? lag(kResidentBlocks / 2, group_a) : 0;
+    pl->lag_f = pl->has_resid ? lag(kResidentBlocks / 2, group_a) : 0;
+    pl->lag_b = pl->has_bonus ? lag(kResidentBlocks, pl->w_bonus + 1) : 0;
     pl->rows_t = s.rows_t;
     pl->rows_d = s.rows_d;
     pl->greedy = s.greedy;
@@ -98,8 +116,7 @@ void carve_workspace(const Shape& s, void* ws, Plan* pl) {
     char* base = static_cast<char*>(ws);
     pl->partials = reinterpret_cast<uint64_t*>(base + L.partials);
     pl->resid = reinterpret_cast<uint64_t*>(base + L.resid);
-    pl->row_mz = reinterpret_cast<float2*>(base + L.row_mz);
-    pl->jobs = reinterpret_cast<ResidJob*>(base + L.jobs);
+    pl->dec = reinterpret_cast<uint64_t*>(base + L.dec);
     pl->tag = next_tag();
 }
 
@@ -112,10 +129,8 @@ WorkspaceLayout workspace_layout(int64_t rows, int64_t batch, int64_t chunks) {
     off = align_up(off + static_cast<size_t>(rows * chunks) * 2 * sizeof(uint64_t));
     L.resid = off;
     off = align_up(off + static_cast<size_t>(batch * chunks) * sizeof(uint64_t));
-    L.row_mz = off;
-    off = align_up(off + static_cast<size_t>(rows) * sizeof(float2));
-    L.jobs = off;
-    off = align_up(off + static_cast<size_t>(batch) * sizeof(ResidJob));
+    L.dec = off;
+    off = align_up(off + static_cast<size_t>(batch) * kDecWords * sizeof(uint64_t));
     L.total = off;
     return L;
 }

@@ -8,24 +8,31 @@
 // 的锚点": the same rule on training blocks, labels and first-rejection-
 // anchored weights).
 //
-// Kernels (one call: k_stream, then k_residual when draft logits are read at
-// T > 0):
-//  k_stream    the HBM-bound pass.  Worker blocks: one wavefront per (row,
-//              8 KiB chunk), sequence-major, 16-byte coalesced loads, the
-//              chunk's max and sum of exp2((l - m) * log2(e)/T) (or, at T == 0,
-//              max and lowest index), wave butterfly reductions, one partial
-//              handed off as tagged words; workers never wait.  Finisher
-//              blocks, one per sequence, sit in the same grid about one
-//              residency behind their sequence's workers, so they run while
-//              later sequences stream: poll and stage the partials in LDS,
-//              combine them into (m, Z) per row, p(x_i) and q(x_i), the test
-//              u*q < p on one lane per position, wave ballot -> first rejection
-//              r, accepted prefix or VAT labels and weights, and the draw
-//              itself when it needs no second pass over the logits (bonus token
-//              from the chunk masses; one-hot residual = p_r without x_r).
-//  k_residual  only for draft logits at T > 0: worker blocks compute the
-//              residual mass max(0, p_r - q_r) of each chunk of a rejected row
-//              pair; the sequence's finisher block draws the token.
+// One call is one launch of k_verify, a grid of 256-thread blocks, each of
+// which decodes its role from its block index (a "task grid").  The roles:
+//  decision worker   one wavefront per (row, 8 KiB chunk) of the k target rows
+//                    and k draft rows of a sequence: non-temporal 16-byte
+//                    coalesced loads, the chunk's max and sum of
+//                    exp2((l - m) * log2(e)/T) (at T == 0: max and lowest
+//                    index), DPP wave reductions, the partial published as
+//                    tagged words.  Workers never wait.
+//  decision finisher per sequence: waits for that sequence's partials, combines
+//                    them into (m, Z) per row, p(x_i), q(x_i), runs the test
+//                    u*q < p on one lane per position, ballot -> first
+//                    rejection r, accepted prefix or VAT labels and weights,
+//                    and the one-hot residual draw (p_r without x_r) inline.
+//  residual worker   draft logits at T > 0 only: residual mass max(0, p_r - q_r)
+//                    of one chunk of the rejected row pair.
+//  residual finisher the residual draw (chunk prefix scan, then one chunk).
+//  bonus worker      streams the target row at position k (the bonus row).
+//  bonus finisher    its statistics and, after full acceptance, the draw.
+// Blocks run in index order within the grid closely enough that each role only
+// ever waits on blocks with smaller indices, and finishers are placed about one
+// residency (a lag, in sequences) behind the workers they wait on, so that
+// they overlap the streaming of later sequences instead of stalling it.  Every
+// wait is bounded (about a second); a sequence whose wait runs out reports -2.
+// Hand-off words carry a per-call tag in their upper half, so the workspace
+// needs no clearing between calls and no fence is ever issued.
 //
 // Draws: block prefix scan over the chunk masses finds the chunk holding the
 // draw, then an LDS block scan of that one chunk finds the token.  No
@@ -100,6 +107,16 @@ struct Chunk {
     static constexpr int kPerThread = kElems / kBlock;                // chunk scan: per thread
 };
 
+// Streaming loads of logits are non-temporal: every logit is read once, and
+// keeping the stream out of the caches' normal replacement measurably raises
+// the read rate on gfx950 (about 6.2 -> 7.0 TB/s for a plain 428 MB read).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Loads chunk [start, start+len) of one row into the lanes of a wavefront.
 // Vector layout: lane l holds vectors l, l+64, ..., l+448 (coalesced 1 KiB per
 // instruction).  Scalar layout (unaligned rows): lane l holds logits l, l+64, ...
@@ -113,14 +130,14 @@ __device__ __forceinline__ void load_chunk(const char* row, int64_t start, int l
         uint4 raw[kVecPerLane];
         if (len == Chunk<EB>::kElems) {
 #pragma unroll
-            for (int j = 0; j < kVecPerLane; ++j) raw[j] = p[j * kWave + lane];
+            for (int j = 0; j < kVecPerLane; ++j) raw[j] = load_stream(p + j * kWave + lane);
         } else {
             const int nvec = len / PV;  // rows are whole vectors on this path
             const uint32_t ni = Elem<EB>::kNegInfWord;
 #pragma unroll
             for (int j = 0; j < kVecPerLane; ++j) {
                 const int idx = j * kWave + lane;
-                raw[j] = idx < nvec ? p[idx] : make_uint4(ni, ni, ni, ni);
+                raw[j] = idx < nvec ? load_stream(p + idx) : make_uint4(ni, ni, ni, ni);
             }
         }
 #pragma unroll
@@ -288,13 +305,6 @@ __device__ __forceinline__ const char* row_of(const Plan& pl, int64_t grow) {
                             : row_base(pl.draft, grow - pl.rows_t, pl.vocab, EB);
 }
 
-// Global row of local row j of sequence b (j < n_t: target position j; else
-// draft position j - n_t).
-__device__ __forceinline__ int64_t global_row(const Plan& pl, int b, int j) {
-    const int n_t = pl.target_rows_per_seq;
-    return j < n_t ? static_cast<int64_t>(b) * n_t + j : pl.rows_t + static_cast<int64_t>(b) * pl.k + (j - n_t);
-}
-
 // ------------------------------------------------------------------ chunk partials
 
 // (m, s) of one chunk: m = max raw logit, s = sum of exp2((l - m) * c2) with
@@ -354,10 +364,6 @@ __device__ __forceinline__ float2 chunk_argmax(const char* rp, int64_t start, in
 // left dirty in an XCD's L2 and workers never wait.  The finisher reads with
 // device-scope atomic loads and polls until every word carries the call's
 // tag; no release/acquire fence (an L2 writeback or invalidate) is needed.
-__device__ __forceinline__ uint32_t canon_nan(uint32_t bits) {
-    return ((bits & 0x7f800000u) == 0x7f800000u && (bits & 0x007fffffu)) ? 0x7fc00000u : bits;
-}
-
 __device__ __forceinline__ void put_word(uint64_t* p, uint32_t data, uint32_t tag) {
     __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | data, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -369,9 +375,9 @@ __device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
 __device__ __forceinline__ uint32_t word_data(uint64_t w) { return static_cast<uint32_t>(w); }
 
 // Chunk partial i of a sequence: words 2i (m or max) and 2i+1 (s or index).
-__device__ __forceinline__ void put_partial(uint64_t* seq_words, int i, float2 v, bool index_in_y, uint32_t tag) {
-    put_word(seq_words + 2 * i, canon_nan(__float_as_uint(v.x)), tag);
-    put_word(seq_words + 2 * i + 1, index_in_y ? __float_as_uint(v.y) : canon_nan(__float_as_uint(v.y)), tag);
+__device__ __forceinline__ void put_partial(uint64_t* seq_words, int i, float2 v, uint32_t tag) {
+    put_word(seq_words + 2 * i, __float_as_uint(v.x), tag);
+    put_word(seq_words + 2 * i + 1, __float_as_uint(v.y), tag);
 }
 
 // A finisher gives up after about a second of polling (the wall clock runs at
@@ -408,48 +414,11 @@ struct PartialSrc {
     }
 };
 
-// Block roles of a grid with W worker blocks per sequence and one finisher
-// block per sequence, the finisher of sequence b placed after the workers of
-// sequence b + L (or at the end).  With blocks dispatched in grid order, all
-// workers a finisher waits for were dispatched before it.
-struct Role {
-    int seq;
-    int worker;  // worker index within the sequence, -1 for the finisher
-};
-
-__device__ __forceinline__ Role decode_role(int64_t blk, int B, int W, int L) {
-    const int64_t head = static_cast<int64_t>(L) * W;
-    Role r;
-    if (blk < head) {
-        r.seq = static_cast<int>(blk / W);
-        r.worker = static_cast<int>(blk - static_cast<int64_t>(r.seq) * W);
-        return r;
-    }
-    const int64_t rel = blk - head;
-    const int64_t mid = static_cast<int64_t>(B - L) * (W + 1);
-    if (rel < mid) {
-        const int g = L + static_cast<int>(rel / (W + 1));
-        const int pos = static_cast<int>(rel - static_cast<int64_t>(g - L) * (W + 1));
-        if (pos < W) {
-            r.seq = g;
-            r.worker = pos;
-        } else {
-            r.seq = g - L;
-            r.worker = -1;
-        }
-        return r;
-    }
-    r.seq = B - L + static_cast<int>(rel - mid);
-    r.worker = -1;
-    return r;
-}
-
 struct TailShared {
     uint32_t stage[kStageWords];   // staged hand-off words
     float2 mz[2 * kMaxDraft + 1];  // (m, Z) or (max, argmax) of the sequence's rows
     float wt[kWavesPerBlock];      // block scan scratch
     float prev_mass;               // running mass before the selected chunk
-    float u_draw;
     int sel;
     int last_pos;
     int r;
@@ -743,9 +712,205 @@ __device__ int draw_token(const DrawRow& d, float u, int P, int64_t V, TailShare
     return draw_scan<EB>(pk, w, sh);
 }
 
-// ------------------------------------------------------------------ sequence tail
+// ------------------------------------------------------------------ task grid
 
-// Outputs of a sequence whose finisher timed out waiting for its workers.
+enum RoleKind : int {
+    kDecWorker = 0,     // streams one chunk of a decision row (rows 0..k-1, draft rows)
+    kDecFinisher = 1,   // per sequence: (m, Z), p(x), q(x), accept test, first rejection
+    kResWorker = 2,     // residual mass of one chunk of the rejected row pair
+    kResFinisher = 3,   // per sequence: the residual draw
+    kBonusWorker = 4,   // streams one chunk of the bonus row (target position k)
+    kBonusFinisher = 5  // per sequence: the bonus row's statistics and draw
+};
+
+struct Role {
+    int kind;
+    int seq;
+    int index;  // worker index within the sequence
+};
+
+__device__ __forceinline__ int64_t clamp_b(int64_t x, int B) { return min(max(x, int64_t{0}), static_cast<int64_t>(B)); }
+
+// First block of group g of phase A / phase B.
+__device__ __forceinline__ int64_t phase_a_start(const Plan& pl, int64_t g) {
+    const int B = pl.batch;
+    int64_t s = pl.w_dec * clamp_b(g, B) + clamp_b(g - pl.lag_a, B);
+    if (pl.has_resid) s += pl.w_res * clamp_b(g - pl.lag_a - pl.lag_r, B) + clamp_b(g - pl.lag_a - pl.lag_r - pl.lag_f, B);
+    return s;
+}
+
+__device__ __forceinline__ int64_t phase_b_start(const Plan& pl, int64_t h) {
+    return pl.w_bonus * clamp_b(h, pl.batch) + clamp_b(h - pl.lag_b, pl.batch);
+}
+
+// Largest group g in [0, G) whose first block is <= blk (group starts strictly
+// increase: no group is empty).
+template <typename F>
+__device__ __forceinline__ int64_t find_group(int64_t blk, int64_t G, F start) {
+    int64_t lo = 0, hi = G - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (start(mid) <= blk) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ Role decode_role(const Plan& pl, int64_t blk) {
+    const int B = pl.batch;
+    Role r;
+    r.index = 0;
+    const int64_t GA = B + pl.lag_a + (pl.has_resid ? pl.lag_r + pl.lag_f : 0);
+    const int64_t TA = phase_a_start(pl, GA);
+    if (blk < TA) {
+        const int64_t g = find_group(blk, GA, [&](int64_t x) { return phase_a_start(pl, x); });
+        int64_t o = blk - phase_a_start(pl, g);
+        if (g < B) {
+            if (o < pl.w_dec) {
+                r.kind = kDecWorker;
+                r.seq = static_cast<int>(g);
+                r.index = static_cast<int>(o);
+                return r;
+            }
+            o -= pl.w_dec;
+        }
+        int64_t s = g - pl.lag_a;
+        if (s >= 0 && s < B) {
+            if (o == 0) {
+                r.kind = kDecFinisher;
+                r.seq = static_cast<int>(s);
+                return r;
+            }
+            o -= 1;
+        }
+        s = g - pl.lag_a - pl.lag_r;
+        if (o < pl.w_res && s >= 0 && s < B) {
+            r.kind = kResWorker;
+            r.seq = static_cast<int>(s);
+            r.index = static_cast<int>(o);
+            return r;
+        }
+        if (s >= 0 && s < B) o -= pl.w_res;
+        r.kind = kResFinisher;
+        r.seq = static_cast<int>(g - pl.lag_a - pl.lag_r - pl.lag_f);
+        return r;
+    }
+    const int64_t bl = blk - TA;
+    const int64_t h = find_group(bl, B + pl.lag_b, [&](int64_t x) { return phase_b_start(pl, x); });
+    const int64_t o = bl - phase_b_start(pl, h);
+    if (h < B && o < pl.w_bonus) {
+        r.kind = kBonusWorker;
+        r.seq = static_cast<int>(h);
+        r.index = static_cast<int>(o);
+        return r;
+    }
+    r.kind = kBonusFinisher;
+    r.seq = static_cast<int>(h - pl.lag_b);
+    return r;
+}
+
+// Global row (the numbering of row_stats_out) of local row j of sequence b.
+__device__ __forceinline__ int64_t global_row(const Plan& pl, int b, int j) {
+    const int k = pl.k;
+    const int n_t = pl.target_rows_per_seq;
+    if (j < k) return static_cast<int64_t>(b) * n_t + j;
+    if (j < pl.dec_rows) return pl.rows_t + static_cast<int64_t>(b) * k + (j - k);
+    return static_cast<int64_t>(b) * n_t + k;
+}
+
+__device__ __forceinline__ uint64_t* seq_words(const Plan& pl, int b) {
+    return pl.partials + static_cast<int64_t>(b) * pl.rows_per_seq * pl.chunks * 2;
+}
+
+// ------------------------------------------------------------------ workers
+
+// Partial of chunk c of local row j of sequence b, handed off as two words.
+template <int EB, bool VEC>
+__device__ __forceinline__ void stream_chunk(const Plan& pl, int b, int j, int c) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const char* rp = row_of<EB>(pl, global_row(pl, b, j));
+    const int64_t start = static_cast<int64_t>(c) * Chunk<EB>::kElems;
+    const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), pl.vocab - start));
+    const float2 part = pl.greedy ? chunk_argmax<EB, VEC>(rp, start, len, lane)
+                                  : chunk_stats<EB, VEC>(rp, start, len, lane, pl.c2);
+    if (lane == 0) put_partial(seq_words(pl, b), j * pl.chunks + c, part, pl.tag);
+}
+
+// Residual mass of chunk [start, start+len) of a target/draft row pair, in
+// the wavefront's chunk layout.  The vector path reads half the chunk at a
+// time and decodes in registers, keeping the kernel's register budget at the
+// streaming pass's.
+template <int EB, bool VEC>
+__device__ __forceinline__ float chunk_resid_mass(const char* rt, const char* rd, int64_t start, int len, int lane,
+                                                  const ResidW& wf) {
+    float s = 0.f;
+    if constexpr (VEC) {
+        constexpr int PV = Elem<EB>::kPerVec;
+        constexpr int kHalf = kVecPerLane / 2;
+        const uint4* pt = reinterpret_cast<const uint4*>(rt + start * EB);
+        const uint4* pd = reinterpret_cast<const uint4*>(rd + start * EB);
+        const int nvec = len / PV;
+        const uint32_t ni = Elem<EB>::kNegInfWord;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint4 at[kHalf], ad[kHalf];
+#pragma unroll
+            for (int j = 0; j < kHalf; ++j) {
+                const int idx = (h * kHalf + j) * kWave + lane;
+                at[j] = idx < nvec ? load_stream(pt + idx) : make_uint4(ni, ni, ni, ni);
+                ad[j] = idx < nvec ? load_stream(pd + idx) : make_uint4(ni, ni, ni, ni);
+            }
+#pragma unroll
+            for (int j = 0; j < kHalf; ++j) {
+                float ft[PV], fd[PV];
+                Elem<EB>::decode(at[j], ft);
+                Elem<EB>::decode(ad[j], fd);
+#pragma unroll
+                for (int e = 0; e < PV; ++e) s += wf(ft[e], fd[e]);
+            }
+        }
+    } else {
+        for (int e = 0; e < Chunk<EB>::kPerLane; ++e) {
+            const int idx = e * kWave + lane;
+            if (idx < len) s += wf(Elem<EB>::at(rt, start + idx), Elem<EB>::at(rd, start + idx));
+        }
+    }
+    return wave_sum(s);
+}
+
+// ------------------------------------------------------------------ decision words
+
+struct Decision {
+    int r;     // first rejection (k if none), -1 invalid, -2 timed out
+    int mode;  // SampleMode
+    float2 mzt, mzd;
+    float u;
+};
+
+__device__ __forceinline__ void put_decision(const Plan& pl, int b, const Decision& d) {
+    uint64_t* w = pl.dec + static_cast<int64_t>(b) * kDecWords;
+    put_word(w + kDecRMode, static_cast<uint32_t>(d.r + 2) | (static_cast<uint32_t>(d.mode) << 16), pl.tag);
+    put_word(w + kDecMt, __float_as_uint(d.mzt.x), pl.tag);
+    put_word(w + kDecZt, __float_as_uint(d.mzt.y), pl.tag);
+    put_word(w + kDecMd, __float_as_uint(d.mzd.x), pl.tag);
+    put_word(w + kDecZd, __float_as_uint(d.mzd.y), pl.tag);
+    put_word(w + kDecU, __float_as_uint(d.u), pl.tag);
+}
+
+// From staged decision words (after collect).
+__device__ __forceinline__ Decision read_decision(const uint32_t* st) {
+    Decision d;
+    d.r = static_cast<int>(st[kDecRMode] & 0xffffu) - 2;
+    d.mode = static_cast<int>(st[kDecRMode] >> 16);
+    d.mzt = make_float2(__uint_as_float(st[kDecMt]), __uint_as_float(st[kDecZt]));
+    d.mzd = make_float2(__uint_as_float(st[kDecMd]), __uint_as_float(st[kDecZd]));
+    d.u = __uint_as_float(st[kDecU]);
+    return d;
+}
+
+// ------------------------------------------------------------------ finishers
+
+// Marks a sequence whose finisher gave up waiting (see kPollTimeoutTicks).
 __device__ void fail_sequence(const Plan& pl, int b) {
     const int k = pl.k;
     for (int j = threadIdx.x; j <= k; j += kBlock) {
@@ -759,15 +924,8 @@ __device__ void fail_sequence(const Plan& pl, int b) {
         }
     }
     if (threadIdx.x == 0) {
-        if (pl.vat) {
-            pl.first_reject[b] = -2;
-        } else {
-            pl.accepted_len[b] = -2;
-            ResidJob job{};
-            job.r = -2;
-            job.mode = kModeDone;
-            pl.jobs[b] = job;
-        }
+        if (pl.vat) pl.first_reject[b] = -2;
+        else pl.accepted_len[b] = -2;
     }
 }
 
@@ -808,28 +966,31 @@ __device__ __forceinline__ float2 combine_row(const PartialSrc& src, int j, int 
     return make_float2(m, s);
 }
 
-// Everything after the streaming pass for sequence b, run by its finisher block.
+__device__ __forceinline__ void write_row_stats(const Plan& pl, int64_t grow, float2 res) {
+    if (!pl.row_stats_out) return;
+    pl.row_stats_out[2 * grow] = pl.greedy ? res.x : res.x / pl.temperature;
+    pl.row_stats_out[2 * grow + 1] = pl.greedy ? static_cast<float>(__float_as_int(res.y)) : res.y;
+}
+
+// Decision finisher of sequence b: everything that needs rows 0..k-1.
 template <int EB, bool VEC>
-__device__ void finish_sequence(const Plan& pl, int b, TailShared& sh) {
-    constexpr int CH = Chunk<EB>::kElems;
-    constexpr int PT = Chunk<EB>::kPerThread;
+__device__ void decide_sequence(const Plan& pl, int b, TailShared& sh) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int k = pl.k;
     const int n_t = pl.target_rows_per_seq;
-    const int R_s = pl.rows_per_seq;
     const int P = pl.chunks;
     const int64_t V = pl.vocab;
     const float c2 = pl.c2;
     const int n_u = pl.vat ? k : k + 1;
-    const int items = R_s * P;
-    const uint64_t* words = pl.partials + static_cast<int64_t>(b) * items * 2;
+    const int dec_items = pl.dec_rows * P;
+    const uint64_t* words = seq_words(pl, b);
     const bool sampling = !pl.vat && !pl.greedy;
 
-    // Loads that do not depend on the partials go out before the polling, all
-    // issued back to back (no branch on a loaded value): one lane per position
-    // loads its token, uniform and the two logits at the token (index clamped
-    // into the row; an invalid token flags the sequence below).
+    // Loads that do not depend on the partials go out before the polling:
+    // one lane per position loads its token and uniform, then the two logits
+    // at the token (index clamped into the row; an invalid token flags the
+    // sequence below).
     const bool active = wave == 0 && lane < k;
     int x = 0;
     float lt = 0.f, ld = 0.f, u = 0.f;
@@ -845,49 +1006,27 @@ __device__ void finish_sequence(const Plan& pl, int b, TailShared& sh) {
     }
     const float u_draw = sampling ? pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k] : 0.f;
 
-    const bool staged = 2 * items <= kStageWords;
-    if (!collect(words, 2 * items, pl.tag, staged ? sh.stage : nullptr)) {
+    const bool staged = 2 * dec_items <= kStageWords;
+    if (!collect(words, 2 * dec_items, pl.tag, staged ? sh.stage : nullptr)) {
         fail_sequence(pl, b);
+        if (!pl.vat && threadIdx.x == 0) {
+            Decision d{};
+            d.r = -2;
+            d.mode = kModeDone;
+            put_decision(pl, b, d);
+        }
         return;
     }
     const PartialSrc src{staged ? sh.stage : nullptr, words};
 
-    // Combine the chunk partials of every row of the sequence.
-    for (int j = wave; j < R_s; j += kWavesPerBlock) {
+    for (int j = wave; j < pl.dec_rows; j += kWavesPerBlock) {
         const float2 res = combine_row(src, j, P, pl.greedy, c2);
         if (lane == 0) {
-            const int64_t grow = global_row(pl, b, j);
             sh.mz[j] = res;
-            pl.row_mz[grow] = res;
-            if (pl.row_stats_out) {
-                pl.row_stats_out[2 * grow] = pl.greedy ? res.x : res.x / pl.temperature;
-                pl.row_stats_out[2 * grow + 1] = pl.greedy ? static_cast<float>(__float_as_int(res.y)) : res.y;
-            }
+            write_row_stats(pl, global_row(pl, b, j), res);
         }
     }
     __syncthreads();
-
-    // The bonus token (drawn from target row k if all k drafts are kept) needs
-    // only row k's partials: pick its chunk now and start loading that chunk,
-    // so the loads overlap the accept decisions below.
-    DrawRow db;
-    DrawPick pb;
-    float lt_b[PT], ld_b[PT];
-    if (sampling) {
-        db.mode = kModeBonus;
-        db.rt = row_base(pl.target, static_cast<int64_t>(b) * n_t + k, V, EB);
-        db.rd = nullptr;
-        db.part = src;
-        db.part_base = k * P;
-        db.rstage = nullptr;
-        db.rwords = nullptr;
-        db.c2 = c2;
-        db.mrow = sh.mz[k].x;
-        db.mt = row_scale(db.mrow, c2, db.corr);
-        db.excl = -1;
-        pb = pick_chunk<EB, VEC>(db, u_draw, P, V, sh);
-        load_runs<EB, VEC>(db, pb.cs, V, lt_b, ld_b);
-    }
 
     if (wave == 0) {
         const int i = lane;
@@ -903,7 +1042,7 @@ __device__ void finish_sequence(const Plan& pl, int b, TailShared& sh) {
                 // The test u*q < p, taken in the log2 domain so that
                 // probabilities below the fp32 range still decide correctly.
                 const float lp = (lt - sh.mz[i].x) * c2 - log2_hw(sh.mz[i].y);
-                const float lq = pl.onehot ? 0.f : (ld - sh.mz[n_t + i].x) * c2 - log2_hw(sh.mz[n_t + i].y);
+                const float lq = pl.onehot ? 0.f : (ld - sh.mz[k + i].x) * c2 - log2_hw(sh.mz[k + i].y);
                 keep = log2_hw(u) + lq < lp;
                 p = exp2_hw(lp);
                 q = exp2_hw(lq);
@@ -918,7 +1057,6 @@ __device__ void finish_sequence(const Plan& pl, int b, TailShared& sh) {
             pl.probs_out[2 * (static_cast<int64_t>(b) * k + i)] = p;
             pl.probs_out[2 * (static_cast<int64_t>(b) * k + i) + 1] = q;
         }
-        int mode = kModeDone;
         if (pl.vat) {
             if (active) {
                 const int64_t o = static_cast<int64_t>(b) * k + i;
@@ -931,44 +1069,38 @@ __device__ void finish_sequence(const Plan& pl, int b, TailShared& sh) {
             }
             if (lane == 0) pl.first_reject[b] = r;
         } else {
+            int mode = kModeDone;
             if (!invalid && !pl.greedy) mode = r == k ? kModeBonus : (pl.onehot ? kModeOneHot : kModeResidual);
-            const int x_r = (r >= 0 && r < k) ? __builtin_amdgcn_readlane(x, r) : -1;
-            const int g_r = (pl.greedy && r >= 0) ? __float_as_int(sh.mz[r].y) : -1;
+            // out[r] belongs to whoever supplies the target's token there:
+            // this block at T == 0 with r < k and for one-hot drafts, the
+            // bonus finisher at r == k, the residual finisher otherwise.
             int32_t* out = pl.out_tokens + static_cast<int64_t>(b) * (k + 1);
             for (int j = lane; j <= k; j += kWave) {
-                int val = -1;
-                if (!invalid) {
-                    if (j < r) val = x;          // j < r <= k <= 64 here, so j == lane
-                    else if (j == r) val = g_r;  // T > 0: the draw overwrites it
-                }
-                out[j] = val;
+                if (invalid) out[j] = -1;
+                else if (j < r) out[j] = x;  // j < r <= k <= 64 here, so j == lane
+                else if (j > r) out[j] = -1;
+                else if (pl.greedy && r < k) out[j] = __float_as_int(sh.mz[r].y);
             }
             if (lane == 0) {
                 pl.accepted_len[b] = r;
-                ResidJob job{};
-                job.r = r;
-                job.mode = mode;
-                if (mode == kModeResidual) {
-                    job.u = u_draw;
-                    job.mzt = sh.mz[r];
-                    job.mzd = sh.mz[n_t + r];
-                }
-                pl.jobs[b] = job;
                 sh.r = r;
-                sh.x_r = x_r;
+                sh.mode = mode;
+                sh.x_r = (r >= 0 && r < k) ? __builtin_amdgcn_readlane(x, r) : -1;
+                Decision d{};
+                d.r = r;
+                d.mode = mode;
+                d.u = u_draw;
+                if (r >= 0 && r < k) {
+                    d.mzt = sh.mz[r];
+                    if (!pl.onehot && !pl.greedy) d.mzd = sh.mz[k + r];
+                }
+                put_decision(pl, b, d);
             }
         }
-        if (lane == 0) sh.mode = mode;
     }
     __syncthreads();
 
-    const int mode = sh.mode;
-    if (mode == kModeBonus) {
-        float w[PT];
-        run_weights<EB>(db, static_cast<int64_t>(pb.cs) * CH, lt_b, ld_b, w);
-        const int y = draw_scan<EB>(pb, w, sh);
-        if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + k] = y;
-    } else if (mode == kModeOneHot) {
+    if (!pl.vat && sh.mode == kModeOneHot) {
         const int r = sh.r;
         DrawRow d;
         d.mode = kModeOneHot;
@@ -987,90 +1119,166 @@ __device__ void finish_sequence(const Plan& pl, int b, TailShared& sh) {
     }
 }
 
-// ------------------------------------------------------------------ kernels
-
+// Residual worker `w` of sequence b: mass of one chunk of max(0, p_r - q_r).
 template <int EB, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_stream(Plan pl) {
-    __shared__ TailShared sh;
-    const Role role = decode_role(blockIdx.x, pl.batch, pl.wg_per_seq_a, pl.lag_a);
-    const int b = role.seq;
-    if (role.worker >= 0) {
-        const int lane = threadIdx.x & (kWave - 1);
-        const int P = pl.chunks;
-        const int items = pl.rows_per_seq * P;
-        const int li = role.worker * kWavesPerBlock + static_cast<int>(threadIdx.x / kWave);
-        if (li >= items) return;
-        const int j = li / P;
-        const int c = li - j * P;
-        const char* rp = row_of<EB>(pl, global_row(pl, b, j));
+__device__ void residual_worker(const Plan& pl, int b, int w, TailShared& sh) {
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage)) return;
+    const Decision dc = read_decision(sh.stage);
+    if (dc.mode != kModeResidual) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int P = pl.chunks;
+    const int64_t V = pl.vocab;
+    const ResidW wf = make_resid_w(dc.mzt, dc.mzd, pl.c2);
+    const char* rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + dc.r, V, EB);
+    const char* rd = row_base(pl.draft, static_cast<int64_t>(b) * pl.k + dc.r, V, EB);
+    const int base = w * kWavesPerBlock * pl.nc_res + static_cast<int>(threadIdx.x / kWave);
+#pragma unroll 1
+    for (int n = 0; n < pl.nc_res; ++n) {
+        const int c = base + n * kWavesPerBlock;
+        if (c >= P) break;
         const int64_t start = static_cast<int64_t>(c) * Chunk<EB>::kElems;
-        const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), pl.vocab - start));
-        const float2 part = pl.greedy ? chunk_argmax<EB, VEC>(rp, start, len, lane)
-                                      : chunk_stats<EB, VEC>(rp, start, len, lane, pl.c2);
-        if (lane == 0) put_partial(pl.partials + static_cast<int64_t>(b) * items * 2, li, part, pl.greedy, pl.tag);
-        return;
+        const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), V - start));
+        const float s = chunk_resid_mass<EB, VEC>(rt, rd, start, len, lane, wf);
+        if (lane == 0) put_word(pl.resid + static_cast<int64_t>(b) * P + c, __float_as_uint(s), pl.tag);
     }
-    finish_sequence<EB, VEC>(pl, b, sh);
 }
 
-// Residual mass of each chunk of a rejected row pair; the sequence's finisher
-// block draws the token.
+// Residual finisher of sequence b: draws the target's token at r < k.
 template <int EB, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_residual(Plan pl) {
-    __shared__ TailShared sh;
-    const Role role = decode_role(blockIdx.x, pl.batch, pl.wg_per_seq_b, pl.lag_b);
-    const int b = role.seq;
-    const ResidJob job = pl.jobs[b];
-    if (job.mode != kModeResidual) return;  // workers and finisher of the sequence agree
+__device__ void residual_finisher(const Plan& pl, int b, TailShared& sh) {
     const int P = pl.chunks;
     const int k = pl.k;
     const int64_t V = pl.vocab;
-    const int64_t trow = static_cast<int64_t>(b) * pl.target_rows_per_seq + job.r;
-    const int64_t drow = static_cast<int64_t>(b) * k + job.r;
-    const ResidW wf = make_resid_w(job.mzt, job.mzd, pl.c2);
     uint64_t* rwords = pl.resid + static_cast<int64_t>(b) * P;
-    if (role.worker >= 0) {
-        const int lane = threadIdx.x & (kWave - 1);
-        const int c = role.worker * kWavesPerBlock + static_cast<int>(threadIdx.x / kWave);
-        if (c >= P) return;
-        const int64_t start = static_cast<int64_t>(c) * Chunk<EB>::kElems;
-        const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), V - start));
-        float vt[Chunk<EB>::kPerLane];
-        float vd[Chunk<EB>::kPerLane];
-        load_chunk<EB, VEC>(row_base(pl.target, trow, V, EB), start, len, lane, vt);
-        load_chunk<EB, VEC>(row_base(pl.draft, drow, V, EB), start, len, lane, vd);
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < Chunk<EB>::kPerLane; ++e) s += wf(vt[e], vd[e]);
-        s = wave_sum(s);
-        if (lane == 0) put_word(rwords + c, canon_nan(__float_as_uint(s)), pl.tag);
+    const bool staged = P + kDecWords <= kStageWords;
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage)) {
+        fail_sequence(pl, b);
         return;
     }
-    const bool staged = P <= kStageWords;
-    if (!collect(rwords, P, pl.tag, staged ? sh.stage : nullptr)) {
+    const Decision dc = read_decision(sh.stage);
+    if (dc.mode != kModeResidual) return;
+    if (!collect(rwords, P, pl.tag, staged ? sh.stage + kDecWords : nullptr)) {
         fail_sequence(pl, b);
         return;
     }
     DrawRow d;
     d.mode = kModeResidual;
-    d.rt = row_base(pl.target, trow, V, EB);
-    d.rd = row_base(pl.draft, drow, V, EB);
-    d.part = PartialSrc{nullptr, pl.partials + static_cast<int64_t>(b) * pl.rows_per_seq * P * 2};
-    d.part_base = job.r * P;
-    d.rstage = staged ? sh.stage : nullptr;
+    d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + dc.r, V, EB);
+    d.rd = row_base(pl.draft, static_cast<int64_t>(b) * k + dc.r, V, EB);
+    d.part = PartialSrc{nullptr, seq_words(pl, b)};
+    d.part_base = dc.r * P;
+    d.rstage = staged ? sh.stage + kDecWords : nullptr;
     d.rwords = rwords;
     d.c2 = pl.c2;
-    d.mrow = job.mzt.x;
-    d.mt = row_scale(job.mzt.x, pl.c2, d.corr);
+    d.mrow = dc.mzt.x;
+    d.mt = row_scale(dc.mzt.x, pl.c2, d.corr);
     d.excl = -1;
-    d.rw = wf;
+    d.rw = make_resid_w(dc.mzt, dc.mzd, pl.c2);
     // A residual that rounds to zero mass (only possible through rounding,
     // since a rejection has probability TV(p, q)): draw from p_r instead.
     float zsum = 0.f;
     for (int cc = threadIdx.x; cc < P; cc += kBlock) zsum += chunk_mass(d, cc, -1, 0.f);
     if (!__syncthreads_or(zsum > 0.f)) d.mode = kModeBonus;
-    const int y = draw_token<EB, VEC>(d, job.u, P, V, sh);
-    if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + job.r] = y;
+    const int y = draw_token<EB, VEC>(d, dc.u, P, V, sh);
+    if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + dc.r] = y;
+}
+
+// Bonus finisher of sequence b: statistics of target row k and, when all k
+// drafts were kept, the token drawn from it (its argmax at T == 0).
+template <int EB, bool VEC>
+__device__ void bonus_finisher(const Plan& pl, int b, TailShared& sh) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int k = pl.k;
+    const int P = pl.chunks;
+    const int64_t V = pl.vocab;
+    const float c2 = pl.c2;
+    const uint64_t* words = seq_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * P * 2;
+    const bool staged = 2 * P + kDecWords <= kStageWords;
+    // The decision words and the bonus row's partials are polled together.
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage) ||
+        !collect(words, 2 * P, pl.tag, staged ? sh.stage + kDecWords : nullptr)) {
+        fail_sequence(pl, b);
+        return;
+    }
+    const Decision dc = read_decision(sh.stage);
+    const PartialSrc src{staged ? sh.stage + kDecWords : nullptr, words};
+    if (threadIdx.x < kWave) {
+        const float2 res = combine_row(src, 0, P, pl.greedy, c2);
+        if (lane == 0) {
+            sh.mz[0] = res;
+            write_row_stats(pl, global_row(pl, b, pl.dec_rows), res);
+        }
+    }
+    __syncthreads();
+    if (dc.r != k) return;
+    if (pl.greedy) {
+        if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + k] = __float_as_int(sh.mz[0].y);
+        return;
+    }
+    DrawRow d;
+    d.mode = kModeBonus;
+    d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + k, V, EB);
+    d.rd = nullptr;
+    d.part = src;
+    d.part_base = 0;
+    d.rstage = nullptr;
+    d.rwords = nullptr;
+    d.c2 = c2;
+    d.mrow = sh.mz[0].x;
+    d.mt = row_scale(d.mrow, c2, d.corr);
+    d.excl = -1;
+    const int y = draw_token<EB, VEC>(d, dc.u, P, V, sh);
+    if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + k] = y;
+}
+
+// ------------------------------------------------------------------ kernel
+
+// Five resident blocks per CU (five waves per SIMD): the register budget the
+// streaming loop is written for (at most 102 VGPRs).
+constexpr int kMinBlocksPerCU = 5;
+
+template <int EB, bool VEC>
+__global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
+    __shared__ TailShared sh;
+    const Role role = decode_role(pl, blockIdx.x);
+    const int b = role.seq;
+    switch (role.kind) {
+        case kDecWorker: {
+            // Step n: the block's waves take items base + n*4 + wave (32 KiB
+            // of contiguous logits per step when the items share a row).
+            const int items = pl.dec_rows * pl.chunks;
+            const int base = role.index * kWavesPerBlock * pl.nc_dec + static_cast<int>(threadIdx.x / kWave);
+#pragma unroll 1
+            for (int n = 0; n < pl.nc_dec; ++n) {
+                const int li = base + n * kWavesPerBlock;
+                if (li >= items) break;
+                stream_chunk<EB, VEC>(pl, b, li / pl.chunks, li % pl.chunks);
+            }
+            return;
+        }
+        case kBonusWorker: {
+            const int base = role.index * kWavesPerBlock * pl.nc_dec + static_cast<int>(threadIdx.x / kWave);
+#pragma unroll 1
+            for (int n = 0; n < pl.nc_dec; ++n) {
+                const int c = base + n * kWavesPerBlock;
+                if (c >= pl.chunks) break;
+                stream_chunk<EB, VEC>(pl, b, pl.dec_rows, c);
+            }
+            return;
+        }
+        case kDecFinisher:
+            decide_sequence<EB, VEC>(pl, b, sh);
+            return;
+        case kResWorker:
+            residual_worker<EB, VEC>(pl, b, role.index, sh);
+            return;
+        case kResFinisher:
+            residual_finisher<EB, VEC>(pl, b, sh);
+            return;
+        default:
+            bonus_finisher<EB, VEC>(pl, b, sh);
+            return;
+    }
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -1082,21 +1290,25 @@ hipError_t launch_typed(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipE
         e = hipEventRecord(ev0, stream);
         if (e != hipSuccess) return e;
     }
-    const unsigned grid_a = static_cast<unsigned>(static_cast<int64_t>(pl.batch) * (pl.wg_per_seq_a + 1));
-    hipLaunchKernelGGL((k_stream<EB, VEC>), dim3(grid_a), dim3(kBlock), 0, stream, pl);
+    hipLaunchKernelGGL((k_verify<EB, VEC>), dim3(static_cast<unsigned>(grid_blocks(pl))), dim3(kBlock), 0, stream, pl);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev0 && ev1) {
         e = hipEventRecord(ev1, stream);
         if (e != hipSuccess) return e;
     }
-    if (pl.vat || pl.greedy || pl.onehot) return hipSuccess;
-    const unsigned grid_b = static_cast<unsigned>(static_cast<int64_t>(pl.batch) * (pl.wg_per_seq_b + 1));
-    hipLaunchKernelGGL((k_residual<EB, VEC>), dim3(grid_b), dim3(kBlock), 0, stream, pl);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace
+
+int64_t grid_blocks(const Plan& pl) {
+    const int64_t B = pl.batch;
+    int64_t n = B * (pl.w_dec + 1);
+    if (pl.has_resid) n += B * (pl.w_res + 1);
+    if (pl.has_bonus) n += B * (pl.w_bonus + 1);
+    return n;
+}
 
 hipError_t launch_path(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (pl.batch == 0) return hipSuccess;

@@ -28,14 +28,16 @@ enum SampleMode : int32_t {
     kModeResidual = 3  // draft logits rejected at r: draw from max(0, p_r - q_r)
 };
 
-// What the finisher of a sequence leaves for the residual kernel.
-struct ResidJob {
-    int32_t r;     // first rejection (k if none), -1 invalid, -2 timed out
-    int32_t mode;  // SampleMode
-    float u;       // the uniform of the draw
-    int32_t pad;
-    float2 mzt;    // (max, Z) of target row r
-    float2 mzd;    // (max, Z) of draft row r
+// Tagged words the decision finisher of a sequence leaves for the residual
+// and bonus roles (see kTagFirst).
+enum DecisionWord : int32_t {
+    kDecRMode = 0,  // (r + 2) | mode << 16; r = -1 invalid token, -2 timed out
+    kDecMt = 1,     // max of target row r (residual)
+    kDecZt = 2,     // Z of target row r
+    kDecMd = 3,     // max of draft row r
+    kDecZd = 4,     // Z of draft row r
+    kDecU = 5,      // the uniform of the draw
+    kDecWords = 8
 };
 
 // Everything the kernels of one call need.  Global row numbering (row_mz,
@@ -51,11 +53,20 @@ struct Plan {
     int32_t target_rows_per_seq;  // k+1 (verify) or k (VAT)
     int32_t chunks;           // P = ceil(V / chunk)
     int32_t chunk;            // elements per chunk
-    int32_t rows_per_seq;     // R_s = target_rows_per_seq + (k if draft logits are read)
-    int32_t wg_per_seq_a;     // worker blocks per sequence of the streaming kernel
-    int32_t wg_per_seq_b;     // worker blocks per sequence of the residual kernel
-    int32_t lag_a;            // finisher of sequence b follows the workers of sequence b + lag
-    int32_t lag_b;
+    // Per sequence, the chunk partials hold local rows: target positions
+    // 0..k-1, then draft positions 0..k-1 (when draft logits are read), then
+    // the bonus row (target position k, verification only).
+    int32_t dec_rows;         // rows the decision reads: k or 2k
+    int32_t rows_per_seq;     // dec_rows + (1 if there is a bonus row)
+    bool has_resid;           // draft logits at T > 0: residual roles exist
+    bool has_bonus;           // verification (not VAT): bonus roles exist
+    // Task grid: phase A groups (decision workers, decision finisher of the
+    // sequence LA groups back, residual workers LA+LR back, residual finisher
+    // LA+LR+LF back), then phase B groups (bonus workers, bonus finisher LB
+    // back).  Every block depends only on blocks before it in the grid.
+    int32_t w_dec, w_res, w_bonus;  // worker blocks per sequence of each kind
+    int32_t nc_dec, nc_res;         // chunks per worker wavefront
+    int32_t lag_a, lag_r, lag_f, lag_b;
     uint32_t tag;             // this call's tag of hand-off words
     int64_t rows_t;
     int64_t rows_d;           // 0 for one-hot drafts and T == 0
@@ -83,8 +94,7 @@ struct Plan {
     // workspace regions
     uint64_t* partials;       // [B][R_s][P][2] tagged words (m, s) or (max, index)
     uint64_t* resid;          // [B][P] tagged residual masses
-    float2* row_mz;           // [rows] (max, Z) or (max, argmax)
-    ResidJob* jobs;           // [B]
+    uint64_t* dec;            // [B][kDecWords] tagged decision words
 };
 
 // Blocks the GPU keeps resident at once (256 CUs x ~5 workgroups of 256
@@ -92,23 +102,31 @@ struct Plan {
 // finisher block.
 constexpr int64_t kResidentBlocks = 1280;
 
-// Values handed between blocks inside a kernel travel as 64-bit words: 32
-// data bits and a 32-bit tag that is unique to the call.  Tags are
-// signalling-NaN bit patterns (0x7f800001 .. 0x7fbfffff); data words never
-// hold one (NaN data is written as the canonical quiet NaN, and integers are
-// below 2^24).  A reader polls until every word it needs carries its call's
-// tag, so no slot ever needs clearing.
-constexpr uint32_t kTagFirst = 0x7f800001u;
-constexpr uint32_t kTagCount = 0x3fffffu;
+// Chunks each worker wavefront streams (one after the other): fewer, longer
+// lived blocks.  Block dispatch, not HBM, bounds a grid of short blocks (the
+// dispatcher issues on the order of 150-200 blocks per microsecond).
+constexpr int kChunksPerWave = 4;       // decision and bonus rows
+constexpr int kChunksPerWaveResid = 2;  // residual row pairs (two rows per chunk)
+
+// Values handed between blocks inside a kernel travel as 64-bit words,
+// written and read whole (single-copy atomic): 32 data bits and a 32-bit tag
+// that names the call.  Tags run 1 .. 2^32 - 1 over the calls a process makes;
+// a zero-filled slot matches none.  A reader polls until every word it needs
+// carries its call's tag, so no slot needs clearing between calls.
+constexpr uint32_t kTagFirst = 1u;
+constexpr uint32_t kTagCount = 0xffffffffu;
 
 // Staging capacity of a finisher block in LDS: 32-bit words of partials.
 constexpr int kStageWords = 4096;
 
 struct WorkspaceLayout {
-    size_t partials, resid, row_mz, jobs, total;
+    size_t partials, resid, dec, total;
 };
 
 WorkspaceLayout workspace_layout(int64_t rows, int64_t batch, int64_t chunks);
+
+// Blocks of the task grid.
+int64_t grid_blocks(const Plan& plan);
 
 // Enqueue the whole path on `stream`.  Returns hipSuccess or the first error.
 hipError_t launch_path(const Plan& plan, hipStream_t stream, hipEvent_t probe_start, hipEvent_t probe_stop);
