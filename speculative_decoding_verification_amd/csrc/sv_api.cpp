@@ -70,7 +70,7 @@ size_t workspace_bytes_for(const Shape& s) {
     return workspace_layout(s.rows_t + s.rows_d, s.batch, s.chunks).total;
 }
 
-void fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
+bool fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
     pl->batch = static_cast<int32_t>(s.batch);
     pl->k = static_cast<int32_t>(s.k);
     pl->vocab = static_cast<int32_t>(s.vocab);
@@ -82,25 +82,12 @@ void fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
     pl->has_bonus = !s.vat;
     pl->has_resid = !s.vat && !s.greedy && !s.onehot;
     pl->rows_per_seq = pl->dec_rows + (pl->has_bonus ? 1 : 0);
-    pl->nc_dec = kChunksPerWave;
+    pl->nc_dec = s.batch * pl->dec_rows * s.chunks <= kSmallCallChunks ? kChunksPerWaveSmall : kChunksPerWave;
     pl->nc_res = kChunksPerWaveResid;
-    const int64_t per_block_dec = static_cast<int64_t>(kWavesPerBlock) * pl->nc_dec;
-    const int64_t per_block_res = static_cast<int64_t>(kWavesPerBlock) * pl->nc_res;
-    pl->w_dec = static_cast<int32_t>(ceil_div(static_cast<int64_t>(pl->dec_rows) * s.chunks, per_block_dec));
-    pl->w_res = pl->has_resid ? static_cast<int32_t>(ceil_div(s.chunks, per_block_res)) : 0;
-    pl->w_bonus = pl->has_bonus ? static_cast<int32_t>(ceil_div(s.chunks, per_block_dec)) : 0;
-    // Lags, in groups, chosen so that a finisher is dispatched about when what
-    // it waits for is done: a residency (the lifetime of a worker block) after
-    // its workers; residual workers half a residency after the decision; the
-    // residual finisher half a residency after its workers.
-    const int64_t group_a = pl->w_dec + 1 + (pl->has_resid ? pl->w_res + 1 : 0);
-    const auto lag = [&](int64_t blocks, int64_t group) {
-        return static_cast<int32_t>(std::min<int64_t>(s.batch, ceil_div(blocks, group)));
-    };
-    pl->lag_a = lag(kResidentBlocks, group_a);
-    pl->lag_r = pl->has_resid ? lag(kResidentBlocks / 2, group_a) : 0;
-    pl->lag_f = pl->has_resid ? lag(kResidentBlocks / 2, group_a) : 0;
-    pl->lag_b = pl->has_bonus ? lag(kResidentBlocks, pl->w_bonus + 1) : 0;
+    if (!plan_task_grid(pl->batch, static_cast<int64_t>(pl->dec_rows) * s.chunks, s.chunks, pl->has_resid,
+                        pl->has_bonus, kWavesPerBlock * pl->nc_dec, kWavesPerBlock * pl->nc_res, kResidentBlocks,
+                        &pl->grid))
+        return false;
     pl->rows_t = s.rows_t;
     pl->rows_d = s.rows_d;
     pl->greedy = s.greedy;
@@ -109,6 +96,7 @@ void fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
     pl->temperature = temperature;
     pl->c2 = s.greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
     pl->decay = decay;
+    return true;
 }
 
 void carve_workspace(const Shape& s, void* ws, Plan* pl) {
@@ -184,7 +172,7 @@ sv_status sv_verify(const sv_verify_desc* desc, const void* target_logits, const
     if (workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
 
     sv::Plan pl{};
-    sv::fill_plan(s, desc->temperature, 0.f, &pl);
+    if (!sv::fill_plan(s, desc->temperature, 0.f, &pl)) return SV_ERR_BAD_SHAPE;
     pl.vec = (s.vocab * s.elem_bytes) % 16 == 0 && sv::aligned16(target_logits) &&
              (!s.rows_d || sv::aligned16(draft_logits));
     pl.target = target_logits;
@@ -229,7 +217,7 @@ sv_status sv_vat_labels(const sv_vat_desc* desc, const void* target_logits, cons
     if (workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
 
     sv::Plan pl{};
-    sv::fill_plan(s, desc->temperature, desc->decay, &pl);
+    if (!sv::fill_plan(s, desc->temperature, desc->decay, &pl)) return SV_ERR_BAD_SHAPE;
     pl.vec = (s.vocab * s.elem_bytes) % 16 == 0 && sv::aligned16(target_logits) &&
              (!s.rows_d || sv::aligned16(draft_logits));
     pl.target = target_logits;

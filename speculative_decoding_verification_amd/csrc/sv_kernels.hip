@@ -388,7 +388,7 @@ constexpr uint64_t kPollTimeoutTicks = 1ull << 27;
 // Polls the n words at `words` until all carry `tag`; with `stage` (n <=
 // kStageWords) their data is left in stage[0..n).  Whole block.  Returns
 // false on timeout.
-__device__ bool collect(const uint64_t* words, int n, uint32_t tag, uint32_t* stage) {
+__device__ __forceinline__ bool collect(const uint64_t* words, int n, uint32_t tag, uint32_t* stage) {
     const uint64_t t0 = wall_clock64();
     for (;;) {
         int missing = 0;
@@ -538,7 +538,7 @@ struct DrawPick {
 // total weight, in ascending id order.  First step: the chunk, from a block
 // prefix scan over the chunk masses.  Whole block.
 template <int EB, bool VEC>
-__device__ DrawPick draw_select(const DrawRow& d, float u, int P, int64_t V, TailShared& sh) {
+__device__ __forceinline__ DrawPick draw_select(const DrawRow& d, float u, int P, int64_t V, TailShared& sh) {
     constexpr int CH = Chunk<EB>::kElems;
     constexpr int PT = Chunk<EB>::kPerThread;
     const int tid = threadIdx.x;
@@ -631,7 +631,7 @@ __device__ __forceinline__ DrawPick wave_pick(float mass, float u, int P) {
 // its run of that chunk (block scan: DPP within waves, LDS across them).
 // Whole block; returns the token on every thread.
 template <int EB>
-__device__ int draw_scan(const DrawPick& pk, const float (&w)[Chunk<EB>::kPerThread], TailShared& sh) {
+__device__ __forceinline__ int draw_scan(const DrawPick& pk, const float (&w)[Chunk<EB>::kPerThread], TailShared& sh) {
     constexpr int CH = Chunk<EB>::kElems;
     constexpr int PT = Chunk<EB>::kPerThread;
     const int tid = threadIdx.x;
@@ -676,7 +676,7 @@ __device__ int draw_scan(const DrawPick& pk, const float (&w)[Chunk<EB>::kPerThr
 // The chunk of a draw from `d`: one wave-level pick when P <= 64, else the
 // tiled block-level selection.  Whole block.
 template <int EB, bool VEC>
-__device__ DrawPick pick_chunk(const DrawRow& d, float u, int P, int64_t V, TailShared& sh) {
+__device__ __forceinline__ DrawPick pick_chunk(const DrawRow& d, float u, int P, int64_t V, TailShared& sh) {
     constexpr int CH = Chunk<EB>::kElems;
     constexpr int PT = Chunk<EB>::kPerThread;
     if (P > kWave) return draw_select<EB, VEC>(d, u, P, V, sh);
@@ -702,7 +702,7 @@ __device__ DrawPick pick_chunk(const DrawRow& d, float u, int P, int64_t V, Tail
 
 // Draws one token from the weights of `d` with uniform u.  Whole block.
 template <int EB, bool VEC>
-__device__ int draw_token(const DrawRow& d, float u, int P, int64_t V, TailShared& sh) {
+__device__ __forceinline__ int draw_token(const DrawRow& d, float u, int P, int64_t V, TailShared& sh) {
     constexpr int CH = Chunk<EB>::kElems;
     constexpr int PT = Chunk<EB>::kPerThread;
     const DrawPick pk = pick_chunk<EB, VEC>(d, u, P, V, sh);
@@ -713,101 +713,6 @@ __device__ int draw_token(const DrawRow& d, float u, int P, int64_t V, TailShare
 }
 
 // ------------------------------------------------------------------ task grid
-
-enum RoleKind : int {
-    kDecWorker = 0,     // streams one chunk of a decision row (rows 0..k-1, draft rows)
-    kDecFinisher = 1,   // per sequence: (m, Z), p(x), q(x), accept test, first rejection
-    kResWorker = 2,     // residual mass of one chunk of the rejected row pair
-    kResFinisher = 3,   // per sequence: the residual draw
-    kBonusWorker = 4,   // streams one chunk of the bonus row (target position k)
-    kBonusFinisher = 5  // per sequence: the bonus row's statistics and draw
-};
-
-struct Role {
-    int kind;
-    int seq;
-    int index;  // worker index within the sequence
-};
-
-__device__ __forceinline__ int64_t clamp_b(int64_t x, int B) { return min(max(x, int64_t{0}), static_cast<int64_t>(B)); }
-
-// First block of group g of phase A / phase B.
-__device__ __forceinline__ int64_t phase_a_start(const Plan& pl, int64_t g) {
-    const int B = pl.batch;
-    int64_t s = pl.w_dec * clamp_b(g, B) + clamp_b(g - pl.lag_a, B);
-    if (pl.has_resid) s += pl.w_res * clamp_b(g - pl.lag_a - pl.lag_r, B) + clamp_b(g - pl.lag_a - pl.lag_r - pl.lag_f, B);
-    return s;
-}
-
-__device__ __forceinline__ int64_t phase_b_start(const Plan& pl, int64_t h) {
-    return pl.w_bonus * clamp_b(h, pl.batch) + clamp_b(h - pl.lag_b, pl.batch);
-}
-
-// Largest group g in [0, G) whose first block is <= blk (group starts strictly
-// increase: no group is empty).
-template <typename F>
-__device__ __forceinline__ int64_t find_group(int64_t blk, int64_t G, F start) {
-    int64_t lo = 0, hi = G - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) / 2;
-        if (start(mid) <= blk) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
-__device__ Role decode_role(const Plan& pl, int64_t blk) {
-    const int B = pl.batch;
-    Role r;
-    r.index = 0;
-    const int64_t GA = B + pl.lag_a + (pl.has_resid ? pl.lag_r + pl.lag_f : 0);
-    const int64_t TA = phase_a_start(pl, GA);
-    if (blk < TA) {
-        const int64_t g = find_group(blk, GA, [&](int64_t x) { return phase_a_start(pl, x); });
-        int64_t o = blk - phase_a_start(pl, g);
-        if (g < B) {
-            if (o < pl.w_dec) {
-                r.kind = kDecWorker;
-                r.seq = static_cast<int>(g);
-                r.index = static_cast<int>(o);
-                return r;
-            }
-            o -= pl.w_dec;
-        }
-        int64_t s = g - pl.lag_a;
-        if (s >= 0 && s < B) {
-            if (o == 0) {
-                r.kind = kDecFinisher;
-                r.seq = static_cast<int>(s);
-                return r;
-            }
-            o -= 1;
-        }
-        s = g - pl.lag_a - pl.lag_r;
-        if (o < pl.w_res && s >= 0 && s < B) {
-            r.kind = kResWorker;
-            r.seq = static_cast<int>(s);
-            r.index = static_cast<int>(o);
-            return r;
-        }
-        if (s >= 0 && s < B) o -= pl.w_res;
-        r.kind = kResFinisher;
-        r.seq = static_cast<int>(g - pl.lag_a - pl.lag_r - pl.lag_f);
-        return r;
-    }
-    const int64_t bl = blk - TA;
-    const int64_t h = find_group(bl, B + pl.lag_b, [&](int64_t x) { return phase_b_start(pl, x); });
-    const int64_t o = bl - phase_b_start(pl, h);
-    if (h < B && o < pl.w_bonus) {
-        r.kind = kBonusWorker;
-        r.seq = static_cast<int>(h);
-        r.index = static_cast<int>(o);
-        return r;
-    }
-    r.kind = kBonusFinisher;
-    r.seq = static_cast<int>(h - pl.lag_b);
-    return r;
-}
 
 // Global row (the numbering of row_stats_out) of local row j of sequence b.
 __device__ __forceinline__ int64_t global_row(const Plan& pl, int b, int j) {
@@ -911,7 +816,7 @@ __device__ __forceinline__ Decision read_decision(const uint32_t* st) {
 // ------------------------------------------------------------------ finishers
 
 // Marks a sequence whose finisher gave up waiting (see kPollTimeoutTicks).
-__device__ void fail_sequence(const Plan& pl, int b) {
+__device__ __forceinline__ void fail_sequence(const Plan& pl, int b) {
     const int k = pl.k;
     for (int j = threadIdx.x; j <= k; j += kBlock) {
         if (pl.vat) {
@@ -974,7 +879,7 @@ __device__ __forceinline__ void write_row_stats(const Plan& pl, int64_t grow, fl
 
 // Decision finisher of sequence b: everything that needs rows 0..k-1.
 template <int EB, bool VEC>
-__device__ void decide_sequence(const Plan& pl, int b, TailShared& sh) {
+__device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShared& sh) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int k = pl.k;
@@ -1121,7 +1026,7 @@ __device__ void decide_sequence(const Plan& pl, int b, TailShared& sh) {
 
 // Residual worker `w` of sequence b: mass of one chunk of max(0, p_r - q_r).
 template <int EB, bool VEC>
-__device__ void residual_worker(const Plan& pl, int b, int w, TailShared& sh) {
+__device__ __forceinline__ void residual_worker(const Plan& pl, int b, int w, TailShared& sh) {
     if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage)) return;
     const Decision dc = read_decision(sh.stage);
     if (dc.mode != kModeResidual) return;
@@ -1145,7 +1050,7 @@ __device__ void residual_worker(const Plan& pl, int b, int w, TailShared& sh) {
 
 // Residual finisher of sequence b: draws the target's token at r < k.
 template <int EB, bool VEC>
-__device__ void residual_finisher(const Plan& pl, int b, TailShared& sh) {
+__device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailShared& sh) {
     const int P = pl.chunks;
     const int k = pl.k;
     const int64_t V = pl.vocab;
@@ -1186,7 +1091,7 @@ __device__ void residual_finisher(const Plan& pl, int b, TailShared& sh) {
 // Bonus finisher of sequence b: statistics of target row k and, when all k
 // drafts were kept, the token drawn from it (its argmax at T == 0).
 template <int EB, bool VEC>
-__device__ void bonus_finisher(const Plan& pl, int b, TailShared& sh) {
+__device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared& sh) {
     const int lane = threadIdx.x & (kWave - 1);
     const int k = pl.k;
     const int P = pl.chunks;
@@ -1240,7 +1145,7 @@ constexpr int kMinBlocksPerCU = 5;
 template <int EB, bool VEC>
 __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
     __shared__ TailShared sh;
-    const Role role = decode_role(pl, blockIdx.x);
+    const Role role = decode_role(pl.grid, static_cast<int32_t>(blockIdx.x));
     const int b = role.seq;
     switch (role.kind) {
         case kDecWorker: {
@@ -1290,7 +1195,7 @@ hipError_t launch_typed(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipE
         e = hipEventRecord(ev0, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_verify<EB, VEC>), dim3(static_cast<unsigned>(grid_blocks(pl))), dim3(kBlock), 0, stream, pl);
+    hipLaunchKernelGGL((k_verify<EB, VEC>), dim3(static_cast<unsigned>(pl.grid.total_blocks)), dim3(kBlock), 0, stream, pl);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev0 && ev1) {
@@ -1301,14 +1206,6 @@ hipError_t launch_typed(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipE
 }
 
 }  // namespace
-
-int64_t grid_blocks(const Plan& pl) {
-    const int64_t B = pl.batch;
-    int64_t n = B * (pl.w_dec + 1);
-    if (pl.has_resid) n += B * (pl.w_res + 1);
-    if (pl.has_bonus) n += B * (pl.w_bonus + 1);
-    return n;
-}
 
 hipError_t launch_path(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (pl.batch == 0) return hipSuccess;

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime_api.h>
 #include <hip/hip_vector_types.h>
 
+#include "sv_grid.h"
+
 namespace sv {
 
 // One wavefront streams one "chunk" of a logit row: 64 lanes x 8 vectors of
@@ -60,13 +62,7 @@ struct Plan {
     int32_t rows_per_seq;     // dec_rows + (1 if there is a bonus row)
     bool has_resid;           // draft logits at T > 0: residual roles exist
     bool has_bonus;           // verification (not VAT): bonus roles exist
-    // Task grid: phase A groups (decision workers, decision finisher of the
-    // sequence LA groups back, residual workers LA+LR back, residual finisher
-    // LA+LR+LF back), then phase B groups (bonus workers, bonus finisher LB
-    // back).  Every block depends only on blocks before it in the grid.
-    int32_t w_dec, w_res, w_bonus;  // worker blocks per sequence of each kind
-    int32_t nc_dec, nc_res;         // chunks per worker wavefront
-    int32_t lag_a, lag_r, lag_f, lag_b;
+    int32_t nc_dec, nc_res;   // chunks per worker wavefront
     uint32_t tag;             // this call's tag of hand-off words
     int64_t rows_t;
     int64_t rows_d;           // 0 for one-hot drafts and T == 0
@@ -95,6 +91,8 @@ struct Plan {
     uint64_t* partials;       // [B][R_s][P][2] tagged words (m, s) or (max, index)
     uint64_t* resid;          // [B][P] tagged residual masses
     uint64_t* dec;            // [B][kDecWords] tagged decision words
+
+    TaskGrid grid;            // role of every block of the launch
 };
 
 // Blocks the GPU keeps resident at once (256 CUs x ~5 workgroups of 256
@@ -102,11 +100,15 @@ struct Plan {
 // finisher block.
 constexpr int64_t kResidentBlocks = 1280;
 
-// Chunks each worker wavefront streams (one after the other): fewer, longer
-// lived blocks.  Block dispatch, not HBM, bounds a grid of short blocks (the
-// dispatcher issues on the order of 150-200 blocks per microsecond).
-constexpr int kChunksPerWave = 4;       // decision and bonus rows
-constexpr int kChunksPerWaveResid = 2;  // residual row pairs (two rows per chunk)
+// Chunks each worker wavefront streams, one after the other.  Two per wave
+// for large calls: block dispatch (on the order of 150-200 blocks per
+// microsecond) would otherwise bound the grid; one per wave for small calls,
+// where the drain of long-lived blocks at the end dominates.  Residual
+// workers read two rows per chunk and take one chunk pair per wave.
+constexpr int kChunksPerWave = 2;
+constexpr int kChunksPerWaveSmall = 1;
+constexpr int64_t kSmallCallChunks = 4 * kWavesPerBlock * kResidentBlocks;
+constexpr int kChunksPerWaveResid = 1;
 
 // Values handed between blocks inside a kernel travel as 64-bit words,
 // written and read whole (single-copy atomic): 32 data bits and a 32-bit tag
@@ -124,9 +126,6 @@ struct WorkspaceLayout {
 };
 
 WorkspaceLayout workspace_layout(int64_t rows, int64_t batch, int64_t chunks);
-
-// Blocks of the task grid.
-int64_t grid_blocks(const Plan& plan);
 
 // Enqueue the whole path on `stream`.  Returns hipSuccess or the first error.
 hipError_t launch_path(const Plan& plan, hipStream_t stream, hipEvent_t probe_start, hipEvent_t probe_stop);

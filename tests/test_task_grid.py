@@ -1,0 +1,123 @@
+"""The kernel's task grid, decoded on the host with the kernel's own code
+(csrc/sv_grid.h): every role instance appears exactly once, and every role
+comes after the roles of its sequence that it waits on, so that blocks
+dispatched in grid order never wait on a block that has not started."""
+from __future__ import annotations
+
+import ctypes
+import itertools
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "speculative_decoding_verification_amd", "csrc")
+
+DW, DF, RW, RF, BW, BF = range(6)
+
+
+@pytest.fixture(scope="module")
+def probe(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("grid") / "libgridprobe.so")
+    subprocess.check_call(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-I", CSRC,
+                           os.path.join(CSRC, "sv_grid.cpp"), os.path.join(ROOT, "tests", "grid_probe.cpp"),
+                           "-o", out])
+    lib = ctypes.CDLL(out)
+    i32, i64, p32 = ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
+    lib.probe_plan.argtypes = [i32, i64, i64, i32, i32, i64, i64, i64, p32]
+    lib.probe_plan.restype = i32
+    lib.probe_decode.argtypes = [i32] * 10 + [p32, p32, p32, i32]
+    lib.probe_decode.restype = i32
+    return lib
+
+
+def decode(lib, B, w_dec, w_res, w_bonus, has_resid, has_bonus, la, lr, lf, lb, cap=1 << 20):
+    kind = np.empty(cap, np.int32)
+    seq = np.empty(cap, np.int32)
+    idx = np.empty(cap, np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    n = lib.probe_decode(B, w_dec, w_res, w_bonus, int(has_resid), int(has_bonus), la, lr, lf, lb, p(kind), p(seq),
+                         p(idx), cap)
+    assert n > 0, n
+    return kind[:n], seq[:n], idx[:n]
+
+
+def check_grid(kind, seq, idx, B, w_dec, w_res, w_bonus, has_resid, has_bonus):
+    where = {}
+    for blk, (k, s, i) in enumerate(zip(kind.tolist(), seq.tolist(), idx.tolist())):
+        assert 0 <= s < B, (blk, k, s, i)
+        key = (k, s, i)
+        assert key not in where, ("role twice", key)
+        where[key] = blk
+    want = B * (w_dec + 1 + ((w_res + 1) if has_resid else 0) + ((w_bonus + 1) if has_bonus else 0))
+    assert len(where) == want == len(kind)
+    for s in range(B):
+        df = where[(DF, s, 0)]
+        assert all(where[(DW, s, w)] < df for w in range(w_dec))
+        if has_resid:
+            rf = where[(RF, s, 0)]
+            assert all(df < where[(RW, s, w)] < rf for w in range(w_res))
+        if has_bonus:
+            bf = where[(BF, s, 0)]
+            assert df < bf and all(where[(BW, s, w)] < bf for w in range(w_bonus))
+
+
+def test_every_block_decodes_to_one_role_in_dependency_order(probe):
+    n = 0
+    for B in (1, 2, 3, 7, 40):
+        for w_dec in (1, 2, 5, 24):
+            for has_resid, w_res in ((False, 0), (True, 1), (True, 5)):
+                for has_bonus, w_bonus in ((False, 0), (True, 1), (True, 3)):
+                    lags_a = sorted({0, 1, B // 2, B})
+                    for la, lr, lf, lb in itertools.product(lags_a, (0, 1, B) if has_resid else (0,),
+                                                            (0, B) if has_resid else (0,),
+                                                            (0, 1, B) if has_bonus else (0,)):
+                        lr, lf, lb = min(lr, B), min(lf, B), min(lb, B)
+                        k, s, i = decode(probe, B, w_dec, w_res, w_bonus, has_resid, has_bonus, la, lr, lf, lb)
+                        check_grid(k, s, i, B, w_dec, w_res, w_bonus, has_resid, has_bonus)
+                        n += 1
+    assert n > 500
+
+
+@pytest.mark.parametrize("name,B,k,V,eb,T,onehot,vat", [
+    ("selfdraft", 128, 5, 151936, 2, 1.0, False, False),
+    ("ngram_tail", 8, 16, 151936, 2, 1.0, True, False),
+    ("grpo", 320, 7, 151936, 2, 0.6, False, False),
+    ("grpo_greedy", 320, 7, 151936, 2, 0.0, False, False),
+    ("vat", 2048, 16, 128256, 4, 1.0, False, True),
+    ("tiny", 4, 4, 1000, 4, 1.0, False, False),
+])
+def test_planned_grids_of_the_workloads(probe, name, B, k, V, eb, T, onehot, vat):
+    """The planner's own widths and lags at the workload shapes (four
+    wavefronts per block, the chunk counts of 8 KiB chunks)."""
+    chunks = -(-V // (8192 // eb))
+    reads_draft = not onehot and T != 0.0
+    dec_rows = k + (k if reads_draft else 0)
+    has_resid = (not vat) and T != 0.0 and not onehot
+    has_bonus = not vat
+    params = np.zeros(8, np.int32)
+    for per_dec, per_res in ((4, 4), (8, 4), (16, 8)):
+        n = probe.probe_plan(B, dec_rows * chunks, chunks, int(has_resid), int(has_bonus), per_dec, per_res, 1280,
+                             params.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+        assert n > 0
+        w_dec, w_res, w_bonus, la, lr, lf, lb, nseg = params.tolist()
+        assert w_dec == -(-dec_rows * chunks // per_dec)
+        assert 1 <= nseg <= 12
+        assert all(0 <= x <= B for x in (la, lr, lf, lb))
+        kind, seq, idx = decode(probe, B, w_dec, w_res, w_bonus, has_resid, has_bonus, la, lr, lf, lb,
+                                cap=1 << 22)
+        assert len(kind) == n
+        check_grid(kind, seq, idx, B, w_dec, w_res, w_bonus, has_resid, has_bonus)
+
+
+def test_grid_division_is_exact(probe):
+    """The float-reciprocal division with integer corrections, at the limits."""
+    # a grid whose groups are large and whose block count is near 2^24 and beyond
+    for B, w_dec in ((3, 7_000_001), (1000, 16411), (70000, 31)):
+        kind, seq, idx = decode(probe, B, w_dec, 0, 0, False, False, B, 0, 0, 0, cap=1 << 25)
+        n = B * (w_dec + 1)
+        assert len(kind) == n
+        assert np.count_nonzero(kind == DF) == B
+        assert np.array_equal(np.bincount(seq[kind == DW], minlength=B), np.full(B, w_dec))
