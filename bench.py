@@ -11,8 +11,12 @@ V=151936, bf16 target and draft logits, T=1.  Prints ONE JSON line.
   value        verified draft positions per second = B*k*K / wall time of K
                steps (synchronised on both sides); VAT: labelled positions
   roofline     k_verify: algorithmic bytes per launch (every logit the path
-               needs, read once) / its mean duration, measured live with HIP
-               events recorded on the launch stream around each launch;
+               needs, read once: the k target and k draft rows of every
+               sequence, and target row k of the sequences that kept all k
+               drafts, the only ones that draw from it) / its mean duration, measured live with HIP
+               events recorded on the launch stream around the K timed
+               launches (per-launch events would add several microseconds
+               of stream work between launches);
                `traffic` = HBM bytes per launch from committed rocprofv3
                FETCH_SIZE/WRITE_SIZE counters when they were taken on the
                current kernel source, else null
@@ -50,7 +54,8 @@ METRIC = "verified draft positions/sec + achieved HBM GB/s (V=151936 bf16, k=5..
 
 
 class HipEvents:
-    """Raw hipEvent_t handles (the probe slots of the verify descriptor take them)."""
+    """Raw hipEvent_t handles recorded on the launch stream (torch.cuda.Event
+    would record on torch's current stream, which need not be it)."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
@@ -58,15 +63,21 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
-        # No system-scope fence at record time: the probes only timestamp the
+        # No system-scope fence at record time: the events only timestamp the
         # launch stream and should disturb it as little as possible.
         ev = ctypes.c_void_p()
         rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE)
         if rc != 0:
             raise RuntimeError("hipEventCreate failed: %d" % rc)
         return ev.value
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
 
     def elapsed_ms(self, a, b) -> float:
         self.hip.hipEventSynchronize(ctypes.c_void_p(b))
@@ -151,14 +162,15 @@ def copy_probe(steps: int) -> int:
     return 0
 
 
-def _launchers(cfg, sets, probes, sv, n_launch):
+def _launchers(cfg, sets, sv, n):
+    """One prepared call per resident input copy (they rotate)."""
     out = []
-    for i in range(n_launch):
+    for i in range(n):
         t, d, x, u = sets[i % len(sets)]
         if cfg.kind == "vat":
-            out.append(sv.VatLabeler(t, d, x, u, cfg.T, cfg.decay, probe=probes[i]))
+            out.append(sv.VatLabeler(t, d, x, u, cfg.T, cfg.decay))
         else:
-            out.append(sv.Verifier(t, d, x, u, cfg.T, onehot=cfg.onehot, probe=probes[i]))
+            out.append(sv.Verifier(t, d, x, u, cfg.T, onehot=cfg.onehot))
     return out
 
 
@@ -166,7 +178,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="selfdraft",
                     choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -207,39 +219,48 @@ def main(argv=None):
         del wl
     ev = HipEvents()
     n_launch = args.warmup + args.steps
-    probes = [(ev.create(), ev.create()) for _ in range(n_launch)]
-    calls = _launchers(cfg, sets, probes, sv, n_launch)
+    calls = _launchers(cfg, sets, sv, len(sets))
     stream = torch.cuda.current_stream(dev).cuda_stream
+    region = (ev.create(), ev.create())
 
     print("bench: %d copies of %.1f MB, %d warmup + %d timed steps" % (copies, in_bytes / 1e6, args.warmup,
                                                                         args.steps), file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        calls[i](stream)
+        calls[i % len(calls)](stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev.record(region[0], stream)
     for i in range(args.warmup, n_launch):
-        calls[i](stream)
+        calls[i % len(calls)](stream)
+    ev.record(region[1], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
-    k1_ms = [ev.elapsed_ms(*probes[i]) for i in range(args.warmup, n_launch)]
-    k1_ms.sort()
-    k1_mean = sum(k1_ms) / len(k1_ms)
+    # The only work on the stream inside the region is the K launches of the
+    # kernel, back to back: the region's device time over K is the kernel's
+    # average launch duration (any gap between launches counts against it).
+    k1_mean = ev.elapsed_ms(*region) / args.steps
     ms_per_step = elapsed * 1e3 / args.steps
     positions = cfg.positions() * args.steps
     value = positions / elapsed
     kernel = "k_verify"
-    achieved = in_bytes / (k1_mean * 1e-3) / 1e9
-    last = calls[-1]
+    last = calls[(n_launch - 1) % len(calls)]
     if cfg.kind == "vat":
         fr = last.first_reject.float()
         extra = {"mean_first_reject": fr.mean().item(), "timeouts": int((fr == -2).sum().item())}
+        needed = in_bytes
     else:
         acc = last.accepted_len.float()
-        extra = {"mean_accepted_len": acc.mean().item(), "timeouts": int((acc == -2).sum().item())}
-    for a, b in probes:
-        ev.destroy(a)
-        ev.destroy(b)
+        full = int((acc == cfg.k).sum().item())
+        extra = {"mean_accepted_len": acc.mean().item(), "timeouts": int((acc == -2).sum().item()),
+                 "full_acceptance": full}
+        # every input copy holds the same logits, so every call needs the
+        # same rows: the decision rows of all sequences and the bonus row
+        # (target position k) of those that kept all k drafts
+        needed = in_bytes - (cfg.B - full) * cfg.V * cfg.elem_bytes
+    achieved = needed / (k1_mean * 1e-3) / 1e9
+    for e in region:
+        ev.destroy(e)
     del calls, sets
 
     res = {
@@ -258,12 +279,12 @@ def main(argv=None):
         "config": {"workload": cfg.name, "batch": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
                    "logits": cfg.dtype, "temperature": cfg.T, "draft": "one-hot" if cfg.onehot else "logits",
                    "input_copies_rotated": copies},
-        "hbm_gbps_whole_step": in_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_gbps_whole_step": needed / (ms_per_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(kernel, cfg.name),
-                     "algorithmic_bytes_per_launch": in_bytes, "mean_launch_us": k1_mean * 1e3,
-                     "median_launch_us": k1_ms[len(k1_ms) // 2] * 1e3},
+                     "algorithmic_bytes_per_launch": needed, "all_rows_bytes_per_launch": in_bytes,
+                     "mean_launch_us": k1_mean * 1e3},
     }
     res.update(extra)
     if cfg.kind == "vat":

@@ -216,6 +216,38 @@ __device__ __forceinline__ float wave_sum(float v) {
     return ((readlane(v, 0) + readlane(v, 16)) + readlane(v, 32)) + readlane(v, 48);
 }
 
+// Integer maximum / minimum over the wave, on every lane.
+__device__ __forceinline__ int wave_max_i(int v) {
+    v = max(v, dpp_i<kDppQuadSwap1>(v, v));
+    v = max(v, dpp_i<kDppQuadSwap2>(v, v));
+    v = max(v, dpp_i<kDppRowRor4>(v, v));
+    v = max(v, dpp_i<kDppRowRor8>(v, v));
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+    v = min(v, dpp_i<kDppQuadSwap1>(v, v));
+    v = min(v, dpp_i<kDppQuadSwap2>(v, v));
+    v = min(v, dpp_i<kDppRowRor4>(v, v));
+    v = min(v, dpp_i<kDppRowRor8>(v, v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Block-wide "any": a ballot per wave, one LDS flag per wave, a barrier.
+// (flags: kWavesPerBlock ints of LDS.)  Whole block.
+__device__ __forceinline__ bool block_any(bool pred, int* flags) {
+    const bool w = __ballot(pred) != 0ull;
+    if ((threadIdx.x & (kWave - 1)) == 0) flags[threadIdx.x / kWave] = w;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int q = 0; q < kWavesPerBlock; ++q) any |= flags[q];
+    __syncthreads();
+    return any != 0;
+}
+
 // Larger value wins; equal values: lower index wins.  Result on every lane.
 __device__ __forceinline__ void argmax_step(float& best, int& idx, float ob, int oi) {
     if (ob > best || (ob == best && oi < idx)) {
@@ -386,18 +418,18 @@ __device__ __forceinline__ void put_partial(uint64_t* seq_words, int i, float2 v
 constexpr uint64_t kPollTimeoutTicks = 1ull << 27;
 
 // Polls the n words at `words` until all carry `tag`; with `stage` (n <=
-// kStageWords) their data is left in stage[0..n).  Whole block.  Returns
-// false on timeout.
-__device__ __forceinline__ bool collect(const uint64_t* words, int n, uint32_t tag, uint32_t* stage) {
+// kStageWords) their data is left in stage[0..n).  Whole block (flags: the
+// block's LDS vote slots).  Returns false on timeout.
+__device__ __forceinline__ bool collect(const uint64_t* words, int n, uint32_t tag, uint32_t* stage, int* flags) {
     const uint64_t t0 = wall_clock64();
     for (;;) {
-        int missing = 0;
+        bool missing = false;
         for (int i = threadIdx.x; i < n; i += kBlock) {
             const uint64_t w = get_word(words + i);
-            if (static_cast<uint32_t>(w >> 32) != tag) missing = 1;
+            if (static_cast<uint32_t>(w >> 32) != tag) missing = true;
             else if (stage) stage[i] = word_data(w);
         }
-        if (!__syncthreads_or(missing)) return true;
+        if (!block_any(missing, flags)) return true;
         if (wall_clock64() - t0 > kPollTimeoutTicks) return false;
         __builtin_amdgcn_s_sleep(8);
     }
@@ -418,6 +450,9 @@ struct TailShared {
     uint32_t stage[kStageWords];   // staged hand-off words
     float2 mz[2 * kMaxDraft + 1];  // (m, Z) or (max, argmax) of the sequence's rows
     float wt[kWavesPerBlock];      // block scan scratch
+    int vote[kWavesPerBlock];      // block_any scratch
+    int wlast[kWavesPerBlock];     // per-wave last positive position (draws)
+    int wsel[kWavesPerBlock];      // per-wave selected position (draws)
     float prev_mass;               // running mass before the selected chunk
     int sel;
     int last_pos;
@@ -584,8 +619,9 @@ __device__ __forceinline__ DrawPick draw_select(const DrawRow& d, float u, int P
                 sh.sel = c;  // unique: the running mass is non-decreasing
                 sh.prev_mass = prev;
             }
-            if (v > 0.f) atomicMax(&sh.last_pos, c);
         }
+        const int wl = wave_max_i(c < P && v > 0.f ? c : -1);
+        if ((tid & (kWave - 1)) == 0 && wl >= 0) atomicMax(&sh.last_pos, wl);
         carry = carry + total;
         __syncthreads();
         if (sh.sel != INT_MAX) break;
@@ -646,29 +682,33 @@ __device__ __forceinline__ int draw_scan(const DrawPick& pk, const float (&w)[Ch
     }
     const float incl = wave_incl_scan(my_sum);
     if (lane == kWave - 1) sh.wt[wave] = incl;
-    if (tid == 0) {
-        sh.sel = INT_MAX;
-        sh.last_pos = -1;
-    }
+    const int wl = wave_max_i(my_last);
+    if (lane == 0) sh.wlast[wave] = wl;
     __syncthreads();
     float prefix = 0.f;
 #pragma unroll
     for (int q = 0; q < kWavesPerBlock; ++q)
         if (q < wave) prefix += sh.wt[q];
     const float excl = prefix + dpp<kDppWaveShr1>(0.f, incl);
-    if (my_last >= 0) atomicMax(&sh.last_pos, my_last);
+    int pick = INT_MAX;
     if (!pk.open_end && excl + my_sum > pk.th) {
         float run = excl;
-        int pick = -1;
 #pragma unroll
         for (int e = 0; e < PT; ++e) {
             run += w[e];
-            if (pick < 0 && w[e] > 0.f && run > pk.th) pick = tid * PT + e;
+            if (pick == INT_MAX && w[e] > 0.f && run > pk.th) pick = tid * PT + e;
         }
-        if (pick >= 0) atomicMin(&sh.sel, pick);
     }
+    pick = wave_min_i(pick);
+    if (lane == 0) sh.wsel[wave] = pick;
     __syncthreads();
-    const int y = sh.sel != INT_MAX ? sh.sel : (sh.last_pos >= 0 ? sh.last_pos : 0);
+    int sel = INT_MAX, last = -1;
+#pragma unroll
+    for (int q = 0; q < kWavesPerBlock; ++q) {
+        sel = min(sel, sh.wsel[q]);
+        last = max(last, sh.wlast[q]);
+    }
+    const int y = sel != INT_MAX ? sel : (last >= 0 ? last : 0);
     __syncthreads();
     return pk.cs * CH + y;
 }
@@ -912,7 +952,7 @@ __device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShare
     const float u_draw = sampling ? pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k] : 0.f;
 
     const bool staged = 2 * dec_items <= kStageWords;
-    if (!collect(words, 2 * dec_items, pl.tag, staged ? sh.stage : nullptr)) {
+    if (!collect(words, 2 * dec_items, pl.tag, staged ? sh.stage : nullptr, sh.vote)) {
         fail_sequence(pl, b);
         if (!pl.vat && threadIdx.x == 0) {
             Decision d{};
@@ -1027,7 +1067,7 @@ __device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShare
 // Residual worker `w` of sequence b: mass of one chunk of max(0, p_r - q_r).
 template <int EB, bool VEC>
 __device__ __forceinline__ void residual_worker(const Plan& pl, int b, int w, TailShared& sh) {
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage)) return;
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote)) return;
     const Decision dc = read_decision(sh.stage);
     if (dc.mode != kModeResidual) return;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1056,13 +1096,13 @@ __device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailSha
     const int64_t V = pl.vocab;
     uint64_t* rwords = pl.resid + static_cast<int64_t>(b) * P;
     const bool staged = P + kDecWords <= kStageWords;
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage)) {
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote)) {
         fail_sequence(pl, b);
         return;
     }
     const Decision dc = read_decision(sh.stage);
     if (dc.mode != kModeResidual) return;
-    if (!collect(rwords, P, pl.tag, staged ? sh.stage + kDecWords : nullptr)) {
+    if (!collect(rwords, P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote)) {
         fail_sequence(pl, b);
         return;
     }
@@ -1083,7 +1123,7 @@ __device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailSha
     // since a rejection has probability TV(p, q)): draw from p_r instead.
     float zsum = 0.f;
     for (int cc = threadIdx.x; cc < P; cc += kBlock) zsum += chunk_mass(d, cc, -1, 0.f);
-    if (!__syncthreads_or(zsum > 0.f)) d.mode = kModeBonus;
+    if (!block_any(zsum > 0.f, sh.vote)) d.mode = kModeBonus;
     const int y = draw_token<EB, VEC>(d, dc.u, P, V, sh);
     if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + dc.r] = y;
 }
@@ -1099,13 +1139,18 @@ __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared
     const float c2 = pl.c2;
     const uint64_t* words = seq_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * P * 2;
     const bool staged = 2 * P + kDecWords <= kStageWords;
-    // The decision words and the bonus row's partials are polled together.
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage) ||
-        !collect(words, 2 * P, pl.tag, staged ? sh.stage + kDecWords : nullptr)) {
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote)) {
         fail_sequence(pl, b);
         return;
     }
     const Decision dc = read_decision(sh.stage);
+    // Without full acceptance the bonus row was not read (unless every row's
+    // statistics are asked for): nothing to do.
+    if (dc.r != k && !pl.row_stats_out) return;
+    if (!collect(words, 2 * P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote)) {
+        fail_sequence(pl, b);
+        return;
+    }
     const PartialSrc src{staged ? sh.stage + kDecWords : nullptr, words};
     if (threadIdx.x < kWave) {
         const float2 res = combine_row(src, 0, P, pl.greedy, c2);
@@ -1162,6 +1207,13 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
             return;
         }
         case kBonusWorker: {
+            // The bonus row is read only when the sequence kept all k drafts
+            // (or when every row's statistics are asked for).
+            if (!pl.row_stats_out) {
+                const uint64_t* dw = pl.dec + static_cast<int64_t>(b) * kDecWords + kDecRMode;
+                if (!collect(dw, 1, pl.tag, sh.stage, sh.vote)) return;
+                if (static_cast<int>(sh.stage[0] & 0xffffu) - 2 != pl.k) return;
+            }
             const int base = role.index * kWavesPerBlock * pl.nc_dec + static_cast<int>(threadIdx.x / kWave);
 #pragma unroll 1
             for (int n = 0; n < pl.nc_dec; ++n) {

@@ -43,7 +43,13 @@ def run_verify_gpu(wl, device, temperature=None, onehot=None):
     x = to_torch(wl.tokens, device)
     u = to_torch(wl.uniforms, device)
     res = sv.verify(t, d, x, u, T, onehot=oh, return_probs=True, return_row_stats=True)
-    return {name: getattr(res, name).cpu().numpy() for name in ("accepted_len", "out_tokens", "probs", "row_stats")}
+    out = {name: getattr(res, name).cpu().numpy() for name in ("accepted_len", "out_tokens", "probs", "row_stats")}
+    # Without row statistics the library skips the bonus rows that no draw
+    # needs; the decisions and tokens must not change.
+    lean = sv.verify(t, d, x, u, T, onehot=oh)
+    assert np.array_equal(lean.accepted_len.cpu().numpy(), out["accepted_len"]), "accepted_len differs without row stats"
+    assert np.array_equal(lean.out_tokens.cpu().numpy(), out["out_tokens"]), "out_tokens differ without row stats"
+    return out
 
 
 def run_vat_gpu(wl, device, temperature=None, decay=None):
