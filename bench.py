@@ -25,6 +25,8 @@ V=151936, bf16 target and draft logits, T=1.  Prints ONE JSON line.
 
 Inputs rotate through enough copies that each timed sweep touches more than
 twice the 256 MB last-level (MALL) cache, so the figures are HBM figures.
+The default warm-up (200 calls, tens of milliseconds) lets the GPU reach its
+steady clocks; with a few warm-up calls the first timed calls run slower.
 
     python bench.py --copy-probe [--steps K]
 
@@ -177,8 +179,8 @@ def _launchers(cfg, sets, sv, n):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="selfdraft",
                     choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -84,9 +84,10 @@ bool fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
     pl->rows_per_seq = pl->dec_rows + (pl->has_bonus ? 1 : 0);
     pl->nc_dec = s.batch * pl->dec_rows * s.chunks <= kSmallCallChunks ? kChunksPerWaveSmall : kChunksPerWave;
     pl->nc_res = kChunksPerWaveResid;
+    pl->nc_bonus = std::min(pl->nc_dec, kChunksPerWaveBonus);
     if (!plan_task_grid(pl->batch, static_cast<int64_t>(pl->dec_rows) * s.chunks, s.chunks, pl->has_resid,
-                        pl->has_bonus, kWavesPerBlock * pl->nc_dec, kWavesPerBlock * pl->nc_res, kResidentBlocks,
-                        &pl->grid))
+                        pl->has_bonus, kWavesPerBlock * pl->nc_dec, kWavesPerBlock * pl->nc_bonus,
+                        kWavesPerBlock * pl->nc_res, kResidentBlocks, &pl->grid))
         return false;
     pl->rows_t = s.rows_t;
     pl->rows_d = s.rows_d;

@@ -114,12 +114,14 @@ bool build_task_grid(int32_t batch, int32_t w_dec, int32_t w_res, int32_t w_bonu
 }
 
 bool plan_task_grid(int32_t batch, int64_t dec_items, int64_t chunks, bool has_resid, bool has_bonus,
-                    int64_t per_block_dec, int64_t per_block_res, int64_t resident_blocks, TaskGrid* tg) {
+                    int64_t per_block_dec, int64_t per_block_bonus, int64_t per_block_res, int64_t resident_blocks,
+                    TaskGrid* tg) {
     const auto ceil_div = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
-    if (batch < 1 || dec_items < 1 || chunks < 1 || per_block_dec < 1 || per_block_res < 1) return false;
+    if (batch < 1 || dec_items < 1 || chunks < 1 || per_block_dec < 1 || per_block_bonus < 1 || per_block_res < 1)
+        return false;
     const int64_t w_dec = ceil_div(dec_items, per_block_dec);
     const int64_t w_res = has_resid ? ceil_div(chunks, per_block_res) : 0;
-    const int64_t w_bonus = has_bonus ? ceil_div(chunks, per_block_dec) : 0;
+    const int64_t w_bonus = has_bonus ? ceil_div(chunks, per_block_bonus) : 0;
     if (w_dec > 0x7fffffffLL || w_res > 0x7fffffffLL || w_bonus > 0x7fffffffLL) return false;
     // A finisher goes about one residency of blocks after its workers, the
     // residual workers half a residency after the decision, the residual

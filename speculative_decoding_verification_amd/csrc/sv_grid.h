@@ -130,11 +130,13 @@ SV_HOST_DEVICE inline Role decode_role(const TaskGrid& tg, int32_t blk) {
 
 // Host: the grid of one call.  dec_items = decision-row chunks per sequence,
 // chunks = chunks per row; a worker block covers `per_block_dec` chunks of
-// decision or bonus rows and `per_block_res` chunk pairs of the residual; the
-// lags are derived from the number of blocks the device keeps resident.
-// Returns false if the grid does not fit the limits.
+// decision rows, `per_block_bonus` chunks of the bonus row and
+// `per_block_res` chunk pairs of the residual; the lags are derived from the
+// number of blocks the device keeps resident.  Returns false if the grid
+// does not fit the limits.
 bool plan_task_grid(int32_t batch, int64_t dec_items, int64_t chunks, bool has_resid, bool has_bonus,
-                    int64_t per_block_dec, int64_t per_block_res, int64_t resident_blocks, TaskGrid* tg);
+                    int64_t per_block_dec, int64_t per_block_bonus, int64_t per_block_res, int64_t resident_blocks,
+                    TaskGrid* tg);
 
 // Host: the segments of a grid.  Returns false if the grid does not fit the
 // limits (more than 2^31 - 1 blocks, or lags outside [0, B]).

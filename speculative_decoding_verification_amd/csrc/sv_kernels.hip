@@ -1214,9 +1214,9 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
                 if (!collect(dw, 1, pl.tag, sh.stage, sh.vote)) return;
                 if (static_cast<int>(sh.stage[0] & 0xffffu) - 2 != pl.k) return;
             }
-            const int base = role.index * kWavesPerBlock * pl.nc_dec + static_cast<int>(threadIdx.x / kWave);
+            const int base = role.index * kWavesPerBlock * pl.nc_bonus + static_cast<int>(threadIdx.x / kWave);
 #pragma unroll 1
-            for (int n = 0; n < pl.nc_dec; ++n) {
+            for (int n = 0; n < pl.nc_bonus; ++n) {
                 const int c = base + n * kWavesPerBlock;
                 if (c >= pl.chunks) break;
                 stream_chunk<EB, VEC>(pl, b, pl.dec_rows, c);

@@ -62,7 +62,7 @@ struct Plan {
     int32_t rows_per_seq;     // dec_rows + (1 if there is a bonus row)
     bool has_resid;           // draft logits at T > 0: residual roles exist
     bool has_bonus;           // verification (not VAT): bonus roles exist
-    int32_t nc_dec, nc_res;   // chunks per worker wavefront
+    int32_t nc_dec, nc_bonus, nc_res;  // chunks per worker wavefront
     uint32_t tag;             // this call's tag of hand-off words
     int64_t rows_t;
     int64_t rows_d;           // 0 for one-hot drafts and T == 0
@@ -109,6 +109,7 @@ constexpr int kChunksPerWave = 2;
 constexpr int kChunksPerWaveSmall = 1;
 constexpr int64_t kSmallCallChunks = 4 * kWavesPerBlock * kResidentBlocks;
 constexpr int kChunksPerWaveResid = 1;
+constexpr int kChunksPerWaveBonus = 2;
 
 // Values handed between blocks inside a kernel travel as 64-bit words,
 // written and read whole (single-copy atomic): 32 data bits and a 32-bit tag

@@ -6,10 +6,11 @@
 #include "sv_grid.h"
 
 extern "C" int32_t probe_plan(int32_t batch, int64_t dec_items, int64_t chunks, int32_t has_resid, int32_t has_bonus,
-                              int64_t per_block_dec, int64_t per_block_res, int64_t resident, int32_t* params) {
+                              int64_t per_block_dec, int64_t per_block_bonus, int64_t per_block_res, int64_t resident,
+                              int32_t* params) {
     sv::TaskGrid tg;
-    if (!sv::plan_task_grid(batch, dec_items, chunks, has_resid != 0, has_bonus != 0, per_block_dec, per_block_res,
-                            resident, &tg))
+    if (!sv::plan_task_grid(batch, dec_items, chunks, has_resid != 0, has_bonus != 0, per_block_dec, per_block_bonus,
+                            per_block_res, resident, &tg))
         return -1;
     params[0] = tg.w_dec;
     params[1] = tg.w_res;

@@ -26,7 +26,7 @@ def probe(tmp_path_factory):
                            "-o", out])
     lib = ctypes.CDLL(out)
     i32, i64, p32 = ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
-    lib.probe_plan.argtypes = [i32, i64, i64, i32, i32, i64, i64, i64, p32]
+    lib.probe_plan.argtypes = [i32, i64, i64, i32, i32, i64, i64, i64, i64, p32]
     lib.probe_plan.restype = i32
     lib.probe_decode.argtypes = [i32] * 10 + [p32, p32, p32, i32]
     lib.probe_decode.restype = i32
@@ -98,12 +98,13 @@ def test_planned_grids_of_the_workloads(probe, name, B, k, V, eb, T, onehot, vat
     has_resid = (not vat) and T != 0.0 and not onehot
     has_bonus = not vat
     params = np.zeros(8, np.int32)
-    for per_dec, per_res in ((4, 4), (8, 4), (16, 8)):
-        n = probe.probe_plan(B, dec_rows * chunks, chunks, int(has_resid), int(has_bonus), per_dec, per_res, 1280,
-                             params.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    for per_dec, per_bonus, per_res in ((4, 4, 4), (8, 4, 4), (8, 8, 4), (16, 8, 8)):
+        n = probe.probe_plan(B, dec_rows * chunks, chunks, int(has_resid), int(has_bonus), per_dec, per_bonus,
+                             per_res, 1280, params.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
         assert n > 0
         w_dec, w_res, w_bonus, la, lr, lf, lb, nseg = params.tolist()
         assert w_dec == -(-dec_rows * chunks // per_dec)
+        assert w_bonus == (-(-chunks // per_bonus) if has_bonus else 0)
         assert 1 <= nseg <= 12
         assert all(0 <= x <= B for x in (la, lr, lf, lb))
         kind, seq, idx = decode(probe, B, w_dec, w_res, w_bonus, has_resid, has_bonus, la, lr, lf, lb,
