@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for batched speculative-sampling verification and VAT labels.
+"""fp64 CPU oracle for batched speculative-sampling verification, VAT labels and
+the VAT training loss.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
 bench's CPU-baseline leg are its only callers.  The product path never imports
@@ -70,6 +71,9 @@ def _load():
     lib.orc_vat.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_double, c.c_double,
                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_vat.restype = c.c_int
+    lib.orc_vat_loss.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_double, c.c_double, c.c_double,
+                                 vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.orc_vat_loss.restype = c.c_int
     _lib = lib
     return lib
 
@@ -191,7 +195,7 @@ def verify(target, draft, tokens, uniforms, temperature: float, onehot: bool = F
 
 class VatResult:
     __slots__ = ("accept_mask", "first_reject", "weights", "probs", "target_mz", "draft_mz",
-                 "accept_margin")
+                 "accept_margin", "soft", "hard", "block_loss")
 
     def __init__(self, **kw):
         for k, v in kw.items():
@@ -224,3 +228,32 @@ def vat_labels(target, draft, tokens, uniforms, temperature: float, decay: float
         raise ValueError("orc_vat rejected its arguments")
     return VatResult(accept_mask=mask, first_reject=fr, weights=w, probs=probs, target_mz=tmz,
                      draft_mz=dmz, accept_margin=am)
+
+
+def vat_loss(target, draft, tokens, uniforms, hard_tokens, temperature: float, decay: float,
+             hard_weight: float = 1.0) -> VatResult:
+    """VAT labels plus the weighted training loss of each block: soft term
+    -sum p ln q, hard term -ln q(h), block loss sum_i w_i (soft_i +
+    hard_weight * hard_i).  target/draft: [N][k][V]; tokens, uniforms,
+    hard_tokens: [N][k]; temperature > 0."""
+    lib = _load()
+    t, dt = _logits_arg(target)
+    N, k, V = t.shape
+    d, dd = _logits_arg(draft)
+    assert dd == dt and d.shape == (N, k, V)
+    x = np.ascontiguousarray(tokens, dtype=np.int32)
+    h = np.ascontiguousarray(hard_tokens, dtype=np.int32)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    assert x.shape == (N, k) and h.shape == (N, k) and u.shape == (N, k)
+    mask = np.empty((N, k), np.uint8)
+    fr = np.empty(N, np.int32)
+    w = np.empty((N, k), np.float64)
+    soft = np.empty((N, k), np.float64)
+    hard = np.empty((N, k), np.float64)
+    loss = np.empty(N, np.float64)
+    rc = lib.orc_vat_loss(N, k, V, dt, float(temperature), float(decay), float(hard_weight), _ptr(t), _ptr(d),
+                          _ptr(x), _ptr(u), _ptr(h), _ptr(mask), _ptr(fr), _ptr(w), _ptr(soft), _ptr(hard),
+                          _ptr(loss))
+    if rc != 0:
+        raise ValueError("orc_vat_loss rejected its arguments")
+    return VatResult(accept_mask=mask, first_reject=fr, weights=w, soft=soft, hard=hard, block_loss=loss)

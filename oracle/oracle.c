@@ -31,7 +31,10 @@
  *        labelled as rejected.
  *  [VAT2] same page, section "第二件事，改权重分配的锚点": positions before the
  *        first rejection get full weight; the usual decay curve (EAGLE-3: 0.8
- *        to the power position-1) restarts at the first rejection.
+ *        to the power position-1) restarts at the first rejection.  The end of
+ *        that section: the drafter's loss combines soft-label distillation
+ *        from the target's output distribution with hard-label supervision
+ *        from the token the target actually sampled.
  *
  * Readings where the pages leave a step open (each also listed in the design
  * notes of the repository):
@@ -54,6 +57,14 @@
  *    out_tokens all -1;
  *  - VAT weight at the rejected position itself is decay^0 = 1; no rejection
  *    gives first_reject = k and all weights 1.
+ *  - VAT loss (orc_vat_loss): at every position the soft term is the cross
+ *    entropy of the draft's distribution against the target's at the same
+ *    temperature, -sum_y p(y) ln q(y); the hard term is -ln q(h) for the
+ *    target's sampled token h; the block's loss is
+ *    sum_i w_i (soft_i + hard_weight * hard_i) with the VAT weights w_i.
+ *    Natural logarithms (nats).  T must be > 0 (both distributions are
+ *    needed).  A block with a draft or hard token outside [0,V) is flagged:
+ *    first_reject -1, mask 0, weights 0, soft/hard/loss NaN.
  */
 #include <math.h>
 #include <stdint.h>
@@ -424,6 +435,62 @@ int orc_vat(int64_t N, int32_t k, int64_t V, int32_t dtype, double T, double dec
             mask[n * k + i] = (uint8_t)(i < r);
             weights[n * k + i] = i < r ? 1.0 : pow(decay, (double)(i - r));
         }
+    }
+    free(lt); free(ld); free(p); free(q);
+    return 0;
+}
+
+/* VAT training loss of each block [VAT2]: the labels and weights of orc_vat,
+ * then per position the soft term -sum_y p(y) ln q(y) and the hard term
+ * -ln q(h_i), and the weighted block loss.  p, q: softmax at temperature T. */
+int orc_vat_loss(int64_t N, int32_t k, int64_t V, int32_t dtype, double T, double decay, double hard_weight,
+                 const void* target, const void* draft, const int32_t* tokens, const float* u,
+                 const int32_t* hard_tokens, uint8_t* mask, int32_t* first_reject, double* weights,
+                 double* soft, double* hard, double* block_loss) {
+    int64_t n, y;
+    int32_t i;
+    double *lt, *ld, *p, *q;
+    if (N < 0 || k < 1 || V < 1 || !(T > 0.0) || !(decay == decay) || !(hard_weight == hard_weight)) return -1;
+    if (!target || !draft || !tokens || !u || !hard_tokens || !soft || !hard || !block_loss) return -1;
+    if (orc_vat(N, k, V, dtype, T, decay, target, draft, tokens, u, mask, first_reject, weights, 0, 0, 0, 0))
+        return -1;
+    lt = (double*)malloc(sizeof(double) * V);
+    ld = (double*)malloc(sizeof(double) * V);
+    p = (double*)malloc(sizeof(double) * V);
+    q = (double*)malloc(sizeof(double) * V);
+    if (!lt || !ld || !p || !q) {
+        free(lt); free(ld); free(p); free(q);
+        return -1;
+    }
+    for (n = 0; n < N; ++n) {
+        const int32_t* h = hard_tokens + n * k;
+        double total = 0.0;
+        if (first_reject[n] < 0 || !tokens_valid(h, k, V)) {
+            first_reject[n] = -1;
+            for (i = 0; i < k; ++i) {
+                mask[n * k + i] = 0;
+                weights[n * k + i] = 0.0;
+                soft[n * k + i] = NAN;
+                hard[n * k + i] = NAN;
+            }
+            block_loss[n] = NAN;
+            continue;
+        }
+        for (i = 0; i < k; ++i) {
+            double mt, zt, md, zd, ce = 0.0;
+            load_row(target, dtype, n * k + i, V, lt);
+            load_row(draft, dtype, n * k + i, V, ld);
+            orc_softmax(lt, V, T, p, &mt, &zt);
+            orc_softmax(ld, V, T, q, &md, &zd);
+            /* ln q(y) = l_d(y)/T - md - ln zd */
+            for (y = 0; y < V; ++y) {
+                if (p[y] > 0.0) ce -= p[y] * (ld[y] / T - md - log(zd));
+            }
+            soft[n * k + i] = ce;
+            hard[n * k + i] = -(ld[h[i]] / T - md - log(zd));
+            total += weights[n * k + i] * (ce + hard_weight * hard[n * k + i]);
+        }
+        block_loss[n] = total;
     }
     free(lt); free(ld); free(p); free(q);
     return 0;

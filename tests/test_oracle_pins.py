@@ -376,3 +376,110 @@ def test_vat_labels_follow_inference_rule(orc):
     g = orc.verify(lt, None, x, None, 0.0)
     tg = orc.vat_labels(np.ascontiguousarray(lt[:, :k]), None, x, None, 0.0, 0.8)
     np.testing.assert_array_equal(g.accepted_len, tg.first_reject)
+
+
+# ----------------------------------------------------------------- VAT loss
+
+def _pq_block(rng, N, k, V, s_t=2.0, s_d=0.7):
+    lt = (s_t * rng.standard_normal((N, k, V))).astype(np.float32)
+    ld = (lt + s_d * rng.standard_normal((N, k, V))).astype(np.float32)
+    x = rng.integers(0, V, (N, k)).astype(np.int32)
+    h = rng.integers(0, V, (N, k)).astype(np.int32)
+    u = rng.random((N, k), dtype=np.float32)
+    return lt, ld, x, u, h
+
+
+def test_vat_soft_term_with_identical_draft_is_the_target_entropy(orc):
+    """q = p: the soft term is the Shannon entropy of p (scipy's entropy, in nats)."""
+    rng = np.random.default_rng(50)
+    lt, _, x, u, h = _pq_block(rng, 3, 5, 64)
+    for T in (1.0, 0.7):
+        res = orc.vat_loss(lt, lt, x, u, h, T, 0.8)
+        for n in range(3):
+            for i in range(5):
+                p = special.softmax(lt[n, i].astype(np.float64) / T)
+                assert res.soft[n, i] == pytest.approx(stats.entropy(p), rel=1e-12)
+
+
+def test_vat_soft_term_is_entropy_plus_kl(orc):
+    """Gibbs: -sum p ln q = H(p) + KL(p||q) >= H(p), KL from scipy's rel_entr."""
+    rng = np.random.default_rng(51)
+    lt, ld, x, u, h = _pq_block(rng, 4, 6, 97)
+    T = 1.3
+    res = orc.vat_loss(lt, ld, x, u, h, T, 0.8)
+    for n in range(4):
+        for i in range(6):
+            p = special.softmax(lt[n, i].astype(np.float64) / T)
+            q = special.softmax(ld[n, i].astype(np.float64) / T)
+            kl = special.rel_entr(p, q).sum()
+            assert kl > 0
+            assert res.soft[n, i] == pytest.approx(stats.entropy(p) + kl, rel=1e-11)
+
+
+def test_vat_uniform_draft_gives_log_v(orc):
+    """A flat draft distribution costs ln V on both terms, whatever p is."""
+    rng = np.random.default_rng(52)
+    V = 1000
+    lt, _, x, u, h = _pq_block(rng, 2, 3, V)
+    ld = np.full_like(lt, 3.5)
+    res = orc.vat_loss(lt, ld, x, u, h, 1.0, 0.8)
+    assert np.allclose(res.soft, math.log(V), rtol=1e-13)
+    assert np.allclose(res.hard, math.log(V), rtol=1e-13)
+
+
+def test_vat_hard_term_is_log_softmax(orc):
+    rng = np.random.default_rng(53)
+    lt, ld, x, u, h = _pq_block(rng, 3, 4, 300)
+    T = 0.6
+    res = orc.vat_loss(lt, ld, x, u, h, T, 0.8)
+    for n in range(3):
+        for i in range(4):
+            ls = special.log_softmax(ld[n, i].astype(np.float64) / T)
+            assert res.hard[n, i] == pytest.approx(-ls[h[n, i]], rel=1e-12)
+
+
+def test_vat_block_loss_weights_follow_first_rejection(orc):
+    """Blocks built to reject first at r: the block loss is the first-rejection
+    weighted sum of the two terms (weights 1 before r, decay^(i-r) from r)."""
+    k, decay, lam = 7, 0.8, 0.5
+    rs = [0, 3, k]
+    lt, ld, x, u = _vat_inputs_with_reject_at(rs, k)
+    h = np.tile(np.arange(k, dtype=np.int32) % 4, (len(rs), 1))
+    res = orc.vat_loss(lt, ld, x, u, h, 1.0, decay, lam)
+    # the distributions of the stored (fp32) logits
+    p = special.softmax(lt[0, 0].astype(np.float64))
+    q = special.softmax(ld[0, 0].astype(np.float64))
+    soft = stats.entropy(p) + special.rel_entr(p, q).sum()
+    for n, r in enumerate(rs):
+        assert res.first_reject[n] == r
+        i = np.arange(k)
+        w = np.where(i < r, 1.0, decay ** np.maximum(i - r, 0))
+        want = sum(w[j] * (soft + lam * -math.log(q[h[n, j]])) for j in range(k))
+        assert res.block_loss[n] == pytest.approx(want, rel=1e-12)
+        assert np.allclose(res.soft[n], soft, rtol=1e-12)
+
+
+def test_vat_loss_temperature_scales_logits(orc):
+    """Logits times T at temperature T give the T = 1 losses."""
+    rng = np.random.default_rng(54)
+    lt, ld, x, u, h = _pq_block(rng, 2, 4, 120)
+    a = orc.vat_loss(lt.astype(np.float64).astype(np.float32), ld, x, u, h, 1.0, 0.8)
+    T = 2.0  # a power of two keeps the scaled fp32 logits exact
+    b = orc.vat_loss(lt * np.float32(T), ld * np.float32(T), x, u, h, T, 0.8)
+    assert np.allclose(a.soft, b.soft, rtol=1e-13)
+    assert np.allclose(a.hard, b.hard, rtol=1e-13)
+    assert np.array_equal(a.first_reject, b.first_reject)
+
+
+def test_vat_loss_labels_match_vat_labels_and_invalid_hard_token_flags(orc):
+    rng = np.random.default_rng(55)
+    lt, ld, x, u, h = _pq_block(rng, 5, 6, 50)
+    h[2, 4] = 50
+    res = orc.vat_loss(lt, ld, x, u, h, 1.0, 0.8)
+    lab = orc.vat_labels(lt, ld, x, u, 1.0, 0.8)
+    keep = np.arange(5) != 2
+    assert np.array_equal(res.first_reject[keep], lab.first_reject[keep])
+    assert np.array_equal(res.weights[keep], lab.weights[keep])
+    assert res.first_reject[2] == -1 and np.all(res.weights[2] == 0)
+    assert np.isnan(res.block_loss[2]) and np.all(np.isnan(res.soft[2]))
+    assert np.all(np.isfinite(res.block_loss[keep]))

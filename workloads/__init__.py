@@ -125,6 +125,7 @@ class Workload:
     draft: Optional[np.ndarray]   # [n][k][V] or None (one-hot)
     tokens: np.ndarray            # [n][k] int32
     uniforms: np.ndarray          # [n][k+1] (verify) or [n][k] (vat) float32
+    hard_tokens: Optional[np.ndarray] = None  # vat: [n][k] int32, the target's sampled tokens
 
     @property
     def n(self) -> int:
@@ -139,7 +140,7 @@ def _as_values(stored: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(stored) if stored.dtype == np.uint16 else stored
 
 
-def _one_sequence(cfg: Config, b: int, target_out, draft_out, tokens_out, u_out, i: int) -> None:
+def _one_sequence(cfg: Config, b: int, target_out, draft_out, tokens_out, u_out, i: int, hard_out=None) -> None:
     rows_t = cfg.target_rows_per_seq
     z = _rng(cfg.seed_logits, 0, b).standard_normal((rows_t, cfg.V), dtype=np.float32)
     t = (np.float32(cfg.sigma_t) * z).astype(np.float32)
@@ -169,6 +170,11 @@ def _one_sequence(cfg: Config, b: int, target_out, draft_out, tokens_out, u_out,
     else:
         raise ValueError(cfg.draft_mode)
     u_out[i] = _rng(cfg.seed_u, b).random(cfg.n_uniforms, dtype=np.float32)
+    if hard_out is not None:
+        # the target's own sample at each position (exponential race at T)
+        tv = _as_values(t_st).astype(np.float64)[: cfg.k]
+        e = _rng(cfg.seed_draft + 1, b).standard_exponential((cfg.k, cfg.V))
+        hard_out[i] = np.argmax(tv / cfg.T - np.log(e), axis=1)
 
 
 def generate(cfg: Config, lo: int = 0, hi: Optional[int] = None, workers: Optional[int] = None,
@@ -184,16 +190,17 @@ def generate(cfg: Config, lo: int = 0, hi: Optional[int] = None, workers: Option
         draft = np.empty((n, cfg.k, cfg.V), dtype=st_dtype)
     tokens = np.empty((n, cfg.k), dtype=np.int32)
     u = np.empty((n, cfg.n_uniforms), dtype=np.float32)
+    hard = np.empty((n, cfg.k), dtype=np.int32) if (cfg.kind == "vat" and cfg.T > 0) else None
     if workers is None:
         workers = max(1, min(16, os.cpu_count() or 1))
-    jobs = [(cfg, lo + i, target, draft, tokens, u, i) for i in range(n)]
+    jobs = [(cfg, lo + i, target, draft, tokens, u, i, hard) for i in range(n)]
     if workers == 1 or n <= 1:
         for j in jobs:
             _one_sequence(*j)
     else:
         with ThreadPoolExecutor(workers) as ex:
             list(ex.map(lambda j: _one_sequence(*j), jobs))
-    return Workload(cfg, lo, target, draft, tokens, u)
+    return Workload(cfg, lo, target, draft, tokens, u, hard)
 
 
 def generate_on_device(cfg: Config, device, slab: int = 64):
@@ -238,6 +245,24 @@ def generate_on_device(cfg: Config, device, slab: int = 64):
         uniforms[s0:s1] = torch.rand((s1 - s0, cfg.n_uniforms), generator=g, device=device, dtype=torch.float32)
         del t
     return target, draft, tokens, uniforms
+
+
+def hard_tokens_on_device(cfg: Config, target, device, slab: int = 64):
+    """The target's own sample at each position of device-generated VAT
+    blocks (exponential race at T over the stored logits), drawn by torch's
+    generator per slab of `slab` blocks."""
+    import torch
+
+    hard = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device=device)
+    for s0 in range(0, cfg.B, slab):
+        s1 = min(cfg.B, s0 + slab)
+        g = torch.Generator(device=device)
+        g.manual_seed(int(cfg.seed_logits) * 1_000_003 + 500_000 + s0 // slab)
+        tv = target[s0:s1, : cfg.k].double()
+        e = torch.empty(tv.shape, dtype=torch.float64, device=device).exponential_(generator=g)
+        hard[s0:s1] = torch.argmax(tv / cfg.T - torch.log(e), dim=2).to(torch.int32)
+        del tv, e
+    return hard
 
 
 def to_device(wl: Workload, device):
