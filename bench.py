@@ -2,7 +2,8 @@
 
     python bench.py [--steps K] [--warmup W] [--workload selfdraft] [--gpus 1]
 
-One step = one sv_verify call (sv_vat_labels for --workload vat) over one
+One step = one sv_verify call (sv_vat_labels for --workload vat, sv_vat_loss
+for --workload vat_loss) over one
 batch of synthetic logits already resident in HBM; the call is the whole path
 (one launch of the task-grid kernel k_verify).  The default workload is the
 quantized-self-drafter batch: B=128 sequences, k=5 draft positions,
@@ -114,7 +115,7 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, seconds: float):
+def cpu_baseline(cfg, seconds: float, loss: bool = False):
     """The oracle as it is (plain fp64 C, one thread) over whole sequences (VAT:
     blocks) of the same workload until `seconds` of CPU work have elapsed; the
     sample is drawn on the host by the same seeded generator."""
@@ -130,7 +131,10 @@ def cpu_baseline(cfg, seconds: float):
         lo = done % n_sample
         hi = min(n_sample, lo + step)
         d = wl.draft[lo:hi] if wl.draft is not None else None
-        if cfg.kind == "vat":
+        if loss:
+            oracle.vat_loss(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], wl.hard_tokens[lo:hi],
+                            cfg.T, cfg.decay, 1.0)
+        elif cfg.kind == "vat":
             oracle.vat_labels(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, cfg.decay)
         else:
             oracle.verify(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, onehot=cfg.onehot)
@@ -139,6 +143,8 @@ def cpu_baseline(cfg, seconds: float):
             break
     dt = time.perf_counter() - t0
     what = "blocks" if cfg.kind == "vat" else "sequences"
+    if loss:
+        what = "blocks (labels and loss)"
     return {"value": done * cfg.k / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
             "sample": "%d whole %s (%d positions; cycling over the first %d) of the %s workload, fp64 C oracle, "
                       "1 thread, %.1f s" % (done, what, done * cfg.k, n_sample, cfg.name, dt),
@@ -164,10 +170,14 @@ def copy_probe(steps: int) -> int:
     return 0
 
 
-def _launchers(cfg, sets, sv, n):
+def _launchers(cfg, sets, sv, n, loss=False):
     """One prepared call per resident input copy (they rotate)."""
     out = []
     for i in range(n):
+        if loss:
+            t, d, x, u, h = sets[i % len(sets)]
+            out.append(sv.VatLoss(t, d, x, u, h, cfg.T, cfg.decay, 1.0))
+            continue
         t, d, x, u = sets[i % len(sets)]
         if cfg.kind == "vat":
             out.append(sv.VatLabeler(t, d, x, u, cfg.T, cfg.decay))
@@ -182,7 +192,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="selfdraft",
-                    choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "tiny"])
+                    choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "vat_loss", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -205,7 +215,8 @@ def main(argv=None):
     import workloads
 
     dev = torch.device("cuda:0")
-    cfg = workloads.get_config(args.workload)
+    loss = args.workload == "vat_loss"
+    cfg = workloads.get_config("vat" if loss else args.workload)
     print("bench: generating %s (B=%d k=%d V=%d %s T=%g)" % (cfg.name, cfg.B, cfg.k, cfg.V, cfg.dtype, cfg.T),
           file=sys.stderr, flush=True)
     in_bytes = cfg.algorithmic_bytes()
@@ -213,6 +224,8 @@ def main(argv=None):
     if cfg.kind == "vat":
         # 33.6 GB: drawn on the device (same distributions, torch's generator)
         sets = [workloads.generate_on_device(cfg, dev)]
+        if loss:
+            sets[0] = sets[0] + (workloads.hard_tokens_on_device(cfg, sets[0][0], dev),)
         for _ in range(copies - 1):
             sets.append(tuple(a.clone() for a in sets[0]))
     else:
@@ -221,7 +234,7 @@ def main(argv=None):
         del wl
     ev = HipEvents()
     n_launch = args.warmup + args.steps
-    calls = _launchers(cfg, sets, sv, len(sets))
+    calls = _launchers(cfg, sets, sv, len(sets), loss)
     stream = torch.cuda.current_stream(dev).cuda_stream
     region = (ev.create(), ev.create())
 
@@ -250,6 +263,8 @@ def main(argv=None):
     if cfg.kind == "vat":
         fr = last.first_reject.float()
         extra = {"mean_first_reject": fr.mean().item(), "timeouts": int((fr == -2).sum().item())}
+        if loss:
+            extra["mean_block_loss"] = last.block_loss.float().mean().item()
         needed = in_bytes
     else:
         acc = last.accepted_len.float()
@@ -278,22 +293,24 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
+        "config": {"workload": args.workload, "batch": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
                    "logits": cfg.dtype, "temperature": cfg.T, "draft": "one-hot" if cfg.onehot else "logits",
                    "input_copies_rotated": copies},
         "hbm_gbps_whole_step": needed / (ms_per_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(kernel, cfg.name),
+                     "traffic": measured_traffic(kernel, args.workload),
                      "algorithmic_bytes_per_launch": needed, "all_rows_bytes_per_launch": in_bytes,
                      "mean_launch_us": k1_mean * 1e3},
     }
     res.update(extra)
     if cfg.kind == "vat":
         res["config"]["decay"] = cfg.decay
+    if loss:
+        res["config"]["hard_weight"] = 1.0
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, loss)
     print(json.dumps(res), flush=True)
     return 0
 

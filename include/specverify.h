@@ -28,6 +28,17 @@
  *                 before the first rejection r get weight 1 and the decay
  *                 curve restarts at r (weight decay^(i-r) for i >= r).
  *
+ *  sv_vat_loss -- the same page and sections, with the end of section
+ *                 "第二件事，改权重分配的锚点": the drafter's training loss
+ *                 combines soft-label distillation from the target's output
+ *                 distribution with hard-label supervision from the token the
+ *                 target actually sampled.  Per position: soft term
+ *                 -sum_y p(y) ln q(y) (cross entropy of the draft against the
+ *                 target), hard term -ln q(h); per block:
+ *                 sum_i w_i (soft_i + hard_weight * hard_i) with the VAT
+ *                 weights w_i.  Labels, weights and losses come from one pass
+ *                 over the logits.
+ *
  * Readings this library takes where the pages leave a step open:
  *  - p = softmax(target_logits / T), q = softmax(draft_logits / T), one T;
  *  - acceptance: x_i is kept iff u[b][i] * q_i(x_i) < p_i(x_i);
@@ -84,7 +95,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 1
+#define SV_ABI_VERSION 2
 #define SV_MAX_DRAFT 64 /* k is limited to one 64-lane wavefront */
 
 typedef enum sv_status {
@@ -96,7 +107,8 @@ typedef enum sv_status {
     SV_ERR_BAD_DRAFT_KIND = 5,    /* draft_kind not SV_DRAFT_LOGITS / SV_DRAFT_ONEHOT */
     SV_ERR_WORKSPACE_TOO_SMALL = 6,
     SV_ERR_BAD_DECAY = 7,         /* VAT decay not in [0, 1] */
-    SV_ERR_HIP = 8                /* a kernel launch or event record failed */
+    SV_ERR_HIP = 8,               /* a kernel launch or event record failed */
+    SV_ERR_BAD_HARD_WEIGHT = 9    /* VAT loss hard_weight not finite and >= 0 */
 } sv_status;
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -106,7 +118,7 @@ typedef enum sv_draft_kind { SV_DRAFT_LOGITS = 0, SV_DRAFT_ONEHOT = 1 } sv_draft
 /* Shape and options of one sv_verify call.
  * probe_start / probe_stop: optional instrumentation (NULL to skip).  When both
  * are non-NULL they are recorded on `stream` immediately before and after the
- * row-statistics kernel, the kernel that streams the logits. */
+ * call's single kernel launch. */
 typedef struct sv_verify_desc {
     int32_t batch;       /* B >= 0 sequences (0: nothing to do) */
     int32_t num_draft;   /* k in [1, 64] */
@@ -129,6 +141,19 @@ typedef struct sv_vat_desc {
     hipEvent_t probe_start;
     hipEvent_t probe_stop;
 } sv_vat_desc;
+
+/* Shape and options of one sv_vat_loss call (probe events as above). */
+typedef struct sv_vat_loss_desc {
+    int32_t blocks;      /* N >= 0 draft blocks */
+    int32_t num_draft;   /* k in [1, 64] positions per block */
+    int32_t vocab;       /* V >= 1 */
+    int32_t dtype;       /* sv_dtype */
+    float temperature;   /* T: finite >= 1e-4 (both distributions are needed) */
+    float decay;         /* as for sv_vat_desc, in [0,1] */
+    float hard_weight;   /* weight of the hard-label term, finite >= 0 */
+    hipEvent_t probe_start;
+    hipEvent_t probe_stop;
+} sv_vat_loss_desc;
 
 /* Returns SV_ABI_VERSION of the built library. */
 int sv_abi_version(void);
@@ -202,6 +227,41 @@ sv_status sv_vat_labels(const sv_vat_desc* desc, const void* target_logits, cons
                         const int32_t* draft_tokens, const float* uniforms, uint8_t* accept_mask,
                         int32_t* first_reject, float* weights, float* probs_out, float* row_stats_out,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes sv_vat_loss needs for `desc`.  Errors as for
+ * sv_vat_workspace_size (T == 0 is SV_ERR_BAD_TEMPERATURE here), plus
+ * SV_ERR_BAD_HARD_WEIGHT. */
+sv_status sv_vat_loss_workspace_size(const sv_vat_loss_desc* desc, size_t* bytes);
+
+/*
+ * VAT labels, weights and the weighted training loss in one pass.  Source:
+ * VAT write-up, sections "VAT怎么把“验收规则”塞进训练里" and
+ * "第二件事，改权重分配的锚点" (labels, weights; soft plus hard labels).
+ *
+ *  target_logits, draft_logits  device, [N][k][V] dtype (both required)
+ *  draft_tokens   device, [N][k] int32: the draft's proposals (simulated test)
+ *  uniforms       device, [N][k] float32 in [0,1)
+ *  hard_tokens    device, [N][k] int32: the target's sampled token at each
+ *                 position (the hard label), expected in [0, V)
+ *  accept_mask, first_reject, weights: as for sv_vat_labels
+ *  soft_ce        device out, [N][k] float32: -sum_y p_i(y) ln q_i(y) (nats)
+ *  hard_ce        device out, [N][k] float32: -ln q_i(h_i)
+ *  block_loss     device out, [N] float32: sum_i w_i (soft_i + hard_weight hard_i)
+ *  probs_out      device out or NULL, [N][k][2] float32 (p_i(x_i), q_i(x_i))
+ *  row_stats_out  device out or NULL, [N k + N k][2] float32, as for sv_vat_labels
+ *  workspace, workspace_bytes, stream: as for sv_verify
+ *
+ * A block holding a draft or hard token outside [0, V) gets first_reject -1,
+ * mask 0, weights 0 and NaN losses.  Draft logits of -inf where the target
+ * has positive mass make the exact soft or hard term +inf; the returned
+ * value is then unspecified.
+ * Errors as for sv_vat_labels, plus SV_ERR_BAD_HARD_WEIGHT.
+ */
+sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms, const int32_t* hard_tokens,
+                      uint8_t* accept_mask, int32_t* first_reject, float* weights, float* soft_ce, float* hard_ce,
+                      float* block_loss, float* probs_out, float* row_stats_out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

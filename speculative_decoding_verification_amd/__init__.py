@@ -9,7 +9,8 @@ library is not built, importing works but every call raises.
     acc, out = verify(target, draft, tokens, uniforms, temperature=1.0)
 
 Names follow the C ABI in ``include/specverify.h``: ``sv_verify`` ->
-:func:`verify`, ``sv_vat_labels`` -> :func:`vat_labels`.
+:func:`verify`, ``sv_vat_labels`` -> :func:`vat_labels`, ``sv_vat_loss`` ->
+:func:`vat_loss`.
 """
 from __future__ import annotations
 
@@ -17,8 +18,8 @@ import ctypes
 import os
 from typing import NamedTuple, Optional
 
-__all__ = ["verify", "vat_labels", "Verifier", "VatLabeler", "SVError", "library_path", "load_library",
-           "SV_F32", "SV_BF16", "SV_DRAFT_LOGITS", "SV_DRAFT_ONEHOT", "STATUS"]
+__all__ = ["verify", "vat_labels", "vat_loss", "Verifier", "VatLabeler", "VatLoss", "SVError", "library_path",
+           "load_library", "SV_F32", "SV_BF16", "SV_DRAFT_LOGITS", "SV_DRAFT_ONEHOT", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspecverify.so")
@@ -27,10 +28,10 @@ SV_F32, SV_BF16 = 0, 1
 SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT = 0, 1
 STATUS = {0: "SV_OK", 1: "SV_ERR_NULL_ARG", 2: "SV_ERR_BAD_SHAPE", 3: "SV_ERR_BAD_DTYPE",
           4: "SV_ERR_BAD_TEMPERATURE", 5: "SV_ERR_BAD_DRAFT_KIND", 6: "SV_ERR_WORKSPACE_TOO_SMALL",
-          7: "SV_ERR_BAD_DECAY", 8: "SV_ERR_HIP"}
+          7: "SV_ERR_BAD_DECAY", 8: "SV_ERR_HIP", 9: "SV_ERR_BAD_HARD_WEIGHT"}
 
 EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_size", "sv_verify",
-                    "sv_vat_workspace_size", "sv_vat_labels")
+                    "sv_vat_workspace_size", "sv_vat_labels", "sv_vat_loss_workspace_size", "sv_vat_loss")
 
 
 class SVError(RuntimeError):
@@ -52,6 +53,12 @@ class VatDesc(ctypes.Structure):
     _fields_ = [("blocks", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float), ("decay", ctypes.c_float),
                 ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+
+
+class VatLossDesc(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float), ("decay", ctypes.c_float),
+                ("hard_weight", ctypes.c_float), ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
 
 
 _lib = None
@@ -83,6 +90,10 @@ def load_library():
     lib.sv_vat_workspace_size.argtypes = [ctypes.POINTER(VatDesc), ctypes.POINTER(sz)]
     lib.sv_vat_labels.restype = ctypes.c_int
     lib.sv_vat_labels.argtypes = [ctypes.POINTER(VatDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sv_vat_loss_workspace_size.restype = ctypes.c_int
+    lib.sv_vat_loss_workspace_size.argtypes = [ctypes.POINTER(VatLossDesc), ctypes.POINTER(sz)]
+    lib.sv_vat_loss.restype = ctypes.c_int
+    lib.sv_vat_loss.argtypes = [ctypes.POINTER(VatLossDesc)] + [vp] * 14 + [sz, vp]
     _lib = lib
     return lib
 
@@ -288,3 +299,78 @@ def vat_labels(target, draft, draft_tokens, uniforms, temperature: float, decay:
     """sv_vat_labels on torch tensors: target/draft [N][k][V], tokens/uniforms [N][k]."""
     return VatLabeler(target, draft, draft_tokens, uniforms, temperature, decay, return_probs=return_probs,
                       return_row_stats=return_row_stats, workspace=workspace)()
+
+
+class VatLossOutput(NamedTuple):
+    accept_mask: "object"
+    first_reject: "object"
+    weights: "object"
+    soft_ce: "object"
+    hard_ce: "object"
+    block_loss: "object"
+    probs: "object"
+    row_stats: "object"
+
+
+class VatLoss:
+    """A prepared sv_vat_loss call (see :class:`Verifier`)."""
+
+    def __init__(self, target, draft, draft_tokens, uniforms, hard_tokens, temperature: float, decay: float = 0.8,
+                 hard_weight: float = 1.0, *, return_probs: bool = False, return_row_stats: bool = False,
+                 workspace=None, probe=None):
+        torch = _torch()
+        lib = load_library()
+        if target.dim() != 3:
+            raise ValueError("target must be [N][k][V]")
+        N, k, V = (int(s) for s in target.shape)
+        device = target.device
+        dt = _dtype_code(target)
+        _check_dev("target", target, device)
+        _check_dev("draft", draft, device, target.dtype, (N, k, V))
+        _check_dev("draft_tokens", draft_tokens, device, torch.int32, (N, k))
+        _check_dev("uniforms", uniforms, device, torch.float32, (N, k))
+        _check_dev("hard_tokens", hard_tokens, device, torch.int32, (N, k))
+        self.desc = VatLossDesc(N, k, V, dt, float(temperature), float(decay), float(hard_weight), None, None)
+        if probe is not None:
+            self.desc.probe_start, self.desc.probe_stop = probe
+        nbytes = ctypes.c_size_t()
+        st = lib.sv_vat_loss_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
+        if st:
+            raise SVError(st, "sv_vat_loss_workspace_size", lib)
+        if workspace is None:
+            workspace = _WS.get(device, nbytes.value)
+        elif workspace.numel() * workspace.element_size() < nbytes.value:
+            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+        self.accept_mask = torch.empty((N, k), dtype=torch.uint8, device=device)
+        self.first_reject = torch.empty(N, dtype=torch.int32, device=device)
+        self.weights = torch.empty((N, k), dtype=torch.float32, device=device)
+        self.soft_ce = torch.empty((N, k), dtype=torch.float32, device=device)
+        self.hard_ce = torch.empty((N, k), dtype=torch.float32, device=device)
+        self.block_loss = torch.empty(N, dtype=torch.float32, device=device)
+        self.probs = torch.empty((N, k, 2), dtype=torch.float32, device=device) if return_probs else None
+        self.row_stats = (torch.empty((2 * N * k, 2), dtype=torch.float32, device=device)
+                          if return_row_stats else None)
+        self._keep = (target, draft, draft_tokens, uniforms, hard_tokens, workspace)
+        self._lib = lib
+        self._device = device
+        self._args = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                      _ptr(hard_tokens), _ptr(self.accept_mask), _ptr(self.first_reject), _ptr(self.weights),
+                      _ptr(self.soft_ce), _ptr(self.hard_ce), _ptr(self.block_loss), _ptr(self.probs),
+                      _ptr(self.row_stats), workspace.data_ptr(), workspace.numel() * workspace.element_size())
+
+    def __call__(self, stream: Optional[int] = None) -> VatLossOutput:
+        s = _stream_handle(self._device) if stream is None else stream
+        st = self._lib.sv_vat_loss(*self._args, s)
+        if st:
+            raise SVError(st, "sv_vat_loss", self._lib)
+        return VatLossOutput(self.accept_mask, self.first_reject, self.weights, self.soft_ce, self.hard_ce,
+                             self.block_loss, self.probs, self.row_stats)
+
+
+def vat_loss(target, draft, draft_tokens, uniforms, hard_tokens, temperature: float, decay: float = 0.8,
+             hard_weight: float = 1.0, *, return_probs: bool = False, return_row_stats: bool = False,
+             workspace=None) -> VatLossOutput:
+    """sv_vat_loss on torch tensors: target/draft [N][k][V]; draft tokens, uniforms and hard tokens [N][k].
+    Labels, weights, the soft and hard terms per position and the weighted loss per block."""
+    return VatLoss(target, draft, draft_tokens, uniforms, hard_tokens, temperature, decay, hard_weight,
+                   return_probs=return_probs, return_row_stats=return_row_stats, workspace=workspace)()

@@ -39,6 +39,7 @@ struct Shape {
     int64_t rows_t, rows_d;
     int64_t chunk, chunks;
     bool greedy, onehot, vat;
+    bool loss;  // VAT with the training loss
 };
 
 // Shared checks of both entry points.  `draft_kind` is SV_DRAFT_LOGITS for VAT.
@@ -55,6 +56,7 @@ sv_status check_shape(int32_t batch, int32_t k, int32_t vocab, int32_t dtype, in
     s->greedy = temperature == 0.f;
     s->onehot = draft_kind == SV_DRAFT_ONEHOT;
     s->vat = vat;
+    s->loss = false;
     s->target_rows_per_seq = vat ? k : k + 1;
     s->rows_t = s->batch * s->target_rows_per_seq;
     s->rows_d = (s->greedy || s->onehot) ? 0 : s->batch * k;
@@ -66,8 +68,14 @@ sv_status check_shape(int32_t batch, int32_t k, int32_t vocab, int32_t dtype, in
     return SV_OK;
 }
 
+// Tagged words of chunk partials: two per row chunk, or five per chunk pair
+// for the VAT loss.
+int64_t partial_words(const Shape& s) {
+    return s.loss ? s.batch * s.k * s.chunks * kPairWords : (s.rows_t + s.rows_d) * s.chunks * 2;
+}
+
 size_t workspace_bytes_for(const Shape& s) {
-    return workspace_layout(s.rows_t + s.rows_d, s.batch, s.chunks).total;
+    return workspace_layout(partial_words(s), s.batch, s.chunks).total;
 }
 
 bool fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
@@ -78,10 +86,13 @@ bool fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
     pl->target_rows_per_seq = static_cast<int32_t>(s.target_rows_per_seq);
     pl->chunks = static_cast<int32_t>(s.chunks);
     pl->chunk = static_cast<int32_t>(s.chunk);
-    pl->dec_rows = static_cast<int32_t>(s.k + (s.rows_d ? s.k : 0));
+    // The VAT loss streams k chunk-pair "rows" (target row i with draft row i).
+    pl->dec_rows = static_cast<int32_t>(s.loss ? s.k : s.k + (s.rows_d ? s.k : 0));
     pl->has_bonus = !s.vat;
     pl->has_resid = !s.vat && !s.greedy && !s.onehot;
     pl->rows_per_seq = pl->dec_rows + (pl->has_bonus ? 1 : 0);
+    pl->vat_loss = s.loss;
+    pl->words_per_seq = static_cast<int32_t>(s.loss ? s.k * s.chunks * kPairWords : pl->rows_per_seq * s.chunks * 2);
     pl->nc_dec = s.batch * pl->dec_rows * s.chunks <= kSmallCallChunks ? kChunksPerWaveSmall : kChunksPerWave;
     pl->nc_res = kChunksPerWaveResid;
     pl->nc_bonus = std::min(pl->nc_dec, kChunksPerWaveBonus);
@@ -101,7 +112,7 @@ bool fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
 }
 
 void carve_workspace(const Shape& s, void* ws, Plan* pl) {
-    const WorkspaceLayout L = workspace_layout(s.rows_t + s.rows_d, s.batch, s.chunks);
+    const WorkspaceLayout L = workspace_layout(partial_words(s), s.batch, s.chunks);
     char* base = static_cast<char*>(ws);
     pl->partials = reinterpret_cast<uint64_t*>(base + L.partials);
     pl->resid = reinterpret_cast<uint64_t*>(base + L.resid);
@@ -111,11 +122,11 @@ void carve_workspace(const Shape& s, void* ws, Plan* pl) {
 
 }  // namespace
 
-WorkspaceLayout workspace_layout(int64_t rows, int64_t batch, int64_t chunks) {
+WorkspaceLayout workspace_layout(int64_t partial_words, int64_t batch, int64_t chunks) {
     WorkspaceLayout L;
     size_t off = 0;
     L.partials = off;
-    off = align_up(off + static_cast<size_t>(rows * chunks) * 2 * sizeof(uint64_t));
+    off = align_up(off + static_cast<size_t>(partial_words) * sizeof(uint64_t));
     L.resid = off;
     off = align_up(off + static_cast<size_t>(batch * chunks) * sizeof(uint64_t));
     L.dec = off;
@@ -138,6 +149,7 @@ const char* sv_status_str(int status) {
         case SV_ERR_BAD_DTYPE: return "SV_ERR_BAD_DTYPE: dtype must be SV_F32 or SV_BF16";
         case SV_ERR_BAD_TEMPERATURE: return "SV_ERR_BAD_TEMPERATURE: temperature must be 0 or finite and >= 1e-4";
         case SV_ERR_BAD_DRAFT_KIND: return "SV_ERR_BAD_DRAFT_KIND: draft_kind must be SV_DRAFT_LOGITS or SV_DRAFT_ONEHOT";
+        case SV_ERR_BAD_HARD_WEIGHT: return "SV_ERR_BAD_HARD_WEIGHT: hard_weight must be finite and >= 0";
         case SV_ERR_WORKSPACE_TOO_SMALL: return "SV_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the size query";
         case SV_ERR_BAD_DECAY: return "SV_ERR_BAD_DECAY: decay must be in [0, 1]";
         case SV_ERR_HIP: return "SV_ERR_HIP: a HIP launch or event record failed";
@@ -230,6 +242,64 @@ sv_status sv_vat_labels(const sv_vat_desc* desc, const void* target_logits, cons
     pl.weights = weights;
     pl.probs_out = probs_out;
     pl.row_stats_out = row_stats_out;
+    sv::carve_workspace(s, workspace, &pl);
+    const hipError_t e = sv::launch_path(pl, stream, desc->probe_start, desc->probe_stop);
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status sv_vat_loss_workspace_size(const sv_vat_loss_desc* desc, size_t* bytes) {
+    if (!desc || !bytes) return SV_ERR_NULL_ARG;
+    sv::Shape s;
+    const sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
+                                         desc->temperature, true, &s);
+    if (st != SV_OK) return st;
+    if (s.greedy) return SV_ERR_BAD_TEMPERATURE;
+    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
+    if (!(desc->hard_weight >= 0.f && std::isfinite(desc->hard_weight))) return SV_ERR_BAD_HARD_WEIGHT;
+    s.loss = true;
+    *bytes = sv::workspace_bytes_for(s);
+    return SV_OK;
+}
+
+sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms, const int32_t* hard_tokens,
+                      uint8_t* accept_mask, int32_t* first_reject, float* weights, float* soft_ce, float* hard_ce,
+                      float* block_loss, float* probs_out, float* row_stats_out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    if (!desc) return SV_ERR_NULL_ARG;
+    sv::Shape s;
+    sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
+                                   desc->temperature, true, &s);
+    if (st != SV_OK) return st;
+    if (s.greedy) return SV_ERR_BAD_TEMPERATURE;
+    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
+    if (!(desc->hard_weight >= 0.f && std::isfinite(desc->hard_weight))) return SV_ERR_BAD_HARD_WEIGHT;
+    s.loss = true;
+    if (s.batch == 0) return SV_OK;
+    if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !hard_tokens || !accept_mask ||
+        !first_reject || !weights || !soft_ce || !hard_ce || !block_loss)
+        return SV_ERR_NULL_ARG;
+    const size_t need = sv::workspace_bytes_for(s);
+    if (!workspace) return SV_ERR_NULL_ARG;
+    if (workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
+
+    sv::Plan pl{};
+    if (!sv::fill_plan(s, desc->temperature, desc->decay, &pl)) return SV_ERR_BAD_SHAPE;
+    pl.vec = (s.vocab * s.elem_bytes) % 16 == 0 && sv::aligned16(target_logits) && sv::aligned16(draft_logits);
+    pl.target = target_logits;
+    pl.draft = draft_logits;
+    pl.tokens = draft_tokens;
+    pl.uniforms = uniforms;
+    pl.mask = accept_mask;
+    pl.first_reject = first_reject;
+    pl.weights = weights;
+    pl.probs_out = probs_out;
+    pl.row_stats_out = row_stats_out;
+    pl.hard_tokens = hard_tokens;
+    pl.hard_weight = desc->hard_weight;
+    pl.soft_ce = soft_ce;
+    pl.hard_ce = hard_ce;
+    pl.block_loss = block_loss;
     sv::carve_workspace(s, workspace, &pl);
     const hipError_t e = sv::launch_path(pl, stream, desc->probe_start, desc->probe_stop);
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;

@@ -48,6 +48,7 @@ namespace sv {
 namespace {
 
 constexpr int kMaxDraft = 64;
+constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -449,6 +450,7 @@ struct PartialSrc {
 struct TailShared {
     uint32_t stage[kStageWords];   // staged hand-off words
     float2 mz[2 * kMaxDraft + 1];  // (m, Z) or (max, argmax) of the sequence's rows
+    float xs[kMaxDraft];           // VAT loss: sum_y p(y) (l_d(y) - m_d) c2, times Z_t
     float wt[kWavesPerBlock];      // block scan scratch
     int vote[kWavesPerBlock];      // block_any scratch
     int wlast[kWavesPerBlock];     // per-wave last positive position (draws)
@@ -764,7 +766,7 @@ __device__ __forceinline__ int64_t global_row(const Plan& pl, int b, int j) {
 }
 
 __device__ __forceinline__ uint64_t* seq_words(const Plan& pl, int b) {
-    return pl.partials + static_cast<int64_t>(b) * pl.rows_per_seq * pl.chunks * 2;
+    return pl.partials + static_cast<int64_t>(b) * pl.words_per_seq;
 }
 
 // ------------------------------------------------------------------ workers
@@ -821,6 +823,153 @@ __device__ __forceinline__ float chunk_resid_mass(const char* rt, const char* rd
         }
     }
     return wave_sum(s);
+}
+
+// ------------------------------------------------------------------ VAT loss partials
+//
+// The loss needs, per position, the target's (m, Z), the draft's (m, Z) and
+// sum_y p(y) (l_d(y) - m_d) c2, the expectation under p of the draft's
+// log2-probability up to its normaliser.  A chunk pair contributes
+// (m_t, s_t, m_d, s_d, x) with x = sum_y 2^((l_t(y) - m_t) c2) (l_d(y) - m_d) c2
+// over its tokens; pairs merge by rescaling to the larger maxima.
+
+struct PairPart {
+    float mt, st;  // target: max raw logit, sum of 2^((l - mt) c2)
+    float md, sd;  // draft: the same
+    float x;       // cross term, <= 0, relative to (mt, md)
+};
+
+__device__ __forceinline__ PairPart pair_empty() { return PairPart{neg_inf(), 0.f, neg_inf(), 0.f, 0.f}; }
+
+// Commutative in its arguments bit for bit (sums of two terms, maxima), so a
+// DPP butterfly leaves the same value on both lanes of every exchange.
+__device__ __forceinline__ PairPart pair_merge(const PairPart& a, const PairPart& b, float c2) {
+    PairPart r;
+    r.mt = fmaxf(a.mt, b.mt);
+    r.md = fmaxf(a.md, b.md);
+    const float fa = a.st > 0.f ? exp2_hw((a.mt - r.mt) * c2) : 0.f;
+    const float fb = b.st > 0.f ? exp2_hw((b.mt - r.mt) * c2) : 0.f;
+    const float ga = a.sd > 0.f ? exp2_hw((a.md - r.md) * c2) : 0.f;
+    const float gb = b.sd > 0.f ? exp2_hw((b.md - r.md) * c2) : 0.f;
+    r.st = a.st * fa + b.st * fb;
+    r.sd = a.sd * ga + b.sd * gb;
+    const float xa = a.st > 0.f ? fa * fmaf((a.md - r.md) * c2, a.st, a.x) : 0.f;
+    const float xb = b.st > 0.f ? fb * fmaf((b.md - r.md) * c2, b.st, b.x) : 0.f;
+    r.x = xa + xb;
+    return r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ PairPart dpp_pair(const PairPart& v) {
+    return PairPart{dpp<CTRL>(v.mt, v.mt), dpp<CTRL>(v.st, v.st), dpp<CTRL>(v.md, v.md), dpp<CTRL>(v.sd, v.sd),
+                    dpp<CTRL>(v.x, v.x)};
+}
+
+__device__ __forceinline__ PairPart readlane_pair(const PairPart& v, int l) {
+    return PairPart{readlane(v.mt, l), readlane(v.st, l), readlane(v.md, l), readlane(v.sd, l), readlane(v.x, l)};
+}
+
+// Merge over the wave; the same bits on every lane.
+__device__ __forceinline__ PairPart wave_merge_pair(PairPart v, float c2) {
+    v = pair_merge(v, dpp_pair<kDppQuadSwap1>(v), c2);
+    v = pair_merge(v, dpp_pair<kDppQuadSwap2>(v), c2);
+    v = pair_merge(v, dpp_pair<kDppRowRor4>(v), c2);
+    v = pair_merge(v, dpp_pair<kDppRowRor8>(v), c2);
+    const PairPart lo = pair_merge(readlane_pair(v, 0), readlane_pair(v, 16), c2);
+    const PairPart hi = pair_merge(readlane_pair(v, 32), readlane_pair(v, 48), c2);
+    return pair_merge(lo, hi, c2);
+}
+
+// One lane's part of n target/draft logit pairs (fetched twice by `get`).
+template <typename Get>
+__device__ __forceinline__ PairPart lane_pair(int n, Get get, float c2) {
+    float mt = neg_inf(), md = neg_inf();
+#pragma unroll
+    for (int e = 0; e < n; ++e) {
+        const float2 v = get(e);
+        mt = fmaxf(mt, v.x);
+        md = fmaxf(md, v.y);
+    }
+    PairPart p{mt, 0.f, md, 0.f, 0.f};
+    float ct = 1.f, cd = 1.f;
+    const float mtc = mt != neg_inf() ? row_scale(mt, c2, ct) : 0.f;
+    const float mdc = md != neg_inf() ? row_scale(md, c2, cd) : 0.f;
+    float st = 0.f, sd = 0.f, x = 0.f;
+#pragma unroll
+    for (int e = 0; e < n; ++e) {
+        const float2 v = get(e);
+        const float w = mt != neg_inf() ? exp2_hw(fmaf(v.x, c2, -mtc)) : 0.f;
+        st += w;
+        if (w > 0.f) x = fmaf(w, (v.y - md) * c2, x);
+        sd += md != neg_inf() ? exp2_hw(fmaf(v.y, c2, -mdc)) : 0.f;
+    }
+    p.st = st * ct;
+    p.sd = sd * cd;
+    p.x = x * ct;
+    return p;
+}
+
+// Pair partials of chunk c of target row i and draft row i of block b,
+// published as five tagged words.  Whole wave.
+template <int EB, bool VEC>
+__device__ __forceinline__ void stream_pair(const Plan& pl, int b, int i, int c) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t V = pl.vocab;
+    const char* rt = row_base(pl.target, static_cast<int64_t>(b) * pl.k + i, V, EB);
+    const char* rd = row_base(pl.draft, static_cast<int64_t>(b) * pl.k + i, V, EB);
+    const int64_t start = static_cast<int64_t>(c) * Chunk<EB>::kElems;
+    const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), V - start));
+    const float c2 = pl.c2;
+    PairPart acc = pair_empty();
+    if constexpr (VEC) {
+        // Two 16-byte vectors of each row per step keeps the decoded values
+        // of both rows within the register budget of the streaming loop.
+        constexpr int PV = Elem<EB>::kPerVec;
+        constexpr int kStep = 2;
+        const uint4* pt = reinterpret_cast<const uint4*>(rt + start * EB);
+        const uint4* pd = reinterpret_cast<const uint4*>(rd + start * EB);
+        const int nvec = len / PV;
+        const uint32_t ni = Elem<EB>::kNegInfWord;
+        uint4 at[kVecPerLane], ad[kVecPerLane];
+#pragma unroll
+        for (int j = 0; j < kVecPerLane; ++j) {
+            const int idx = j * kWave + lane;
+            at[j] = idx < nvec ? load_stream(pt + idx) : make_uint4(ni, ni, ni, ni);
+            ad[j] = idx < nvec ? load_stream(pd + idx) : make_uint4(ni, ni, ni, ni);
+        }
+#pragma unroll
+        for (int h = 0; h < kVecPerLane; h += kStep) {
+            float ft[kStep * PV], fd[kStep * PV];
+#pragma unroll
+            for (int j = 0; j < kStep; ++j) {
+                Elem<EB>::decode(at[h + j], &ft[j * PV]);
+                Elem<EB>::decode(ad[h + j], &fd[j * PV]);
+            }
+            acc = pair_merge(acc, lane_pair(kStep * PV, [&](int e) { return make_float2(ft[e], fd[e]); }, c2), c2);
+        }
+    } else {
+        constexpr int kStep = 8;
+#pragma unroll 1
+        for (int e0 = 0; e0 < Chunk<EB>::kPerLane; e0 += kStep) {
+            float ft[kStep], fd[kStep];
+#pragma unroll
+            for (int e = 0; e < kStep; ++e) {
+                const int idx = (e0 + e) * kWave + lane;
+                ft[e] = idx < len ? Elem<EB>::at(rt, start + idx) : neg_inf();
+                fd[e] = idx < len ? Elem<EB>::at(rd, start + idx) : neg_inf();
+            }
+            acc = pair_merge(acc, lane_pair(kStep, [&](int e) { return make_float2(ft[e], fd[e]); }, c2), c2);
+        }
+    }
+    acc = wave_merge_pair(acc, c2);
+    if (lane == 0) {
+        uint64_t* w = seq_words(pl, b) + (static_cast<int64_t>(i) * pl.chunks + c) * kPairWords;
+        put_word(w + 0, __float_as_uint(acc.mt), pl.tag);
+        put_word(w + 1, __float_as_uint(acc.st), pl.tag);
+        put_word(w + 2, __float_as_uint(acc.md), pl.tag);
+        put_word(w + 3, __float_as_uint(acc.sd), pl.tag);
+        put_word(w + 4, __float_as_uint(acc.x), pl.tag);
+    }
 }
 
 // ------------------------------------------------------------------ decision words
@@ -1181,6 +1330,137 @@ __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared
     if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + k] = y;
 }
 
+// VAT loss finisher of block b: the pair partials of each position, combined
+// by one wave per position; then on wave 0, one lane per position: the
+// simulated acceptance, labels and weights (as decide_sequence), the soft
+// and hard terms and the block's weighted loss.
+template <int EB, bool VEC>
+__device__ __forceinline__ void vat_loss_finisher(const Plan& pl, int b, TailShared& sh) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int k = pl.k;
+    const int P = pl.chunks;
+    const int64_t V = pl.vocab;
+    const float c2 = pl.c2;
+    const int64_t o = static_cast<int64_t>(b) * k;
+
+    // Token and logit loads that need no partials go out first.
+    const bool active = wave == 0 && lane < k;
+    int x = 0, h = 0;
+    float u = 0.f, lt = 0.f, ld = 0.f, ldh = 0.f;
+    if (active) {
+        x = pl.tokens[o + lane];
+        h = pl.hard_tokens[o + lane];
+        u = pl.uniforms[o + lane];
+    }
+    const bool bad = active && (x < 0 || x >= pl.vocab || h < 0 || h >= pl.vocab);
+    if (active) {
+        const int xc = min(max(x, 0), pl.vocab - 1);
+        const int hc = min(max(h, 0), pl.vocab - 1);
+        const char* rt = row_base(pl.target, o + lane, V, EB);
+        const char* rd = row_base(pl.draft, o + lane, V, EB);
+        lt = Elem<EB>::at(rt, xc);
+        ld = Elem<EB>::at(rd, xc);
+        ldh = Elem<EB>::at(rd, hc);
+    }
+
+    // Position i on wave i % 4: lanes poll their chunks' five words.
+    const uint64_t* words = seq_words(pl, b);
+    bool timed_out = false;
+    const uint64_t t0 = wall_clock64();
+    for (int i = wave; i < k; i += kWavesPerBlock) {
+        PairPart acc = pair_empty();
+        for (int c0 = 0; c0 < P && !timed_out; c0 += kWave) {
+            const int c = c0 + lane;
+            const uint64_t* w = words + (static_cast<int64_t>(i) * P + c) * kPairWords;
+            uint32_t d[kPairWords] = {0u, 0u, 0u, 0u, 0u};
+            for (;;) {
+                bool missing = false;
+                if (c < P) {
+#pragma unroll
+                    for (int q = 0; q < kPairWords; ++q) {
+                        const uint64_t v = get_word(w + q);
+                        if (static_cast<uint32_t>(v >> 32) != pl.tag) missing = true;
+                        d[q] = word_data(v);
+                    }
+                }
+                if (__ballot(missing) == 0ull) break;
+                if (wall_clock64() - t0 > kPollTimeoutTicks) {
+                    timed_out = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+            if (c < P)
+                acc = pair_merge(acc, PairPart{__uint_as_float(d[0]), __uint_as_float(d[1]), __uint_as_float(d[2]),
+                                               __uint_as_float(d[3]), __uint_as_float(d[4])}, c2);
+        }
+        acc = wave_merge_pair(acc, c2);
+        if (lane == 0) {
+            sh.mz[i] = make_float2(acc.mt, acc.st);
+            sh.mz[k + i] = make_float2(acc.md, acc.sd);
+            sh.xs[i] = acc.x;
+            write_row_stats(pl, o + i, make_float2(acc.mt, acc.st));
+            write_row_stats(pl, pl.rows_t + o + i, make_float2(acc.md, acc.sd));
+        }
+    }
+    if (block_any(timed_out, sh.vote)) {
+        fail_sequence(pl, b);
+        for (int j = threadIdx.x; j < k; j += kBlock) {
+            pl.soft_ce[o + j] = __builtin_nanf("");
+            pl.hard_ce[o + j] = __builtin_nanf("");
+        }
+        if (threadIdx.x == 0) pl.block_loss[b] = __builtin_nanf("");
+        return;
+    }
+    if (wave != 0) return;
+
+    const int i = lane;
+    const bool invalid = __ballot(bad) != 0ull;
+    bool keep = false;
+    float p = __builtin_nanf(""), q = __builtin_nanf("");
+    float log2zd = 0.f;
+    if (!invalid && active) {
+        const float2 mzt = sh.mz[i], mzd = sh.mz[k + i];
+        const float lp = (lt - mzt.x) * c2 - log2_hw(mzt.y);
+        log2zd = log2_hw(mzd.y);
+        const float lq = (ld - mzd.x) * c2 - log2zd;
+        keep = log2_hw(u) + lq < lp;
+        p = exp2_hw(lp);
+        q = exp2_hw(lq);
+    }
+    const uint64_t kept = __ballot(keep);
+    const uint64_t lowk = (k == 64) ? ~0ull : ((1ull << k) - 1ull);
+    const uint64_t rej = ~kept & lowk;
+    const int r = invalid ? -1 : (rej ? __builtin_ctzll(rej) : k);
+    float contrib = 0.f;
+    if (active) {
+        float wi = 0.f, soft = __builtin_nanf(""), hard = __builtin_nanf("");
+        if (!invalid) {
+            wi = i < r ? 1.f
+                       : static_cast<float>(pow(static_cast<double>(pl.decay), static_cast<double>(i - r)));
+            const float2 mzt = sh.mz[i], mzd = sh.mz[k + i];
+            // -sum p ln q = ln2 (log2 Z_d - sum_y p(y) (l_d(y) - m_d) c2)
+            soft = kLn2 * (log2zd - sh.xs[i] / mzt.y);
+            hard = kLn2 * (log2zd - (ldh - mzd.x) * c2);
+            contrib = wi * fmaf(pl.hard_weight, hard, soft);
+        }
+        pl.mask[o + i] = static_cast<uint8_t>(!invalid && i < r);
+        pl.weights[o + i] = wi;
+        pl.soft_ce[o + i] = soft;
+        pl.hard_ce[o + i] = hard;
+        if (pl.probs_out) {
+            pl.probs_out[2 * (o + i)] = p;
+            pl.probs_out[2 * (o + i) + 1] = q;
+        }
+    }
+    const float total = wave_sum(contrib);
+    if (lane == 0) {
+        pl.first_reject[b] = r;
+        pl.block_loss[b] = invalid ? __builtin_nanf("") : total;
+    }
+}
+
 // ------------------------------------------------------------------ kernel
 
 // Five resident blocks per CU (five waves per SIMD): the register budget the
@@ -1202,7 +1482,8 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
             for (int n = 0; n < pl.nc_dec; ++n) {
                 const int li = base + n * kWavesPerBlock;
                 if (li >= items) break;
-                stream_chunk<EB, VEC>(pl, b, li / pl.chunks, li % pl.chunks);
+                if (pl.vat_loss) stream_pair<EB, VEC>(pl, b, li / pl.chunks, li % pl.chunks);
+                else stream_chunk<EB, VEC>(pl, b, li / pl.chunks, li % pl.chunks);
             }
             return;
         }
@@ -1224,7 +1505,8 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
             return;
         }
         case kDecFinisher:
-            decide_sequence<EB, VEC>(pl, b, sh);
+            if (pl.vat_loss) vat_loss_finisher<EB, VEC>(pl, b, sh);
+            else decide_sequence<EB, VEC>(pl, b, sh);
             return;
         case kResWorker:
             residual_worker<EB, VEC>(pl, b, role.index, sh);

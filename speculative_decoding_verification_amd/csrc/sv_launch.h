@@ -60,6 +60,7 @@ struct Plan {
     // the bonus row (target position k, verification only).
     int32_t dec_rows;         // rows the decision reads: k or 2k
     int32_t rows_per_seq;     // dec_rows + (1 if there is a bonus row)
+    int32_t words_per_seq;    // hand-off words of one sequence in `partials`
     bool has_resid;           // draft logits at T > 0: residual roles exist
     bool has_bonus;           // verification (not VAT): bonus roles exist
     int32_t nc_dec, nc_bonus, nc_res;  // chunks per worker wavefront
@@ -70,6 +71,7 @@ struct Plan {
     bool greedy;              // T == 0
     bool onehot;
     bool vat;
+    bool vat_loss;            // VAT with the training loss: workers read chunk pairs
     float temperature;
     float c2;                 // log2(e) / T
     float decay;
@@ -86,9 +88,15 @@ struct Plan {
     float* weights;
     float* probs_out;
     float* row_stats_out;
+    const int32_t* hard_tokens;  // VAT loss: the target's sampled token per position
+    float hard_weight;
+    float* soft_ce;           // [N][k] -sum_y p(y) ln q(y)
+    float* hard_ce;           // [N][k] -ln q(h)
+    float* block_loss;        // [N] sum_i w_i (soft_i + hard_weight * hard_i)
 
     // workspace regions
-    uint64_t* partials;       // [B][R_s][P][2] tagged words (m, s) or (max, index)
+    uint64_t* partials;       // [B][R_s][P][2] tagged words (m, s) or (max, index);
+                              // VAT loss: [B][k][P][5] (pair partials)
     uint64_t* resid;          // [B][P] tagged residual masses
     uint64_t* dec;            // [B][kDecWords] tagged decision words
 
@@ -126,7 +134,11 @@ struct WorkspaceLayout {
     size_t partials, resid, dec, total;
 };
 
-WorkspaceLayout workspace_layout(int64_t rows, int64_t batch, int64_t chunks);
+// partial_words: tagged words of chunk partials over the whole call.
+WorkspaceLayout workspace_layout(int64_t partial_words, int64_t batch, int64_t chunks);
+
+// Words per chunk pair of the VAT loss: (m_t, s_t, m_d, s_d, x).
+constexpr int kPairWords = 5;
 
 // Enqueue the whole path on `stream`.  Returns hipSuccess or the first error.
 hipError_t launch_path(const Plan& plan, hipStream_t stream, hipEvent_t probe_start, hipEvent_t probe_stop);

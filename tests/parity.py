@@ -17,6 +17,10 @@ import numpy as np
 
 BAND = 1e-5
 RTOL = 1e-5
+# VAT loss terms are log-sum-exp differences in fp32: their error is relative
+# (1e-5) for typical values and absolute near zero (log2 of a sum close to 1
+# resolves to about one ulp of 1.0, 1.2e-7; the floor allows a few of them).
+LOSS_ATOL = 1e-6
 # fp32 outputs cannot hold probabilities below the smallest normal float (the
 # hardware exp2 flushes subnormal results): an absolute floor for p(x), q(x).
 FLT_MIN = float(np.finfo(np.float32).tiny)
@@ -186,4 +190,58 @@ def compare_vat(gpu, orc, k, decay, greedy, blk_index=None):
         assert rg == ro, ("first_reject", int(n), rg, ro)
         _assert_close("weights vs oracle", gpu["weights"][j], orc.weights[n], rtol=1e-7)
         assert np.array_equal(gpu["accept_mask"][j], orc.accept_mask[n])
+    return {"blocks": len(rows), "ambiguous_accept": amb}
+
+
+def run_vat_loss_gpu(wl, device, temperature=None, decay=None, hard_weight=1.0, hard=None):
+    import speculative_decoding_verification_amd as sv
+
+    cfg = wl.config
+    T = cfg.T if temperature is None else temperature
+    dec = cfg.decay if decay is None else decay
+    h = wl.hard_tokens if hard is None else hard
+    res = sv.vat_loss(to_torch(wl.target, device), to_torch(wl.draft, device), to_torch(wl.tokens, device),
+                      to_torch(wl.uniforms, device), to_torch(h, device), T, dec, hard_weight,
+                      return_probs=True, return_row_stats=True)
+    return {name: getattr(res, name).cpu().numpy()
+            for name in ("accept_mask", "first_reject", "weights", "soft_ce", "hard_ce", "block_loss", "probs",
+                         "row_stats")}
+
+
+def compare_vat_loss(gpu, orc_loss, orc_lab, k, decay, hard_weight, blk_index=None):
+    """Labels as compare_vat; soft and hard terms within RTOL of the oracle;
+    the block loss equals the weighted sum of the oracle's terms under the
+    GPU's own weights (RTOL), which must be the oracle's weights wherever the
+    first rejection is not ambiguous.  `orc_lab` is orc.vat_labels on the same
+    inputs (for the acceptance margins)."""
+    decay = float(np.float32(decay))
+    hard_weight = float(np.float32(hard_weight))
+    fr_g = gpu["first_reject"]
+    N = fr_g.shape[0]
+    rows = np.arange(N) if blk_index is None else blk_index
+    valid = orc_loss.first_reject[rows] >= 0
+    _assert_close("soft", gpu["soft_ce"][valid], orc_loss.soft[rows][valid], atol=LOSS_ATOL)
+    _assert_close("hard", gpu["hard_ce"][valid], orc_loss.hard[rows][valid], atol=LOSS_ATOL)
+    amb = 0
+    i = np.arange(k)
+    for j, n in enumerate(rows):
+        ro = int(orc_loss.first_reject[n])
+        rg = int(fr_g[j])
+        if ro < 0:
+            assert rg == -1 and np.all(gpu["weights"][j] == 0) and np.isnan(gpu["block_loss"][j]), n
+            assert np.all(np.isnan(gpu["soft_ce"][j])) and np.all(np.isnan(gpu["hard_ce"][j])), n
+            continue
+        assert 0 <= rg <= k, (n, rg)
+        assert np.array_equal(gpu["accept_mask"][j], (i < rg).astype(np.uint8)), n
+        want_w = np.where(i < rg, 1.0, np.power(decay, np.maximum(i - rg, 0).astype(np.float64)))
+        _assert_close("weights", gpu["weights"][j], want_w, rtol=1e-7)
+        want_loss = float(np.sum(want_w * (orc_loss.soft[n] + hard_weight * orc_loss.hard[n])))
+        _assert_close("block loss", np.array([gpu["block_loss"][j]]), np.array([want_loss]), atol=k * LOSS_ATOL)
+        tested = range(min(ro + 1, k))
+        a = [p for p in tested if abs(orc_lab.accept_margin[n, p]) < BAND]
+        if a:
+            amb += 1
+            assert rg >= a[0]
+            continue
+        assert rg == ro, ("first_reject", int(n), rg, ro)
     return {"blocks": len(rows), "ambiguous_accept": amb}

@@ -212,3 +212,66 @@ def test_vat_null_and_workspace_errors(lib):
     assert call(w=None) == 1
     assert call(n=8) == 6
     assert np.all(mask == 7) and np.all(fr == 7) and np.all(w == 7) and h.untouched()
+
+
+def _loss_desc(N=2, k=3, V=1000, dtype=sv.SV_F32, T=1.0, decay=0.8, hw=1.0):
+    return sv.VatLossDesc(N, k, V, dtype, T, decay, hw, None, None)
+
+
+class _LossBufs(_HostBufs):
+    def __init__(self, N=2, k=3, V=1000):
+        super().__init__(N, k, V)
+        self.hard = np.zeros(N * k, np.int32)
+        self.mask = np.full(N * k, 7, np.uint8)
+        self.fr = np.full(N, 7, np.int32)
+        self.w = np.full(N * k, 7, np.float32)
+        self.soft_ce = np.full(N * k, 7, np.float32)
+        self.hard_ce = np.full(N * k, 7, np.float32)
+        self.loss = np.full(N, 7, np.float32)
+
+    def loss_untouched(self):
+        return (self.untouched() and np.all(self.mask == 7) and np.all(self.fr == 7) and np.all(self.w == 7)
+                and np.all(self.soft_ce == 7) and np.all(self.hard_ce == 7) and np.all(self.loss == 7))
+
+
+def _call_loss(lib, d, h, **over):
+    a = dict(target=h.target, draft=h.draft, tokens=h.tokens, u=h.u, hard=h.hard, mask=h.mask, fr=h.fr, w=h.w,
+             soft=h.soft_ce, hardce=h.hard_ce, loss=h.loss, ws=h.ws, ws_bytes=h.ws.nbytes)
+    a.update(over)
+    return lib.sv_vat_loss(ctypes.byref(d) if d is not None else None, h.p(a["target"]), h.p(a["draft"]),
+                           h.p(a["tokens"]), h.p(a["u"]), h.p(a["hard"]), h.p(a["mask"]), h.p(a["fr"]),
+                           h.p(a["w"]), h.p(a["soft"]), h.p(a["hardce"]), h.p(a["loss"]), None, None,
+                           h.p(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(decay=1.5), 7), (dict(hw=-0.5), 9), (dict(hw=float("nan")), 9),
+    (dict(hw=float("inf")), 9), (dict(k=0), 2), (dict(dtype=5), 3),
+])
+def test_vat_loss_rejects_bad_desc(lib, over, status):
+    d = _loss_desc(**over)
+    n = ctypes.c_size_t()
+    assert lib.sv_vat_loss_workspace_size(ctypes.byref(d), ctypes.byref(n)) == status
+    h = _LossBufs()
+    assert _call_loss(lib, d, h) == status
+    assert h.loss_untouched()
+
+
+def test_vat_loss_null_args_and_workspace(lib):
+    h = _LossBufs()
+    d = _loss_desc()
+    assert _call_loss(lib, None, h) == 1
+    for name in ("target", "draft", "tokens", "u", "hard", "mask", "fr", "w", "soft", "hardce", "loss", "ws"):
+        assert _call_loss(lib, d, h, **{name: None}) == 1, name
+    n = ctypes.c_size_t()
+    assert lib.sv_vat_loss_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert _call_loss(lib, d, h, ws_bytes=n.value - 1) == 6
+    assert h.loss_untouched()
+    # the loss keeps five words per chunk pair: more workspace than the labels
+    m = ctypes.c_size_t()
+    big = _loss_desc(N=64, k=16, V=128256)
+    assert lib.sv_vat_loss_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert lib.sv_vat_workspace_size(ctypes.byref(_vat_desc(N=64, k=16, V=128256)), ctypes.byref(m)) == 0
+    assert n.value > m.value
+    e = _loss_desc(N=0)
+    assert lib.sv_vat_loss(ctypes.byref(e), *([None] * 14), 0, None) == 0

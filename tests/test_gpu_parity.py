@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 import workloads
-from parity import compare_vat, compare_verify, check_row_stats, run_vat_gpu, run_verify_gpu, to_torch
+from parity import (check_row_stats, compare_vat, compare_vat_loss, compare_verify, run_vat_gpu, run_vat_loss_gpu,
+                    run_verify_gpu, to_torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +84,47 @@ def test_vat_reduced(dev, T):
     orc = oracle.vat_labels(wl.target, wl.draft, wl.tokens, wl.uniforms, T, float(np.float32(cfg.decay)))
     check_row_stats(gpu["row_stats"], orc.target_mz, orc.draft_mz, T == 0.0, T != 0.0)
     _say("  parity ok:", compare_vat(gpu, orc, cfg.k, cfg.decay, T == 0.0))
+
+
+# ------------------------------------------------------------------ VAT loss
+
+def _vat_loss_case(cfg, dev, hard_weight=1.0, hard=None):
+    wl = workloads.generate(cfg)
+    h = wl.hard_tokens if hard is None else hard
+    _say("case vat loss N=%d k=%d V=%d %s T=%g hard_weight=%g" % (cfg.B, cfg.k, cfg.V, cfg.dtype, cfg.T,
+                                                                   hard_weight))
+    gpu = run_vat_loss_gpu(wl, dev, hard_weight=hard_weight, hard=h)
+    dec = float(np.float32(cfg.decay))
+    orc = oracle.vat_loss(wl.target, wl.draft, wl.tokens, wl.uniforms, h, cfg.T, dec, float(np.float32(hard_weight)))
+    lab = oracle.vat_labels(wl.target, wl.draft, wl.tokens, wl.uniforms, cfg.T, dec)
+    valid = orc.first_reject >= 0
+    if valid.any():
+        check_row_stats(gpu["row_stats"], lab.target_mz, lab.draft_mz, False, True)
+    _say("  parity ok:", compare_vat_loss(gpu, orc, lab, cfg.k, cfg.decay, hard_weight))
+    return gpu, orc
+
+
+@pytest.mark.parametrize("B,k,V,dtype,T,hw", [
+    (12, 16, 128256, "f32", 1.0, 1.0),    # the VAT block shape, 12 blocks
+    (6, 16, 151936, "bf16", 0.7, 0.5),    # bf16 rows, ragged last chunk
+    (3, 5, 140000, "f32", 1.0, 2.0),      # 69 chunks: more than one pass of the lanes
+    (20, 1, 3000, "f32", 1.3, 0.0),       # k = 1, no hard term
+    (4, 7, 1001, "bf16", 1.0, 1.0),       # rows not 16-byte aligned: scalar loads
+    (3, 64, 2500, "f32", 0.9, 1.0),       # k = 64
+])
+def test_vat_loss_reduced(dev, B, k, V, dtype, T, hw):
+    cfg = workloads.Config("vatloss", "vat", B, k, V, dtype, T, 4.0, 0.25, "sample", 777)
+    _vat_loss_case(cfg, dev, hard_weight=hw)
+
+
+def test_vat_loss_invalid_hard_token_flags_block(dev):
+    cfg = workloads.Config("vatloss", "vat", 5, 6, 4000, "f32", 1.0, 4.0, 0.25, "sample", 778)
+    wl = workloads.generate(cfg)
+    h = wl.hard_tokens.copy()
+    h[1, 3] = cfg.V
+    h[3, 0] = -1
+    gpu, orc = _vat_loss_case(cfg, dev, hard=h)
+    assert gpu["first_reject"][1] == -1 and gpu["first_reject"][3] == -1
 
 
 def _custom(B, k, V, dtype, T, sigma_t=3.0, sigma_d=0.5, mode="sample", onehot=False, seed=900):
@@ -251,4 +293,35 @@ def test_full_vat_sampled(dev):
     rep = compare_vat(gpu, orc, cfg.k, cfg.decay, False)
     _say("  parity ok:", rep, "mean first_reject", fr.mean())
     del t, d, x, u, res
+    torch.cuda.empty_cache()
+
+
+def test_full_vat_loss_sampled(dev):
+    """The VAT workload (N=2048, k=16, V=128256, fp32) through sv_vat_loss, with
+    the target's own samples as hard labels; sampled blocks against the oracle."""
+    import speculative_decoding_verification_amd as sv
+    import torch
+
+    cfg = workloads.get_config("vat")
+    _say("case vat loss full N=2048 k=16 V=128256 f32 (33.6 GB, device-generated)")
+    t, d, x, u = workloads.generate_on_device(cfg, dev)
+    h = workloads.hard_tokens_on_device(cfg, t, dev)
+    res = sv.vat_loss(t, d, x, u, h, cfg.T, cfg.decay, 1.0)
+    torch.cuda.synchronize()
+    fr = res.first_reject.cpu().numpy()
+    loss = res.block_loss.cpu().numpy()
+    assert np.all((fr >= 0) & (fr <= cfg.k)) and np.all(np.isfinite(loss)) and np.all(loss > 0)
+    idx = np.random.default_rng(6).choice(cfg.B, 16, replace=False)
+    idx.sort()
+    ti = torch.as_tensor(idx, device=dev)
+    tl, dl = t.index_select(0, ti).cpu().numpy(), d.index_select(0, ti).cpu().numpy()
+    xs, us, hs = (a.index_select(0, ti).cpu().numpy() for a in (x, u, h))
+    dec = float(np.float32(cfg.decay))
+    orc = oracle.vat_loss(tl, dl, xs, us, hs, cfg.T, dec, 1.0)
+    lab = oracle.vat_labels(tl, dl, xs, us, cfg.T, dec)
+    gpu = {"first_reject": fr[idx], "accept_mask": res.accept_mask.cpu().numpy()[idx],
+           "weights": res.weights.cpu().numpy()[idx], "soft_ce": res.soft_ce.cpu().numpy()[idx],
+           "hard_ce": res.hard_ce.cpu().numpy()[idx], "block_loss": loss[idx]}
+    _say("  parity ok:", compare_vat_loss(gpu, orc, lab, cfg.k, cfg.decay, 1.0), "mean loss", loss.mean())
+    del t, d, x, u, h, res
     torch.cuda.empty_cache()
