@@ -275,6 +275,18 @@ def main(argv=None):
         # same rows: the decision rows of all sequences and the bonus row
         # (target position k) of those that kept all k drafts
         needed = in_bytes - (cfg.B - full) * cfg.V * cfg.elem_bytes
+        # acceptance telemetry: the histogram of accepted lengths after a call
+        hist = sv.accept_histogram(last.accepted_len, cfg.k)
+        torch.cuda.synchronize()
+        ev.record(region[0], stream)
+        for _ in range(200):
+            sv.accept_histogram(last.accepted_len, cfg.k, out=hist, stream=stream)
+        ev.record(region[1], stream)
+        torch.cuda.synchronize()
+        ctl = sv.DraftLengthController()
+        ctl.update(hist.cpu())
+        extra["accept_histogram_us"] = ev.elapsed_ms(*region) / 200 * 1e3
+        extra["block_efficiency"] = ctl.efficiency
     achieved = needed / (k1_mean * 1e-3) / 1e9
     for e in region:
         ev.destroy(e)

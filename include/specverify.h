@@ -28,6 +28,19 @@
  *                 before the first rejection r get weight 1 and the decay
  *                 curve restarts at r (weight decay^(i-r) for i >= r).
  *
+ *  sv_accept_histogram, sv_draft_len_init, sv_draft_len_update --
+ *                 EfficientRollout write-up (qunfachuanzhen.com), section
+ *                 "四、自适应草稿长度": the draft length is picked from a fixed
+ *                 set (5, 7, 9, 11 in the experiments), starting from the
+ *                 shortest; after every training step the block efficiency
+ *                 (tokens a draft-verify cycle commits) is measured; the
+ *                 length moves up when two consecutive steps run close to
+ *                 the current length's limit, down when they run too low,
+ *                 and waits two steps so that one noisy step moves nothing.
+ *                 NgramRL summary, section "自适应 fan-out 预取": the
+ *                 distribution P(j) of accepted lengths is the statistic a
+ *                 prefetcher plans with; the histogram is that distribution.
+ *
  *  sv_vat_loss -- the same page and sections, with the end of section
  *                 "第二件事，改权重分配的锚点": the drafter's training loss
  *                 combines soft-label distillation from the target's output
@@ -95,8 +108,9 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 2
+#define SV_ABI_VERSION 3
 #define SV_MAX_DRAFT 64 /* k is limited to one 64-lane wavefront */
+#define SV_MAX_DRAFT_CHOICES 8
 
 typedef enum sv_status {
     SV_OK = 0,
@@ -108,7 +122,8 @@ typedef enum sv_status {
     SV_ERR_WORKSPACE_TOO_SMALL = 6,
     SV_ERR_BAD_DECAY = 7,         /* VAT decay not in [0, 1] */
     SV_ERR_HIP = 8,               /* a kernel launch or event record failed */
-    SV_ERR_BAD_HARD_WEIGHT = 9    /* VAT loss hard_weight not finite and >= 0 */
+    SV_ERR_BAD_HARD_WEIGHT = 9,   /* VAT loss hard_weight not finite and >= 0 */
+    SV_ERR_BAD_CONTROL = 10       /* draft-length controller thresholds out of range */
 } sv_status;
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -262,6 +277,45 @@ sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, c
                       uint8_t* accept_mask, int32_t* first_reject, float* weights, float* soft_ce, float* hard_ce,
                       float* block_loss, float* probs_out, float* row_stats_out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Histogram of accepted lengths (device in, device out).
+ *  accepted_len  device, [B] int32 as written by sv_verify
+ *  hist          device out, [k + 4] int32: hist[j] = #sequences with
+ *                accepted_len == j for j in [0, k]; hist[k+1] = #(-1, invalid
+ *                token); hist[k+2] = #(-2, wait timed out); hist[k+3] = #other
+ * Counts are exact.  One small kernel on `stream`.
+ * Errors: SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE (B < 0 or k outside [1, 64]),
+ * SV_ERR_HIP.
+ */
+sv_status sv_accept_histogram(const int32_t* accepted_len, int32_t batch, int32_t k, int32_t* hist,
+                              hipStream_t stream);
+
+/* State of the draft-length controller: host memory, owned by the caller. */
+typedef struct sv_draft_len_ctl {
+    int32_t n_choices;                      /* 1 .. SV_MAX_DRAFT_CHOICES */
+    int32_t choices[SV_MAX_DRAFT_CHOICES];  /* strictly increasing draft lengths in [1, 64] */
+    int32_t index;                          /* current choice (starts at 0, the shortest) */
+    float up_frac;                          /* move up when efficiency >= up_frac * (k+1) ... */
+    float down_frac;                        /* move down when efficiency <= down_frac * (k+1) ... */
+    int32_t patience;                       /* ... on this many consecutive steps */
+    int32_t up_streak, down_streak;
+    float last_efficiency;                  /* the last step's block efficiency */
+} sv_draft_len_ctl;
+
+/* Initialises `ctl` (host).  0 <= down_frac < up_frac <= 1, patience >= 1.
+ * Errors: SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE (choices), SV_ERR_BAD_CONTROL. */
+sv_status sv_draft_len_init(sv_draft_len_ctl* ctl, const int32_t* choices, int32_t n_choices, float up_frac,
+                            float down_frac, int32_t patience);
+
+/* One step of the controller (host).  hist: HOST copy of sv_accept_histogram's
+ * output for a step run at draft length k (= the current choice).  Block
+ * efficiency = sum_j (j+1) hist[j] / sum_j hist[j] over j in [0, k] (accepted
+ * drafts plus the target's token, per cycle; at most k+1).  Writes the draft
+ * length for the next step to *next_k.  A histogram with no valid sequence
+ * changes nothing.  Errors: SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE (k is not the
+ * current choice). */
+sv_status sv_draft_len_update(sv_draft_len_ctl* ctl, const int32_t* hist, int32_t k, int32_t* next_k);
 
 #ifdef __cplusplus
 }

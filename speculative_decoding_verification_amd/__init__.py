@@ -18,8 +18,9 @@ import ctypes
 import os
 from typing import NamedTuple, Optional
 
-__all__ = ["verify", "vat_labels", "vat_loss", "Verifier", "VatLabeler", "VatLoss", "SVError", "library_path",
-           "load_library", "SV_F32", "SV_BF16", "SV_DRAFT_LOGITS", "SV_DRAFT_ONEHOT", "STATUS"]
+__all__ = ["verify", "vat_labels", "vat_loss", "accept_histogram", "Verifier", "VatLabeler", "VatLoss",
+           "DraftLengthController", "SVError", "library_path", "load_library", "SV_F32", "SV_BF16", "SV_DRAFT_LOGITS",
+           "SV_DRAFT_ONEHOT", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspecverify.so")
@@ -28,10 +29,11 @@ SV_F32, SV_BF16 = 0, 1
 SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT = 0, 1
 STATUS = {0: "SV_OK", 1: "SV_ERR_NULL_ARG", 2: "SV_ERR_BAD_SHAPE", 3: "SV_ERR_BAD_DTYPE",
           4: "SV_ERR_BAD_TEMPERATURE", 5: "SV_ERR_BAD_DRAFT_KIND", 6: "SV_ERR_WORKSPACE_TOO_SMALL",
-          7: "SV_ERR_BAD_DECAY", 8: "SV_ERR_HIP", 9: "SV_ERR_BAD_HARD_WEIGHT"}
+          7: "SV_ERR_BAD_DECAY", 8: "SV_ERR_HIP", 9: "SV_ERR_BAD_HARD_WEIGHT", 10: "SV_ERR_BAD_CONTROL"}
 
 EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_size", "sv_verify",
-                    "sv_vat_workspace_size", "sv_vat_labels", "sv_vat_loss_workspace_size", "sv_vat_loss")
+                    "sv_vat_workspace_size", "sv_vat_labels", "sv_vat_loss_workspace_size", "sv_vat_loss",
+                    "sv_accept_histogram", "sv_draft_len_init", "sv_draft_len_update")
 
 
 class SVError(RuntimeError):
@@ -59,6 +61,16 @@ class VatLossDesc(ctypes.Structure):
     _fields_ = [("blocks", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float), ("decay", ctypes.c_float),
                 ("hard_weight", ctypes.c_float), ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+
+
+SV_MAX_DRAFT_CHOICES = 8
+
+
+class DraftLenCtl(ctypes.Structure):
+    _fields_ = [("n_choices", ctypes.c_int32), ("choices", ctypes.c_int32 * SV_MAX_DRAFT_CHOICES),
+                ("index", ctypes.c_int32), ("up_frac", ctypes.c_float), ("down_frac", ctypes.c_float),
+                ("patience", ctypes.c_int32), ("up_streak", ctypes.c_int32), ("down_streak", ctypes.c_int32),
+                ("last_efficiency", ctypes.c_float)]
 
 
 _lib = None
@@ -94,6 +106,14 @@ def load_library():
     lib.sv_vat_loss_workspace_size.argtypes = [ctypes.POINTER(VatLossDesc), ctypes.POINTER(sz)]
     lib.sv_vat_loss.restype = ctypes.c_int
     lib.sv_vat_loss.argtypes = [ctypes.POINTER(VatLossDesc)] + [vp] * 14 + [sz, vp]
+    i32 = ctypes.c_int32
+    lib.sv_accept_histogram.restype = ctypes.c_int
+    lib.sv_accept_histogram.argtypes = [vp, i32, i32, vp, vp]
+    lib.sv_draft_len_init.restype = ctypes.c_int
+    lib.sv_draft_len_init.argtypes = [ctypes.POINTER(DraftLenCtl), ctypes.POINTER(i32), i32, ctypes.c_float,
+                                      ctypes.c_float, i32]
+    lib.sv_draft_len_update.restype = ctypes.c_int
+    lib.sv_draft_len_update.argtypes = [ctypes.POINTER(DraftLenCtl), ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
     _lib = lib
     return lib
 
@@ -374,3 +394,58 @@ def vat_loss(target, draft, draft_tokens, uniforms, hard_tokens, temperature: fl
     Labels, weights, the soft and hard terms per position and the weighted loss per block."""
     return VatLoss(target, draft, draft_tokens, uniforms, hard_tokens, temperature, decay, hard_weight,
                    return_probs=return_probs, return_row_stats=return_row_stats, workspace=workspace)()
+
+
+def accept_histogram(accepted_len, k: int, out=None, stream: Optional[int] = None):
+    """sv_accept_histogram: counts of accepted lengths 0..k, then -1, -2 and
+    other values, as an int32 tensor of k+4 on the same device."""
+    torch = _torch()
+    lib = load_library()
+    device = accepted_len.device
+    _check_dev("accepted_len", accepted_len, device, torch.int32)
+    if out is None:
+        out = torch.empty(k + 4, dtype=torch.int32, device=device)
+    _check_dev("out", out, device, torch.int32, (k + 4,))
+    s = _stream_handle(device) if stream is None else stream
+    st = lib.sv_accept_histogram(_ptr(accepted_len), int(accepted_len.numel()), int(k), _ptr(out), s)
+    if st:
+        raise SVError(st, "sv_accept_histogram", lib)
+    return out
+
+
+class DraftLengthController:
+    """The host-side draft-length rule (sv_draft_len_init / sv_draft_len_update):
+    choices ascending (default 5, 7, 9, 11), start at the shortest, move one
+    step up or down after `patience` consecutive steps whose block efficiency
+    is at least up_frac*(k+1) or at most down_frac*(k+1)."""
+
+    def __init__(self, choices=(5, 7, 9, 11), up_frac: float = 0.9, down_frac: float = 0.5, patience: int = 2):
+        lib = load_library()
+        self._lib = lib
+        self.ctl = DraftLenCtl()
+        arr = (ctypes.c_int32 * len(choices))(*choices)
+        st = lib.sv_draft_len_init(ctypes.byref(self.ctl), arr, len(choices), float(up_frac), float(down_frac),
+                                   int(patience))
+        if st:
+            raise SVError(st, "sv_draft_len_init", lib)
+
+    @property
+    def k(self) -> int:
+        return int(self.ctl.choices[self.ctl.index])
+
+    @property
+    def efficiency(self) -> float:
+        return float(self.ctl.last_efficiency)
+
+    def update(self, hist) -> int:
+        """hist: host sequence (or tensor) of the k+4 counts for a step run at
+        the current k.  Returns the draft length for the next step."""
+        vals = [int(v) for v in (hist.tolist() if hasattr(hist, "tolist") else hist)]
+        if len(vals) < self.k + 1:
+            raise ValueError("hist needs at least k+1 = %d counts" % (self.k + 1))
+        arr = (ctypes.c_int32 * len(vals))(*vals)
+        nxt = ctypes.c_int32()
+        st = self._lib.sv_draft_len_update(ctypes.byref(self.ctl), arr, self.k, ctypes.byref(nxt))
+        if st:
+            raise SVError(st, "sv_draft_len_update", self._lib)
+        return int(nxt.value)

@@ -150,6 +150,7 @@ const char* sv_status_str(int status) {
         case SV_ERR_BAD_TEMPERATURE: return "SV_ERR_BAD_TEMPERATURE: temperature must be 0 or finite and >= 1e-4";
         case SV_ERR_BAD_DRAFT_KIND: return "SV_ERR_BAD_DRAFT_KIND: draft_kind must be SV_DRAFT_LOGITS or SV_DRAFT_ONEHOT";
         case SV_ERR_BAD_HARD_WEIGHT: return "SV_ERR_BAD_HARD_WEIGHT: hard_weight must be finite and >= 0";
+        case SV_ERR_BAD_CONTROL: return "SV_ERR_BAD_CONTROL: need 0 <= down_frac < up_frac <= 1";
         case SV_ERR_WORKSPACE_TOO_SMALL: return "SV_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the size query";
         case SV_ERR_BAD_DECAY: return "SV_ERR_BAD_DECAY: decay must be in [0, 1]";
         case SV_ERR_HIP: return "SV_ERR_HIP: a HIP launch or event record failed";
@@ -302,6 +303,14 @@ sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, c
     pl.block_loss = block_loss;
     sv::carve_workspace(s, workspace, &pl);
     const hipError_t e = sv::launch_path(pl, stream, desc->probe_start, desc->probe_stop);
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status sv_accept_histogram(const int32_t* accepted_len, int32_t batch, int32_t k, int32_t* hist,
+                              hipStream_t stream) {
+    if (batch < 0 || k < 1 || k > SV_MAX_DRAFT) return SV_ERR_BAD_SHAPE;
+    if (!hist || (batch > 0 && !accepted_len)) return SV_ERR_NULL_ARG;
+    const hipError_t e = sv::launch_accept_hist(accepted_len, batch, k, hist, stream);
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -1541,6 +1541,34 @@ hipError_t launch_typed(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipE
 
 }  // namespace
 
+// ------------------------------------------------------------------ acceptance telemetry
+
+namespace {
+
+// Counts of the accepted lengths of one call: bins 0..k, then -1 (invalid
+// token), -2 (wait timed out), anything else.  One block; integer LDS
+// atomics, so the counts are exact.
+__global__ __launch_bounds__(kBlock) void k_accept_hist(const int32_t* acc, int32_t batch, int32_t k, int32_t* hist) {
+    __shared__ int counts[kMaxDraft + 4];
+    const int nb = k + 4;
+    for (int j = threadIdx.x; j < nb; j += kBlock) counts[j] = 0;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < batch; i += kBlock) {
+        const int v = acc[i];
+        const int bin = (v >= 0 && v <= k) ? v : (v == -1 ? k + 1 : (v == -2 ? k + 2 : k + 3));
+        atomicAdd(&counts[bin], 1);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nb; j += kBlock) hist[j] = counts[j];
+}
+
+}  // namespace
+
+hipError_t launch_accept_hist(const int32_t* acc, int32_t batch, int32_t k, int32_t* hist, hipStream_t stream) {
+    hipLaunchKernelGGL(k_accept_hist, dim3(1), dim3(kBlock), 0, stream, acc, batch, k, hist);
+    return hipGetLastError();
+}
+
 hipError_t launch_path(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (pl.batch == 0) return hipSuccess;
     if (pl.elem_bytes == 2) {

@@ -143,4 +143,7 @@ constexpr int kPairWords = 5;
 // Enqueue the whole path on `stream`.  Returns hipSuccess or the first error.
 hipError_t launch_path(const Plan& plan, hipStream_t stream, hipEvent_t probe_start, hipEvent_t probe_stop);
 
+// Histogram of accepted lengths into hist[0 .. k+3] (one block).
+hipError_t launch_accept_hist(const int32_t* acc, int32_t batch, int32_t k, int32_t* hist, hipStream_t stream);
+
 }  // namespace sv

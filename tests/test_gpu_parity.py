@@ -325,3 +325,44 @@ def test_full_vat_loss_sampled(dev):
     _say("  parity ok:", compare_vat_loss(gpu, orc, lab, cfg.k, cfg.decay, 1.0), "mean loss", loss.mean())
     del t, d, x, u, h, res
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ acceptance telemetry
+
+def _hist_ref(acc, k):
+    acc = np.asarray(acc, np.int64)
+    h = np.zeros(k + 4, np.int64)
+    valid = (acc >= 0) & (acc <= k)
+    h[: k + 1] = np.bincount(acc[valid], minlength=k + 1)
+    h[k + 1] = np.count_nonzero(acc == -1)
+    h[k + 2] = np.count_nonzero(acc == -2)
+    h[k + 3] = acc.size - h[: k + 3].sum()
+    return h
+
+
+@pytest.mark.parametrize("B,k", [(0, 5), (1, 1), (257, 7), (100003, 16), (4096, 64)])
+def test_accept_histogram_exact(dev, B, k):
+    import speculative_decoding_verification_amd as sv
+    import torch
+
+    _say("case accept histogram B=%d k=%d" % (B, k))
+    rng = np.random.default_rng(B + k)
+    acc = rng.integers(-3, k + 3, size=B).astype(np.int32)
+    h = sv.accept_histogram(torch.from_numpy(acc).to(dev), k).cpu().numpy()
+    assert np.array_equal(h, _hist_ref(acc, k))
+
+
+def test_telemetry_after_verify_drives_the_controller(dev):
+    import speculative_decoding_verification_amd as sv
+
+    cfg = workloads.get_config("selfdraft").scaled(B=64)
+    wl = workloads.generate(cfg)
+    t, d, x, u = workloads.to_device(wl, dev)
+    res = sv.verify(t, d, x, u, cfg.T)
+    h = sv.accept_histogram(res.accepted_len, cfg.k).cpu().numpy()
+    acc = res.accepted_len.cpu().numpy()
+    assert np.array_equal(h, _hist_ref(acc, cfg.k))
+    ctl = sv.DraftLengthController()
+    ctl.update(h)
+    assert ctl.efficiency == pytest.approx(float(np.mean(acc + 1)), rel=1e-6)
+    _say("  block efficiency %.3f at k=%d" % (ctl.efficiency, cfg.k))
