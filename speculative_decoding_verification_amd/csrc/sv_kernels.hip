@@ -431,7 +431,8 @@ __device__ __forceinline__ bool collect(const uint64_t* words, int n, uint32_t t
             else if (stage) stage[i] = word_data(w);
         }
         if (!block_any(missing, flags)) return true;
-        if (wall_clock64() - t0 > kPollTimeoutTicks) return false;
+        // waves read the clock at slightly different times: decide together
+        if (block_any(wall_clock64() - t0 > kPollTimeoutTicks, flags)) return false;
         __builtin_amdgcn_s_sleep(8);
     }
 }

@@ -67,8 +67,13 @@ def run_vat_gpu(wl, device, temperature=None, decay=None):
     x = to_torch(wl.tokens, device)
     u = to_torch(wl.uniforms, device) if T != 0.0 else None
     res = sv.vat_labels(t, d, x, u, T, dec, return_probs=True, return_row_stats=True)
-    return {name: getattr(res, name).cpu().numpy()
-            for name in ("accept_mask", "first_reject", "weights", "probs", "row_stats")}
+    out = {name: getattr(res, name).cpu().numpy()
+           for name in ("accept_mask", "first_reject", "weights", "probs", "row_stats")}
+    # The same call without the optional outputs gives the same labels.
+    lean = sv.vat_labels(t, d, x, u, T, dec)
+    for name in ("accept_mask", "first_reject", "weights"):
+        assert np.array_equal(getattr(lean, name).cpu().numpy(), out[name]), name + " differs without probs"
+    return out
 
 
 def _close(a, b, rtol=RTOL, atol=0.0):
