@@ -74,6 +74,8 @@ def _load():
     lib.orc_vat_loss.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_double, c.c_double, c.c_double,
                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_vat_loss.restype = c.c_int
+    lib.orc_lm_head_greedy.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int64, vp, vp, vp, vp, vp, vp, vp]
+    lib.orc_lm_head_greedy.restype = c.c_int
     _lib = lib
     return lib
 
@@ -257,3 +259,34 @@ def vat_loss(target, draft, tokens, uniforms, hard_tokens, temperature: float, d
     if rc != 0:
         raise ValueError("orc_vat_loss rejected its arguments")
     return VatResult(accept_mask=mask, first_reject=fr, weights=w, soft=soft, hard=hard, block_loss=loss)
+
+
+class LmHeadResult:
+    __slots__ = ("accepted_len", "out_tokens", "argmax", "top2_gap")
+
+    def __init__(self, **kw):
+        for k, v in kw.items():
+            setattr(self, k, v)
+
+
+def lm_head_greedy(hidden, weight, tokens) -> LmHeadResult:
+    """Greedy verification with logits formed from hidden states: hidden
+    [B][k+1][D] and weight [V][D] as bf16 bit patterns (uint16), tokens
+    [B][k].  fp64 logits, lowest-index argmax."""
+    lib = _load()
+    h = np.ascontiguousarray(hidden, dtype=np.uint16)
+    w = np.ascontiguousarray(weight, dtype=np.uint16)
+    B, kp1, D = h.shape
+    V, D2 = w.shape
+    assert D2 == D
+    k = kp1 - 1
+    x = np.ascontiguousarray(tokens, dtype=np.int32)
+    assert x.shape == (B, k)
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, k + 1), np.int32)
+    am = np.empty((B, k + 1), np.int32)
+    gap = np.empty((B, k + 1), np.float64)
+    rc = lib.orc_lm_head_greedy(B, k, V, D, _ptr(h), _ptr(w), _ptr(x), _ptr(acc), _ptr(out), _ptr(am), _ptr(gap))
+    if rc != 0:
+        raise ValueError("orc_lm_head_greedy rejected its arguments")
+    return LmHeadResult(accepted_len=acc, out_tokens=out, argmax=am, top2_gap=gap)

@@ -57,6 +57,9 @@
  *    out_tokens all -1;
  *  - VAT weight at the rejected position itself is decay^0 = 1; no rejection
  *    gives first_reject = k and all weights 1.
+ *  - LM-head greedy verification (orc_lm_head_greedy): the logits are the
+ *    product of the hidden state with the output layer's weights, formed in
+ *    fp64 from their bf16 values; the rest is the T == 0 rule above.
  *  - VAT loss (orc_vat_loss): at every position the soft term is the cross
  *    entropy of the draft's distribution against the target's at the same
  *    temperature, -sum_y p(y) ln q(y); the hard term is -ln q(h) for the
@@ -493,5 +496,65 @@ int orc_vat_loss(int64_t N, int32_t k, int64_t V, int32_t dtype, double T, doubl
         block_loss[n] = total;
     }
     free(lt); free(ld); free(p); free(q);
+    return 0;
+}
+
+/* LM-head greedy verification (the T = 0 reading of [NG1], with the logits
+ * formed from hidden states): logits l_i(y) = sum_d h_i[d] w_y[d] in fp64 from
+ * bf16 hidden states h [B][k+1][D] and output-layer weights w [V][D]; the
+ * target's choice g_i is the lowest-index argmax; a draft token is kept iff it
+ * equals g_i; r = first mismatch (k if none); out = x_0..x_{r-1}, g_r, -1...
+ * Also returns every row's argmax and the gap between its two largest logits
+ * (the margin a rounding of the logits would have to overcome). */
+int orc_lm_head_greedy(int64_t B, int32_t k, int64_t V, int64_t D, const uint16_t* hidden, const uint16_t* weight,
+                       const int32_t* tokens, int32_t* accepted_len, int32_t* out_tokens, int32_t* argmax_out,
+                       double* top2_gap) {
+    int64_t b, y, d;
+    int32_t i;
+    double* h;
+    if (B < 0 || k < 1 || V < 1 || D < 1 || !hidden || !weight || !tokens || !accepted_len || !out_tokens) return -1;
+    h = (double*)malloc(sizeof(double) * D);
+    if (!h) return -1;
+    for (b = 0; b < B; ++b) {
+        const int32_t* x = tokens + b * k;
+        int32_t r = k;
+        int valid = tokens_valid(x, k, V);
+        for (i = 0; i <= k; ++i) {
+            double best = -INFINITY, second = -INFINITY;
+            int64_t g = 0;
+            const uint16_t* hr = hidden + (b * (k + 1) + i) * D;
+            for (d = 0; d < D; ++d) h[d] = orc_decode_bf16(hr[d]);
+            for (y = 0; y < V; ++y) {
+                const uint16_t* wr = weight + y * D;
+                double s = 0.0;
+                for (d = 0; d < D; ++d) s += h[d] * orc_decode_bf16(wr[d]);
+                if (s > best) {
+                    second = best;
+                    best = s;
+                    g = y;
+                } else if (s > second) {
+                    second = s;
+                }
+            }
+            if (argmax_out) argmax_out[b * (k + 1) + i] = (int32_t)g;
+            if (top2_gap) top2_gap[b * (k + 1) + i] = best - second;
+            if (i < k && r == k && valid && x[i] != g) r = i;
+            if (i == r) {
+                /* the target's token at the first mismatch (or after all k) */
+                out_tokens[b * (k + 1) + i] = (int32_t)g;
+            }
+        }
+        if (!valid) {
+            accepted_len[b] = -1;
+            for (i = 0; i <= k; ++i) out_tokens[b * (k + 1) + i] = -1;
+            continue;
+        }
+        accepted_len[b] = r;
+        for (i = 0; i <= k; ++i) {
+            if (i < r) out_tokens[b * (k + 1) + i] = x[i];
+            else if (i > r) out_tokens[b * (k + 1) + i] = -1;
+        }
+    }
+    free(h);
     return 0;
 }

@@ -483,3 +483,64 @@ def test_vat_loss_labels_match_vat_labels_and_invalid_hard_token_flags(orc):
     assert res.first_reject[2] == -1 and np.all(res.weights[2] == 0)
     assert np.isnan(res.block_loss[2]) and np.all(np.isnan(res.soft[2]))
     assert np.all(np.isfinite(res.block_loss[keep]))
+
+
+# ----------------------------------------------------------------- LM-head greedy verification
+
+def _bf16_bits(a):
+    a = np.ascontiguousarray(a, np.float32)
+    u = a.view(np.uint32)
+    # round to nearest even on the discarded half
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _bf16_vals(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_lm_head_logits_are_the_fp64_matmul(orc):
+    rng = np.random.default_rng(70)
+    B, k, V, D = 3, 4, 300, 96
+    h = _bf16_bits(rng.standard_normal((B, k + 1, D)))
+    w = _bf16_bits(rng.standard_normal((V, D)) * 0.3)
+    logits = _bf16_vals(h) @ _bf16_vals(w).T            # numpy matmul in fp64
+    x = np.argmax(logits[:, :k], axis=2).astype(np.int32)
+    res = orc.lm_head_greedy(h, w, x)
+    assert np.array_equal(res.argmax, np.argmax(logits, axis=2))
+    srt = np.sort(logits, axis=2)
+    assert np.allclose(res.top2_gap, srt[..., -1] - srt[..., -2], rtol=1e-9, atol=1e-12)
+    assert np.all(res.accepted_len == k)
+    assert np.array_equal(res.out_tokens[:, :k], x) and np.array_equal(res.out_tokens[:, k], res.argmax[:, k])
+
+
+def test_lm_head_greedy_matches_logit_greedy_on_exact_integers(orc):
+    """Small integer hidden states and weights make every logit an exact
+    integer (ties included); the result must equal greedy verification on
+    those logits, lowest index first among ties."""
+    rng = np.random.default_rng(71)
+    B, k, V, D = 40, 5, 64, 8
+    h = _bf16_bits(rng.integers(-2, 3, (B, k + 1, D)).astype(np.float32))
+    w = _bf16_bits(rng.integers(-2, 3, (V, D)).astype(np.float32))
+    logits = (_bf16_vals(h) @ _bf16_vals(w).T).astype(np.float32)
+    g = np.argmax(logits, axis=2)
+    x = np.where(rng.random((B, k)) < 0.7, g[:, :k], rng.integers(0, V, (B, k))).astype(np.int32)
+    res = orc.lm_head_greedy(h, w, x)
+    ref = orc.verify(logits, None, x, None, 0.0)
+    assert np.array_equal(res.accepted_len, ref.accepted_len)
+    assert np.array_equal(res.out_tokens, ref.out_tokens)
+    assert np.any(res.top2_gap == 0.0)   # ties occur and follow the lowest index
+
+
+def test_lm_head_greedy_first_mismatch_and_invalid_token(orc):
+    rng = np.random.default_rng(72)
+    B, k, V, D = 2, 4, 50, 16
+    h = _bf16_bits(rng.standard_normal((B, k + 1, D)))
+    w = _bf16_bits(rng.standard_normal((V, D)))
+    g = np.argmax(_bf16_vals(h) @ _bf16_vals(w).T, axis=2)
+    x = g[:, :k].astype(np.int32).copy()
+    x[0, 2] = (x[0, 2] + 1) % V
+    x[1, 0] = V
+    res = orc.lm_head_greedy(h, w, x)
+    assert res.accepted_len[0] == 2
+    assert list(res.out_tokens[0]) == [x[0, 0], x[0, 1], g[0, 2], -1, -1]
+    assert res.accepted_len[1] == -1 and np.all(res.out_tokens[1] == -1)
