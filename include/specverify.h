@@ -108,7 +108,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 3
+#define SV_ABI_VERSION 4
 #define SV_MAX_DRAFT 64 /* k is limited to one 64-lane wavefront */
 #define SV_MAX_DRAFT_CHOICES 8
 
@@ -123,7 +123,8 @@ typedef enum sv_status {
     SV_ERR_BAD_DECAY = 7,         /* VAT decay not in [0, 1] */
     SV_ERR_HIP = 8,               /* a kernel launch or event record failed */
     SV_ERR_BAD_HARD_WEIGHT = 9,   /* VAT loss hard_weight not finite and >= 0 */
-    SV_ERR_BAD_CONTROL = 10       /* draft-length controller thresholds out of range */
+    SV_ERR_BAD_CONTROL = 10,      /* draft-length controller thresholds out of range */
+    SV_ERR_MISALIGNED = 11        /* an array that must be 16-byte aligned is not */
 } sv_status;
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -169,6 +170,18 @@ typedef struct sv_vat_loss_desc {
     hipEvent_t probe_start;
     hipEvent_t probe_stop;
 } sv_vat_loss_desc;
+
+/* Shape and options of one sv_verify_lm_head_greedy call.  probe_start /
+ * probe_stop (NULL to skip) bracket the call's GEMM launch (the first of its
+ * two kernels). */
+typedef struct sv_lm_head_desc {
+    int32_t batch;       /* B >= 0 sequences */
+    int32_t num_draft;   /* k in [1, 64] */
+    int32_t vocab;       /* V in [1, 2^24]: rows of the output layer */
+    int32_t hidden;      /* D: hidden size, a multiple of 32 in [32, 65536] */
+    hipEvent_t probe_start;
+    hipEvent_t probe_stop;
+} sv_lm_head_desc;
 
 /* Returns SV_ABI_VERSION of the built library. */
 int sv_abi_version(void);
@@ -277,6 +290,47 @@ sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, c
                       uint8_t* accept_mask, int32_t* first_reject, float* weights, float* soft_ce, float* hard_ce,
                       float* block_loss, float* probs_out, float* row_stats_out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes sv_verify_lm_head_greedy needs for `desc`.  Errors:
+ * SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE. */
+sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes);
+
+/*
+ * Greedy (T == 0) verification with the target's logits formed from its
+ * final hidden states and output-layer weights inside the call, so that the
+ * [B][k+1][V] logits never reach memory.  Source: NgramRL essay, section
+ * "投机解码：让草稿先跑，考官殿后" (the rule, read at T == 0 as above: the
+ * target's choice is its lowest-index argmax, a draft token is kept iff it
+ * equals it); the target's logit at a position is the dot product of the
+ * hidden state with the output layer's row of that token.  EfficientRollout
+ * write-up, section "二、量化压缩：从大模型里“变”出一个代笔助理": in the tail
+ * phase most of a forward's time goes to loading dense weights, the output
+ * (LM-head) layer among them; this call reads that layer once for all
+ * B(k+1) positions.
+ *
+ *  hidden_states  device, [B][k+1][D] bfloat16, 16-byte aligned: the target's
+ *                 final hidden state at positions 0..k
+ *  weight         device, [V][D] bfloat16, 16-byte aligned: output layer,
+ *                 row y gives token y's logit
+ *  draft_tokens   device, [B][k] int32, expected in [0, V)
+ *  accepted_len   device out, [B] int32 in [0, k] (-1: invalid token)
+ *  out_tokens     device out, [B][k+1] int32, as for sv_verify
+ *  argmax_out     device out or NULL, [B][k+1] int32: every position's
+ *                 choice (written for invalid sequences too)
+ *  workspace      device, >= sv_lm_head_workspace_size bytes (needs no
+ *                 clearing: every byte read is written earlier in the call)
+ *  stream         HIP stream the two kernels are enqueued on
+ *
+ * Arithmetic: bf16 x bf16 products accumulated in fp32 on the matrix cores;
+ * the accumulation order differs from a sequential sum, so a position whose
+ * two largest logits lie within rounding of each other may pick either.
+ * Errors (nothing launched): SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE,
+ * SV_ERR_MISALIGNED, SV_ERR_WORKSPACE_TOO_SMALL.  Launch failure: SV_ERR_HIP.
+ */
+sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidden_states, const void* weight,
+                                   const int32_t* draft_tokens, int32_t* accepted_len, int32_t* out_tokens,
+                                   int32_t* argmax_out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 /*
  * Histogram of accepted lengths (device in, device out).

@@ -505,56 +505,77 @@ int orc_vat_loss(int64_t N, int32_t k, int64_t V, int32_t dtype, double T, doubl
  * target's choice g_i is the lowest-index argmax; a draft token is kept iff it
  * equals g_i; r = first mismatch (k if none); out = x_0..x_{r-1}, g_r, -1...
  * Also returns every row's argmax and the gap between its two largest logits
- * (the margin a rounding of the logits would have to overcome). */
+ * (the margin a rounding of the logits would have to overcome).
+ * Each weight row is decoded once and dotted with every hidden row of the
+ * call (each dot product is the plain sequential fp64 sum over d); tokens
+ * are visited in ascending id, so the first strict maximum is the lowest. */
 int orc_lm_head_greedy(int64_t B, int32_t k, int64_t V, int64_t D, const uint16_t* hidden, const uint16_t* weight,
                        const int32_t* tokens, int32_t* accepted_len, int32_t* out_tokens, int32_t* argmax_out,
                        double* top2_gap) {
-    int64_t b, y, d;
+    int64_t b, y, d, row;
     int32_t i;
-    double* h;
+    const int64_t rows = B * (k + 1);
+    double *h, *wy, *best, *second;
+    int64_t* g;
     if (B < 0 || k < 1 || V < 1 || D < 1 || !hidden || !weight || !tokens || !accepted_len || !out_tokens) return -1;
-    h = (double*)malloc(sizeof(double) * D);
-    if (!h) return -1;
-    for (b = 0; b < B; ++b) {
-        const int32_t* x = tokens + b * k;
-        int32_t r = k;
-        int valid = tokens_valid(x, k, V);
-        for (i = 0; i <= k; ++i) {
-            double best = -INFINITY, second = -INFINITY;
-            int64_t g = 0;
-            const uint16_t* hr = hidden + (b * (k + 1) + i) * D;
-            for (d = 0; d < D; ++d) h[d] = orc_decode_bf16(hr[d]);
-            for (y = 0; y < V; ++y) {
-                const uint16_t* wr = weight + y * D;
-                double s = 0.0;
-                for (d = 0; d < D; ++d) s += h[d] * orc_decode_bf16(wr[d]);
-                if (s > best) {
-                    second = best;
-                    best = s;
-                    g = y;
-                } else if (s > second) {
-                    second = s;
-                }
-            }
-            if (argmax_out) argmax_out[b * (k + 1) + i] = (int32_t)g;
-            if (top2_gap) top2_gap[b * (k + 1) + i] = best - second;
-            if (i < k && r == k && valid && x[i] != g) r = i;
-            if (i == r) {
-                /* the target's token at the first mismatch (or after all k) */
-                out_tokens[b * (k + 1) + i] = (int32_t)g;
+    h = (double*)malloc(sizeof(double) * (rows * D + D + 2 * rows + 1));
+    g = (int64_t*)malloc(sizeof(int64_t) * (rows + 1));
+    if (!h || !g) {
+        free(h);
+        free(g);
+        return -1;
+    }
+    wy = h + rows * D;
+    best = wy + D;
+    second = best + rows;
+    for (row = 0; row < rows; ++row) {
+        for (d = 0; d < D; ++d) h[row * D + d] = orc_decode_bf16(hidden[row * D + d]);
+        best[row] = -INFINITY;
+        second[row] = -INFINITY;
+        g[row] = 0;
+    }
+    for (y = 0; y < V; ++y) {
+        for (d = 0; d < D; ++d) wy[d] = orc_decode_bf16(weight[y * D + d]);
+        for (row = 0; row < rows; ++row) {
+            const double* hr = h + row * D;
+            double s = 0.0;
+            for (d = 0; d < D; ++d) s += hr[d] * wy[d];
+            if (s > best[row]) {
+                second[row] = best[row];
+                best[row] = s;
+                g[row] = y;
+            } else if (s > second[row]) {
+                second[row] = s;
             }
         }
-        if (!valid) {
+    }
+    for (b = 0; b < B; ++b) {
+        const int32_t* x = tokens + b * k;
+        const int64_t r0 = b * (k + 1);
+        int32_t r = k;
+        for (i = 0; i <= k; ++i) {
+            if (argmax_out) argmax_out[r0 + i] = (int32_t)g[r0 + i];
+            if (top2_gap) top2_gap[r0 + i] = best[r0 + i] - second[r0 + i];
+        }
+        if (!tokens_valid(x, k, V)) {
             accepted_len[b] = -1;
-            for (i = 0; i <= k; ++i) out_tokens[b * (k + 1) + i] = -1;
+            for (i = 0; i <= k; ++i) out_tokens[r0 + i] = -1;
             continue;
+        }
+        for (i = 0; i < k; ++i) {
+            if (x[i] != g[r0 + i]) {
+                r = i;
+                break;
+            }
         }
         accepted_len[b] = r;
         for (i = 0; i <= k; ++i) {
-            if (i < r) out_tokens[b * (k + 1) + i] = x[i];
-            else if (i > r) out_tokens[b * (k + 1) + i] = -1;
+            if (i < r) out_tokens[r0 + i] = x[i];
+            else if (i == r) out_tokens[r0 + i] = (int32_t)g[r0 + i];  /* the target's token */
+            else out_tokens[r0 + i] = -1;
         }
     }
     free(h);
+    free(g);
     return 0;
 }

@@ -10,7 +10,7 @@ library is not built, importing works but every call raises.
 
 Names follow the C ABI in ``include/specverify.h``: ``sv_verify`` ->
 :func:`verify`, ``sv_vat_labels`` -> :func:`vat_labels`, ``sv_vat_loss`` ->
-:func:`vat_loss`.
+:func:`vat_loss`, ``sv_verify_lm_head_greedy`` -> :func:`verify_lm_head_greedy`.
 """
 from __future__ import annotations
 
@@ -18,7 +18,8 @@ import ctypes
 import os
 from typing import NamedTuple, Optional
 
-__all__ = ["verify", "vat_labels", "vat_loss", "accept_histogram", "Verifier", "VatLabeler", "VatLoss",
+__all__ = ["verify", "vat_labels", "vat_loss", "verify_lm_head_greedy", "accept_histogram", "Verifier",
+           "VatLabeler", "VatLoss", "LmHeadVerifier",
            "DraftLengthController", "SVError", "library_path", "load_library", "SV_F32", "SV_BF16", "SV_DRAFT_LOGITS",
            "SV_DRAFT_ONEHOT", "STATUS"]
 
@@ -29,11 +30,13 @@ SV_F32, SV_BF16 = 0, 1
 SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT = 0, 1
 STATUS = {0: "SV_OK", 1: "SV_ERR_NULL_ARG", 2: "SV_ERR_BAD_SHAPE", 3: "SV_ERR_BAD_DTYPE",
           4: "SV_ERR_BAD_TEMPERATURE", 5: "SV_ERR_BAD_DRAFT_KIND", 6: "SV_ERR_WORKSPACE_TOO_SMALL",
-          7: "SV_ERR_BAD_DECAY", 8: "SV_ERR_HIP", 9: "SV_ERR_BAD_HARD_WEIGHT", 10: "SV_ERR_BAD_CONTROL"}
+          7: "SV_ERR_BAD_DECAY", 8: "SV_ERR_HIP", 9: "SV_ERR_BAD_HARD_WEIGHT", 10: "SV_ERR_BAD_CONTROL",
+          11: "SV_ERR_MISALIGNED"}
 
 EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_size", "sv_verify",
                     "sv_vat_workspace_size", "sv_vat_labels", "sv_vat_loss_workspace_size", "sv_vat_loss",
-                    "sv_accept_histogram", "sv_draft_len_init", "sv_draft_len_update")
+                    "sv_lm_head_workspace_size", "sv_verify_lm_head_greedy", "sv_accept_histogram",
+                    "sv_draft_len_init", "sv_draft_len_update")
 
 
 class SVError(RuntimeError):
@@ -61,6 +64,11 @@ class VatLossDesc(ctypes.Structure):
     _fields_ = [("blocks", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float), ("decay", ctypes.c_float),
                 ("hard_weight", ctypes.c_float), ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+
+
+class LmHeadDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
 
 
 SV_MAX_DRAFT_CHOICES = 8
@@ -106,6 +114,10 @@ def load_library():
     lib.sv_vat_loss_workspace_size.argtypes = [ctypes.POINTER(VatLossDesc), ctypes.POINTER(sz)]
     lib.sv_vat_loss.restype = ctypes.c_int
     lib.sv_vat_loss.argtypes = [ctypes.POINTER(VatLossDesc)] + [vp] * 14 + [sz, vp]
+    lib.sv_lm_head_workspace_size.restype = ctypes.c_int
+    lib.sv_lm_head_workspace_size.argtypes = [ctypes.POINTER(LmHeadDesc), ctypes.POINTER(sz)]
+    lib.sv_verify_lm_head_greedy.restype = ctypes.c_int
+    lib.sv_verify_lm_head_greedy.argtypes = [ctypes.POINTER(LmHeadDesc)] + [vp] * 7 + [sz, vp]
     i32 = ctypes.c_int32
     lib.sv_accept_histogram.restype = ctypes.c_int
     lib.sv_accept_histogram.argtypes = [vp, i32, i32, vp, vp]
@@ -394,6 +406,67 @@ def vat_loss(target, draft, draft_tokens, uniforms, hard_tokens, temperature: fl
     Labels, weights, the soft and hard terms per position and the weighted loss per block."""
     return VatLoss(target, draft, draft_tokens, uniforms, hard_tokens, temperature, decay, hard_weight,
                    return_probs=return_probs, return_row_stats=return_row_stats, workspace=workspace)()
+
+
+class LmHeadOutput(NamedTuple):
+    accepted_len: "object"
+    out_tokens: "object"
+    argmax: "object"
+
+
+class LmHeadVerifier:
+    """A prepared sv_verify_lm_head_greedy call (greedy verification with the
+    target's logits formed from its hidden states inside the call)."""
+
+    def __init__(self, hidden_states, weight, draft_tokens, *, return_argmax: bool = False, workspace=None,
+                 probe=None):
+        torch = _torch()
+        lib = load_library()
+        if hidden_states.dim() != 3 or weight.dim() != 2:
+            raise ValueError("hidden_states must be [B][k+1][D] and weight [V][D]")
+        B, kp1, D = (int(s) for s in hidden_states.shape)
+        k = kp1 - 1
+        V = int(weight.shape[0])
+        device = hidden_states.device
+        _check_dev("hidden_states", hidden_states, device, torch.bfloat16)
+        _check_dev("weight", weight, device, torch.bfloat16, (V, D))
+        _check_dev("draft_tokens", draft_tokens, device, torch.int32, (B, k))
+        self.desc = LmHeadDesc(B, k, V, D, None, None)
+        if probe is not None:
+            self.desc.probe_start, self.desc.probe_stop = probe
+        nbytes = ctypes.c_size_t()
+        st = lib.sv_lm_head_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
+        if st:
+            raise SVError(st, "sv_lm_head_workspace_size", lib)
+        if workspace is None:
+            workspace = _WS.get(device, nbytes.value)
+        elif workspace.numel() * workspace.element_size() < nbytes.value:
+            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+        self.accepted_len = torch.empty(B, dtype=torch.int32, device=device)
+        self.out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
+        self.argmax = torch.empty((B, k + 1), dtype=torch.int32, device=device) if return_argmax else None
+        self._keep = (hidden_states, weight, draft_tokens, workspace)
+        self._lib = lib
+        self._device = device
+        self._args = (ctypes.byref(self.desc), _ptr(hidden_states), _ptr(weight), _ptr(draft_tokens),
+                      _ptr(self.accepted_len), _ptr(self.out_tokens), _ptr(self.argmax), workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size())
+
+    def __call__(self, stream: Optional[int] = None) -> LmHeadOutput:
+        s = _stream_handle(self._device) if stream is None else stream
+        st = self._lib.sv_verify_lm_head_greedy(*self._args, s)
+        if st:
+            raise SVError(st, "sv_verify_lm_head_greedy", self._lib)
+        return LmHeadOutput(self.accepted_len, self.out_tokens, self.argmax)
+
+
+def verify_lm_head_greedy(hidden_states, weight, draft_tokens, *, return_argmax: bool = False,
+                          workspace=None) -> LmHeadOutput:
+    """sv_verify_lm_head_greedy on torch tensors: hidden_states [B][k+1][D]
+    bf16, weight [V][D] bf16, draft_tokens [B][k] int32.  Returns
+    (accepted_len [B], out_tokens [B][k+1], argmax [B][k+1] or None)."""
+    return LmHeadVerifier(hidden_states, weight, draft_tokens, return_argmax=return_argmax,
+                          workspace=workspace)()
 
 
 def accept_histogram(accepted_len, k: int, out=None, stream: Optional[int] = None):

@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "sv_launch.h"
+#include "sv_lmhead.h"
 #include "specverify.h"
 
 namespace sv {
@@ -120,6 +121,36 @@ void carve_workspace(const Shape& s, void* ws, Plan* pl) {
     pl->tag = next_tag();
 }
 
+// LM-head greedy verification: shape checks and the workspace of run partials.
+struct LmShape {
+    int64_t batch, k, vocab, hidden, rows, m_tiles, n_runs;
+};
+
+constexpr int64_t kMaxHidden = 65536;
+
+sv_status check_lm_shape(const sv_lm_head_desc* d, LmShape* s) {
+    if (d->batch < 0 || d->num_draft < 1 || d->num_draft > SV_MAX_DRAFT || d->vocab < 1 || d->vocab > kMaxVocab ||
+        d->hidden < kLmBK || d->hidden > kMaxHidden || d->hidden % kLmBK != 0)
+        return SV_ERR_BAD_SHAPE;
+    s->batch = d->batch;
+    s->k = d->num_draft;
+    s->vocab = d->vocab;
+    s->hidden = d->hidden;
+    s->rows = s->batch * (s->k + 1);
+    s->m_tiles = ceil_div(s->rows, kLmBM);
+    s->n_runs = ceil_div(ceil_div(s->vocab, kLmBN), kLmRunTiles);
+    if (s->rows > 0x7fffffffLL) return SV_ERR_BAD_SHAPE;
+    // Launch limit: blocks * threads of one grid dimension below 2^32.
+    const int64_t blocks = ceil_div(s->n_runs, kXcds) * kXcds * s->m_tiles;
+    if (blocks * kLmThreads > 0xffffffffLL) return SV_ERR_BAD_SHAPE;
+    return SV_OK;
+}
+
+size_t lm_workspace_bytes(const LmShape& s) {
+    const size_t n = static_cast<size_t>(s.rows * s.n_runs);
+    return align_up(n * sizeof(float)) + align_up(n * sizeof(int32_t));
+}
+
 }  // namespace
 
 WorkspaceLayout workspace_layout(int64_t partial_words, int64_t batch, int64_t chunks) {
@@ -154,6 +185,7 @@ const char* sv_status_str(int status) {
         case SV_ERR_WORKSPACE_TOO_SMALL: return "SV_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the size query";
         case SV_ERR_BAD_DECAY: return "SV_ERR_BAD_DECAY: decay must be in [0, 1]";
         case SV_ERR_HIP: return "SV_ERR_HIP: a HIP launch or event record failed";
+        case SV_ERR_MISALIGNED: return "SV_ERR_MISALIGNED: hidden_states and weight must be 16-byte aligned";
         default: return "unknown status";
     }
 }
@@ -311,6 +343,50 @@ sv_status sv_accept_histogram(const int32_t* accepted_len, int32_t batch, int32_
     if (batch < 0 || k < 1 || k > SV_MAX_DRAFT) return SV_ERR_BAD_SHAPE;
     if (!hist || (batch > 0 && !accepted_len)) return SV_ERR_NULL_ARG;
     const hipError_t e = sv::launch_accept_hist(accepted_len, batch, k, hist, stream);
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes) {
+    if (!desc || !bytes) return SV_ERR_NULL_ARG;
+    sv::LmShape s;
+    const sv_status st = sv::check_lm_shape(desc, &s);
+    if (st != SV_OK) return st;
+    *bytes = sv::lm_workspace_bytes(s);
+    return SV_OK;
+}
+
+sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidden_states, const void* weight,
+                                   const int32_t* draft_tokens, int32_t* accepted_len, int32_t* out_tokens,
+                                   int32_t* argmax_out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    if (!desc) return SV_ERR_NULL_ARG;
+    sv::LmShape s;
+    const sv_status st = sv::check_lm_shape(desc, &s);
+    if (st != SV_OK) return st;
+    if (s.batch == 0) return SV_OK;
+    if (!hidden_states || !weight || !draft_tokens || !accepted_len || !out_tokens || !workspace)
+        return SV_ERR_NULL_ARG;
+    if (!sv::aligned16(hidden_states) || !sv::aligned16(weight)) return SV_ERR_MISALIGNED;
+    if (workspace_bytes < sv::lm_workspace_bytes(s)) return SV_ERR_WORKSPACE_TOO_SMALL;
+    sv::LmPlan pl{};
+    pl.hidden_states = static_cast<const uint16_t*>(hidden_states);
+    pl.weight = static_cast<const uint16_t*>(weight);
+    pl.tokens = draft_tokens;
+    pl.accepted_len = accepted_len;
+    pl.out_tokens = out_tokens;
+    pl.argmax_out = argmax_out;
+    char* base = static_cast<char*>(workspace);
+    const size_t n = static_cast<size_t>(s.rows * s.n_runs);
+    pl.part_v = reinterpret_cast<float*>(base);
+    pl.part_i = reinterpret_cast<int32_t*>(base + sv::align_up(n * sizeof(float)));
+    pl.rows = static_cast<int32_t>(s.rows);
+    pl.batch = static_cast<int32_t>(s.batch);
+    pl.k = static_cast<int32_t>(s.k);
+    pl.vocab = static_cast<int32_t>(s.vocab);
+    pl.hidden = static_cast<int32_t>(s.hidden);
+    pl.m_tiles = static_cast<int32_t>(s.m_tiles);
+    pl.n_runs = static_cast<int32_t>(s.n_runs);
+    const hipError_t e = sv::launch_lmhead(pl, stream, desc->probe_start, desc->probe_stop);
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -275,3 +275,74 @@ def test_vat_loss_null_args_and_workspace(lib):
     assert n.value > m.value
     e = _loss_desc(N=0)
     assert lib.sv_vat_loss(ctypes.byref(e), *([None] * 14), 0, None) == 0
+
+
+def _lm_desc(B=2, k=3, V=1000, D=64):
+    return sv.LmHeadDesc(B, k, V, D, None, None)
+
+
+class _LmBufs:
+    def __init__(self, B=2, k=3, V=1000, D=64):
+        self.hidden = np.zeros(B * (k + 1) * D, np.uint16)
+        self.weight = np.zeros(V * D, np.uint16)
+        self.tokens = np.zeros(B * k, np.int32)
+        self.acc = np.full(B, 777, np.int32)
+        self.out = np.full(B * (k + 1), 777, np.int32)
+        self.am = np.full(B * (k + 1), 777, np.int32)
+        self.ws = np.full(1 << 16, 0xAB, np.uint8)
+
+    def untouched(self):
+        return (np.all(self.acc == 777) and np.all(self.out == 777) and np.all(self.am == 777)
+                and np.all(self.ws == 0xAB))
+
+
+def _call_lm(lib, d, h, **over):
+    args = dict(hidden=h.hidden.ctypes.data, weight=h.weight.ctypes.data, tokens=h.tokens.ctypes.data,
+                acc=h.acc.ctypes.data, out=h.out.ctypes.data, am=h.am.ctypes.data, ws=h.ws.ctypes.data,
+                ws_bytes=h.ws.nbytes)
+    args.update(over)
+    return lib.sv_verify_lm_head_greedy(ctypes.byref(d) if d is not None else None, args["hidden"], args["weight"],
+                                        args["tokens"], args["acc"], args["out"], args["am"], args["ws"],
+                                        args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("field,value", [("num_draft", 0), ("num_draft", 65), ("vocab", 0), ("vocab", (1 << 24) + 1),
+                                         ("hidden", 0), ("hidden", 48), ("hidden", 16), ("hidden", 65536 + 32),
+                                         ("batch", -1)])
+def test_lm_head_rejects_bad_shape(lib, field, value):
+    d = _lm_desc()
+    setattr(d, field, value)
+    n = ctypes.c_size_t(123)
+    assert lib.sv_lm_head_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 2
+    assert n.value == 123
+    h = _LmBufs()
+    assert _call_lm(lib, d, h) == 2
+    assert h.untouched()
+
+
+def test_lm_head_workspace_holds_one_partial_per_row_and_run(lib):
+    n = ctypes.c_size_t()
+    assert lib.sv_lm_head_workspace_size(None, ctypes.byref(n)) == 1
+    assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc()), None) == 1
+    # rows = B(k+1); runs = ceil(ceil(V/128)/8): a float and an int32 each, 256-byte aligned halves
+    for B, k, V in [(2, 3, 1000), (128, 5, 151936), (320, 7, 151936), (1, 1, 1)]:
+        assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc(B, k, V, 4096)), ctypes.byref(n)) == 0
+        runs = -(-(-(-V // 128)) // 8)
+        half = -(-(B * (k + 1) * runs * 4) // 256) * 256
+        assert n.value == 2 * half, (B, k, V)
+
+
+def test_lm_head_null_misaligned_and_workspace_errors(lib):
+    h = _LmBufs()
+    d = _lm_desc()
+    assert _call_lm(lib, None, h) == 1
+    for name in ("hidden", "weight", "tokens", "acc", "out", "ws"):
+        assert _call_lm(lib, d, h, **{name: None}) == 1, name
+    assert _call_lm(lib, d, h, hidden=h.hidden.ctypes.data + 2) == 11
+    assert _call_lm(lib, d, h, weight=h.weight.ctypes.data + 8) == 11
+    n = ctypes.c_size_t()
+    assert lib.sv_lm_head_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert _call_lm(lib, d, h, ws_bytes=n.value - 1) == 6
+    assert h.untouched()
+    e = _lm_desc(B=0)
+    assert lib.sv_verify_lm_head_greedy(ctypes.byref(e), *([None] * 7), 0, None) == 0

@@ -26,6 +26,19 @@ grpo_greedy    same logits as grpo, T=0; x = argmax d (lowest id)
 vat            N=2048 blocks, k=16, V=128256, fp32, T=1, decay 0.8; t = 4z, d = t + 0.25z',
                x ~ softmax(d/T); target has k rows per block (no bonus row)
 =============  ======================================================================
+
+LM-head workloads (greedy verification with the logits formed from hidden
+states ``h`` [B][k+1][D] and output-layer weights ``W`` [V][D], both bf16):
+``W = z_w / sqrt(D)`` (so every logit h . w_y of an unplanted row is about
+N(0, |h|^2 / D)), ``h = z + plant * W[t]`` for a planted token t per
+position (t uniform over [0, V)), so that t is the likely argmax by a margin
+of about ``plant``; draft token = t w.p. ``hit``, else uniform over [0, V).
+
+=================  ===================================================================
+lmhead_tiny        B=6, k=4, V=1000, D=128, plant 8, hit 0.8
+lmhead_selfdraft   B=128, k=5, V=151936, D=4096, plant 8, hit 0.95
+lmhead_grpo        B=320, k=7, V=151936, D=4096, plant 8, hit 0.9
+=================  ===================================================================
 """
 from __future__ import annotations
 
@@ -37,7 +50,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Config", "Workload", "CONFIGS", "get_config", "generate", "generate_on_device", "to_device",
-           "round_to_bf16_bits", "bf16_bits_to_f32"]
+           "round_to_bf16_bits", "bf16_bits_to_f32", "LmHeadConfig", "LmHeadWorkload", "LM_CONFIGS",
+           "lm_head_weight", "generate_lm_head", "lm_head_to_device"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -279,3 +293,96 @@ def to_device(wl: Workload, device):
         return torch.from_numpy(a).to(device)
 
     return up(wl.target), up(wl.draft), up(wl.tokens), up(wl.uniforms)
+
+
+@dataclasses.dataclass(frozen=True)
+class LmHeadConfig:
+    name: str
+    B: int
+    k: int
+    V: int
+    D: int
+    plant: float = 8.0   # margin planted for the intended token of each position
+    hit: float = 0.9     # probability that a draft token is the planted token
+    seed: int = 11
+
+    @property
+    def rows(self) -> int:
+        return self.B * (self.k + 1)
+
+    def flops(self) -> int:
+        """Multiply-adds of the logits, counted as 2 flops each."""
+        return 2 * self.rows * self.V * self.D
+
+    def scaled(self, **changes) -> "LmHeadConfig":
+        return dataclasses.replace(self, **changes)
+
+
+LM_CONFIGS = {
+    "lmhead_tiny": LmHeadConfig("lmhead_tiny", 6, 4, 1000, 128, hit=0.8),
+    "lmhead_selfdraft": LmHeadConfig("lmhead_selfdraft", 128, 5, 151936, 4096, hit=0.95),
+    "lmhead_grpo": LmHeadConfig("lmhead_grpo", 320, 7, 151936, 4096, hit=0.9),
+}
+
+_W_SLAB = 4096  # weight rows drawn per generator stream
+
+
+@dataclasses.dataclass
+class LmHeadWorkload:
+    config: LmHeadConfig
+    hidden: np.ndarray    # [B][k+1][D] uint16 (bf16 bits)
+    weight: np.ndarray    # [V][D] uint16
+    tokens: np.ndarray    # [B][k] int32
+    planted: np.ndarray   # [B][k+1] int32: the token each position was planted for
+
+
+def lm_head_weight(cfg: LmHeadConfig, workers: Optional[int] = None) -> np.ndarray:
+    """W [V][D] as bf16 bits; rows drawn in slabs of 4096, one stream each."""
+    w = np.empty((cfg.V, cfg.D), dtype=np.uint16)
+    scale = np.float32(1.0 / np.sqrt(cfg.D))
+
+    def slab(s0):
+        s1 = min(cfg.V, s0 + _W_SLAB)
+        z = _rng(cfg.seed, 2, s0 // _W_SLAB).standard_normal((s1 - s0, cfg.D), dtype=np.float32)
+        w[s0:s1] = round_to_bf16_bits(z * scale)
+
+    starts = list(range(0, cfg.V, _W_SLAB))
+    if workers is None:
+        workers = max(1, min(16, os.cpu_count() or 1))
+    if workers == 1 or len(starts) == 1:
+        for s0 in starts:
+            slab(s0)
+    else:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(slab, starts))
+    return w
+
+
+def generate_lm_head(cfg: LmHeadConfig, weight: Optional[np.ndarray] = None) -> LmHeadWorkload:
+    """All B sequences of ``cfg``; sequence b draws from its own streams."""
+    w = lm_head_weight(cfg) if weight is None else weight
+    assert w.shape == (cfg.V, cfg.D) and w.dtype == np.uint16
+    hidden = np.empty((cfg.B, cfg.k + 1, cfg.D), dtype=np.uint16)
+    tokens = np.empty((cfg.B, cfg.k), dtype=np.int32)
+    planted = np.empty((cfg.B, cfg.k + 1), dtype=np.int32)
+    for b in range(cfg.B):
+        r = _rng(cfg.seed, 0, b)
+        t = r.integers(0, cfg.V, size=cfg.k + 1)
+        z = r.standard_normal((cfg.k + 1, cfg.D), dtype=np.float32)
+        hidden[b] = round_to_bf16_bits(z + np.float32(cfg.plant) * bf16_bits_to_f32(w[t]))
+        planted[b] = t
+        rx = _rng(cfg.seed, 1, b)
+        hit = rx.random(cfg.k) < cfg.hit
+        other = rx.integers(0, cfg.V, size=cfg.k)
+        tokens[b] = np.where(hit, t[: cfg.k], other)
+    return LmHeadWorkload(cfg, hidden, w, tokens, planted)
+
+
+def lm_head_to_device(wl: LmHeadWorkload, device):
+    """(hidden bf16, weight bf16, tokens int32) as torch tensors on `device`."""
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    return bf(wl.hidden), bf(wl.weight), torch.from_numpy(np.ascontiguousarray(wl.tokens)).to(device)
