@@ -29,6 +29,17 @@ twice the 256 MB last-level (MALL) cache, so the figures are HBM figures.
 The default warm-up (200 calls, tens of milliseconds) lets the GPU reach its
 steady clocks; with a few warm-up calls the first timed calls run slower.
 
+    python bench.py --workload lmhead_selfdraft|lmhead_grpo [--steps K]
+
+times greedy verification with the target's logits formed inside the call
+from its hidden states and output layer (sv_verify_lm_head_greedy: the
+k_lmhead_argmax GEMM with its argmax epilogue, then the per-sequence
+finisher), B(k+1) hidden states of size D=4096 against a [151936][4096] bf16
+output layer.  value = verified draft positions per second; roofline: the
+GEMM's 2 B(k+1) V D flops per launch / its mean duration (HIP events recorded
+around every GEMM launch on the launch stream) against the bf16 dense MFMA
+peak.
+
     python bench.py --copy-probe [--steps K]
 
 runs K plain device-to-device copies of 1 GiB (torch's copy kernel) and
@@ -51,6 +62,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 * 2**20
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 METRIC = "verified draft positions/sec + achieved HBM GB/s (V=151936 bf16, k=5..16)"
@@ -102,7 +114,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, source_hash=None):
     """HBM bytes per launch from committed rocprofv3 PMC counters, if they were
     taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "pmc_%s_%s.json" % (kernel, workload))
@@ -110,7 +122,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != (source_hash or kernel_source_hash()):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -149,6 +161,105 @@ def cpu_baseline(cfg, seconds: float, loss: bool = False):
             "sample": "%d whole %s (%d positions; cycling over the first %d) of the %s workload, fp64 C oracle, "
                       "1 thread, %.1f s" % (done, what, done * cfg.k, n_sample, cfg.name, dt),
             "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+
+
+def lm_kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("sv_lmhead.hip", "sv_lmhead.h"):
+        with open(os.path.join(ROOT, "speculative_decoding_verification_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def lm_cpu_baseline(cfg, wl, seconds: float):
+    """The oracle as it is over whole sequences of the LM-head workload (fp64
+    logits over the full vocabulary, one thread) until `seconds` elapsed."""
+    import oracle
+
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        b = done % cfg.B
+        oracle.lm_head_greedy(wl.hidden[b:b + 1], wl.weight, wl.tokens[b:b + 1])
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * cfg.k / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": "%d whole sequences (%d positions, %d logits of dimension %d each) of the %s workload, fp64 C "
+                      "oracle, 1 thread, %.1f s" % (done, done * cfg.k, done * (cfg.k + 1) * cfg.V, cfg.D, cfg.name, dt),
+            "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+
+
+def bench_lm_head(args) -> int:
+    import torch
+
+    import speculative_decoding_verification_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    cfg = workloads.LM_CONFIGS[args.workload]
+    print("bench: generating %s (B=%d k=%d V=%d D=%d)" % (cfg.name, cfg.B, cfg.k, cfg.V, cfg.D), file=sys.stderr,
+          flush=True)
+    wl = workloads.generate_lm_head(cfg)
+    h, w, x = workloads.lm_head_to_device(wl, dev)
+    ev = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ver = sv.LmHeadVerifier(h, w, x)
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    region = (ev.create(), ev.create())
+    print("bench: %d warmup + %d timed steps" % (args.warmup, args.steps), file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        ver(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(region[0], stream)
+    for i in range(args.steps):
+        ver.desc.probe_start, ver.desc.probe_stop = pairs[i]
+        ver(stream)
+    ev.record(region[1], stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gemm_ms = sum(ev.elapsed_ms(a, b) for a, b in pairs) / args.steps
+    step_device_ms = ev.elapsed_ms(*region) / args.steps
+    ver.desc.probe_start = ver.desc.probe_stop = None
+    for e in [e for p in pairs for e in p] + list(region):
+        ev.destroy(e)
+    acc = ver.accepted_len.float()
+    flops = cfg.flops()
+    tflops = flops / (gemm_ms * 1e-3) / 1e12
+    ms_per_step = elapsed * 1e3 / args.steps
+    res = {
+        "metric": METRIC,
+        "value": cfg.B * cfg.k * args.steps / elapsed,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
+                   "hidden": cfg.D, "temperature": 0.0, "weights": "bf16", "accumulate": "f32"},
+        "roofline": {"bound": "mfma", "kernel": "k_lmhead_argmax", "achieved": tflops,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("k_lmhead_argmax", args.workload, lm_kernel_source_hash()),
+                     "flops_per_launch": flops, "mean_launch_us": gemm_ms * 1e3,
+                     "weight_bytes_per_launch": cfg.V * cfg.D * 2,
+                     "hbm_floor_us": cfg.V * cfg.D * 2 / (HBM_PEAK_GBPS * 1e9) * 1e6},
+        "device_ms_per_step": step_device_ms,
+        "mean_accepted_len": acc.mean().item(),
+        "full_acceptance": int((acc == cfg.k).sum().item()),
+    }
+    del ver, h, w, x
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
+        res["cpu_baseline"] = lm_cpu_baseline(cfg, wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def copy_probe(steps: int) -> int:
@@ -192,7 +303,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="selfdraft",
-                    choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "vat_loss", "tiny"])
+                    choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "vat_loss", "tiny",
+                             "lmhead_selfdraft", "lmhead_grpo"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -210,6 +322,9 @@ def main(argv=None):
         return 1
     if args.copy_probe:
         return copy_probe(args.steps)
+
+    if args.workload.startswith("lmhead_"):
+        return bench_lm_head(args)
 
     import speculative_decoding_verification_amd as sv
     import workloads

@@ -178,7 +178,7 @@ typedef struct sv_lm_head_desc {
     int32_t batch;       /* B >= 0 sequences */
     int32_t num_draft;   /* k in [1, 64] */
     int32_t vocab;       /* V in [1, 2^24]: rows of the output layer */
-    int32_t hidden;      /* D: hidden size, a multiple of 32 in [32, 65536] */
+    int32_t hidden;      /* D: hidden size, a multiple of 64 in [64, 65536] */
     hipEvent_t probe_start;
     hipEvent_t probe_stop;
 } sv_lm_head_desc;

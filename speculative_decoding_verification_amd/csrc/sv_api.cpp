@@ -121,33 +121,26 @@ void carve_workspace(const Shape& s, void* ws, Plan* pl) {
     pl->tag = next_tag();
 }
 
-// LM-head greedy verification: shape checks and the workspace of run partials.
-struct LmShape {
-    int64_t batch, k, vocab, hidden, rows, m_tiles, n_runs;
-};
-
+// LM-head greedy verification: shape checks and the workspace of partials.
 constexpr int64_t kMaxHidden = 65536;
 
-sv_status check_lm_shape(const sv_lm_head_desc* d, LmShape* s) {
+sv_status check_lm_shape(const sv_lm_head_desc* d, LmPlan* pl) {
     if (d->batch < 0 || d->num_draft < 1 || d->num_draft > SV_MAX_DRAFT || d->vocab < 1 || d->vocab > kMaxVocab ||
-        d->hidden < kLmBK || d->hidden > kMaxHidden || d->hidden % kLmBK != 0)
+        d->hidden < kLmHiddenMultiple || d->hidden > kMaxHidden || d->hidden % kLmHiddenMultiple != 0)
         return SV_ERR_BAD_SHAPE;
-    s->batch = d->batch;
-    s->k = d->num_draft;
-    s->vocab = d->vocab;
-    s->hidden = d->hidden;
-    s->rows = s->batch * (s->k + 1);
-    s->m_tiles = ceil_div(s->rows, kLmBM);
-    s->n_runs = ceil_div(ceil_div(s->vocab, kLmBN), kLmRunTiles);
-    if (s->rows > 0x7fffffffLL) return SV_ERR_BAD_SHAPE;
-    // Launch limit: blocks * threads of one grid dimension below 2^32.
-    const int64_t blocks = ceil_div(s->n_runs, kXcds) * kXcds * s->m_tiles;
-    if (blocks * kLmThreads > 0xffffffffLL) return SV_ERR_BAD_SHAPE;
+    const int64_t rows = static_cast<int64_t>(d->batch) * (d->num_draft + 1);
+    if (rows > 0x7fffffffLL) return SV_ERR_BAD_SHAPE;
+    pl->rows = static_cast<int32_t>(rows);
+    pl->batch = d->batch;
+    pl->k = d->num_draft;
+    pl->vocab = d->vocab;
+    pl->hidden = d->hidden;
+    lmhead_shape(pl);
     return SV_OK;
 }
 
-size_t lm_workspace_bytes(const LmShape& s) {
-    const size_t n = static_cast<size_t>(s.rows * s.n_runs);
+size_t lm_workspace_bytes(const LmPlan& pl) {
+    const size_t n = static_cast<size_t>(pl.rows) * static_cast<size_t>(pl.n_parts);
     return align_up(n * sizeof(float)) + align_up(n * sizeof(int32_t));
 }
 
@@ -348,10 +341,10 @@ sv_status sv_accept_histogram(const int32_t* accepted_len, int32_t batch, int32_
 
 sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes) {
     if (!desc || !bytes) return SV_ERR_NULL_ARG;
-    sv::LmShape s;
-    const sv_status st = sv::check_lm_shape(desc, &s);
+    sv::LmPlan pl{};
+    const sv_status st = sv::check_lm_shape(desc, &pl);
     if (st != SV_OK) return st;
-    *bytes = sv::lm_workspace_bytes(s);
+    *bytes = sv::lm_workspace_bytes(pl);
     return SV_OK;
 }
 
@@ -360,15 +353,14 @@ sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidd
                                    int32_t* argmax_out, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream) {
     if (!desc) return SV_ERR_NULL_ARG;
-    sv::LmShape s;
-    const sv_status st = sv::check_lm_shape(desc, &s);
+    sv::LmPlan pl{};
+    const sv_status st = sv::check_lm_shape(desc, &pl);
     if (st != SV_OK) return st;
-    if (s.batch == 0) return SV_OK;
+    if (pl.batch == 0) return SV_OK;
     if (!hidden_states || !weight || !draft_tokens || !accepted_len || !out_tokens || !workspace)
         return SV_ERR_NULL_ARG;
     if (!sv::aligned16(hidden_states) || !sv::aligned16(weight)) return SV_ERR_MISALIGNED;
-    if (workspace_bytes < sv::lm_workspace_bytes(s)) return SV_ERR_WORKSPACE_TOO_SMALL;
-    sv::LmPlan pl{};
+    if (workspace_bytes < sv::lm_workspace_bytes(pl)) return SV_ERR_WORKSPACE_TOO_SMALL;
     pl.hidden_states = static_cast<const uint16_t*>(hidden_states);
     pl.weight = static_cast<const uint16_t*>(weight);
     pl.tokens = draft_tokens;
@@ -376,16 +368,9 @@ sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidd
     pl.out_tokens = out_tokens;
     pl.argmax_out = argmax_out;
     char* base = static_cast<char*>(workspace);
-    const size_t n = static_cast<size_t>(s.rows * s.n_runs);
+    const size_t n = static_cast<size_t>(pl.rows) * static_cast<size_t>(pl.n_parts);
     pl.part_v = reinterpret_cast<float*>(base);
     pl.part_i = reinterpret_cast<int32_t*>(base + sv::align_up(n * sizeof(float)));
-    pl.rows = static_cast<int32_t>(s.rows);
-    pl.batch = static_cast<int32_t>(s.batch);
-    pl.k = static_cast<int32_t>(s.k);
-    pl.vocab = static_cast<int32_t>(s.vocab);
-    pl.hidden = static_cast<int32_t>(s.hidden);
-    pl.m_tiles = static_cast<int32_t>(s.m_tiles);
-    pl.n_runs = static_cast<int32_t>(s.n_runs);
     const hipError_t e = sv::launch_lmhead(pl, stream, desc->probe_start, desc->probe_stop);
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

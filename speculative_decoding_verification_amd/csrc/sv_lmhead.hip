@@ -11,23 +11,29 @@
 // Kernels:
 //  k_lmhead_argmax   a bf16 GEMM H . W^T on the matrix cores
 //                    (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with an
-//                    argmax epilogue.  A workgroup owns 128 hidden rows and a
-//                    run of 8 vocabulary tiles of 128; per tile it stages
-//                    32-wide slices of K for both operands in LDS (double
-//                    buffered), each wave computes a 64 x 64 block, and the
-//                    epilogue folds the tile into a running (max, lowest
-//                    index) per row.  The run's result is one partial per row.
-//                    Workgroups of one vocabulary run sit on one XCD (grid
-//                    index = XCD + 8 * slot), so the run's weight rows are
-//                    fetched into that XCD's L2 once for all its row tiles.
+//                    argmax epilogue.  A work item is a 256 x 256 tile (hidden
+//                    rows x vocabulary columns); its K dimension is staged in
+//                    LDS 64 at a time (double buffered, the next slice's global
+//                    loads in flight during the current slice's MFMAs); each
+//                    of the 8 wavefronts computes a 128 x 64 block; the
+//                    epilogue reduces the tile to (max, lowest index) per row,
+//                    one partial per row and vocabulary tile.  The grid is
+//                    persistent, one workgroup per compute unit, each taking
+//                    every G-th item: all workgroups advance through the
+//                    items in step, and the items a die (XCD) takes in one
+//                    step are consecutive, so the row tiles of one vocabulary
+//                    tile run side by side on one die and share its weight
+//                    rows in that die's L2.
 //  k_lmhead_finish   per sequence: combines its rows' partials, decides every
 //                    position on one lane, writes accepted_len and
 //                    out_tokens.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 
+#include "specverify.h"
 #include "sv_lmhead.h"
 
 namespace sv {
@@ -36,7 +42,9 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kLdsStride = kLmBK + 8;  // bf16 per staged row: 80 bytes, shifts banks row to row
+constexpr int kLmMaxRows = SV_MAX_DRAFT + 1;  // positions of one sequence
+
+constexpr int kLdsStride = kLmBK + 8;  // bf16 per staged row: 16 bytes of padding shift the banks row to row
 
 __device__ __forceinline__ float neg_inf_f() { return -__builtin_inff(); }
 
@@ -70,79 +78,76 @@ __device__ __forceinline__ void half_wave_argmax(float& v, int& i) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__global__ __launch_bounds__(kLmThreads) void k_lmhead_argmax(LmPlan pl) {
+__global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_argmax(LmPlan pl) {
+    constexpr int FM = kLmWaveM / 32;  // 32 x 32 fragments per wavefront block
+    constexpr int FN = kLmWaveN / 32;
+    constexpr int WAVES_M = kLmBM / kLmWaveM;
+    constexpr int WAVES_N = kLmBN / kLmWaveN;
+    static_assert(WAVES_M * WAVES_N * 64 == kLmThreads, "one wavefront per block of the tile");
+    constexpr int ROWS_PER_PASS = kLmThreads / (kLmBK / 8);  // tile rows one pass of 16-byte pieces covers
+    constexpr int PA = kLmBM / ROWS_PER_PASS;                 // pieces per thread: A
+    constexpr int PB = kLmBN / ROWS_PER_PASS;                 // and B
+    static_assert(PA * ROWS_PER_PASS == kLmBM && PB * ROWS_PER_PASS == kLmBN, "whole passes");
+    static_assert(kLmHiddenMultiple % kLmBK == 0, "whole K slices");
     __shared__ __attribute__((aligned(16))) uint16_t sa[2][kLmBM * kLdsStride];
     __shared__ __attribute__((aligned(16))) uint16_t sb[2][kLmBN * kLdsStride];
-    __shared__ float cand_v[2][kLmBM];
-    __shared__ int cand_i[2][kLmBM];
-    __shared__ float run_v[kLmBM];
-    __shared__ int run_i[kLmBM];
-
-    // Grid index -> (vocabulary run ng, row tile mt); all row tiles of a run
-    // share an XCD (blocks are spread over the 8 XCDs by index mod 8).
-    const int x = blockIdx.x;
-    const int slot = x / kXcds;
-    const int mt = slot % pl.m_tiles;
-    const int ng = (slot / pl.m_tiles) * kXcds + x % kXcds;
-    if (ng >= pl.n_runs) return;
+    __shared__ float cand_v[WAVES_N][kLmBM];
+    __shared__ int cand_i[WAVES_N][kLmBM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave & 1;   // 64-row half of the tile
-    const int wn = wave >> 1;  // 64-column half of the tile
-    const int m0 = mt * kLmBM;
+    const int wm = wave % WAVES_M;  // row block of the tile
+    const int wn = wave / WAVES_M;  // column block of the tile
     const int D = pl.hidden;
     const int kblocks = D / kLmBK;
+    const int64_t items = lmhead_items(pl);
+    const int G = gridDim.x;  // a multiple of kXcds
+    // Blocks are dealt to the XCDs by index mod 8: give each die a run of
+    // consecutive items per step.
+    const int slot = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
 
-    for (int r = tid; r < kLmBM; r += kLmThreads) {
-        run_v[r] = neg_inf_f();
-        run_i[r] = INT_MAX;
-    }
+    // Piece q of a thread: tile row tid / 4 + ROWS_PER_PASS q, K segment
+    // tid % 4 (8 bf16 each).  Rows past the end of H or W are read as the
+    // last row (their results are never written or are masked out), so no
+    // load is guarded.
+    const int prow = tid / (kLmBK / 8);
+    const int pseg = tid % (kLmBK / 8);
+    uint16_t* const sa_st = &sa[0][prow * kLdsStride + pseg * 8];
+    uint16_t* const sb_st = &sb[0][prow * kLdsStride + pseg * 8];
 
-    // Global -> LDS: 512 16-byte pieces per operand tile, two per thread.
-    // Piece c: row c / 4, K segment c % 4 (8 bf16 each).
-    int a_row[2], seg[2];
-    const uint16_t* a_src[2];
+    for (int64_t item = slot; item < items; item += G) {
+        const int mt = static_cast<int>(item % pl.m_tiles);
+        const int nt = static_cast<int>(item / pl.m_tiles);
+        const int m0 = mt * kLmBM;
+        const int n0 = nt * kLmBN;
+        const uint16_t* const a_base = pl.hidden_states + static_cast<int64_t>(m0) * D;
+        const uint16_t* const b_base = pl.weight + static_cast<int64_t>(n0) * D;
+        const int a_last = pl.rows - 1 - m0;
+        const int b_last = pl.vocab - 1 - n0;
+        uint32_t a_off[PA], b_off[PB];  // elements from the tile's base, < 256 * 65536
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int c = tid + q * kLmThreads;
-        a_row[q] = c >> 2;
-        seg[q] = c & 3;
-        const int m = m0 + a_row[q];
-        a_src[q] = m < pl.rows ? pl.hidden_states + static_cast<int64_t>(m) * D + seg[q] * 8 : nullptr;
-    }
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-
-    for (int nt = 0; nt < kLmRunTiles; ++nt) {
-        const int n0 = (ng * kLmRunTiles + nt) * kLmBN;
-        if (n0 >= pl.vocab) break;
-        const uint16_t* b_src[2];
+        for (int q = 0; q < PA; ++q) a_off[q] = static_cast<uint32_t>(min(prow + q * ROWS_PER_PASS, a_last) * D + pseg * 8);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int n = n0 + a_row[q];
-            b_src[q] = n < pl.vocab ? pl.weight + static_cast<int64_t>(n) * D + seg[q] * 8 : nullptr;
-        }
-        floatx16_t acc[2][2];
+        for (int q = 0; q < PB; ++q) b_off[q] = static_cast<uint32_t>(min(prow + q * ROWS_PER_PASS, b_last) * D + pseg * 8);
+        floatx16_t acc[FM][FN];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
+            for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
 
-        uint4 ra[2], rb[2];
+        uint4 ra[PA], rb[PB];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            ra[q] = a_src[q] ? ld16(a_src[q]) : zero;
-            rb[q] = b_src[q] ? ld16(b_src[q]) : zero;
-        }
-        __syncthreads();  // the previous tile's readers of buffer 0 are done
+        for (int q = 0; q < PA; ++q) ra[q] = ld16(a_base + a_off[q]);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            *reinterpret_cast<uint4*>(&sa[0][a_row[q] * kLdsStride + seg[q] * 8]) = ra[q];
-            *reinterpret_cast<uint4*>(&sb[0][a_row[q] * kLdsStride + seg[q] * 8]) = rb[q];
-        }
+        for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + b_off[q]);
+        __syncthreads();  // the previous item's readers of buffer 0 and of cand are done
+#pragma unroll
+        for (int q = 0; q < PA; ++q) *reinterpret_cast<uint4*>(sa_st + q * ROWS_PER_PASS * kLdsStride) = ra[q];
+#pragma unroll
+        for (int q = 0; q < PB; ++q) *reinterpret_cast<uint4*>(sb_st + q * ROWS_PER_PASS * kLdsStride) = rb[q];
         __syncthreads();
 
         for (int kb = 0; kb < kblocks; ++kb) {
@@ -151,38 +156,38 @@ __global__ __launch_bounds__(kLmThreads) void k_lmhead_argmax(LmPlan pl) {
             if (more) {
                 const int koff = (kb + 1) * kLmBK;
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    ra[q] = a_src[q] ? ld16(a_src[q] + koff) : zero;
-                    rb[q] = b_src[q] ? ld16(b_src[q] + koff) : zero;
-                }
+                for (int q = 0; q < PA; ++q) ra[q] = ld16(a_base + koff + a_off[q]);
+#pragma unroll
+                for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + koff + b_off[q]);
             }
 #pragma unroll
             for (int ks = 0; ks < kLmBK / 16; ++ks) {
                 const int kcol = ks * 16 + 8 * (lane >> 5);
-                bf16x8_t fa[2], fb[2];
+                bf16x8_t fa[FM], fb[FN];
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) {
-                    const int row = wm * 64 + mi * 32 + (lane & 31);
+                for (int mi = 0; mi < FM; ++mi) {
+                    const int row = wm * kLmWaveM + mi * 32 + (lane & 31);
                     fa[mi] = *reinterpret_cast<const bf16x8_t*>(&sa[cur][row * kLdsStride + kcol]);
                 }
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int row = wn * 64 + ni * 32 + (lane & 31);
+                for (int ni = 0; ni < FN; ++ni) {
+                    const int row = wn * kLmWaveN + ni * 32 + (lane & 31);
                     fb[ni] = *reinterpret_cast<const bf16x8_t*>(&sb[cur][row * kLdsStride + kcol]);
                 }
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
+                for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-                    for (int ni = 0; ni < 2; ++ni)
+                    for (int ni = 0; ni < FN; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
             }
             if (more) {
                 const int nxt = cur ^ 1;
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    *reinterpret_cast<uint4*>(&sa[nxt][a_row[q] * kLdsStride + seg[q] * 8]) = ra[q];
-                    *reinterpret_cast<uint4*>(&sb[nxt][a_row[q] * kLdsStride + seg[q] * 8]) = rb[q];
-                }
+                for (int q = 0; q < PA; ++q)
+                    *reinterpret_cast<uint4*>(sa_st + (nxt * kLmBM + q * ROWS_PER_PASS) * kLdsStride) = ra[q];
+#pragma unroll
+                for (int q = 0; q < PB; ++q)
+                    *reinterpret_cast<uint4*>(sb_st + (nxt * kLmBN + q * ROWS_PER_PASS) * kLdsStride) = rb[q];
             }
             __syncthreads();
         }
@@ -190,18 +195,18 @@ __global__ __launch_bounds__(kLmThreads) void k_lmhead_argmax(LmPlan pl) {
         // Epilogue: accumulator j of lane l holds row 8(j/4) + 4(l/32) + j%4
         // of a 32 x 32 block, column l % 32.
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
+        for (int mi = 0; mi < FM; ++mi) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 float v = neg_inf_f();
                 int idx = INT_MAX;
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int col = n0 + wn * 64 + ni * 32 + (lane & 31);
+                for (int ni = 0; ni < FN; ++ni) {
+                    const int col = n0 + wn * kLmWaveN + ni * 32 + (lane & 31);
                     if (col < pl.vocab) better(v, idx, acc[mi][ni][j], col);
                 }
                 half_wave_argmax(v, idx);
-                const int row = wm * 64 + mi * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+                const int row = wm * kLmWaveM + mi * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
                 if ((lane & 31) == 0) {
                     cand_v[wn][row] = v;
                     cand_i[wn][row] = idx;
@@ -210,55 +215,68 @@ __global__ __launch_bounds__(kLmThreads) void k_lmhead_argmax(LmPlan pl) {
         }
         __syncthreads();
         for (int r = tid; r < kLmBM; r += kLmThreads) {
-            float v = run_v[r];
-            int idx = run_i[r];
-            better(v, idx, cand_v[0][r], cand_i[0][r]);
-            better(v, idx, cand_v[1][r], cand_i[1][r]);
-            run_v[r] = v;
-            run_i[r] = idx;
-        }
-        // (the next tile's first barrier orders these updates before reuse)
-    }
-    __syncthreads();
-    for (int r = tid; r < kLmBM; r += kLmThreads) {
-        const int m = m0 + r;
-        if (m < pl.rows) {
-            pl.part_v[static_cast<int64_t>(m) * pl.n_runs + ng] = run_v[r];
-            pl.part_i[static_cast<int64_t>(m) * pl.n_runs + ng] = run_i[r];
+            const int m = m0 + r;
+            if (m < pl.rows) {
+                float v = cand_v[0][r];
+                int idx = cand_i[0][r];
+#pragma unroll
+                for (int c = 1; c < WAVES_N; ++c) better(v, idx, cand_v[c][r], cand_i[c][r]);
+                pl.part_v[static_cast<int64_t>(m) * pl.n_parts + nt] = v;
+                pl.part_i[static_cast<int64_t>(m) * pl.n_parts + nt] = idx;
+            }
         }
     }
 }
 
-// One wavefront per sequence: row argmaxes from the partials, then the
-// decisions on lane i for position i.
-__global__ __launch_bounds__(64) void k_lmhead_finish(LmPlan pl) {
+// One workgroup per sequence: each wavefront reduces the partials of every
+// fourth row (four independent loads per lane in flight), then wavefront 0
+// decides every position on one lane.
+constexpr int kFinishThreads = 256;
+
+__global__ __launch_bounds__(kFinishThreads) void k_lmhead_finish(LmPlan pl) {
+    __shared__ int g_row[kLmMaxRows];
     const int b = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int k = pl.k;
-    const int n_rows = k + 1;
-    int my_g = -1;    // lane i: the choice at position i < k
-    int g_last = -1;  // the choice at position k (after full acceptance)
-    for (int i = 0; i < n_rows; ++i) {
-        const int64_t row = static_cast<int64_t>(b) * n_rows + i;
+    const int n = pl.n_parts;
+    for (int i = wave; i <= k; i += kFinishThreads / 64) {
+        const int64_t row = static_cast<int64_t>(b) * (k + 1) + i;
+        const float* pv = pl.part_v + row * n;
+        const int32_t* pi = pl.part_i + row * n;
         float v = neg_inf_f();
         int idx = INT_MAX;
-        for (int c = lane; c < pl.n_runs; c += 64) better(v, idx, pl.part_v[row * pl.n_runs + c], pl.part_i[row * pl.n_runs + c]);
+        for (int c0 = 0; c0 < n; c0 += 256) {
+            float tv[4];
+            int ti[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * 64 + lane;
+                tv[u] = c < n ? pv[c] : neg_inf_f();
+                ti[u] = c < n ? pi[c] : INT_MAX;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) better(v, idx, tv[u], ti[u]);
+        }
         half_wave_argmax(v, idx);
-        const float v2 = __shfl_xor(v, 32);
-        const int i2 = __shfl_xor(idx, 32);
-        better(v, idx, v2, i2);
-        if (lane == i) my_g = idx;
-        if (i == k) g_last = idx;
-        if (pl.argmax_out && lane == 0) pl.argmax_out[row] = idx;
+        better(v, idx, __shfl_xor(v, 32), __shfl_xor(idx, 32));
+        if (lane == 0) {
+            g_row[i] = idx;
+            if (pl.argmax_out) pl.argmax_out[row] = idx;
+        }
     }
+    __syncthreads();
+    if (wave != 0) return;
     const bool active = lane < k;
     int x = 0;
     if (active) x = pl.tokens[static_cast<int64_t>(b) * k + lane];
+    const int my_g = active ? g_row[lane] : -1;
     const bool bad = active && (x < 0 || x >= pl.vocab);
     const bool invalid = __ballot(bad) != 0ull;
     const uint64_t mismatch = __ballot(active && x != my_g);
     const int r = invalid ? -1 : (mismatch ? __builtin_ctzll(mismatch) : k);
-    const int g_r = r < 0 ? -1 : (r == k ? g_last : __shfl(my_g, r));
+    const int g_r = r < 0 ? -1 : g_row[r];
     int32_t* out = pl.out_tokens + static_cast<int64_t>(b) * (k + 1);
     for (int j = lane; j <= k; j += 64) {
         if (invalid) out[j] = -1;
@@ -271,26 +289,30 @@ __global__ __launch_bounds__(64) void k_lmhead_finish(LmPlan pl) {
 
 }  // namespace
 
-int64_t lmhead_grid_blocks(const LmPlan& pl) {
-    const int64_t groups = (static_cast<int64_t>(pl.n_runs) + kXcds - 1) / kXcds;
-    return groups * kXcds * pl.m_tiles;
-}
-
 hipError_t launch_lmhead(const LmPlan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     hipError_t e;
     if (ev0 && ev1) {
         e = hipEventRecord(ev0, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_lmhead_argmax, dim3(static_cast<unsigned>(lmhead_grid_blocks(pl))), dim3(kLmThreads), 0,
-                       stream, pl);
+    // As many workgroups as the compute units hold at once, a multiple of
+    // the XCD count, no more than there are items.
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t items = lmhead_items(pl);
+    int64_t grid = std::max<int64_t>(kXcds, static_cast<int64_t>(cus) * kLmBlocksPerCu / kXcds * kXcds);
+    grid = std::min<int64_t>(grid, (items + kXcds - 1) / kXcds * kXcds);
+    hipLaunchKernelGGL(k_lmhead_argmax, dim3(static_cast<unsigned>(grid)), dim3(kLmThreads), 0, stream, pl);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev0 && ev1) {
         e = hipEventRecord(ev1, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_lmhead_finish, dim3(static_cast<unsigned>(pl.batch)), dim3(64), 0, stream, pl);
+    hipLaunchKernelGGL(k_lmhead_finish, dim3(static_cast<unsigned>(pl.batch)), dim3(kFinishThreads), 0, stream, pl);
     return hipGetLastError();
 }
 

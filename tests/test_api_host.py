@@ -307,7 +307,8 @@ def _call_lm(lib, d, h, **over):
 
 
 @pytest.mark.parametrize("field,value", [("num_draft", 0), ("num_draft", 65), ("vocab", 0), ("vocab", (1 << 24) + 1),
-                                         ("hidden", 0), ("hidden", 48), ("hidden", 16), ("hidden", 65536 + 32),
+                                         ("hidden", 0), ("hidden", 48), ("hidden", 32), ("hidden", 96),
+                                         ("hidden", 65536 + 64),
                                          ("batch", -1)])
 def test_lm_head_rejects_bad_shape(lib, field, value):
     d = _lm_desc()
@@ -324,10 +325,10 @@ def test_lm_head_workspace_holds_one_partial_per_row_and_run(lib):
     n = ctypes.c_size_t()
     assert lib.sv_lm_head_workspace_size(None, ctypes.byref(n)) == 1
     assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc()), None) == 1
-    # rows = B(k+1); runs = ceil(ceil(V/128)/8): a float and an int32 each, 256-byte aligned halves
+    # rows = B(k+1); tiles = ceil(V/256): a float and an int32 each, 256-byte aligned halves
     for B, k, V in [(2, 3, 1000), (128, 5, 151936), (320, 7, 151936), (1, 1, 1)]:
         assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc(B, k, V, 4096)), ctypes.byref(n)) == 0
-        runs = -(-(-(-V // 128)) // 8)
+        runs = -(-V // 256)
         half = -(-(B * (k + 1) * runs * 4) // 256) * 256
         assert n.value == 2 * half, (B, k, V)
 

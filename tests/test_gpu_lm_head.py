@@ -113,12 +113,12 @@ def _planted(B, k, V, D, hit=0.8, seed=11):
 
 
 @pytest.mark.parametrize("B,k,V,D", [
-    (50, 5, 3000, 256),      # 3 row tiles (ragged), 24 vocabulary tiles (ragged), 3 runs (ragged)
-    (1, 1, 1, 32),           # one token, one K slice
-    (3, 64, 130, 64),        # longest draft (65 rows per sequence), V just over one tile
-    (9, 16, 8193, 96),       # last run holds one column
-    (20, 7, 2048, 4096),     # the full hidden size, V a multiple of the run width
-    (2, 3, 127, 32),         # V below one tile
+    (90, 5, 3000, 256),      # 3 row tiles (ragged), 12 vocabulary tiles (ragged)
+    (1, 1, 1, 64),           # one token, one K slice
+    (3, 64, 300, 64),        # longest draft (65 rows per sequence), V just over one tile
+    (9, 16, 8193, 192),      # last vocabulary tile holds one column
+    (40, 7, 2048, 4096),     # the full hidden size, two row tiles, V a multiple of the tile width
+    (2, 3, 127, 64),         # V below one tile
 ])
 def test_lm_head_reduced(dev, B, k, V, D):
     _say("case lm_head planted B=%d k=%d V=%d D=%d" % (B, k, V, D))
