@@ -12,18 +12,24 @@
 //  k_lmhead_argmax   a bf16 GEMM H . W^T on the matrix cores
 //                    (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with an
 //                    argmax epilogue.  A work item is a 256 x 256 tile (hidden
-//                    rows x vocabulary columns); its K dimension is staged in
-//                    LDS 64 at a time (double buffered, the next slice's global
-//                    loads in flight during the current slice's MFMAs); each
-//                    of the 8 wavefronts computes a 128 x 64 block; the
-//                    epilogue reduces the tile to (max, lowest index) per row,
-//                    one partial per row and vocabulary tile.  The grid is
-//                    persistent, one workgroup per compute unit, each taking
-//                    every G-th item: all workgroups advance through the
-//                    items in step, and the items a die (XCD) takes in one
-//                    step are consecutive, so the row tiles of one vocabulary
-//                    tile run side by side on one die and share its weight
-//                    rows in that die's L2.
+//                    rows x vocabulary columns); each of the 8 wavefronts
+//                    computes a 128 x 64 block.  K is staged through two LDS
+//                    buffers 64 at a time.  A slice is four 16-deep MFMA
+//                    groups; between the MFMAs of one group the wavefront reads
+//                    the next group's fragments, writes the next slice (held in
+//                    registers) to the other buffer, or issues the global loads
+//                    of the slice after it, in a fixed interleave, so that the
+//                    matrix pipe is not left waiting behind a burst of memory
+//                    instructions; one barrier per slice, before the last group,
+//                    whose MFMAs overlap the reads of the next slice's first
+//                    fragments.  The epilogue reduces the tile to (max, lowest
+//                    index) per row: one partial per row and vocabulary tile.
+//                    The grid is persistent, one workgroup per compute unit,
+//                    each taking every G-th item: all workgroups advance
+//                    through the items in step, and the items a die (XCD)
+//                    takes in one step are consecutive, so the row tiles of
+//                    one vocabulary tile run side by side on one die and share
+//                    its weight rows in that die's L2.
 //  k_lmhead_finish   per sequence: combines its rows' partials, decides every
 //                    position on one lane, writes accepted_len and
 //                    out_tokens.
@@ -139,58 +145,100 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_argmax(Lm
                 for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
 
         uint4 ra[PA], rb[PB];
+        static_assert(kLmBK == 64, "four 16-deep MFMA groups per slice");
+        constexpr int NMF = FM * FN;     // MFMAs per group
+        constexpr int NRD = FM + FN;     // fragment reads per group
+        constexpr int NGL = PA + PB;     // global loads (and LDS writes) per slice
+        static_assert(2 * NMF >= NRD && NMF >= NGL, "interleave slots");
+        bf16x8_t f0a[FM], f0b[FN], f1a[FM], f1b[FN];
+#define LM_FRAGS(FA, FB, BUF, KS)                                                           \
+    {                                                                                       \
+        const int kcol_ = (KS) * 16 + 8 * (lane >> 5);                                      \
+        _Pragma("unroll") for (int mi = 0; mi < FM; ++mi)                                   \
+            FA[mi] = *reinterpret_cast<const bf16x8_t*>(&sa[BUF][(wm * kLmWaveM + mi * 32 + (lane & 31)) * kLdsStride + kcol_]); \
+        _Pragma("unroll") for (int ni = 0; ni < FN; ++ni)                                   \
+            FB[ni] = *reinterpret_cast<const bf16x8_t*>(&sb[BUF][(wn * kLmWaveN + ni * 32 + (lane & 31)) * kLdsStride + kcol_]); \
+    }
+#define LM_MFMA(FA, FB)                                                                     \
+    {                                                                                       \
+        _Pragma("unroll") for (int mi = 0; mi < FM; ++mi)                                   \
+            _Pragma("unroll") for (int ni = 0; ni < FN; ++ni)                               \
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0); \
+    }
+// After each MFMA of a group: up to two fragment reads (READS), one global load (LOADS), one LDS write (WRITES).
+#define LM_INTERLEAVE(READS, LOADS, WRITES)                                                 \
+    {                                                                                       \
+        _Pragma("unroll") for (int t = 0; t < NMF; ++t) {                                   \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+            if ((READS) && 2 * t < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  \
+            if ((READS) && 2 * t + 1 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); \
+            if ((LOADS) && t < NGL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      \
+            if ((WRITES) && t < NGL) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);     \
+        }                                                                                   \
+    }
+
+        // Pipeline over K slices with two LDS buffers: slice kb+1 is written
+        // to the other buffer during group 2 of step kb, a barrier follows,
+        // and group 3 reads the first fragments of slice kb+1 and issues the
+        // global loads of slice kb+2 while its MFMAs run.
 #pragma unroll
         for (int q = 0; q < PA; ++q) ra[q] = ld16(a_base + a_off[q]);
 #pragma unroll
         for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + b_off[q]);
-        __syncthreads();  // the previous item's readers of buffer 0 and of cand are done
+        __syncthreads();  // the previous item's readers of the buffers and of cand are done
 #pragma unroll
         for (int q = 0; q < PA; ++q) *reinterpret_cast<uint4*>(sa_st + q * ROWS_PER_PASS * kLdsStride) = ra[q];
 #pragma unroll
         for (int q = 0; q < PB; ++q) *reinterpret_cast<uint4*>(sb_st + q * ROWS_PER_PASS * kLdsStride) = rb[q];
+        {
+            const int k1 = min(1, kblocks - 1) * kLmBK;
+#pragma unroll
+            for (int q = 0; q < PA; ++q) ra[q] = ld16(a_base + k1 + a_off[q]);
+#pragma unroll
+            for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + k1 + b_off[q]);
+        }
         __syncthreads();
-
+        LM_FRAGS(f0a, f0b, 0, 0);
         for (int kb = 0; kb < kblocks; ++kb) {
             const int cur = kb & 1;
-            const bool more = kb + 1 < kblocks;
-            if (more) {
-                const int koff = (kb + 1) * kLmBK;
+            const int nxt = cur ^ 1;
+            const int kload = min(kb + 2, kblocks - 1) * kLmBK;  // clamped: the last steps reload a slice nobody reads
+            __builtin_amdgcn_sched_barrier(0);
+            // group 0: reads of group 1
+            LM_FRAGS(f1a, f1b, cur, 1);
+            LM_MFMA(f0a, f0b);
+            LM_INTERLEAVE(true, false, false);
+            __builtin_amdgcn_sched_barrier(0);
+            // group 1: reads of group 2
+            LM_FRAGS(f0a, f0b, cur, 2);
+            LM_MFMA(f1a, f1b);
+            LM_INTERLEAVE(true, false, false);
+            __builtin_amdgcn_sched_barrier(0);
+            // group 2: reads of group 3, slice kb+1 (staged in registers) to the other buffer
+            LM_FRAGS(f1a, f1b, cur, 3);
 #pragma unroll
-                for (int q = 0; q < PA; ++q) ra[q] = ld16(a_base + koff + a_off[q]);
+            for (int q = 0; q < PA; ++q)
+                *reinterpret_cast<uint4*>(sa_st + (nxt * kLmBM + q * ROWS_PER_PASS) * kLdsStride) = ra[q];
 #pragma unroll
-                for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + koff + b_off[q]);
-            }
+            for (int q = 0; q < PB; ++q)
+                *reinterpret_cast<uint4*>(sb_st + (nxt * kLmBN + q * ROWS_PER_PASS) * kLdsStride) = rb[q];
+            LM_MFMA(f0a, f0b);
+            LM_INTERLEAVE(true, false, true);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();  // slice kb+1 visible; every read of this buffer done
+            // group 3: first fragments of slice kb+1, global loads of slice kb+2
+            LM_FRAGS(f0a, f0b, nxt, 0);
 #pragma unroll
-            for (int ks = 0; ks < kLmBK / 16; ++ks) {
-                const int kcol = ks * 16 + 8 * (lane >> 5);
-                bf16x8_t fa[FM], fb[FN];
+            for (int q = 0; q < PA; ++q) ra[q] = ld16(a_base + kload + a_off[q]);
 #pragma unroll
-                for (int mi = 0; mi < FM; ++mi) {
-                    const int row = wm * kLmWaveM + mi * 32 + (lane & 31);
-                    fa[mi] = *reinterpret_cast<const bf16x8_t*>(&sa[cur][row * kLdsStride + kcol]);
-                }
-#pragma unroll
-                for (int ni = 0; ni < FN; ++ni) {
-                    const int row = wn * kLmWaveN + ni * 32 + (lane & 31);
-                    fb[ni] = *reinterpret_cast<const bf16x8_t*>(&sb[cur][row * kLdsStride + kcol]);
-                }
-#pragma unroll
-                for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < FN; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-            }
-            if (more) {
-                const int nxt = cur ^ 1;
-#pragma unroll
-                for (int q = 0; q < PA; ++q)
-                    *reinterpret_cast<uint4*>(sa_st + (nxt * kLmBM + q * ROWS_PER_PASS) * kLdsStride) = ra[q];
-#pragma unroll
-                for (int q = 0; q < PB; ++q)
-                    *reinterpret_cast<uint4*>(sb_st + (nxt * kLmBN + q * ROWS_PER_PASS) * kLdsStride) = rb[q];
-            }
-            __syncthreads();
+            for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + kload + b_off[q]);
+            LM_MFMA(f1a, f1b);
+            LM_INTERLEAVE(true, true, false);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#undef LM_INTERLEAVE
+#undef LM_MFMA
+#undef LM_FRAGS
 
         // Epilogue: accumulator j of lane l holds row 8(j/4) + 4(l/32) + j%4
         // of a 32 x 32 block, column l % 32.
