@@ -23,6 +23,7 @@ _LIB_PATH = os.environ.get("ORACLE_LIB_OVERRIDE") or os.path.join(_HERE, "libora
 
 F32 = 0
 BF16 = 1
+F64 = 2
 
 _lib = None
 
@@ -76,6 +77,8 @@ def _load():
     lib.orc_vat_loss.restype = c.c_int
     lib.orc_lm_head_greedy.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int64, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_lm_head_greedy.restype = c.c_int
+    lib.orc_lm_head_logits.argtypes = [c.c_int64, c.c_int64, c.c_int64, vp, vp, vp]
+    lib.orc_lm_head_logits.restype = c.c_int
     _lib = lib
     return lib
 
@@ -93,7 +96,9 @@ def _logits_arg(a):
         return a, F32
     if a.dtype == np.uint16:
         return a, BF16
-    raise TypeError("logits must be float32 or uint16 (bfloat16 bits), got %s" % a.dtype)
+    if a.dtype == np.float64:
+        return a, F64
+    raise TypeError("logits must be float32, float64 or uint16 (bfloat16 bits), got %s" % a.dtype)
 
 
 # ---------------------------------------------------------------- primitives
@@ -290,3 +295,30 @@ def lm_head_greedy(hidden, weight, tokens) -> LmHeadResult:
     if rc != 0:
         raise ValueError("orc_lm_head_greedy rejected its arguments")
     return LmHeadResult(accepted_len=acc, out_tokens=out, argmax=am, top2_gap=gap)
+
+
+def lm_head_logits(hidden, weight) -> np.ndarray:
+    """fp64 logits hidden . weight^T from bf16 bit patterns: hidden [..., D],
+    weight [V][D]; returns [..., V] float64."""
+    lib = _load()
+    h = np.ascontiguousarray(hidden, dtype=np.uint16)
+    w = np.ascontiguousarray(weight, dtype=np.uint16)
+    V, D = w.shape
+    assert h.shape[-1] == D
+    rows = int(np.prod(h.shape[:-1]))
+    out = np.empty(h.shape[:-1] + (V,), np.float64)
+    rc = lib.orc_lm_head_logits(rows, V, D, _ptr(h), _ptr(w), _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_lm_head_logits rejected its arguments")
+    return out
+
+
+def lm_head_verify(target_hidden, target_weight, draft_hidden, draft_weight, tokens, uniforms,
+                   temperature: float) -> VerifyResult:
+    """Verification at T > 0 with both distributions formed from hidden
+    states: p = softmax(H_t W_t^T / T), q = softmax(H_d W_d^T / T) in fp64, then
+    the rule of verify()."""
+    assert temperature > 0.0
+    lt = lm_head_logits(target_hidden, target_weight)
+    ld = lm_head_logits(draft_hidden, draft_weight)
+    return verify(lt, ld, tokens, uniforms, temperature)

@@ -60,6 +60,10 @@
  *  - LM-head greedy verification (orc_lm_head_greedy): the logits are the
  *    product of the hidden state with the output layer's weights, formed in
  *    fp64 from their bf16 values; the rest is the T == 0 rule above.
+ *  - LM-head verification at T > 0 (orc_lm_head_logits, then orc_verify on
+ *    ORC_F64 rows): target logits from the target's hidden states and output
+ *    layer, draft logits from the draft's hidden states and its output layer,
+ *    both formed in fp64 from bf16 values; the rest is the rule above.
  *  - VAT loss (orc_vat_loss): at every position the soft term is the cross
  *    entropy of the draft's distribution against the target's at the same
  *    temperature, -sum_y p(y) ln q(y); the hard term is -ln q(h) for the
@@ -76,6 +80,7 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_F64 2 /* logits already in fp64 (formed by orc_lm_head_logits) */
 
 int orc_abi_version(void) { return 1; }
 
@@ -120,6 +125,9 @@ static void load_row(const void* base, int dtype, int64_t row, int64_t V, double
     if (dtype == ORC_BF16) {
         const uint16_t* p = (const uint16_t*)base + row * V;
         for (y = 0; y < V; ++y) out[y] = orc_decode_bf16(p[y]);
+    } else if (dtype == ORC_F64) {
+        const double* p = (const double*)base + row * V;
+        for (y = 0; y < V; ++y) out[y] = p[y];
     } else {
         const uint32_t* p = (const uint32_t*)base + row * V;
         for (y = 0; y < V; ++y) out[y] = decode_f32(p[y]);
@@ -577,5 +585,34 @@ int orc_lm_head_greedy(int64_t B, int32_t k, int64_t V, int64_t D, const uint16_
     }
     free(h);
     free(g);
+    return 0;
+}
+
+/* Logits formed from hidden states: out[row][y] = sum_d h_row[d] w_y[d] in
+ * fp64 from bf16 hidden states h [rows][D] and output-layer weights w [V][D]
+ * (no bias).  Each weight row is decoded once and dotted with every hidden
+ * row; each dot product is the plain sequential sum over d.  With T > 0 the
+ * verification rule then runs on these rows unchanged (orc_verify with
+ * ORC_F64 logits). */
+int orc_lm_head_logits(int64_t rows, int64_t V, int64_t D, const uint16_t* hidden, const uint16_t* weight,
+                       double* out) {
+    int64_t r, y, d;
+    double *h, *wy;
+    if (rows < 0 || V < 1 || D < 1 || !hidden || !weight || !out) return -1;
+    h = (double*)malloc(sizeof(double) * (rows * D + D + 1));
+    if (!h) return -1;
+    wy = h + rows * D;
+    for (r = 0; r < rows; ++r)
+        for (d = 0; d < D; ++d) h[r * D + d] = orc_decode_bf16(hidden[r * D + d]);
+    for (y = 0; y < V; ++y) {
+        for (d = 0; d < D; ++d) wy[d] = orc_decode_bf16(weight[y * D + d]);
+        for (r = 0; r < rows; ++r) {
+            const double* hr = h + r * D;
+            double s = 0.0;
+            for (d = 0; d < D; ++d) s += hr[d] * wy[d];
+            out[r * V + y] = s;
+        }
+    }
+    free(h);
     return 0;
 }

@@ -544,3 +544,50 @@ def test_lm_head_greedy_first_mismatch_and_invalid_token(orc):
     assert res.accepted_len[0] == 2
     assert list(res.out_tokens[0]) == [x[0, 0], x[0, 1], g[0, 2], -1, -1]
     assert res.accepted_len[1] == -1 and np.all(res.out_tokens[1] == -1)
+
+
+def test_lm_head_logits_equal_the_fp64_matmul_and_integers_exactly(orc):
+    rng = np.random.default_rng(73)
+    h = _bf16_bits(rng.standard_normal((2, 3, 40)))
+    w = _bf16_bits(rng.standard_normal((57, 40)) * 0.2)
+    got = orc.lm_head_logits(h, w)
+    assert got.shape == (2, 3, 57)
+    assert np.allclose(got, _bf16_vals(h) @ _bf16_vals(w).T, rtol=1e-12, atol=1e-12)
+    hi = _bf16_bits(rng.integers(-3, 4, (5, 16)).astype(np.float32))
+    wi = _bf16_bits(rng.integers(-3, 4, (9, 16)).astype(np.float32))
+    exact = _bf16_vals(hi).astype(np.int64) @ _bf16_vals(wi).astype(np.int64).T
+    assert np.array_equal(orc.lm_head_logits(hi, wi), exact.astype(np.float64))
+
+
+def test_f64_logits_run_the_same_rule_as_f32(orc):
+    """fp64 rows holding fp32-representable values give bit-identical results
+    to the same values passed as fp32."""
+    rng = np.random.default_rng(74)
+    B, k, V = 6, 4, 300
+    t = (rng.standard_normal((B, k + 1, V)) * 3).astype(np.float32)
+    d = (t[:, :k] + rng.standard_normal((B, k, V)).astype(np.float32) * 0.5).astype(np.float32)
+    x = rng.integers(0, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    a = orc.verify(t, d, x, u, 0.8)
+    b = orc.verify(t.astype(np.float64), d.astype(np.float64), x, u, 0.8)
+    for name in ("accepted_len", "out_tokens", "probs", "target_mz", "draft_mz"):
+        assert np.array_equal(getattr(a, name), getattr(b, name), equal_nan=True), name
+
+
+def test_lm_head_verify_with_the_target_as_draft_never_rejects(orc):
+    """q = p makes every test u*q < p succeed (u < 1): all k drafts kept, and
+    the bonus token is drawn from the target's last position."""
+    rng = np.random.default_rng(75)
+    B, k, V, D = 5, 3, 80, 24
+    h = _bf16_bits(rng.standard_normal((B, k + 1, D)))
+    w = _bf16_bits(rng.standard_normal((V, D)) * 0.4)
+    x = rng.integers(0, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    res = orc.lm_head_verify(h, w, h[:, :k], w, x, u, 1.0)
+    assert np.all(res.accepted_len == k)
+    assert np.allclose(res.probs[..., 0], res.probs[..., 1], rtol=0, atol=0)
+    lk = _bf16_vals(h[:, k]).astype(np.float64) @ _bf16_vals(w).astype(np.float64).T
+    for b in range(B):
+        p = np.exp(lk[b] - lk[b].max())
+        c = np.cumsum(p)
+        assert res.out_tokens[b, k] == int(np.searchsorted(c, u[b, k] * c[-1], side="right"))
