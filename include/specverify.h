@@ -108,7 +108,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 4
+#define SV_ABI_VERSION 5
 #define SV_MAX_DRAFT 64 /* k is limited to one 64-lane wavefront */
 #define SV_MAX_DRAFT_CHOICES 8
 
@@ -182,6 +182,18 @@ typedef struct sv_lm_head_desc {
     hipEvent_t probe_start;
     hipEvent_t probe_stop;
 } sv_lm_head_desc;
+
+/* Shape and options of one sv_verify_lm_head call (sampling); probe_start /
+ * probe_stop (NULL to skip) bracket its first kernel, the statistics GEMM. */
+typedef struct sv_lm_head_sample_desc {
+    int32_t batch;       /* B >= 0 sequences */
+    int32_t num_draft;   /* k in [1, 64] */
+    int32_t vocab;       /* V in [1, 2^24] */
+    int32_t hidden;      /* D: a multiple of 64 in [64, 65536] */
+    float temperature;   /* T: finite >= 1e-4 (T == 0 is sv_verify_lm_head_greedy) */
+    hipEvent_t probe_start;
+    hipEvent_t probe_stop;
+} sv_lm_head_sample_desc;
 
 /* Returns SV_ABI_VERSION of the built library. */
 int sv_abi_version(void);
@@ -324,13 +336,54 @@ sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes);
  * Arithmetic: bf16 x bf16 products accumulated in fp32 on the matrix cores;
  * the accumulation order differs from a sequential sum, so a position whose
  * two largest logits lie within rounding of each other may pick either.
- * Errors (nothing launched): SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE,
- * SV_ERR_MISALIGNED, SV_ERR_WORKSPACE_TOO_SMALL.  Launch failure: SV_ERR_HIP.
+ * Errors (nothing launched): SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE (also when
+ * B(k+1) D >= 2^31), SV_ERR_MISALIGNED, SV_ERR_WORKSPACE_TOO_SMALL.  Launch
+ * failure: SV_ERR_HIP.
  */
 sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidden_states, const void* weight,
                                    const int32_t* draft_tokens, int32_t* accepted_len, int32_t* out_tokens,
                                    int32_t* argmax_out, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* Workspace bytes sv_verify_lm_head needs for `desc`: about
+ * 8 B (2k+1) ceil(V/256) + 8 B V per sequence.  Errors: SV_ERR_NULL_ARG,
+ * SV_ERR_BAD_SHAPE, SV_ERR_BAD_TEMPERATURE. */
+sv_status sv_lm_head_sample_workspace_size(const sv_lm_head_sample_desc* desc, size_t* bytes);
+
+/*
+ * Speculative-sampling verification (T > 0) with the target's and the
+ * draft's logits formed from their hidden states and output layers inside
+ * the call.  Source: NgramRL essay, section "投机解码：让草稿先跑，考官殿后"
+ * (the rule, as for sv_verify with draft logits: p = softmax(l_t / T),
+ * q = softmax(l_d / T), x_i kept iff u_i q_i(x_i) < p_i(x_i), the draw at the
+ * first rejection from max(0, p_r - q_r) renormalised, or from p_k after full
+ * acceptance, with u[b][k], inverting the cumulative weight in ascending
+ * token order).  Logits: l(y) = h . w_y, bf16 inputs, fp32 accumulation.  The
+ * softmax statistics of every row come from one pass over both output layers
+ * (the [B][k+1][V] and [B][k][V] logits are never stored); the draw then
+ * recomputes only the rows it needs (one target row and one draft row per
+ * sequence) and stores those in the workspace.
+ *
+ *  target_hidden  device, [B][k+1][D] bf16, 16-byte aligned
+ *  target_weight  device, [V][D] bf16, 16-byte aligned
+ *  draft_hidden   device, [B][k][D] bf16, 16-byte aligned
+ *  draft_weight   device, [V][D] bf16, 16-byte aligned (may be target_weight)
+ *  draft_tokens   device, [B][k] int32, expected in [0, V)
+ *  uniforms       device, [B][k+1] float32 in [0,1), as for sv_verify
+ *  accepted_len   device out, [B] int32 in [0, k] (-1: invalid token)
+ *  out_tokens     device out, [B][k+1] int32, as for sv_verify
+ *  probs_out      device out or NULL, [B][k][2] float32 (p_i(x_i), q_i(x_i))
+ *  workspace      device, >= sv_lm_head_sample_workspace_size bytes (needs no
+ *                 clearing)
+ *
+ * Errors (nothing launched): SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE,
+ * SV_ERR_BAD_TEMPERATURE, SV_ERR_MISALIGNED, SV_ERR_WORKSPACE_TOO_SMALL.
+ * Launch failure: SV_ERR_HIP.
+ */
+sv_status sv_verify_lm_head(const sv_lm_head_sample_desc* desc, const void* target_hidden, const void* target_weight,
+                            const void* draft_hidden, const void* draft_weight, const int32_t* draft_tokens,
+                            const float* uniforms, int32_t* accepted_len, int32_t* out_tokens, float* probs_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Histogram of accepted lengths (device in, device out).

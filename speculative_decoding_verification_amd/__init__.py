@@ -10,7 +10,8 @@ library is not built, importing works but every call raises.
 
 Names follow the C ABI in ``include/specverify.h``: ``sv_verify`` ->
 :func:`verify`, ``sv_vat_labels`` -> :func:`vat_labels`, ``sv_vat_loss`` ->
-:func:`vat_loss`, ``sv_verify_lm_head_greedy`` -> :func:`verify_lm_head_greedy`.
+:func:`vat_loss`, ``sv_verify_lm_head_greedy`` -> :func:`verify_lm_head_greedy`,
+``sv_verify_lm_head`` -> :func:`verify_lm_head`.
 """
 from __future__ import annotations
 
@@ -18,8 +19,8 @@ import ctypes
 import os
 from typing import NamedTuple, Optional
 
-__all__ = ["verify", "vat_labels", "vat_loss", "verify_lm_head_greedy", "accept_histogram", "Verifier",
-           "VatLabeler", "VatLoss", "LmHeadVerifier",
+__all__ = ["verify", "vat_labels", "vat_loss", "verify_lm_head_greedy", "verify_lm_head", "accept_histogram",
+           "Verifier", "VatLabeler", "VatLoss", "LmHeadVerifier", "LmHeadSampler",
            "DraftLengthController", "SVError", "library_path", "load_library", "SV_F32", "SV_BF16", "SV_DRAFT_LOGITS",
            "SV_DRAFT_ONEHOT", "STATUS"]
 
@@ -35,7 +36,8 @@ STATUS = {0: "SV_OK", 1: "SV_ERR_NULL_ARG", 2: "SV_ERR_BAD_SHAPE", 3: "SV_ERR_BA
 
 EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_size", "sv_verify",
                     "sv_vat_workspace_size", "sv_vat_labels", "sv_vat_loss_workspace_size", "sv_vat_loss",
-                    "sv_lm_head_workspace_size", "sv_verify_lm_head_greedy", "sv_accept_histogram",
+                    "sv_lm_head_workspace_size", "sv_verify_lm_head_greedy", "sv_lm_head_sample_workspace_size",
+                    "sv_verify_lm_head", "sv_accept_histogram",
                     "sv_draft_len_init", "sv_draft_len_update")
 
 
@@ -69,6 +71,12 @@ class VatLossDesc(ctypes.Structure):
 class LmHeadDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+
+
+class LmHeadSampleDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("temperature", ctypes.c_float), ("probe_start", ctypes.c_void_p),
+                ("probe_stop", ctypes.c_void_p)]
 
 
 SV_MAX_DRAFT_CHOICES = 8
@@ -118,6 +126,10 @@ def load_library():
     lib.sv_lm_head_workspace_size.argtypes = [ctypes.POINTER(LmHeadDesc), ctypes.POINTER(sz)]
     lib.sv_verify_lm_head_greedy.restype = ctypes.c_int
     lib.sv_verify_lm_head_greedy.argtypes = [ctypes.POINTER(LmHeadDesc)] + [vp] * 7 + [sz, vp]
+    lib.sv_lm_head_sample_workspace_size.restype = ctypes.c_int
+    lib.sv_lm_head_sample_workspace_size.argtypes = [ctypes.POINTER(LmHeadSampleDesc), ctypes.POINTER(sz)]
+    lib.sv_verify_lm_head.restype = ctypes.c_int
+    lib.sv_verify_lm_head.argtypes = [ctypes.POINTER(LmHeadSampleDesc)] + [vp] * 10 + [sz, vp]
     i32 = ctypes.c_int32
     lib.sv_accept_histogram.restype = ctypes.c_int
     lib.sv_accept_histogram.argtypes = [vp, i32, i32, vp, vp]
@@ -467,6 +479,71 @@ def verify_lm_head_greedy(hidden_states, weight, draft_tokens, *, return_argmax:
     (accepted_len [B], out_tokens [B][k+1], argmax [B][k+1] or None)."""
     return LmHeadVerifier(hidden_states, weight, draft_tokens, return_argmax=return_argmax,
                           workspace=workspace)()
+
+
+class LmHeadSampleOutput(NamedTuple):
+    accepted_len: "object"
+    out_tokens: "object"
+    probs: "object"
+
+
+class LmHeadSampler:
+    """A prepared sv_verify_lm_head call (T > 0: both distributions formed
+    from hidden states inside the call)."""
+
+    def __init__(self, target_hidden, target_weight, draft_hidden, draft_weight, draft_tokens, uniforms,
+                 temperature: float, *, return_probs: bool = False, workspace=None, probe=None):
+        torch = _torch()
+        lib = load_library()
+        if target_hidden.dim() != 3 or target_weight.dim() != 2:
+            raise ValueError("target_hidden must be [B][k+1][D] and target_weight [V][D]")
+        B, kp1, D = (int(s) for s in target_hidden.shape)
+        k = kp1 - 1
+        V = int(target_weight.shape[0])
+        device = target_hidden.device
+        _check_dev("target_hidden", target_hidden, device, torch.bfloat16)
+        _check_dev("target_weight", target_weight, device, torch.bfloat16, (V, D))
+        _check_dev("draft_hidden", draft_hidden, device, torch.bfloat16, (B, k, D))
+        _check_dev("draft_weight", draft_weight, device, torch.bfloat16, (V, D))
+        _check_dev("draft_tokens", draft_tokens, device, torch.int32, (B, k))
+        _check_dev("uniforms", uniforms, device, torch.float32, (B, k + 1))
+        self.desc = LmHeadSampleDesc(B, k, V, D, float(temperature), None, None)
+        if probe is not None:
+            self.desc.probe_start, self.desc.probe_stop = probe
+        nbytes = ctypes.c_size_t()
+        st = lib.sv_lm_head_sample_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
+        if st:
+            raise SVError(st, "sv_lm_head_sample_workspace_size", lib)
+        if workspace is None:
+            workspace = _WS.get(device, nbytes.value)
+        elif workspace.numel() * workspace.element_size() < nbytes.value:
+            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+        self.accepted_len = torch.empty(B, dtype=torch.int32, device=device)
+        self.out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
+        self.probs = torch.empty((B, k, 2), dtype=torch.float32, device=device) if return_probs else None
+        self._keep = (target_hidden, target_weight, draft_hidden, draft_weight, draft_tokens, uniforms, workspace)
+        self._lib = lib
+        self._device = device
+        self._args = (ctypes.byref(self.desc), _ptr(target_hidden), _ptr(target_weight), _ptr(draft_hidden),
+                      _ptr(draft_weight), _ptr(draft_tokens), _ptr(uniforms), _ptr(self.accepted_len),
+                      _ptr(self.out_tokens), _ptr(self.probs), workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size())
+
+    def __call__(self, stream: Optional[int] = None) -> LmHeadSampleOutput:
+        s = _stream_handle(self._device) if stream is None else stream
+        st = self._lib.sv_verify_lm_head(*self._args, s)
+        if st:
+            raise SVError(st, "sv_verify_lm_head", self._lib)
+        return LmHeadSampleOutput(self.accepted_len, self.out_tokens, self.probs)
+
+
+def verify_lm_head(target_hidden, target_weight, draft_hidden, draft_weight, draft_tokens, uniforms,
+                   temperature: float, *, return_probs: bool = False, workspace=None) -> LmHeadSampleOutput:
+    """sv_verify_lm_head on torch tensors (bf16 hidden states and weights,
+    int32 tokens, float32 uniforms [B][k+1]).  Returns (accepted_len [B],
+    out_tokens [B][k+1], probs [B][k][2] or None)."""
+    return LmHeadSampler(target_hidden, target_weight, draft_hidden, draft_weight, draft_tokens, uniforms,
+                         temperature, return_probs=return_probs, workspace=workspace)()
 
 
 def accept_histogram(accepted_len, k: int, out=None, stream: Optional[int] = None):

@@ -121,27 +121,77 @@ void carve_workspace(const Shape& s, void* ws, Plan* pl) {
     pl->tag = next_tag();
 }
 
-// LM-head greedy verification: shape checks and the workspace of partials.
+// LM-head verification: shape checks and workspace layouts.
 constexpr int64_t kMaxHidden = 65536;
+constexpr int64_t kMaxRowElems = 0x7fffffffLL;  // hidden-state offsets are 32-bit
 
-sv_status check_lm_shape(const sv_lm_head_desc* d, LmPlan* pl) {
-    if (d->batch < 0 || d->num_draft < 1 || d->num_draft > SV_MAX_DRAFT || d->vocab < 1 || d->vocab > kMaxVocab ||
-        d->hidden < kLmHiddenMultiple || d->hidden > kMaxHidden || d->hidden % kLmHiddenMultiple != 0)
+struct LmShape {
+    int64_t batch, k, vocab, hidden, rows_t, rows_d, n_tiles;
+};
+
+sv_status check_lm_shape(int32_t batch, int32_t k, int32_t vocab, int32_t hidden, LmShape* s) {
+    if (batch < 0 || k < 1 || k > SV_MAX_DRAFT || vocab < 1 || vocab > kMaxVocab || hidden < kLmHiddenMultiple ||
+        hidden > kMaxHidden || hidden % kLmHiddenMultiple != 0)
         return SV_ERR_BAD_SHAPE;
-    const int64_t rows = static_cast<int64_t>(d->batch) * (d->num_draft + 1);
-    if (rows > 0x7fffffffLL) return SV_ERR_BAD_SHAPE;
-    pl->rows = static_cast<int32_t>(rows);
-    pl->batch = d->batch;
-    pl->k = d->num_draft;
-    pl->vocab = d->vocab;
-    pl->hidden = d->hidden;
-    lmhead_shape(pl);
+    s->batch = batch;
+    s->k = k;
+    s->vocab = vocab;
+    s->hidden = hidden;
+    s->rows_t = s->batch * (k + 1);
+    s->rows_d = s->batch * k;
+    s->n_tiles = ceil_div(vocab, kLmBN);
+    if (s->rows_t * s->hidden > kMaxRowElems) return SV_ERR_BAD_SHAPE;
     return SV_OK;
 }
 
-size_t lm_workspace_bytes(const LmPlan& pl) {
-    const size_t n = static_cast<size_t>(pl.rows) * static_cast<size_t>(pl.n_parts);
+// Greedy: argmax partials (value and index) per target row and vocabulary tile.
+size_t lm_greedy_workspace_bytes(const LmShape& s) {
+    const size_t n = static_cast<size_t>(s.rows_t * s.n_tiles);
     return align_up(n * sizeof(float)) + align_up(n * sizeof(int32_t));
+}
+
+struct LmSampleLayout {
+    size_t part_m, part_s, lx, seq, logits, total;
+};
+
+// Sampling: (m, s) partials per target and draft row and tile, the token
+// logits, the per-sequence draw records, and the draw rows' logits.
+LmSampleLayout lm_sample_layout(const LmShape& s) {
+    LmSampleLayout L;
+    const size_t rows = static_cast<size_t>(s.rows_t + s.rows_d);
+    const size_t n = rows * static_cast<size_t>(s.n_tiles);
+    size_t off = 0;
+    L.part_m = off;
+    off = align_up(off + n * sizeof(float));
+    L.part_s = off;
+    off = align_up(off + n * sizeof(float));
+    L.lx = off;
+    off = align_up(off + rows * sizeof(float));
+    L.seq = off;
+    off = align_up(off + static_cast<size_t>(s.batch) * sizeof(LmSeqDraw));
+    L.logits = off;
+    off = align_up(off + 2 * static_cast<size_t>(s.batch) * static_cast<size_t>(s.vocab) * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+void lm_common(const LmShape& s, LmPlan* pl) {
+    pl->batch = static_cast<int32_t>(s.batch);
+    pl->k = static_cast<int32_t>(s.k);
+    pl->vocab = static_cast<int32_t>(s.vocab);
+    pl->hidden = static_cast<int32_t>(s.hidden);
+    pl->rows_t = static_cast<int32_t>(s.rows_t);
+}
+
+LmGemm lm_gemm(const void* a, const void* w, int64_t rows, int64_t out_row0, int32_t gather, int32_t tokens) {
+    LmGemm g{};
+    g.a = static_cast<const uint16_t*>(a);
+    g.w = static_cast<const uint16_t*>(w);
+    g.rows = static_cast<int32_t>(rows);
+    g.out_row0 = static_cast<int32_t>(out_row0);
+    g.gather = gather;
+    g.tokens = tokens;
+    return g;
 }
 
 }  // namespace
@@ -341,10 +391,10 @@ sv_status sv_accept_histogram(const int32_t* accepted_len, int32_t batch, int32_
 
 sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes) {
     if (!desc || !bytes) return SV_ERR_NULL_ARG;
-    sv::LmPlan pl{};
-    const sv_status st = sv::check_lm_shape(desc, &pl);
+    sv::LmShape s;
+    const sv_status st = sv::check_lm_shape(desc->batch, desc->num_draft, desc->vocab, desc->hidden, &s);
     if (st != SV_OK) return st;
-    *bytes = sv::lm_workspace_bytes(pl);
+    *bytes = sv::lm_greedy_workspace_bytes(s);
     return SV_OK;
 }
 
@@ -353,25 +403,86 @@ sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidd
                                    int32_t* argmax_out, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream) {
     if (!desc) return SV_ERR_NULL_ARG;
-    sv::LmPlan pl{};
-    const sv_status st = sv::check_lm_shape(desc, &pl);
+    sv::LmShape s;
+    const sv_status st = sv::check_lm_shape(desc->batch, desc->num_draft, desc->vocab, desc->hidden, &s);
     if (st != SV_OK) return st;
-    if (pl.batch == 0) return SV_OK;
+    if (s.batch == 0) return SV_OK;
     if (!hidden_states || !weight || !draft_tokens || !accepted_len || !out_tokens || !workspace)
         return SV_ERR_NULL_ARG;
     if (!sv::aligned16(hidden_states) || !sv::aligned16(weight)) return SV_ERR_MISALIGNED;
-    if (workspace_bytes < sv::lm_workspace_bytes(pl)) return SV_ERR_WORKSPACE_TOO_SMALL;
-    pl.hidden_states = static_cast<const uint16_t*>(hidden_states);
-    pl.weight = static_cast<const uint16_t*>(weight);
+    if (workspace_bytes < sv::lm_greedy_workspace_bytes(s)) return SV_ERR_WORKSPACE_TOO_SMALL;
+    sv::LmPlan pl{};
+    sv::lm_common(s, &pl);
+    pl.g[0] = sv::lm_gemm(hidden_states, weight, s.rows_t, 0, sv::kLmRows, sv::kLmNoTokens);
+    pl.n_gemms = 1;
+    pl.mode = sv::kLmArgmax;
+    sv::lmhead_layout(&pl);
     pl.tokens = draft_tokens;
     pl.accepted_len = accepted_len;
     pl.out_tokens = out_tokens;
     pl.argmax_out = argmax_out;
     char* base = static_cast<char*>(workspace);
-    const size_t n = static_cast<size_t>(pl.rows) * static_cast<size_t>(pl.n_parts);
+    const size_t n = static_cast<size_t>(s.rows_t * s.n_tiles);
     pl.part_v = reinterpret_cast<float*>(base);
     pl.part_i = reinterpret_cast<int32_t*>(base + sv::align_up(n * sizeof(float)));
-    const hipError_t e = sv::launch_lmhead(pl, stream, desc->probe_start, desc->probe_stop);
+    const hipError_t e = sv::launch_lmhead_greedy(pl, stream, desc->probe_start, desc->probe_stop);
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status sv_lm_head_sample_workspace_size(const sv_lm_head_sample_desc* desc, size_t* bytes) {
+    if (!desc || !bytes) return SV_ERR_NULL_ARG;
+    sv::LmShape s;
+    const sv_status st = sv::check_lm_shape(desc->batch, desc->num_draft, desc->vocab, desc->hidden, &s);
+    if (st != SV_OK) return st;
+    if (!(desc->temperature > 0.f) || !sv::temperature_ok(desc->temperature)) return SV_ERR_BAD_TEMPERATURE;
+    *bytes = sv::lm_sample_layout(s).total;
+    return SV_OK;
+}
+
+sv_status sv_verify_lm_head(const sv_lm_head_sample_desc* desc, const void* target_hidden, const void* target_weight,
+                            const void* draft_hidden, const void* draft_weight, const int32_t* draft_tokens,
+                            const float* uniforms, int32_t* accepted_len, int32_t* out_tokens, float* probs_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!desc) return SV_ERR_NULL_ARG;
+    sv::LmShape s;
+    const sv_status st = sv::check_lm_shape(desc->batch, desc->num_draft, desc->vocab, desc->hidden, &s);
+    if (st != SV_OK) return st;
+    if (!(desc->temperature > 0.f) || !sv::temperature_ok(desc->temperature)) return SV_ERR_BAD_TEMPERATURE;
+    if (s.batch == 0) return SV_OK;
+    if (!target_hidden || !target_weight || !draft_hidden || !draft_weight || !draft_tokens || !uniforms ||
+        !accepted_len || !out_tokens || !workspace)
+        return SV_ERR_NULL_ARG;
+    if (!sv::aligned16(target_hidden) || !sv::aligned16(target_weight) || !sv::aligned16(draft_hidden) ||
+        !sv::aligned16(draft_weight))
+        return SV_ERR_MISALIGNED;
+    const sv::LmSampleLayout L = sv::lm_sample_layout(s);
+    if (workspace_bytes < L.total) return SV_ERR_WORKSPACE_TOO_SMALL;
+    char* base = static_cast<char*>(workspace);
+    sv::LmPlan stats{};
+    sv::lm_common(s, &stats);
+    stats.tokens = draft_tokens;
+    stats.uniforms = uniforms;
+    stats.accepted_len = accepted_len;
+    stats.out_tokens = out_tokens;
+    stats.probs_out = probs_out;
+    stats.part_v = reinterpret_cast<float*>(base + L.part_m);
+    stats.part_s = reinterpret_cast<float*>(base + L.part_s);
+    stats.lx = reinterpret_cast<float*>(base + L.lx);
+    stats.seq = reinterpret_cast<sv::LmSeqDraw*>(base + L.seq);
+    stats.logits = reinterpret_cast<float*>(base + L.logits);
+    stats.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(desc->temperature));
+    sv::LmPlan draw = stats;
+    stats.g[0] = sv::lm_gemm(target_hidden, target_weight, s.rows_t, 0, sv::kLmRows, sv::kLmTargetTokens);
+    stats.g[1] = sv::lm_gemm(draft_hidden, draft_weight, s.rows_d, s.rows_t, sv::kLmRows, sv::kLmDraftTokens);
+    stats.n_gemms = 2;
+    stats.mode = sv::kLmStats;
+    sv::lmhead_layout(&stats);
+    draw.g[0] = sv::lm_gemm(target_hidden, target_weight, s.batch, 0, sv::kLmTargetDraw, sv::kLmNoTokens);
+    draw.g[1] = sv::lm_gemm(draft_hidden, draft_weight, s.batch, s.batch, sv::kLmDraftDraw, sv::kLmNoTokens);
+    draw.n_gemms = 2;
+    draw.mode = sv::kLmStore;
+    sv::lmhead_layout(&draw);
+    const hipError_t e = sv::launch_lmhead_sample(stats, draw, stream, desc->probe_start, desc->probe_stop);
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -1,38 +1,48 @@
-// gfx950 kernels of LM-head-fused greedy verification.
+// gfx950 kernels of LM-head-fused verification.
 //
-// What is computed: the T == 0 reading of the acceptance rule (NgramRL essay
-// "AI 开始抄自己的作业——而且抄得理直气壮", section "投机解码：让草稿先跑，
-// 考官殿后"), with the target's logits formed from its hidden states and
-// output-layer weights inside the kernel: l_i(y) = h_i . w_y.  The target's
-// choice at a position is its lowest-index argmax; a draft token is kept iff
-// it equals that choice; the chain stops at the first mismatch, where the
-// target's choice is the committed token.  The logits never reach memory.
+// What is computed: the acceptance rule of speculative sampling (NgramRL
+// essay "AI 开始抄自己的作业——而且抄得理直气壮", section "投机解码：让草稿先跑，
+// 考官殿后") with the target's and the draft's logits formed from their hidden
+// states and output-layer weights inside the call, l_i(y) = h_i . w_y, so that
+// the [B][k+1][V] logits are never stored.  Greedy (T == 0): the target's
+// choice is its lowest-index argmax, a draft token is kept iff it equals it.
+// Sampling (T > 0): p = softmax(l_t / T), q = softmax(l_d / T); x_i is kept iff
+// u_i q_i(x_i) < p_i(x_i); at the first rejection r a token is drawn from
+// max(0, p_r - q_r), after full acceptance from p_k.
 //
 // Kernels:
-//  k_lmhead_argmax   a bf16 GEMM H . W^T on the matrix cores
-//                    (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with an
-//                    argmax epilogue.  A work item is a 256 x 256 tile (hidden
-//                    rows x vocabulary columns); each of the 8 wavefronts
-//                    computes a 128 x 64 block.  K is staged through two LDS
-//                    buffers 64 at a time.  A slice is four 16-deep MFMA
-//                    groups; between the MFMAs of one group the wavefront reads
-//                    the next group's fragments, writes the next slice (held in
-//                    registers) to the other buffer, or issues the global loads
-//                    of the slice after it, in a fixed interleave, so that the
-//                    matrix pipe is not left waiting behind a burst of memory
-//                    instructions; one barrier per slice, before the last group,
-//                    whose MFMAs overlap the reads of the next slice's first
-//                    fragments.  The epilogue reduces the tile to (max, lowest
-//                    index) per row: one partial per row and vocabulary tile.
-//                    The grid is persistent, one workgroup per compute unit,
-//                    each taking every G-th item: all workgroups advance
-//                    through the items in step, and the items a die (XCD)
-//                    takes in one step are consecutive, so the row tiles of
-//                    one vocabulary tile run side by side on one die and share
-//                    its weight rows in that die's L2.
-//  k_lmhead_finish   per sequence: combines its rows' partials, decides every
-//                    position on one lane, writes accepted_len and
-//                    out_tokens.
+//  k_lmhead_gemm<MODE>  a bf16 GEMM H . W^T on the matrix cores
+//                    (v_mfma_f32_32x32x16_bf16, fp32 accumulation) whose
+//                    epilogue reduces each 256 x 256 tile: per row (max,
+//                    lowest index) for greedy, per row the softmax statistics
+//                    (m, s) and the logit of the row's draft token for
+//                    sampling, or the fp32 logits of a few rows for the draws.
+//                    One launch can hold two GEMMs (target rows against the
+//                    target's output layer, draft rows against the draft's).
+//                    Each of the 8 wavefronts computes a 128 x 64 block.  K
+//                    is staged through two LDS buffers 64 at a time.  A slice
+//                    is four 16-deep MFMA groups; between the MFMAs of one
+//                    group the wavefront reads the next group's fragments,
+//                    writes the next slice (held in registers) to the other
+//                    buffer, or issues the global loads of the slice after it,
+//                    in a fixed interleave, so that the matrix pipe is not left
+//                    waiting behind a burst of memory instructions; one barrier
+//                    per slice, before the last group, whose MFMAs overlap the
+//                    reads of the next slice's first fragments.  The grid is
+//                    persistent, one workgroup per compute unit, each taking
+//                    every G-th item: all workgroups advance through the items
+//                    in step, and the items a die (XCD) takes in one step are
+//                    consecutive, so the row tiles of one vocabulary tile run
+//                    side by side on one die and share its weight rows in that
+//                    die's L2.
+//  k_lmhead_finish   greedy, per sequence: the rows' argmaxes from the
+//                    partials, the decisions on one lane per position.
+//  k_lmhead_decide   sampling, per sequence: (m, Z) of every row from the
+//                    partials, p(x_i), q(x_i), the tests and the first
+//                    rejection; which rows the draw needs.
+//  k_lmhead_draw     sampling, per sequence: the draw from the residual (or
+//                    from p_k) over the draw rows' logits, by inverting the
+//                    cumulative weight in ascending token order.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -82,9 +92,47 @@ __device__ __forceinline__ void half_wave_argmax(float& v, int& i) {
     better(v, i, __shfl_xor(v, 16), __shfl_xor(i, 16));
 }
 
+// Maximum and sum over the 32 lanes of each half-wave, fixed order.
+__device__ __forceinline__ float half_wave_max(float v) {
+    v = fmaxf(v, dppf<0xb1>(v));
+    v = fmaxf(v, dppf<0x4e>(v));
+    v = fmaxf(v, dppf<0x124>(v));
+    v = fmaxf(v, dppf<0x128>(v));
+    return fmaxf(v, __shfl_xor(v, 16));
+}
+
+__device__ __forceinline__ float half_wave_sum(float v) {
+    v += dppf<0xb1>(v);
+    v += dppf<0x4e>(v);
+    v += dppf<0x124>(v);
+    v += dppf<0x128>(v);
+    return v + __shfl_xor(v, 16);
+}
+
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_argmax(LmPlan pl) {
+// The hidden-state row GEMM row m reads.
+__device__ __forceinline__ int gather_row(const LmPlan& pl, int gather, int m) {
+    if (gather == kLmRows) return m;
+    const int r = pl.seq[m].r;
+    if (gather == kLmTargetDraw) return m * (pl.k + 1) + max(r, 0);
+    return m * pl.k + min(max(r, 0), pl.k - 1);
+}
+
+// The token whose logit statistics row m captures (-1: none).
+__device__ __forceinline__ int row_token(const LmPlan& pl, int tokens, int m) {
+    int x = -1;
+    if (tokens == kLmTargetTokens) {
+        const int i = m % (pl.k + 1);
+        if (i < pl.k) x = pl.tokens[static_cast<int64_t>(m / (pl.k + 1)) * pl.k + i];
+    } else if (tokens == kLmDraftTokens) {
+        x = pl.tokens[m];
+    }
+    return (x >= 0 && x < pl.vocab) ? x : -1;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPlan pl) {
     constexpr int FM = kLmWaveM / 32;  // 32 x 32 fragments per wavefront block
     constexpr int FN = kLmWaveN / 32;
     constexpr int WAVES_M = kLmBM / kLmWaveM;
@@ -97,8 +145,10 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_argmax(Lm
     static_assert(kLmHiddenMultiple % kLmBK == 0, "whole K slices");
     __shared__ __attribute__((aligned(16))) uint16_t sa[2][kLmBM * kLdsStride];
     __shared__ __attribute__((aligned(16))) uint16_t sb[2][kLmBN * kLdsStride];
-    __shared__ float cand_v[WAVES_N][kLmBM];
-    __shared__ int cand_i[WAVES_N][kLmBM];
+    __shared__ float cand_v[WAVES_N][kLmBM];  // argmax max, statistics m
+    __shared__ int cand_i[WAVES_N][kLmBM];    // argmax index
+    __shared__ float cand_s[WAVES_N][kLmBM];  // statistics s
+    __shared__ int stok[kLmBM];               // statistics: each row's token
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -107,7 +157,7 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_argmax(Lm
     const int wn = wave / WAVES_M;  // column block of the tile
     const int D = pl.hidden;
     const int kblocks = D / kLmBK;
-    const int64_t items = lmhead_items(pl);
+    const int64_t items = pl.items;
     const int G = gridDim.x;  // a multiple of kXcds
     // Blocks are dealt to the XCDs by index mod 8: give each die a run of
     // consecutive items per step.
@@ -123,17 +173,31 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_argmax(Lm
     uint16_t* const sb_st = &sb[0][prow * kLdsStride + pseg * 8];
 
     for (int64_t item = slot; item < items; item += G) {
-        const int mt = static_cast<int>(item % pl.m_tiles);
-        const int nt = static_cast<int>(item / pl.m_tiles);
+        // The GEMM this item belongs to (fields picked one by one: indexing
+        // the argument's array with a varying index would copy it to scratch).
+        const bool g1 = pl.n_gemms > 1 && item >= pl.g[1].item0;
+        const uint16_t* const ga = g1 ? pl.g[1].a : pl.g[0].a;
+        const uint16_t* const gw = g1 ? pl.g[1].w : pl.g[0].w;
+        const int g_rows = g1 ? pl.g[1].rows : pl.g[0].rows;
+        const int g_mt = g1 ? pl.g[1].m_tiles : pl.g[0].m_tiles;
+        const int g_out0 = g1 ? pl.g[1].out_row0 : pl.g[0].out_row0;
+        const int g_gather = g1 ? pl.g[1].gather : pl.g[0].gather;
+        const int64_t li = item - (g1 ? pl.g[1].item0 : pl.g[0].item0);
+        const int mt = static_cast<int>(li % g_mt);
+        const int nt = static_cast<int>(li / g_mt);
         const int m0 = mt * kLmBM;
         const int n0 = nt * kLmBN;
-        const uint16_t* const a_base = pl.hidden_states + static_cast<int64_t>(m0) * D;
-        const uint16_t* const b_base = pl.weight + static_cast<int64_t>(n0) * D;
-        const int a_last = pl.rows - 1 - m0;
+        const uint16_t* const a_base = ga;
+        const uint16_t* const b_base = gw + static_cast<int64_t>(n0) * D;
         const int b_last = pl.vocab - 1 - n0;
-        uint32_t a_off[PA], b_off[PB];  // elements from the tile's base, < 256 * 65536
+        // A offsets are absolute (rows x hidden < 2^31 is checked on the
+        // host), W offsets are from the tile's first row.
+        uint32_t a_off[PA], b_off[PB];
 #pragma unroll
-        for (int q = 0; q < PA; ++q) a_off[q] = static_cast<uint32_t>(min(prow + q * ROWS_PER_PASS, a_last) * D + pseg * 8);
+        for (int q = 0; q < PA; ++q) {
+            const int m = min(m0 + prow + q * ROWS_PER_PASS, g_rows - 1);
+            a_off[q] = static_cast<uint32_t>(gather_row(pl, g_gather, m) * D + pseg * 8);
+        }
 #pragma unroll
         for (int q = 0; q < PB; ++q) b_off[q] = static_cast<uint32_t>(min(prow + q * ROWS_PER_PASS, b_last) * D + pseg * 8);
         floatx16_t acc[FM][FN];
@@ -186,6 +250,11 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_argmax(Lm
 #pragma unroll
         for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + b_off[q]);
         __syncthreads();  // the previous item's readers of the buffers and of cand are done
+        if (MODE == kLmStats) {
+            const int g_tok = g1 ? pl.g[1].tokens : pl.g[0].tokens;
+            for (int r = tid; r < kLmBM; r += kLmThreads)
+                stok[r] = m0 + r < g_rows ? row_token(pl, g_tok, m0 + r) : -1;
+        }
 #pragma unroll
         for (int q = 0; q < PA; ++q) *reinterpret_cast<uint4*>(sa_st + q * ROWS_PER_PASS * kLdsStride) = ra[q];
 #pragma unroll
@@ -242,35 +311,83 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_argmax(Lm
 
         // Epilogue: accumulator j of lane l holds row 8(j/4) + 4(l/32) + j%4
         // of a 32 x 32 block, column l % 32.
+        if (MODE == kLmStore) {
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int m = m0 + wm * kLmWaveM + mi * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+                    float* const out = pl.logits + static_cast<int64_t>(g_out0 + m) * pl.vocab;
+#pragma unroll
+                    for (int ni = 0; ni < FN; ++ni) {
+                        const int col = n0 + wn * kLmWaveN + ni * 32 + (lane & 31);
+                        if (m < g_rows && col < pl.vocab) out[col] = acc[mi][ni][j];
+                    }
+                }
+            continue;
+        }
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                float v = neg_inf_f();
-                int idx = INT_MAX;
-#pragma unroll
-                for (int ni = 0; ni < FN; ++ni) {
-                    const int col = n0 + wn * kLmWaveN + ni * 32 + (lane & 31);
-                    if (col < pl.vocab) better(v, idx, acc[mi][ni][j], col);
-                }
-                half_wave_argmax(v, idx);
                 const int row = wm * kLmWaveM + mi * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-                if ((lane & 31) == 0) {
-                    cand_v[wn][row] = v;
-                    cand_i[wn][row] = idx;
+                if (MODE == kLmArgmax) {
+                    float v = neg_inf_f();
+                    int idx = INT_MAX;
+#pragma unroll
+                    for (int ni = 0; ni < FN; ++ni) {
+                        const int col = n0 + wn * kLmWaveN + ni * 32 + (lane & 31);
+                        if (col < pl.vocab) better(v, idx, acc[mi][ni][j], col);
+                    }
+                    half_wave_argmax(v, idx);
+                    if ((lane & 31) == 0) {
+                        cand_v[wn][row] = v;
+                        cand_i[wn][row] = idx;
+                    }
+                } else {
+                    const int tok = stok[row];
+                    float v[FN];
+                    float mx = neg_inf_f();
+#pragma unroll
+                    for (int ni = 0; ni < FN; ++ni) {
+                        const int col = n0 + wn * kLmWaveN + ni * 32 + (lane & 31);
+                        v[ni] = col < pl.vocab ? acc[mi][ni][j] * pl.c2 : neg_inf_f();
+                        mx = fmaxf(mx, v[ni]);
+                        if (col == tok && m0 + row < g_rows) pl.lx[g_out0 + m0 + row] = acc[mi][ni][j];
+                    }
+                    mx = half_wave_max(mx);
+                    float sum = 0.f;
+#pragma unroll
+                    for (int ni = 0; ni < FN; ++ni) sum += v[ni] == neg_inf_f() ? 0.f : exp2f(v[ni] - mx);
+                    sum = half_wave_sum(sum);
+                    if ((lane & 31) == 0) {
+                        cand_v[wn][row] = mx;
+                        cand_s[wn][row] = sum;
+                    }
                 }
             }
         }
         __syncthreads();
         for (int r = tid; r < kLmBM; r += kLmThreads) {
             const int m = m0 + r;
-            if (m < pl.rows) {
+            if (m >= g_rows) continue;
+            const int64_t at = static_cast<int64_t>(g_out0 + m) * pl.n_parts + nt;
+            if (MODE == kLmArgmax) {
                 float v = cand_v[0][r];
                 int idx = cand_i[0][r];
 #pragma unroll
                 for (int c = 1; c < WAVES_N; ++c) better(v, idx, cand_v[c][r], cand_i[c][r]);
-                pl.part_v[static_cast<int64_t>(m) * pl.n_parts + nt] = v;
-                pl.part_i[static_cast<int64_t>(m) * pl.n_parts + nt] = idx;
+                pl.part_v[at] = v;
+                pl.part_i[at] = idx;
+            } else {
+                float mx = cand_v[0][r];
+#pragma unroll
+                for (int c = 1; c < WAVES_N; ++c) mx = fmaxf(mx, cand_v[c][r]);
+                float sum = 0.f;
+#pragma unroll
+                for (int c = 0; c < WAVES_N; ++c) sum += cand_s[c][r] * exp2f(cand_v[c][r] - mx);
+                pl.part_v[at] = mx;
+                pl.part_s[at] = sum;
             }
         }
     }
@@ -335,32 +452,232 @@ __global__ __launch_bounds__(kFinishThreads) void k_lmhead_finish(LmPlan pl) {
     if (lane == 0) pl.accepted_len[b] = r;
 }
 
+// Sampling, per sequence: (m, Z) of target rows 0..k and draft rows
+// 0..k-1 from their partials (one wavefront per row, rows round-robin), then
+// on one lane per position p(x_i), q(x_i) and the test u_i q < p.
+__global__ __launch_bounds__(kFinishThreads) void k_lmhead_decide(LmPlan pl) {
+    __shared__ float row_m[2 * kLmMaxRows], row_z[2 * kLmMaxRows];  // target rows 0..k, then draft rows
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int k = pl.k;
+    const int n = pl.n_parts;
+    for (int t = wave; t < 2 * k + 1; t += kFinishThreads / 64) {
+        const int64_t row = t <= k ? static_cast<int64_t>(b) * (k + 1) + t
+                                   : pl.rows_t + static_cast<int64_t>(b) * k + (t - k - 1);
+        const float* pm = pl.part_v + row * n;
+        const float* ps = pl.part_s + row * n;
+        float mx = neg_inf_f();
+        for (int c0 = 0; c0 < n; c0 += 256) {
+            float tv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * 64 + lane;
+                tv[u] = c < n ? pm[c] : neg_inf_f();
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) mx = fmaxf(mx, tv[u]);
+        }
+        mx = half_wave_max(mx);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float z = 0.f;
+        for (int c0 = 0; c0 < n; c0 += 256) {
+            float tm[4], tz[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * 64 + lane;
+                tm[u] = c < n ? pm[c] : mx;
+                tz[u] = c < n ? ps[c] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) z += tz[u] * exp2f(tm[u] - mx);
+        }
+        z = half_wave_sum(z);
+        z += __shfl_xor(z, 32);
+        if (lane == 0) {
+            row_m[t] = mx;
+            row_z[t] = z;
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const bool active = lane < k;
+    int x = 0;
+    float p = 0.f, q = 0.f;
+    bool keep = false;
+    if (active) {
+        x = pl.tokens[static_cast<int64_t>(b) * k + lane];
+        const float lt = pl.lx[static_cast<int64_t>(b) * (k + 1) + lane];
+        const float ld = pl.lx[pl.rows_t + static_cast<int64_t>(b) * k + lane];
+        // log2 p(x) and log2 q(x): the test u q < p is taken in the log
+        // domain, where p and q far below the smallest float still compare.
+        const float lp = lt * pl.c2 - row_m[lane] - log2f(row_z[lane]);
+        const float lq = ld * pl.c2 - row_m[k + 1 + lane] - log2f(row_z[k + 1 + lane]);
+        p = exp2f(lp);
+        q = exp2f(lq);
+        const float u = pl.uniforms[static_cast<int64_t>(b) * (k + 1) + lane];
+        keep = (u > 0.f ? log2f(u) : neg_inf_f()) + lq < lp;
+    }
+    const bool bad = active && (x < 0 || x >= pl.vocab);
+    const bool invalid = __ballot(bad) != 0ull;
+    const uint64_t rejected = __ballot(active && !keep);
+    const int r = invalid ? -1 : (rejected ? __builtin_ctzll(rejected) : k);
+    if (pl.probs_out && active) {
+        pl.probs_out[(static_cast<int64_t>(b) * k + lane) * 2] = invalid ? __builtin_nanf("") : p;
+        pl.probs_out[(static_cast<int64_t>(b) * k + lane) * 2 + 1] = invalid ? __builtin_nanf("") : q;
+    }
+    int32_t* out = pl.out_tokens + static_cast<int64_t>(b) * (k + 1);
+    for (int j = lane; j <= k; j += 64) {
+        if (invalid || j > r) out[j] = -1;
+        else if (j < r) out[j] = x;  // j < r <= k: lane j holds x_j
+        // j == r: the draw writes it
+    }
+    if (lane == 0) {
+        pl.accepted_len[b] = r;
+        LmSeqDraw d;
+        d.r = r;
+        const int rt = max(r, 0);
+        const int rd = min(max(r, 0), k - 1);
+        d.mt = row_m[rt];
+        d.zt = row_z[rt];
+        d.md = row_m[k + 1 + rd];
+        d.zd = row_z[k + 1 + rd];
+        d.pad[0] = d.pad[1] = d.pad[2] = 0;
+        pl.seq[b] = d;
+    }
+}
+
+// Sampling, per sequence: the draw at the first rejection r from
+// max(0, p_r - q_r), or after full acceptance from p_k, over the draw rows'
+// logits.  Each thread sums the weights of one contiguous range of tokens in
+// ascending order; the ranges' prefix finds the range holding u * total,
+// and that range's thread finds the token.
+__global__ __launch_bounds__(kFinishThreads) void k_lmhead_draw(LmPlan pl) {
+    __shared__ float sums[kFinishThreads];
+    __shared__ float excl[kFinishThreads];
+    __shared__ float s_total;
+    __shared__ int s_first, s_last;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const LmSeqDraw d = pl.seq[b];
+    const int k = pl.k;
+    const int r = d.r;
+    if (r < 0) return;  // invalid token: the decision step wrote -1 everywhere
+    const int V = pl.vocab;
+    const float* lt = pl.logits + static_cast<int64_t>(b) * V;
+    const float* ld = pl.logits + static_cast<int64_t>(pl.batch + b) * V;
+    const int span = (V + kFinishThreads - 1) / kFinishThreads;
+    const int y0 = min(V, tid * span), y1 = min(V, y0 + span);
+    const float c2 = pl.c2;
+    bool residual = r < k;
+    auto weight = [&](int y) {
+        const float pt = exp2f(lt[y] * c2 - d.mt) / d.zt;
+        if (!residual) return pt;
+        const float qd = exp2f(ld[y] * c2 - d.md) / d.zd;
+        return pt > qd ? pt - qd : 0.f;
+    };
+    float mine = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+        mine = 0.f;
+        for (int y = y0; y < y1; ++y) mine += weight(y);
+        sums[tid] = mine;
+        __syncthreads();
+        if (tid == 0) {
+            float c = 0.f;
+            for (int t = 0; t < kFinishThreads; ++t) {
+                excl[t] = c;
+                c += sums[t];
+            }
+            s_total = c;
+            s_first = INT_MAX;
+            s_last = -1;
+        }
+        __syncthreads();
+        const bool retry = residual && !(s_total > 0.f);
+        __syncthreads();  // every thread has read s_total before a second pass rewrites it
+        if (!retry) break;
+        residual = false;  // an all-zero residual (p_r == q_r): draw from p_r
+    }
+    const float theta = pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k] * s_total;
+    // The first range (ascending tokens) whose inclusive prefix exceeds
+    // theta; if rounding leaves none, the last range with any weight.
+    if (mine > 0.f) {
+        if (excl[tid] + mine > theta) atomicMin(&s_first, tid);
+        atomicMax(&s_last, tid);
+    }
+    __syncthreads();
+    const int pick = s_first != INT_MAX ? s_first : max(s_last, 0);
+    if (tid != pick) return;
+    float c = excl[tid];
+    int ystar = -1, last_pos = -1;
+    for (int y = y0; y < y1; ++y) {
+        const float w = weight(y);
+        if (w > 0.f) last_pos = y;
+        c += w;
+        if (c > theta) {
+            ystar = y;
+            break;
+        }
+    }
+    if (ystar < 0) ystar = last_pos >= 0 ? last_pos : max(y0, min(y1, V) - 1);
+    pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + r] = ystar;
+}
+
 }  // namespace
 
-hipError_t launch_lmhead(const LmPlan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-    hipError_t e;
+namespace {
+
+// As many workgroups as the compute units hold at once, a multiple of the
+// XCD count, no more than there are items.
+hipError_t gemm_grid(const LmPlan& pl, unsigned* grid) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    int64_t g = std::max<int64_t>(kXcds, static_cast<int64_t>(cus) * kLmBlocksPerCu / kXcds * kXcds);
+    g = std::min<int64_t>(g, (pl.items + kXcds - 1) / kXcds * kXcds);
+    *grid = static_cast<unsigned>(g);
+    return hipSuccess;
+}
+
+template <int MODE>
+hipError_t launch_gemm(const LmPlan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    unsigned grid = 0;
+    hipError_t e = gemm_grid(pl, &grid);
+    if (e != hipSuccess) return e;
     if (ev0 && ev1) {
         e = hipEventRecord(ev0, stream);
         if (e != hipSuccess) return e;
     }
-    // As many workgroups as the compute units hold at once, a multiple of
-    // the XCD count, no more than there are items.
-    int dev = 0, cus = 0;
-    e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    const int64_t items = lmhead_items(pl);
-    int64_t grid = std::max<int64_t>(kXcds, static_cast<int64_t>(cus) * kLmBlocksPerCu / kXcds * kXcds);
-    grid = std::min<int64_t>(grid, (items + kXcds - 1) / kXcds * kXcds);
-    hipLaunchKernelGGL(k_lmhead_argmax, dim3(static_cast<unsigned>(grid)), dim3(kLmThreads), 0, stream, pl);
+    hipLaunchKernelGGL(k_lmhead_gemm<MODE>, dim3(grid), dim3(kLmThreads), 0, stream, pl);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (ev0 && ev1) {
-        e = hipEventRecord(ev1, stream);
-        if (e != hipSuccess) return e;
-    }
+    if (ev0 && ev1) e = hipEventRecord(ev1, stream);
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_lmhead_greedy(const LmPlan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    hipError_t e = launch_gemm<kLmArgmax>(pl, stream, ev0, ev1);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_lmhead_finish, dim3(static_cast<unsigned>(pl.batch)), dim3(kFinishThreads), 0, stream, pl);
+    return hipGetLastError();
+}
+
+hipError_t launch_lmhead_sample(const LmPlan& stats, const LmPlan& draw, hipStream_t stream, hipEvent_t ev0,
+                                hipEvent_t ev1) {
+    hipError_t e = launch_gemm<kLmStats>(stats, stream, ev0, ev1);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_lmhead_decide, dim3(static_cast<unsigned>(stats.batch)), dim3(kFinishThreads), 0, stream,
+                       stats);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_gemm<kLmStore>(draw, stream, nullptr, nullptr);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_lmhead_draw, dim3(static_cast<unsigned>(draw.batch)), dim3(kFinishThreads), 0, stream, draw);
     return hipGetLastError();
 }
 

@@ -347,3 +347,59 @@ def test_lm_head_null_misaligned_and_workspace_errors(lib):
     assert h.untouched()
     e = _lm_desc(B=0)
     assert lib.sv_verify_lm_head_greedy(ctypes.byref(e), *([None] * 7), 0, None) == 0
+
+
+def _lms_desc(B=2, k=3, V=1000, D=64, T=1.0):
+    return sv.LmHeadSampleDesc(B, k, V, D, T, None, None)
+
+
+def _call_lms(lib, d, h, **over):
+    args = dict(th=h.hidden.ctypes.data, tw=h.weight.ctypes.data, dh=h.hidden.ctypes.data, dw=h.weight.ctypes.data,
+                tokens=h.tokens.ctypes.data, u=h.u.ctypes.data, acc=h.acc.ctypes.data, out=h.out.ctypes.data,
+                probs=None, ws=h.ws.ctypes.data, ws_bytes=h.ws.nbytes)
+    args.update(over)
+    return lib.sv_verify_lm_head(ctypes.byref(d) if d is not None else None, args["th"], args["tw"], args["dh"],
+                                 args["dw"], args["tokens"], args["u"], args["acc"], args["out"], args["probs"],
+                                 args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("T", [0.0, -1.0, 1e-5, float("nan"), float("inf")])
+def test_lm_head_sample_rejects_bad_temperature(lib, T):
+    n = ctypes.c_size_t(7)
+    assert lib.sv_lm_head_sample_workspace_size(ctypes.byref(_lms_desc(T=T)), ctypes.byref(n)) == 4
+    assert n.value == 7
+    h = _LmBufs()
+    h.u = np.zeros(2 * 4, np.float32)
+    assert _call_lms(lib, _lms_desc(T=T), h) == 4
+    assert h.untouched()
+
+
+def test_lm_head_sample_args_and_workspace(lib):
+    h = _LmBufs()
+    h.u = np.zeros(2 * 4, np.float32)
+    d = _lms_desc()
+    assert _call_lms(lib, None, h) == 1
+    for name in ("th", "tw", "dh", "dw", "tokens", "u", "acc", "out", "ws"):
+        assert _call_lms(lib, d, h, **{name: None}) == 1, name
+    assert _call_lms(lib, d, h, dh=h.hidden.ctypes.data + 4) == 11
+    assert _call_lms(lib, d, h, dw=h.weight.ctypes.data + 2) == 11
+    bad = _lms_desc(D=96)
+    assert _call_lms(lib, bad, h) == 2
+    n = ctypes.c_size_t()
+    assert lib.sv_lm_head_sample_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert _call_lms(lib, d, h, ws_bytes=n.value - 1) == 6
+    assert h.untouched()
+    # the draw rows' logits dominate: two fp32 rows of V per sequence
+    big = ctypes.c_size_t()
+    assert lib.sv_lm_head_sample_workspace_size(ctypes.byref(_lms_desc(B=128, k=5, V=151936, D=4096)),
+                                                ctypes.byref(big)) == 0
+    assert big.value >= 2 * 128 * 151936 * 4
+    e = _lms_desc(B=0)
+    assert lib.sv_verify_lm_head(ctypes.byref(e), *([None] * 10), 0, None) == 0
+
+
+def test_lm_head_rows_times_hidden_limit(lib):
+    n = ctypes.c_size_t()
+    # B (k+1) D >= 2^31 elements: hidden-state offsets would not fit 32 bits
+    assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc(B=8192, k=63, V=1000, D=4096)), ctypes.byref(n)) == 2
+    assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc(B=8191, k=63, V=1000, D=4096)), ctypes.byref(n)) == 0

@@ -39,6 +39,19 @@ lmhead_tiny        B=6, k=4, V=1000, D=128, plant 8, hit 0.8
 lmhead_selfdraft   B=128, k=5, V=151936, D=4096, plant 8, hit 0.95
 lmhead_grpo        B=320, k=7, V=151936, D=4096, plant 8, hit 0.9
 =================  ===================================================================
+
+Sampling (T > 0) LM-head workloads add the draft side: the draft's hidden
+state at position i is the target's plus ``draft_noise`` * N(0, I) (bf16),
+its output layer is the target's (a drafter that shares the output layer) or,
+with ``draft_weight_noise`` > 0, the target's plus that much relative noise;
+uniforms U[0,1) per sequence.  The planted margin is larger (14 at V=151936:
+the planted token holds about 80% of the target's mass at T=1).
+
+=======================  =============================================================
+lmhead_sample_tiny       B=6, k=4, V=1000, D=128, T=1, plant 8, hit 0.8
+lmhead_sample_selfdraft  B=128, k=5, V=151936, D=4096, T=1, plant 14, hit 0.95
+lmhead_sample_grpo       B=320, k=7, V=151936, D=4096, T=0.6, plant 14, hit 0.9
+=======================  =============================================================
 """
 from __future__ import annotations
 
@@ -51,7 +64,8 @@ import numpy as np
 
 __all__ = ["Config", "Workload", "CONFIGS", "get_config", "generate", "generate_on_device", "to_device",
            "round_to_bf16_bits", "bf16_bits_to_f32", "LmHeadConfig", "LmHeadWorkload", "LM_CONFIGS",
-           "lm_head_weight", "generate_lm_head", "lm_head_to_device"]
+           "lm_head_weight", "generate_lm_head", "lm_head_to_device", "LmHeadSampleWorkload",
+           "generate_lm_head_sample", "lm_head_sample_to_device"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -305,6 +319,9 @@ class LmHeadConfig:
     plant: float = 8.0   # margin planted for the intended token of each position
     hit: float = 0.9     # probability that a draft token is the planted token
     seed: int = 11
+    T: float = 0.0       # temperature (0: greedy workloads)
+    draft_noise: float = 0.3         # draft hidden state = target's + draft_noise * N(0, I)
+    draft_weight_noise: float = 0.0  # > 0: the draft's own output layer, W (1 + noise N(0,1))
 
     @property
     def rows(self) -> int:
@@ -322,6 +339,10 @@ LM_CONFIGS = {
     "lmhead_tiny": LmHeadConfig("lmhead_tiny", 6, 4, 1000, 128, hit=0.8),
     "lmhead_selfdraft": LmHeadConfig("lmhead_selfdraft", 128, 5, 151936, 4096, hit=0.95),
     "lmhead_grpo": LmHeadConfig("lmhead_grpo", 320, 7, 151936, 4096, hit=0.9),
+    "lmhead_sample_tiny": LmHeadConfig("lmhead_sample_tiny", 6, 4, 1000, 128, hit=0.8, T=1.0),
+    "lmhead_sample_selfdraft": LmHeadConfig("lmhead_sample_selfdraft", 128, 5, 151936, 4096, plant=14.0,
+                                            hit=0.95, T=1.0),
+    "lmhead_sample_grpo": LmHeadConfig("lmhead_sample_grpo", 320, 7, 151936, 4096, plant=14.0, hit=0.9, T=0.6),
 }
 
 _W_SLAB = 4096  # weight rows drawn per generator stream
@@ -386,3 +407,48 @@ def lm_head_to_device(wl: LmHeadWorkload, device):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
 
     return bf(wl.hidden), bf(wl.weight), torch.from_numpy(np.ascontiguousarray(wl.tokens)).to(device)
+
+
+@dataclasses.dataclass
+class LmHeadSampleWorkload:
+    config: LmHeadConfig
+    target_hidden: np.ndarray   # [B][k+1][D] uint16
+    target_weight: np.ndarray   # [V][D] uint16
+    draft_hidden: np.ndarray    # [B][k][D] uint16
+    draft_weight: np.ndarray    # [V][D] uint16 (the target's array when shared)
+    tokens: np.ndarray          # [B][k] int32
+    uniforms: np.ndarray        # [B][k+1] float32
+    planted: np.ndarray         # [B][k+1] int32
+
+
+def generate_lm_head_sample(cfg: LmHeadConfig, weight: Optional[np.ndarray] = None) -> LmHeadSampleWorkload:
+    """Target side as generate_lm_head; draft hidden states, the draft's
+    output layer and the uniforms from streams of their own."""
+    base = generate_lm_head(cfg, weight)
+    w = base.weight
+    if cfg.draft_weight_noise > 0.0:
+        z = _rng(cfg.seed, 5).standard_normal(w.shape, dtype=np.float32)
+        wd = round_to_bf16_bits(bf16_bits_to_f32(w) * (np.float32(1.0) + np.float32(cfg.draft_weight_noise) * z))
+    else:
+        wd = w
+    hd = np.empty((cfg.B, cfg.k, cfg.D), dtype=np.uint16)
+    u = np.empty((cfg.B, cfg.k + 1), dtype=np.float32)
+    for b in range(cfg.B):
+        z = _rng(cfg.seed, 3, b).standard_normal((cfg.k, cfg.D), dtype=np.float32)
+        hd[b] = round_to_bf16_bits(bf16_bits_to_f32(base.hidden[b, : cfg.k]) + np.float32(cfg.draft_noise) * z)
+        u[b] = _rng(cfg.seed, 4, b).random(cfg.k + 1, dtype=np.float32)
+    return LmHeadSampleWorkload(cfg, base.hidden, w, hd, wd, base.tokens, u, base.planted)
+
+
+def lm_head_sample_to_device(wl: LmHeadSampleWorkload, device):
+    """(target_hidden, target_weight, draft_hidden, draft_weight, tokens,
+    uniforms) on `device`; a shared output layer is uploaded once."""
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    th, tw = bf(wl.target_hidden), bf(wl.target_weight)
+    dw = tw if wl.draft_weight is wl.target_weight else bf(wl.draft_weight)
+    return (th, tw, bf(wl.draft_hidden), dw, torch.from_numpy(np.ascontiguousarray(wl.tokens)).to(device),
+            torch.from_numpy(np.ascontiguousarray(wl.uniforms)).to(device))
