@@ -26,13 +26,6 @@ enum LmMode : int32_t {
     kLmStore = 2    // the logits themselves, fp32
 };
 
-// Which hidden-state row GEMM row m reads.
-enum LmGather : int32_t {
-    kLmRows = 0,        // row m
-    kLmTargetDraw = 1,  // sequence m's target row at its first rejection r (k after full acceptance)
-    kLmDraftDraw = 2    // sequence m's draft row at min(r, k-1)
-};
-
 // Which token's logit a statistics row captures.
 enum LmTokens : int32_t {
     kLmNoTokens = 0,
@@ -48,9 +41,7 @@ struct LmGemm {
     int32_t m_tiles;    // ceil(rows / kLmBM)
     int64_t item0;      // its first work item in the launch
     int32_t out_row0;   // its first row in the per-row outputs
-    int32_t gather;     // LmGather
     int32_t tokens;     // LmTokens (statistics mode)
-    int32_t pad;
 };
 
 // Per-sequence result of the decision step of sampling verification.
@@ -78,6 +69,9 @@ struct LmPlan {
     float* lx;                      // workspace [rows]: the logit of the row's token (sampling)
     LmSeqDraw* seq;                 // workspace [batch] (sampling)
     float* logits;                  // workspace [2 batch][vocab]: target, then draft draw rows (sampling)
+    const uint16_t* target_hidden;  // [batch][k+1][hidden] (sampling: the decision step copies draw rows)
+    const uint16_t* draft_hidden;   // [batch][k][hidden]
+    uint16_t* draw_hidden;          // workspace [2 batch][hidden]: each sequence's target, then draft draw row
     int32_t batch;
     int32_t k;
     int32_t vocab;
@@ -107,7 +101,8 @@ hipError_t launch_lmhead_greedy(const LmPlan& pl, hipStream_t stream, hipEvent_t
 
 // Sampling verification: the statistics GEMM over target and draft rows
 // (bracketed by the events), the decision step, the logits GEMM over every
-// sequence's draw rows (`draw` holds those GEMMs), then the draws.
+// sequence's draw rows (copied by the decision step; `draw` holds those
+// GEMMs), then the draws.
 hipError_t launch_lmhead_sample(const LmPlan& stats, const LmPlan& draw, hipStream_t stream, hipEvent_t ev0,
                                 hipEvent_t ev1);
 

@@ -111,14 +111,6 @@ __device__ __forceinline__ float half_wave_sum(float v) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// The hidden-state row GEMM row m reads.
-__device__ __forceinline__ int gather_row(const LmPlan& pl, int gather, int m) {
-    if (gather == kLmRows) return m;
-    const int r = pl.seq[m].r;
-    if (gather == kLmTargetDraw) return m * (pl.k + 1) + max(r, 0);
-    return m * pl.k + min(max(r, 0), pl.k - 1);
-}
-
 // The token whose logit statistics row m captures (-1: none).
 __device__ __forceinline__ int row_token(const LmPlan& pl, int tokens, int m) {
     int x = -1;
@@ -181,7 +173,6 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
         const int g_rows = g1 ? pl.g[1].rows : pl.g[0].rows;
         const int g_mt = g1 ? pl.g[1].m_tiles : pl.g[0].m_tiles;
         const int g_out0 = g1 ? pl.g[1].out_row0 : pl.g[0].out_row0;
-        const int g_gather = g1 ? pl.g[1].gather : pl.g[0].gather;
         const int64_t li = item - (g1 ? pl.g[1].item0 : pl.g[0].item0);
         const int mt = static_cast<int>(li % g_mt);
         const int nt = static_cast<int>(li / g_mt);
@@ -196,7 +187,7 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
 #pragma unroll
         for (int q = 0; q < PA; ++q) {
             const int m = min(m0 + prow + q * ROWS_PER_PASS, g_rows - 1);
-            a_off[q] = static_cast<uint32_t>(gather_row(pl, g_gather, m) * D + pseg * 8);
+            a_off[q] = static_cast<uint32_t>(m * D + pseg * 8);
         }
 #pragma unroll
         for (int q = 0; q < PB; ++q) b_off[q] = static_cast<uint32_t>(min(prow + q * ROWS_PER_PASS, b_last) * D + pseg * 8);
@@ -501,65 +492,103 @@ __global__ __launch_bounds__(kFinishThreads) void k_lmhead_decide(LmPlan pl) {
         }
     }
     __syncthreads();
-    if (wave != 0) return;
-    const bool active = lane < k;
-    int x = 0;
-    float p = 0.f, q = 0.f;
-    bool keep = false;
-    if (active) {
-        x = pl.tokens[static_cast<int64_t>(b) * k + lane];
-        const float lt = pl.lx[static_cast<int64_t>(b) * (k + 1) + lane];
-        const float ld = pl.lx[pl.rows_t + static_cast<int64_t>(b) * k + lane];
-        // log2 p(x) and log2 q(x): the test u q < p is taken in the log
-        // domain, where p and q far below the smallest float still compare.
-        const float lp = lt * pl.c2 - row_m[lane] - log2f(row_z[lane]);
-        const float lq = ld * pl.c2 - row_m[k + 1 + lane] - log2f(row_z[k + 1 + lane]);
-        p = exp2f(lp);
-        q = exp2f(lq);
-        const float u = pl.uniforms[static_cast<int64_t>(b) * (k + 1) + lane];
-        keep = (u > 0.f ? log2f(u) : neg_inf_f()) + lq < lp;
+    __shared__ int s_r;
+    if (wave == 0) {
+        const bool active = lane < k;
+        int x = 0;
+        float p = 0.f, q = 0.f;
+        bool keep = false;
+        if (active) {
+            x = pl.tokens[static_cast<int64_t>(b) * k + lane];
+            const float lt = pl.lx[static_cast<int64_t>(b) * (k + 1) + lane];
+            const float ld = pl.lx[pl.rows_t + static_cast<int64_t>(b) * k + lane];
+            // log2 p(x) and log2 q(x): the test u q < p is taken in the log
+            // domain, where p and q far below the smallest float still compare.
+            const float lp = lt * pl.c2 - row_m[lane] - log2f(row_z[lane]);
+            const float lq = ld * pl.c2 - row_m[k + 1 + lane] - log2f(row_z[k + 1 + lane]);
+            p = exp2f(lp);
+            q = exp2f(lq);
+            const float u = pl.uniforms[static_cast<int64_t>(b) * (k + 1) + lane];
+            keep = (u > 0.f ? log2f(u) : neg_inf_f()) + lq < lp;
+        }
+        const bool bad = active && (x < 0 || x >= pl.vocab);
+        const bool invalid = __ballot(bad) != 0ull;
+        const uint64_t rejected = __ballot(active && !keep);
+        const int r = invalid ? -1 : (rejected ? __builtin_ctzll(rejected) : k);
+        if (pl.probs_out && active) {
+            pl.probs_out[(static_cast<int64_t>(b) * k + lane) * 2] = invalid ? __builtin_nanf("") : p;
+            pl.probs_out[(static_cast<int64_t>(b) * k + lane) * 2 + 1] = invalid ? __builtin_nanf("") : q;
+        }
+        int32_t* out = pl.out_tokens + static_cast<int64_t>(b) * (k + 1);
+        for (int j = lane; j <= k; j += 64) {
+            if (invalid || j > r) out[j] = -1;
+            else if (j < r) out[j] = x;  // j < r <= k: lane j holds x_j
+            // j == r: the draw writes it
+        }
+        if (lane == 0) {
+            pl.accepted_len[b] = r;
+            LmSeqDraw d;
+            d.r = r;
+            const int rt = max(r, 0);
+            const int rd = min(max(r, 0), k - 1);
+            d.mt = row_m[rt];
+            d.zt = row_z[rt];
+            d.md = row_m[k + 1 + rd];
+            d.zd = row_z[k + 1 + rd];
+            d.pad[0] = d.pad[1] = d.pad[2] = 0;
+            pl.seq[b] = d;
+            s_r = r;
+        }
     }
-    const bool bad = active && (x < 0 || x >= pl.vocab);
-    const bool invalid = __ballot(bad) != 0ull;
-    const uint64_t rejected = __ballot(active && !keep);
-    const int r = invalid ? -1 : (rejected ? __builtin_ctzll(rejected) : k);
-    if (pl.probs_out && active) {
-        pl.probs_out[(static_cast<int64_t>(b) * k + lane) * 2] = invalid ? __builtin_nanf("") : p;
-        pl.probs_out[(static_cast<int64_t>(b) * k + lane) * 2 + 1] = invalid ? __builtin_nanf("") : q;
-    }
-    int32_t* out = pl.out_tokens + static_cast<int64_t>(b) * (k + 1);
-    for (int j = lane; j <= k; j += 64) {
-        if (invalid || j > r) out[j] = -1;
-        else if (j < r) out[j] = x;  // j < r <= k: lane j holds x_j
-        // j == r: the draw writes it
-    }
-    if (lane == 0) {
-        pl.accepted_len[b] = r;
-        LmSeqDraw d;
-        d.r = r;
-        const int rt = max(r, 0);
-        const int rd = min(max(r, 0), k - 1);
-        d.mt = row_m[rt];
-        d.zt = row_z[rt];
-        d.md = row_m[k + 1 + rd];
-        d.zd = row_z[k + 1 + rd];
-        d.pad[0] = d.pad[1] = d.pad[2] = 0;
-        pl.seq[b] = d;
+    __syncthreads();
+    // The draw rows (target row r, or k after full acceptance; draft row r)
+    // go to the draw GEMM's input, 16 bytes per thread per step.
+    const int r = s_r;
+    const int64_t D = pl.hidden;
+    const uint4* src_t = reinterpret_cast<const uint4*>(pl.target_hidden + (static_cast<int64_t>(b) * (k + 1) + max(r, 0)) * D);
+    const uint4* src_d = reinterpret_cast<const uint4*>(pl.draft_hidden + (static_cast<int64_t>(b) * k + min(max(r, 0), k - 1)) * D);
+    uint4* dst_t = reinterpret_cast<uint4*>(pl.draw_hidden + static_cast<int64_t>(b) * D);
+    uint4* dst_d = reinterpret_cast<uint4*>(pl.draw_hidden + static_cast<int64_t>(pl.batch + b) * D);
+    for (int64_t e = tid; e < D / 8; e += kFinishThreads) {
+        dst_t[e] = src_t[e];
+        dst_d[e] = src_d[e];
     }
 }
 
 // Sampling, per sequence: the draw at the first rejection r from
 // max(0, p_r - q_r), or after full acceptance from p_k, over the draw rows'
-// logits.  Each thread sums the weights of one contiguous range of tokens in
-// ascending order; the ranges' prefix finds the range holding u * total,
-// and that range's thread finds the token.
-__global__ __launch_bounds__(kFinishThreads) void k_lmhead_draw(LmPlan pl) {
-    __shared__ float sums[kFinishThreads];
-    __shared__ float excl[kFinishThreads];
+// logits, inverting the cumulative weight in ascending token order.  The
+// row is cut into segments of 1024 consecutive tokens (lane l of a
+// wavefront takes tokens l, l+64, ..., so every load is coalesced); a
+// segment's weight is a wavefront sum; the segments' running sum finds the
+// segment holding u * total, and one wavefront scans that segment in order.
+constexpr int kDrawThreads = 1024;
+constexpr int kDrawWaves = kDrawThreads / 64;
+constexpr int kDrawSeg = 1024;                                    // tokens per segment
+constexpr int kDrawMaxSegs = ((1 << 24) + kDrawSeg - 1) / kDrawSeg;  // V <= 2^24
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = half_wave_sum(v);
+    return v + __shfl_xor(v, 32);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_prefix(float v) {
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+        const float o = __shfl_up(v, sh);
+        if ((threadIdx.x & 63) >= sh) v += o;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kDrawThreads) void k_lmhead_draw(LmPlan pl) {
+    __shared__ float seg_sum[kDrawMaxSegs];
     __shared__ float s_total;
-    __shared__ int s_first, s_last;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const LmSeqDraw d = pl.seq[b];
     const int k = pl.k;
     const int r = d.r;
@@ -567,61 +596,97 @@ __global__ __launch_bounds__(kFinishThreads) void k_lmhead_draw(LmPlan pl) {
     const int V = pl.vocab;
     const float* lt = pl.logits + static_cast<int64_t>(b) * V;
     const float* ld = pl.logits + static_cast<int64_t>(pl.batch + b) * V;
-    const int span = (V + kFinishThreads - 1) / kFinishThreads;
-    const int y0 = min(V, tid * span), y1 = min(V, y0 + span);
     const float c2 = pl.c2;
+    const float inv_zt = 1.f / d.zt, inv_zd = 1.f / d.zd;
+    const int nseg = (V + kDrawSeg - 1) / kDrawSeg;
     bool residual = r < k;
-    auto weight = [&](int y) {
-        const float pt = exp2f(lt[y] * c2 - d.mt) / d.zt;
-        if (!residual) return pt;
-        const float qd = exp2f(ld[y] * c2 - d.md) / d.zd;
-        return pt > qd ? pt - qd : 0.f;
+    constexpr int PER_LANE = kDrawSeg / 64;
+    // A segment's weights, lane l holding tokens l + 64 i (i < PER_LANE);
+    // every load of the segment is issued before any is used.
+    auto seg_weights = [&](int sg, float* w) {
+        float a[PER_LANE], c[PER_LANE];
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            const int y = min(sg * kDrawSeg + i * 64 + lane, V - 1);
+            a[i] = lt[y];
+            c[i] = residual ? ld[y] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            const bool in = sg * kDrawSeg + i * 64 + lane < V;
+            const float pt = exp2f(a[i] * c2 - d.mt) * inv_zt;
+            const float qd = residual ? exp2f(c[i] * c2 - d.md) * inv_zd : 0.f;
+            w[i] = in ? (pt > qd ? pt - qd : 0.f) : 0.f;
+        }
     };
-    float mine = 0.f;
     for (int pass = 0; pass < 2; ++pass) {
-        mine = 0.f;
-        for (int y = y0; y < y1; ++y) mine += weight(y);
-        sums[tid] = mine;
+        for (int sg = wave; sg < nseg; sg += kDrawWaves) {
+            float w[PER_LANE];
+            seg_weights(sg, w);
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) acc += w[i];
+            acc = wave_sum(acc);
+            if (lane == 0) seg_sum[sg] = acc;
+        }
         __syncthreads();
-        if (tid == 0) {
+        if (wave == 0) {
+            // the running sum over the segments in ascending order, 64 at a time
             float c = 0.f;
-            for (int t = 0; t < kFinishThreads; ++t) {
-                excl[t] = c;
-                c += sums[t];
+            for (int c0 = 0; c0 < nseg; c0 += 64) {
+                const float pre = wave_prefix(c0 + lane < nseg ? seg_sum[c0 + lane] : 0.f);
+                c += __shfl(pre, 63);
             }
-            s_total = c;
-            s_first = INT_MAX;
-            s_last = -1;
+            if (lane == 0) s_total = c;
         }
         __syncthreads();
         const bool retry = residual && !(s_total > 0.f);
-        __syncthreads();  // every thread has read s_total before a second pass rewrites it
+        __syncthreads();  // every thread has read s_total (and wave 0 seg_sum) before a second pass
         if (!retry) break;
         residual = false;  // an all-zero residual (p_r == q_r): draw from p_r
     }
+    if (wave != 0) return;
     const float theta = pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k] * s_total;
-    // The first range (ascending tokens) whose inclusive prefix exceeds
-    // theta; if rounding leaves none, the last range with any weight.
-    if (mine > 0.f) {
-        if (excl[tid] + mine > theta) atomicMin(&s_first, tid);
-        atomicMax(&s_last, tid);
-    }
-    __syncthreads();
-    const int pick = s_first != INT_MAX ? s_first : max(s_last, 0);
-    if (tid != pick) return;
-    float c = excl[tid];
-    int ystar = -1, last_pos = -1;
-    for (int y = y0; y < y1; ++y) {
-        const float w = weight(y);
-        if (w > 0.f) last_pos = y;
-        c += w;
-        if (c > theta) {
-            ystar = y;
-            break;
+    // The first segment whose inclusive running sum exceeds theta, and the
+    // running sum before it (the same operations as the total's).
+    int sg = -1;
+    float base = 0.f;
+    {
+        float c = 0.f;
+        for (int c0 = 0; c0 < nseg && sg < 0; c0 += 64) {
+            const float v = c0 + lane < nseg ? seg_sum[c0 + lane] : 0.f;
+            const float pre = wave_prefix(v);
+            const uint64_t crossed = __ballot(v > 0.f && c + pre > theta);
+            if (crossed) {
+                const int L = __builtin_ctzll(crossed);
+                const float before = __shfl(pre, L > 0 ? L - 1 : 0);
+                sg = c0 + L;
+                base = L > 0 ? c + before : c;
+            }
+            c += __shfl(pre, 63);
         }
     }
-    if (ystar < 0) ystar = last_pos >= 0 ? last_pos : max(y0, min(y1, V) - 1);
-    pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + r] = ystar;
+    if (sg < 0) {
+        // rounding left theta at or past the total: the last segment with
+        // weight, whose last positive token is taken
+        sg = nseg - 1;
+        while (sg > 0 && !(seg_sum[sg] > 0.f)) --sg;
+        base = -__builtin_inff();
+    }
+    int ystar = -1, last_pos = -1;
+    float c = base;
+    float w[PER_LANE];
+    seg_weights(sg, w);
+    for (int i = 0; i < PER_LANE && ystar < 0; ++i) {
+        const float pre = wave_prefix(w[i]);
+        const uint64_t crossed = __ballot(w[i] > 0.f && c + pre > theta);
+        const uint64_t pos = __ballot(w[i] > 0.f);
+        if (pos) last_pos = sg * kDrawSeg + i * 64 + 63 - __builtin_clzll(pos);
+        if (crossed) ystar = sg * kDrawSeg + i * 64 + __builtin_ctzll(crossed);
+        c += __shfl(pre, 63);
+    }
+    if (ystar < 0) ystar = last_pos >= 0 ? last_pos : min(V - 1, sg * kDrawSeg);
+    if (lane == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + r] = ystar;
 }
 
 }  // namespace
@@ -677,7 +742,7 @@ hipError_t launch_lmhead_sample(const LmPlan& stats, const LmPlan& draw, hipStre
     if (e != hipSuccess) return e;
     e = launch_gemm<kLmStore>(draw, stream, nullptr, nullptr);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lmhead_draw, dim3(static_cast<unsigned>(draw.batch)), dim3(kFinishThreads), 0, stream, draw);
+    hipLaunchKernelGGL(k_lmhead_draw, dim3(static_cast<unsigned>(draw.batch)), dim3(kDrawThreads), 0, stream, draw);
     return hipGetLastError();
 }
 
