@@ -33,12 +33,15 @@ steady clocks; with a few warm-up calls the first timed calls run slower.
 
 times greedy verification with the target's logits formed inside the call
 from its hidden states and output layer (sv_verify_lm_head_greedy: the
-k_lmhead_argmax GEMM with its argmax epilogue, then the per-sequence
-finisher), B(k+1) hidden states of size D=4096 against a [151936][4096] bf16
-output layer.  value = verified draft positions per second; roofline: the
-GEMM's 2 B(k+1) V D flops per launch / its mean duration (HIP events recorded
+GEMM with its argmax epilogue, then the per-sequence finisher), B(k+1)
+hidden states of size D=4096 against a [151936][4096] bf16 output layer.
+value = verified draft positions per second; roofline: the GEMM's
+2 B(k+1) V D flops per launch / its mean duration (HIP events recorded
 around every GEMM launch on the launch stream) against the bf16 dense MFMA
-peak.
+peak.  --workload lmhead_sample_selfdraft|lmhead_sample_grpo does the same
+for sampling verification (sv_verify_lm_head, T > 0): the GEMM timed is the
+statistics pass over the B(k+1) target and B k draft rows; the step also
+holds the decision, the draw rows' GEMM and the draws.
 
     python bench.py --copy-probe [--steps K]
 
@@ -180,14 +183,19 @@ def lm_cpu_baseline(cfg, wl, seconds: float):
     t0 = time.perf_counter()
     while True:
         b = done % cfg.B
-        oracle.lm_head_greedy(wl.hidden[b:b + 1], wl.weight, wl.tokens[b:b + 1])
+        if cfg.T > 0:
+            oracle.lm_head_verify(wl.target_hidden[b:b + 1], wl.target_weight, wl.draft_hidden[b:b + 1],
+                                  wl.draft_weight, wl.tokens[b:b + 1], wl.uniforms[b:b + 1], cfg.T)
+        else:
+            oracle.lm_head_greedy(wl.hidden[b:b + 1], wl.weight, wl.tokens[b:b + 1])
         done += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
     return {"value": done * cfg.k / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
             "sample": "%d whole sequences (%d positions, %d logits of dimension %d each) of the %s workload, fp64 C "
-                      "oracle, 1 thread, %.1f s" % (done, done * cfg.k, done * (cfg.k + 1) * cfg.V, cfg.D, cfg.name, dt),
+                      "oracle, 1 thread, %.1f s" % (done, done * cfg.k, done * (cfg.k + 1 + (cfg.k if cfg.T > 0 else 0))
+                                                    * cfg.V, cfg.D, cfg.name, dt),
             "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
 
 
@@ -199,13 +207,21 @@ def bench_lm_head(args) -> int:
 
     dev = torch.device("cuda:0")
     cfg = workloads.LM_CONFIGS[args.workload]
-    print("bench: generating %s (B=%d k=%d V=%d D=%d)" % (cfg.name, cfg.B, cfg.k, cfg.V, cfg.D), file=sys.stderr,
-          flush=True)
-    wl = workloads.generate_lm_head(cfg)
-    h, w, x = workloads.lm_head_to_device(wl, dev)
+    sample = cfg.T > 0
+    print("bench: generating %s (B=%d k=%d V=%d D=%d T=%g)" % (cfg.name, cfg.B, cfg.k, cfg.V, cfg.D, cfg.T),
+          file=sys.stderr, flush=True)
+    if sample:
+        wl = workloads.generate_lm_head_sample(cfg)
+        th, tw, dh, dw, x, u = workloads.lm_head_sample_to_device(wl, dev)
+        ver = sv.LmHeadSampler(th, tw, dh, dw, x, u, cfg.T)
+        tensors = (th, tw, dh, dw, x, u)
+    else:
+        wl = workloads.generate_lm_head(cfg)
+        h, w, x = workloads.lm_head_to_device(wl, dev)
+        ver = sv.LmHeadVerifier(h, w, x)
+        tensors = (h, w, x)
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev).cuda_stream
-    ver = sv.LmHeadVerifier(h, w, x)
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
     region = (ev.create(), ev.create())
     print("bench: %d warmup + %d timed steps" % (args.warmup, args.steps), file=sys.stderr, flush=True)
@@ -226,7 +242,8 @@ def bench_lm_head(args) -> int:
     for e in [e for p in pairs for e in p] + list(region):
         ev.destroy(e)
     acc = ver.accepted_len.float()
-    flops = cfg.flops()
+    # the GEMM the events bracket: target rows (and, sampling, draft rows)
+    flops = cfg.flops() + (2 * cfg.B * cfg.k * cfg.V * cfg.D if sample else 0)
     tflops = flops / (gemm_ms * 1e-3) / 1e12
     ms_per_step = elapsed * 1e3 / args.steps
     res = {
@@ -243,10 +260,12 @@ def bench_lm_head(args) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
-                   "hidden": cfg.D, "temperature": 0.0, "weights": "bf16", "accumulate": "f32"},
-        "roofline": {"bound": "mfma", "kernel": "k_lmhead_argmax", "achieved": tflops,
+                   "hidden": cfg.D, "temperature": cfg.T, "weights": "bf16", "accumulate": "f32",
+                   "draft_output_layer": "shared with the target" if sample else None},
+        "roofline": {"bound": "mfma", "kernel": "k_lmhead_gemm<stats>" if sample else "k_lmhead_gemm<argmax>",
+                     "achieved": tflops,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic("k_lmhead_argmax", args.workload, lm_kernel_source_hash()),
+                     "traffic": measured_traffic("k_lmhead_gemm", args.workload, lm_kernel_source_hash()),
                      "flops_per_launch": flops, "mean_launch_us": gemm_ms * 1e3,
                      "weight_bytes_per_launch": cfg.V * cfg.D * 2,
                      "hbm_floor_us": cfg.V * cfg.D * 2 / (HBM_PEAK_GBPS * 1e9) * 1e6},
@@ -254,7 +273,7 @@ def bench_lm_head(args) -> int:
         "mean_accepted_len": acc.mean().item(),
         "full_acceptance": int((acc == cfg.k).sum().item()),
     }
-    del ver, h, w, x
+    del ver, tensors
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
         res["cpu_baseline"] = lm_cpu_baseline(cfg, wl, args.cpu_seconds)
@@ -304,7 +323,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="selfdraft",
                     choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "vat_loss", "tiny",
-                             "lmhead_selfdraft", "lmhead_grpo"])
+                             "lmhead_selfdraft", "lmhead_grpo", "lmhead_sample_selfdraft", "lmhead_sample_grpo"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
