@@ -101,6 +101,10 @@ bool fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
                         pl->has_bonus, kWavesPerBlock * pl->nc_dec, kWavesPerBlock * pl->nc_bonus,
                         kWavesPerBlock * pl->nc_res, kResidentBlocks, &pl->grid))
         return false;
+    // The decisions of the sequences in the last residency of phase A come
+    // after the bonus phase has started; their bonus rows are read without
+    // waiting, so that reading them is not added to the end of the chain.
+    pl->eager_bonus_from = std::max(0, pl->batch - pl->grid.lag_a);
     pl->rows_t = s.rows_t;
     pl->rows_d = s.rows_d;
     pl->greedy = s.greedy;

@@ -469,6 +469,9 @@ struct TailShared {
 struct ResidW {
     float c2, mt, izt, md, izd;  // mt, md: row max * c2 (rounded); izt, izd: corr / Z
     __device__ __forceinline__ float operator()(float lt, float ld) const {
+        // p and q rounded on their own before the difference (no fused
+        // multiply-subtract): equal rows give exactly zero residual mass.
+#pragma clang fp contract(off)
         const float p = exp2_hw(fmaf(lt, c2, -mt)) * izt;
         const float q = exp2_hw(fmaf(ld, c2, -md)) * izd;
         return fmaxf(0.f, p - q);
@@ -1490,8 +1493,9 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
         }
         case kBonusWorker: {
             // The bonus row is read only when the sequence kept all k drafts
-            // (or when every row's statistics are asked for).
-            if (!pl.row_stats_out) {
+            // (or when every row's statistics are asked for), except for the
+            // last sequences, whose decisions come late: they read it at once.
+            if (!pl.row_stats_out && b < pl.eager_bonus_from) {
                 const uint64_t* dw = pl.dec + static_cast<int64_t>(b) * kDecWords + kDecRMode;
                 if (!collect(dw, 1, pl.tag, sh.stage, sh.vote)) return;
                 if (static_cast<int>(sh.stage[0] & 0xffffu) - 2 != pl.k) return;

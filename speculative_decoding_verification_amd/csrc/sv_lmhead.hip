@@ -611,11 +611,14 @@ __global__ __launch_bounds__(kDrawThreads) void k_lmhead_draw(LmPlan pl) {
             a[i] = lt[y];
             c[i] = residual ? ld[y] : 0.f;
         }
+        // p and q rounded on their own before the difference (no fused
+        // multiply-subtract): equal rows give exactly zero residual weight.
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i) {
+#pragma clang fp contract(off)
             const bool in = sg * kDrawSeg + i * 64 + lane < V;
-            const float pt = exp2f(a[i] * c2 - d.mt) * inv_zt;
-            const float qd = residual ? exp2f(c[i] * c2 - d.md) * inv_zd : 0.f;
+            const float pt = exp2f(fmaf(a[i], c2, -d.mt)) * inv_zt;
+            const float qd = residual ? exp2f(fmaf(c[i], c2, -d.md)) * inv_zd : 0.f;
             w[i] = in ? (pt > qd ? pt - qd : 0.f) : 0.f;
         }
     };

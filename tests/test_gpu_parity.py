@@ -170,6 +170,39 @@ def test_neg_inf_logits_and_greedy_ties(dev):
     assert not np.any(((outs >= 4096) & (outs < 6000)) | (outs >= 7000))
 
 
+@pytest.mark.parametrize("V,dtype", [(5000, "bf16"), (1001, "bf16"), (3000, "f32"), (151936, "bf16")])
+def test_rejection_with_zero_residual_draws_from_target(dev, V, dtype):
+    """Draft rows equal to the target rows and a draft token at a -inf logit:
+    p(x) = q(x) = 0 rejects, and max(0, p - q) is zero everywhere, so the
+    token comes from p_r (the degenerate-residual reading).  The kernel must
+    round p and q on their own before the difference for the residual to be
+    exactly zero.  V = 1001 bf16 rows are not 16-byte aligned (scalar loads);
+    V = 151936 spans 38 chunks."""
+    rng = np.random.default_rng(78)
+    B, k = 10, 4
+    t = (3.0 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+    dead = np.arange(V // 3, V // 3 + max(V // 50, 4))
+    t[:, :, dead] = -np.inf
+    if dtype == "bf16":
+        bits = workloads.round_to_bf16_bits(t)
+        t_in, d_in = bits, bits[:, :k].copy()
+        tf = workloads.bf16_bits_to_f32(bits)
+    else:
+        t_in, d_in = t, t[:, :k].copy()
+        tf = t
+    g = np.argmax(tf, axis=2)
+    r = rng.integers(0, k, B)
+    x = g[:, :k].astype(np.int32).copy()
+    x[np.arange(B), r] = rng.choice(dead, B)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    cfg = _custom(B, k, V, dtype, 1.0)
+    wl = workloads.Workload(cfg, 0, t_in, d_in, x, u)
+    gpu, _ = _verify_case(wl, dev)
+    assert np.array_equal(gpu["accepted_len"], r)
+    outs = gpu["out_tokens"][np.arange(B), r]
+    assert not np.any(np.isin(outs, dead))
+
+
 def test_invalid_tokens_flag_sequence(dev):
     cfg = _custom(6, 3, 2000, "f32", 1.0)
     wl = workloads.generate(cfg)
