@@ -40,8 +40,8 @@ value = verified draft positions per second; roofline: the GEMM's
 around every GEMM launch on the launch stream) against the bf16 dense MFMA
 peak.  --workload lmhead_sample_selfdraft|lmhead_sample_grpo does the same
 for sampling verification (sv_verify_lm_head, T > 0): the GEMM timed is the
-statistics pass over the B(k+1) target and B k draft rows; the step also
-holds the decision, the draw rows' GEMM and the draws.
+statistics pass over the B(k+1) target and B k draft rows (which also stores
+every row's fp32 logits); the step also holds the decisions and the draws.
 
     python bench.py --copy-probe [--steps K]
 

@@ -346,7 +346,8 @@ sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidd
                                    hipStream_t stream);
 
 /* Workspace bytes sv_verify_lm_head needs for `desc`: about
- * 8 B (2k+1) ceil(V/256) + 8 B V per sequence.  Errors: SV_ERR_NULL_ARG,
+ * (2k+1) (8 B ceil(V/256) + 4 B V) per sequence (every row's fp32 logits
+ * dominate: 856 MB at B = 128, k = 5, V = 151936).  Errors: SV_ERR_NULL_ARG,
  * SV_ERR_BAD_SHAPE, SV_ERR_BAD_TEMPERATURE. */
 sv_status sv_lm_head_sample_workspace_size(const sv_lm_head_sample_desc* desc, size_t* bytes);
 
@@ -359,10 +360,11 @@ sv_status sv_lm_head_sample_workspace_size(const sv_lm_head_sample_desc* desc, s
  * first rejection from max(0, p_r - q_r) renormalised, or from p_k after full
  * acceptance, with u[b][k], inverting the cumulative weight in ascending
  * token order).  Logits: l(y) = h . w_y, bf16 inputs, fp32 accumulation.  The
- * softmax statistics of every row come from one pass over both output layers
- * (the [B][k+1][V] and [B][k][V] logits are never stored); the draw then
- * recomputes only the rows it needs (one target row and one draft row per
- * sequence) and stores those in the workspace.
+ * softmax statistics of every row come from one pass over both output layers,
+ * whose epilogue also writes every row's fp32 logits into the workspace
+ * (the GEMM is bound by the matrix cores, so the writes cost little memory
+ * time); the draw then reads its two rows (target row r, or k, and draft
+ * row r) from there instead of forming them again.
  *
  *  target_hidden  device, [B][k+1][D] bf16, 16-byte aligned
  *  target_weight  device, [V][D] bf16, 16-byte aligned

@@ -155,12 +155,11 @@ size_t lm_greedy_workspace_bytes(const LmShape& s) {
 }
 
 struct LmSampleLayout {
-    size_t part_m, part_s, lx, seq, draw_hidden, logits, total;
+    size_t part_m, part_s, lx, seq, logits, total;
 };
 
 // Sampling: (m, s) partials per target and draft row and tile, the token
-// logits, the per-sequence draw records, the draw rows' hidden states and
-// their logits.
+// logits, the per-sequence draw records and every row's fp32 logits.
 LmSampleLayout lm_sample_layout(const LmShape& s) {
     LmSampleLayout L;
     const size_t rows = static_cast<size_t>(s.rows_t + s.rows_d);
@@ -174,10 +173,8 @@ LmSampleLayout lm_sample_layout(const LmShape& s) {
     off = align_up(off + rows * sizeof(float));
     L.seq = off;
     off = align_up(off + static_cast<size_t>(s.batch) * sizeof(LmSeqDraw));
-    L.draw_hidden = off;
-    off = align_up(off + 2 * static_cast<size_t>(s.batch) * static_cast<size_t>(s.hidden) * sizeof(uint16_t));
     L.logits = off;
-    off = align_up(off + 2 * static_cast<size_t>(s.batch) * static_cast<size_t>(s.vocab) * sizeof(float));
+    off = align_up(off + rows * static_cast<size_t>(s.vocab) * sizeof(float));
     L.total = off;
     return L;
 }
@@ -477,29 +474,12 @@ sv_status sv_verify_lm_head(const sv_lm_head_sample_desc* desc, const void* targ
     stats.seq = reinterpret_cast<sv::LmSeqDraw*>(base + L.seq);
     stats.logits = reinterpret_cast<float*>(base + L.logits);
     stats.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(desc->temperature));
-    stats.target_hidden = static_cast<const uint16_t*>(target_hidden);
-    stats.draft_hidden = static_cast<const uint16_t*>(draft_hidden);
-    stats.draw_hidden = reinterpret_cast<uint16_t*>(base + L.draw_hidden);
-    sv::LmPlan draw = stats;
     stats.g[0] = sv::lm_gemm(target_hidden, target_weight, s.rows_t, 0, sv::kLmTargetTokens);
     stats.g[1] = sv::lm_gemm(draft_hidden, draft_weight, s.rows_d, s.rows_t, sv::kLmDraftTokens);
     stats.n_gemms = 2;
     stats.mode = sv::kLmStats;
     sv::lmhead_layout(&stats);
-    // The draw rows: B target rows then B draft rows, one GEMM when both
-    // sides share the output layer.
-    if (draft_weight == target_weight) {
-        draw.g[0] = sv::lm_gemm(draw.draw_hidden, target_weight, 2 * s.batch, 0, sv::kLmNoTokens);
-        draw.n_gemms = 1;
-    } else {
-        draw.g[0] = sv::lm_gemm(draw.draw_hidden, target_weight, s.batch, 0, sv::kLmNoTokens);
-        draw.g[1] = sv::lm_gemm(draw.draw_hidden + s.batch * s.hidden, draft_weight, s.batch, s.batch,
-                                sv::kLmNoTokens);
-        draw.n_gemms = 2;
-    }
-    draw.mode = sv::kLmStore;
-    sv::lmhead_layout(&draw);
-    const hipError_t e = sv::launch_lmhead_sample(stats, draw, stream, desc->probe_start, desc->probe_stop);
+    const hipError_t e = sv::launch_lmhead_sample(stats, stream, desc->probe_start, desc->probe_stop);
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

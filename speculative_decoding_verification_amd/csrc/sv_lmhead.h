@@ -22,8 +22,8 @@ constexpr int kXcds = 8;          // accelerator complex dies of gfx950
 // What the GEMM's epilogue makes of a 256 x 256 tile of logits.
 enum LmMode : int32_t {
     kLmArgmax = 0,  // per row: (max, lowest index)
-    kLmStats = 1,   // per row: m = max l c2, s = sum 2^(l c2 - m); the logit of the row's token
-    kLmStore = 2    // the logits themselves, fp32
+    kLmStats = 1    // per row: m = max l c2, s = sum 2^(l c2 - m); the logit of the row's token; and the
+                    // logits themselves, fp32
 };
 
 // Which token's logit a statistics row captures.
@@ -68,10 +68,7 @@ struct LmPlan {
     float* part_s;                  // workspace [rows][n_parts]: statistics s (sampling)
     float* lx;                      // workspace [rows]: the logit of the row's token (sampling)
     LmSeqDraw* seq;                 // workspace [batch] (sampling)
-    float* logits;                  // workspace [2 batch][vocab]: target, then draft draw rows (sampling)
-    const uint16_t* target_hidden;  // [batch][k+1][hidden] (sampling: the decision step copies draw rows)
-    const uint16_t* draft_hidden;   // [batch][k][hidden]
-    uint16_t* draw_hidden;          // workspace [2 batch][hidden]: each sequence's target, then draft draw row
+    float* logits;                  // workspace [rows_t + rows_d][vocab], fp32 (sampling): every row's logits
     int32_t batch;
     int32_t k;
     int32_t vocab;
@@ -100,10 +97,8 @@ inline void lmhead_layout(LmPlan* pl) {
 hipError_t launch_lmhead_greedy(const LmPlan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 // Sampling verification: the statistics GEMM over target and draft rows
-// (bracketed by the events), the decision step, the logits GEMM over every
-// sequence's draw rows (copied by the decision step; `draw` holds those
-// GEMMs), then the draws.
-hipError_t launch_lmhead_sample(const LmPlan& stats, const LmPlan& draw, hipStream_t stream, hipEvent_t ev0,
-                                hipEvent_t ev1);
+// (bracketed by the events; it also stores every row's logits), the
+// decision step, then the draws from the stored rows.
+hipError_t launch_lmhead_sample(const LmPlan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace sv

@@ -3,8 +3,8 @@
 // What is computed: the acceptance rule of speculative sampling (NgramRL
 // essay "AI 开始抄自己的作业——而且抄得理直气壮", section "投机解码：让草稿先跑，
 // 考官殿后") with the target's and the draft's logits formed from their hidden
-// states and output-layer weights inside the call, l_i(y) = h_i . w_y, so that
-// the [B][k+1][V] logits are never stored.  Greedy (T == 0): the target's
+// states and output-layer weights inside the call, l_i(y) = h_i . w_y.
+// Greedy (T == 0) never stores the [B][k+1][V] logits: the target's
 // choice is its lowest-index argmax, a draft token is kept iff it equals it.
 // Sampling (T > 0): p = softmax(l_t / T), q = softmax(l_d / T); x_i is kept iff
 // u_i q_i(x_i) < p_i(x_i); at the first rejection r a token is drawn from
@@ -14,9 +14,11 @@
 //  k_lmhead_gemm<MODE>  a bf16 GEMM H . W^T on the matrix cores
 //                    (v_mfma_f32_32x32x16_bf16, fp32 accumulation) whose
 //                    epilogue reduces each 256 x 256 tile: per row (max,
-//                    lowest index) for greedy, per row the softmax statistics
-//                    (m, s) and the logit of the row's draft token for
-//                    sampling, or the fp32 logits of a few rows for the draws.
+//                    lowest index) for greedy; for sampling per row the
+//                    softmax statistics (m, s) and the logit of the row's
+//                    draft token, with the fp32 logits stored for the draws
+//                    (writes that fit in the memory bandwidth the
+//                    matrix-bound GEMM leaves idle).
 //                    One launch can hold two GEMMs (target rows against the
 //                    target's output layer, draft rows against the draft's).
 //                    Each of the 8 wavefronts computes a 128 x 64 block.  K
@@ -41,8 +43,9 @@
 //                    partials, p(x_i), q(x_i), the tests and the first
 //                    rejection; which rows the draw needs.
 //  k_lmhead_draw     sampling, per sequence: the draw from the residual (or
-//                    from p_k) over the draw rows' logits, by inverting the
-//                    cumulative weight in ascending token order.
+//                    from p_k) over the stored logits of target row r (or k)
+//                    and draft row r, by inverting the cumulative weight in
+//                    ascending token order.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -301,8 +304,14 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
 #undef LM_FRAGS
 
         // Epilogue: accumulator j of lane l holds row 8(j/4) + 4(l/32) + j%4
-        // of a 32 x 32 block, column l % 32.
-        if (MODE == kLmStore) {
+        // of a 32 x 32 block, column l % 32.  Statistics mode first stores
+        // the logits (each half-wave writes 128 contiguous bytes of a row,
+        // non-temporal: they are read once, by the draws, after the GEMM).
+        // The writes add about 8% to the GEMM (all workgroups write at the
+        // same time and the next tile's loads queue behind them); forming
+        // the draw rows again took a second GEMM of one row tile per
+        // vocabulary tile, which cost more.
+        if (MODE == kLmStats) {
 #pragma unroll
             for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
@@ -312,10 +321,9 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
 #pragma unroll
                     for (int ni = 0; ni < FN; ++ni) {
                         const int col = n0 + wn * kLmWaveN + ni * 32 + (lane & 31);
-                        if (m < g_rows && col < pl.vocab) out[col] = acc[mi][ni][j];
+                        if (m < g_rows && col < pl.vocab) __builtin_nontemporal_store(acc[mi][ni][j], out + col);
                     }
                 }
-            continue;
         }
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi) {
@@ -492,7 +500,6 @@ __global__ __launch_bounds__(kFinishThreads) void k_lmhead_decide(LmPlan pl) {
         }
     }
     __syncthreads();
-    __shared__ int s_r;
     if (wave == 0) {
         const bool active = lane < k;
         int x = 0;
@@ -537,21 +544,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_lmhead_decide(LmPlan pl) {
             d.zd = row_z[k + 1 + rd];
             d.pad[0] = d.pad[1] = d.pad[2] = 0;
             pl.seq[b] = d;
-            s_r = r;
         }
-    }
-    __syncthreads();
-    // The draw rows (target row r, or k after full acceptance; draft row r)
-    // go to the draw GEMM's input, 16 bytes per thread per step.
-    const int r = s_r;
-    const int64_t D = pl.hidden;
-    const uint4* src_t = reinterpret_cast<const uint4*>(pl.target_hidden + (static_cast<int64_t>(b) * (k + 1) + max(r, 0)) * D);
-    const uint4* src_d = reinterpret_cast<const uint4*>(pl.draft_hidden + (static_cast<int64_t>(b) * k + min(max(r, 0), k - 1)) * D);
-    uint4* dst_t = reinterpret_cast<uint4*>(pl.draw_hidden + static_cast<int64_t>(b) * D);
-    uint4* dst_d = reinterpret_cast<uint4*>(pl.draw_hidden + static_cast<int64_t>(pl.batch + b) * D);
-    for (int64_t e = tid; e < D / 8; e += kFinishThreads) {
-        dst_t[e] = src_t[e];
-        dst_d[e] = src_d[e];
     }
 }
 
@@ -594,8 +587,9 @@ __global__ __launch_bounds__(kDrawThreads) void k_lmhead_draw(LmPlan pl) {
     const int r = d.r;
     if (r < 0) return;  // invalid token: the decision step wrote -1 everywhere
     const int V = pl.vocab;
-    const float* lt = pl.logits + static_cast<int64_t>(b) * V;
-    const float* ld = pl.logits + static_cast<int64_t>(pl.batch + b) * V;
+    // target row r (k after full acceptance) and draft row r of the stored logits
+    const float* lt = pl.logits + (static_cast<int64_t>(b) * (k + 1) + r) * V;
+    const float* ld = pl.logits + (pl.rows_t + static_cast<int64_t>(b) * k + min(r, k - 1)) * V;
     const float c2 = pl.c2;
     const float inv_zt = 1.f / d.zt, inv_zd = 1.f / d.zd;
     const int nseg = (V + kDrawSeg - 1) / kDrawSeg;
@@ -735,17 +729,13 @@ hipError_t launch_lmhead_greedy(const LmPlan& pl, hipStream_t stream, hipEvent_t
     return hipGetLastError();
 }
 
-hipError_t launch_lmhead_sample(const LmPlan& stats, const LmPlan& draw, hipStream_t stream, hipEvent_t ev0,
-                                hipEvent_t ev1) {
-    hipError_t e = launch_gemm<kLmStats>(stats, stream, ev0, ev1);
+hipError_t launch_lmhead_sample(const LmPlan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    hipError_t e = launch_gemm<kLmStats>(pl, stream, ev0, ev1);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lmhead_decide, dim3(static_cast<unsigned>(stats.batch)), dim3(kFinishThreads), 0, stream,
-                       stats);
+    hipLaunchKernelGGL(k_lmhead_decide, dim3(static_cast<unsigned>(pl.batch)), dim3(kFinishThreads), 0, stream, pl);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_gemm<kLmStore>(draw, stream, nullptr, nullptr);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lmhead_draw, dim3(static_cast<unsigned>(draw.batch)), dim3(kDrawThreads), 0, stream, draw);
+    hipLaunchKernelGGL(k_lmhead_draw, dim3(static_cast<unsigned>(pl.batch)), dim3(kDrawThreads), 0, stream, pl);
     return hipGetLastError();
 }
 
