@@ -1064,6 +1064,60 @@ __device__ __forceinline__ float2 combine_row(const PartialSrc& src, int j, int 
     return make_float2(m, s);
 }
 
+// (m, Z) -- or (max, argmax) at T == 0 -- of local rows 0..n_rows-1 at once:
+// each row on the 16 lanes of one DPP row (16 rows per pass over the block),
+// a lane merging chunks sub, sub+16, ... in order, then four DPP steps inside
+// the row.  No readlane and no cross-row step, so all rows of a sequence are
+// combined in about the time one wave-wide merge takes.  Lane 0 of each row
+// writes mz[j].  Whole block.
+__device__ __forceinline__ void combine_rows(const PartialSrc& src, int n_rows, int P, bool greedy, float c2,
+                                             float2* mz) {
+    const int sub = threadIdx.x & 15;
+    for (int j0 = 0; j0 < n_rows; j0 += kBlock / 16) {
+        const int j = j0 + static_cast<int>(threadIdx.x / 16);
+        const bool on = j < n_rows;
+        if (greedy) {
+            float best = neg_inf();
+            int bi = INT_MAX;
+            if (on) {
+                for (int c = sub; c < P; c += 16) {
+                    const float2 pc = src.get(j * P + c);
+                    argmax_step(best, bi, pc.x, __float_as_int(pc.y));
+                }
+            }
+            argmax_step(best, bi, dpp<kDppQuadSwap1>(best, best), dpp_i<kDppQuadSwap1>(bi, bi));
+            argmax_step(best, bi, dpp<kDppQuadSwap2>(best, best), dpp_i<kDppQuadSwap2>(bi, bi));
+            argmax_step(best, bi, dpp<kDppRowRor4>(best, best), dpp_i<kDppRowRor4>(bi, bi));
+            argmax_step(best, bi, dpp<kDppRowRor8>(best, best), dpp_i<kDppRowRor8>(bi, bi));
+            if (on && sub == 0) mz[j] = make_float2(best, __int_as_float(bi));
+        } else {
+            float m = neg_inf(), s = 0.f;
+            if (on) {
+                for (int c = sub; c < P; c += 16) {
+                    const float2 pc = src.get(j * P + c);
+                    if (pc.x == neg_inf()) continue;
+                    if (pc.x > m) {
+                        s = (m == neg_inf() ? 0.f : s * exp2_hw((m - pc.x) * c2)) + pc.y;
+                        m = pc.x;
+                    } else {
+                        s += pc.y * exp2_hw((pc.x - m) * c2);
+                    }
+                }
+            }
+            float M = fmaxf(m, dpp<kDppQuadSwap1>(m, m));
+            M = fmaxf(M, dpp<kDppQuadSwap2>(M, M));
+            M = fmaxf(M, dpp<kDppRowRor4>(M, M));
+            M = fmaxf(M, dpp<kDppRowRor8>(M, M));
+            float t = m == neg_inf() ? 0.f : s * exp2_hw((m - M) * c2);
+            t += dpp<kDppQuadSwap1>(t, t);
+            t += dpp<kDppQuadSwap2>(t, t);
+            t += dpp<kDppRowRor4>(t, t);
+            t += dpp<kDppRowRor8>(t, t);
+            if (on && sub == 0) mz[j] = make_float2(M, t);
+        }
+    }
+}
+
 __device__ __forceinline__ void write_row_stats(const Plan& pl, int64_t grow, float2 res) {
     if (!pl.row_stats_out) return;
     pl.row_stats_out[2 * grow] = pl.greedy ? res.x : res.x / pl.temperature;
@@ -1117,14 +1171,10 @@ __device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShare
     }
     const PartialSrc src{staged ? sh.stage : nullptr, words};
 
-    for (int j = wave; j < pl.dec_rows; j += kWavesPerBlock) {
-        const float2 res = combine_row(src, j, P, pl.greedy, c2);
-        if (lane == 0) {
-            sh.mz[j] = res;
-            write_row_stats(pl, global_row(pl, b, j), res);
-        }
-    }
+    combine_rows(src, pl.dec_rows, P, pl.greedy, c2, sh.mz);
     __syncthreads();
+    if (pl.row_stats_out)
+        for (int j = threadIdx.x; j < pl.dec_rows; j += kBlock) write_row_stats(pl, global_row(pl, b, j), sh.mz[j]);
 
     if (wave == 0) {
         const int i = lane;
