@@ -91,8 +91,11 @@
  *    before first use; every call that returns SV_OK leaves it ready for the
  *    next call (each call tags what it writes with a fresh 32-bit call
  *    number, so nothing needs clearing; the numbers repeat only after 2^32 - 1
- *    calls in one process).  Calls that use the same workspace must not
- *    overlap in time.
+ *    calls in one process).  This holds for sv_verify, sv_vat_labels and
+ *    sv_vat_loss, which may share one workspace; a buffer that anything else
+ *    has written since (the LM-head entry points, which need no clearing,
+ *    included) must be zero-filled again before one of them uses it.  Calls
+ *    that use the same workspace must not overlap in time.
  *  - Determinism: results are bitwise reproducible for identical inputs (no
  *    floating-point atomics; fixed reduction orders).
  */

@@ -187,7 +187,11 @@ class _Workspace:
         return buf
 
 
+# sv_verify / sv_vat_labels / sv_vat_loss hand values between blocks through
+# tagged words and need a workspace that only they have written since it was
+# zero-filled; the LM-head entry points write plain data and get their own.
 _WS = _Workspace()
+_WS_LM = _Workspace()
 
 
 def _stream_handle(device) -> int:
@@ -451,7 +455,7 @@ class LmHeadVerifier:
         if st:
             raise SVError(st, "sv_lm_head_workspace_size", lib)
         if workspace is None:
-            workspace = _WS.get(device, nbytes.value)
+            workspace = _WS_LM.get(device, nbytes.value)
         elif workspace.numel() * workspace.element_size() < nbytes.value:
             raise ValueError("workspace too small: need %d bytes" % nbytes.value)
         self.accepted_len = torch.empty(B, dtype=torch.int32, device=device)
@@ -515,7 +519,7 @@ class LmHeadSampler:
         if st:
             raise SVError(st, "sv_lm_head_sample_workspace_size", lib)
         if workspace is None:
-            workspace = _WS.get(device, nbytes.value)
+            workspace = _WS_LM.get(device, nbytes.value)
         elif workspace.numel() * workspace.element_size() < nbytes.value:
             raise ValueError("workspace too small: need %d bytes" % nbytes.value)
         self.accepted_len = torch.empty(B, dtype=torch.int32, device=device)
