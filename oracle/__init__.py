@@ -75,6 +75,9 @@ def _load():
     lib.orc_vat_loss.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_double, c.c_double, c.c_double,
                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_vat_loss.restype = c.c_int
+    lib.orc_vat_loss_grad.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int32, c.c_double, c.c_double,
+                                      vp, vp, vp, vp, vp]
+    lib.orc_vat_loss_grad.restype = c.c_int
     lib.orc_lm_head_greedy.argtypes = [c.c_int64, c.c_int32, c.c_int64, c.c_int64, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_lm_head_greedy.restype = c.c_int
     lib.orc_lm_head_logits.argtypes = [c.c_int64, c.c_int64, c.c_int64, vp, vp, vp]
@@ -264,6 +267,25 @@ def vat_loss(target, draft, tokens, uniforms, hard_tokens, temperature: float, d
     if rc != 0:
         raise ValueError("orc_vat_loss rejected its arguments")
     return VatResult(accept_mask=mask, first_reject=fr, weights=w, soft=soft, hard=hard, block_loss=loss)
+
+
+def vat_loss_grad(target, draft, hard_tokens, weights, temperature: float, hard_weight: float = 1.0) -> np.ndarray:
+    """d(block loss)/d(draft logits), [N][k][V] fp64, with the weights (as
+    returned by vat_loss) held fixed: w_i/T ((1 + hard_weight) q - p - hard_weight e_h)."""
+    lib = _load()
+    t, dt = _logits_arg(target)
+    N, k, V = t.shape
+    d, dd = _logits_arg(draft)
+    assert dd == dt and d.shape == (N, k, V)
+    h = np.ascontiguousarray(hard_tokens, dtype=np.int32)
+    w = np.ascontiguousarray(weights, dtype=np.float64)
+    assert h.shape == (N, k) and w.shape == (N, k)
+    g = np.empty((N, k, V), np.float64)
+    rc = lib.orc_vat_loss_grad(N, k, V, dt, float(temperature), float(hard_weight), _ptr(t), _ptr(d), _ptr(h),
+                               _ptr(w), _ptr(g))
+    if rc != 0:
+        raise ValueError("orc_vat_loss_grad rejected its arguments")
+    return g
 
 
 class LmHeadResult:

@@ -72,6 +72,9 @@
  *    Natural logarithms (nats).  T must be > 0 (both distributions are
  *    needed).  A block with a draft or hard token outside [0,V) is flagged:
  *    first_reject -1, mask 0, weights 0, soft/hard/loss NaN.
+ *  - VAT loss gradient (orc_vat_loss_grad): the derivative of the block loss
+ *    with respect to the draft logits, the weights held fixed (they are the
+ *    labels of the simulated verification); derived from the definition above.
  */
 #include <math.h>
 #include <stdint.h>
@@ -502,6 +505,57 @@ int orc_vat_loss(int64_t N, int32_t k, int64_t V, int32_t dtype, double T, doubl
             total += weights[n * k + i] * (ce + hard_weight * hard[n * k + i]);
         }
         block_loss[n] = total;
+    }
+    free(lt); free(ld); free(p); free(q);
+    return 0;
+}
+
+/* Gradient of the VAT block loss of orc_vat_loss with respect to the draft
+ * logits [VAT2], the VAT weights held fixed (they are per-position labels of
+ * the simulated verification, not functions of the logits).  With
+ * q = softmax(l_d/T), p = softmax(l_t/T) and ln q(z) = l_d(z)/T - logsumexp:
+ *   d(-sum_z p(z) ln q(z)) / d l_d(y) = (q(y) - p(y)) / T,
+ *   d(-ln q(h)) / d l_d(y)             = (q(y) - [y == h]) / T,
+ * so grad[n][i][y] = w_i / T * ((1 + hard_weight) q(y) - p(y) - hard_weight [y == h_i]).
+ * Inputs: the logits as for orc_vat_loss, hard tokens [N][k], the weights
+ * [N][k] that orc_vat_loss returned.  A position of weight 0 (a flagged
+ * block, or decay 0 after the first rejection) has an all-zero row. */
+int orc_vat_loss_grad(int64_t N, int32_t k, int64_t V, int32_t dtype, double T, double hard_weight,
+                      const void* target, const void* draft, const int32_t* hard_tokens, const double* weights,
+                      double* grad) {
+    int64_t n, y;
+    int32_t i;
+    double *lt, *ld, *p, *q;
+    if (N < 0 || k < 1 || V < 1 || !(T > 0.0) || !(hard_weight == hard_weight)) return -1;
+    if (!target || !draft || !hard_tokens || !weights || !grad) return -1;
+    lt = (double*)malloc(sizeof(double) * V);
+    ld = (double*)malloc(sizeof(double) * V);
+    p = (double*)malloc(sizeof(double) * V);
+    q = (double*)malloc(sizeof(double) * V);
+    if (!lt || !ld || !p || !q) {
+        free(lt); free(ld); free(p); free(q);
+        return -1;
+    }
+    for (n = 0; n < N; ++n) {
+        for (i = 0; i < k; ++i) {
+            const int64_t row = n * k + i;
+            const double w = weights[row];
+            double* g = grad + row * V;
+            double mt, zt, md, zd, s;
+            int64_t h;
+            if (w == 0.0) {
+                for (y = 0; y < V; ++y) g[y] = 0.0;
+                continue;
+            }
+            h = hard_tokens[row];
+            load_row(target, dtype, row, V, lt);
+            load_row(draft, dtype, row, V, ld);
+            orc_softmax(lt, V, T, p, &mt, &zt);
+            orc_softmax(ld, V, T, q, &md, &zd);
+            s = w / T;
+            for (y = 0; y < V; ++y)
+                g[y] = s * ((1.0 + hard_weight) * q[y] - p[y] - (y == h ? hard_weight : 0.0));
+        }
     }
     free(lt); free(ld); free(p); free(q);
     return 0;

@@ -485,6 +485,52 @@ def test_vat_loss_labels_match_vat_labels_and_invalid_hard_token_flags(orc):
     assert np.all(np.isfinite(res.block_loss[keep]))
 
 
+def test_vat_loss_grad_matches_central_differences_of_the_block_loss(orc):
+    """The gradient against the block loss itself: a central difference of
+    orc.vat_loss on fp64 logits, one draft logit at a time, with the
+    acceptance outcome unchanged by the step (the weights are labels).  A
+    dropped term, a wrong sign, a missing 1/T or the hard term on the wrong
+    token fails this."""
+    rng = np.random.default_rng(56)
+    N, k, V, eps = 3, 4, 7, 1e-6
+    lt, ld, x, u, h = _pq_block(rng, N, k, V)
+    lt = lt.astype(np.float64)
+    ld = ld.astype(np.float64)
+    for T, lam, decay in ((1.0, 1.0, 0.8), (0.7, 0.5, 0.6), (1.6, 0.0, 0.8)):
+        base = orc.vat_loss(lt, ld, x, u, h, T, decay, lam)
+        g = orc.vat_loss_grad(lt, ld, h, base.weights, T, lam)
+        checked = 0
+        for n in range(N):
+            for i in range(k):
+                for y in range(V):
+                    lp, lm = ld.copy(), ld.copy()
+                    lp[n, i, y] += eps
+                    lm[n, i, y] -= eps
+                    a = orc.vat_loss(lt, lp, x, u, h, T, decay, lam)
+                    b = orc.vat_loss(lt, lm, x, u, h, T, decay, lam)
+                    if a.first_reject[n] != base.first_reject[n] or b.first_reject[n] != base.first_reject[n]:
+                        continue
+                    fd = (a.block_loss[n] - b.block_loss[n]) / (2 * eps)
+                    assert g[n, i, y] == pytest.approx(fd, abs=2e-8), (T, lam, n, i, y)
+                    checked += 1
+        assert checked > 0.9 * N * k * V
+
+
+def test_vat_loss_grad_rows_sum_to_zero_and_vanish_with_zero_weight(orc):
+    """Softmax gradients sum to zero over the vocabulary ((1 + lam) - 1 - lam);
+    positions of weight 0 (decay 0 after the first rejection, or a flagged
+    block) have all-zero rows."""
+    rng = np.random.default_rng(57)
+    lt, ld, x, u, h = _pq_block(rng, 6, 5, 300)
+    res = orc.vat_loss(lt, ld, x, u, h, 0.9, 0.0, 0.7)
+    g = orc.vat_loss_grad(lt, ld, h, res.weights, 0.9, 0.7)
+    assert np.allclose(g.sum(axis=2), 0.0, atol=1e-13)
+    zero = res.weights == 0.0
+    assert zero.any() and (~zero).any()
+    assert np.all(g[zero] == 0.0)
+    assert np.all(np.abs(g[~zero]).max(axis=1) > 0)
+
+
 # ----------------------------------------------------------------- LM-head greedy verification
 
 def _bf16_bits(a):
