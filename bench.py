@@ -3,9 +3,11 @@
     python bench.py [--steps K] [--warmup W] [--workload selfdraft] [--gpus 1]
 
 One step = one sv_verify call (sv_vat_labels for --workload vat, sv_vat_loss
-for --workload vat_loss) over one
+for --workload vat_loss, sv_vat_loss_grad for --workload vat_loss_grad: the
+gradient of the VAT loss with respect to the draft logits, kernel k_vat_grad,
+after one sv_vat_loss call outside the timed region) over one
 batch of synthetic logits already resident in HBM; the call is the whole path
-(one launch of the task-grid kernel k_verify).  The default workload is the
+(one launch of the task-grid kernel k_verify, or of k_vat_grad).  The default workload is the
 quantized-self-drafter batch: B=128 sequences, k=5 draft positions,
 V=151936, bf16 target and draft logits, T=1.  Prints ONE JSON line.
 
@@ -130,10 +132,11 @@ def measured_traffic(kernel: str, workload: str, source_hash=None):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, seconds: float, loss: bool = False):
+def cpu_baseline(cfg, seconds: float, loss: bool = False, grad: bool = False):
     """The oracle as it is (plain fp64 C, one thread) over whole sequences (VAT:
     blocks) of the same workload until `seconds` of CPU work have elapsed; the
-    sample is drawn on the host by the same seeded generator."""
+    sample is drawn on the host by the same seeded generator.  With `grad`, the
+    loss and then its gradient with respect to the draft logits."""
     import oracle
     import workloads
 
@@ -147,8 +150,10 @@ def cpu_baseline(cfg, seconds: float, loss: bool = False):
         hi = min(n_sample, lo + step)
         d = wl.draft[lo:hi] if wl.draft is not None else None
         if loss:
-            oracle.vat_loss(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], wl.hard_tokens[lo:hi],
-                            cfg.T, cfg.decay, 1.0)
+            r = oracle.vat_loss(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], wl.hard_tokens[lo:hi],
+                                cfg.T, cfg.decay, 1.0)
+            if grad:
+                oracle.vat_loss_grad(wl.target[lo:hi], d, wl.hard_tokens[lo:hi], r.weights, cfg.T, 1.0)
         elif cfg.kind == "vat":
             oracle.vat_labels(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, cfg.decay)
         else:
@@ -159,7 +164,7 @@ def cpu_baseline(cfg, seconds: float, loss: bool = False):
     dt = time.perf_counter() - t0
     what = "blocks" if cfg.kind == "vat" else "sequences"
     if loss:
-        what = "blocks (labels and loss)"
+        what = "blocks (labels, loss and its gradient)" if grad else "blocks (labels and loss)"
     return {"value": done * cfg.k / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
             "sample": "%d whole %s (%d positions; cycling over the first %d) of the %s workload, fp64 C oracle, "
                       "1 thread, %.1f s" % (done, what, done * cfg.k, n_sample, cfg.name, dt),
@@ -322,7 +327,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="selfdraft",
-                    choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "vat_loss", "tiny",
+                    choices=["selfdraft", "ngram_tail", "grpo", "grpo_greedy", "vat", "vat_loss", "vat_loss_grad", "tiny",
                              "lmhead_selfdraft", "lmhead_grpo", "lmhead_sample_selfdraft", "lmhead_sample_grpo"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -349,7 +354,8 @@ def main(argv=None):
     import workloads
 
     dev = torch.device("cuda:0")
-    loss = args.workload == "vat_loss"
+    grad = args.workload == "vat_loss_grad"
+    loss = args.workload in ("vat_loss", "vat_loss_grad")
     cfg = workloads.get_config("vat" if loss else args.workload)
     print("bench: generating %s (B=%d k=%d V=%d %s T=%g)" % (cfg.name, cfg.B, cfg.k, cfg.V, cfg.dtype, cfg.T),
           file=sys.stderr, flush=True)
@@ -368,7 +374,13 @@ def main(argv=None):
         del wl
     ev = HipEvents()
     n_launch = args.warmup + args.steps
-    calls = _launchers(cfg, sets, sv, len(sets), loss)
+    if grad:
+        # the gradient pass consumes what sv_vat_loss wrote for the same logits
+        t, d, x, u, h = sets[0]
+        pre = sv.VatLoss(t, d, x, u, h, cfg.T, cfg.decay, 1.0, return_row_stats=True)()
+        calls = [sv.VatLossGrad(t, d, h, pre.weights, pre.row_stats, cfg.T, 1.0)]
+    else:
+        calls = _launchers(cfg, sets, sv, len(sets), loss)
     stream = torch.cuda.current_stream(dev).cuda_stream
     region = (ev.create(), ev.create())
 
@@ -392,9 +404,16 @@ def main(argv=None):
     ms_per_step = elapsed * 1e3 / args.steps
     positions = cfg.positions() * args.steps
     value = positions / elapsed
-    kernel = "k_verify"
+    kernel = "k_vat_grad" if grad else "k_verify"
     last = calls[(n_launch - 1) % len(calls)]
-    if cfg.kind == "vat":
+    if grad:
+        rows = cfg.B * cfg.k
+        zero_rows = int((pre.weights == 0).sum().item())
+        # every row's gradient is written (fp32); rows of weight 0 read no logits
+        needed = rows * cfg.V * 4 + (rows - zero_rows) * cfg.V * 2 * cfg.elem_bytes
+        extra = {"mean_block_loss": pre.block_loss.float().mean().item(), "zero_weight_rows": zero_rows}
+        in_bytes = rows * cfg.V * (4 + 2 * cfg.elem_bytes)
+    elif cfg.kind == "vat":
         fr = last.first_reject.float()
         extra = {"mean_first_reject": fr.mean().item(), "timeouts": int((fr == -2).sum().item())}
         if loss:
@@ -456,7 +475,7 @@ def main(argv=None):
         res["config"]["hard_weight"] = 1.0
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, loss)
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, loss, grad)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -111,7 +111,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 5
+#define SV_ABI_VERSION 6
 #define SV_MAX_DRAFT 64 /* k is limited to one 64-lane wavefront */
 #define SV_MAX_DRAFT_CHOICES 8
 
@@ -305,6 +305,37 @@ sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, c
                       uint8_t* accept_mask, int32_t* first_reject, float* weights, float* soft_ce, float* hard_ce,
                       float* block_loss, float* probs_out, float* row_stats_out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Gradient of the VAT training loss with respect to the draft logits, for
+ * the backward pass of drafter training.  Source: VAT write-up, section
+ * "第二件事，改权重分配的锚点" (the weighted soft-plus-hard-label loss that
+ * sv_vat_loss computes); the derivative is taken with the VAT weights held
+ * fixed, as labels of the simulated verification:
+ *   grad[n][i][y] = w_i / T * ((1 + hard_weight) q_i(y) - p_i(y) - hard_weight [y == h_i]),
+ * p_i = softmax(l_t/T), q_i = softmax(l_d/T).  It consumes what sv_vat_loss
+ * wrote for the same logits and descriptor (its weights and row_stats_out).
+ *
+ *  desc           as for sv_vat_loss (decay unused here); probe events
+ *                 bracket the kernel
+ *  target_logits, draft_logits  device, [N][k][V] dtype
+ *  hard_tokens    device, [N][k] int32, as for sv_vat_loss
+ *  weights        device, [N][k] float32: the weights sv_vat_loss wrote
+ *  row_stats      device, [N k + N k][2] float32: sv_vat_loss's row_stats_out
+ *  grad           device out, [N][k][V] float32 (16-byte aligned with V a
+ *                 multiple of 4 for the vector path; any alignment works)
+ *  stream         HIP stream
+ *
+ * A position of weight 0 (a flagged block, or decay 0 after the first
+ * rejection) gets a row of zeros and its logits are not read.  One streaming
+ * kernel: reads both logit rows once and writes the gradient row once.
+ * Errors (nothing launched): SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE,
+ * SV_ERR_BAD_DTYPE, SV_ERR_BAD_TEMPERATURE (T == 0 included),
+ * SV_ERR_BAD_HARD_WEIGHT.  Launch failure: SV_ERR_HIP.
+ */
+sv_status sv_vat_loss_grad(const sv_vat_loss_desc* desc, const void* target_logits, const void* draft_logits,
+                           const int32_t* hard_tokens, const float* weights, const float* row_stats, float* grad,
+                           hipStream_t stream);
 
 /* Workspace bytes sv_verify_lm_head_greedy needs for `desc`.  Errors:
  * SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE. */

@@ -36,6 +36,7 @@ STATUS = {0: "SV_OK", 1: "SV_ERR_NULL_ARG", 2: "SV_ERR_BAD_SHAPE", 3: "SV_ERR_BA
 
 EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_size", "sv_verify",
                     "sv_vat_workspace_size", "sv_vat_labels", "sv_vat_loss_workspace_size", "sv_vat_loss",
+                    "sv_vat_loss_grad",
                     "sv_lm_head_workspace_size", "sv_verify_lm_head_greedy", "sv_lm_head_sample_workspace_size",
                     "sv_verify_lm_head", "sv_accept_histogram",
                     "sv_draft_len_init", "sv_draft_len_update")
@@ -122,6 +123,8 @@ def load_library():
     lib.sv_vat_loss_workspace_size.argtypes = [ctypes.POINTER(VatLossDesc), ctypes.POINTER(sz)]
     lib.sv_vat_loss.restype = ctypes.c_int
     lib.sv_vat_loss.argtypes = [ctypes.POINTER(VatLossDesc)] + [vp] * 14 + [sz, vp]
+    lib.sv_vat_loss_grad.restype = ctypes.c_int
+    lib.sv_vat_loss_grad.argtypes = [ctypes.POINTER(VatLossDesc)] + [vp] * 7
     lib.sv_lm_head_workspace_size.restype = ctypes.c_int
     lib.sv_lm_head_workspace_size.argtypes = [ctypes.POINTER(LmHeadDesc), ctypes.POINTER(sz)]
     lib.sv_verify_lm_head_greedy.restype = ctypes.c_int
@@ -422,6 +425,50 @@ def vat_loss(target, draft, draft_tokens, uniforms, hard_tokens, temperature: fl
     Labels, weights, the soft and hard terms per position and the weighted loss per block."""
     return VatLoss(target, draft, draft_tokens, uniforms, hard_tokens, temperature, decay, hard_weight,
                    return_probs=return_probs, return_row_stats=return_row_stats, workspace=workspace)()
+
+
+class VatLossGrad:
+    """A prepared sv_vat_loss_grad call: d(block loss)/d(draft logits), [N][k][V] float32, from the logits and
+    what sv_vat_loss wrote for them (weights, row statistics)."""
+
+    def __init__(self, target, draft, hard_tokens, weights, row_stats, temperature: float, hard_weight: float = 1.0,
+                 *, out=None, probe=None):
+        torch = _torch()
+        lib = load_library()
+        if target.dim() != 3:
+            raise ValueError("target must be [N][k][V]")
+        N, k, V = (int(s) for s in target.shape)
+        device = target.device
+        dt = _dtype_code(target)
+        _check_dev("target", target, device)
+        _check_dev("draft", draft, device, target.dtype, (N, k, V))
+        _check_dev("hard_tokens", hard_tokens, device, torch.int32, (N, k))
+        _check_dev("weights", weights, device, torch.float32, (N, k))
+        _check_dev("row_stats", row_stats, device, torch.float32, (2 * N * k, 2))
+        self.grad = out if out is not None else torch.empty((N, k, V), dtype=torch.float32, device=device)
+        _check_dev("out", self.grad, device, torch.float32, (N, k, V))
+        self.desc = VatLossDesc(N, k, V, dt, float(temperature), 0.0, float(hard_weight), None, None)
+        if probe is not None:
+            self.desc.probe_start, self.desc.probe_stop = probe
+        self._keep = (target, draft, hard_tokens, weights, row_stats)
+        self._lib = lib
+        self._device = device
+        self._args = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(hard_tokens), _ptr(weights),
+                      _ptr(row_stats), _ptr(self.grad))
+
+    def __call__(self, stream: Optional[int] = None):
+        s = _stream_handle(self._device) if stream is None else stream
+        st = self._lib.sv_vat_loss_grad(*self._args, s)
+        if st:
+            raise SVError(st, "sv_vat_loss_grad", self._lib)
+        return self.grad
+
+
+def vat_loss_grad(target, draft, hard_tokens, weights, row_stats, temperature: float, hard_weight: float = 1.0,
+                  *, out=None):
+    """sv_vat_loss_grad on torch tensors: the gradient of vat_loss's block losses with respect to the draft
+    logits, given the weights and row statistics vat_loss returned (return_row_stats=True)."""
+    return VatLossGrad(target, draft, hard_tokens, weights, row_stats, temperature, hard_weight, out=out)()
 
 
 class LmHeadOutput(NamedTuple):

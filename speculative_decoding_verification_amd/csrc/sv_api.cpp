@@ -392,6 +392,39 @@ sv_status sv_accept_histogram(const int32_t* accepted_len, int32_t batch, int32_
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+sv_status sv_vat_loss_grad(const sv_vat_loss_desc* desc, const void* target_logits, const void* draft_logits,
+                           const int32_t* hard_tokens, const float* weights, const float* row_stats, float* grad,
+                           hipStream_t stream) {
+    if (!desc) return SV_ERR_NULL_ARG;
+    sv::Shape s;
+    const sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
+                                         desc->temperature, true, &s);
+    if (st != SV_OK) return st;
+    if (s.greedy) return SV_ERR_BAD_TEMPERATURE;
+    if (!(desc->hard_weight >= 0.f && std::isfinite(desc->hard_weight))) return SV_ERR_BAD_HARD_WEIGHT;
+    if (s.batch == 0) return SV_OK;
+    if (!target_logits || !draft_logits || !hard_tokens || !weights || !row_stats || !grad) return SV_ERR_NULL_ARG;
+    sv::GradPlan g{};
+    g.target = target_logits;
+    g.draft = draft_logits;
+    g.hard = hard_tokens;
+    g.weights = weights;
+    g.row_stats = row_stats;
+    g.grad = grad;
+    g.rows = s.batch * s.k;
+    g.vocab = static_cast<int32_t>(s.vocab);
+    g.chunks = static_cast<int32_t>(s.chunks);
+    g.items = g.rows * s.chunks;
+    g.elem_bytes = s.elem_bytes;
+    g.vec = (s.vocab * s.elem_bytes) % 16 == 0 && s.vocab % 4 == 0 && sv::aligned16(target_logits) &&
+            sv::aligned16(draft_logits) && sv::aligned16(grad);
+    g.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(desc->temperature));
+    g.inv_t = static_cast<float>(1.0 / static_cast<double>(desc->temperature));
+    g.hard_weight = desc->hard_weight;
+    const hipError_t e = sv::launch_vat_grad(g, stream, desc->probe_start, desc->probe_stop);
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes) {
     if (!desc || !bytes) return SV_ERR_NULL_ARG;
     sv::LmShape s;

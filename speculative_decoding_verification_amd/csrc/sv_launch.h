@@ -147,4 +147,25 @@ hipError_t launch_path(const Plan& plan, hipStream_t stream, hipEvent_t probe_st
 // Histogram of accepted lengths into hist[0 .. k+3] (one block).
 hipError_t launch_accept_hist(const int32_t* acc, int32_t batch, int32_t k, int32_t* hist, hipStream_t stream);
 
+// The VAT loss gradient with respect to the draft logits (sv_vat_loss_grad).
+struct GradPlan {
+    const void* target;       // [rows][V] logits, elem_bytes each
+    const void* draft;        // [rows][V]
+    const int32_t* hard;      // [rows] hard tokens
+    const float* weights;     // [rows] VAT weights
+    const float* row_stats;   // [2 rows][2]: (m/T, Z), target rows then draft rows
+    float* grad;              // [rows][V] out
+    int64_t rows;             // N k
+    int64_t items;            // rows * chunks
+    int32_t vocab;
+    int32_t chunks;           // ceil(V / chunk)
+    int32_t elem_bytes;
+    bool vec;                 // 16-byte rows and pointers
+    float c2;                 // log2(e) / T
+    float inv_t;              // 1 / T
+    float hard_weight;
+};
+
+hipError_t launch_vat_grad(const GradPlan& g, hipStream_t stream, hipEvent_t probe_start, hipEvent_t probe_stop);
+
 }  // namespace sv

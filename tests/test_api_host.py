@@ -277,6 +277,37 @@ def test_vat_loss_null_args_and_workspace(lib):
     assert lib.sv_vat_loss(ctypes.byref(e), *([None] * 14), 0, None) == 0
 
 
+def _call_grad(lib, d, h, **over):
+    a = dict(target=h.target, draft=h.draft, hard=h.hard, w=h.w, stats=h.stats, grad=h.grad)
+    a.update(over)
+    return lib.sv_vat_loss_grad(ctypes.byref(d) if d is not None else None, h.p(a["target"]), h.p(a["draft"]),
+                                h.p(a["hard"]), h.p(a["w"]), h.p(a["stats"]), h.p(a["grad"]), None)
+
+
+class _GradBufs(_LossBufs):
+    def __init__(self, N=2, k=3, V=1000):
+        super().__init__(N, k, V)
+        self.stats = np.ones(4 * N * k, np.float32)
+        self.grad = np.full(N * k * V, 7, np.float32)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(hw=-0.5), 9), (dict(hw=float("nan")), 9), (dict(k=0), 2),
+    (dict(k=65), 2), (dict(dtype=5), 3),
+])
+def test_vat_loss_grad_rejects_bad_desc_and_null_args(lib, over, status):
+    h = _GradBufs()
+    assert _call_grad(lib, _loss_desc(**over), h) == status
+    assert np.all(h.grad == 7)
+    d = _loss_desc()
+    assert _call_grad(lib, None, h) == 1
+    for name in ("target", "draft", "hard", "w", "stats", "grad"):
+        assert _call_grad(lib, d, h, **{name: None}) == 1, name
+    assert np.all(h.grad == 7)
+    # the decay is not used by the gradient: any value is accepted
+    assert lib.sv_vat_loss_grad(ctypes.byref(_loss_desc(N=0, decay=5.0)), *([None] * 6), None) == 0
+
+
 def _lm_desc(B=2, k=3, V=1000, D=64):
     return sv.LmHeadDesc(B, k, V, D, None, None)
 

@@ -127,6 +127,85 @@ def test_vat_loss_invalid_hard_token_flags_block(dev):
     assert gpu["first_reject"][1] == -1 and gpu["first_reject"][3] == -1
 
 
+# ------------------------------------------------------------------ VAT loss gradient
+
+GRAD_RTOL = 2e-5
+
+
+def _softmax_rows(a, T):
+    from scipy import special
+
+    return special.softmax(np.asarray(a, np.float64) / T, axis=-1)
+
+
+def _logits_f64(a):
+    return workloads.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def _compare_grad(g, target, draft, hard, weights, T, hw):
+    """Element by element against the oracle's gradient for the GPU's own
+    weights (the gradient takes them as given), within GRAD_RTOL of the size
+    of the three terms w/T ((1 + hw) q, p, hw [y == h]) at each element."""
+    T = float(np.float32(T))
+    hw = float(np.float32(hw))
+    w = weights.astype(np.float64)
+    o = oracle.vat_loss_grad(target, draft, hard, w, T, hw)
+    p = _softmax_rows(_logits_f64(target), T)
+    q = _softmax_rows(_logits_f64(draft), T)
+    eh = np.zeros_like(p)
+    N, k, V = p.shape
+    np.put_along_axis(eh, np.clip(hard, 0, V - 1)[..., None].astype(np.int64), 1.0, axis=2)
+    scale = (np.abs(w) / T)[..., None] * ((1 + hw) * q + p + hw * eh)
+    err = np.abs(g.astype(np.float64) - o)
+    bad = err > GRAD_RTOL * scale + 1e-30
+    assert not bad.any(), (np.argwhere(bad)[:5], err[bad][:5], scale[bad][:5])
+    assert np.all(g[w == 0.0] == 0.0)
+    return float((err / np.maximum(scale, 1e-300)).max())
+
+
+@pytest.mark.parametrize("B,k,V,dtype,T,hw,decay", [
+    (12, 16, 128256, "f32", 1.0, 1.0, 0.8),    # the VAT block shape, 12 blocks
+    (6, 16, 151936, "bf16", 0.7, 0.5, 0.8),    # bf16 rows, ragged last chunk
+    (3, 5, 140000, "f32", 1.0, 2.0, 0.0),      # decay 0: zero rows after the first rejection
+    (20, 1, 3000, "f32", 1.3, 0.0, 0.8),       # k = 1, no hard term
+    (4, 7, 1001, "bf16", 1.0, 1.0, 0.8),       # rows not 16-byte aligned: scalar path
+    (3, 64, 2502, "f32", 0.9, 1.0, 0.8),       # k = 64, V not a multiple of 4: scalar path
+])
+def test_vat_loss_grad_reduced(dev, B, k, V, dtype, T, hw, decay):
+    import speculative_decoding_verification_amd as sv
+
+    cfg = workloads.Config("vatgrad", "vat", B, k, V, dtype, T, 4.0, 0.25, "sample", 779)
+    wl = workloads.generate(cfg)
+    _say("case vat loss grad B=%d k=%d V=%d %s T=%g hw=%g decay=%g" % (B, k, V, dtype, T, hw, decay))
+    t, d = to_torch(wl.target, dev), to_torch(wl.draft, dev)
+    h = to_torch(wl.hard_tokens, dev)
+    res = sv.vat_loss(t, d, to_torch(wl.tokens, dev), to_torch(wl.uniforms, dev), h, T, decay, hw,
+                      return_row_stats=True)
+    g = sv.vat_loss_grad(t, d, h, res.weights, res.row_stats, T, hw).cpu().numpy()
+    w = res.weights.cpu().numpy()
+    worst = _compare_grad(g, wl.target, wl.draft, wl.hard_tokens, w, T, hw)
+    assert np.allclose(g.astype(np.float64).sum(axis=2), 0.0, atol=1e-5 * max(1.0, float(np.abs(w).max()) / T))
+    _say("  grad parity ok, worst error / bound scale %.3g" % worst)
+
+
+def test_vat_loss_grad_flagged_block_is_zero(dev):
+    import speculative_decoding_verification_amd as sv
+
+    cfg = workloads.Config("vatgrad", "vat", 5, 6, 4000, "f32", 1.0, 4.0, 0.25, "sample", 780)
+    wl = workloads.generate(cfg)
+    hard = wl.hard_tokens.copy()
+    hard[2, 1] = cfg.V
+    _say("case vat loss grad with a flagged block")
+    t, d = to_torch(wl.target, dev), to_torch(wl.draft, dev)
+    h = to_torch(hard, dev)
+    res = sv.vat_loss(t, d, to_torch(wl.tokens, dev), to_torch(wl.uniforms, dev), h, 1.0, 0.8, 1.0,
+                      return_row_stats=True)
+    g = sv.vat_loss_grad(t, d, h, res.weights, res.row_stats, 1.0, 1.0).cpu().numpy()
+    assert res.first_reject.cpu().numpy()[2] == -1
+    assert np.all(g[2] == 0.0)
+    _compare_grad(g, wl.target, wl.draft, hard, res.weights.cpu().numpy(), 1.0, 1.0)
+
+
 def _custom(B, k, V, dtype, T, sigma_t=3.0, sigma_d=0.5, mode="sample", onehot=False, seed=900):
     return workloads.Config("custom", "verify", B, k, V, dtype, T, sigma_t, None if onehot else sigma_d,
                             mode if not onehot else "ngram", seed)
@@ -357,6 +436,34 @@ def test_full_vat_loss_sampled(dev):
            "hard_ce": res.hard_ce.cpu().numpy()[idx], "block_loss": loss[idx]}
     _say("  parity ok:", compare_vat_loss(gpu, orc, lab, cfg.k, cfg.decay, 1.0), "mean loss", loss.mean())
     del t, d, x, u, h, res
+    torch.cuda.empty_cache()
+
+
+def test_full_vat_loss_grad_sampled(dev):
+    """The gradient of the VAT workload's loss (N=2048, k=16, V=128256, fp32:
+    16.8 GB written): every row sums to zero, sampled blocks against the oracle."""
+    import speculative_decoding_verification_amd as sv
+    import torch
+
+    cfg = workloads.get_config("vat")
+    _say("case vat loss grad full N=2048 k=16 V=128256 f32 (device-generated)")
+    t, d, x, u = workloads.generate_on_device(cfg, dev)
+    h = workloads.hard_tokens_on_device(cfg, t, dev)
+    res = sv.vat_loss(t, d, x, u, h, cfg.T, cfg.decay, 1.0, return_row_stats=True)
+    g = sv.vat_loss_grad(t, d, h, res.weights, res.row_stats, cfg.T, 1.0)
+    rs = g.sum(dim=2, dtype=torch.float64)
+    torch.cuda.synchronize()
+    assert float(rs.abs().max()) < 1e-4
+    idx = np.random.default_rng(7).choice(cfg.B, 6, replace=False)
+    idx.sort()
+    ti = torch.as_tensor(idx, device=dev)
+    gs = g.index_select(0, ti).cpu().numpy()
+    tl, dl = t.index_select(0, ti).cpu().numpy(), d.index_select(0, ti).cpu().numpy()
+    hs = h.index_select(0, ti).cpu().numpy()
+    ws = res.weights.index_select(0, ti).cpu().numpy()
+    worst = _compare_grad(gs, tl, dl, hs, ws, cfg.T, 1.0)
+    _say("  grad parity ok on blocks", idx.tolist(), "worst error / bound scale %.3g" % worst)
+    del t, d, x, u, h, res, g, rs
     torch.cuda.empty_cache()
 
 
