@@ -37,6 +37,10 @@
 // Draws: block prefix scan over the chunk masses finds the chunk holding the
 // draw, then an LDS block scan of that one chunk finds the token.  No
 // floating-point atomics and fixed reduction orders: bitwise reproducible.
+//
+// Also here: k_vat_grad, the gradient of the VAT loss with respect to the
+// draft logits (one streaming pass over both rows, from the row statistics
+// the loss pass wrote), and k_accept_hist, the histogram of accepted lengths.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
