@@ -22,13 +22,16 @@
 //                    One launch can hold two GEMMs (target rows against the
 //                    target's output layer, draft rows against the draft's).
 //                    Each of the 8 wavefronts computes a 128 x 64 block.  K
-//                    is staged through two LDS buffers 64 at a time.  A slice
-//                    is four 16-deep MFMA groups; between the MFMAs of one
-//                    group the wavefront reads the next group's fragments,
-//                    writes the next slice (held in registers) to the other
-//                    buffer, or issues the global loads of the slice after it,
-//                    in a fixed interleave, so that the matrix pipe is not left
-//                    waiting behind a burst of memory instructions; one barrier
+//                    is staged 64 at a time through two LDS buffers, filled by
+//                    direct-to-LDS loads (global_load_lds_dwordx4: no staging
+//                    registers, no LDS-write instructions) into unpadded
+//                    128-byte rows whose 16-byte pieces are XOR-swizzled by
+//                    row, so fragment reads hit distinct banks.  A slice is
+//                    four 16-deep MFMA groups; between the MFMAs of one group
+//                    the wavefront reads the next group's fragments, or issues
+//                    the loads of the slice after next, in a fixed interleave,
+//                    so that the matrix pipe is not left waiting behind a
+//                    burst of memory instructions; one wait and one barrier
 //                    per slice, before the last group, whose MFMAs overlap the
 //                    reads of the next slice's first fragments.  The grid is
 //                    persistent, one workgroup per compute unit, each taking
@@ -63,7 +66,6 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kLmMaxRows = SV_MAX_DRAFT + 1;  // positions of one sequence
 
-constexpr int kLdsStride = kLmBK + 8;  // bf16 per staged row: 16 bytes of padding shift the banks row to row
 
 __device__ __forceinline__ float neg_inf_f() { return -__builtin_inff(); }
 
@@ -112,7 +114,6 @@ __device__ __forceinline__ float half_wave_sum(float v) {
     return v + __shfl_xor(v, 16);
 }
 
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // The token whose logit statistics row m captures (-1: none).
 __device__ __forceinline__ int row_token(const LmPlan& pl, int tokens, int m) {
@@ -134,12 +135,19 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
     constexpr int WAVES_N = kLmBN / kLmWaveN;
     static_assert(WAVES_M * WAVES_N * 64 == kLmThreads, "one wavefront per block of the tile");
     constexpr int ROWS_PER_PASS = kLmThreads / (kLmBK / 8);  // tile rows one pass of 16-byte pieces covers
-    constexpr int PA = kLmBM / ROWS_PER_PASS;                 // pieces per thread: A
+    constexpr int PA = kLmBM / ROWS_PER_PASS;                 // direct-to-LDS loads per wavefront and slice: A
     constexpr int PB = kLmBN / ROWS_PER_PASS;                 // and B
     static_assert(PA * ROWS_PER_PASS == kLmBM && PB * ROWS_PER_PASS == kLmBN, "whole passes");
+    static_assert(kLmBK == 64 && kLmThreads == 512, "a load of 64 lanes fills 8 rows of 8 pieces; 8 wavefronts");
     static_assert(kLmHiddenMultiple % kLmBK == 0, "whole K slices");
-    __shared__ __attribute__((aligned(16))) uint16_t sa[2][kLmBM * kLdsStride];
-    __shared__ __attribute__((aligned(16))) uint16_t sb[2][kLmBN * kLdsStride];
+    // two stages, each buffer its own array (so the compiler can tell a
+    // direct-to-LDS load into one from reads of the other); rows of 64 bf16
+    // (128 B) unpadded, 16-byte pieces XOR-swizzled by row: piece s of row r
+    // sits at slot s ^ (r & 7)
+    __shared__ __attribute__((aligned(16))) uint16_t sa0[kLmBM * kLmBK];
+    __shared__ __attribute__((aligned(16))) uint16_t sa1[kLmBM * kLmBK];
+    __shared__ __attribute__((aligned(16))) uint16_t sb0[kLmBN * kLmBK];
+    __shared__ __attribute__((aligned(16))) uint16_t sb1[kLmBN * kLmBK];
     __shared__ float cand_v[WAVES_N][kLmBM];  // argmax max, statistics m
     __shared__ int cand_i[WAVES_N][kLmBM];    // argmax index
     __shared__ float cand_s[WAVES_N][kLmBM];  // statistics s
@@ -158,14 +166,14 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
     // consecutive items per step.
     const int slot = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
 
-    // Piece q of a thread: tile row tid / 4 + ROWS_PER_PASS q, K segment
-    // tid % 4 (8 bf16 each).  Rows past the end of H or W are read as the
-    // last row (their results are never written or are masked out), so no
-    // load is guarded.
-    const int prow = tid / (kLmBK / 8);
-    const int pseg = tid % (kLmBK / 8);
-    uint16_t* const sa_st = &sa[0][prow * kLdsStride + pseg * 8];
-    uint16_t* const sb_st = &sb[0][prow * kLdsStride + pseg * 8];
+    // Rows past the end of H or W are read as the last row (their results
+    // are never written or are masked out), so no load is guarded.
+    //
+    // Direct-to-LDS piece q of a wavefront: 64 lanes write 1 KiB contiguous,
+    // tile rows (8q + wave) * 8 + lane / 8, slot lane % 8, which holds the
+    // row's K piece (lane % 8) ^ (lane / 8).
+    const int drow = (lane >> 3);
+    const int dseg = (lane & 7) ^ (lane >> 3);
 
     for (int64_t item = slot; item < items; item += G) {
         // The GEMM this item belongs to (fields picked one by one: indexing
@@ -189,11 +197,12 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
         uint32_t a_off[PA], b_off[PB];
 #pragma unroll
         for (int q = 0; q < PA; ++q) {
-            const int m = min(m0 + prow + q * ROWS_PER_PASS, g_rows - 1);
-            a_off[q] = static_cast<uint32_t>(m * D + pseg * 8);
+            const int m = min(m0 + (q * 8 + wave) * 8 + drow, g_rows - 1);
+            a_off[q] = static_cast<uint32_t>(m * D + dseg * 8);
         }
 #pragma unroll
-        for (int q = 0; q < PB; ++q) b_off[q] = static_cast<uint32_t>(min(prow + q * ROWS_PER_PASS, b_last) * D + pseg * 8);
+        for (int q = 0; q < PB; ++q)
+            b_off[q] = static_cast<uint32_t>(min((q * 8 + wave) * 8 + drow, b_last) * D + dseg * 8);
         floatx16_t acc[FM][FN];
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
@@ -202,20 +211,32 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
 #pragma unroll
                 for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
 
-        uint4 ra[PA], rb[PB];
         static_assert(kLmBK == 64, "four 16-deep MFMA groups per slice");
         constexpr int NMF = FM * FN;     // MFMAs per group
         constexpr int NRD = FM + FN;     // fragment reads per group
         constexpr int NGL = PA + PB;     // global loads (and LDS writes) per slice
         static_assert(2 * NMF >= NRD && NMF >= NGL, "interleave slots");
         bf16x8_t f0a[FM], f0b[FN], f1a[FM], f1b[FN];
-#define LM_FRAGS(FA, FB, BUF, KS)                                                           \
+#define LM_FRAGS(FA, FB, SA, SB, KS)                                                        \
     {                                                                                       \
-        const int kcol_ = (KS) * 16 + 8 * (lane >> 5);                                      \
-        _Pragma("unroll") for (int mi = 0; mi < FM; ++mi)                                   \
-            FA[mi] = *reinterpret_cast<const bf16x8_t*>(&sa[BUF][(wm * kLmWaveM + mi * 32 + (lane & 31)) * kLdsStride + kcol_]); \
-        _Pragma("unroll") for (int ni = 0; ni < FN; ++ni)                                   \
-            FB[ni] = *reinterpret_cast<const bf16x8_t*>(&sb[BUF][(wn * kLmWaveN + ni * 32 + (lane & 31)) * kLdsStride + kcol_]); \
+        const int kp_ = (KS) * 2 + (lane >> 5);                                             \
+        _Pragma("unroll") for (int mi = 0; mi < FM; ++mi) {                                 \
+            const int r_ = wm * kLmWaveM + mi * 32 + (lane & 31);                           \
+            FA[mi] = *reinterpret_cast<const bf16x8_t*>(&SA[r_ * kLmBK + ((kp_ ^ (r_ & 7)) << 3)]); \
+        }                                                                                   \
+        _Pragma("unroll") for (int ni = 0; ni < FN; ++ni) {                                 \
+            const int r_ = wn * kLmWaveN + ni * 32 + (lane & 31);                           \
+            FB[ni] = *reinterpret_cast<const bf16x8_t*>(&SB[r_ * kLmBK + ((kp_ ^ (r_ & 7)) << 3)]); \
+        }                                                                                   \
+    }
+#define LM_DMA(SA, SB, K0)                                                                  \
+    {                                                                                       \
+        _Pragma("unroll") for (int q = 0; q < PA; ++q)                                      \
+            __builtin_amdgcn_global_load_lds((const void*)(a_base + (K0) + a_off[q]),       \
+                (__attribute__((address_space(3))) void*)(SA + (q * 8 + wave) * 512), 16, 0, 0); \
+        _Pragma("unroll") for (int q = 0; q < PB; ++q)                                      \
+            __builtin_amdgcn_global_load_lds((const void*)(b_base + (K0) + b_off[q]),       \
+                (__attribute__((address_space(3))) void*)(SB + (q * 8 + wave) * 512), 16, 0, 0); \
     }
 #define LM_MFMA(FA, FB)                                                                     \
     {                                                                                       \
@@ -223,7 +244,7 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
             _Pragma("unroll") for (int ni = 0; ni < FN; ++ni)                               \
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0); \
     }
-// After each MFMA of a group: up to two fragment reads (READS), one global load (LOADS), one LDS write (WRITES).
+// After each MFMA of a group: up to two fragment reads (READS), one direct-to-LDS load (LOADS), one LDS write (WRITES).
 #define LM_INTERLEAVE(READS, LOADS, WRITES)                                                 \
     {                                                                                       \
         _Pragma("unroll") for (int t = 0; t < NMF; ++t) {                                   \
@@ -235,73 +256,53 @@ __global__ __launch_bounds__(kLmThreads, kLmBlocksPerCu) void k_lmhead_gemm(LmPl
         }                                                                                   \
     }
 
-        // Pipeline over K slices with two LDS buffers: slice kb+1 is written
-        // to the other buffer during group 2 of step kb, a barrier follows,
-        // and group 3 reads the first fragments of slice kb+1 and issues the
-        // global loads of slice kb+2 while its MFMAs run.
-#pragma unroll
-        for (int q = 0; q < PA; ++q) ra[q] = ld16(a_base + a_off[q]);
-#pragma unroll
-        for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + b_off[q]);
+        // Two stages: the direct-to-LDS loads of slice kb+2 go out in group 3
+        // of slice kb, into the buffer slice kb has just finished with; one
+        // wait for this wavefront's loads and one barrier per slice.
         __syncthreads();  // the previous item's readers of the buffers and of cand are done
         if (MODE == kLmStats) {
             const int g_tok = g1 ? pl.g[1].tokens : pl.g[0].tokens;
             for (int r = tid; r < kLmBM; r += kLmThreads)
                 stok[r] = m0 + r < g_rows ? row_token(pl, g_tok, m0 + r) : -1;
         }
-#pragma unroll
-        for (int q = 0; q < PA; ++q) *reinterpret_cast<uint4*>(sa_st + q * ROWS_PER_PASS * kLdsStride) = ra[q];
-#pragma unroll
-        for (int q = 0; q < PB; ++q) *reinterpret_cast<uint4*>(sb_st + q * ROWS_PER_PASS * kLdsStride) = rb[q];
-        {
-            const int k1 = min(1, kblocks - 1) * kLmBK;
-#pragma unroll
-            for (int q = 0; q < PA; ++q) ra[q] = ld16(a_base + k1 + a_off[q]);
-#pragma unroll
-            for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + k1 + b_off[q]);
-        }
+        LM_DMA(sa0, sb0, 0);
+        LM_DMA(sa1, sb1, min(1, kblocks - 1) * kLmBK);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | NGL);  // vmcnt(NGL): slice 0 has landed
         __syncthreads();
-        LM_FRAGS(f0a, f0b, 0, 0);
-        for (int kb = 0; kb < kblocks; ++kb) {
-            const int cur = kb & 1;
-            const int nxt = cur ^ 1;
-            const int kload = min(kb + 2, kblocks - 1) * kLmBK;  // clamped: the last steps reload a slice nobody reads
-            __builtin_amdgcn_sched_barrier(0);
-            // group 0: reads of group 1
-            LM_FRAGS(f1a, f1b, cur, 1);
-            LM_MFMA(f0a, f0b);
-            LM_INTERLEAVE(true, false, false);
-            __builtin_amdgcn_sched_barrier(0);
-            // group 1: reads of group 2
-            LM_FRAGS(f0a, f0b, cur, 2);
-            LM_MFMA(f1a, f1b);
-            LM_INTERLEAVE(true, false, false);
-            __builtin_amdgcn_sched_barrier(0);
-            // group 2: reads of group 3, slice kb+1 (staged in registers) to the other buffer
-            LM_FRAGS(f1a, f1b, cur, 3);
-#pragma unroll
-            for (int q = 0; q < PA; ++q)
-                *reinterpret_cast<uint4*>(sa_st + (nxt * kLmBM + q * ROWS_PER_PASS) * kLdsStride) = ra[q];
-#pragma unroll
-            for (int q = 0; q < PB; ++q)
-                *reinterpret_cast<uint4*>(sb_st + (nxt * kLmBN + q * ROWS_PER_PASS) * kLdsStride) = rb[q];
-            LM_MFMA(f0a, f0b);
-            LM_INTERLEAVE(true, false, true);
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();  // slice kb+1 visible; every read of this buffer done
-            // group 3: first fragments of slice kb+1, global loads of slice kb+2
-            LM_FRAGS(f0a, f0b, nxt, 0);
-#pragma unroll
-            for (int q = 0; q < PA; ++q) ra[q] = ld16(a_base + kload + a_off[q]);
-#pragma unroll
-            for (int q = 0; q < PB; ++q) rb[q] = ld16(b_base + kload + b_off[q]);
-            LM_MFMA(f1a, f1b);
-            LM_INTERLEAVE(true, true, false);
+        LM_FRAGS(f0a, f0b, sa0, sb0, 0);
+#define LM_SLICE(CA, CB, NA, NB, KB)                                                        \
+    {                                                                                       \
+        const int kload_ = min((KB) + 2, kblocks - 1) * kLmBK;                              \
+        __builtin_amdgcn_sched_barrier(0);                                                  \
+        LM_FRAGS(f1a, f1b, CA, CB, 1);                                                      \
+        LM_MFMA(f0a, f0b);                                                                  \
+        LM_INTERLEAVE(true, false, false);                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                  \
+        LM_FRAGS(f0a, f0b, CA, CB, 2);                                                      \
+        LM_MFMA(f1a, f1b);                                                                  \
+        LM_INTERLEAVE(true, false, false);                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                  \
+        LM_FRAGS(f1a, f1b, CA, CB, 3);                                                      \
+        LM_MFMA(f0a, f0b);                                                                  \
+        LM_INTERLEAVE(true, false, false);                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                  \
+        __builtin_amdgcn_s_waitcnt(0x0F70);  /* vmcnt(0): slice KB+1 has landed */          \
+        __syncthreads();                                                                    \
+        LM_FRAGS(f0a, f0b, NA, NB, 0);                                                      \
+        LM_DMA(CA, CB, kload_);                                                             \
+        LM_MFMA(f1a, f1b);                                                                  \
+        LM_INTERLEAVE(true, true, false);                                                   \
+    }
+        for (int kb = 0; kb < kblocks; kb += 2) {
+            LM_SLICE(sa0, sb0, sa1, sb1, kb);
+            if (kb + 1 < kblocks) LM_SLICE(sa1, sb1, sa0, sb0, kb + 1);
         }
+#undef LM_SLICE
         __builtin_amdgcn_sched_barrier(0);
 #undef LM_INTERLEAVE
 #undef LM_MFMA
 #undef LM_FRAGS
+#undef LM_DMA
 
         // Epilogue: accumulator j of lane l holds row 8(j/4) + 4(l/32) + j%4
         // of a 32 x 32 block, column l % 32.  Statistics mode first stores
