@@ -176,17 +176,23 @@ def _check_dev(name, t, device, dtype=None, shape=None):
 
 
 class _Workspace:
-    """Per-device zero-filled workspace, grown on demand (the library allocates nothing)."""
+    """Zero-filled workspaces, one per (device, stream), grown on demand (the
+    library allocates nothing).  Calls on one stream run in order and may share
+    a workspace; calls on different streams may overlap, so each stream gets
+    its own.  The stream is the device's current stream when the call object
+    is built: an object built on one stream and called on another needs a
+    workspace of its own (the `workspace` argument)."""
 
     def __init__(self):
         self._buf = {}
 
     def get(self, device, nbytes: int):
         torch = _torch()
-        buf = self._buf.get(device)
+        key = (device, _stream_handle(device))
+        buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
             buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-            self._buf[device] = buf
+            self._buf[key] = buf
         return buf
 
 
@@ -278,6 +284,8 @@ def verify(target, draft, draft_tokens, uniforms, temperature: float, *, onehot:
     onehot or temperature == 0); draft_tokens [B][k] int32; uniforms [B][k+1]
     float32 (ignored at temperature 0).  Returns (accepted_len [B],
     out_tokens [B][k+1], probs [B][k][2] or None, row_stats or None).
+    Runs on the device's current stream; without `workspace`, each stream
+    gets a zero-filled workspace of its own.
     """
     return Verifier(target, draft, draft_tokens, uniforms, temperature, onehot=onehot, return_probs=return_probs,
                     return_row_stats=return_row_stats, workspace=workspace)()

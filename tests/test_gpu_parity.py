@@ -302,6 +302,38 @@ def test_determinism_bitwise(dev):
             assert np.array_equal(runs[0][key].view(np.uint8), r[key].view(np.uint8)), key
 
 
+def test_two_streams_in_flight_match_one_stream(dev):
+    """Calls on two streams at once, each with the workspace the binding keeps
+    for its stream, give the results of the same calls made one at a time."""
+    import speculative_decoding_verification_amd as sv
+    import torch
+
+    from parity import to_torch
+
+    cases = [workloads.generate(workloads.get_config("grpo").scaled(B=24)),
+             workloads.generate(_custom(40, 6, 20000, "bf16", 0.8, seed=901))]
+    args = []
+    for wl in cases:
+        args.append((to_torch(wl.target, dev), to_torch(wl.draft, dev), to_torch(wl.tokens, dev),
+                     to_torch(wl.uniforms, dev), wl.config.T))
+    ref = [sv.verify(*a, return_row_stats=True) for a in args]
+    ref = [(r.accepted_len.cpu().numpy(), r.out_tokens.cpu().numpy(), r.row_stats.cpu().numpy()) for r in ref]
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream(dev))
+    outs = [[], []]
+    for _ in range(4):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                outs[i].append(sv.verify(*args[i], return_row_stats=True))
+    torch.cuda.synchronize(dev)
+    for i in range(2):
+        for r in outs[i]:
+            assert np.array_equal(r.accepted_len.cpu().numpy(), ref[i][0])
+            assert np.array_equal(r.out_tokens.cpu().numpy(), ref[i][1])
+            assert np.array_equal(r.row_stats.cpu().numpy().view(np.uint32), ref[i][2].view(np.uint32))
+
+
 def test_gpu_losslessness_chi_square(dev):
     """The HIP sampler's outputs follow the target: V=8, k=3, 200k sequences."""
     from scipy import stats
