@@ -434,3 +434,19 @@ def test_lm_head_rows_times_hidden_limit(lib):
     # B (k+1) D >= 2^31 elements: hidden-state offsets would not fit 32 bits
     assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc(B=8192, k=63, V=1000, D=4096)), ctypes.byref(n)) == 2
     assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc(B=8191, k=63, V=1000, D=4096)), ctypes.byref(n)) == 0
+
+
+def test_missing_library_raises_and_package_has_no_fallback(monkeypatch, tmp_path):
+    """Without the built library the binding raises instead of computing
+    anything on the CPU, and no module of the package imports the oracle."""
+    monkeypatch.setattr(sv, "_lib", None)
+    monkeypatch.setattr(sv, "_LIB_PATH", str(tmp_path / "libspecverify.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        sv.load_library()
+    pkg = os.path.dirname(os.path.abspath(sv.__file__))
+    for dirpath, _, files in os.walk(pkg):
+        for name in files:
+            if name.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, name)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), name
+                assert "orc_" not in text, name
