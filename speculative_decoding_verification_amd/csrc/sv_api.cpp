@@ -94,7 +94,9 @@ bool fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
     pl->rows_per_seq = pl->dec_rows + (pl->has_bonus ? 1 : 0);
     pl->vat_loss = s.loss;
     pl->words_per_seq = static_cast<int32_t>(s.loss ? s.k * s.chunks * kPairWords : pl->rows_per_seq * s.chunks * 2);
-    pl->nc_dec = s.batch * pl->dec_rows * s.chunks <= kSmallCallChunks ? kChunksPerWaveSmall : kChunksPerWave;
+    const bool small = s.batch * pl->dec_rows * s.chunks <= kSmallCallChunks;
+    pl->nc_dec = small ? kChunksPerWaveSmall : kChunksPerWave;
+    pl->two_deep_polls = small;
     pl->nc_res = kChunksPerWaveResid;
     pl->nc_bonus = std::min(pl->nc_dec, kChunksPerWaveBonus);
     if (!plan_task_grid(pl->batch, static_cast<int64_t>(pl->dec_rows) * s.chunks, s.chunks, pl->has_resid,

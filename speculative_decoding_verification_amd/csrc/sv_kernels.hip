@@ -422,11 +422,57 @@ __device__ __forceinline__ void put_partial(uint64_t* seq_words, int i, float2 v
 // turns any other case into an error code instead of a hung kernel.
 constexpr uint64_t kPollTimeoutTicks = 1ull << 27;
 
+// Two-deep polls: each thread reads at most kPollPer of the words.
+constexpr int kPollPer = 6;
+
+__device__ __forceinline__ void poll_read(const uint64_t* words, int n, uint64_t (&w)[kPollPer]) {
+#pragma unroll
+    for (int j = 0; j < kPollPer; ++j) {
+        const int i = threadIdx.x + j * kBlock;
+        w[j] = i < n ? get_word(words + i) : 0ull;
+    }
+}
+
+// Whether one of this thread's words lacks the tag; stages the others' data.
+__device__ __forceinline__ bool poll_missing(int n, uint32_t tag, uint32_t* stage, const uint64_t (&w)[kPollPer]) {
+    bool missing = false;
+#pragma unroll
+    for (int j = 0; j < kPollPer; ++j) {
+        const int i = threadIdx.x + j * kBlock;
+        if (i < n) {
+            if (static_cast<uint32_t>(w[j] >> 32) != tag) missing = true;
+            else if (stage) stage[i] = word_data(w[j]);
+        }
+    }
+    return missing;
+}
+
 // Polls the n words at `words` until all carry `tag`; with `stage` (n <=
 // kStageWords) their data is left in stage[0..n).  Whole block (flags: the
 // block's LDS vote slots).  Returns false on timeout.
-__device__ __forceinline__ bool collect(const uint64_t* words, int n, uint32_t tag, uint32_t* stage, int* flags) {
+//
+// With `two_deep` (n <= kPollPer * kBlock) the next read of the words goes
+// out before the current one is checked and voted on, so a word is seen about
+// half a memory round trip sooner.  That pays when the whole grid is resident
+// at once; under a full stream the extra reads cost as much as they save, so
+// larger calls read once per round.
+__device__ __forceinline__ bool collect(const uint64_t* words, int n, uint32_t tag, uint32_t* stage, int* flags,
+                                        bool two_deep) {
     const uint64_t t0 = wall_clock64();
+    if (two_deep && n <= kPollPer * kBlock) {
+        uint64_t wa[kPollPer], wb[kPollPer];
+        poll_read(words, n, wa);
+        for (;;) {
+            __builtin_amdgcn_s_sleep(4);
+            poll_read(words, n, wb);
+            if (!block_any(poll_missing(n, tag, stage, wa), flags)) return true;
+            if (block_any(wall_clock64() - t0 > kPollTimeoutTicks, flags)) return false;
+            __builtin_amdgcn_s_sleep(4);
+            poll_read(words, n, wa);
+            if (!block_any(poll_missing(n, tag, stage, wb), flags)) return true;
+            if (block_any(wall_clock64() - t0 > kPollTimeoutTicks, flags)) return false;
+        }
+    }
     for (;;) {
         bool missing = false;
         for (int i = threadIdx.x; i < n; i += kBlock) {
@@ -1163,7 +1209,7 @@ __device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShare
     const float u_draw = sampling ? pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k] : 0.f;
 
     const bool staged = 2 * dec_items <= kStageWords;
-    if (!collect(words, 2 * dec_items, pl.tag, staged ? sh.stage : nullptr, sh.vote)) {
+    if (!collect(words, 2 * dec_items, pl.tag, staged ? sh.stage : nullptr, sh.vote, pl.two_deep_polls)) {
         fail_sequence(pl, b);
         if (!pl.vat && threadIdx.x == 0) {
             Decision d{};
@@ -1274,7 +1320,7 @@ __device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShare
 // Residual worker `w` of sequence b: mass of one chunk of max(0, p_r - q_r).
 template <int EB, bool VEC>
 __device__ __forceinline__ void residual_worker(const Plan& pl, int b, int w, TailShared& sh) {
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote)) return;
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls)) return;
     const Decision dc = read_decision(sh.stage);
     if (dc.mode != kModeResidual) return;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1303,13 +1349,13 @@ __device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailSha
     const int64_t V = pl.vocab;
     uint64_t* rwords = pl.resid + static_cast<int64_t>(b) * P;
     const bool staged = P + kDecWords <= kStageWords;
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote)) {
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls)) {
         fail_sequence(pl, b);
         return;
     }
     const Decision dc = read_decision(sh.stage);
     if (dc.mode != kModeResidual) return;
-    if (!collect(rwords, P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote)) {
+    if (!collect(rwords, P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote, pl.two_deep_polls)) {
         fail_sequence(pl, b);
         return;
     }
@@ -1346,7 +1392,7 @@ __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared
     const float c2 = pl.c2;
     const uint64_t* words = seq_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * P * 2;
     const bool staged = 2 * P + kDecWords <= kStageWords;
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote)) {
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls)) {
         fail_sequence(pl, b);
         return;
     }
@@ -1354,7 +1400,7 @@ __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared
     // Without full acceptance the bonus row was not read (unless every row's
     // statistics are asked for): nothing to do.
     if (dc.r != k && !pl.row_stats_out) return;
-    if (!collect(words, 2 * P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote)) {
+    if (!collect(words, 2 * P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote, pl.two_deep_polls)) {
         fail_sequence(pl, b);
         return;
     }
@@ -1551,7 +1597,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
             // last sequences, whose decisions come late: they read it at once.
             if (!pl.row_stats_out && b < pl.eager_bonus_from) {
                 const uint64_t* dw = pl.dec + static_cast<int64_t>(b) * kDecWords + kDecRMode;
-                if (!collect(dw, 1, pl.tag, sh.stage, sh.vote)) return;
+                if (!collect(dw, 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls)) return;
                 if (static_cast<int>(sh.stage[0] & 0xffffu) - 2 != pl.k) return;
             }
             const int base = role.index * kWavesPerBlock * pl.nc_bonus + static_cast<int>(threadIdx.x / kWave);

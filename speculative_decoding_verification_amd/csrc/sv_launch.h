@@ -65,6 +65,7 @@ struct Plan {
     bool has_bonus;           // verification (not VAT): bonus roles exist
     int32_t nc_dec, nc_bonus, nc_res;  // chunks per worker wavefront
     int32_t eager_bonus_from; // sequences b >= this read their bonus row without waiting for the decision
+    bool two_deep_polls;      // finishers keep two reads of their words in flight (grids of one residency)
     uint32_t tag;             // this call's tag of hand-off words
     int64_t rows_t;
     int64_t rows_d;           // 0 for one-hot drafts and T == 0
