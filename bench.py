@@ -236,14 +236,14 @@ def bench_lm_head(args) -> int:
     t0 = time.perf_counter()
     ev.record(region[0], stream)
     for i in range(args.steps):
-        ver.desc.probe_start, ver.desc.probe_stop = pairs[i]
+        ver.set_probe(pairs[i])
         ver(stream)
     ev.record(region[1], stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gemm_ms = sum(ev.elapsed_ms(a, b) for a, b in pairs) / args.steps
     step_device_ms = ev.elapsed_ms(*region) / args.steps
-    ver.desc.probe_start = ver.desc.probe_stop = None
+    ver.set_probe(None)
     for e in [e for p in pairs for e in p] + list(region):
         ev.destroy(e)
     acc = ver.accepted_len.float()

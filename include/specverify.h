@@ -68,34 +68,45 @@
  *  - Shapes are row-major with the vocabulary contiguous.  Logits are either
  *    IEEE binary32 (SV_F32) or bfloat16 (SV_BF16, the top half of binary32).
  *  - Ownership: every array is caller-owned DEVICE memory on the current HIP
- *    device; the descriptor and the size out-parameter are host memory.  The
- *    library allocates nothing and keeps no state between calls.
+ *    device; descriptors, probe records and size out-parameters are host
+ *    memory.  The library allocates nothing and keeps no per-call state.
  *  - Asynchrony: compute entry points enqueue kernels on `stream` and return;
  *    outputs are valid once the stream reaches that point.
  *  - Errors: arguments are checked on the host before anything is enqueued;
  *    on any error nothing is launched and no output or workspace byte is
  *    touched.  A failed launch returns SV_ERR_HIP (a workspace used by a call
  *    that returned SV_ERR_HIP must be zero-filled again before reuse).
+ *  - Workspace queries (`*_workspace_bytes`) return the bytes a call with
+ *    that descriptor needs; a valid descriptor always needs at least 256, so
+ *    0 means the descriptor is NULL or invalid (the compute call then
+ *    returns the reason).
  *  - Inside one call, blocks hand partial results to later blocks of the same
  *    grid through the workspace and wait for them with a bounded poll (about
  *    one second).  If a wait runs out (it cannot while the device dispatches
- *    blocks in grid order, as gfx950 does), the sequence (block) is reported
- *    with accepted_len = -2 / first_reject = -2, out_tokens -1, mask 0 and
- *    weights 0; the kernel still ends normally.
+ *    blocks in grid order, as gfx950 does), the kernel still ends normally and
+ *    the block that owns the affected output reports it: accepted_len = -2
+ *    (first_reject = -2, mask 0, weights 0 for VAT) when the wait for a
+ *    sequence's partials ran out, out_tokens[b][accepted_len[b]] = -2 when the
+ *    wait of the draw of the target's token ran out.
  *  - Data checks done on the device: a sequence (block) holding a draft token
  *    outside [0, V) is flagged (accepted_len = -1 / first_reject = -1, its
  *    out_tokens -1, mask 0, weights 0) and never indexes memory with that
  *    token.  Uniforms outside [0,1), NaN logits or rows that are all -inf
  *    give unspecified (but in-bounds) results.
- *  - Workspace: query its size, allocate it on the device, zero-fill it once
- *    before first use; every call that returns SV_OK leaves it ready for the
- *    next call (each call tags what it writes with a fresh 32-bit call
- *    number, so nothing needs clearing; the numbers repeat only after 2^32 - 1
- *    calls in one process).  This holds for sv_verify, sv_vat_labels and
- *    sv_vat_loss, which may share one workspace; a buffer that anything else
- *    has written since (the LM-head entry points, which need no clearing,
+ *  - Tagged workspaces (sv_verify, sv_vat_labels, sv_vat_loss and their _ex
+ *    forms, which may share one workspace): allocate it on the device and
+ *    zero-fill it once before first use; every call that returns SV_OK leaves
+ *    it ready for the next call.  Each call tags the words it hands between
+ *    blocks with a call number from a process-wide 64-bit counter (mapped to
+ *    1 .. 2^32 - 1, so two consecutive calls never share a number and a
+ *    zero-filled word matches none).  The number is a kernel argument, so
+ *    these calls cannot be captured into a HIP graph (every replay would
+ *    reuse it): they return SV_ERR_CAPTURING while `stream` is capturing.  A
+ *    buffer that anything else has written since (the LM-head entry points
  *    included) must be zero-filled again before one of them uses it.  Calls
- *    that use the same workspace must not overlap in time.
+ *    that use the same workspace must not overlap in time.  The LM-head entry
+ *    points and sv_vat_loss_grad hand nothing between blocks through tags and
+ *    may be captured.
  *  - Determinism: results are bitwise reproducible for identical inputs (no
  *    floating-point atomics; fixed reduction orders).
  */
@@ -111,103 +122,97 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 6
+#define SV_ABI_VERSION 7
 #define SV_MAX_DRAFT 64 /* k is limited to one 64-lane wavefront */
 #define SV_MAX_DRAFT_CHOICES 8
 
+/* Status codes.  The first seven are the core contract of sv_verify and
+ * sv_vat_labels; the later ones belong to options and entry points beyond it. */
 typedef enum sv_status {
     SV_OK = 0,
     SV_ERR_NULL_ARG = 1,          /* a required pointer is NULL */
-    SV_ERR_BAD_SHAPE = 2,         /* batch < 0, k outside [1,64], vocab < 1, or size overflow */
+    SV_ERR_BAD_SHAPE = 2,         /* B/N < 0, k outside [1,64], V outside [1, 2^24], or size overflow */
     SV_ERR_BAD_DTYPE = 3,         /* dtype not SV_F32 / SV_BF16 */
     SV_ERR_BAD_TEMPERATURE = 4,   /* T not 0 and not a finite value >= 1e-4 */
-    SV_ERR_BAD_DRAFT_KIND = 5,    /* draft_kind not SV_DRAFT_LOGITS / SV_DRAFT_ONEHOT */
-    SV_ERR_WORKSPACE_TOO_SMALL = 6,
-    SV_ERR_BAD_DECAY = 7,         /* VAT decay not in [0, 1] */
-    SV_ERR_HIP = 8,               /* a kernel launch or event record failed */
+    SV_ERR_WORKSPACE_TOO_SMALL = 5,
+    SV_ERR_HIP = 6,               /* a kernel launch, event record or stream query failed */
+    SV_ERR_BAD_DRAFT_KIND = 7,    /* draft_kind not SV_DRAFT_LOGITS / SV_DRAFT_ONEHOT */
+    SV_ERR_BAD_DECAY = 8,         /* VAT decay not in [0, 1] */
     SV_ERR_BAD_HARD_WEIGHT = 9,   /* VAT loss hard_weight not finite and >= 0 */
     SV_ERR_BAD_CONTROL = 10,      /* draft-length controller thresholds out of range */
-    SV_ERR_MISALIGNED = 11        /* an array that must be 16-byte aligned is not */
+    SV_ERR_MISALIGNED = 11,       /* an array that must be 16-byte aligned is not */
+    SV_ERR_CAPTURING = 12         /* a tagged call on a stream that is being captured into a graph */
 } sv_status;
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 typedef enum sv_draft_kind { SV_DRAFT_LOGITS = 0, SV_DRAFT_ONEHOT = 1 } sv_draft_kind;
 
-/* Shape and options of one sv_verify call.
- * probe_start / probe_stop: optional instrumentation (NULL to skip).  When both
- * are non-NULL they are recorded on `stream` immediately before and after the
- * call's single kernel launch. */
+/* Shape and options of one sv_verify call. */
 typedef struct sv_verify_desc {
-    int32_t batch;       /* B >= 0 sequences (0: nothing to do) */
-    int32_t num_draft;   /* k in [1, 64] */
-    int32_t vocab;       /* V >= 1 */
-    int32_t dtype;       /* sv_dtype of both logit arrays */
-    int32_t draft_kind;  /* sv_draft_kind */
-    float temperature;   /* T: 0 (greedy) or finite >= 1e-4 */
-    hipEvent_t probe_start;
-    hipEvent_t probe_stop;
+    int32_t B;                 /* sequences, >= 0 (0: nothing to do) */
+    int32_t k;                 /* draft positions per sequence, in [1, 64] */
+    int32_t V;                 /* vocabulary size, >= 1 */
+    sv_dtype dtype;            /* of both logit arrays */
+    sv_draft_kind draft_kind;  /* draft logits, or one-hot draft (tokens only) */
+    float temperature;         /* T: 0 (greedy) or finite >= 1e-4 */
 } sv_verify_desc;
 
-/* Shape and options of one sv_vat_labels call (probe events as above). */
+/* Shape and options of one sv_vat_labels call. */
 typedef struct sv_vat_desc {
-    int32_t blocks;      /* N >= 0 draft blocks */
-    int32_t num_draft;   /* k in [1, 64] positions per block */
-    int32_t vocab;       /* V >= 1 */
-    int32_t dtype;       /* sv_dtype */
-    float temperature;   /* T: 0 (greedy labels) or finite >= 1e-4 */
-    float decay;         /* weight decay per position after the first rejection, in [0,1] */
-    hipEvent_t probe_start;
-    hipEvent_t probe_stop;
+    int32_t N;                 /* draft blocks, >= 0 */
+    int32_t k;                 /* positions per block, in [1, 64] */
+    int32_t V;                 /* vocabulary size, >= 1 */
+    sv_dtype dtype;
+    float temperature;         /* T: 0 (greedy labels) or finite >= 1e-4 */
+    float decay;               /* weight decay per position after the first rejection, in [0, 1] */
 } sv_vat_desc;
 
-/* Shape and options of one sv_vat_loss call (probe events as above). */
+/* Shape and options of one sv_vat_loss / sv_vat_loss_grad call. */
 typedef struct sv_vat_loss_desc {
-    int32_t blocks;      /* N >= 0 draft blocks */
-    int32_t num_draft;   /* k in [1, 64] positions per block */
-    int32_t vocab;       /* V >= 1 */
-    int32_t dtype;       /* sv_dtype */
-    float temperature;   /* T: finite >= 1e-4 (both distributions are needed) */
-    float decay;         /* as for sv_vat_desc, in [0,1] */
-    float hard_weight;   /* weight of the hard-label term, finite >= 0 */
-    hipEvent_t probe_start;
-    hipEvent_t probe_stop;
+    int32_t N;                 /* draft blocks, >= 0 */
+    int32_t k;                 /* positions per block, in [1, 64] */
+    int32_t V;                 /* vocabulary size, >= 1 */
+    sv_dtype dtype;
+    float temperature;         /* T: finite >= 1e-4 (both distributions are needed) */
+    float decay;               /* as for sv_vat_desc, in [0, 1] */
+    float hard_weight;         /* weight of the hard-label term, finite >= 0 */
 } sv_vat_loss_desc;
 
-/* Shape and options of one sv_verify_lm_head_greedy call.  probe_start /
- * probe_stop (NULL to skip) bracket the call's GEMM launch (the first of its
- * two kernels). */
+/* Shape of one sv_verify_lm_head_greedy call. */
 typedef struct sv_lm_head_desc {
-    int32_t batch;       /* B >= 0 sequences */
-    int32_t num_draft;   /* k in [1, 64] */
-    int32_t vocab;       /* V in [1, 2^24]: rows of the output layer */
-    int32_t hidden;      /* D: hidden size, a multiple of 64 in [64, 65536] */
-    hipEvent_t probe_start;
-    hipEvent_t probe_stop;
+    int32_t B;                 /* sequences, >= 0 */
+    int32_t k;                 /* draft positions, in [1, 64] */
+    int32_t V;                 /* rows of the output layer, in [1, 2^24] */
+    int32_t D;                 /* hidden size, a multiple of 64 in [64, 65536] */
 } sv_lm_head_desc;
 
-/* Shape and options of one sv_verify_lm_head call (sampling); probe_start /
- * probe_stop (NULL to skip) bracket its first kernel, the statistics GEMM. */
+/* Shape and options of one sv_verify_lm_head call (sampling). */
 typedef struct sv_lm_head_sample_desc {
-    int32_t batch;       /* B >= 0 sequences */
-    int32_t num_draft;   /* k in [1, 64] */
-    int32_t vocab;       /* V in [1, 2^24] */
-    int32_t hidden;      /* D: a multiple of 64 in [64, 65536] */
-    float temperature;   /* T: finite >= 1e-4 (T == 0 is sv_verify_lm_head_greedy) */
-    hipEvent_t probe_start;
-    hipEvent_t probe_stop;
+    int32_t B;                 /* sequences, >= 0 */
+    int32_t k;                 /* draft positions, in [1, 64] */
+    int32_t V;                 /* rows of each output layer, in [1, 2^24] */
+    int32_t D;                 /* hidden size, a multiple of 64 in [64, 65536] */
+    float temperature;         /* T: finite >= 1e-4 (T == 0 is sv_verify_lm_head_greedy) */
 } sv_lm_head_sample_desc;
+
+/* Optional instrumentation of one call (host memory, may be NULL): two HIP
+ * events, both non-NULL, recorded on `stream` immediately before and after
+ * the call's main kernel (sv_verify, sv_vat_labels, sv_vat_loss: its single
+ * launch; sv_vat_loss_grad: its single launch; the LM-head calls: the GEMM). */
+typedef struct sv_probe {
+    hipEvent_t start;
+    hipEvent_t stop;
+} sv_probe;
 
 /* Returns SV_ABI_VERSION of the built library. */
 int sv_abi_version(void);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
-const char* sv_status_str(int status);
+const char* sv_status_str(sv_status status);
 
-/* Workspace bytes sv_verify needs for `desc` (host out-parameter `bytes`).
- * Errors: SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE, SV_ERR_BAD_DTYPE,
- * SV_ERR_BAD_TEMPERATURE, SV_ERR_BAD_DRAFT_KIND. */
-sv_status sv_verify_workspace_size(const sv_verify_desc* desc, size_t* bytes);
+/* Workspace bytes sv_verify needs for `desc` (0: desc NULL or invalid). */
+size_t sv_verify_workspace_bytes(const sv_verify_desc* desc);
 
 /*
  * Batched verification.  Source: NgramRL essay, section "投机解码：让草稿先跑，
@@ -227,25 +232,35 @@ sv_status sv_verify_workspace_size(const sv_verify_desc* desc, size_t* bytes);
  *                 token at r, then -1
  *  probs_out      device out or NULL, [B][k][2] float32: (p_i(x_i), q_i(x_i))
  *                 for every position (T == 0: ([x_i == g_i], 1))
+ *  workspace      device, >= sv_verify_workspace_bytes(desc) bytes, zero-filled
+ *                 once (see "Tagged workspaces" above)
+ *  stream         HIP stream the kernel is enqueued on (0 = null stream)
+ *
+ * Errors (nothing launched): SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE,
+ * SV_ERR_BAD_DTYPE, SV_ERR_BAD_TEMPERATURE, SV_ERR_BAD_DRAFT_KIND,
+ * SV_ERR_WORKSPACE_TOO_SMALL, SV_ERR_CAPTURING.  Launch failure: SV_ERR_HIP.
+ */
+sv_status sv_verify(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len,
+                    int32_t* out_tokens, float* probs_out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * sv_verify with two additions (same source):
  *  row_stats_out  device out or NULL, [B(k+1) + B k][2] float32, target rows
  *                 then draft rows (one-hot or T == 0: target rows only):
  *                 (m, Z) with m = max_y l(y)/T and Z = sum_y exp(l(y)/T - m);
  *                 at T == 0: (max_y l(y), first argmax as a float)
- *  workspace      device, >= sv_verify_workspace_size bytes, zero-filled once
- *  stream         HIP stream the kernels are enqueued on (0 = null stream)
- *
- * Errors (nothing launched): SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE,
- * SV_ERR_BAD_DTYPE, SV_ERR_BAD_TEMPERATURE, SV_ERR_BAD_DRAFT_KIND,
- * SV_ERR_WORKSPACE_TOO_SMALL.  Launch failure: SV_ERR_HIP.
+ *  probe          host, NULL or the events that bracket the kernel launch
+ * Errors as for sv_verify, plus SV_ERR_HIP if an event record fails.
  */
-sv_status sv_verify(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
-                    const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len,
-                    int32_t* out_tokens, float* probs_out, float* row_stats_out, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream);
+sv_status sv_verify_ex(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len,
+                       int32_t* out_tokens, float* probs_out, float* row_stats_out, const sv_probe* probe,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes sv_vat_labels needs for `desc`.  Errors as for
- * sv_verify_workspace_size, plus SV_ERR_BAD_DECAY. */
-sv_status sv_vat_workspace_size(const sv_vat_desc* desc, size_t* bytes);
+/* Workspace bytes sv_vat_labels needs for `desc` (0: NULL or invalid). */
+size_t sv_vat_workspace_bytes(const sv_vat_desc* desc);
 
 /*
  * VAT labels.  Source: VAT write-up, sections "VAT怎么把“验收规则”塞进训练里"
@@ -261,20 +276,28 @@ sv_status sv_vat_workspace_size(const sv_vat_desc* desc, size_t* bytes);
  *                 token, -2: wait timed out)
  *  weights        device out, [N][k] float32: 1 for i < r, decay^(i-r) for i >= r
  *  probs_out      device out or NULL, [N][k][2] float32 (p_i(x_i), q_i(x_i))
- *  row_stats_out  device out or NULL, [N k + N k][2] float32, as for sv_verify
  *  workspace, workspace_bytes, stream: as for sv_verify
  *
- * Errors as for sv_verify, plus SV_ERR_BAD_DECAY.
+ * Errors as for sv_verify (SV_ERR_BAD_DRAFT_KIND excepted), plus
+ * SV_ERR_BAD_DECAY.
  */
 sv_status sv_vat_labels(const sv_vat_desc* desc, const void* target_logits, const void* draft_logits,
                         const int32_t* draft_tokens, const float* uniforms, uint8_t* accept_mask,
-                        int32_t* first_reject, float* weights, float* probs_out, float* row_stats_out,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+                        int32_t* first_reject, float* weights, float* probs_out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes sv_vat_loss needs for `desc`.  Errors as for
- * sv_vat_workspace_size (T == 0 is SV_ERR_BAD_TEMPERATURE here), plus
- * SV_ERR_BAD_HARD_WEIGHT. */
-sv_status sv_vat_loss_workspace_size(const sv_vat_loss_desc* desc, size_t* bytes);
+/*
+ * sv_vat_labels with row_stats_out (device out or NULL, [N k + N k][2]
+ * float32, target rows then draft rows, as for sv_verify_ex) and a probe.
+ */
+sv_status sv_vat_labels_ex(const sv_vat_desc* desc, const void* target_logits, const void* draft_logits,
+                           const int32_t* draft_tokens, const float* uniforms, uint8_t* accept_mask,
+                           int32_t* first_reject, float* weights, float* probs_out, float* row_stats_out,
+                           const sv_probe* probe, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes sv_vat_loss needs for `desc` (0: NULL or invalid; T == 0
+ * is invalid here). */
+size_t sv_vat_loss_workspace_bytes(const sv_vat_loss_desc* desc);
 
 /*
  * VAT labels, weights and the weighted training loss in one pass.  Source:
@@ -291,7 +314,9 @@ sv_status sv_vat_loss_workspace_size(const sv_vat_loss_desc* desc, size_t* bytes
  *  hard_ce        device out, [N][k] float32: -ln q_i(h_i)
  *  block_loss     device out, [N] float32: sum_i w_i (soft_i + hard_weight hard_i)
  *  probs_out      device out or NULL, [N][k][2] float32 (p_i(x_i), q_i(x_i))
- *  row_stats_out  device out or NULL, [N k + N k][2] float32, as for sv_vat_labels
+ *  row_stats_out  device out or NULL, [N k + N k][2] float32, as for
+ *                 sv_vat_labels_ex (sv_vat_loss_grad consumes it)
+ *  probe          host, NULL or the events that bracket the kernel launch
  *  workspace, workspace_bytes, stream: as for sv_verify
  *
  * A block holding a draft or hard token outside [0, V) gets first_reject -1,
@@ -303,8 +328,8 @@ sv_status sv_vat_loss_workspace_size(const sv_vat_loss_desc* desc, size_t* bytes
 sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, const void* draft_logits,
                       const int32_t* draft_tokens, const float* uniforms, const int32_t* hard_tokens,
                       uint8_t* accept_mask, int32_t* first_reject, float* weights, float* soft_ce, float* hard_ce,
-                      float* block_loss, float* probs_out, float* row_stats_out, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream);
+                      float* block_loss, float* probs_out, float* row_stats_out, const sv_probe* probe,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Gradient of the VAT training loss with respect to the draft logits, for
@@ -316,14 +341,14 @@ sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, c
  * p_i = softmax(l_t/T), q_i = softmax(l_d/T).  It consumes what sv_vat_loss
  * wrote for the same logits and descriptor (its weights and row_stats_out).
  *
- *  desc           as for sv_vat_loss (decay unused here); probe events
- *                 bracket the kernel
+ *  desc           as for sv_vat_loss (decay unused here)
  *  target_logits, draft_logits  device, [N][k][V] dtype
  *  hard_tokens    device, [N][k] int32, as for sv_vat_loss
  *  weights        device, [N][k] float32: the weights sv_vat_loss wrote
  *  row_stats      device, [N k + N k][2] float32: sv_vat_loss's row_stats_out
  *  grad           device out, [N][k][V] float32 (16-byte aligned with V a
  *                 multiple of 4 for the vector path; any alignment works)
+ *  probe          host, NULL or the events that bracket the kernel
  *  stream         HIP stream
  *
  * A position of weight 0 (a flagged block, or decay 0 after the first
@@ -335,11 +360,11 @@ sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, c
  */
 sv_status sv_vat_loss_grad(const sv_vat_loss_desc* desc, const void* target_logits, const void* draft_logits,
                            const int32_t* hard_tokens, const float* weights, const float* row_stats, float* grad,
-                           hipStream_t stream);
+                           const sv_probe* probe, hipStream_t stream);
 
-/* Workspace bytes sv_verify_lm_head_greedy needs for `desc`.  Errors:
- * SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE. */
-sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes);
+/* Workspace bytes sv_verify_lm_head_greedy needs for `desc` (0: NULL or
+ * invalid). */
+size_t sv_lm_head_workspace_bytes(const sv_lm_head_desc* desc);
 
 /*
  * Greedy (T == 0) verification with the target's logits formed from its
@@ -363,7 +388,8 @@ sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes);
  *  out_tokens     device out, [B][k+1] int32, as for sv_verify
  *  argmax_out     device out or NULL, [B][k+1] int32: every position's
  *                 choice (written for invalid sequences too)
- *  workspace      device, >= sv_lm_head_workspace_size bytes (needs no
+ *  probe          host, NULL or the events that bracket the GEMM launch
+ *  workspace      device, >= sv_lm_head_workspace_bytes bytes (needs no
  *                 clearing: every byte read is written earlier in the call)
  *  stream         HIP stream the two kernels are enqueued on
  *
@@ -376,14 +402,13 @@ sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes);
  */
 sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidden_states, const void* weight,
                                    const int32_t* draft_tokens, int32_t* accepted_len, int32_t* out_tokens,
-                                   int32_t* argmax_out, void* workspace, size_t workspace_bytes,
-                                   hipStream_t stream);
+                                   int32_t* argmax_out, const sv_probe* probe, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes sv_verify_lm_head needs for `desc`: about
- * (2k+1) (8 B ceil(V/256) + 4 B V) per sequence (every row's fp32 logits
- * dominate: 856 MB at B = 128, k = 5, V = 151936).  Errors: SV_ERR_NULL_ARG,
- * SV_ERR_BAD_SHAPE, SV_ERR_BAD_TEMPERATURE. */
-sv_status sv_lm_head_sample_workspace_size(const sv_lm_head_sample_desc* desc, size_t* bytes);
+/* Workspace bytes sv_verify_lm_head needs for `desc` (0: NULL or invalid):
+ * about (2k+1) (8 B ceil(V/256) + 4 B V) per sequence (every row's fp32
+ * logits dominate: 856 MB at B = 128, k = 5, V = 151936). */
+size_t sv_lm_head_sample_workspace_bytes(const sv_lm_head_sample_desc* desc);
 
 /*
  * Speculative-sampling verification (T > 0) with the target's and the
@@ -409,7 +434,8 @@ sv_status sv_lm_head_sample_workspace_size(const sv_lm_head_sample_desc* desc, s
  *  accepted_len   device out, [B] int32 in [0, k] (-1: invalid token)
  *  out_tokens     device out, [B][k+1] int32, as for sv_verify
  *  probs_out      device out or NULL, [B][k][2] float32 (p_i(x_i), q_i(x_i))
- *  workspace      device, >= sv_lm_head_sample_workspace_size bytes (needs no
+ *  probe          host, NULL or the events that bracket the statistics GEMM
+ *  workspace      device, >= sv_lm_head_sample_workspace_bytes bytes (needs no
  *                 clearing)
  *
  * Errors (nothing launched): SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE,
@@ -419,7 +445,7 @@ sv_status sv_lm_head_sample_workspace_size(const sv_lm_head_sample_desc* desc, s
 sv_status sv_verify_lm_head(const sv_lm_head_sample_desc* desc, const void* target_hidden, const void* target_weight,
                             const void* draft_hidden, const void* draft_weight, const int32_t* draft_tokens,
                             const float* uniforms, int32_t* accepted_len, int32_t* out_tokens, float* probs_out,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+                            const sv_probe* probe, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Histogram of accepted lengths (device in, device out).

@@ -8,8 +8,9 @@ library is not built, importing works but every call raises.
     from speculative_decoding_verification_amd import verify, vat_labels
     acc, out = verify(target, draft, tokens, uniforms, temperature=1.0)
 
-Names follow the C ABI in ``include/specverify.h``: ``sv_verify`` ->
-:func:`verify`, ``sv_vat_labels`` -> :func:`vat_labels`, ``sv_vat_loss`` ->
+Names follow the C ABI in ``include/specverify.h``: ``sv_verify`` (and
+``sv_verify_ex`` when row statistics or a probe are asked for) ->
+:func:`verify`, ``sv_vat_labels`` (``sv_vat_labels_ex``) -> :func:`vat_labels`, ``sv_vat_loss`` ->
 :func:`vat_loss`, ``sv_verify_lm_head_greedy`` -> :func:`verify_lm_head_greedy`,
 ``sv_verify_lm_head`` -> :func:`verify_lm_head`.
 """
@@ -30,14 +31,14 @@ _LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 SV_F32, SV_BF16 = 0, 1
 SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT = 0, 1
 STATUS = {0: "SV_OK", 1: "SV_ERR_NULL_ARG", 2: "SV_ERR_BAD_SHAPE", 3: "SV_ERR_BAD_DTYPE",
-          4: "SV_ERR_BAD_TEMPERATURE", 5: "SV_ERR_BAD_DRAFT_KIND", 6: "SV_ERR_WORKSPACE_TOO_SMALL",
-          7: "SV_ERR_BAD_DECAY", 8: "SV_ERR_HIP", 9: "SV_ERR_BAD_HARD_WEIGHT", 10: "SV_ERR_BAD_CONTROL",
-          11: "SV_ERR_MISALIGNED"}
+          4: "SV_ERR_BAD_TEMPERATURE", 5: "SV_ERR_WORKSPACE_TOO_SMALL", 6: "SV_ERR_HIP",
+          7: "SV_ERR_BAD_DRAFT_KIND", 8: "SV_ERR_BAD_DECAY", 9: "SV_ERR_BAD_HARD_WEIGHT", 10: "SV_ERR_BAD_CONTROL",
+          11: "SV_ERR_MISALIGNED", 12: "SV_ERR_CAPTURING"}
 
-EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_size", "sv_verify",
-                    "sv_vat_workspace_size", "sv_vat_labels", "sv_vat_loss_workspace_size", "sv_vat_loss",
-                    "sv_vat_loss_grad",
-                    "sv_lm_head_workspace_size", "sv_verify_lm_head_greedy", "sv_lm_head_sample_workspace_size",
+EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_bytes", "sv_verify", "sv_verify_ex",
+                    "sv_vat_workspace_bytes", "sv_vat_labels", "sv_vat_labels_ex", "sv_vat_loss_workspace_bytes",
+                    "sv_vat_loss", "sv_vat_loss_grad",
+                    "sv_lm_head_workspace_bytes", "sv_verify_lm_head_greedy", "sv_lm_head_sample_workspace_bytes",
                     "sv_verify_lm_head", "sv_accept_histogram",
                     "sv_draft_len_init", "sv_draft_len_update")
 
@@ -52,32 +53,35 @@ class SVError(RuntimeError):
 
 
 class VerifyDesc(ctypes.Structure):
-    _fields_ = [("batch", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("draft_kind", ctypes.c_int32), ("temperature", ctypes.c_float),
-                ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+    """sv_verify_desc: B, k, V, dtype (sv_dtype), draft_kind (sv_draft_kind), temperature."""
+    _fields_ = [("B", ctypes.c_int32), ("k", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("draft_kind", ctypes.c_int32), ("temperature", ctypes.c_float)]
 
 
 class VatDesc(ctypes.Structure):
-    _fields_ = [("blocks", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float), ("decay", ctypes.c_float),
-                ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+    """sv_vat_desc: N, k, V, dtype, temperature, decay."""
+    _fields_ = [("N", ctypes.c_int32), ("k", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float), ("decay", ctypes.c_float)]
 
 
 class VatLossDesc(ctypes.Structure):
-    _fields_ = [("blocks", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
+    _fields_ = [("N", ctypes.c_int32), ("k", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float), ("decay", ctypes.c_float),
-                ("hard_weight", ctypes.c_float), ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+                ("hard_weight", ctypes.c_float)]
 
 
 class LmHeadDesc(ctypes.Structure):
-    _fields_ = [("batch", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
-                ("hidden", ctypes.c_int32), ("probe_start", ctypes.c_void_p), ("probe_stop", ctypes.c_void_p)]
+    _fields_ = [("B", ctypes.c_int32), ("k", ctypes.c_int32), ("V", ctypes.c_int32), ("D", ctypes.c_int32)]
 
 
 class LmHeadSampleDesc(ctypes.Structure):
-    _fields_ = [("batch", ctypes.c_int32), ("num_draft", ctypes.c_int32), ("vocab", ctypes.c_int32),
-                ("hidden", ctypes.c_int32), ("temperature", ctypes.c_float), ("probe_start", ctypes.c_void_p),
-                ("probe_stop", ctypes.c_void_p)]
+    _fields_ = [("B", ctypes.c_int32), ("k", ctypes.c_int32), ("V", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("temperature", ctypes.c_float)]
+
+
+class Probe(ctypes.Structure):
+    """sv_probe: two hipEvent_t handles recorded around a call's main kernel."""
+    _fields_ = [("start", ctypes.c_void_p), ("stop", ctypes.c_void_p)]
 
 
 SV_MAX_DRAFT_CHOICES = 8
@@ -111,28 +115,33 @@ def load_library():
     lib.sv_abi_version.argtypes = []
     lib.sv_status_str.restype = ctypes.c_char_p
     lib.sv_status_str.argtypes = [ctypes.c_int]
-    lib.sv_verify_workspace_size.restype = ctypes.c_int
-    lib.sv_verify_workspace_size.argtypes = [ctypes.POINTER(VerifyDesc), ctypes.POINTER(sz)]
+    pr = ctypes.POINTER(Probe)
+    lib.sv_verify_workspace_bytes.restype = sz
+    lib.sv_verify_workspace_bytes.argtypes = [ctypes.POINTER(VerifyDesc)]
     lib.sv_verify.restype = ctypes.c_int
-    lib.sv_verify.argtypes = [ctypes.POINTER(VerifyDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.sv_vat_workspace_size.restype = ctypes.c_int
-    lib.sv_vat_workspace_size.argtypes = [ctypes.POINTER(VatDesc), ctypes.POINTER(sz)]
+    lib.sv_verify.argtypes = [ctypes.POINTER(VerifyDesc)] + [vp] * 8 + [sz, vp]
+    lib.sv_verify_ex.restype = ctypes.c_int
+    lib.sv_verify_ex.argtypes = [ctypes.POINTER(VerifyDesc)] + [vp] * 8 + [pr, vp, sz, vp]
+    lib.sv_vat_workspace_bytes.restype = sz
+    lib.sv_vat_workspace_bytes.argtypes = [ctypes.POINTER(VatDesc)]
     lib.sv_vat_labels.restype = ctypes.c_int
-    lib.sv_vat_labels.argtypes = [ctypes.POINTER(VatDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.sv_vat_loss_workspace_size.restype = ctypes.c_int
-    lib.sv_vat_loss_workspace_size.argtypes = [ctypes.POINTER(VatLossDesc), ctypes.POINTER(sz)]
+    lib.sv_vat_labels.argtypes = [ctypes.POINTER(VatDesc)] + [vp] * 9 + [sz, vp]
+    lib.sv_vat_labels_ex.restype = ctypes.c_int
+    lib.sv_vat_labels_ex.argtypes = [ctypes.POINTER(VatDesc)] + [vp] * 9 + [pr, vp, sz, vp]
+    lib.sv_vat_loss_workspace_bytes.restype = sz
+    lib.sv_vat_loss_workspace_bytes.argtypes = [ctypes.POINTER(VatLossDesc)]
     lib.sv_vat_loss.restype = ctypes.c_int
-    lib.sv_vat_loss.argtypes = [ctypes.POINTER(VatLossDesc)] + [vp] * 14 + [sz, vp]
+    lib.sv_vat_loss.argtypes = [ctypes.POINTER(VatLossDesc)] + [vp] * 13 + [pr, vp, sz, vp]
     lib.sv_vat_loss_grad.restype = ctypes.c_int
-    lib.sv_vat_loss_grad.argtypes = [ctypes.POINTER(VatLossDesc)] + [vp] * 7
-    lib.sv_lm_head_workspace_size.restype = ctypes.c_int
-    lib.sv_lm_head_workspace_size.argtypes = [ctypes.POINTER(LmHeadDesc), ctypes.POINTER(sz)]
+    lib.sv_vat_loss_grad.argtypes = [ctypes.POINTER(VatLossDesc)] + [vp] * 6 + [pr, vp]
+    lib.sv_lm_head_workspace_bytes.restype = sz
+    lib.sv_lm_head_workspace_bytes.argtypes = [ctypes.POINTER(LmHeadDesc)]
     lib.sv_verify_lm_head_greedy.restype = ctypes.c_int
-    lib.sv_verify_lm_head_greedy.argtypes = [ctypes.POINTER(LmHeadDesc)] + [vp] * 7 + [sz, vp]
-    lib.sv_lm_head_sample_workspace_size.restype = ctypes.c_int
-    lib.sv_lm_head_sample_workspace_size.argtypes = [ctypes.POINTER(LmHeadSampleDesc), ctypes.POINTER(sz)]
+    lib.sv_verify_lm_head_greedy.argtypes = [ctypes.POINTER(LmHeadDesc)] + [vp] * 6 + [pr, vp, sz, vp]
+    lib.sv_lm_head_sample_workspace_bytes.restype = sz
+    lib.sv_lm_head_sample_workspace_bytes.argtypes = [ctypes.POINTER(LmHeadSampleDesc)]
     lib.sv_verify_lm_head.restype = ctypes.c_int
-    lib.sv_verify_lm_head.argtypes = [ctypes.POINTER(LmHeadSampleDesc)] + [vp] * 10 + [sz, vp]
+    lib.sv_verify_lm_head.argtypes = [ctypes.POINTER(LmHeadSampleDesc)] + [vp] * 9 + [pr, vp, sz, vp]
     i32 = ctypes.c_int32
     lib.sv_accept_histogram.restype = ctypes.c_int
     lib.sv_accept_histogram.argtypes = [vp, i32, i32, vp, vp]
@@ -173,6 +182,23 @@ def _check_dev(name, t, device, dtype=None, shape=None):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _probe_ref(probe):
+    """(start, stop) hipEvent_t handles -> a Probe record (kept by the caller), or None."""
+    if probe is None:
+        return None
+    return Probe(*probe)
+
+
+def _workspace_bytes(lib, query, call, desc, n_args, name) -> int:
+    """Size query; an invalid descriptor (size 0) raises with the reason the
+    compute entry point gives for it (it checks the descriptor first)."""
+    n = query(ctypes.byref(desc))
+    if n == 0:
+        st = call(ctypes.byref(desc), *n_args)
+        raise SVError(st if st else 2, name, lib)
+    return n
 
 
 class _Workspace:
@@ -244,18 +270,13 @@ class Verifier:
             _check_dev("uniforms", uniforms, device, torch.float32, (B, k + 1))
         else:
             uniforms = None
-        self.desc = VerifyDesc(B, k, V, dt, SV_DRAFT_ONEHOT if onehot else SV_DRAFT_LOGITS, float(temperature),
-                               None, None)
-        if probe is not None:
-            self.desc.probe_start, self.desc.probe_stop = probe
-        nbytes = ctypes.c_size_t()
-        st = lib.sv_verify_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
-        if st:
-            raise SVError(st, "sv_verify_workspace_size", lib)
+        self.desc = VerifyDesc(B, k, V, dt, SV_DRAFT_ONEHOT if onehot else SV_DRAFT_LOGITS, float(temperature))
+        nbytes = _workspace_bytes(lib, lib.sv_verify_workspace_bytes, lib.sv_verify, self.desc,
+                                  [None] * 8 + [0, None], "sv_verify")
         if workspace is None:
-            workspace = _WS.get(device, nbytes.value)
-        elif workspace.numel() * workspace.element_size() < nbytes.value:
-            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+            workspace = _WS.get(device, nbytes)
+        elif workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small: need %d bytes" % nbytes)
         self.accepted_len = torch.empty(B, dtype=torch.int32, device=device)
         self.out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
         self.probs = torch.empty((B, k, 2), dtype=torch.float32, device=device) if return_probs else None
@@ -264,15 +285,26 @@ class Verifier:
         self._keep = (target, draft, draft_tokens, uniforms, workspace)
         self._lib = lib
         self._device = device
-        self._args = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
-                      _ptr(self.accepted_len), _ptr(self.out_tokens), _ptr(self.probs), _ptr(self.row_stats),
-                      workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        self._head = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                      _ptr(self.accepted_len), _ptr(self.out_tokens), _ptr(self.probs))
+        self._ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        self.set_probe(probe)
+
+    def set_probe(self, probe) -> None:
+        """(start, stop) hipEvent_t handles to record around the kernel, or None."""
+        self.probe = _probe_ref(probe)
 
     def __call__(self, stream: Optional[int] = None) -> VerifyOutput:
         s = _stream_handle(self._device) if stream is None else stream
-        st = self._lib.sv_verify(*self._args, s)
+        if self.row_stats is None and self.probe is None:
+            st = self._lib.sv_verify(*self._head, *self._ws, s)
+            name = "sv_verify"
+        else:
+            st = self._lib.sv_verify_ex(*self._head, _ptr(self.row_stats),
+                                        None if self.probe is None else ctypes.byref(self.probe), *self._ws, s)
+            name = "sv_verify_ex"
         if st:
-            raise SVError(st, "sv_verify", self._lib)
+            raise SVError(st, name, self._lib)
         return VerifyOutput(self.accepted_len, self.out_tokens, self.probs, self.row_stats)
 
 
@@ -321,17 +353,13 @@ class VatLabeler:
         else:
             draft, uniforms = None, None
         _check_dev("draft_tokens", draft_tokens, device, torch.int32, (N, k))
-        self.desc = VatDesc(N, k, V, dt, float(temperature), float(decay), None, None)
-        if probe is not None:
-            self.desc.probe_start, self.desc.probe_stop = probe
-        nbytes = ctypes.c_size_t()
-        st = lib.sv_vat_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
-        if st:
-            raise SVError(st, "sv_vat_workspace_size", lib)
+        self.desc = VatDesc(N, k, V, dt, float(temperature), float(decay))
+        nbytes = _workspace_bytes(lib, lib.sv_vat_workspace_bytes, lib.sv_vat_labels, self.desc,
+                                  [None] * 9 + [0, None], "sv_vat_labels")
         if workspace is None:
-            workspace = _WS.get(device, nbytes.value)
-        elif workspace.numel() * workspace.element_size() < nbytes.value:
-            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+            workspace = _WS.get(device, nbytes)
+        elif workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small: need %d bytes" % nbytes)
         self.accept_mask = torch.empty((N, k), dtype=torch.uint8, device=device)
         self.first_reject = torch.empty(N, dtype=torch.int32, device=device)
         self.weights = torch.empty((N, k), dtype=torch.float32, device=device)
@@ -341,15 +369,25 @@ class VatLabeler:
         self._keep = (target, draft, draft_tokens, uniforms, workspace)
         self._lib = lib
         self._device = device
-        self._args = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
-                      _ptr(self.accept_mask), _ptr(self.first_reject), _ptr(self.weights), _ptr(self.probs),
-                      _ptr(self.row_stats), workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        self._head = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                      _ptr(self.accept_mask), _ptr(self.first_reject), _ptr(self.weights), _ptr(self.probs))
+        self._ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        self.set_probe(probe)
+
+    def set_probe(self, probe) -> None:
+        self.probe = _probe_ref(probe)
 
     def __call__(self, stream: Optional[int] = None) -> VatOutput:
         s = _stream_handle(self._device) if stream is None else stream
-        st = self._lib.sv_vat_labels(*self._args, s)
+        if self.row_stats is None and self.probe is None:
+            st = self._lib.sv_vat_labels(*self._head, *self._ws, s)
+            name = "sv_vat_labels"
+        else:
+            st = self._lib.sv_vat_labels_ex(*self._head, _ptr(self.row_stats),
+                                            None if self.probe is None else ctypes.byref(self.probe), *self._ws, s)
+            name = "sv_vat_labels_ex"
         if st:
-            raise SVError(st, "sv_vat_labels", self._lib)
+            raise SVError(st, name, self._lib)
         return VatOutput(self.accept_mask, self.first_reject, self.weights, self.probs, self.row_stats)
 
 
@@ -389,17 +427,13 @@ class VatLoss:
         _check_dev("draft_tokens", draft_tokens, device, torch.int32, (N, k))
         _check_dev("uniforms", uniforms, device, torch.float32, (N, k))
         _check_dev("hard_tokens", hard_tokens, device, torch.int32, (N, k))
-        self.desc = VatLossDesc(N, k, V, dt, float(temperature), float(decay), float(hard_weight), None, None)
-        if probe is not None:
-            self.desc.probe_start, self.desc.probe_stop = probe
-        nbytes = ctypes.c_size_t()
-        st = lib.sv_vat_loss_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
-        if st:
-            raise SVError(st, "sv_vat_loss_workspace_size", lib)
+        self.desc = VatLossDesc(N, k, V, dt, float(temperature), float(decay), float(hard_weight))
+        nbytes = _workspace_bytes(lib, lib.sv_vat_loss_workspace_bytes, lib.sv_vat_loss, self.desc,
+                                  [None] * 15 + [0, None], "sv_vat_loss")
         if workspace is None:
-            workspace = _WS.get(device, nbytes.value)
-        elif workspace.numel() * workspace.element_size() < nbytes.value:
-            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+            workspace = _WS.get(device, nbytes)
+        elif workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small: need %d bytes" % nbytes)
         self.accept_mask = torch.empty((N, k), dtype=torch.uint8, device=device)
         self.first_reject = torch.empty(N, dtype=torch.int32, device=device)
         self.weights = torch.empty((N, k), dtype=torch.float32, device=device)
@@ -415,11 +449,17 @@ class VatLoss:
         self._args = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
                       _ptr(hard_tokens), _ptr(self.accept_mask), _ptr(self.first_reject), _ptr(self.weights),
                       _ptr(self.soft_ce), _ptr(self.hard_ce), _ptr(self.block_loss), _ptr(self.probs),
-                      _ptr(self.row_stats), workspace.data_ptr(), workspace.numel() * workspace.element_size())
+                      _ptr(self.row_stats))
+        self._ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        self.set_probe(probe)
+
+    def set_probe(self, probe) -> None:
+        self.probe = _probe_ref(probe)
 
     def __call__(self, stream: Optional[int] = None) -> VatLossOutput:
         s = _stream_handle(self._device) if stream is None else stream
-        st = self._lib.sv_vat_loss(*self._args, s)
+        st = self._lib.sv_vat_loss(*self._args, None if self.probe is None else ctypes.byref(self.probe),
+                                   *self._ws, s)
         if st:
             raise SVError(st, "sv_vat_loss", self._lib)
         return VatLossOutput(self.accept_mask, self.first_reject, self.weights, self.soft_ce, self.hard_ce,
@@ -455,18 +495,20 @@ class VatLossGrad:
         _check_dev("row_stats", row_stats, device, torch.float32, (2 * N * k, 2))
         self.grad = out if out is not None else torch.empty((N, k, V), dtype=torch.float32, device=device)
         _check_dev("out", self.grad, device, torch.float32, (N, k, V))
-        self.desc = VatLossDesc(N, k, V, dt, float(temperature), 0.0, float(hard_weight), None, None)
-        if probe is not None:
-            self.desc.probe_start, self.desc.probe_stop = probe
+        self.desc = VatLossDesc(N, k, V, dt, float(temperature), 0.0, float(hard_weight))
         self._keep = (target, draft, hard_tokens, weights, row_stats)
         self._lib = lib
         self._device = device
         self._args = (ctypes.byref(self.desc), _ptr(target), _ptr(draft), _ptr(hard_tokens), _ptr(weights),
                       _ptr(row_stats), _ptr(self.grad))
+        self.set_probe(probe)
+
+    def set_probe(self, probe) -> None:
+        self.probe = _probe_ref(probe)
 
     def __call__(self, stream: Optional[int] = None):
         s = _stream_handle(self._device) if stream is None else stream
-        st = self._lib.sv_vat_loss_grad(*self._args, s)
+        st = self._lib.sv_vat_loss_grad(*self._args, None if self.probe is None else ctypes.byref(self.probe), s)
         if st:
             raise SVError(st, "sv_vat_loss_grad", self._lib)
         return self.grad
@@ -502,17 +544,13 @@ class LmHeadVerifier:
         _check_dev("hidden_states", hidden_states, device, torch.bfloat16)
         _check_dev("weight", weight, device, torch.bfloat16, (V, D))
         _check_dev("draft_tokens", draft_tokens, device, torch.int32, (B, k))
-        self.desc = LmHeadDesc(B, k, V, D, None, None)
-        if probe is not None:
-            self.desc.probe_start, self.desc.probe_stop = probe
-        nbytes = ctypes.c_size_t()
-        st = lib.sv_lm_head_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
-        if st:
-            raise SVError(st, "sv_lm_head_workspace_size", lib)
+        self.desc = LmHeadDesc(B, k, V, D)
+        nbytes = _workspace_bytes(lib, lib.sv_lm_head_workspace_bytes, lib.sv_verify_lm_head_greedy, self.desc,
+                                  [None] * 8 + [0, None], "sv_verify_lm_head_greedy")
         if workspace is None:
-            workspace = _WS_LM.get(device, nbytes.value)
-        elif workspace.numel() * workspace.element_size() < nbytes.value:
-            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+            workspace = _WS_LM.get(device, nbytes)
+        elif workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small: need %d bytes" % nbytes)
         self.accepted_len = torch.empty(B, dtype=torch.int32, device=device)
         self.out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
         self.argmax = torch.empty((B, k + 1), dtype=torch.int32, device=device) if return_argmax else None
@@ -520,12 +558,17 @@ class LmHeadVerifier:
         self._lib = lib
         self._device = device
         self._args = (ctypes.byref(self.desc), _ptr(hidden_states), _ptr(weight), _ptr(draft_tokens),
-                      _ptr(self.accepted_len), _ptr(self.out_tokens), _ptr(self.argmax), workspace.data_ptr(),
-                      workspace.numel() * workspace.element_size())
+                      _ptr(self.accepted_len), _ptr(self.out_tokens), _ptr(self.argmax))
+        self._ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        self.set_probe(probe)
+
+    def set_probe(self, probe) -> None:
+        self.probe = _probe_ref(probe)
 
     def __call__(self, stream: Optional[int] = None) -> LmHeadOutput:
         s = _stream_handle(self._device) if stream is None else stream
-        st = self._lib.sv_verify_lm_head_greedy(*self._args, s)
+        st = self._lib.sv_verify_lm_head_greedy(*self._args, None if self.probe is None else ctypes.byref(self.probe),
+                                                *self._ws, s)
         if st:
             raise SVError(st, "sv_verify_lm_head_greedy", self._lib)
         return LmHeadOutput(self.accepted_len, self.out_tokens, self.argmax)
@@ -566,17 +609,13 @@ class LmHeadSampler:
         _check_dev("draft_weight", draft_weight, device, torch.bfloat16, (V, D))
         _check_dev("draft_tokens", draft_tokens, device, torch.int32, (B, k))
         _check_dev("uniforms", uniforms, device, torch.float32, (B, k + 1))
-        self.desc = LmHeadSampleDesc(B, k, V, D, float(temperature), None, None)
-        if probe is not None:
-            self.desc.probe_start, self.desc.probe_stop = probe
-        nbytes = ctypes.c_size_t()
-        st = lib.sv_lm_head_sample_workspace_size(ctypes.byref(self.desc), ctypes.byref(nbytes))
-        if st:
-            raise SVError(st, "sv_lm_head_sample_workspace_size", lib)
+        self.desc = LmHeadSampleDesc(B, k, V, D, float(temperature))
+        nbytes = _workspace_bytes(lib, lib.sv_lm_head_sample_workspace_bytes, lib.sv_verify_lm_head, self.desc,
+                                  [None] * 11 + [0, None], "sv_verify_lm_head")
         if workspace is None:
-            workspace = _WS_LM.get(device, nbytes.value)
-        elif workspace.numel() * workspace.element_size() < nbytes.value:
-            raise ValueError("workspace too small: need %d bytes" % nbytes.value)
+            workspace = _WS_LM.get(device, nbytes)
+        elif workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small: need %d bytes" % nbytes)
         self.accepted_len = torch.empty(B, dtype=torch.int32, device=device)
         self.out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
         self.probs = torch.empty((B, k, 2), dtype=torch.float32, device=device) if return_probs else None
@@ -585,12 +624,17 @@ class LmHeadSampler:
         self._device = device
         self._args = (ctypes.byref(self.desc), _ptr(target_hidden), _ptr(target_weight), _ptr(draft_hidden),
                       _ptr(draft_weight), _ptr(draft_tokens), _ptr(uniforms), _ptr(self.accepted_len),
-                      _ptr(self.out_tokens), _ptr(self.probs), workspace.data_ptr(),
-                      workspace.numel() * workspace.element_size())
+                      _ptr(self.out_tokens), _ptr(self.probs))
+        self._ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        self.set_probe(probe)
+
+    def set_probe(self, probe) -> None:
+        self.probe = _probe_ref(probe)
 
     def __call__(self, stream: Optional[int] = None) -> LmHeadSampleOutput:
         s = _stream_handle(self._device) if stream is None else stream
-        st = self._lib.sv_verify_lm_head(*self._args, s)
+        st = self._lib.sv_verify_lm_head(*self._args, None if self.probe is None else ctypes.byref(self.probe),
+                                         *self._ws, s)
         if st:
             raise SVError(st, "sv_verify_lm_head", self._lib)
         return LmHeadSampleOutput(self.accepted_len, self.out_tokens, self.probs)

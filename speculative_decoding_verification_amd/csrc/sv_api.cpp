@@ -26,11 +26,22 @@ bool temperature_ok(float t) { return t == 0.f || (std::isfinite(t) && t >= kMin
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Tag of this call's hand-off words (see kTagFirst): consecutive calls get
-// consecutive tags, so words left by an earlier call never match.
+// Tag of this call's hand-off words (see kTagFirst).  The counter is 64-bit
+// and tags run through 1 .. 2^32 - 1 in turn, so consecutive calls never
+// share a tag (a 32-bit counter would repeat tag 1 across its wrap).
 uint32_t next_tag() {
-    static std::atomic<uint32_t> calls{0};
-    return kTagFirst + calls.fetch_add(1u, std::memory_order_relaxed) % kTagCount;
+    static std::atomic<uint64_t> calls{0};
+    return kTagFirst + static_cast<uint32_t>(calls.fetch_add(1u, std::memory_order_relaxed) % kTagCount);
+}
+
+// Tagged calls bake their tag into the kernel arguments, so a captured graph
+// would replay it; they refuse a stream that is being captured.
+sv_status capture_check(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e == hipErrorStreamCaptureImplicit) return SV_ERR_CAPTURING;
+    if (e != hipSuccess) return SV_ERR_HIP;
+    return cs == hipStreamCaptureStatusNone ? SV_OK : SV_ERR_CAPTURING;
 }
 
 struct Shape {
@@ -42,6 +53,27 @@ struct Shape {
     bool greedy, onehot, vat;
     bool loss;  // VAT with the training loss
 };
+
+// Blocks of k_verify the current device holds at once: its compute units
+// times the kernel's occupancy per unit (queried once per device).
+int64_t resident_blocks(const Shape& s, bool vec) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int64_t> cache[kMaxDevices][2][2];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+    const int e = s.elem_bytes == 2 ? 1 : 0, v = vec ? 1 : 0;
+    if (dev >= 0) {
+        const int64_t c = cache[dev][e][v].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = kDefaultComputeUnits;
+    const int per_cu = verify_blocks_per_cu(s.elem_bytes, vec);
+    const int64_t r = static_cast<int64_t>(cus) * (per_cu > 0 ? per_cu : kMinBlocksPerCu);
+    if (dev >= 0) cache[dev][e][v].store(r, std::memory_order_relaxed);
+    return r;
+}
 
 // Shared checks of both entry points.  `draft_kind` is SV_DRAFT_LOGITS for VAT.
 sv_status check_shape(int32_t batch, int32_t k, int32_t vocab, int32_t dtype, int32_t draft_kind,
@@ -79,7 +111,8 @@ size_t workspace_bytes_for(const Shape& s) {
     return workspace_layout(partial_words(s), s.batch, s.chunks).total;
 }
 
-bool fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
+bool fill_plan(const Shape& s, float temperature, float decay, bool vec, Plan* pl) {
+    const int64_t resident = resident_blocks(s, vec);
     pl->batch = static_cast<int32_t>(s.batch);
     pl->k = static_cast<int32_t>(s.k);
     pl->vocab = static_cast<int32_t>(s.vocab);
@@ -94,15 +127,17 @@ bool fill_plan(const Shape& s, float temperature, float decay, Plan* pl) {
     pl->rows_per_seq = pl->dec_rows + (pl->has_bonus ? 1 : 0);
     pl->vat_loss = s.loss;
     pl->words_per_seq = static_cast<int32_t>(s.loss ? s.k * s.chunks * kPairWords : pl->rows_per_seq * s.chunks * 2);
-    const bool small = s.batch * pl->dec_rows * s.chunks <= kSmallCallChunks;
+    const bool small = s.batch * pl->dec_rows * s.chunks <= kSmallCallWaves * resident;
     pl->nc_dec = small ? kChunksPerWaveSmall : kChunksPerWave;
-    pl->two_deep_polls = small;
     pl->nc_res = kChunksPerWaveResid;
     pl->nc_bonus = std::min(pl->nc_dec, kChunksPerWaveBonus);
     if (!plan_task_grid(pl->batch, static_cast<int64_t>(pl->dec_rows) * s.chunks, s.chunks, pl->has_resid,
                         pl->has_bonus, kWavesPerBlock * pl->nc_dec, kWavesPerBlock * pl->nc_bonus,
-                        kWavesPerBlock * pl->nc_res, kResidentBlocks, &pl->grid))
+                        kWavesPerBlock * pl->nc_res, resident, &pl->grid))
         return false;
+    // Two reads in flight per poll only when the whole grid is resident at
+    // once (no stream left for the extra reads to slow down).
+    pl->two_deep_polls = pl->grid.total_blocks <= resident;
     // The decisions of the sequences in the last residency of phase A come
     // after the bonus phase has started; their bonus rows are read without
     // waiting, so that reading them is not added to the end of the chain.
@@ -216,59 +251,72 @@ WorkspaceLayout workspace_layout(int64_t partial_words, int64_t batch, int64_t c
 
 }  // namespace sv
 
-extern "C" {
+namespace sv {
+namespace {
 
-int sv_abi_version(void) { return SV_ABI_VERSION; }
+// A valid descriptor always needs at least this many workspace bytes, so a
+// size query can report an invalid one as 0.
+constexpr size_t kMinWorkspace = 256;
 
-const char* sv_status_str(int status) {
-    switch (status) {
-        case SV_OK: return "SV_OK";
-        case SV_ERR_NULL_ARG: return "SV_ERR_NULL_ARG: a required pointer is NULL";
-        case SV_ERR_BAD_SHAPE: return "SV_ERR_BAD_SHAPE: batch < 0, k outside [1,64], vocab outside [1,2^24] or size overflow";
-        case SV_ERR_BAD_DTYPE: return "SV_ERR_BAD_DTYPE: dtype must be SV_F32 or SV_BF16";
-        case SV_ERR_BAD_TEMPERATURE: return "SV_ERR_BAD_TEMPERATURE: temperature must be 0 or finite and >= 1e-4";
-        case SV_ERR_BAD_DRAFT_KIND: return "SV_ERR_BAD_DRAFT_KIND: draft_kind must be SV_DRAFT_LOGITS or SV_DRAFT_ONEHOT";
-        case SV_ERR_BAD_HARD_WEIGHT: return "SV_ERR_BAD_HARD_WEIGHT: hard_weight must be finite and >= 0";
-        case SV_ERR_BAD_CONTROL: return "SV_ERR_BAD_CONTROL: need 0 <= down_frac < up_frac <= 1";
-        case SV_ERR_WORKSPACE_TOO_SMALL: return "SV_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the size query";
-        case SV_ERR_BAD_DECAY: return "SV_ERR_BAD_DECAY: decay must be in [0, 1]";
-        case SV_ERR_HIP: return "SV_ERR_HIP: a HIP launch or event record failed";
-        case SV_ERR_MISALIGNED: return "SV_ERR_MISALIGNED: hidden_states and weight must be 16-byte aligned";
-        default: return "unknown status";
-    }
+size_t query_bytes(size_t need) { return std::max(need, kMinWorkspace); }
+
+hipEvent_t probe_start(const sv_probe* p) { return p && p->start && p->stop ? p->start : nullptr; }
+hipEvent_t probe_stop(const sv_probe* p) { return p && p->start && p->stop ? p->stop : nullptr; }
+
+sv_status verify_shape(const sv_verify_desc* desc, Shape* s) {
+    if (!desc) return SV_ERR_NULL_ARG;
+    return check_shape(desc->B, desc->k, desc->V, desc->dtype, desc->draft_kind, desc->temperature, false, s);
 }
 
-sv_status sv_verify_workspace_size(const sv_verify_desc* desc, size_t* bytes) {
-    if (!desc || !bytes) return SV_ERR_NULL_ARG;
-    sv::Shape s;
-    const sv_status st = sv::check_shape(desc->batch, desc->num_draft, desc->vocab, desc->dtype, desc->draft_kind,
-                                         desc->temperature, false, &s);
+sv_status vat_shape(const sv_vat_desc* desc, Shape* s) {
+    if (!desc) return SV_ERR_NULL_ARG;
+    const sv_status st = check_shape(desc->N, desc->k, desc->V, desc->dtype, SV_DRAFT_LOGITS, desc->temperature,
+                                     true, s);
     if (st != SV_OK) return st;
-    *bytes = sv::workspace_bytes_for(s);
+    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
     return SV_OK;
 }
 
-sv_status sv_verify(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
-                    const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len, int32_t* out_tokens,
-                    float* probs_out, float* row_stats_out, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+sv_status vat_loss_shape(const sv_vat_loss_desc* desc, Shape* s) {
     if (!desc) return SV_ERR_NULL_ARG;
-    sv::Shape s;
-    sv_status st = sv::check_shape(desc->batch, desc->num_draft, desc->vocab, desc->dtype, desc->draft_kind,
-                                   desc->temperature, false, &s);
+    const sv_status st = check_shape(desc->N, desc->k, desc->V, desc->dtype, SV_DRAFT_LOGITS, desc->temperature,
+                                     true, s);
+    if (st != SV_OK) return st;
+    if (s->greedy) return SV_ERR_BAD_TEMPERATURE;
+    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
+    if (!(desc->hard_weight >= 0.f && std::isfinite(desc->hard_weight))) return SV_ERR_BAD_HARD_WEIGHT;
+    s->loss = true;
+    return SV_OK;
+}
+
+// Workspace check, plan, tag and launch shared by the tagged entry points.
+sv_status launch_tagged(const Shape& s, float temperature, float decay, void* workspace, size_t workspace_bytes,
+                        const sv_probe* probe, hipStream_t stream, Plan* pl) {
+    if (!workspace) return SV_ERR_NULL_ARG;
+    if (workspace_bytes < workspace_bytes_for(s)) return SV_ERR_WORKSPACE_TOO_SMALL;
+    const sv_status cs = capture_check(stream);
+    if (cs != SV_OK) return cs;
+    const bool vec = (s.vocab * s.elem_bytes) % 16 == 0 && aligned16(pl->target) &&
+                     (!pl->draft || aligned16(pl->draft));
+    if (!fill_plan(s, temperature, decay, vec, pl)) return SV_ERR_BAD_SHAPE;
+    pl->vec = vec;
+    carve_workspace(s, workspace, pl);
+    const hipError_t e = launch_path(*pl, stream, probe_start(probe), probe_stop(probe));
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status verify_impl(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len, int32_t* out_tokens,
+                      float* probs_out, float* row_stats_out, const sv_probe* probe, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    Shape s;
+    const sv_status st = verify_shape(desc, &s);
     if (st != SV_OK) return st;
     if (s.batch == 0) return SV_OK;
     if (!target_logits || !draft_tokens || !accepted_len || !out_tokens) return SV_ERR_NULL_ARG;
     if (!s.greedy && !uniforms) return SV_ERR_NULL_ARG;
     if (s.rows_d && !draft_logits) return SV_ERR_NULL_ARG;
-    const size_t need = sv::workspace_bytes_for(s);
-    if (!workspace) return SV_ERR_NULL_ARG;
-    if (workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
-
-    sv::Plan pl{};
-    if (!sv::fill_plan(s, desc->temperature, 0.f, &pl)) return SV_ERR_BAD_SHAPE;
-    pl.vec = (s.vocab * s.elem_bytes) % 16 == 0 && sv::aligned16(target_logits) &&
-             (!s.rows_d || sv::aligned16(draft_logits));
+    Plan pl{};
     pl.target = target_logits;
     pl.draft = s.rows_d ? draft_logits : nullptr;
     pl.tokens = draft_tokens;
@@ -277,43 +325,20 @@ sv_status sv_verify(const sv_verify_desc* desc, const void* target_logits, const
     pl.out_tokens = out_tokens;
     pl.probs_out = probs_out;
     pl.row_stats_out = row_stats_out;
-    sv::carve_workspace(s, workspace, &pl);
-    const hipError_t e = sv::launch_path(pl, stream, desc->probe_start, desc->probe_stop);
-    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+    return launch_tagged(s, desc->temperature, 0.f, workspace, workspace_bytes, probe, stream, &pl);
 }
 
-sv_status sv_vat_workspace_size(const sv_vat_desc* desc, size_t* bytes) {
-    if (!desc || !bytes) return SV_ERR_NULL_ARG;
-    sv::Shape s;
-    const sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
-                                         desc->temperature, true, &s);
+sv_status vat_impl(const sv_vat_desc* desc, const void* target_logits, const void* draft_logits,
+                   const int32_t* draft_tokens, const float* uniforms, uint8_t* accept_mask, int32_t* first_reject,
+                   float* weights, float* probs_out, float* row_stats_out, const sv_probe* probe, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+    Shape s;
+    const sv_status st = vat_shape(desc, &s);
     if (st != SV_OK) return st;
-    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
-    *bytes = sv::workspace_bytes_for(s);
-    return SV_OK;
-}
-
-sv_status sv_vat_labels(const sv_vat_desc* desc, const void* target_logits, const void* draft_logits,
-                        const int32_t* draft_tokens, const float* uniforms, uint8_t* accept_mask,
-                        int32_t* first_reject, float* weights, float* probs_out, float* row_stats_out,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!desc) return SV_ERR_NULL_ARG;
-    sv::Shape s;
-    sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
-                                   desc->temperature, true, &s);
-    if (st != SV_OK) return st;
-    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
     if (s.batch == 0) return SV_OK;
     if (!target_logits || !draft_tokens || !accept_mask || !first_reject || !weights) return SV_ERR_NULL_ARG;
     if (!s.greedy && (!uniforms || !draft_logits)) return SV_ERR_NULL_ARG;
-    const size_t need = sv::workspace_bytes_for(s);
-    if (!workspace) return SV_ERR_NULL_ARG;
-    if (workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
-
-    sv::Plan pl{};
-    if (!sv::fill_plan(s, desc->temperature, desc->decay, &pl)) return SV_ERR_BAD_SHAPE;
-    pl.vec = (s.vocab * s.elem_bytes) % 16 == 0 && sv::aligned16(target_logits) &&
-             (!s.rows_d || sv::aligned16(draft_logits));
+    Plan pl{};
     pl.target = target_logits;
     pl.draft = s.rows_d ? draft_logits : nullptr;
     pl.tokens = draft_tokens;
@@ -323,50 +348,97 @@ sv_status sv_vat_labels(const sv_vat_desc* desc, const void* target_logits, cons
     pl.weights = weights;
     pl.probs_out = probs_out;
     pl.row_stats_out = row_stats_out;
-    sv::carve_workspace(s, workspace, &pl);
-    const hipError_t e = sv::launch_path(pl, stream, desc->probe_start, desc->probe_stop);
-    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+    return launch_tagged(s, desc->temperature, desc->decay, workspace, workspace_bytes, probe, stream, &pl);
 }
 
-sv_status sv_vat_loss_workspace_size(const sv_vat_loss_desc* desc, size_t* bytes) {
-    if (!desc || !bytes) return SV_ERR_NULL_ARG;
+}  // namespace
+}  // namespace sv
+
+extern "C" {
+
+int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char* sv_status_str(sv_status status) {
+    switch (status) {
+        case SV_OK: return "SV_OK";
+        case SV_ERR_NULL_ARG: return "SV_ERR_NULL_ARG: a required pointer is NULL";
+        case SV_ERR_BAD_SHAPE: return "SV_ERR_BAD_SHAPE: batch < 0, k outside [1,64], vocab outside [1,2^24] or size overflow";
+        case SV_ERR_BAD_DTYPE: return "SV_ERR_BAD_DTYPE: dtype must be SV_F32 or SV_BF16";
+        case SV_ERR_BAD_TEMPERATURE: return "SV_ERR_BAD_TEMPERATURE: temperature must be 0 or finite and >= 1e-4";
+        case SV_ERR_WORKSPACE_TOO_SMALL: return "SV_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the size query";
+        case SV_ERR_HIP: return "SV_ERR_HIP: a HIP launch, event record or stream query failed";
+        case SV_ERR_BAD_DRAFT_KIND: return "SV_ERR_BAD_DRAFT_KIND: draft_kind must be SV_DRAFT_LOGITS or SV_DRAFT_ONEHOT";
+        case SV_ERR_BAD_DECAY: return "SV_ERR_BAD_DECAY: decay must be in [0, 1]";
+        case SV_ERR_BAD_HARD_WEIGHT: return "SV_ERR_BAD_HARD_WEIGHT: hard_weight must be finite and >= 0";
+        case SV_ERR_BAD_CONTROL: return "SV_ERR_BAD_CONTROL: need 0 <= down_frac < up_frac <= 1";
+        case SV_ERR_MISALIGNED: return "SV_ERR_MISALIGNED: hidden_states and weight must be 16-byte aligned";
+        case SV_ERR_CAPTURING: return "SV_ERR_CAPTURING: tagged calls cannot be captured into a HIP graph";
+        default: return "unknown status";
+    }
+}
+
+size_t sv_verify_workspace_bytes(const sv_verify_desc* desc) {
     sv::Shape s;
-    const sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
-                                         desc->temperature, true, &s);
-    if (st != SV_OK) return st;
-    if (s.greedy) return SV_ERR_BAD_TEMPERATURE;
-    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
-    if (!(desc->hard_weight >= 0.f && std::isfinite(desc->hard_weight))) return SV_ERR_BAD_HARD_WEIGHT;
-    s.loss = true;
-    *bytes = sv::workspace_bytes_for(s);
-    return SV_OK;
+    if (sv::verify_shape(desc, &s) != SV_OK) return 0;
+    return sv::query_bytes(sv::workspace_bytes_for(s));
+}
+
+sv_status sv_verify(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len, int32_t* out_tokens,
+                    float* probs_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return sv::verify_impl(desc, target_logits, draft_logits, draft_tokens, uniforms, accepted_len, out_tokens,
+                           probs_out, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+sv_status sv_verify_ex(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len,
+                       int32_t* out_tokens, float* probs_out, float* row_stats_out, const sv_probe* probe,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return sv::verify_impl(desc, target_logits, draft_logits, draft_tokens, uniforms, accepted_len, out_tokens,
+                           probs_out, row_stats_out, probe, workspace, workspace_bytes, stream);
+}
+
+size_t sv_vat_workspace_bytes(const sv_vat_desc* desc) {
+    sv::Shape s;
+    if (sv::vat_shape(desc, &s) != SV_OK) return 0;
+    return sv::query_bytes(sv::workspace_bytes_for(s));
+}
+
+sv_status sv_vat_labels(const sv_vat_desc* desc, const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms, uint8_t* accept_mask,
+                        int32_t* first_reject, float* weights, float* probs_out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    return sv::vat_impl(desc, target_logits, draft_logits, draft_tokens, uniforms, accept_mask, first_reject,
+                        weights, probs_out, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+sv_status sv_vat_labels_ex(const sv_vat_desc* desc, const void* target_logits, const void* draft_logits,
+                           const int32_t* draft_tokens, const float* uniforms, uint8_t* accept_mask,
+                           int32_t* first_reject, float* weights, float* probs_out, float* row_stats_out,
+                           const sv_probe* probe, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return sv::vat_impl(desc, target_logits, draft_logits, draft_tokens, uniforms, accept_mask, first_reject,
+                        weights, probs_out, row_stats_out, probe, workspace, workspace_bytes, stream);
+}
+
+size_t sv_vat_loss_workspace_bytes(const sv_vat_loss_desc* desc) {
+    sv::Shape s;
+    if (sv::vat_loss_shape(desc, &s) != SV_OK) return 0;
+    return sv::query_bytes(sv::workspace_bytes_for(s));
 }
 
 sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, const void* draft_logits,
                       const int32_t* draft_tokens, const float* uniforms, const int32_t* hard_tokens,
                       uint8_t* accept_mask, int32_t* first_reject, float* weights, float* soft_ce, float* hard_ce,
-                      float* block_loss, float* probs_out, float* row_stats_out, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
-    if (!desc) return SV_ERR_NULL_ARG;
+                      float* block_loss, float* probs_out, float* row_stats_out, const sv_probe* probe,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
     sv::Shape s;
-    sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
-                                   desc->temperature, true, &s);
+    const sv_status st = sv::vat_loss_shape(desc, &s);
     if (st != SV_OK) return st;
-    if (s.greedy) return SV_ERR_BAD_TEMPERATURE;
-    if (!(desc->decay >= 0.f && desc->decay <= 1.f)) return SV_ERR_BAD_DECAY;
-    if (!(desc->hard_weight >= 0.f && std::isfinite(desc->hard_weight))) return SV_ERR_BAD_HARD_WEIGHT;
-    s.loss = true;
     if (s.batch == 0) return SV_OK;
     if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !hard_tokens || !accept_mask ||
         !first_reject || !weights || !soft_ce || !hard_ce || !block_loss)
         return SV_ERR_NULL_ARG;
-    const size_t need = sv::workspace_bytes_for(s);
-    if (!workspace) return SV_ERR_NULL_ARG;
-    if (workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
-
     sv::Plan pl{};
-    if (!sv::fill_plan(s, desc->temperature, desc->decay, &pl)) return SV_ERR_BAD_SHAPE;
-    pl.vec = (s.vocab * s.elem_bytes) % 16 == 0 && sv::aligned16(target_logits) && sv::aligned16(draft_logits);
     pl.target = target_logits;
     pl.draft = draft_logits;
     pl.tokens = draft_tokens;
@@ -381,9 +453,7 @@ sv_status sv_vat_loss(const sv_vat_loss_desc* desc, const void* target_logits, c
     pl.soft_ce = soft_ce;
     pl.hard_ce = hard_ce;
     pl.block_loss = block_loss;
-    sv::carve_workspace(s, workspace, &pl);
-    const hipError_t e = sv::launch_path(pl, stream, desc->probe_start, desc->probe_stop);
-    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+    return sv::launch_tagged(s, desc->temperature, desc->decay, workspace, workspace_bytes, probe, stream, &pl);
 }
 
 sv_status sv_accept_histogram(const int32_t* accepted_len, int32_t batch, int32_t k, int32_t* hist,
@@ -396,10 +466,10 @@ sv_status sv_accept_histogram(const int32_t* accepted_len, int32_t batch, int32_
 
 sv_status sv_vat_loss_grad(const sv_vat_loss_desc* desc, const void* target_logits, const void* draft_logits,
                            const int32_t* hard_tokens, const float* weights, const float* row_stats, float* grad,
-                           hipStream_t stream) {
+                           const sv_probe* probe, hipStream_t stream) {
     if (!desc) return SV_ERR_NULL_ARG;
     sv::Shape s;
-    const sv_status st = sv::check_shape(desc->blocks, desc->num_draft, desc->vocab, desc->dtype, SV_DRAFT_LOGITS,
+    const sv_status st = sv::check_shape(desc->N, desc->k, desc->V, desc->dtype, SV_DRAFT_LOGITS,
                                          desc->temperature, true, &s);
     if (st != SV_OK) return st;
     if (s.greedy) return SV_ERR_BAD_TEMPERATURE;
@@ -423,26 +493,24 @@ sv_status sv_vat_loss_grad(const sv_vat_loss_desc* desc, const void* target_logi
     g.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(desc->temperature));
     g.inv_t = static_cast<float>(1.0 / static_cast<double>(desc->temperature));
     g.hard_weight = desc->hard_weight;
-    const hipError_t e = sv::launch_vat_grad(g, stream, desc->probe_start, desc->probe_stop);
+    const hipError_t e = sv::launch_vat_grad(g, stream, sv::probe_start(probe), sv::probe_stop(probe));
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
-sv_status sv_lm_head_workspace_size(const sv_lm_head_desc* desc, size_t* bytes) {
-    if (!desc || !bytes) return SV_ERR_NULL_ARG;
+size_t sv_lm_head_workspace_bytes(const sv_lm_head_desc* desc) {
+    if (!desc) return 0;
     sv::LmShape s;
-    const sv_status st = sv::check_lm_shape(desc->batch, desc->num_draft, desc->vocab, desc->hidden, &s);
-    if (st != SV_OK) return st;
-    *bytes = sv::lm_greedy_workspace_bytes(s);
-    return SV_OK;
+    if (sv::check_lm_shape(desc->B, desc->k, desc->V, desc->D, &s) != SV_OK) return 0;
+    return sv::query_bytes(sv::lm_greedy_workspace_bytes(s));
 }
 
 sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidden_states, const void* weight,
                                    const int32_t* draft_tokens, int32_t* accepted_len, int32_t* out_tokens,
-                                   int32_t* argmax_out, void* workspace, size_t workspace_bytes,
-                                   hipStream_t stream) {
+                                   int32_t* argmax_out, const sv_probe* probe, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
     if (!desc) return SV_ERR_NULL_ARG;
     sv::LmShape s;
-    const sv_status st = sv::check_lm_shape(desc->batch, desc->num_draft, desc->vocab, desc->hidden, &s);
+    const sv_status st = sv::check_lm_shape(desc->B, desc->k, desc->V, desc->D, &s);
     if (st != SV_OK) return st;
     if (s.batch == 0) return SV_OK;
     if (!hidden_states || !weight || !draft_tokens || !accepted_len || !out_tokens || !workspace)
@@ -463,27 +531,25 @@ sv_status sv_verify_lm_head_greedy(const sv_lm_head_desc* desc, const void* hidd
     const size_t n = static_cast<size_t>(s.rows_t * s.n_tiles);
     pl.part_v = reinterpret_cast<float*>(base);
     pl.part_i = reinterpret_cast<int32_t*>(base + sv::align_up(n * sizeof(float)));
-    const hipError_t e = sv::launch_lmhead_greedy(pl, stream, desc->probe_start, desc->probe_stop);
+    const hipError_t e = sv::launch_lmhead_greedy(pl, stream, sv::probe_start(probe), sv::probe_stop(probe));
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
-sv_status sv_lm_head_sample_workspace_size(const sv_lm_head_sample_desc* desc, size_t* bytes) {
-    if (!desc || !bytes) return SV_ERR_NULL_ARG;
+size_t sv_lm_head_sample_workspace_bytes(const sv_lm_head_sample_desc* desc) {
+    if (!desc) return 0;
     sv::LmShape s;
-    const sv_status st = sv::check_lm_shape(desc->batch, desc->num_draft, desc->vocab, desc->hidden, &s);
-    if (st != SV_OK) return st;
-    if (!(desc->temperature > 0.f) || !sv::temperature_ok(desc->temperature)) return SV_ERR_BAD_TEMPERATURE;
-    *bytes = sv::lm_sample_layout(s).total;
-    return SV_OK;
+    if (sv::check_lm_shape(desc->B, desc->k, desc->V, desc->D, &s) != SV_OK) return 0;
+    if (!(desc->temperature > 0.f) || !sv::temperature_ok(desc->temperature)) return 0;
+    return sv::query_bytes(sv::lm_sample_layout(s).total);
 }
 
 sv_status sv_verify_lm_head(const sv_lm_head_sample_desc* desc, const void* target_hidden, const void* target_weight,
                             const void* draft_hidden, const void* draft_weight, const int32_t* draft_tokens,
                             const float* uniforms, int32_t* accepted_len, int32_t* out_tokens, float* probs_out,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                            const sv_probe* probe, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!desc) return SV_ERR_NULL_ARG;
     sv::LmShape s;
-    const sv_status st = sv::check_lm_shape(desc->batch, desc->num_draft, desc->vocab, desc->hidden, &s);
+    const sv_status st = sv::check_lm_shape(desc->B, desc->k, desc->V, desc->D, &s);
     if (st != SV_OK) return st;
     if (!(desc->temperature > 0.f) || !sv::temperature_ok(desc->temperature)) return SV_ERR_BAD_TEMPERATURE;
     if (s.batch == 0) return SV_OK;
@@ -514,7 +580,7 @@ sv_status sv_verify_lm_head(const sv_lm_head_sample_desc* desc, const void* targ
     stats.n_gemms = 2;
     stats.mode = sv::kLmStats;
     sv::lmhead_layout(&stats);
-    const hipError_t e = sv::launch_lmhead_sample(stats, stream, desc->probe_start, desc->probe_stop);
+    const hipError_t e = sv::launch_lmhead_sample(stats, stream, sv::probe_start(probe), sv::probe_stop(probe));
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

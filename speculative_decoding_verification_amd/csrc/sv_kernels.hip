@@ -419,8 +419,12 @@ __device__ __forceinline__ void put_partial(uint64_t* seq_words, int i, float2 v
 
 // A finisher gives up after about a second of polling (the wall clock runs at
 // 100 MHz): it cannot happen when blocks are dispatched in grid order, and it
-// turns any other case into an error code instead of a hung kernel.
+// turns any other case into an error code instead of a hung kernel.  Roles
+// that wait on a sequence's decision wait twice as long: its finisher comes
+// earlier in the grid, so by then it has either published the decision or
+// reported its own timeout (it owns accepted_len; a draw owns only its token).
 constexpr uint64_t kPollTimeoutTicks = 1ull << 27;
+constexpr uint64_t kDecisionTimeoutTicks = 2 * kPollTimeoutTicks;
 
 // Two-deep polls: each thread reads at most kPollPer of the words.
 constexpr int kPollPer = 6;
@@ -457,7 +461,7 @@ __device__ __forceinline__ bool poll_missing(int n, uint32_t tag, uint32_t* stag
 // at once; under a full stream the extra reads cost as much as they save, so
 // larger calls read once per round.
 __device__ __forceinline__ bool collect(const uint64_t* words, int n, uint32_t tag, uint32_t* stage, int* flags,
-                                        bool two_deep) {
+                                        bool two_deep, uint64_t timeout = kPollTimeoutTicks) {
     const uint64_t t0 = wall_clock64();
     if (two_deep && n <= kPollPer * kBlock) {
         uint64_t wa[kPollPer], wb[kPollPer];
@@ -466,11 +470,11 @@ __device__ __forceinline__ bool collect(const uint64_t* words, int n, uint32_t t
             __builtin_amdgcn_s_sleep(4);
             poll_read(words, n, wb);
             if (!block_any(poll_missing(n, tag, stage, wa), flags)) return true;
-            if (block_any(wall_clock64() - t0 > kPollTimeoutTicks, flags)) return false;
+            if (block_any(wall_clock64() - t0 > timeout, flags)) return false;
             __builtin_amdgcn_s_sleep(4);
             poll_read(words, n, wa);
             if (!block_any(poll_missing(n, tag, stage, wb), flags)) return true;
-            if (block_any(wall_clock64() - t0 > kPollTimeoutTicks, flags)) return false;
+            if (block_any(wall_clock64() - t0 > timeout, flags)) return false;
         }
     }
     for (;;) {
@@ -482,7 +486,7 @@ __device__ __forceinline__ bool collect(const uint64_t* words, int n, uint32_t t
         }
         if (!block_any(missing, flags)) return true;
         // waves read the clock at slightly different times: decide together
-        if (block_any(wall_clock64() - t0 > kPollTimeoutTicks, flags)) return false;
+        if (block_any(wall_clock64() - t0 > timeout, flags)) return false;
         __builtin_amdgcn_s_sleep(8);
     }
 }
@@ -1320,7 +1324,9 @@ __device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShare
 // Residual worker `w` of sequence b: mass of one chunk of max(0, p_r - q_r).
 template <int EB, bool VEC>
 __device__ __forceinline__ void residual_worker(const Plan& pl, int b, int w, TailShared& sh) {
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls)) return;
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls,
+                 kDecisionTimeoutTicks))
+        return;
     const Decision dc = read_decision(sh.stage);
     if (dc.mode != kModeResidual) return;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1349,22 +1355,23 @@ __device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailSha
     const int64_t V = pl.vocab;
     uint64_t* rwords = pl.resid + static_cast<int64_t>(b) * P;
     const bool staged = P + kDecWords <= kStageWords;
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls)) {
-        fail_sequence(pl, b);
+    // A decision that never comes is reported by the decision finisher.
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls,
+                 kDecisionTimeoutTicks))
         return;
-    }
     const Decision dc = read_decision(sh.stage);
     if (dc.mode != kModeResidual) return;
+    int32_t* token = pl.out_tokens + static_cast<int64_t>(b) * (k + 1) + dc.r;
     if (!collect(rwords, P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote, pl.two_deep_polls)) {
-        fail_sequence(pl, b);
+        if (threadIdx.x == 0) *token = -2;
         return;
     }
     DrawRow d;
     d.mode = kModeResidual;
     d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + dc.r, V, EB);
     d.rd = row_base(pl.draft, static_cast<int64_t>(b) * k + dc.r, V, EB);
-    d.part = PartialSrc{nullptr, seq_words(pl, b)};
-    d.part_base = dc.r * P;
+    d.part = PartialSrc{nullptr, nullptr};
+    d.part_base = 0;
     d.rstage = staged ? sh.stage + kDecWords : nullptr;
     d.rwords = rwords;
     d.c2 = pl.c2;
@@ -1373,12 +1380,23 @@ __device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailSha
     d.excl = -1;
     d.rw = make_resid_w(dc.mzt, dc.mzd, pl.c2);
     // A residual that rounds to zero mass (only possible through rounding,
-    // since a rejection has probability TV(p, q)): draw from p_r instead.
+    // since a rejection has probability TV(p, q)): draw from p_r instead,
+    // from target row r's chunk partials, collected (and their tags checked)
+    // here.
     float zsum = 0.f;
     for (int cc = threadIdx.x; cc < P; cc += kBlock) zsum += chunk_mass(d, cc, -1, 0.f);
-    if (!block_any(zsum > 0.f, sh.vote)) d.mode = kModeBonus;
+    if (!block_any(zsum > 0.f, sh.vote)) {
+        const uint64_t* pw = seq_words(pl, b) + static_cast<int64_t>(dc.r) * P * 2;
+        const bool pstaged = 2 * P <= kStageWords;
+        if (!collect(pw, 2 * P, pl.tag, pstaged ? sh.stage : nullptr, sh.vote, false)) {
+            if (threadIdx.x == 0) *token = -2;
+            return;
+        }
+        d.mode = kModeBonus;
+        d.part = PartialSrc{pstaged ? sh.stage : nullptr, pw};
+    }
     const int y = draw_token<EB, VEC>(d, dc.u, P, V, sh);
-    if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + dc.r] = y;
+    if (threadIdx.x == 0) *token = y;
 }
 
 // Bonus finisher of sequence b: statistics of target row k and, when all k
@@ -1392,16 +1410,16 @@ __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared
     const float c2 = pl.c2;
     const uint64_t* words = seq_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * P * 2;
     const bool staged = 2 * P + kDecWords <= kStageWords;
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls)) {
-        fail_sequence(pl, b);
+    // A decision that never comes is reported by the decision finisher.
+    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls,
+                 kDecisionTimeoutTicks))
         return;
-    }
     const Decision dc = read_decision(sh.stage);
     // Without full acceptance the bonus row was not read (unless every row's
     // statistics are asked for): nothing to do.
     if (dc.r != k && !pl.row_stats_out) return;
     if (!collect(words, 2 * P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote, pl.two_deep_polls)) {
-        fail_sequence(pl, b);
+        if (dc.r == k && threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + k] = -2;
         return;
     }
     const PartialSrc src{staged ? sh.stage + kDecWords : nullptr, words};
@@ -1567,12 +1585,10 @@ __device__ __forceinline__ void vat_loss_finisher(const Plan& pl, int b, TailSha
 
 // ------------------------------------------------------------------ kernel
 
-// Five resident blocks per CU (five waves per SIMD): the register budget the
-// streaming loop is written for (at most 102 VGPRs).
-constexpr int kMinBlocksPerCU = 5;
-
+// Five resident blocks per CU (five waves per SIMD, kMinBlocksPerCu): the
+// register budget the streaming loop is written for (at most 102 VGPRs).
 template <int EB, bool VEC>
-__global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
+__global__ __launch_bounds__(kBlock, kMinBlocksPerCu) void k_verify(Plan pl) {
     __shared__ TailShared sh;
     const Role role = decode_role(pl.grid, static_cast<int32_t>(blockIdx.x));
     const int b = role.seq;
@@ -1597,7 +1613,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void k_verify(Plan pl) {
             // last sequences, whose decisions come late: they read it at once.
             if (!pl.row_stats_out && b < pl.eager_bonus_from) {
                 const uint64_t* dw = pl.dec + static_cast<int64_t>(b) * kDecWords + kDecRMode;
-                if (!collect(dw, 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls)) return;
+                if (!collect(dw, 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls, kDecisionTimeoutTicks)) return;
                 if (static_cast<int>(sh.stage[0] & 0xffffu) - 2 != pl.k) return;
             }
             const int base = role.index * kWavesPerBlock * pl.nc_bonus + static_cast<int>(threadIdx.x / kWave);
@@ -1781,6 +1797,22 @@ __global__ __launch_bounds__(kBlock) void k_accept_hist(const int32_t* acc, int3
 hipError_t launch_accept_hist(const int32_t* acc, int32_t batch, int32_t k, int32_t* hist, hipStream_t stream) {
     hipLaunchKernelGGL(k_accept_hist, dim3(1), dim3(kBlock), 0, stream, acc, batch, k, hist);
     return hipGetLastError();
+}
+
+namespace {
+
+template <int EB, bool VEC>
+int blocks_per_cu_typed() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_verify<EB, VEC>, kBlock, 0) != hipSuccess) return 0;
+    return n;
+}
+
+}  // namespace
+
+int verify_blocks_per_cu(int elem_bytes, bool vec) {
+    if (elem_bytes == 2) return vec ? blocks_per_cu_typed<2, true>() : blocks_per_cu_typed<2, false>();
+    return vec ? blocks_per_cu_typed<4, true>() : blocks_per_cu_typed<4, false>();
 }
 
 hipError_t launch_path(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {

@@ -105,19 +105,26 @@ struct Plan {
     TaskGrid grid;            // role of every block of the launch
 };
 
-// Blocks the GPU keeps resident at once (256 CUs x ~5 workgroups of 256
-// threads): the lag, in blocks, between a sequence's worker blocks and its
-// finisher block.
-constexpr int64_t kResidentBlocks = 1280;
+// Residency: the lags between a sequence's worker blocks and its finisher
+// block are about one residency of blocks, the device's compute units times
+// the blocks of k_verify each holds (verify_blocks_per_cu, from the
+// occupancy calculator; kMinBlocksPerCu is what the kernel's launch bounds
+// guarantee).  kDefaultComputeUnits stands in only if the device query fails.
+constexpr int kMinBlocksPerCu = 5;
+constexpr int kDefaultComputeUnits = 256;
+
+// Blocks of k_verify<EB, VEC> one compute unit holds at once (0 on failure).
+int verify_blocks_per_cu(int elem_bytes, bool vec);
 
 // Chunks each worker wavefront streams, one after the other.  Two per wave
 // for large calls: block dispatch (on the order of 150-200 blocks per
-// microsecond) would otherwise bound the grid; one per wave for small calls,
-// where the drain of long-lived blocks at the end dominates.  Residual
-// workers read two rows per chunk and take one chunk pair per wave.
+// microsecond) would otherwise bound the grid; one per wave for small calls
+// (at most kSmallCallWaves chunks per resident block), where the drain of
+// long-lived blocks at the end dominates.  Residual workers read two rows
+// per chunk and take one chunk pair per wave.
 constexpr int kChunksPerWave = 2;
 constexpr int kChunksPerWaveSmall = 1;
-constexpr int64_t kSmallCallChunks = 4 * kWavesPerBlock * kResidentBlocks;
+constexpr int64_t kSmallCallWaves = 4 * kWavesPerBlock;
 constexpr int kChunksPerWaveResid = 1;
 constexpr int kChunksPerWaveBonus = 2;
 

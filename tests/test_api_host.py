@@ -5,6 +5,7 @@ import ctypes
 import math
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -56,47 +57,90 @@ def test_status_codes_match_header():
         assert m and int(m.group(1)) == code, name
 
 
+CONTRACT_STATUS = {"SV_OK": 0, "SV_ERR_NULL_ARG": 1, "SV_ERR_BAD_SHAPE": 2, "SV_ERR_BAD_DTYPE": 3,
+                   "SV_ERR_BAD_TEMPERATURE": 4, "SV_ERR_WORKSPACE_TOO_SMALL": 5, "SV_ERR_HIP": 6}
+
+
+@pytest.fixture(scope="module")
+def contract(lib, tmp_path_factory):
+    """tests/abi_contract.c built with gcc -Werror against the header: the
+    core prototypes and codes are checked at compile time, the descriptor
+    layouts by contract_layout()."""
+    out = str(tmp_path_factory.mktemp("abi") / "libabicontract.so")
+    subprocess.check_call(["gcc", "-std=c11", "-Wall", "-Werror", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+                           "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+                           os.path.join(ROOT, "tests", "abi_contract.c"), sv.library_path(),
+                           "-Wl,-rpath," + os.path.dirname(sv.library_path()), "-o", out])
+    c = ctypes.CDLL(out)
+    c.contract_layout.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+    return c
+
+
+def test_core_contract_prototypes_codes_and_layout(lib, contract):
+    lay = (ctypes.c_int64 * 14)()
+    contract.contract_layout(lay)
+    # sv_verify_desc {int32 B, k, V; sv_dtype dtype; sv_draft_kind draft_kind; float temperature}
+    assert list(lay[0:7]) == [24, 0, 4, 8, 12, 16, 20]
+    # sv_vat_desc {int32 N, k, V; sv_dtype dtype; float temperature; float decay}
+    assert list(lay[7:14]) == [24, 0, 4, 8, 12, 16, 20]
+    assert ctypes.sizeof(sv.VerifyDesc) == 24 and ctypes.sizeof(sv.VatDesc) == 24
+    assert [f[0] for f in sv.VerifyDesc._fields_] == ["B", "k", "V", "dtype", "draft_kind", "temperature"]
+    assert [f[0] for f in sv.VatDesc._fields_] == ["N", "k", "V", "dtype", "temperature", "decay"]
+    for name, code in CONTRACT_STATUS.items():
+        assert sv.STATUS[code] == name
+        assert lib.sv_status_str(code).decode().startswith(name)
+
+
 def _vdesc(B=2, k=3, V=1000, dtype=sv.SV_F32, kind=sv.SV_DRAFT_LOGITS, T=1.0):
-    return sv.VerifyDesc(B, k, V, dtype, kind, T, None, None)
+    return sv.VerifyDesc(B, k, V, dtype, kind, T)
 
 
 def _wsize(lib, d):
-    n = ctypes.c_size_t(0)
-    st = lib.sv_verify_workspace_size(ctypes.byref(d), ctypes.byref(n))
-    return st, n.value
+    return lib.sv_verify_workspace_bytes(ctypes.byref(d))
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("batch", -1, 2), ("num_draft", 0, 2), ("num_draft", 65, 2), ("vocab", 0, 2), ("vocab", (1 << 24) + 1, 2),
+    ("B", -1, 2), ("k", 0, 2), ("k", 65, 2), ("V", 0, 2), ("V", (1 << 24) + 1, 2),
     ("dtype", 2, 3), ("dtype", -1, 3), ("temperature", -1.0, 4), ("temperature", float("nan"), 4),
-    ("temperature", float("inf"), 4), ("temperature", 1e-5, 4), ("draft_kind", 2, 5),
+    ("temperature", float("inf"), 4), ("temperature", 1e-5, 4), ("draft_kind", 2, 7),
 ])
-def test_workspace_size_rejects_bad_desc(lib, field, value, status):
+def test_workspace_query_rejects_bad_desc(lib, field, value, status):
+    """An invalid descriptor sizes to 0; the compute call names the reason."""
     d = _vdesc()
     setattr(d, field, value)
-    st, _ = _wsize(lib, d)
-    assert st == status
+    assert _wsize(lib, d) == 0
+    h = _HostBufs()
+    assert _call_verify(lib, d, h) == status
+    assert _call_verify(lib, d, h, ex=True) == status
+    assert h.untouched()
 
 
-def test_workspace_size_null_args(lib):
-    n = ctypes.c_size_t(0)
-    assert lib.sv_verify_workspace_size(None, ctypes.byref(n)) == 1
-    d = _vdesc()
-    assert lib.sv_verify_workspace_size(ctypes.byref(d), None) == 1
+def test_workspace_query_null_desc(lib):
+    assert lib.sv_verify_workspace_bytes(None) == 0
+    assert lib.sv_vat_workspace_bytes(None) == 0
+    assert lib.sv_vat_loss_workspace_bytes(None) == 0
+    assert lib.sv_lm_head_workspace_bytes(None) == 0
+    assert lib.sv_lm_head_sample_workspace_bytes(None) == 0
+
+
+def test_workspace_query_valid_desc_is_never_zero(lib):
+    assert _wsize(lib, _vdesc(B=0)) >= 256
+    assert _wsize(lib, _vdesc(B=1, k=1, V=1)) >= 256
+    assert lib.sv_vat_workspace_bytes(ctypes.byref(_vat_desc(N=0))) >= 256
 
 
 def test_workspace_size_grows_with_problem(lib):
     sizes = []
     for B in (1, 8, 64):
-        st, n = _wsize(lib, _vdesc(B=B, V=151936, dtype=sv.SV_BF16))
-        assert st == 0
+        n = _wsize(lib, _vdesc(B=B, V=151936, dtype=sv.SV_BF16))
+        assert n > 0
         sizes.append(n)
     assert sizes[0] < sizes[1] < sizes[2]
     assert all(s % 256 == 0 for s in sizes)
     # one-hot and greedy read no draft rows: smaller workspace
-    _, n_logits = _wsize(lib, _vdesc(B=8, V=151936, dtype=sv.SV_BF16))
-    _, n_onehot = _wsize(lib, _vdesc(B=8, V=151936, dtype=sv.SV_BF16, kind=sv.SV_DRAFT_ONEHOT))
-    _, n_greedy = _wsize(lib, _vdesc(B=8, V=151936, dtype=sv.SV_BF16, T=0.0))
+    n_logits = _wsize(lib, _vdesc(B=8, V=151936, dtype=sv.SV_BF16))
+    n_onehot = _wsize(lib, _vdesc(B=8, V=151936, dtype=sv.SV_BF16, kind=sv.SV_DRAFT_ONEHOT))
+    n_greedy = _wsize(lib, _vdesc(B=8, V=151936, dtype=sv.SV_BF16, T=0.0))
     assert n_onehot < n_logits and n_greedy == n_onehot
 
 
@@ -122,72 +166,86 @@ class _HostBufs:
                 and np.all(self.ws == 0xAB))
 
 
-def _call_verify(lib, d, h, **over):
+def _call_verify(lib, d, h, ex=False, **over):
+    """sv_verify, or sv_verify_ex (with a row-statistics buffer and no probe)."""
     args = dict(target=h.target, draft=h.draft, tokens=h.tokens, u=h.u, acc=h.acc, out=h.out, probs=h.probs,
-                stats=None, ws=h.ws, ws_bytes=h.ws.nbytes)
+                stats=h.probs, ws=h.ws, ws_bytes=h.ws.nbytes)
     args.update(over)
-    return lib.sv_verify(ctypes.byref(d) if d is not None else None, h.p(args["target"]), h.p(args["draft"]),
-                         h.p(args["tokens"]), h.p(args["u"]), h.p(args["acc"]), h.p(args["out"]),
-                         h.p(args["probs"]), h.p(args["stats"]), h.p(args["ws"]), args["ws_bytes"], None)
+    head = (ctypes.byref(d) if d is not None else None, h.p(args["target"]), h.p(args["draft"]),
+            h.p(args["tokens"]), h.p(args["u"]), h.p(args["acc"]), h.p(args["out"]), h.p(args["probs"]))
+    if ex:
+        return lib.sv_verify_ex(*head, h.p(args["stats"]), None, h.p(args["ws"]), args["ws_bytes"], None)
+    return lib.sv_verify(*head, h.p(args["ws"]), args["ws_bytes"], None)
 
 
-def test_verify_null_and_shape_errors_leave_outputs_untouched(lib):
+@pytest.mark.parametrize("ex", [False, True])
+def test_verify_null_and_shape_errors_leave_outputs_untouched(lib, ex):
     h = _HostBufs()
-    assert _call_verify(lib, None, h) == 1
-    assert _call_verify(lib, _vdesc(), h, target=None) == 1
-    assert _call_verify(lib, _vdesc(), h, tokens=None) == 1
-    assert _call_verify(lib, _vdesc(), h, acc=None) == 1
-    assert _call_verify(lib, _vdesc(), h, out=None) == 1
-    assert _call_verify(lib, _vdesc(), h, u=None) == 1            # T > 0 needs uniforms
-    assert _call_verify(lib, _vdesc(), h, draft=None) == 1        # draft logits needed
-    assert _call_verify(lib, _vdesc(), h, ws=None) == 1
+    assert _call_verify(lib, None, h, ex) == 1
+    assert _call_verify(lib, _vdesc(), h, ex, target=None) == 1
+    assert _call_verify(lib, _vdesc(), h, ex, tokens=None) == 1
+    assert _call_verify(lib, _vdesc(), h, ex, acc=None) == 1
+    assert _call_verify(lib, _vdesc(), h, ex, out=None) == 1
+    assert _call_verify(lib, _vdesc(), h, ex, u=None) == 1            # T > 0 needs uniforms
+    assert _call_verify(lib, _vdesc(), h, ex, draft=None) == 1        # draft logits needed
+    assert _call_verify(lib, _vdesc(), h, ex, ws=None) == 1
     d = _vdesc()
-    d.num_draft = 70
-    assert _call_verify(lib, d, h) == 2
+    d.k = 70
+    assert _call_verify(lib, d, h, ex) == 2
     d = _vdesc(T=-0.5)
-    assert _call_verify(lib, d, h) == 4
+    assert _call_verify(lib, d, h, ex) == 4
     d = _vdesc(dtype=7)
-    assert _call_verify(lib, d, h) == 3
+    assert _call_verify(lib, d, h, ex) == 3
     assert h.untouched()
 
 
-def test_verify_workspace_too_small(lib):
+@pytest.mark.parametrize("ex", [False, True])
+def test_verify_workspace_too_small(lib, ex):
     h = _HostBufs()
     d = _vdesc()
-    st, need = _wsize(lib, d)
-    assert st == 0 and need > 16
-    assert _call_verify(lib, d, h, ws_bytes=need - 1) == 6
+    need = _wsize(lib, d)
+    assert need > 16
+    assert _call_verify(lib, d, h, ex, ws_bytes=need - 1) == 5
     # one-hot drafts need no draft logits: the missing pointer is not an error,
     # the workspace is (nothing is launched either way)
     d1 = _vdesc(kind=sv.SV_DRAFT_ONEHOT)
-    assert _call_verify(lib, d1, h, draft=None, ws_bytes=8) == 6
+    assert _call_verify(lib, d1, h, ex, draft=None, ws_bytes=8) == 5
     # greedy needs neither uniforms nor draft logits
     d0 = _vdesc(T=0.0)
-    assert _call_verify(lib, d0, h, draft=None, u=None, ws_bytes=8) == 6
+    assert _call_verify(lib, d0, h, ex, draft=None, u=None, ws_bytes=8) == 5
     assert h.untouched()
 
 
 def test_verify_empty_batch_is_a_noop(lib):
     d = _vdesc(B=0)
-    assert lib.sv_verify(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.sv_verify(ctypes.byref(d), *([None] * 8), 0, None) == 0
+    assert lib.sv_verify_ex(ctypes.byref(d), *([None] * 10), 0, None) == 0
 
 
 def _vat_desc(N=2, k=3, V=1000, dtype=sv.SV_F32, T=1.0, decay=0.8):
-    return sv.VatDesc(N, k, V, dtype, T, decay, None, None)
+    return sv.VatDesc(N, k, V, dtype, T, decay)
+
+
+def _call_vat(lib, d, h, mask, fr, wt, ex=False, **o):
+    a = dict(t=h.target, dr=h.draft, x=h.tokens, u=h.u, m=mask, f=fr, w=wt, ws=h.ws, n=h.ws.nbytes)
+    a.update(o)
+    head = (ctypes.byref(d) if d is not None else None, h.p(a["t"]), h.p(a["dr"]), h.p(a["x"]), h.p(a["u"]),
+            h.p(a["m"]), h.p(a["f"]), h.p(a["w"]), None)
+    if ex:
+        return lib.sv_vat_labels_ex(*head, None, None, h.p(a["ws"]), a["n"], None)
+    return lib.sv_vat_labels(*head, h.p(a["ws"]), a["n"], None)
 
 
 @pytest.mark.parametrize("decay", [-0.1, 1.5, float("nan")])
-def test_vat_bad_decay(lib, decay):
-    n = ctypes.c_size_t()
+@pytest.mark.parametrize("ex", [False, True])
+def test_vat_bad_decay(lib, decay, ex):
     d = _vat_desc(decay=decay)
-    assert lib.sv_vat_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 7
+    assert lib.sv_vat_workspace_bytes(ctypes.byref(d)) == 0
     h = _HostBufs()
     mask = np.full(6, 7, np.uint8)
     fr = np.full(2, 7, np.int32)
     w = np.full(6, 7, np.float32)
-    st = lib.sv_vat_labels(ctypes.byref(d), h.p(h.target), h.p(h.draft), h.p(h.tokens), h.p(h.u), h.p(mask),
-                           h.p(fr), h.p(w), None, None, h.p(h.ws), h.ws.nbytes, None)
-    assert st == 7
+    assert _call_vat(lib, d, h, mask, fr, w, ex) == 8
     assert np.all(mask == 7) and np.all(fr == 7) and np.all(w == 7) and h.untouched()
 
 
@@ -197,25 +255,25 @@ def test_vat_null_and_workspace_errors(lib):
     fr = np.full(2, 7, np.int32)
     w = np.full(6, 7, np.float32)
     d = _vat_desc()
+    for ex in (False, True):
+        def call(**o):
+            return _call_vat(lib, d, h, mask, fr, w, ex, **o)
 
-    def call(**o):
-        a = dict(t=h.target, dr=h.draft, x=h.tokens, u=h.u, m=mask, f=fr, w=w, ws=h.ws, n=h.ws.nbytes)
-        a.update(o)
-        return lib.sv_vat_labels(ctypes.byref(d), h.p(a["t"]), h.p(a["dr"]), h.p(a["x"]), h.p(a["u"]),
-                                 h.p(a["m"]), h.p(a["f"]), h.p(a["w"]), None, None, h.p(a["ws"]), a["n"], None)
-
-    assert call(t=None) == 1
-    assert call(dr=None) == 1
-    assert call(u=None) == 1
-    assert call(m=None) == 1
-    assert call(f=None) == 1
-    assert call(w=None) == 1
-    assert call(n=8) == 6
+        assert call(t=None) == 1
+        assert call(dr=None) == 1
+        assert call(u=None) == 1
+        assert call(m=None) == 1
+        assert call(f=None) == 1
+        assert call(w=None) == 1
+        assert call(n=8) == 5
+        assert _call_vat(lib, None, h, mask, fr, w, ex) == 1
     assert np.all(mask == 7) and np.all(fr == 7) and np.all(w == 7) and h.untouched()
+    e = _vat_desc(N=0)
+    assert lib.sv_vat_labels(ctypes.byref(e), *([None] * 9), 0, None) == 0
 
 
 def _loss_desc(N=2, k=3, V=1000, dtype=sv.SV_F32, T=1.0, decay=0.8, hw=1.0):
-    return sv.VatLossDesc(N, k, V, dtype, T, decay, hw, None, None)
+    return sv.VatLossDesc(N, k, V, dtype, T, decay, hw)
 
 
 class _LossBufs(_HostBufs):
@@ -240,18 +298,17 @@ def _call_loss(lib, d, h, **over):
     a.update(over)
     return lib.sv_vat_loss(ctypes.byref(d) if d is not None else None, h.p(a["target"]), h.p(a["draft"]),
                            h.p(a["tokens"]), h.p(a["u"]), h.p(a["hard"]), h.p(a["mask"]), h.p(a["fr"]),
-                           h.p(a["w"]), h.p(a["soft"]), h.p(a["hardce"]), h.p(a["loss"]), None, None,
+                           h.p(a["w"]), h.p(a["soft"]), h.p(a["hardce"]), h.p(a["loss"]), None, None, None,
                            h.p(a["ws"]), a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(decay=1.5), 7), (dict(hw=-0.5), 9), (dict(hw=float("nan")), 9),
+    (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(decay=1.5), 8), (dict(hw=-0.5), 9), (dict(hw=float("nan")), 9),
     (dict(hw=float("inf")), 9), (dict(k=0), 2), (dict(dtype=5), 3),
 ])
 def test_vat_loss_rejects_bad_desc(lib, over, status):
     d = _loss_desc(**over)
-    n = ctypes.c_size_t()
-    assert lib.sv_vat_loss_workspace_size(ctypes.byref(d), ctypes.byref(n)) == status
+    assert lib.sv_vat_loss_workspace_bytes(ctypes.byref(d)) == 0
     h = _LossBufs()
     assert _call_loss(lib, d, h) == status
     assert h.loss_untouched()
@@ -263,25 +320,23 @@ def test_vat_loss_null_args_and_workspace(lib):
     assert _call_loss(lib, None, h) == 1
     for name in ("target", "draft", "tokens", "u", "hard", "mask", "fr", "w", "soft", "hardce", "loss", "ws"):
         assert _call_loss(lib, d, h, **{name: None}) == 1, name
-    n = ctypes.c_size_t()
-    assert lib.sv_vat_loss_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
-    assert _call_loss(lib, d, h, ws_bytes=n.value - 1) == 6
+    n = lib.sv_vat_loss_workspace_bytes(ctypes.byref(d))
+    assert n > 0
+    assert _call_loss(lib, d, h, ws_bytes=n - 1) == 5
     assert h.loss_untouched()
     # the loss keeps five words per chunk pair: more workspace than the labels
-    m = ctypes.c_size_t()
-    big = _loss_desc(N=64, k=16, V=128256)
-    assert lib.sv_vat_loss_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
-    assert lib.sv_vat_workspace_size(ctypes.byref(_vat_desc(N=64, k=16, V=128256)), ctypes.byref(m)) == 0
-    assert n.value > m.value
+    big = lib.sv_vat_loss_workspace_bytes(ctypes.byref(_loss_desc(N=64, k=16, V=128256)))
+    labels = lib.sv_vat_workspace_bytes(ctypes.byref(_vat_desc(N=64, k=16, V=128256)))
+    assert big > labels > 0
     e = _loss_desc(N=0)
-    assert lib.sv_vat_loss(ctypes.byref(e), *([None] * 14), 0, None) == 0
+    assert lib.sv_vat_loss(ctypes.byref(e), *([None] * 15), 0, None) == 0
 
 
 def _call_grad(lib, d, h, **over):
     a = dict(target=h.target, draft=h.draft, hard=h.hard, w=h.w, stats=h.stats, grad=h.grad)
     a.update(over)
     return lib.sv_vat_loss_grad(ctypes.byref(d) if d is not None else None, h.p(a["target"]), h.p(a["draft"]),
-                                h.p(a["hard"]), h.p(a["w"]), h.p(a["stats"]), h.p(a["grad"]), None)
+                                h.p(a["hard"]), h.p(a["w"]), h.p(a["stats"]), h.p(a["grad"]), None, None)
 
 
 class _GradBufs(_LossBufs):
@@ -305,11 +360,11 @@ def test_vat_loss_grad_rejects_bad_desc_and_null_args(lib, over, status):
         assert _call_grad(lib, d, h, **{name: None}) == 1, name
     assert np.all(h.grad == 7)
     # the decay is not used by the gradient: any value is accepted
-    assert lib.sv_vat_loss_grad(ctypes.byref(_loss_desc(N=0, decay=5.0)), *([None] * 6), None) == 0
+    assert lib.sv_vat_loss_grad(ctypes.byref(_loss_desc(N=0, decay=5.0)), *([None] * 7), None) == 0
 
 
 def _lm_desc(B=2, k=3, V=1000, D=64):
-    return sv.LmHeadDesc(B, k, V, D, None, None)
+    return sv.LmHeadDesc(B, k, V, D)
 
 
 class _LmBufs:
@@ -333,35 +388,31 @@ def _call_lm(lib, d, h, **over):
                 ws_bytes=h.ws.nbytes)
     args.update(over)
     return lib.sv_verify_lm_head_greedy(ctypes.byref(d) if d is not None else None, args["hidden"], args["weight"],
-                                        args["tokens"], args["acc"], args["out"], args["am"], args["ws"],
+                                        args["tokens"], args["acc"], args["out"], args["am"], None, args["ws"],
                                         args["ws_bytes"], None)
 
 
-@pytest.mark.parametrize("field,value", [("num_draft", 0), ("num_draft", 65), ("vocab", 0), ("vocab", (1 << 24) + 1),
-                                         ("hidden", 0), ("hidden", 48), ("hidden", 32), ("hidden", 96),
-                                         ("hidden", 65536 + 64),
-                                         ("batch", -1)])
+@pytest.mark.parametrize("field,value", [("k", 0), ("k", 65), ("V", 0), ("V", (1 << 24) + 1),
+                                         ("D", 0), ("D", 48), ("D", 32), ("D", 96),
+                                         ("D", 65536 + 64),
+                                         ("B", -1)])
 def test_lm_head_rejects_bad_shape(lib, field, value):
     d = _lm_desc()
     setattr(d, field, value)
-    n = ctypes.c_size_t(123)
-    assert lib.sv_lm_head_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 2
-    assert n.value == 123
+    assert lib.sv_lm_head_workspace_bytes(ctypes.byref(d)) == 0
     h = _LmBufs()
     assert _call_lm(lib, d, h) == 2
     assert h.untouched()
 
 
 def test_lm_head_workspace_holds_one_partial_per_row_and_run(lib):
-    n = ctypes.c_size_t()
-    assert lib.sv_lm_head_workspace_size(None, ctypes.byref(n)) == 1
-    assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc()), None) == 1
+    assert lib.sv_lm_head_workspace_bytes(None) == 0
     # rows = B(k+1); tiles = ceil(V/256): a float and an int32 each, 256-byte aligned halves
     for B, k, V in [(2, 3, 1000), (128, 5, 151936), (320, 7, 151936), (1, 1, 1)]:
-        assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc(B, k, V, 4096)), ctypes.byref(n)) == 0
+        n = lib.sv_lm_head_workspace_bytes(ctypes.byref(_lm_desc(B, k, V, 4096)))
         runs = -(-V // 256)
         half = -(-(B * (k + 1) * runs * 4) // 256) * 256
-        assert n.value == 2 * half, (B, k, V)
+        assert n == 2 * half, (B, k, V)
 
 
 def test_lm_head_null_misaligned_and_workspace_errors(lib):
@@ -372,16 +423,15 @@ def test_lm_head_null_misaligned_and_workspace_errors(lib):
         assert _call_lm(lib, d, h, **{name: None}) == 1, name
     assert _call_lm(lib, d, h, hidden=h.hidden.ctypes.data + 2) == 11
     assert _call_lm(lib, d, h, weight=h.weight.ctypes.data + 8) == 11
-    n = ctypes.c_size_t()
-    assert lib.sv_lm_head_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
-    assert _call_lm(lib, d, h, ws_bytes=n.value - 1) == 6
+    n = lib.sv_lm_head_workspace_bytes(ctypes.byref(d))
+    assert _call_lm(lib, d, h, ws_bytes=n - 1) == 5
     assert h.untouched()
     e = _lm_desc(B=0)
-    assert lib.sv_verify_lm_head_greedy(ctypes.byref(e), *([None] * 7), 0, None) == 0
+    assert lib.sv_verify_lm_head_greedy(ctypes.byref(e), *([None] * 8), 0, None) == 0
 
 
 def _lms_desc(B=2, k=3, V=1000, D=64, T=1.0):
-    return sv.LmHeadSampleDesc(B, k, V, D, T, None, None)
+    return sv.LmHeadSampleDesc(B, k, V, D, T)
 
 
 def _call_lms(lib, d, h, **over):
@@ -391,14 +441,12 @@ def _call_lms(lib, d, h, **over):
     args.update(over)
     return lib.sv_verify_lm_head(ctypes.byref(d) if d is not None else None, args["th"], args["tw"], args["dh"],
                                  args["dw"], args["tokens"], args["u"], args["acc"], args["out"], args["probs"],
-                                 args["ws"], args["ws_bytes"], None)
+                                 None, args["ws"], args["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("T", [0.0, -1.0, 1e-5, float("nan"), float("inf")])
 def test_lm_head_sample_rejects_bad_temperature(lib, T):
-    n = ctypes.c_size_t(7)
-    assert lib.sv_lm_head_sample_workspace_size(ctypes.byref(_lms_desc(T=T)), ctypes.byref(n)) == 4
-    assert n.value == 7
+    assert lib.sv_lm_head_sample_workspace_bytes(ctypes.byref(_lms_desc(T=T))) == 0
     h = _LmBufs()
     h.u = np.zeros(2 * 4, np.float32)
     assert _call_lms(lib, _lms_desc(T=T), h) == 4
@@ -416,24 +464,21 @@ def test_lm_head_sample_args_and_workspace(lib):
     assert _call_lms(lib, d, h, dw=h.weight.ctypes.data + 2) == 11
     bad = _lms_desc(D=96)
     assert _call_lms(lib, bad, h) == 2
-    n = ctypes.c_size_t()
-    assert lib.sv_lm_head_sample_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
-    assert _call_lms(lib, d, h, ws_bytes=n.value - 1) == 6
+    n = lib.sv_lm_head_sample_workspace_bytes(ctypes.byref(d))
+    assert _call_lms(lib, d, h, ws_bytes=n - 1) == 5
     assert h.untouched()
     # every row's fp32 logits dominate: 2k+1 rows of V per sequence
-    big = ctypes.c_size_t()
-    assert lib.sv_lm_head_sample_workspace_size(ctypes.byref(_lms_desc(B=128, k=5, V=151936, D=4096)),
-                                                ctypes.byref(big)) == 0
-    assert 128 * 11 * 151936 * 4 <= big.value < 128 * 11 * 151936 * 4 * 1.01
+    big = lib.sv_lm_head_sample_workspace_bytes(ctypes.byref(_lms_desc(B=128, k=5, V=151936, D=4096)))
+    assert 128 * 11 * 151936 * 4 <= big < 128 * 11 * 151936 * 4 * 1.01
     e = _lms_desc(B=0)
-    assert lib.sv_verify_lm_head(ctypes.byref(e), *([None] * 10), 0, None) == 0
+    assert lib.sv_verify_lm_head(ctypes.byref(e), *([None] * 11), 0, None) == 0
 
 
 def test_lm_head_rows_times_hidden_limit(lib):
-    n = ctypes.c_size_t()
     # B (k+1) D >= 2^31 elements: hidden-state offsets would not fit 32 bits
-    assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc(B=8192, k=63, V=1000, D=4096)), ctypes.byref(n)) == 2
-    assert lib.sv_lm_head_workspace_size(ctypes.byref(_lm_desc(B=8191, k=63, V=1000, D=4096)), ctypes.byref(n)) == 0
+    assert lib.sv_lm_head_workspace_bytes(ctypes.byref(_lm_desc(B=8192, k=63, V=1000, D=4096))) == 0
+    assert _call_lm(lib, _lm_desc(B=8192, k=63, V=1000, D=4096), _LmBufs()) == 2
+    assert lib.sv_lm_head_workspace_bytes(ctypes.byref(_lm_desc(B=8191, k=63, V=1000, D=4096))) > 0
 
 
 def test_missing_library_raises_and_package_has_no_fallback(monkeypatch, tmp_path):

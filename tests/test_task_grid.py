@@ -89,9 +89,12 @@ def test_every_block_decodes_to_one_role_in_dependency_order(probe):
     ("vat", 2048, 16, 128256, 4, 1.0, False, True),
     ("tiny", 4, 4, 1000, 4, 1.0, False, False),
 ])
-def test_planned_grids_of_the_workloads(probe, name, B, k, V, eb, T, onehot, vat):
+@pytest.mark.parametrize("resident", [32 * 5, 64 * 5, 80 * 5, 128 * 5, 256 * 5, 256 * 6])
+def test_planned_grids_of_the_workloads(probe, name, B, k, V, eb, T, onehot, vat, resident):
     """The planner's own widths and lags at the workload shapes (four
-    wavefronts per block, the chunk counts of 8 KiB chunks)."""
+    wavefronts per block, the chunk counts of 8 KiB chunks), for devices of
+    32 to 256 compute units: the residency (compute units times blocks per
+    unit) only moves the lags, never the order the waits rely on."""
     chunks = -(-V // (8192 // eb))
     reads_draft = not onehot and T != 0.0
     dec_rows = k + (k if reads_draft else 0)
@@ -100,9 +103,11 @@ def test_planned_grids_of_the_workloads(probe, name, B, k, V, eb, T, onehot, vat
     params = np.zeros(8, np.int32)
     for per_dec, per_bonus, per_res in ((4, 4, 4), (8, 4, 4), (8, 8, 4), (16, 8, 8)):
         n = probe.probe_plan(B, dec_rows * chunks, chunks, int(has_resid), int(has_bonus), per_dec, per_bonus,
-                             per_res, 1280, params.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+                             per_res, resident, params.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
         assert n > 0
         w_dec, w_res, w_bonus, la, lr, lf, lb, nseg = params.tolist()
+        # a finisher sits about one residency of blocks behind its workers
+        assert la == min(B, -(-resident // (w_dec + 1 + ((w_res + 1) if has_resid else 0))))
         assert w_dec == -(-dec_rows * chunks // per_dec)
         assert w_bonus == (-(-chunks // per_bonus) if has_bonus else 0)
         assert 1 <= nseg <= 12
