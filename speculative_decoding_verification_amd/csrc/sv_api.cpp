@@ -135,9 +135,11 @@ bool fill_plan(const Shape& s, float temperature, float decay, bool vec, Plan* p
                         pl->has_bonus, kWavesPerBlock * pl->nc_dec, kWavesPerBlock * pl->nc_bonus,
                         kWavesPerBlock * pl->nc_res, resident, &pl->grid))
         return false;
-    // Two reads in flight per poll only when the whole grid is resident at
-    // once (no stream left for the extra reads to slow down).
-    pl->two_deep_polls = pl->grid.total_blocks <= resident;
+    // Two reads in flight per poll only when (nearly) the whole grid is
+    // resident at once: no stream is left for the extra reads to slow down.
+    // A quarter of a residency over is allowed for the finisher and bonus
+    // blocks that follow a one-residency stream.
+    pl->two_deep_polls = pl->grid.total_blocks <= resident + resident / 4;
     // The decisions of the sequences in the last residency of phase A come
     // after the bonus phase has started; their bonus rows are read without
     // waiting, so that reading them is not added to the end of the chain.

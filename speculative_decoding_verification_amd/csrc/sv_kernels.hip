@@ -516,6 +516,7 @@ struct TailShared {
     int r;
     int mode;
     int x_r;
+    float l_x;
 };
 
 // ------------------------------------------------------------------ sampling
@@ -554,6 +555,7 @@ struct DrawRow {
     const uint64_t* rwords;   // ... or as words
     float c2, mt, corr, mrow; // target row: mt = max*c2 rounded, corr (row_scale), mrow = max
     int excl;                 // one-hot: excluded token, else -1
+    float lx;                 // one-hot: target logit of the excluded token
     ResidW rw;
 };
 
@@ -773,34 +775,50 @@ __device__ __forceinline__ int draw_scan(const DrawPick& pk, const float (&w)[Ch
     return pk.cs * CH + y;
 }
 
-// The chunk of a draw from `d`: one wave-level pick when P <= 64, else the
-// tiled block-level selection.  Whole block.
+// The chunk of a draw from `d` (whole block).  P <= 64: lane c of every wave
+// holds the mass of chunk c and each wave picks redundantly (DPP prefix scan,
+// ballot; no barrier).  A one-hot draw needs x_r's chunk without x_r: its
+// partial minus x_r's weight when that difference keeps the draw's accuracy
+// (the chunk holds at most 8 times the mass left to draw from, so the
+// difference's rounding, about 2^-22 of the chunk, stays below 2^-19 of the
+// total), else the chunk summed again without x_r.  P > 64: the tiled
+// block-level selection.
 template <int EB, bool VEC>
 __device__ __forceinline__ DrawPick pick_chunk(const DrawRow& d, float u, int P, int64_t V, TailShared& sh) {
     constexpr int CH = Chunk<EB>::kElems;
     constexpr int PT = Chunk<EB>::kPerThread;
     if (P > kWave) return draw_select<EB, VEC>(d, u, P, V, sh);
+    const int lane = threadIdx.x & (kWave - 1);
+    float mass = lane < P ? chunk_mass(d, lane, -1, 0.f) : 0.f;
     int cx = -1;
     float mass_cx = 0.f;
     if (d.mode == kModeOneHot) {
         cx = d.excl / CH;
-        float lt[PT], ld[PT], w[PT];
-        load_runs<EB, VEC>(d, cx, V, lt, ld);
-        run_weights<EB>(d, static_cast<int64_t>(cx) * CH, lt, ld, w);
-        float sum = 0.f;
+        const float part = readlane(mass, cx);
+        const float wx = exp2_hw(fmaf(d.lx, d.c2, -d.mt)) * d.corr;
+        const float left = wave_sum(mass) - wx;  // the mass the draw is from
+        if (part <= 8.f * left) {
+            // a remainder within twice its rounding of zero is taken as zero
+            mass_cx = part - wx > 0x1p-21f * part ? part - wx : 0.f;
+        } else {
+            float lt[PT], ld[PT], w[PT];
+            load_runs<EB, VEC>(d, cx, V, lt, ld);
+            run_weights<EB>(d, static_cast<int64_t>(cx) * CH, lt, ld, w);
+            float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < PT; ++e) sum += w[e];
-        mass_cx = block_sum(sum, sh.wt);
+            for (int e = 0; e < PT; ++e) sum += w[e];
+            mass_cx = block_sum(sum, sh.wt);
+        }
+        if (lane == cx) mass = mass_cx;
     }
-    const int lane = threadIdx.x & (kWave - 1);
-    const float mass = lane < P ? chunk_mass(d, lane, cx, mass_cx) : 0.f;
     DrawPick pk = wave_pick(mass, u, P);
     pk.cx = cx;
     pk.mass_cx = mass_cx;
     return pk;
 }
 
-// Draws one token from the weights of `d` with uniform u.  Whole block.
+// Draws one token from the weights of `d` with uniform u.  Whole block;
+// returns the token on every thread.
 template <int EB, bool VEC>
 __device__ __forceinline__ int draw_token(const DrawRow& d, float u, int P, int64_t V, TailShared& sh) {
     constexpr int CH = Chunk<EB>::kElems;
@@ -1178,6 +1196,56 @@ __device__ __forceinline__ void write_row_stats(const Plan& pl, int64_t grow, fl
     pl.row_stats_out[2 * grow + 1] = pl.greedy ? static_cast<float>(__float_as_int(res.y)) : res.y;
 }
 
+// The draw of a one-hot draft rejected at r: target row r without x_r.
+template <int EB>
+__device__ __forceinline__ DrawRow onehot_row(const Plan& pl, int b, int r, const PartialSrc& src, float m_r, int x_r,
+                                              float l_x) {
+    DrawRow d;
+    d.mode = kModeOneHot;
+    d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + r, pl.vocab, EB);
+    d.rd = nullptr;
+    d.part = src;
+    d.part_base = r * pl.chunks;
+    d.rstage = nullptr;
+    d.rwords = nullptr;
+    d.c2 = pl.c2;
+    d.mrow = m_r;
+    d.mt = row_scale(m_r, pl.c2, d.corr);
+    d.excl = x_r;
+    d.lx = l_x;
+    return d;
+}
+
+// Outputs of a sequence's decision, stored by wave 0 of its finisher (lane i
+// holds draft token x_i): accepted_len, out_tokens (x_0..x_{r-1}, -1 after
+// r; at r the greedy argmax, or `token` for a one-hot draw, else left to the
+// block that draws it) and the decision words later roles wait on.
+__device__ __forceinline__ void publish_decision(const Plan& pl, int b, int r, int mode, int x, float u_draw,
+                                                 int token, const TailShared& sh) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int k = pl.k;
+    int32_t* out = pl.out_tokens + static_cast<int64_t>(b) * (k + 1);
+    for (int j = lane; j <= k; j += kWave) {
+        if (r < 0) out[j] = -1;
+        else if (j < r) out[j] = x;  // j < r <= k <= 64 here, so j == lane
+        else if (j > r) out[j] = -1;
+        else if (pl.greedy && r < k) out[j] = __float_as_int(sh.mz[r].y);
+        else if (mode == kModeOneHot) out[j] = token;
+    }
+    if (lane == 0) {
+        pl.accepted_len[b] = r;
+        Decision d{};
+        d.r = r;
+        d.mode = mode;
+        d.u = u_draw;
+        if (r >= 0 && r < k) {
+            d.mzt = sh.mz[r];
+            if (!pl.onehot && !pl.greedy) d.mzd = sh.mz[k + r];
+        }
+        put_decision(pl, b, d);
+    }
+}
+
 // Decision finisher of sequence b: everything that needs rows 0..k-1.
 template <int EB, bool VEC>
 __device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShared& sh) {
@@ -1273,51 +1341,25 @@ __device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShare
         } else {
             int mode = kModeDone;
             if (!invalid && !pl.greedy) mode = r == k ? kModeBonus : (pl.onehot ? kModeOneHot : kModeResidual);
-            // out[r] belongs to whoever supplies the target's token there:
-            // this block at T == 0 with r < k and for one-hot drafts, the
-            // bonus finisher at r == k, the residual finisher otherwise.
-            int32_t* out = pl.out_tokens + static_cast<int64_t>(b) * (k + 1);
-            for (int j = lane; j <= k; j += kWave) {
-                if (invalid) out[j] = -1;
-                else if (j < r) out[j] = x;  // j < r <= k <= 64 here, so j == lane
-                else if (j > r) out[j] = -1;
-                else if (pl.greedy && r < k) out[j] = __float_as_int(sh.mz[r].y);
-            }
             if (lane == 0) {
-                pl.accepted_len[b] = r;
                 sh.r = r;
                 sh.mode = mode;
                 sh.x_r = (r >= 0 && r < k) ? __builtin_amdgcn_readlane(x, r) : -1;
-                Decision d{};
-                d.r = r;
-                d.mode = mode;
-                d.u = u_draw;
-                if (r >= 0 && r < k) {
-                    d.mzt = sh.mz[r];
-                    if (!pl.onehot && !pl.greedy) d.mzd = sh.mz[k + r];
-                }
-                put_decision(pl, b, d);
+                sh.l_x = (r >= 0 && r < k) ? readlane(lt, r) : 0.f;
             }
+            // A one-hot draw is taken by this block before anything is
+            // stored: loads that wait behind this wave's write-through
+            // stores would wait for their acknowledgements as well.
+            if (mode != kModeOneHot) publish_decision(pl, b, r, mode, x, u_draw, -1, sh);
         }
     }
     __syncthreads();
 
     if (!pl.vat && sh.mode == kModeOneHot) {
         const int r = sh.r;
-        DrawRow d;
-        d.mode = kModeOneHot;
-        d.rt = row_base(pl.target, static_cast<int64_t>(b) * n_t + r, V, EB);
-        d.rd = nullptr;
-        d.part = src;
-        d.part_base = r * P;
-        d.rstage = nullptr;
-        d.rwords = nullptr;
-        d.c2 = c2;
-        d.mrow = sh.mz[r].x;
-        d.mt = row_scale(d.mrow, c2, d.corr);
-        d.excl = sh.x_r;
+        const DrawRow d = onehot_row<EB>(pl, b, r, src, sh.mz[r].x, sh.x_r, sh.l_x);
         const int y = draw_token<EB, VEC>(d, u_draw, P, V, sh);
-        if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + r] = y;
+        if (wave == 0) publish_decision(pl, b, r, kModeOneHot, x, u_draw, y, sh);
     }
 }
 
@@ -1378,6 +1420,7 @@ __device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailSha
     d.mrow = dc.mzt.x;
     d.mt = row_scale(dc.mzt.x, pl.c2, d.corr);
     d.excl = -1;
+    d.lx = 0.f;
     d.rw = make_resid_w(dc.mzt, dc.mzd, pl.c2);
     // A residual that rounds to zero mass (only possible through rounding,
     // since a rejection has probability TV(p, q)): draw from p_r instead,
@@ -1448,6 +1491,7 @@ __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared
     d.mrow = sh.mz[0].x;
     d.mt = row_scale(d.mrow, c2, d.corr);
     d.excl = -1;
+    d.lx = 0.f;
     const int y = draw_token<EB, VEC>(d, dc.u, P, V, sh);
     if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + k] = y;
 }

@@ -61,19 +61,22 @@ struct Plan {
     int32_t dec_rows;         // rows the decision reads: k or 2k
     int32_t rows_per_seq;     // dec_rows + (1 if there is a bonus row)
     int32_t words_per_seq;    // hand-off words of one sequence in `partials`
-    bool has_resid;           // draft logits at T > 0: residual roles exist
-    bool has_bonus;           // verification (not VAT): bonus roles exist
+    int32_t has_resid;        // draft logits at T > 0: residual roles exist
+    int32_t has_bonus;        // verification (not VAT): bonus roles exist
     int32_t nc_dec, nc_bonus, nc_res;  // chunks per worker wavefront
     int32_t eager_bonus_from; // sequences b >= this read their bonus row without waiting for the decision
-    bool two_deep_polls;      // finishers keep two reads of their words in flight (grids of one residency)
+    int32_t two_deep_polls;   // finishers keep two reads of their words in flight (grids of one residency)
     uint32_t tag;             // this call's tag of hand-off words
     int64_t rows_t;
     int64_t rows_d;           // 0 for one-hot drafts and T == 0
-    bool vec;                 // 16-byte loads allowed (aligned rows)
-    bool greedy;              // T == 0
-    bool onehot;
-    bool vat;
-    bool vat_loss;            // VAT with the training loss: workers read chunk pairs
+    // Flags are 32-bit: a byte-sized field at an unaligned offset of the
+    // kernel argument block is read with a vector load (a memory round trip
+    // at the start of every block) instead of a scalar one.
+    int32_t vec;              // 16-byte loads allowed (aligned rows)
+    int32_t greedy;           // T == 0
+    int32_t onehot;
+    int32_t vat;
+    int32_t vat_loss;         // VAT with the training loss: workers read chunk pairs
     float temperature;
     float c2;                 // log2(e) / T
     float decay;
@@ -168,7 +171,7 @@ struct GradPlan {
     int32_t vocab;
     int32_t chunks;           // ceil(V / chunk)
     int32_t elem_bytes;
-    bool vec;                 // 16-byte rows and pointers
+    int32_t vec;              // 16-byte rows and pointers
     float c2;                 // log2(e) / T
     float inv_t;              // 1 / T
     float hard_weight;
