@@ -141,7 +141,8 @@ typedef enum sv_status {
     SV_ERR_BAD_HARD_WEIGHT = 9,   /* VAT loss hard_weight not finite and >= 0 */
     SV_ERR_BAD_CONTROL = 10,      /* draft-length controller thresholds out of range */
     SV_ERR_MISALIGNED = 11,       /* an array that must be 16-byte aligned is not */
-    SV_ERR_CAPTURING = 12         /* a tagged call on a stream that is being captured into a graph */
+    SV_ERR_CAPTURING = 12,        /* a tagged call on a stream that is being captured into a graph */
+    SV_ERR_SCRATCH_TOO_SMALL = 13 /* sv_verify_noalloc: the call needs more than SV_NOALLOC_SCRATCH_BYTES */
 } sv_status;
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -258,6 +259,28 @@ sv_status sv_verify_ex(const sv_verify_desc* desc, const void* target_logits, co
                        const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len,
                        int32_t* out_tokens, float* probs_out, float* row_stats_out, const sv_probe* probe,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the workspace built into the library for sv_verify_noalloc. */
+#define SV_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * sv_verify without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory at the call (tight serving
+ * loops, harnesses that forbid allocation).  The hand-off words live in an
+ * array of SV_NOALLOC_SCRATCH_BYTES built into the library, one per device,
+ * held until the process ends; the first call on a device looks its address
+ * up and zero-fills it with a kernel on `stream`.  Arguments, outputs and
+ * errors are those of sv_verify, plus SV_ERR_SCRATCH_TOO_SMALL when
+ * sv_verify_workspace_bytes(desc) exceeds SV_NOALLOC_SCRATCH_BYTES (nothing
+ * launched; about 4 MB covers B = 320, k = 7, V = 151936 bf16 logits).
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (different streams, or host threads) race and must not
+ * be issued; calls in order on one stream are safe.  Not capturable
+ * (SV_ERR_CAPTURING), as for the other tagged calls.
+ */
+sv_status sv_verify_noalloc(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
+                            const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len,
+                            int32_t* out_tokens, float* probs_out, hipStream_t stream);
 
 /* Workspace bytes sv_vat_labels needs for `desc` (0: NULL or invalid). */
 size_t sv_vat_workspace_bytes(const sv_vat_desc* desc);

@@ -20,7 +20,7 @@ import ctypes
 import os
 from typing import NamedTuple, Optional
 
-__all__ = ["verify", "vat_labels", "vat_loss", "verify_lm_head_greedy", "verify_lm_head", "accept_histogram",
+__all__ = ["verify", "verify_noalloc", "vat_labels", "vat_loss", "verify_lm_head_greedy", "verify_lm_head", "accept_histogram",
            "Verifier", "VatLabeler", "VatLoss", "LmHeadVerifier", "LmHeadSampler",
            "DraftLengthController", "SVError", "library_path", "load_library", "SV_F32", "SV_BF16", "SV_DRAFT_LOGITS",
            "SV_DRAFT_ONEHOT", "STATUS"]
@@ -33,9 +33,10 @@ SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT = 0, 1
 STATUS = {0: "SV_OK", 1: "SV_ERR_NULL_ARG", 2: "SV_ERR_BAD_SHAPE", 3: "SV_ERR_BAD_DTYPE",
           4: "SV_ERR_BAD_TEMPERATURE", 5: "SV_ERR_WORKSPACE_TOO_SMALL", 6: "SV_ERR_HIP",
           7: "SV_ERR_BAD_DRAFT_KIND", 8: "SV_ERR_BAD_DECAY", 9: "SV_ERR_BAD_HARD_WEIGHT", 10: "SV_ERR_BAD_CONTROL",
-          11: "SV_ERR_MISALIGNED", 12: "SV_ERR_CAPTURING"}
+          11: "SV_ERR_MISALIGNED", 12: "SV_ERR_CAPTURING", 13: "SV_ERR_SCRATCH_TOO_SMALL"}
 
 EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_bytes", "sv_verify", "sv_verify_ex",
+                    "sv_verify_noalloc",
                     "sv_vat_workspace_bytes", "sv_vat_labels", "sv_vat_labels_ex", "sv_vat_loss_workspace_bytes",
                     "sv_vat_loss", "sv_vat_loss_grad",
                     "sv_lm_head_workspace_bytes", "sv_verify_lm_head_greedy", "sv_lm_head_sample_workspace_bytes",
@@ -122,6 +123,8 @@ def load_library():
     lib.sv_verify.argtypes = [ctypes.POINTER(VerifyDesc)] + [vp] * 8 + [sz, vp]
     lib.sv_verify_ex.restype = ctypes.c_int
     lib.sv_verify_ex.argtypes = [ctypes.POINTER(VerifyDesc)] + [vp] * 8 + [pr, vp, sz, vp]
+    lib.sv_verify_noalloc.restype = ctypes.c_int
+    lib.sv_verify_noalloc.argtypes = [ctypes.POINTER(VerifyDesc)] + [vp] * 8
     lib.sv_vat_workspace_bytes.restype = sz
     lib.sv_vat_workspace_bytes.argtypes = [ctypes.POINTER(VatDesc)]
     lib.sv_vat_labels.restype = ctypes.c_int
@@ -321,6 +324,39 @@ def verify(target, draft, draft_tokens, uniforms, temperature: float, *, onehot:
     """
     return Verifier(target, draft, draft_tokens, uniforms, temperature, onehot=onehot, return_probs=return_probs,
                     return_row_stats=return_row_stats, workspace=workspace)()
+
+
+def verify_noalloc(target, draft, draft_tokens, uniforms, temperature: float, *, onehot: bool = False,
+                   return_probs: bool = False, stream: Optional[int] = None) -> VerifyOutput:
+    """sv_verify_noalloc on torch tensors: as :func:`verify`, with the
+    library's built-in per-device workspace instead of one passed in (the
+    call itself allocates nothing on the device; the output tensors are
+    allocated here).  Calls that overlap on one device must not be issued."""
+    torch = _torch()
+    lib = load_library()
+    B, kp1, V = (int(s) for s in target.shape)
+    k = kp1 - 1
+    device = target.device
+    greedy = float(temperature) == 0.0
+    uses_draft = (not onehot) and not greedy
+    _check_dev("target", target, device)
+    if uses_draft:
+        _check_dev("draft", draft, device, target.dtype, (B, k, V))
+    _check_dev("draft_tokens", draft_tokens, device, torch.int32, (B, k))
+    if not greedy:
+        _check_dev("uniforms", uniforms, device, torch.float32, (B, k + 1))
+    desc = VerifyDesc(B, k, V, _dtype_code(target), SV_DRAFT_ONEHOT if onehot else SV_DRAFT_LOGITS,
+                      float(temperature))
+    acc = torch.empty(B, dtype=torch.int32, device=device)
+    out = torch.empty((B, k + 1), dtype=torch.int32, device=device)
+    probs = torch.empty((B, k, 2), dtype=torch.float32, device=device) if return_probs else None
+    s = _stream_handle(device) if stream is None else stream
+    st = lib.sv_verify_noalloc(ctypes.byref(desc), _ptr(target), _ptr(draft) if uses_draft else None,
+                               _ptr(draft_tokens), _ptr(uniforms) if not greedy else None, _ptr(acc), _ptr(out),
+                               _ptr(probs), s)
+    if st:
+        raise SVError(st, "sv_verify_noalloc", lib)
+    return VerifyOutput(acc, out, probs, None)
 
 
 class VatOutput(NamedTuple):

@@ -375,6 +375,8 @@ const char* sv_status_str(sv_status status) {
         case SV_ERR_BAD_CONTROL: return "SV_ERR_BAD_CONTROL: need 0 <= down_frac < up_frac <= 1";
         case SV_ERR_MISALIGNED: return "SV_ERR_MISALIGNED: hidden_states and weight must be 16-byte aligned";
         case SV_ERR_CAPTURING: return "SV_ERR_CAPTURING: tagged calls cannot be captured into a HIP graph";
+        case SV_ERR_SCRATCH_TOO_SMALL:
+            return "SV_ERR_SCRATCH_TOO_SMALL: the call needs more than the built-in workspace (SV_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -398,6 +400,26 @@ sv_status sv_verify_ex(const sv_verify_desc* desc, const void* target_logits, co
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return sv::verify_impl(desc, target_logits, draft_logits, draft_tokens, uniforms, accepted_len, out_tokens,
                            probs_out, row_stats_out, probe, workspace, workspace_bytes, stream);
+}
+
+sv_status sv_verify_noalloc(const sv_verify_desc* desc, const void* target_logits, const void* draft_logits,
+                            const int32_t* draft_tokens, const float* uniforms, int32_t* accepted_len,
+                            int32_t* out_tokens, float* probs_out, hipStream_t stream) {
+    static_assert(sv::kNoAllocScratchBytes == SV_NOALLOC_SCRATCH_BYTES, "scratch size");
+    sv::Shape s;
+    const sv_status st = sv::verify_shape(desc, &s);
+    if (st != SV_OK) return st;
+    if (s.batch == 0) return SV_OK;
+    if (sv::workspace_bytes_for(s) > sv::kNoAllocScratchBytes) return SV_ERR_SCRATCH_TOO_SMALL;
+    if (!target_logits || !draft_tokens || !accepted_len || !out_tokens) return SV_ERR_NULL_ARG;
+    if (!s.greedy && !uniforms) return SV_ERR_NULL_ARG;
+    if (s.rows_d && !draft_logits) return SV_ERR_NULL_ARG;
+    const sv_status cs = sv::capture_check(stream);
+    if (cs != SV_OK) return cs;
+    void* scratch = nullptr;
+    if (sv::noalloc_scratch(stream, &scratch) != hipSuccess) return SV_ERR_HIP;
+    return sv::verify_impl(desc, target_logits, draft_logits, draft_tokens, uniforms, accepted_len, out_tokens,
+                           probs_out, nullptr, nullptr, scratch, sv::kNoAllocScratchBytes, stream);
 }
 
 size_t sv_vat_workspace_bytes(const sv_vat_desc* desc) {

@@ -45,6 +45,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 
 #include "sv_launch.h"
 
@@ -1857,6 +1858,58 @@ int blocks_per_cu_typed() {
 int verify_blocks_per_cu(int elem_bytes, bool vec) {
     if (elem_bytes == 2) return vec ? blocks_per_cu_typed<2, true>() : blocks_per_cu_typed<2, false>();
     return vec ? blocks_per_cu_typed<4, true>() : blocks_per_cu_typed<4, false>();
+}
+
+// ------------------------------------------------------------------ built-in scratch
+
+namespace {
+
+// The workspace of sv_verify_noalloc: one array per device, in the code
+// object's own device memory, held until the process ends.  Host code never
+// uses the array's name as an address (it is a host-side stand-in): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Zero-fill of a buffer of 16-byte words (the scratch starts at zero, so
+// that no hand-off word in it carries a live call tag).
+__global__ __launch_bounds__(kBlock) void k_fill_zero(uint4* p, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * kBlock)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+constexpr int kMaxScratchDevices = 64;
+
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+
+ScratchSlot g_scratch[kMaxScratchDevices];
+
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&] {
+        void* p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (slot.err != hipSuccess) return;
+        // Cleared once with a kernel on the first call's stream, ordered
+        // before that call's own launch; later calls leave it ready (tags).
+        constexpr int64_t n = kNoAllocScratchBytes / 16;
+        hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(kBlock), 0, stream, static_cast<uint4*>(p), n);
+        slot.err = hipGetLastError();
+        if (slot.err == hipSuccess) slot.ptr = p;
+    });
+    if (slot.err != hipSuccess) return slot.err;
+    *ptr = slot.ptr;
+    return hipSuccess;
 }
 
 hipError_t launch_path(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {

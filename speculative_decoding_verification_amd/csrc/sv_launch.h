@@ -155,6 +155,14 @@ constexpr int kPairWords = 5;
 // Enqueue the whole path on `stream`.  Returns hipSuccess or the first error.
 hipError_t launch_path(const Plan& plan, hipStream_t stream, hipEvent_t probe_start, hipEvent_t probe_stop);
 
+// Size of the built-in workspace of sv_verify_noalloc (SV_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kNoAllocScratchBytes = size_t{8} << 20;
+
+// Device address of the current device's built-in workspace, set up (address
+// looked up, zero-filled by a kernel on `stream`) on the first call per
+// device.
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+
 // Histogram of accepted lengths into hist[0 .. k+3] (one block).
 hipError_t launch_accept_hist(const int32_t* acc, int32_t batch, int32_t k, int32_t* hist, hipStream_t stream);
 
