@@ -52,26 +52,33 @@ struct Shape {
     int64_t chunk, chunks;
     bool greedy, onehot, vat;
     bool loss;  // VAT with the training loss
+    int path() const {
+        if (loss) return kPathVatLoss;
+        if (vat) return greedy ? kPathVatGreedy : kPathVat;
+        if (greedy) return kPathGreedy;
+        return onehot ? kPathOneHot : kPathSample;
+    }
 };
 
 // Blocks of k_verify the current device holds at once: its compute units
 // times the kernel's occupancy per unit (queried once per device).
 int64_t resident_blocks(const Shape& s, bool vec) {
     constexpr int kMaxDevices = 64;
-    static std::atomic<int64_t> cache[kMaxDevices][2][2];
+    constexpr int kPaths = kPathVatLoss + 1;
+    static std::atomic<int64_t> cache[kMaxDevices][2][2][kPaths];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
-    const int e = s.elem_bytes == 2 ? 1 : 0, v = vec ? 1 : 0;
+    const int e = s.elem_bytes == 2 ? 1 : 0, v = vec ? 1 : 0, m = s.path();
     if (dev >= 0) {
-        const int64_t c = cache[dev][e][v].load(std::memory_order_relaxed);
+        const int64_t c = cache[dev][e][v][m].load(std::memory_order_relaxed);
         if (c > 0) return c;
     }
     int cus = 0;
     if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         cus = kDefaultComputeUnits;
-    const int per_cu = verify_blocks_per_cu(s.elem_bytes, vec);
+    const int per_cu = verify_blocks_per_cu(s.elem_bytes, vec, m);
     const int64_t r = static_cast<int64_t>(cus) * (per_cu > 0 ? per_cu : kMinBlocksPerCu);
-    if (dev >= 0) cache[dev][e][v].store(r, std::memory_order_relaxed);
+    if (dev >= 0) cache[dev][e][v][m].store(r, std::memory_order_relaxed);
     return r;
 }
 
@@ -101,15 +108,31 @@ sv_status check_shape(int32_t batch, int32_t k, int32_t vocab, int32_t dtype, in
     return SV_OK;
 }
 
-// Tagged words of chunk partials: two per row chunk, or five per chunk pair
-// for the VAT loss.
-int64_t partial_words(const Shape& s) {
-    return s.loss ? s.batch * s.k * s.chunks * kPairWords : (s.rows_t + s.rows_d) * s.chunks * 2;
+// Chunks per wavefront of the decision and bonus workers.
+int chunks_per_wave(const Shape& s, int64_t resident) {
+    const int64_t dec_rows = s.loss ? s.k : s.k * (s.rows_d ? 2 : 1);
+    return s.batch * dec_rows * s.chunks <= kSmallCallWaves * resident ? kChunksPerWaveSmall : kChunksPerWave;
 }
 
-size_t workspace_bytes_for(const Shape& s) {
-    return workspace_layout(partial_words(s), s.batch, s.chunks).total;
+// Segments per row: one per decision worker block of four wavefronts.
+int64_t segments(const Shape& s, int nc) { return ceil_div(s.chunks, kWavesPerBlock * nc); }
+
+int64_t rows_per_seq(const Shape& s) {
+    const int64_t dec_rows = s.loss ? s.k : s.k * (s.rows_d ? 2 : 1);
+    return dec_rows + (s.vat ? 0 : 1);
 }
+
+// Tagged words: two per row chunk (five per chunk pair for the VAT loss),
+// two per row segment, one residual mass per chunk.  The workspace is sized
+// for the larger segment count (one chunk per wavefront), so that it does
+// not depend on the device.
+WorkspaceLayout layout_for(const Shape& s) {
+    const int64_t chunk_words = s.loss ? s.batch * s.k * s.chunks * kPairWords : s.batch * rows_per_seq(s) * s.chunks * 2;
+    const int64_t seg_words = s.loss ? 0 : s.batch * rows_per_seq(s) * segments(s, kChunksPerWaveSmall) * 2;
+    return workspace_layout(chunk_words, seg_words, s.batch, s.chunks);
+}
+
+size_t workspace_bytes_for(const Shape& s) { return layout_for(s).total; }
 
 bool fill_plan(const Shape& s, float temperature, float decay, bool vec, Plan* pl) {
     const int64_t resident = resident_blocks(s, vec);
@@ -120,35 +143,42 @@ bool fill_plan(const Shape& s, float temperature, float decay, bool vec, Plan* p
     pl->target_rows_per_seq = static_cast<int32_t>(s.target_rows_per_seq);
     pl->chunks = static_cast<int32_t>(s.chunks);
     pl->chunk = static_cast<int32_t>(s.chunk);
+    pl->path = s.path();
     // The VAT loss streams k chunk-pair "rows" (target row i with draft row i).
-    pl->dec_rows = static_cast<int32_t>(s.loss ? s.k : s.k + (s.rows_d ? s.k : 0));
-    pl->has_bonus = !s.vat;
-    pl->has_resid = !s.vat && !s.greedy && !s.onehot;
-    pl->rows_per_seq = pl->dec_rows + (pl->has_bonus ? 1 : 0);
-    pl->vat_loss = s.loss;
-    pl->words_per_seq = static_cast<int32_t>(s.loss ? s.k * s.chunks * kPairWords : pl->rows_per_seq * s.chunks * 2);
-    const bool small = s.batch * pl->dec_rows * s.chunks <= kSmallCallWaves * resident;
-    pl->nc_dec = small ? kChunksPerWaveSmall : kChunksPerWave;
+    pl->halves = (!s.loss && s.rows_d) ? 2 : 1;
+    pl->dec_rows = static_cast<int32_t>(s.loss ? s.k : s.k * pl->halves);
+    const bool has_bonus = !s.vat;
+    const bool has_resid = !s.vat && !s.greedy && !s.onehot;
+    pl->rows_per_seq = static_cast<int32_t>(rows_per_seq(s));
+    const int nc = chunks_per_wave(s, resident);
+    pl->nc_dec = nc;
     pl->nc_res = kChunksPerWaveResid;
-    pl->nc_bonus = std::min(pl->nc_dec, kChunksPerWaveBonus);
-    if (!plan_task_grid(pl->batch, static_cast<int64_t>(pl->dec_rows) * s.chunks, s.chunks, pl->has_resid,
-                        pl->has_bonus, kWavesPerBlock * pl->nc_dec, kWavesPerBlock * pl->nc_bonus,
+    pl->seg_chunks = kWavesPerBlock * nc;
+    pl->segs = static_cast<int32_t>(s.loss ? 1 : segments(s, nc));
+    pl->words_per_seq = static_cast<int32_t>(s.loss ? s.k * s.chunks * kPairWords : pl->rows_per_seq * s.chunks * 2);
+    pl->seg_words_per_seq = static_cast<int32_t>(s.loss ? 0 : pl->rows_per_seq * pl->segs * 2);
+    // A decision worker block covers one segment of one row (VAT loss: 4 nc
+    // chunk pairs); a bonus worker one segment of the bonus row.
+    const int64_t per_block = kWavesPerBlock * nc;
+    const int64_t dec_items = s.loss ? s.k * s.chunks : static_cast<int64_t>(pl->dec_rows) * pl->segs * per_block;
+    if (!plan_task_grid(pl->batch, dec_items, s.chunks, has_resid, has_bonus, per_block, per_block,
                         kWavesPerBlock * pl->nc_res, resident, &pl->grid))
         return false;
-    // Two reads in flight per poll only when (nearly) the whole grid is
-    // resident at once: no stream is left for the extra reads to slow down.
-    // A quarter of a residency over is allowed for the finisher and bonus
-    // blocks that follow a one-residency stream.
+    // Every decision worker block before every finisher: position-major.
+    pl->pos_major = !s.loss && pl->grid.lag_a >= pl->batch;
+    // Short polling sleeps only when (nearly) the whole grid is resident at
+    // once: no stream is left for the extra reads to slow down.  A quarter
+    // of a residency over is allowed for the finisher and bonus blocks that
+    // follow a one-residency stream.
     pl->two_deep_polls = pl->grid.total_blocks <= resident + resident / 4;
     // The decisions of the sequences in the last residency of phase A come
     // after the bonus phase has started; their bonus rows are read without
-    // waiting, so that reading them is not added to the end of the chain.
+    // deciding first, so that reading them is not added to the end of the
+    // chain.
     pl->eager_bonus_from = std::max(0, pl->batch - pl->grid.lag_a);
     pl->rows_t = s.rows_t;
     pl->rows_d = s.rows_d;
     pl->greedy = s.greedy;
-    pl->onehot = s.onehot;
-    pl->vat = s.vat;
     pl->temperature = temperature;
     pl->c2 = s.greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
     pl->decay = decay;
@@ -156,11 +186,11 @@ bool fill_plan(const Shape& s, float temperature, float decay, bool vec, Plan* p
 }
 
 void carve_workspace(const Shape& s, void* ws, Plan* pl) {
-    const WorkspaceLayout L = workspace_layout(partial_words(s), s.batch, s.chunks);
+    const WorkspaceLayout L = layout_for(s);
     char* base = static_cast<char*>(ws);
-    pl->partials = reinterpret_cast<uint64_t*>(base + L.partials);
+    pl->chunkw = reinterpret_cast<uint64_t*>(base + L.chunkw);
+    pl->segw = reinterpret_cast<uint64_t*>(base + L.segw);
     pl->resid = reinterpret_cast<uint64_t*>(base + L.resid);
-    pl->dec = reinterpret_cast<uint64_t*>(base + L.dec);
     pl->tag = next_tag();
 }
 
@@ -238,15 +268,15 @@ LmGemm lm_gemm(const void* a, const void* w, int64_t rows, int64_t out_row0, int
 
 }  // namespace
 
-WorkspaceLayout workspace_layout(int64_t partial_words, int64_t batch, int64_t chunks) {
+WorkspaceLayout workspace_layout(int64_t chunk_words, int64_t seg_words, int64_t batch, int64_t chunks) {
     WorkspaceLayout L;
     size_t off = 0;
-    L.partials = off;
-    off = align_up(off + static_cast<size_t>(partial_words) * sizeof(uint64_t));
+    L.chunkw = off;
+    off = align_up(off + static_cast<size_t>(chunk_words) * sizeof(uint64_t));
+    L.segw = off;
+    off = align_up(off + static_cast<size_t>(seg_words) * sizeof(uint64_t));
     L.resid = off;
-    off = align_up(off + static_cast<size_t>(batch * chunks) * sizeof(uint64_t));
-    L.dec = off;
-    off = align_up(off + static_cast<size_t>(batch) * kDecWords * sizeof(uint64_t));
+    off = align_up(off + static_cast<size_t>(batch * (chunks + 1)) * sizeof(uint64_t));
     L.total = off;
     return L;
 }

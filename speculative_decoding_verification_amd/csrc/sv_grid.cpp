@@ -123,15 +123,15 @@ bool plan_task_grid(int32_t batch, int64_t dec_items, int64_t chunks, bool has_r
     const int64_t w_res = has_resid ? ceil_div(chunks, per_block_res) : 0;
     const int64_t w_bonus = has_bonus ? ceil_div(chunks, per_block_bonus) : 0;
     if (w_dec > 0x7fffffffLL || w_res > 0x7fffffffLL || w_bonus > 0x7fffffffLL) return false;
-    // A finisher goes about one residency of blocks after its workers, the
-    // residual workers half a residency after the decision, the residual
-    // finisher half a residency after its workers.
+    // A finisher goes about one residency of blocks after its workers; the
+    // residual workers go with the decision finisher (each decides for
+    // itself), the residual finisher half a residency after them.
     const int64_t group_a = w_dec + 1 + (has_resid ? w_res + 1 : 0);
     const auto lag = [&](int64_t blocks, int64_t group) {
         return static_cast<int32_t>(std::min<int64_t>(batch, ceil_div(blocks, group)));
     };
     const int32_t lag_a = lag(resident_blocks, group_a);
-    const int32_t lag_r = has_resid ? lag(resident_blocks / 2, group_a) : 0;
+    const int32_t lag_r = 0;
     const int32_t lag_f = has_resid ? lag(resident_blocks / 2, group_a) : 0;
     const int32_t lag_b = has_bonus ? lag(resident_blocks, w_bonus + 1) : 0;
     return build_task_grid(batch, static_cast<int32_t>(w_dec), static_cast<int32_t>(w_res),

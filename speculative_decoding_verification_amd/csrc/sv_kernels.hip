@@ -505,6 +505,7 @@ struct PartialSrc {
 
 struct TailShared {
     uint32_t stage[kStageWords];   // staged hand-off words
+    float2 segp[kWavesPerBlock * kChunksPerWave];  // a segment's chunk partials (decision and bonus workers)
     float2 mz[2 * kMaxDraft + 1];  // (m, Z) or (max, argmax) of the sequence's rows
     float xs[kMaxDraft];           // VAT loss: sum_y p(y) (l_d(y) - m_d) c2, times Z_t
     float wt[kWavesPerBlock];      // block scan scratch
@@ -831,33 +832,100 @@ __device__ __forceinline__ int draw_token(const DrawRow& d, float u, int P, int6
     return draw_scan<EB>(pk, w, sh);
 }
 
-// ------------------------------------------------------------------ task grid
+// ------------------------------------------------------------------ specialisations
+
+template <int MODE>
+struct PathTraits {
+    static constexpr bool greedy = MODE == kPathGreedy || MODE == kPathVatGreedy;
+    static constexpr bool vat = MODE == kPathVat || MODE == kPathVatGreedy || MODE == kPathVatLoss;
+    static constexpr bool loss = MODE == kPathVatLoss;
+    static constexpr bool onehot = MODE == kPathOneHot;
+    static constexpr bool resid = MODE == kPathSample;      // residual draws after a rejection
+    static constexpr bool bonus = !vat;                      // the bonus row and its draw
+    static constexpr int halves = (MODE == kPathSample || MODE == kPathVat) ? 2 : 1;
+};
+
+// ------------------------------------------------------------------ rows and words
 
 // Global row (the numbering of row_stats_out) of local row j of sequence b.
 __device__ __forceinline__ int64_t global_row(const Plan& pl, int b, int j) {
-    const int k = pl.k;
-    const int n_t = pl.target_rows_per_seq;
-    if (j < k) return static_cast<int64_t>(b) * n_t + j;
-    if (j < pl.dec_rows) return pl.rows_t + static_cast<int64_t>(b) * k + (j - k);
-    return static_cast<int64_t>(b) * n_t + k;
+    if (j < pl.dec_rows) {
+        const int i = j / pl.halves;
+        if (j == i * pl.halves) return static_cast<int64_t>(b) * pl.target_rows_per_seq + i;
+        return pl.rows_t + static_cast<int64_t>(b) * pl.k + i;
+    }
+    return static_cast<int64_t>(b) * pl.target_rows_per_seq + pl.k;
 }
 
-__device__ __forceinline__ uint64_t* seq_words(const Plan& pl, int b) {
-    return pl.partials + static_cast<int64_t>(b) * pl.words_per_seq;
+// Chunk words of sequence b: two per chunk of each local row, row-major.
+__device__ __forceinline__ uint64_t* chunk_words(const Plan& pl, int b) {
+    return pl.chunkw + static_cast<int64_t>(b) * pl.words_per_seq;
 }
+
+// Segment words of sequence b: two per segment of each local row, row-major.
+__device__ __forceinline__ uint64_t* seg_words(const Plan& pl, int b) {
+    return pl.segw + static_cast<int64_t>(b) * pl.seg_words_per_seq;
+}
+
+// Residual masses of sequence b (one per chunk), then its decision word:
+// r + 2, from the decision finisher, for the bonus workers that wait for it.
+__device__ __forceinline__ uint64_t* resid_words(const Plan& pl, int b) {
+    return pl.resid + static_cast<int64_t>(b) * (pl.chunks + 1);
+}
+
+__device__ __forceinline__ uint64_t* decision_word(const Plan& pl, int b) { return resid_words(pl, b) + pl.chunks; }
 
 // ------------------------------------------------------------------ workers
 
-// Partial of chunk c of local row j of sequence b, handed off as two words.
-template <int EB, bool VEC>
-__device__ __forceinline__ void stream_chunk(const Plan& pl, int b, int j, int c) {
+// Merges chunk partials (m, s) -- or (max, index) at T == 0 -- in order.
+__device__ __forceinline__ float2 merge_partial(float2 a, float2 b, bool greedy, float c2) {
+    if (greedy) {
+        float best = a.x;
+        int idx = __float_as_int(a.y);
+        argmax_step(best, idx, b.x, __float_as_int(b.y));
+        return make_float2(best, __int_as_float(idx));
+    }
+    if (b.x == neg_inf()) return a;
+    if (a.x == neg_inf()) return b;
+    const float m = fmaxf(a.x, b.x);
+    return make_float2(m, a.y * exp2_hw((a.x - m) * c2) + b.y * exp2_hw((b.x - m) * c2));
+}
+
+// One segment of local row j of sequence b: wavefront w streams chunks
+// c0 + w + 4n (n < nc_dec) of the segment, each handed off as two chunk
+// words; after one barrier, thread 0 merges the segment's chunk partials in
+// chunk order and hands off the segment partial as two segment words.  The
+// finishers poll segment words only (a few per row); the draws read the
+// chunk words of the one row they draw from.  Whole block.
+template <int EB, bool VEC, int MODE>
+__device__ __forceinline__ void stream_segment(const Plan& pl, int b, int j, int s, TailShared& sh) {
+    using Tr = PathTraits<MODE>;
     const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int P = pl.chunks;
+    const int c0 = s * pl.seg_chunks;
+    const int c1 = min(P, c0 + pl.seg_chunks);
     const char* rp = row_of<EB>(pl, global_row(pl, b, j));
-    const int64_t start = static_cast<int64_t>(c) * Chunk<EB>::kElems;
-    const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), pl.vocab - start));
-    const float2 part = pl.greedy ? chunk_argmax<EB, VEC>(rp, start, len, lane)
-                                  : chunk_stats<EB, VEC>(rp, start, len, lane, pl.c2);
-    if (lane == 0) put_partial(seq_words(pl, b), j * pl.chunks + c, part, pl.tag);
+    uint64_t* cw = chunk_words(pl, b) + static_cast<int64_t>(j) * P * 2;
+#pragma unroll 1
+    for (int n = 0; n < pl.nc_dec; ++n) {
+        const int c = c0 + wave + n * kWavesPerBlock;
+        if (c >= c1) break;
+        const int64_t start = static_cast<int64_t>(c) * Chunk<EB>::kElems;
+        const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), pl.vocab - start));
+        const float2 part = Tr::greedy ? chunk_argmax<EB, VEC>(rp, start, len, lane)
+                                       : chunk_stats<EB, VEC>(rp, start, len, lane, pl.c2);
+        if (lane == 0) {
+            put_partial(cw, c, part, pl.tag);
+            sh.segp[c - c0] = part;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float2 acc = sh.segp[0];
+        for (int q = 1; q < c1 - c0; ++q) acc = merge_partial(acc, sh.segp[q], Tr::greedy, pl.c2);
+        put_partial(seg_words(pl, b) + static_cast<int64_t>(j) * pl.segs * 2, s, acc, pl.tag);
+    }
 }
 
 // Residual mass of chunk [start, start+len) of a target/draft row pair, in
@@ -1040,7 +1108,7 @@ __device__ __forceinline__ void stream_pair(const Plan& pl, int b, int i, int c)
     }
     acc = wave_merge_pair(acc, c2);
     if (lane == 0) {
-        uint64_t* w = seq_words(pl, b) + (static_cast<int64_t>(i) * pl.chunks + c) * kPairWords;
+        uint64_t* w = chunk_words(pl, b) + (static_cast<int64_t>(i) * pl.chunks + c) * kPairWords;
         put_word(w + 0, __float_as_uint(acc.mt), pl.tag);
         put_word(w + 1, __float_as_uint(acc.st), pl.tag);
         put_word(w + 2, __float_as_uint(acc.md), pl.tag);
@@ -1049,43 +1117,16 @@ __device__ __forceinline__ void stream_pair(const Plan& pl, int b, int i, int c)
     }
 }
 
-// ------------------------------------------------------------------ decision words
-
-struct Decision {
-    int r;     // first rejection (k if none), -1 invalid, -2 timed out
-    int mode;  // SampleMode
-    float2 mzt, mzd;
-    float u;
-};
-
-__device__ __forceinline__ void put_decision(const Plan& pl, int b, const Decision& d) {
-    uint64_t* w = pl.dec + static_cast<int64_t>(b) * kDecWords;
-    put_word(w + kDecRMode, static_cast<uint32_t>(d.r + 2) | (static_cast<uint32_t>(d.mode) << 16), pl.tag);
-    put_word(w + kDecMt, __float_as_uint(d.mzt.x), pl.tag);
-    put_word(w + kDecZt, __float_as_uint(d.mzt.y), pl.tag);
-    put_word(w + kDecMd, __float_as_uint(d.mzd.x), pl.tag);
-    put_word(w + kDecZd, __float_as_uint(d.mzd.y), pl.tag);
-    put_word(w + kDecU, __float_as_uint(d.u), pl.tag);
-}
-
-// From staged decision words (after collect).
-__device__ __forceinline__ Decision read_decision(const uint32_t* st) {
-    Decision d;
-    d.r = static_cast<int>(st[kDecRMode] & 0xffffu) - 2;
-    d.mode = static_cast<int>(st[kDecRMode] >> 16);
-    d.mzt = make_float2(__uint_as_float(st[kDecMt]), __uint_as_float(st[kDecZt]));
-    d.mzd = make_float2(__uint_as_float(st[kDecMd]), __uint_as_float(st[kDecZd]));
-    d.u = __uint_as_float(st[kDecU]);
-    return d;
-}
-
 // ------------------------------------------------------------------ finishers
 
-// Marks a sequence whose finisher gave up waiting (see kPollTimeoutTicks).
+// Marks a sequence whose decision's wait ran out (see kPollTimeoutTicks).
+// Only the decision finisher, which owns these outputs, calls it.
+template <int MODE>
 __device__ __forceinline__ void fail_sequence(const Plan& pl, int b) {
+    using Tr = PathTraits<MODE>;
     const int k = pl.k;
     for (int j = threadIdx.x; j <= k; j += kBlock) {
-        if (pl.vat) {
+        if constexpr (Tr::vat) {
             if (j < k) {
                 pl.mask[static_cast<int64_t>(b) * k + j] = 0;
                 pl.weights[static_cast<int64_t>(b) * k + j] = 0.f;
@@ -1095,12 +1136,12 @@ __device__ __forceinline__ void fail_sequence(const Plan& pl, int b) {
         }
     }
     if (threadIdx.x == 0) {
-        if (pl.vat) pl.first_reject[b] = -2;
+        if constexpr (Tr::vat) pl.first_reject[b] = -2;
         else pl.accepted_len[b] = -2;
     }
 }
 
-// Row (m, Z) -- or (max, argmax) at T == 0 -- of local row j from its chunk
+// Row (m, Z) -- or (max, argmax) at T == 0 -- of local row j from its P
 // partials; one wave.  Result on every lane.
 __device__ __forceinline__ float2 combine_row(const PartialSrc& src, int j, int P, bool greedy, float c2) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -1115,40 +1156,31 @@ __device__ __forceinline__ float2 combine_row(const PartialSrc& src, int j, int 
         return make_float2(best, __int_as_float(bi));
     }
     float m = neg_inf(), s = 0.f;
-    if (P <= kWave) {
-        if (lane < P) {
-            const float2 pc = src.get(j * P + lane);
+    for (int c = lane; c < P; c += kWave) {
+        const float2 pc = src.get(j * P + c);
+        if (pc.x == neg_inf()) continue;
+        if (pc.x > m) {
+            s = (m == neg_inf() ? 0.f : s * exp2_hw((m - pc.x) * c2)) + pc.y;
             m = pc.x;
-            s = pc.y;
-        }
-    } else {
-        for (int c = lane; c < P; c += kWave) {
-            const float2 pc = src.get(j * P + c);
-            if (pc.x == neg_inf()) continue;
-            if (pc.x > m) {
-                s = (m == neg_inf() ? 0.f : s * exp2_hw((m - pc.x) * c2)) + pc.y;
-                m = pc.x;
-            } else {
-                s += pc.y * exp2_hw((pc.x - m) * c2);
-            }
+        } else {
+            s += pc.y * exp2_hw((pc.x - m) * c2);
         }
     }
     wave_merge_ms(m, s, c2);
     return make_float2(m, s);
 }
 
-// (m, Z) -- or (max, argmax) at T == 0 -- of local rows 0..n_rows-1 at once:
-// each row on the 16 lanes of one DPP row (16 rows per pass over the block),
-// a lane merging chunks sub, sub+16, ... in order, then four DPP steps inside
-// the row.  No readlane and no cross-row step, so all rows of a sequence are
-// combined in about the time one wave-wide merge takes.  Lane 0 of each row
-// writes mz[j].  Whole block.
-__device__ __forceinline__ void combine_rows(const PartialSrc& src, int n_rows, int P, bool greedy, float c2,
+// (m, Z) -- or (max, argmax) at T == 0 -- of local rows [j0, j1) from their
+// P partials each: every row on the 16 lanes of one DPP row (16 rows per pass
+// over the block), a lane merging partials sub, sub+16, ... in order, then
+// four DPP steps inside the row.  No readlane and no cross-row step.  Lane 0
+// of each row writes mz[j].  Whole block.
+__device__ __forceinline__ void combine_rows(const PartialSrc& src, int j0, int j1, int P, bool greedy, float c2,
                                              float2* mz) {
     const int sub = threadIdx.x & 15;
-    for (int j0 = 0; j0 < n_rows; j0 += kBlock / 16) {
-        const int j = j0 + static_cast<int>(threadIdx.x / 16);
-        const bool on = j < n_rows;
+    for (int jb = j0; jb < j1; jb += kBlock / 16) {
+        const int j = jb + static_cast<int>(threadIdx.x / 16);
+        const bool on = j < j1;
         if (greedy) {
             float best = neg_inf();
             int bi = INT_MAX;
@@ -1197,6 +1229,140 @@ __device__ __forceinline__ void write_row_stats(const Plan& pl, int64_t grow, fl
     pl.row_stats_out[2 * grow + 1] = pl.greedy ? static_cast<float>(__float_as_int(res.y)) : res.y;
 }
 
+// Block-wide minimum of one int per thread.  Whole block.
+__device__ __forceinline__ int block_min(int v, int* flags) {
+    const int w = wave_min_i(v);
+    if ((threadIdx.x & (kWave - 1)) == 0) flags[threadIdx.x / kWave] = w;
+    __syncthreads();
+    int m = flags[0];
+#pragma unroll
+    for (int q = 1; q < kWavesPerBlock; ++q) m = min(m, flags[q]);
+    __syncthreads();
+    return m;
+}
+
+// Per-position values a decision needs, held by wave 0 (lane i: position i).
+struct PosRegs {
+    int x;         // draft token
+    float u;       // the uniform of its test
+    float lt, ld;  // target and draft logits at the token (T > 0)
+    float p, q;    // p_i(x_i), q_i(x_i) once the position is tested
+    bool active;   // wave 0, lane < k
+    bool bad;      // token outside [0, V)
+};
+
+// Loads that do not depend on any partial, issued before the polling: the
+// token and uniform of each position, and (T > 0) the logits at the token
+// (index clamped into the row; an invalid token flags the sequence).
+template <int EB, int MODE>
+__device__ __forceinline__ PosRegs load_positions(const Plan& pl, int b) {
+    using Tr = PathTraits<MODE>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int k = pl.k;
+    const int64_t V = pl.vocab;
+    PosRegs pr;
+    pr.x = 0;
+    pr.u = pr.lt = pr.ld = 0.f;
+    pr.p = pr.q = __builtin_nanf("");
+    pr.active = threadIdx.x < kWave && lane < k;
+    if (pr.active) {
+        pr.x = pl.tokens[static_cast<int64_t>(b) * k + lane];
+        if (!Tr::greedy) pr.u = pl.uniforms[static_cast<int64_t>(b) * (Tr::vat ? k : k + 1) + lane];
+    }
+    pr.bad = pr.active && (pr.x < 0 || pr.x >= pl.vocab);
+    if (!Tr::greedy && pr.active) {
+        const int xc = min(max(pr.x, 0), pl.vocab - 1);
+        pr.lt = Elem<EB>::at(row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + lane, V, EB), xc);
+        if (Tr::halves == 2) pr.ld = Elem<EB>::at(row_base(pl.draft, static_cast<int64_t>(b) * k + lane, V, EB), xc);
+    }
+    return pr;
+}
+
+// The test of position i (wave 0, lane i): u q(x) < p(x), taken in the log2
+// domain so that probabilities below the fp32 range still decide correctly;
+// at T == 0, x_i == the row's lowest-index argmax.  Sets pr.p, pr.q.
+template <int MODE>
+__device__ __forceinline__ bool test_position(const Plan& pl, const TailShared& sh, PosRegs& pr, int i) {
+    using Tr = PathTraits<MODE>;
+    constexpr int H = Tr::halves;
+    if constexpr (Tr::greedy) {
+        const bool keep = pr.x == __float_as_int(sh.mz[i * H].y);
+        pr.p = keep ? 1.f : 0.f;
+        pr.q = 1.f;
+        return keep;
+    } else {
+        const float2 mzt = sh.mz[i * H];
+        const float lp = (pr.lt - mzt.x) * pl.c2 - log2_hw(mzt.y);
+        float lq = 0.f;
+        if constexpr (H == 2) {
+            const float2 mzd = sh.mz[i * H + 1];
+            lq = (pr.ld - mzd.x) * pl.c2 - log2_hw(mzd.y);
+        }
+        pr.p = exp2_hw(lp);
+        pr.q = exp2_hw(lq);
+        return log2_hw(pr.u) + lq < lp;
+    }
+}
+
+// The decision of sequence b, taken by every block that needs it (decision
+// finisher, residual and bonus roles), so that none of them waits on
+// another: polls the sequence's segment words, and as soon as all segments
+// of the next positions are there combines their rows and tests them in
+// order; stops at the first rejection unless every position is asked for
+// (`all`: row statistics or probabilities of every position).  Returns r in
+// [0, k] (k: all kept), -1 (a token outside [0, V)) or -2 (the wait ran
+// out); leaves the combined rows in sh.mz (local row numbering) and the
+// tested positions' p_i(x_i), q_i(x_i) in pr.  Whole block.
+template <int EB, bool VEC, int MODE>
+__device__ __forceinline__ int decide(const Plan& pl, int b, TailShared& sh, bool all, PosRegs& pr, uint64_t timeout) {
+    using Tr = PathTraits<MODE>;
+    constexpr int H = Tr::halves;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int k = pl.k;
+    const int S = pl.segs;
+    const int per_pos = 2 * H * S;
+    const int n_words = k * per_pos;
+    const uint64_t* words = seg_words(pl, b);
+    const bool staged = n_words <= kStageWords;
+    const PartialSrc src{staged ? sh.stage : nullptr, words};
+    if (threadIdx.x < kWave) {
+        const bool invalid = __ballot(pr.bad) != 0ull;
+        if (lane == 0) sh.r = invalid ? -1 : k;
+    }
+    __syncthreads();
+    int r = sh.r;
+    if (r < 0) return -1;
+    int done = 0;
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+        int miss = k;  // first position with a segment word not yet there
+        for (int w = done * per_pos + static_cast<int>(threadIdx.x); w < n_words; w += kBlock) {
+            const uint64_t v = get_word(words + w);
+            if (static_cast<uint32_t>(v >> 32) != pl.tag) miss = min(miss, w / per_pos);
+            else if (staged) sh.stage[w] = word_data(v);
+        }
+        const int f = block_min(miss, sh.vote);
+        if (f > done) {
+            combine_rows(src, done * H, f * H, S, Tr::greedy, pl.c2, sh.mz);
+            __syncthreads();
+            if (threadIdx.x < kWave) {
+                const bool in = lane >= done && lane < f;
+                bool keep = true;
+                if (in) keep = test_position<MODE>(pl, sh, pr, lane);
+                const uint64_t rej = __ballot(in && !keep);
+                if (lane == 0 && rej && r == k) sh.r = __builtin_ctzll(rej);
+            }
+            __syncthreads();
+            r = sh.r;
+            done = f;
+        }
+        if (done == k || (r < k && !all)) return r;
+        // waves read the clock at slightly different times: decide together
+        if (block_any(wall_clock64() - t0 > timeout, sh.vote)) return -2;
+        __builtin_amdgcn_s_sleep(4);
+    }
+}
+
 // The draw of a one-hot draft rejected at r: target row r without x_r.
 template <int EB>
 __device__ __forceinline__ DrawRow onehot_row(const Plan& pl, int b, int r, const PartialSrc& src, float m_r, int x_r,
@@ -1206,7 +1372,7 @@ __device__ __forceinline__ DrawRow onehot_row(const Plan& pl, int b, int r, cons
     d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + r, pl.vocab, EB);
     d.rd = nullptr;
     d.part = src;
-    d.part_base = r * pl.chunks;
+    d.part_base = 0;
     d.rstage = nullptr;
     d.rwords = nullptr;
     d.c2 = pl.c2;
@@ -1217,12 +1383,13 @@ __device__ __forceinline__ DrawRow onehot_row(const Plan& pl, int b, int r, cons
     return d;
 }
 
-// Outputs of a sequence's decision, stored by wave 0 of its finisher (lane i
-// holds draft token x_i): accepted_len, out_tokens (x_0..x_{r-1}, -1 after
-// r; at r the greedy argmax, or `token` for a one-hot draw, else left to the
-// block that draws it) and the decision words later roles wait on.
-__device__ __forceinline__ void publish_decision(const Plan& pl, int b, int r, int mode, int x, float u_draw,
-                                                 int token, const TailShared& sh) {
+// accepted_len and out_tokens of a sequence, stored by wave 0 of its
+// decision finisher (lane i holds x_i): x_0..x_{r-1}, -1 after r, and at r
+// the greedy argmax or `token` (a one-hot draw); a residual or bonus token at
+// r is stored by the block that draws it.
+template <int MODE>
+__device__ __forceinline__ void publish_outputs(const Plan& pl, int b, int r, int x, int token, const TailShared& sh) {
+    using Tr = PathTraits<MODE>;
     const int lane = threadIdx.x & (kWave - 1);
     const int k = pl.k;
     int32_t* out = pl.out_tokens + static_cast<int64_t>(b) * (k + 1);
@@ -1230,106 +1397,46 @@ __device__ __forceinline__ void publish_decision(const Plan& pl, int b, int r, i
         if (r < 0) out[j] = -1;
         else if (j < r) out[j] = x;  // j < r <= k <= 64 here, so j == lane
         else if (j > r) out[j] = -1;
-        else if (pl.greedy && r < k) out[j] = __float_as_int(sh.mz[r].y);
-        else if (mode == kModeOneHot) out[j] = token;
+        else if (Tr::greedy && r < k) out[j] = __float_as_int(sh.mz[r].y);
+        else if (Tr::onehot && r < k) out[j] = token;
     }
-    if (lane == 0) {
-        pl.accepted_len[b] = r;
-        Decision d{};
-        d.r = r;
-        d.mode = mode;
-        d.u = u_draw;
-        if (r >= 0 && r < k) {
-            d.mzt = sh.mz[r];
-            if (!pl.onehot && !pl.greedy) d.mzd = sh.mz[k + r];
-        }
-        put_decision(pl, b, d);
-    }
+    if (lane == 0) pl.accepted_len[b] = r;
 }
 
-// Decision finisher of sequence b: everything that needs rows 0..k-1.
-template <int EB, bool VEC>
-__device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShared& sh) {
+// Decision finisher of sequence b: the outputs that depend on rows 0..k-1
+// (accepted prefix, VAT labels and weights, probabilities, row statistics)
+// and the one-hot draw.
+template <int EB, bool VEC, int MODE>
+__device__ __forceinline__ void decision_finisher(const Plan& pl, int b, TailShared& sh) {
+    using Tr = PathTraits<MODE>;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
     const int k = pl.k;
-    const int n_t = pl.target_rows_per_seq;
     const int P = pl.chunks;
     const int64_t V = pl.vocab;
-    const float c2 = pl.c2;
-    const int n_u = pl.vat ? k : k + 1;
-    const int dec_items = pl.dec_rows * P;
-    const uint64_t* words = seq_words(pl, b);
-    const bool sampling = !pl.vat && !pl.greedy;
-
-    // Loads that do not depend on the partials go out before the polling:
-    // one lane per position loads its token and uniform, then the two logits
-    // at the token (index clamped into the row; an invalid token flags the
-    // sequence below).
-    const bool active = wave == 0 && lane < k;
-    int x = 0;
-    float lt = 0.f, ld = 0.f, u = 0.f;
-    if (active) {
-        x = pl.tokens[static_cast<int64_t>(b) * k + lane];
-        if (!pl.greedy) u = pl.uniforms[static_cast<int64_t>(b) * n_u + lane];
-    }
-    const bool bad = active && (x < 0 || x >= pl.vocab);
-    if (active && !pl.greedy) {
-        const int xc = min(max(x, 0), pl.vocab - 1);
-        lt = Elem<EB>::at(row_base(pl.target, static_cast<int64_t>(b) * n_t + lane, V, EB), xc);
-        if (!pl.onehot) ld = Elem<EB>::at(row_base(pl.draft, static_cast<int64_t>(b) * k + lane, V, EB), xc);
-    }
-    const float u_draw = sampling ? pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k] : 0.f;
-
-    const bool staged = 2 * dec_items <= kStageWords;
-    if (!collect(words, 2 * dec_items, pl.tag, staged ? sh.stage : nullptr, sh.vote, pl.two_deep_polls)) {
-        fail_sequence(pl, b);
-        if (!pl.vat && threadIdx.x == 0) {
-            Decision d{};
-            d.r = -2;
-            d.mode = kModeDone;
-            put_decision(pl, b, d);
-        }
+    PosRegs pr = load_positions<EB, MODE>(pl, b);
+    const float u_draw = Tr::onehot ? pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k] : 0.f;
+    const bool all = pl.probs_out || pl.row_stats_out;
+    const int r = decide<EB, VEC, MODE>(pl, b, sh, all, pr, kPollTimeoutTicks);
+    if (r == -2) {
+        fail_sequence<MODE>(pl, b);
         return;
     }
-    const PartialSrc src{staged ? sh.stage : nullptr, words};
-
-    combine_rows(src, pl.dec_rows, P, pl.greedy, c2, sh.mz);
-    __syncthreads();
-    if (pl.row_stats_out)
+    if (pl.row_stats_out && r >= 0)
         for (int j = threadIdx.x; j < pl.dec_rows; j += kBlock) write_row_stats(pl, global_row(pl, b, j), sh.mz[j]);
-
-    if (wave == 0) {
+    const bool draws = Tr::onehot && r >= 0 && r < k;
+    // r for the bonus workers that read the bonus row only after full
+    // acceptance (after the one-hot draw when there is one: see below).
+    if (Tr::bonus && !draws && threadIdx.x == kWave)
+        put_word(decision_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
+    if (threadIdx.x < kWave) {
         const int i = lane;
-        const bool invalid = __ballot(bad) != 0ull;
-        bool keep = false;
-        float p = __builtin_nanf(""), q = __builtin_nanf("");
-        if (!invalid && active) {
-            if (pl.greedy) {
-                keep = (x == __float_as_int(sh.mz[i].y));
-                p = keep ? 1.f : 0.f;
-                q = 1.f;
-            } else {
-                // The test u*q < p, taken in the log2 domain so that
-                // probabilities below the fp32 range still decide correctly.
-                const float lp = (lt - sh.mz[i].x) * c2 - log2_hw(sh.mz[i].y);
-                const float lq = pl.onehot ? 0.f : (ld - sh.mz[k + i].x) * c2 - log2_hw(sh.mz[k + i].y);
-                keep = log2_hw(u) + lq < lp;
-                p = exp2_hw(lp);
-                q = exp2_hw(lq);
-            }
+        if (pl.probs_out && pr.active) {
+            pl.probs_out[2 * (static_cast<int64_t>(b) * k + i)] = pr.p;
+            pl.probs_out[2 * (static_cast<int64_t>(b) * k + i) + 1] = pr.q;
         }
-        const uint64_t kept = __ballot(keep);
-        const uint64_t lowk = (k == 64) ? ~0ull : ((1ull << k) - 1ull);
-        const uint64_t rej = ~kept & lowk;
-        const int r = invalid ? -1 : (rej ? __builtin_ctzll(rej) : k);
-
-        if (pl.probs_out && active) {
-            pl.probs_out[2 * (static_cast<int64_t>(b) * k + i)] = p;
-            pl.probs_out[2 * (static_cast<int64_t>(b) * k + i) + 1] = q;
-        }
-        if (pl.vat) {
-            if (active) {
+        if constexpr (Tr::vat) {
+            const bool invalid = r < 0;
+            if (pr.active) {
                 const int64_t o = static_cast<int64_t>(b) * k + i;
                 pl.mask[o] = static_cast<uint8_t>(!invalid && i < r);
                 // decay^(i-r) in fp64, rounded once to fp32
@@ -1340,44 +1447,48 @@ __device__ __forceinline__ void decide_sequence(const Plan& pl, int b, TailShare
             }
             if (lane == 0) pl.first_reject[b] = r;
         } else {
-            int mode = kModeDone;
-            if (!invalid && !pl.greedy) mode = r == k ? kModeBonus : (pl.onehot ? kModeOneHot : kModeResidual);
-            if (lane == 0) {
-                sh.r = r;
-                sh.mode = mode;
-                sh.x_r = (r >= 0 && r < k) ? __builtin_amdgcn_readlane(x, r) : -1;
-                sh.l_x = (r >= 0 && r < k) ? readlane(lt, r) : 0.f;
+            // A one-hot draw is taken by this block before anything else is
+            // stored: loads behind this wave's write-through stores would
+            // wait for their acknowledgements as well.
+            if (!draws) {
+                publish_outputs<MODE>(pl, b, r, pr.x, -1, sh);
+            } else {
+                const int x_r = __builtin_amdgcn_readlane(pr.x, r);
+                const float l_x = readlane(pr.lt, r);
+                if (lane == 0) {
+                    sh.x_r = x_r;
+                    sh.l_x = l_x;
+                }
             }
-            // A one-hot draw is taken by this block before anything is
-            // stored: loads that wait behind this wave's write-through
-            // stores would wait for their acknowledgements as well.
-            if (mode != kModeOneHot) publish_decision(pl, b, r, mode, x, u_draw, -1, sh);
         }
     }
-    __syncthreads();
-
-    if (!pl.vat && sh.mode == kModeOneHot) {
-        const int r = sh.r;
-        const DrawRow d = onehot_row<EB>(pl, b, r, src, sh.mz[r].x, sh.x_r, sh.l_x);
-        const int y = draw_token<EB, VEC>(d, u_draw, P, V, sh);
-        if (wave == 0) publish_decision(pl, b, r, kModeOneHot, x, u_draw, y, sh);
+    if constexpr (Tr::onehot) {
+        if (!draws) return;
+        // chunk partials of target row r (local row r), tags checked
+        const uint64_t* cw = chunk_words(pl, b) + static_cast<int64_t>(r) * P * 2;
+        const bool cstaged = 2 * P <= kStageWords;
+        const float m_r = sh.mz[r].x;
+        const bool ok = collect(cw, 2 * P, pl.tag, cstaged ? sh.stage : nullptr, sh.vote, false);
+        const DrawRow d = onehot_row<EB>(pl, b, r, PartialSrc{cstaged ? sh.stage : nullptr, cw}, m_r, sh.x_r, sh.l_x);
+        const int y = ok ? draw_token<EB, VEC>(d, u_draw, P, V, sh) : -2;
+        if (threadIdx.x < kWave) publish_outputs<MODE>(pl, b, r, pr.x, y, sh);
+        if (threadIdx.x == kWave) put_word(decision_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
     }
 }
 
-// Residual worker `w` of sequence b: mass of one chunk of max(0, p_r - q_r).
-template <int EB, bool VEC>
+// Residual worker `w` of sequence b: decides, and if the sequence rejected
+// at r, the mass of max(0, p_r - q_r) over one chunk pair per wavefront.
+template <int EB, bool VEC, int MODE>
 __device__ __forceinline__ void residual_worker(const Plan& pl, int b, int w, TailShared& sh) {
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls,
-                 kDecisionTimeoutTicks))
-        return;
-    const Decision dc = read_decision(sh.stage);
-    if (dc.mode != kModeResidual) return;
+    PosRegs pr = load_positions<EB, MODE>(pl, b);
+    const int r = decide<EB, VEC, MODE>(pl, b, sh, false, pr, kDecisionTimeoutTicks);
+    if (r < 0 || r >= pl.k) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int P = pl.chunks;
     const int64_t V = pl.vocab;
-    const ResidW wf = make_resid_w(dc.mzt, dc.mzd, pl.c2);
-    const char* rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + dc.r, V, EB);
-    const char* rd = row_base(pl.draft, static_cast<int64_t>(b) * pl.k + dc.r, V, EB);
+    const ResidW wf = make_resid_w(sh.mz[2 * r], sh.mz[2 * r + 1], pl.c2);
+    const char* rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + r, V, EB);
+    const char* rd = row_base(pl.draft, static_cast<int64_t>(b) * pl.k + r, V, EB);
     const int base = w * kWavesPerBlock * pl.nc_res + static_cast<int>(threadIdx.x / kWave);
 #pragma unroll 1
     for (int n = 0; n < pl.nc_res; ++n) {
@@ -1386,51 +1497,51 @@ __device__ __forceinline__ void residual_worker(const Plan& pl, int b, int w, Ta
         const int64_t start = static_cast<int64_t>(c) * Chunk<EB>::kElems;
         const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), V - start));
         const float s = chunk_resid_mass<EB, VEC>(rt, rd, start, len, lane, wf);
-        if (lane == 0) put_word(pl.resid + static_cast<int64_t>(b) * P + c, __float_as_uint(s), pl.tag);
+        if (lane == 0) put_word(resid_words(pl, b) + c, __float_as_uint(s), pl.tag);
     }
 }
 
-// Residual finisher of sequence b: draws the target's token at r < k.
-template <int EB, bool VEC>
+// Residual finisher of sequence b: decides, and draws the target's token at
+// r < k from the residual masses.
+template <int EB, bool VEC, int MODE>
 __device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailShared& sh) {
     const int P = pl.chunks;
     const int k = pl.k;
     const int64_t V = pl.vocab;
-    uint64_t* rwords = pl.resid + static_cast<int64_t>(b) * P;
-    const bool staged = P + kDecWords <= kStageWords;
-    // A decision that never comes is reported by the decision finisher.
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls,
-                 kDecisionTimeoutTicks))
-        return;
-    const Decision dc = read_decision(sh.stage);
-    if (dc.mode != kModeResidual) return;
-    int32_t* token = pl.out_tokens + static_cast<int64_t>(b) * (k + 1) + dc.r;
-    if (!collect(rwords, P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote, pl.two_deep_polls)) {
+    PosRegs pr = load_positions<EB, MODE>(pl, b);
+    const float u_draw = pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k];
+    // a decision that never comes is reported by the decision finisher
+    const int r = decide<EB, VEC, MODE>(pl, b, sh, false, pr, kDecisionTimeoutTicks);
+    if (r < 0 || r >= k) return;
+    const float2 mzt = sh.mz[2 * r], mzd = sh.mz[2 * r + 1];
+    int32_t* token = pl.out_tokens + static_cast<int64_t>(b) * (k + 1) + r;
+    uint64_t* rwords = resid_words(pl, b);
+    const bool staged = P <= kStageWords;
+    if (!collect(rwords, P, pl.tag, staged ? sh.stage : nullptr, sh.vote, pl.two_deep_polls)) {
         if (threadIdx.x == 0) *token = -2;
         return;
     }
     DrawRow d;
     d.mode = kModeResidual;
-    d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + dc.r, V, EB);
-    d.rd = row_base(pl.draft, static_cast<int64_t>(b) * k + dc.r, V, EB);
+    d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + r, V, EB);
+    d.rd = row_base(pl.draft, static_cast<int64_t>(b) * k + r, V, EB);
     d.part = PartialSrc{nullptr, nullptr};
     d.part_base = 0;
-    d.rstage = staged ? sh.stage + kDecWords : nullptr;
+    d.rstage = staged ? sh.stage : nullptr;
     d.rwords = rwords;
     d.c2 = pl.c2;
-    d.mrow = dc.mzt.x;
-    d.mt = row_scale(dc.mzt.x, pl.c2, d.corr);
+    d.mrow = mzt.x;
+    d.mt = row_scale(mzt.x, pl.c2, d.corr);
     d.excl = -1;
     d.lx = 0.f;
-    d.rw = make_resid_w(dc.mzt, dc.mzd, pl.c2);
+    d.rw = make_resid_w(mzt, mzd, pl.c2);
     // A residual that rounds to zero mass (only possible through rounding,
     // since a rejection has probability TV(p, q)): draw from p_r instead,
-    // from target row r's chunk partials, collected (and their tags checked)
-    // here.
+    // from target row r's chunk partials, collected (tags checked) here.
     float zsum = 0.f;
     for (int cc = threadIdx.x; cc < P; cc += kBlock) zsum += chunk_mass(d, cc, -1, 0.f);
     if (!block_any(zsum > 0.f, sh.vote)) {
-        const uint64_t* pw = seq_words(pl, b) + static_cast<int64_t>(dc.r) * P * 2;
+        const uint64_t* pw = chunk_words(pl, b) + static_cast<int64_t>(2 * r) * P * 2;
         const bool pstaged = 2 * P <= kStageWords;
         if (!collect(pw, 2 * P, pl.tag, pstaged ? sh.stage : nullptr, sh.vote, false)) {
             if (threadIdx.x == 0) *token = -2;
@@ -1439,62 +1550,83 @@ __device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailSha
         d.mode = kModeBonus;
         d.part = PartialSrc{pstaged ? sh.stage : nullptr, pw};
     }
-    const int y = draw_token<EB, VEC>(d, dc.u, P, V, sh);
+    const int y = draw_token<EB, VEC>(d, u_draw, P, V, sh);
     if (threadIdx.x == 0) *token = y;
 }
 
-// Bonus finisher of sequence b: statistics of target row k and, when all k
-// drafts were kept, the token drawn from it (its argmax at T == 0).
-template <int EB, bool VEC>
+// Bonus worker of sequence b, segment s of the bonus row (target position
+// k).  It is read only when the sequence kept all k drafts (or when every
+// row's statistics are asked for), except for the last sequences, whose
+// decisions come late: they read it at once.  The others wait for the
+// decision finisher's word rather than deciding themselves: one word against
+// the sequence's segment words and their combination, for blocks whose
+// decision is long taken when they run.
+template <int EB, bool VEC, int MODE>
+__device__ __forceinline__ void bonus_worker(const Plan& pl, int b, int s, TailShared& sh) {
+    if (!pl.row_stats_out && b < pl.eager_bonus_from) {
+        if (!collect(decision_word(pl, b), 1, pl.tag, sh.stage, sh.vote, false, kDecisionTimeoutTicks)) return;
+        if (static_cast<int>(sh.stage[0]) - 2 != pl.k) return;
+    }
+    stream_segment<EB, VEC, MODE>(pl, b, pl.dec_rows, s, sh);
+}
+
+// Bonus finisher of sequence b: decides; the statistics of target row k
+// and, when all k drafts were kept, the token drawn from it (its argmax at
+// T == 0).
+template <int EB, bool VEC, int MODE>
 __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared& sh) {
+    using Tr = PathTraits<MODE>;
     const int lane = threadIdx.x & (kWave - 1);
     const int k = pl.k;
     const int P = pl.chunks;
+    const int S = pl.segs;
     const int64_t V = pl.vocab;
-    const float c2 = pl.c2;
-    const uint64_t* words = seq_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * P * 2;
-    const bool staged = 2 * P + kDecWords <= kStageWords;
-    // A decision that never comes is reported by the decision finisher.
-    if (!collect(pl.dec + static_cast<int64_t>(b) * kDecWords, kDecU + 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls,
-                 kDecisionTimeoutTicks))
-        return;
-    const Decision dc = read_decision(sh.stage);
-    // Without full acceptance the bonus row was not read (unless every row's
-    // statistics are asked for): nothing to do.
-    if (dc.r != k && !pl.row_stats_out) return;
-    if (!collect(words, 2 * P, pl.tag, staged ? sh.stage + kDecWords : nullptr, sh.vote, pl.two_deep_polls)) {
-        if (dc.r == k && threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + k] = -2;
+    PosRegs pr = load_positions<EB, MODE>(pl, b);
+    const float u_draw = Tr::greedy ? 0.f : pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k];
+    const int r = decide<EB, VEC, MODE>(pl, b, sh, false, pr, kDecisionTimeoutTicks);
+    if (r < 0 || (r != k && !pl.row_stats_out)) return;
+    int32_t* token = pl.out_tokens + static_cast<int64_t>(b) * (k + 1) + k;
+    const uint64_t* sw = seg_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * S * 2;
+    const bool sstaged = 2 * S <= kStageWords;
+    if (!collect(sw, 2 * S, pl.tag, sstaged ? sh.stage : nullptr, sh.vote, pl.two_deep_polls)) {
+        if (r == k && threadIdx.x == 0) *token = -2;
         return;
     }
-    const PartialSrc src{staged ? sh.stage + kDecWords : nullptr, words};
     if (threadIdx.x < kWave) {
-        const float2 res = combine_row(src, 0, P, pl.greedy, c2);
+        const float2 res = combine_row(PartialSrc{sstaged ? sh.stage : nullptr, sw}, 0, S, Tr::greedy, pl.c2);
         if (lane == 0) {
             sh.mz[0] = res;
             write_row_stats(pl, global_row(pl, b, pl.dec_rows), res);
         }
     }
     __syncthreads();
-    if (dc.r != k) return;
-    if (pl.greedy) {
-        if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + k] = __float_as_int(sh.mz[0].y);
-        return;
+    if (r != k) return;
+    if constexpr (Tr::greedy) {
+        if (threadIdx.x == 0) *token = __float_as_int(sh.mz[0].y);
+    } else {
+        const float m_k = sh.mz[0].x;
+        const uint64_t* cw = chunk_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * P * 2;
+        const bool cstaged = 2 * P <= kStageWords;
+        if (!collect(cw, 2 * P, pl.tag, cstaged ? sh.stage : nullptr, sh.vote, false)) {
+            if (threadIdx.x == 0) *token = -2;
+            return;
+        }
+        DrawRow d;
+        d.mode = kModeBonus;
+        d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + k, V, EB);
+        d.rd = nullptr;
+        d.part = PartialSrc{cstaged ? sh.stage : nullptr, cw};
+        d.part_base = 0;
+        d.rstage = nullptr;
+        d.rwords = nullptr;
+        d.c2 = pl.c2;
+        d.mrow = m_k;
+        d.mt = row_scale(m_k, pl.c2, d.corr);
+        d.excl = -1;
+        d.lx = 0.f;
+        const int y = draw_token<EB, VEC>(d, u_draw, P, V, sh);
+        if (threadIdx.x == 0) *token = y;
     }
-    DrawRow d;
-    d.mode = kModeBonus;
-    d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + k, V, EB);
-    d.rd = nullptr;
-    d.part = src;
-    d.part_base = 0;
-    d.rstage = nullptr;
-    d.rwords = nullptr;
-    d.c2 = c2;
-    d.mrow = sh.mz[0].x;
-    d.mt = row_scale(d.mrow, c2, d.corr);
-    d.excl = -1;
-    d.lx = 0.f;
-    const int y = draw_token<EB, VEC>(d, dc.u, P, V, sh);
-    if (threadIdx.x == 0) pl.out_tokens[static_cast<int64_t>(b) * (k + 1) + k] = y;
 }
 
 // VAT loss finisher of block b: the pair partials of each position, combined
@@ -1532,7 +1664,7 @@ __device__ __forceinline__ void vat_loss_finisher(const Plan& pl, int b, TailSha
     }
 
     // Position i on wave i % 4: lanes poll their chunks' five words.
-    const uint64_t* words = seq_words(pl, b);
+    const uint64_t* words = chunk_words(pl, b);
     bool timed_out = false;
     const uint64_t t0 = wall_clock64();
     for (int i = wave; i < k; i += kWavesPerBlock) {
@@ -1572,7 +1704,7 @@ __device__ __forceinline__ void vat_loss_finisher(const Plan& pl, int b, TailSha
         }
     }
     if (block_any(timed_out, sh.vote)) {
-        fail_sequence(pl, b);
+        fail_sequence<kPathVatLoss>(pl, b);
         for (int j = threadIdx.x; j < k; j += kBlock) {
             pl.soft_ce[o + j] = __builtin_nanf("");
             pl.hard_ce[o + j] = __builtin_nanf("");
@@ -1632,70 +1764,75 @@ __device__ __forceinline__ void vat_loss_finisher(const Plan& pl, int b, TailSha
 
 // Five resident blocks per CU (five waves per SIMD, kMinBlocksPerCu): the
 // register budget the streaming loop is written for (at most 102 VGPRs).
-template <int EB, bool VEC>
+template <int EB, bool VEC, int MODE>
 __global__ __launch_bounds__(kBlock, kMinBlocksPerCu) void k_verify(Plan pl) {
+    using Tr = PathTraits<MODE>;
     __shared__ TailShared sh;
     const Role role = decode_role(pl.grid, static_cast<int32_t>(blockIdx.x));
-    const int b = role.seq;
+    int b = role.seq;
     switch (role.kind) {
         case kDecWorker: {
-            // Step n: the block's waves take items base + n*4 + wave (32 KiB
-            // of contiguous logits per step when the items share a row).
-            const int items = pl.dec_rows * pl.chunks;
-            const int base = role.index * kWavesPerBlock * pl.nc_dec + static_cast<int>(threadIdx.x / kWave);
+            if constexpr (Tr::loss) {
+                // Step n: the block's waves take chunk pairs base + n*4 + wave.
+                const int items = pl.dec_rows * pl.chunks;
+                const int base = role.index * kWavesPerBlock * pl.nc_dec + static_cast<int>(threadIdx.x / kWave);
 #pragma unroll 1
-            for (int n = 0; n < pl.nc_dec; ++n) {
-                const int li = base + n * kWavesPerBlock;
-                if (li >= items) break;
-                if (pl.vat_loss) stream_pair<EB, VEC>(pl, b, li / pl.chunks, li % pl.chunks);
-                else stream_chunk<EB, VEC>(pl, b, li / pl.chunks, li % pl.chunks);
+                for (int n = 0; n < pl.nc_dec; ++n) {
+                    const int li = base + n * kWavesPerBlock;
+                    if (li >= items) break;
+                    stream_pair<EB, VEC>(pl, b, li / pl.chunks, li % pl.chunks);
+                }
+            } else {
+                // Block `index` of sequence b: segment index % S of local
+                // row index / S.  When every decision worker block comes
+                // before every finisher (one residency), the blocks are
+                // taken position-major over all sequences instead, so that
+                // the rows of early positions arrive first and decisions
+                // that stop at an early rejection finish while the rest
+                // streams.
+                int idx = role.index;
+                if (pl.pos_major) {
+                    const int64_t q = static_cast<int64_t>(b) * pl.grid.w_dec + idx;
+                    const int64_t t = q / pl.segs;
+                    const int s = static_cast<int>(q - t * pl.segs);
+                    b = static_cast<int>(t % pl.batch);
+                    idx = static_cast<int>(t / pl.batch) * pl.segs + s;
+                }
+                const int j = idx / pl.segs;
+                stream_segment<EB, VEC, MODE>(pl, b, j, idx - j * pl.segs, sh);
             }
             return;
         }
-        case kBonusWorker: {
-            // The bonus row is read only when the sequence kept all k drafts
-            // (or when every row's statistics are asked for), except for the
-            // last sequences, whose decisions come late: they read it at once.
-            if (!pl.row_stats_out && b < pl.eager_bonus_from) {
-                const uint64_t* dw = pl.dec + static_cast<int64_t>(b) * kDecWords + kDecRMode;
-                if (!collect(dw, 1, pl.tag, sh.stage, sh.vote, pl.two_deep_polls, kDecisionTimeoutTicks)) return;
-                if (static_cast<int>(sh.stage[0] & 0xffffu) - 2 != pl.k) return;
-            }
-            const int base = role.index * kWavesPerBlock * pl.nc_bonus + static_cast<int>(threadIdx.x / kWave);
-#pragma unroll 1
-            for (int n = 0; n < pl.nc_bonus; ++n) {
-                const int c = base + n * kWavesPerBlock;
-                if (c >= pl.chunks) break;
-                stream_chunk<EB, VEC>(pl, b, pl.dec_rows, c);
-            }
+        case kBonusWorker:
+            if constexpr (Tr::bonus) bonus_worker<EB, VEC, MODE>(pl, b, role.index, sh);
             return;
-        }
         case kDecFinisher:
-            if (pl.vat_loss) vat_loss_finisher<EB, VEC>(pl, b, sh);
-            else decide_sequence<EB, VEC>(pl, b, sh);
+            if constexpr (Tr::loss) vat_loss_finisher<EB, VEC>(pl, b, sh);
+            else decision_finisher<EB, VEC, MODE>(pl, b, sh);
             return;
         case kResWorker:
-            residual_worker<EB, VEC>(pl, b, role.index, sh);
+            if constexpr (Tr::resid) residual_worker<EB, VEC, MODE>(pl, b, role.index, sh);
             return;
         case kResFinisher:
-            residual_finisher<EB, VEC>(pl, b, sh);
+            if constexpr (Tr::resid) residual_finisher<EB, VEC, MODE>(pl, b, sh);
             return;
         default:
-            bonus_finisher<EB, VEC>(pl, b, sh);
+            if constexpr (Tr::bonus) bonus_finisher<EB, VEC, MODE>(pl, b, sh);
             return;
     }
 }
 
 // ------------------------------------------------------------------ dispatch
 
-template <int EB, bool VEC>
+template <int EB, bool VEC, int MODE>
 hipError_t launch_typed(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     hipError_t e;
     if (ev0 && ev1) {
         e = hipEventRecord(ev0, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_verify<EB, VEC>), dim3(static_cast<unsigned>(pl.grid.total_blocks)), dim3(kBlock), 0, stream, pl);
+    hipLaunchKernelGGL((k_verify<EB, VEC, MODE>), dim3(static_cast<unsigned>(pl.grid.total_blocks)), dim3(kBlock), 0,
+                       stream, pl);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev0 && ev1) {
@@ -1703,6 +1840,39 @@ hipError_t launch_typed(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipE
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+template <int EB, bool VEC>
+hipError_t launch_mode(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    switch (pl.path) {
+        case kPathSample: return launch_typed<EB, VEC, kPathSample>(pl, stream, ev0, ev1);
+        case kPathOneHot: return launch_typed<EB, VEC, kPathOneHot>(pl, stream, ev0, ev1);
+        case kPathGreedy: return launch_typed<EB, VEC, kPathGreedy>(pl, stream, ev0, ev1);
+        case kPathVat: return launch_typed<EB, VEC, kPathVat>(pl, stream, ev0, ev1);
+        case kPathVatGreedy: return launch_typed<EB, VEC, kPathVatGreedy>(pl, stream, ev0, ev1);
+        case kPathVatLoss: return launch_typed<EB, VEC, kPathVatLoss>(pl, stream, ev0, ev1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int EB, bool VEC, int MODE>
+int blocks_per_cu_typed() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_verify<EB, VEC, MODE>, kBlock, 0) != hipSuccess) return 0;
+    return n;
+}
+
+template <int EB, bool VEC>
+int blocks_per_cu_mode(int path) {
+    switch (path) {
+        case kPathSample: return blocks_per_cu_typed<EB, VEC, kPathSample>();
+        case kPathOneHot: return blocks_per_cu_typed<EB, VEC, kPathOneHot>();
+        case kPathGreedy: return blocks_per_cu_typed<EB, VEC, kPathGreedy>();
+        case kPathVat: return blocks_per_cu_typed<EB, VEC, kPathVat>();
+        case kPathVatGreedy: return blocks_per_cu_typed<EB, VEC, kPathVatGreedy>();
+        case kPathVatLoss: return blocks_per_cu_typed<EB, VEC, kPathVatLoss>();
+        default: return 0;
+    }
 }
 
 }  // namespace
@@ -1844,20 +2014,9 @@ hipError_t launch_accept_hist(const int32_t* acc, int32_t batch, int32_t k, int3
     return hipGetLastError();
 }
 
-namespace {
-
-template <int EB, bool VEC>
-int blocks_per_cu_typed() {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_verify<EB, VEC>, kBlock, 0) != hipSuccess) return 0;
-    return n;
-}
-
-}  // namespace
-
-int verify_blocks_per_cu(int elem_bytes, bool vec) {
-    if (elem_bytes == 2) return vec ? blocks_per_cu_typed<2, true>() : blocks_per_cu_typed<2, false>();
-    return vec ? blocks_per_cu_typed<4, true>() : blocks_per_cu_typed<4, false>();
+int verify_blocks_per_cu(int elem_bytes, bool vec, int path) {
+    if (elem_bytes == 2) return vec ? blocks_per_cu_mode<2, true>(path) : blocks_per_cu_mode<2, false>(path);
+    return vec ? blocks_per_cu_mode<4, true>(path) : blocks_per_cu_mode<4, false>(path);
 }
 
 // ------------------------------------------------------------------ built-in scratch
@@ -1915,9 +2074,9 @@ hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
 hipError_t launch_path(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (pl.batch == 0) return hipSuccess;
     if (pl.elem_bytes == 2) {
-        return pl.vec ? launch_typed<2, true>(pl, stream, ev0, ev1) : launch_typed<2, false>(pl, stream, ev0, ev1);
+        return pl.vec ? launch_mode<2, true>(pl, stream, ev0, ev1) : launch_mode<2, false>(pl, stream, ev0, ev1);
     }
-    return pl.vec ? launch_typed<4, true>(pl, stream, ev0, ev1) : launch_typed<4, false>(pl, stream, ev0, ev1);
+    return pl.vec ? launch_mode<4, true>(pl, stream, ev0, ev1) : launch_mode<4, false>(pl, stream, ev0, ev1);
 }
 
 }  // namespace sv

@@ -30,23 +30,24 @@ enum SampleMode : int32_t {
     kModeResidual = 3  // draft logits rejected at r: draw from max(0, p_r - q_r)
 };
 
-// Tagged words the decision finisher of a sequence leaves for the residual
-// and bonus roles (see kTagFirst).
-enum DecisionWord : int32_t {
-    kDecRMode = 0,  // (r + 2) | mode << 16; r = -1 invalid token, -2 timed out
-    kDecMt = 1,     // max of target row r (residual)
-    kDecZt = 2,     // Z of target row r
-    kDecMd = 3,     // max of draft row r
-    kDecZd = 4,     // Z of draft row r
-    kDecU = 5,      // the uniform of the draw
-    kDecWords = 8
+// Specialisations of the verification kernel: which rows a call streams and
+// which roles its grid holds are fixed per specialisation, so each carries
+// only its own code.
+enum PathMode : int32_t {
+    kPathSample = 0,     // verification with draft logits, T > 0
+    kPathOneHot = 1,     // verification with one-hot drafts, T > 0
+    kPathGreedy = 2,     // verification, T == 0
+    kPathVat = 3,        // VAT labels, T > 0
+    kPathVatGreedy = 4,  // VAT labels, T == 0
+    kPathVatLoss = 5,    // VAT labels, weights and loss
 };
 
 // Everything the kernels of one call need.  Global row numbering (row_mz,
 // row_stats_out): target rows 0 .. rows_t-1 (sequence b, position i ->
 // b*target_rows_per_seq + i), then draft rows rows_t .. rows_t+rows_d-1
-// (b, i -> rows_t + b*k + i).  Within a sequence, local row j < n_t is target
-// position j and j >= n_t is draft position j - n_t.
+// (b, i -> rows_t + b*k + i).  Within a sequence, local row j < dec_rows is
+// position j / halves, its target row when j % halves == 0 and its draft
+// row otherwise; local row dec_rows is the bonus row (target position k).
 struct Plan {
     int32_t batch;            // B (verify) or N (VAT)
     int32_t k;
@@ -55,28 +56,26 @@ struct Plan {
     int32_t target_rows_per_seq;  // k+1 (verify) or k (VAT)
     int32_t chunks;           // P = ceil(V / chunk)
     int32_t chunk;            // elements per chunk
-    // Per sequence, the chunk partials hold local rows: target positions
-    // 0..k-1, then draft positions 0..k-1 (when draft logits are read), then
-    // the bonus row (target position k, verification only).
-    int32_t dec_rows;         // rows the decision reads: k or 2k
+    int32_t path;             // PathMode
+    int32_t halves;           // rows per position among the decision rows: 2 with draft logits, else 1
+    int32_t dec_rows;         // k * halves (VAT loss: k chunk-pair rows)
     int32_t rows_per_seq;     // dec_rows + (1 if there is a bonus row)
-    int32_t words_per_seq;    // hand-off words of one sequence in `partials`
-    int32_t has_resid;        // draft logits at T > 0: residual roles exist
-    int32_t has_bonus;        // verification (not VAT): bonus roles exist
-    int32_t nc_dec, nc_bonus, nc_res;  // chunks per worker wavefront
-    int32_t eager_bonus_from; // sequences b >= this read their bonus row without waiting for the decision
-    int32_t two_deep_polls;   // finishers keep two reads of their words in flight (grids of one residency)
-    uint32_t tag;             // this call's tag of hand-off words
-    int64_t rows_t;
-    int64_t rows_d;           // 0 for one-hot drafts and T == 0
+    int32_t words_per_seq;    // chunk words of one sequence (two per row chunk; VAT loss: five per pair)
+    int32_t segs;             // S: segments per row, one per decision worker block
+    int32_t seg_chunks;       // chunks per segment (four wavefronts x nc_dec)
+    int32_t seg_words_per_seq;  // segment words of one sequence: rows_per_seq * S * 2
+    int32_t nc_dec, nc_res;   // chunks per worker wavefront
+    int32_t eager_bonus_from; // sequences b >= this read their bonus row without deciding first
+    int32_t pos_major;        // decision worker blocks ordered position-major over all sequences
     // Flags are 32-bit: a byte-sized field at an unaligned offset of the
     // kernel argument block is read with a vector load (a memory round trip
     // at the start of every block) instead of a scalar one.
+    int32_t two_deep_polls;   // (nearly) the whole grid resident at once: poll with short sleeps
     int32_t vec;              // 16-byte loads allowed (aligned rows)
     int32_t greedy;           // T == 0
-    int32_t onehot;
-    int32_t vat;
-    int32_t vat_loss;         // VAT with the training loss: workers read chunk pairs
+    uint32_t tag;             // this call's tag of hand-off words
+    int64_t rows_t;
+    int64_t rows_d;           // 0 for one-hot drafts and T == 0
     float temperature;
     float c2;                 // log2(e) / T
     float decay;
@@ -100,10 +99,10 @@ struct Plan {
     float* block_loss;        // [N] sum_i w_i (soft_i + hard_weight * hard_i)
 
     // workspace regions
-    uint64_t* partials;       // [B][R_s][P][2] tagged words (m, s) or (max, index);
+    uint64_t* chunkw;         // [B][rows_per_seq][P][2] tagged chunk partials (m, s) or (max, index);
                               // VAT loss: [B][k][P][5] (pair partials)
-    uint64_t* resid;          // [B][P] tagged residual masses
-    uint64_t* dec;            // [B][kDecWords] tagged decision words
+    uint64_t* segw;           // [B][rows_per_seq][S][2] tagged segment partials (not for the VAT loss)
+    uint64_t* resid;          // [B][P + 1] tagged residual masses, then the decision word (r + 2)
 
     TaskGrid grid;            // role of every block of the launch
 };
@@ -116,8 +115,8 @@ struct Plan {
 constexpr int kMinBlocksPerCu = 5;
 constexpr int kDefaultComputeUnits = 256;
 
-// Blocks of k_verify<EB, VEC> one compute unit holds at once (0 on failure).
-int verify_blocks_per_cu(int elem_bytes, bool vec);
+// Blocks of k_verify<EB, VEC, path> one compute unit holds at once (0 on failure).
+int verify_blocks_per_cu(int elem_bytes, bool vec, int path);
 
 // Chunks each worker wavefront streams, one after the other.  Two per wave
 // for large calls: block dispatch (on the order of 150-200 blocks per
@@ -129,7 +128,6 @@ constexpr int kChunksPerWave = 2;
 constexpr int kChunksPerWaveSmall = 1;
 constexpr int64_t kSmallCallWaves = 4 * kWavesPerBlock;
 constexpr int kChunksPerWaveResid = 1;
-constexpr int kChunksPerWaveBonus = 2;
 
 // Values handed between blocks inside a kernel travel as 64-bit words,
 // written and read whole (single-copy atomic): 32 data bits and a 32-bit tag
@@ -143,11 +141,12 @@ constexpr uint32_t kTagCount = 0xffffffffu;
 constexpr int kStageWords = 4096;
 
 struct WorkspaceLayout {
-    size_t partials, resid, dec, total;
+    size_t chunkw, segw, resid, total;
 };
 
-// partial_words: tagged words of chunk partials over the whole call.
-WorkspaceLayout workspace_layout(int64_t partial_words, int64_t batch, int64_t chunks);
+// chunk_words / seg_words: tagged words of chunk and segment partials over
+// the whole call.
+WorkspaceLayout workspace_layout(int64_t chunk_words, int64_t seg_words, int64_t batch, int64_t chunks);
 
 // Words per chunk pair of the VAT loss: (m_t, s_t, m_d, s_d, x).
 constexpr int kPairWords = 5;
