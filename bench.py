@@ -2,34 +2,62 @@
 
     python bench.py [--steps K] [--warmup W] [--workload selfdraft] [--gpus 1]
 
-One step = one sv_verify call (sv_vat_labels for --workload vat, sv_vat_loss
-for --workload vat_loss, sv_vat_loss_grad for --workload vat_loss_grad: the
-gradient of the VAT loss with respect to the draft logits, kernel k_vat_grad,
-after one sv_vat_loss call outside the timed region) over one
-batch of synthetic logits already resident in HBM; the call is the whole path
-(one launch of the task-grid kernel k_verify, or of k_vat_grad).  The default workload is the
-quantized-self-drafter batch: B=128 sequences, k=5 draft positions,
-V=151936, bf16 target and draft logits, T=1.  Prints ONE JSON line.
+One step = one sv_verify call over one batch of synthetic logits already
+resident in HBM; the call is the whole path (one launch of the task-grid
+kernel k_verify).  The default workload is the quantized-self-drafter batch:
+B=128 sequences, k=5 draft positions, V=151936, bf16 target and draft
+logits, T=1.  W untimed calls, then exactly K timed calls, synchronised on
+both sides.  Prints ONE JSON line:
 
   value        verified draft positions per second = B*k*K / wall time of K
-               steps (synchronised on both sides); VAT: labelled positions
-  roofline     k_verify: algorithmic bytes per launch (every logit the path
-               needs, read once: the k target and k draft rows of every
-               sequence, and target row k of the sequences that kept all k
-               drafts, the only ones that draw from it) / its mean duration, measured live with HIP
-               events recorded on the launch stream around the K timed
-               launches (per-launch events would add several microseconds
-               of stream work between launches);
-               `traffic` = HBM bytes per launch from committed rocprofv3
-               FETCH_SIZE/WRITE_SIZE counters when they were taken on the
-               current kernel source, else null
+               steps
+  dtype        the logits' storage type (the arithmetic is fp32: config)
+  roofline     k_verify: algorithmic bytes per launch (every logit of the
+               workload read once: k+1 target rows and, with draft logits,
+               k draft rows per sequence) / its mean launch duration,
+               measured live with HIP events recorded on the launch stream
+               around the K timed launches (per-launch events would add
+               stream work between launches); also the bytes this call
+               needed (the bonus row only of sequences that kept all k) and
+               that fraction; `traffic` = HBM bytes per launch from
+               committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters when they
+               were taken on the current kernel source, else null
+  sol          k_sol_read (sv_sol_read: a plain non-temporal read) over the
+               needed bytes, buffers rotated the same way: its mean launch
+               duration and sol/k_verify
+  call_us      p10 / p50 / p90 of single calls' device time (each between
+               its own events), 200 calls after the timed steps
+  accept_rate, mean_accepted_len, full_acceptance, block_efficiency
+               acceptance of the last call (accept_rate = accepted drafts /
+               tested drafts)
+  parity_sample
+               the fp64 oracle on the first 32 sequences next to the GPU's
+               outputs for them, outside any timed region: positions whose
+               acceptance test is within 1e-5 of its threshold, draws within
+               1e-5 of an interval end (both may legitimately differ between
+               fp32 and fp64; *_differ: those the GPU resolved otherwise)
+               and sequences that differ anywhere else (expect 0)
+  workloads    the same figures for the n-gram tail (B=8, k=16, one-hot
+               drafts) and GRPO batches (B=320, k=7, T=0.6 and T=0), each
+               after 200 warm-up calls over 500 timed calls
   cpu_baseline the fp64 oracle on a bounded sample of the same workload on
-               the host (single thread)
+               the host: all the process's host threads, each taking whole
+               sequences (reported), and one thread (nested)
 
 Inputs rotate through enough copies that each timed sweep touches more than
 twice the 256 MB last-level (MALL) cache, so the figures are HBM figures.
-The default warm-up (200 calls, tens of milliseconds) lets the GPU reach its
-steady clocks; with a few warm-up calls the first timed calls run slower.
+The side workloads run first, so the GPU has reached its steady clocks
+before the headline's warm-up even when W is small.
+
+    python bench.py --workload ngram_tail|grpo|grpo_greedy [--no-side]
+
+makes that workload the headline.  --workload vat|vat_loss|vat_loss_grad
+times sv_vat_labels, sv_vat_loss, or sv_vat_loss_grad (the gradient of the
+VAT loss with respect to the draft logits, kernel k_vat_grad, after one
+sv_vat_loss call outside the timed region) on N=2048 blocks of k=16 fp32
+rows of V=128256; `sol` is then sv_sol_read over the logits, or, for the
+gradient, sv_sol_read_write (both logit arrays read, the fp32 gradient
+written) over the same buffers.
 
     python bench.py --workload lmhead_selfdraft|lmhead_grpo [--steps K]
 
@@ -62,6 +90,8 @@ import os
 import platform
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -132,43 +162,153 @@ def measured_traffic(kernel: str, workload: str, source_hash=None):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, seconds: float, loss: bool = False, grad: bool = False):
-    """The oracle as it is (plain fp64 C, one thread) over whole sequences (VAT:
-    blocks) of the same workload until `seconds` of CPU work have elapsed; the
-    sample is drawn on the host by the same seeded generator.  With `grad`, the
-    loss and then its gradient with respect to the draft logits."""
+def _oracle_call(cfg, wl, lo, hi, loss=False, grad=False):
+    """The oracle on sequences (VAT: blocks) [lo, hi) of a host sample."""
     import oracle
+
+    d = wl.draft[lo:hi] if wl.draft is not None else None
+    if loss:
+        r = oracle.vat_loss(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], wl.hard_tokens[lo:hi],
+                            cfg.T, cfg.decay, 1.0)
+        if grad:
+            oracle.vat_loss_grad(wl.target[lo:hi], d, wl.hard_tokens[lo:hi], r.weights, cfg.T, 1.0)
+        return r
+    if cfg.kind == "vat":
+        return oracle.vat_labels(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, cfg.decay)
+    return oracle.verify(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, onehot=cfg.onehot)
+
+
+HOST_THREADS_MAX = 16  # a GPU's share of its host's cores
+
+
+def host_threads() -> int:
+    """Host threads for the oracle: the process's CPU affinity (else the core
+    count), bounded by OMP_NUM_THREADS when set and by one GPU's share."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, HOST_THREADS_MAX))
+
+
+def cpu_baseline(cfg, seconds: float, loss: bool = False, grad: bool = False, threads: int = 1, wl=None):
+    """The oracle as it is (plain fp64 C) over whole sequences (VAT: blocks) of
+    the same workload until `seconds` of wall time have elapsed, on `threads`
+    host threads that each take the next whole sequence (the C oracle runs
+    without Python's lock held).  The sample is the workload's first
+    sequences, drawn on the host by the same seeded generator.  With `grad`,
+    the loss and then its gradient with respect to the draft logits."""
+    import threading
+
     import workloads
 
     n_sample = min(cfg.B, 32 if cfg.kind == "verify" else 4)
-    wl = workloads.generate(cfg, 0, n_sample)
-    done = 0
+    if wl is None:
+        wl = workloads.generate(cfg, 0, n_sample)
+    n_sample = min(n_sample, wl.n)
+    lock = threading.Lock()
+    state = {"next": 0, "done": 0}
+    deadline = [0.0]
+
+    def worker():
+        while True:
+            with lock:
+                if time.perf_counter() >= deadline[0]:
+                    return
+                i = state["next"] % n_sample
+                state["next"] += 1
+            _oracle_call(cfg, wl, i, i + 1, loss, grad)
+            with lock:
+                state["done"] += 1
+
     t0 = time.perf_counter()
-    step = 4 if cfg.kind == "verify" else 1
-    while True:
-        lo = done % n_sample
-        hi = min(n_sample, lo + step)
-        d = wl.draft[lo:hi] if wl.draft is not None else None
-        if loss:
-            r = oracle.vat_loss(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], wl.hard_tokens[lo:hi],
-                                cfg.T, cfg.decay, 1.0)
-            if grad:
-                oracle.vat_loss_grad(wl.target[lo:hi], d, wl.hard_tokens[lo:hi], r.weights, cfg.T, 1.0)
-        elif cfg.kind == "vat":
-            oracle.vat_labels(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, cfg.decay)
-        else:
-            oracle.verify(wl.target[lo:hi], d, wl.tokens[lo:hi], wl.uniforms[lo:hi], cfg.T, onehot=cfg.onehot)
-        done += hi - lo
-        if time.perf_counter() - t0 >= seconds:
-            break
+    deadline[0] = t0 + seconds
+    if threads == 1:
+        worker()
+    else:
+        pool = [threading.Thread(target=worker) for _ in range(threads)]
+        for t in pool:
+            t.start()
+        for t in pool:
+            t.join()
     dt = time.perf_counter() - t0
+    done = state["done"]
     what = "blocks" if cfg.kind == "vat" else "sequences"
     if loss:
         what = "blocks (labels, loss and its gradient)" if grad else "blocks (labels and loss)"
-    return {"value": done * cfg.k / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+    return {"value": done * cfg.k / dt, "unit": "positions/s", "cores": threads, "kind": "oracle",
             "sample": "%d whole %s (%d positions; cycling over the first %d) of the %s workload, fp64 C oracle, "
-                      "1 thread, %.1f s" % (done, what, done * cfg.k, n_sample, cfg.name, dt),
-            "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+                      "%s, %.1f s" % (done, what, done * cfg.k, n_sample, cfg.name,
+                                     "1 thread" if threads == 1 else "%d threads over %s" % (threads, what.split()[0]),
+                                     dt),
+            "host_cpu": host_cpu_model(), "host_nproc": os.cpu_count()}
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baselines(cfg, seconds: float, loss: bool = False, grad: bool = False):
+    """All host threads (the reported figure) and one thread (nested)."""
+    import workloads
+
+    wl = workloads.generate(cfg, 0, min(cfg.B, 32 if cfg.kind == "verify" else 4))
+    n = host_threads()
+    res = cpu_baseline(cfg, seconds, loss, grad, threads=n, wl=wl)
+    res["single_thread"] = cpu_baseline(cfg, seconds, loss, grad, threads=1, wl=wl)
+    return res
+
+
+def sample_parity(cfg, wl, acc_gpu, out_gpu, threads: int, band: float = 1e-5):
+    """The oracle on the host sample's sequences next to the GPU's outputs for
+    the same sequences (outside any timed region).  Counts, without
+    asserting: positions whose acceptance test sits within `band` of the
+    threshold (the fp32 and fp64 decisions may differ there; the sequence
+    is compared only before it), draws whose u*Z lies within band*Z of an
+    end of the chosen interval, and sequences that differ anywhere else
+    (expected 0); of the first two, how many the GPU resolved differently
+    from the oracle."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = wl.n
+    with ThreadPoolExecutor(max(1, min(threads, n))) as ex:
+        res = list(ex.map(lambda b: _oracle_call(cfg, wl, b, b + 1), range(n)))
+    greedy = cfg.T == 0
+    amb_accept = amb_draw = mismatch = amb_accept_differ = amb_draw_differ = 0
+    for b, r in enumerate(res):
+        ro, rg = int(r.accepted_len[0]), int(acc_gpu[b])
+        if ro < 0:
+            mismatch += int(rg != ro)
+            continue
+        tested = range(min(ro + 1, cfg.k))
+        amb = [i for i in tested if abs(r.accept_margin[0, i]) < band] if not greedy else []
+        if amb:
+            amb_accept += 1
+            n_cmp = min(rg, ro)
+            mismatch += int(rg < amb[0] or not np.array_equal(out_gpu[b, :n_cmp], r.out_tokens[0, :n_cmp]))
+            amb_accept_differ += int(rg != ro or not np.array_equal(out_gpu[b], r.out_tokens[0]))
+            continue
+        if rg != ro or not np.array_equal(out_gpu[b, :ro], r.out_tokens[0, :ro]):
+            mismatch += 1
+            continue
+        if not greedy and r.sample_margin[0] < band:
+            amb_draw += 1
+            amb_draw_differ += int(out_gpu[b, ro] != r.out_tokens[0, ro])
+            continue
+        mismatch += int(out_gpu[b, ro] != r.out_tokens[0, ro])
+    return {"sequences": n, "ambiguous_accept": amb_accept, "ambiguous_accept_differ": amb_accept_differ,
+            "ambiguous_draw": amb_draw, "ambiguous_draw_differ": amb_draw_differ, "mismatches": mismatch,
+            "band": band}
 
 
 def lm_kernel_source_hash() -> str:
@@ -305,6 +445,258 @@ def copy_probe(steps: int) -> int:
     return 0
 
 
+SIDE_WORKLOADS = ("ngram_tail", "grpo", "grpo_greedy")
+SIDE_WARMUP = 200
+SIDE_STEPS = 500
+PER_CALL_SAMPLES = 200
+
+
+class VerifyRun:
+    """One verification workload resident on the device: the seeded inputs
+    in enough copies that a sweep over them touches more than twice the MALL,
+    one prepared sv_verify call per copy (they rotate), and the host copy of
+    the first sequences for the oracle."""
+
+    def __init__(self, name, dev, n_host=32):
+        import speculative_decoding_verification_amd as sv
+        import workloads
+
+        self.cfg = cfg = workloads.get_config(name)
+        print("bench: generating %s (B=%d k=%d V=%d %s T=%g)" % (cfg.name, cfg.B, cfg.k, cfg.V, cfg.dtype, cfg.T),
+              file=sys.stderr, flush=True)
+        wl = workloads.generate(cfg)
+        self.spec_bytes = cfg.algorithmic_bytes()
+        self.copies = max(1, math.ceil(2 * MALL_BYTES / self.spec_bytes))
+        self.sets = [workloads.to_device(wl, dev) for _ in range(self.copies)]
+        self.calls = _launchers(cfg, self.sets, sv, self.copies)
+        n = min(cfg.B, n_host)
+        self.host = workloads.Workload(cfg, 0, wl.target[:n].copy(),
+                                       None if wl.draft is None else wl.draft[:n].copy(), wl.tokens[:n].copy(),
+                                       wl.uniforms[:n].copy())
+        del wl
+        self.launched = 0
+
+    def launch(self, stream):
+        self.calls[self.launched % len(self.calls)](stream)
+        self.launched += 1
+
+    def last(self):
+        return self.calls[(self.launched - 1) % len(self.calls)]
+
+    def region_ms(self, ev, stream, warmup, steps):
+        """Mean device time per call over `steps` back-to-back calls (one event
+        pair around all of them, on the launch stream) and the wall time."""
+        import torch
+
+        for _ in range(warmup):
+            self.launch(stream)
+        torch.cuda.synchronize()
+        a, b = ev.create(), ev.create()
+        t0 = time.perf_counter()
+        ev.record(a, stream)
+        for _ in range(steps):
+            self.launch(stream)
+        ev.record(b, stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = ev.elapsed_ms(a, b) / steps
+        ev.destroy(a)
+        ev.destroy(b)
+        return ms, wall
+
+    def per_call_ms(self, ev, stream, n):
+        """Device time of each of n calls, each bracketed by its own events
+        (the events add a little stream work between calls)."""
+        import torch
+
+        pairs = [(ev.create(), ev.create()) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in pairs:
+            ev.record(a, stream)
+            self.launch(stream)
+            ev.record(b, stream)
+        torch.cuda.synchronize()
+        out = np.array([ev.elapsed_ms(a, b) for a, b in pairs])
+        for a, b in pairs:
+            ev.destroy(a)
+            ev.destroy(b)
+        return out
+
+    def outcome(self):
+        import torch
+
+        torch.cuda.synchronize()
+        last = self.last()
+        acc = last.accepted_len.cpu().numpy()
+        out = last.out_tokens.cpu().numpy()
+        return acc, out
+
+    def needed_bytes(self, acc):
+        """Every logit this call must read once: all decision rows, and the
+        bonus row (target position k) only of sequences that kept all k."""
+        cfg = self.cfg
+        full = int((acc == cfg.k).sum())
+        return self.spec_bytes - (cfg.B - full) * cfg.V * cfg.elem_bytes
+
+
+def sol_read_ms(nbytes, dev, ev, stream, warmup=50, steps=200):
+    """Mean duration of sv_sol_read over `nbytes` (rounded up to 16), the
+    buffers rotated like the workload's inputs."""
+    import torch
+
+    import speculative_decoding_verification_amd as sv
+
+    nbytes = (nbytes + 15) // 16 * 16
+    copies = max(1, math.ceil(2 * MALL_BYTES / nbytes))
+    bufs = [torch.full((nbytes // 4,), 0x3c003c00, dtype=torch.int32, device=dev) for _ in range(copies)]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for i in range(warmup):
+        sv.sol_read(bufs[i % copies], sink, stream)
+    torch.cuda.synchronize()
+    a, b = ev.create(), ev.create()
+    ev.record(a, stream)
+    for i in range(steps):
+        sv.sol_read(bufs[i % copies], sink, stream)
+    ev.record(b, stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(a, b) / steps
+    ev.destroy(a)
+    ev.destroy(b)
+    del bufs
+    return ms
+
+
+def acceptance_stats(acc, k):
+    valid = acc[acc >= 0]
+    tested = np.minimum(valid + 1, k).sum()
+    return {"mean_accepted_len": float(valid.mean()) if valid.size else None,
+            "accept_rate": float(valid.sum() / tested) if tested else None,
+            "full_acceptance": int((acc == k).sum()), "invalid": int((acc == -1).sum()),
+            "timeouts": int((acc == -2).sum())}
+
+
+def workload_figures(run, ev, stream, dev, warmup, steps):
+    """The side measurements of one workload (fixed warm-up and step count)."""
+    cfg = run.cfg
+    ms, _ = run.region_ms(ev, stream, warmup, steps)
+    calls = run.per_call_ms(ev, stream, PER_CALL_SAMPLES)
+    acc, out = run.outcome()
+    needed = run.needed_bytes(acc)
+    sol = sol_read_ms(needed, dev, ev, stream)
+    fig = {"B": cfg.B, "k": cfg.k, "V": cfg.V, "logits": cfg.dtype, "temperature": cfg.T,
+           "draft": "one-hot" if cfg.onehot else ("none (greedy)" if cfg.T == 0 else "logits"),
+           "warmup": warmup, "steps": steps, "mean_launch_us": ms * 1e3,
+           "positions_per_s": cfg.positions() / (ms * 1e-3),
+           "algorithmic_bytes": run.spec_bytes, "needed_bytes": needed,
+           "frac": run.spec_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "frac_needed": needed / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "sol": {"kernel": "k_sol_read", "bytes": needed, "mean_launch_us": sol * 1e3, "frac": sol / ms},
+           "call_us": {"p10": float(np.percentile(calls, 10) * 1e3), "p50": float(np.percentile(calls, 50) * 1e3),
+                       "p90": float(np.percentile(calls, 90) * 1e3), "calls": len(calls)},
+           "traffic": measured_traffic("k_verify", cfg.name)}
+    fig.update(acceptance_stats(acc, cfg.k))
+    fig["parity_sample"] = sample_parity(cfg, run.host, acc[:run.host.n], out[:run.host.n], host_threads())
+    return fig
+
+
+def bench_verify(args) -> int:
+    """Verification workloads (the default): the headline line for
+    args.workload, with the side workloads measured in the same process."""
+    import torch
+
+    import speculative_decoding_verification_amd as sv
+
+    dev = torch.device("cuda:0")
+    ev = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    side = {}
+    if not args.no_side and args.workload not in ("tiny",):
+        for name in SIDE_WORKLOADS:
+            if name == args.workload:
+                continue
+            run = VerifyRun(name, dev)
+            print("bench: side workload %s: %d copies, %d warmup + %d steps" % (name, run.copies, SIDE_WARMUP,
+                                                                               SIDE_STEPS), file=sys.stderr,
+                  flush=True)
+            side[name] = workload_figures(run, ev, stream, dev, SIDE_WARMUP, SIDE_STEPS)
+            del run
+            torch.cuda.empty_cache()
+
+    run = VerifyRun(args.workload, dev)
+    cfg = run.cfg
+    print("bench: %s: %d copies of %.1f MB, %d warmup + %d timed steps" % (cfg.name, run.copies, run.spec_bytes / 1e6,
+                                                                        args.warmup, args.steps), file=sys.stderr,
+          flush=True)
+    k1_mean, elapsed = run.region_ms(ev, stream, args.warmup, args.steps)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = cfg.positions() * args.steps / elapsed
+    acc, out = run.outcome()
+    needed = run.needed_bytes(acc)
+    calls = run.per_call_ms(ev, stream, PER_CALL_SAMPLES)
+    sol = sol_read_ms(needed, dev, ev, stream)
+    achieved = run.spec_bytes / (k1_mean * 1e-3) / 1e9
+
+    # acceptance telemetry: the histogram of accepted lengths after a call
+    last = run.last()
+    hist = sv.accept_histogram(last.accepted_len, cfg.k)
+    torch.cuda.synchronize()
+    a, b = ev.create(), ev.create()
+    ev.record(a, stream)
+    for _ in range(200):
+        sv.accept_histogram(last.accepted_len, cfg.k, out=hist, stream=stream)
+    ev.record(b, stream)
+    torch.cuda.synchronize()
+    hist_us = ev.elapsed_ms(a, b) / 200 * 1e3
+    ev.destroy(a)
+    ev.destroy(b)
+    ctl = sv.DraftLengthController()
+    ctl.update(hist.cpu())
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
+                   "logits": cfg.dtype, "arithmetic": "f32", "temperature": cfg.T,
+                   "draft": "one-hot" if cfg.onehot else ("none (greedy)" if cfg.T == 0 else "logits"),
+                   "input_copies_rotated": run.copies},
+        "hbm_gbps_whole_step": run.spec_bytes / (ms_per_step * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "kernel": "k_verify", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic("k_verify", cfg.name),
+                     "algorithmic_bytes_per_launch": run.spec_bytes, "needed_bytes_per_launch": needed,
+                     "frac_needed": needed / (k1_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "mean_launch_us": k1_mean * 1e3},
+        "sol": {"kernel": "k_sol_read", "bytes": needed, "mean_launch_us": sol * 1e3, "frac": sol / k1_mean},
+        "call_us": {"p10": float(np.percentile(calls, 10) * 1e3), "p50": float(np.percentile(calls, 50) * 1e3),
+                    "p90": float(np.percentile(calls, 90) * 1e3), "calls": len(calls),
+                    "how": "device time of single calls, each between its own HIP events, after the timed steps"},
+        "accept_histogram_us": hist_us,
+        "block_efficiency": ctl.efficiency,
+    }
+    res.update(acceptance_stats(acc, cfg.k))
+    res["parity_sample"] = sample_parity(cfg, run.host, acc[:run.host.n], out[:run.host.n], host_threads())
+    del run
+    torch.cuda.empty_cache()
+    if side:
+        res["workloads"] = side
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (%.0f s, all host threads, then one)" % args.cpu_seconds, file=sys.stderr,
+              flush=True)
+        res["cpu_baseline"] = cpu_baselines(cfg, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def _launchers(cfg, sets, sv, n, loss=False):
     """One prepared call per resident input copy (they rotate)."""
     out = []
@@ -332,6 +724,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-side", action="store_true",
+                    help="time only --workload (no ngram_tail / grpo / grpo_greedy side figures)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -349,6 +743,8 @@ def main(argv=None):
 
     if args.workload.startswith("lmhead_"):
         return bench_lm_head(args)
+    if args.workload in ("selfdraft", "ngram_tail", "grpo", "grpo_greedy", "tiny"):
+        return bench_verify(args)
 
     import speculative_decoding_verification_amd as sv
     import workloads
@@ -419,28 +815,24 @@ def main(argv=None):
         if loss:
             extra["mean_block_loss"] = last.block_loss.float().mean().item()
         needed = in_bytes
-    else:
-        acc = last.accepted_len.float()
-        full = int((acc == cfg.k).sum().item())
-        extra = {"mean_accepted_len": acc.mean().item(), "timeouts": int((acc == -2).sum().item()),
-                 "full_acceptance": full}
-        # every input copy holds the same logits, so every call needs the
-        # same rows: the decision rows of all sequences and the bonus row
-        # (target position k) of those that kept all k drafts
-        needed = in_bytes - (cfg.B - full) * cfg.V * cfg.elem_bytes
-        # acceptance telemetry: the histogram of accepted lengths after a call
-        hist = sv.accept_histogram(last.accepted_len, cfg.k)
+    achieved = needed / (k1_mean * 1e-3) / 1e9
+    # speed of light over the same buffers: the logits read once (labels,
+    # loss), or both logit arrays read and one fp32 array written (gradient)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    t, d = sets[0][0], sets[0][1]
+    sol_kernel = "k_sol_read_write" if grad else "k_sol_read"
+    for rep in range(2):  # the first pass warms up
         torch.cuda.synchronize()
         ev.record(region[0], stream)
-        for _ in range(200):
-            sv.accept_histogram(last.accepted_len, cfg.k, out=hist, stream=stream)
+        for _ in range(5):
+            if grad:
+                sv.sol_read_write(t, d, calls[0].grad, stream)
+            else:
+                sv.sol_read(t, sink, stream)
+                sv.sol_read(d, sink, stream)
         ev.record(region[1], stream)
         torch.cuda.synchronize()
-        ctl = sv.DraftLengthController()
-        ctl.update(hist.cpu())
-        extra["accept_histogram_us"] = ev.elapsed_ms(*region) / 200 * 1e3
-        extra["block_efficiency"] = ctl.efficiency
-    achieved = needed / (k1_mean * 1e-3) / 1e9
+    sol_ms = ev.elapsed_ms(*region) / 5
     for e in region:
         ev.destroy(e)
     del calls, sets
@@ -456,10 +848,10 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
-                   "logits": cfg.dtype, "temperature": cfg.T, "draft": "one-hot" if cfg.onehot else "logits",
+        "config": {"workload": args.workload, "blocks": cfg.B, "draft_positions": cfg.k, "vocab": cfg.V,
+                   "logits": cfg.dtype, "arithmetic": "f32", "temperature": cfg.T, "draft": "logits",
                    "input_copies_rotated": copies},
         "hbm_gbps_whole_step": needed / (ms_per_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBPS,
@@ -467,6 +859,7 @@ def main(argv=None):
                      "traffic": measured_traffic(kernel, args.workload),
                      "algorithmic_bytes_per_launch": needed, "all_rows_bytes_per_launch": in_bytes,
                      "mean_launch_us": k1_mean * 1e3},
+        "sol": {"kernel": sol_kernel, "bytes": in_bytes, "mean_launch_us": sol_ms * 1e3, "frac": sol_ms / k1_mean},
     }
     res.update(extra)
     if cfg.kind == "vat":
@@ -474,8 +867,9 @@ def main(argv=None):
     if loss:
         res["config"]["hard_weight"] = 1.0
     if not args.no_cpu_baseline:
-        print("bench: cpu baseline (%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, loss, grad)
+        print("bench: cpu baseline (%.0f s, all host threads, then one)" % args.cpu_seconds, file=sys.stderr,
+              flush=True)
+        res["cpu_baseline"] = cpu_baselines(cfg, args.cpu_seconds, loss, grad)
     print(json.dumps(res), flush=True)
     return 0
 

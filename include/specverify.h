@@ -509,6 +509,38 @@ sv_status sv_draft_len_init(sv_draft_len_ctl* ctl, const int32_t* choices, int32
  * current choice). */
 sv_status sv_draft_len_update(sv_draft_len_ctl* ctl, const int32_t* hist, int32_t k, int32_t* next_k);
 
+/*
+ * Speed-of-light references (measurement only; no passage of the pages
+ * defines them).  Plain streaming kernels with the memory traffic of the
+ * calls above and none of their arithmetic, so that a call's duration can be
+ * stated as a fraction of the fastest pass over the same bytes on the same
+ * device.
+ *
+ * sv_sol_read: reads `bytes` bytes at `data` (device) once with 16-byte
+ * non-temporal loads, the traffic of sv_verify and sv_vat_labels (every
+ * logit read once, only small outputs written).
+ *  data   device, 16-byte aligned; bytes a multiple of 16 (0: nothing runs)
+ *  sink   device, one uint32; written only if the XOR of the words one lane
+ *         loads equals a fixed constant (it keeps the loads from being
+ *         optimised away)
+ * Errors: SV_ERR_NULL_ARG, SV_ERR_MISALIGNED (data or bytes not 16-byte
+ * multiples), SV_ERR_BAD_SHAPE (too large for one launch), SV_ERR_HIP.
+ */
+sv_status sv_sol_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/*
+ * sv_sol_read_write: out[i] = a[i] - b[i] in fp32 for i in [0, n): two logit
+ * arrays read, one fp32 array written, the traffic of sv_vat_loss_grad
+ * (target and draft logits in, the gradient out).
+ *  a, b   device, [n] elements of `dtype`, 16-byte aligned
+ *  out    device, [n] fp32, 16-byte aligned; may not overlap a or b
+ *  n      a multiple of 4 (SV_F32) or 8 (SV_BF16); 0: nothing runs
+ * Errors: SV_ERR_NULL_ARG, SV_ERR_BAD_DTYPE, SV_ERR_MISALIGNED (pointers or
+ * n), SV_ERR_BAD_SHAPE (n < 0 or too large for one launch), SV_ERR_HIP.
+ */
+sv_status sv_sol_read_write(const void* a, const void* b, float* out, int64_t n, sv_dtype dtype,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,7 @@ STATUS = {0: "SV_OK", 1: "SV_ERR_NULL_ARG", 2: "SV_ERR_BAD_SHAPE", 3: "SV_ERR_BA
           4: "SV_ERR_BAD_TEMPERATURE", 5: "SV_ERR_WORKSPACE_TOO_SMALL", 6: "SV_ERR_HIP",
           7: "SV_ERR_BAD_DRAFT_KIND", 8: "SV_ERR_BAD_DECAY", 9: "SV_ERR_BAD_HARD_WEIGHT", 10: "SV_ERR_BAD_CONTROL",
           11: "SV_ERR_MISALIGNED", 12: "SV_ERR_CAPTURING", 13: "SV_ERR_SCRATCH_TOO_SMALL"}
+STATUS_CODE = {name: code for code, name in STATUS.items()}
 
 EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_bytes", "sv_verify", "sv_verify_ex",
                     "sv_verify_noalloc",
@@ -41,7 +42,7 @@ EXPORTED_SYMBOLS = ("sv_abi_version", "sv_status_str", "sv_verify_workspace_byte
                     "sv_vat_loss", "sv_vat_loss_grad",
                     "sv_lm_head_workspace_bytes", "sv_verify_lm_head_greedy", "sv_lm_head_sample_workspace_bytes",
                     "sv_verify_lm_head", "sv_accept_histogram",
-                    "sv_draft_len_init", "sv_draft_len_update")
+                    "sv_draft_len_init", "sv_draft_len_update", "sv_sol_read", "sv_sol_read_write")
 
 
 class SVError(RuntimeError):
@@ -153,6 +154,10 @@ def load_library():
                                       ctypes.c_float, i32]
     lib.sv_draft_len_update.restype = ctypes.c_int
     lib.sv_draft_len_update.argtypes = [ctypes.POINTER(DraftLenCtl), ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
+    lib.sv_sol_read.restype = ctypes.c_int
+    lib.sv_sol_read.argtypes = [vp, sz, vp, vp]
+    lib.sv_sol_read_write.restype = ctypes.c_int
+    lib.sv_sol_read_write.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int, vp]
     _lib = lib
     return lib
 
@@ -700,6 +705,35 @@ def accept_histogram(accepted_len, k: int, out=None, stream: Optional[int] = Non
     if st:
         raise SVError(st, "sv_accept_histogram", lib)
     return out
+
+
+def sol_read(data, sink, stream: Optional[int] = None) -> None:
+    """sv_sol_read over the bytes of a contiguous device tensor (a multiple
+    of 16 bytes, 16-byte aligned); sink: a device int32/uint32 tensor of at
+    least one element."""
+    lib = load_library()
+    if not data.is_contiguous() or sink.device != data.device:
+        raise ValueError("sol_read: contiguous data and a sink on the same device")
+    s = _stream_handle(data.device) if stream is None else stream
+    st = lib.sv_sol_read(_ptr(data), data.numel() * data.element_size(), _ptr(sink), s)
+    if st:
+        raise SVError(st, "sv_sol_read", lib)
+
+
+def sol_read_write(a, b, out, stream: Optional[int] = None) -> None:
+    """sv_sol_read_write: out = a - b in fp32 (a, b float32 or bfloat16 of the
+    same length as the float32 `out`, all contiguous on one device)."""
+    torch = _torch()
+    lib = load_library()
+    device = a.device
+    _check_dev("b", b, device, a.dtype, tuple(a.shape))
+    _check_dev("out", out, device, torch.float32)
+    if not a.is_contiguous() or out.numel() != a.numel():
+        raise ValueError("sol_read_write: contiguous operands of one length")
+    s = _stream_handle(device) if stream is None else stream
+    st = lib.sv_sol_read_write(_ptr(a), _ptr(b), _ptr(out), a.numel(), _dtype_code(a), s)
+    if st:
+        raise SVError(st, "sv_sol_read_write", lib)
 
 
 class DraftLengthController:

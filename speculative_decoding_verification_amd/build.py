@@ -39,17 +39,20 @@ def build(verbose: bool = False) -> str:
         g_obj = os.path.join(tmp, "sv_grid.o")
         c_obj = os.path.join(tmp, "sv_control.o")
         l_obj = os.path.join(tmp, "sv_lmhead.o")
+        s_obj = os.path.join(tmp, "sv_sol.o")
         cmds = [
             [cc, "-x", "hip", "--offload-arch=" + ARCH, *COMMON_FLAGS, *DEVICE_FLAGS, "-c",
              os.path.join(CSRC, "sv_kernels.hip"), "-o", k_obj],
             [cc, "-x", "hip", "--offload-arch=" + ARCH, *COMMON_FLAGS, *DEVICE_FLAGS, "-c",
              os.path.join(CSRC, "sv_lmhead.hip"), "-o", l_obj],
+            [cc, "-x", "hip", "--offload-arch=" + ARCH, *COMMON_FLAGS, *DEVICE_FLAGS, "-c",
+             os.path.join(CSRC, "sv_sol.hip"), "-o", s_obj],
             [cc, *COMMON_FLAGS, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, "sv_api.cpp"), "-o", a_obj],
             [cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, "sv_grid.cpp"), "-o", g_obj],
             [cc, *COMMON_FLAGS, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, "sv_control.cpp"), "-o", c_obj],
         ]
         tmp_so = os.path.join(tmp, "libspecverify.so")
-        cmds.append([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, l_obj, a_obj, g_obj, c_obj,
+        cmds.append([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, l_obj, s_obj, a_obj, g_obj, c_obj,
                      "-o", tmp_so])
         for cmd in cmds:
             if verbose:

@@ -638,4 +638,25 @@ sv_status sv_verify_lm_head(const sv_lm_head_sample_desc* desc, const void* targ
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+sv_status sv_sol_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream) {
+    if (bytes == 0) return SV_OK;
+    if (!data || !sink) return SV_ERR_NULL_ARG;
+    if (!sv::aligned16(data) || bytes % 16 != 0) return SV_ERR_MISALIGNED;
+    if (bytes / 16 > (size_t{1} << 40)) return SV_ERR_BAD_SHAPE;
+    const hipError_t e = sv::launch_sol_read(data, static_cast<int64_t>(bytes / 16), sink, stream);
+    return e == hipSuccess ? SV_OK : (e == hipErrorInvalidValue ? SV_ERR_BAD_SHAPE : SV_ERR_HIP);
+}
+
+sv_status sv_sol_read_write(const void* a, const void* b, float* out, int64_t n, sv_dtype dtype,
+                            hipStream_t stream) {
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_BAD_DTYPE;
+    if (n < 0 || n > (int64_t{1} << 42)) return SV_ERR_BAD_SHAPE;
+    if (n == 0) return SV_OK;
+    if (!a || !b || !out) return SV_ERR_NULL_ARG;
+    const int per_vec = dtype == SV_F32 ? 4 : 8;
+    if (!sv::aligned16(a) || !sv::aligned16(b) || !sv::aligned16(out) || n % per_vec != 0) return SV_ERR_MISALIGNED;
+    const hipError_t e = sv::launch_sol_read_write(a, b, out, n / per_vec, dtype == SV_F32 ? 4 : 2, stream);
+    return e == hipSuccess ? SV_OK : (e == hipErrorInvalidValue ? SV_ERR_BAD_SHAPE : SV_ERR_HIP);
+}
+
 }  // extern "C"

@@ -46,6 +46,7 @@
 #include <algorithm>
 #include <climits>
 #include <mutex>
+#include <type_traits>
 
 #include "sv_launch.h"
 
@@ -1882,95 +1883,131 @@ int blocks_per_cu_mode(int path) {
 namespace {
 
 // d(block loss)/d l_d(y) = w_i/T ((1 + lambda) q(y) - p(y) - lambda [y == h_i])
-// for one (row, chunk) item per wavefront, items dealt round-robin over the
-// grid's wavefronts.  p and q come from the logits and the row statistics
-// (m/T, Z) that sv_vat_loss wrote: p(y) = 2^(l(y) c2 - (m/T) log2(e)) / Z.
-// A row of weight 0 is written as zeros without reading its logits.
+// for one (row, chunk) item per wavefront, in blocks of two wavefronts, one
+// item each: the shape of the plain two-reads-one-write stream that ran
+// fastest, with the chunk's loads all in flight before its first store and
+// few enough registers for many wavefronts per SIMD.  p and q come from the
+// logits and the row statistics (m/T, Z) that sv_vat_loss wrote:
+// p(y) = 2^(l(y) c2 - (m/T) log2(e)) / Z.  A row of weight 0 is written as
+// zeros without reading its logits.
+constexpr int kGradBlock = 128;
+constexpr int kGradWaves = kGradBlock / kWave;
+
 template <int EB, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_vat_grad(GradPlan g) {
+__global__ __launch_bounds__(kGradBlock) void k_vat_grad(GradPlan g) {
     constexpr int PV = Elem<EB>::kPerVec;
     constexpr int CH = Chunk<EB>::kElems;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    // the item is the wavefront's: row parameters come through scalar loads
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * kGradWaves + wave;
+    if (item >= g.items) return;
+    int64_t row;
+    int c;
+    if (g.items <= INT_MAX) {
+        const uint32_t it = static_cast<uint32_t>(item), nc = static_cast<uint32_t>(g.chunks);
+        const uint32_t r32 = it / nc;
+        row = r32;
+        c = static_cast<int>(it - r32 * nc);
+    } else {
+        row = item / g.chunks;
+        c = static_cast<int>(item - row * g.chunks);
+    }
     const int64_t V = g.vocab;
     const float log2e = 1.4426950408889634f;
-    for (int64_t item = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; item < g.items;
-         item += waves) {
-        const int64_t row = item / g.chunks;
-        const int c = static_cast<int>(item - row * g.chunks);
-        const int64_t start = static_cast<int64_t>(c) * CH;
-        const int len = static_cast<int>(min(static_cast<int64_t>(CH), V - start));
-        float* const out = g.grad + row * V + start;
-        const float w = g.weights[row];
-        const float s = w * g.inv_t;
-        const float aq = s * (1.f + g.hard_weight), hh = s * g.hard_weight;
-        const float mt2 = g.row_stats[2 * row] * log2e, izt = 1.f / g.row_stats[2 * row + 1];
-        const float md2 = g.row_stats[2 * (g.rows + row)] * log2e, izd = 1.f / g.row_stats[2 * (g.rows + row) + 1];
-        const int64_t hx = static_cast<int64_t>(g.hard[row]) - start;  // the hard token's place in the chunk
-        const auto grad_of = [&](float lt, float ld, int64_t idx) {
-            const float p = exp2_hw(fmaf(lt, g.c2, -mt2)) * izt;
-            const float q = exp2_hw(fmaf(ld, g.c2, -md2)) * izd;
-            return fmaf(aq, q, -s * p) - (idx == hx ? hh : 0.f);
-        };
-        const char* rt = row_base(g.target, row, V, EB);
-        const char* rd = row_base(g.draft, row, V, EB);
-        if constexpr (VEC) {
-            typedef float f32x4_t __attribute__((ext_vector_type(4)));
-            const int nvec = len / PV;
-            const uint4* pt = reinterpret_cast<const uint4*>(rt + start * EB);
-            const uint4* pd = reinterpret_cast<const uint4*>(rd + start * EB);
-            uint4 at[kVecPerLane], ad[kVecPerLane];
-            if (w != 0.f) {
+    const int start = c * CH;
+    const int len = min(CH, static_cast<int>(V) - start);
+    float* const out = g.grad + row * V + start;
+    // the row's parameters, all loads issued together before the first use
+    const float w = g.weights[row];
+    const float2 st = *reinterpret_cast<const float2*>(g.row_stats + 2 * row);
+    const float2 sd = *reinterpret_cast<const float2*>(g.row_stats + 2 * (g.rows + row));
+    const int hard = g.hard[row];
+    // an empty statement that takes all five: the loads are not sunk below
+    // the weight test, so one wait covers them
+    asm volatile("" ::"s"(w), "s"(st.x), "s"(st.y), "s"(sd.x), "s"(sd.y), "s"(hard));
+    const float s = w * g.inv_t;
+    const float aq = s * (1.f + g.hard_weight), hh = s * g.hard_weight;
+    const float mt2 = st.x * log2e, izt = 1.f / st.y;
+    const float md2 = sd.x * log2e, izd = 1.f / sd.y;
+    const int64_t hard_at = static_cast<int64_t>(hard) - start;
+    const int hx = hard_at >= 0 && hard_at < CH ? static_cast<int>(hard_at) : -1;  // its place in the chunk
+    const auto grad_of = [&](float lt, float ld, int idx) {
+        const float p = exp2_hw(fmaf(lt, g.c2, -mt2)) * izt;
+        const float q = exp2_hw(fmaf(ld, g.c2, -md2)) * izd;
+        return fmaf(aq, q, -s * p) - (idx == hx ? hh : 0.f);
+    };
+    const char* rt = row_base(g.target, row, V, EB) + static_cast<int64_t>(start) * EB;
+    const char* rd = row_base(g.draft, row, V, EB) + static_cast<int64_t>(start) * EB;
+    if constexpr (VEC) {
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const int nvec = len / PV;
+        const uint4* pt = reinterpret_cast<const uint4*>(rt);
+        const uint4* pd = reinterpret_cast<const uint4*>(rd);
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(out);
+        if (w == 0.f) {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < kVecPerLane; ++j) {
-                    const int idx = j * kWave + lane;
-                    at[j] = idx < nvec ? load_stream(pt + idx) : make_uint4(0u, 0u, 0u, 0u);
-                    ad[j] = idx < nvec ? load_stream(pd + idx) : make_uint4(0u, 0u, 0u, 0u);
+            for (int j = 0; j < kVecPerLane; ++j) {
+                const int idx = j * kWave + lane;
+                if (idx < nvec) {
+#pragma unroll
+                    for (int e = 0; e < PV; e += 4) __builtin_nontemporal_store(z, dst + (idx * PV + e) / 4);
                 }
+            }
+            return;
+        }
+        // a whole chunk (every row's but the last) takes no per-vector tests,
+        // so its loads issue back to back
+        const auto run = [&](auto whole) {
+            constexpr bool kWhole = decltype(whole)::value;
+            uint4 at[kVecPerLane], ad[kVecPerLane];
+#pragma unroll
+            for (int j = 0; j < kVecPerLane; ++j) {
+                const int idx = j * kWave + lane;
+                at[j] = kWhole || idx < nvec ? load_stream(pt + idx) : make_uint4(0u, 0u, 0u, 0u);
+                ad[j] = kWhole || idx < nvec ? load_stream(pd + idx) : make_uint4(0u, 0u, 0u, 0u);
             }
 #pragma unroll
             for (int j = 0; j < kVecPerLane; ++j) {
                 const int idx = j * kWave + lane;
-                if (idx >= nvec) continue;
-                float o[PV];
-                if (w != 0.f) {
-                    float ft[PV], fd[PV];
-                    Elem<EB>::decode(at[j], ft);
-                    Elem<EB>::decode(ad[j], fd);
-#pragma unroll
-                    for (int e = 0; e < PV; ++e) o[e] = grad_of(ft[e], fd[e], static_cast<int64_t>(idx) * PV + e);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < PV; ++e) o[e] = 0.f;
-                }
-                f32x4_t* dst = reinterpret_cast<f32x4_t*>(out + static_cast<int64_t>(idx) * PV);
+                if (!kWhole && idx >= nvec) continue;
+                float ft[PV], fd[PV];
+                Elem<EB>::decode(at[j], ft);
+                Elem<EB>::decode(ad[j], fd);
 #pragma unroll
                 for (int e = 0; e < PV; e += 4) {
-                    const f32x4_t v = {o[e], o[e + 1], o[e + 2], o[e + 3]};
-                    __builtin_nontemporal_store(v, dst + e / 4);
+                    const f32x4_t v = {grad_of(ft[e], fd[e], idx * PV + e),
+                                       grad_of(ft[e + 1], fd[e + 1], idx * PV + e + 1),
+                                       grad_of(ft[e + 2], fd[e + 2], idx * PV + e + 2),
+                                       grad_of(ft[e + 3], fd[e + 3], idx * PV + e + 3)};
+                    __builtin_nontemporal_store(v, dst + (idx * PV + e) / 4);
                 }
             }
-        } else {
-            for (int e = 0; e < Chunk<EB>::kPerLane; ++e) {
-                const int idx = e * kWave + lane;
-                if (idx >= len) break;
-                out[idx] = w != 0.f ? grad_of(Elem<EB>::at(rt, start + idx), Elem<EB>::at(rd, start + idx), idx)
-                                    : 0.f;
-            }
+        };
+        if (nvec == kWave * kVecPerLane)
+            run(std::true_type{});
+        else
+            run(std::false_type{});
+    } else {
+        for (int e = 0; e < Chunk<EB>::kPerLane; ++e) {
+            const int idx = e * kWave + lane;
+            if (idx >= len) break;
+            out[idx] = w != 0.f ? grad_of(Elem<EB>::at(rt, idx), Elem<EB>::at(rd, idx), idx) : 0.f;
         }
     }
 }
 
 template <int EB, bool VEC>
 hipError_t launch_grad_typed(const GradPlan& g, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-    // 8 blocks of 4 wavefronts per compute unit at most; fewer for small calls
-    const int64_t blocks = std::min<int64_t>(256 * 8, (g.items + kWavesPerBlock - 1) / kWavesPerBlock);
+    const int64_t blocks = (g.items + kGradWaves - 1) / kGradWaves;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipError_t e;
     if (ev0 && ev1) {
         e = hipEventRecord(ev0, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_vat_grad<EB, VEC>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream, g);
+    hipLaunchKernelGGL((k_vat_grad<EB, VEC>), dim3(static_cast<unsigned>(blocks)), dim3(kGradBlock), 0, stream, g);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev0 && ev1) e = hipEventRecord(ev1, stream);

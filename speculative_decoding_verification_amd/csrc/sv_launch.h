@@ -186,4 +186,11 @@ struct GradPlan {
 
 hipError_t launch_vat_grad(const GradPlan& g, hipStream_t stream, hipEvent_t probe_start, hipEvent_t probe_stop);
 
+// Speed-of-light references (sv_sol.hip): a plain read of nvec 16-byte
+// vectors, and a read of two arrays of nvec 16-byte vectors with one fp32
+// array of the same element count written.
+hipError_t launch_sol_read(const void* data, int64_t nvec, uint32_t* sink, hipStream_t stream);
+hipError_t launch_sol_read_write(const void* a, const void* b, float* out, int64_t nvec, int elem_bytes,
+                                 hipStream_t stream);
+
 }  // namespace sv

@@ -481,6 +481,26 @@ def test_lm_head_rows_times_hidden_limit(lib):
     assert lib.sv_lm_head_workspace_bytes(ctypes.byref(_lm_desc(B=8191, k=63, V=1000, D=4096))) > 0
 
 
+def test_sol_entry_points_check_arguments(lib):
+    """The speed-of-light references reject bad arguments on the host;
+    nothing reaches a kernel (null device pointers with a nonzero size, or
+    zero sizes, which launch nothing)."""
+    vp = ctypes.c_void_p
+    A = vp(4096)  # never dereferenced: every call below fails or does nothing first
+    assert lib.sv_sol_read(None, 0, None, None) == 0
+    assert lib.sv_sol_read(None, 16, A, None) == sv.STATUS_CODE["SV_ERR_NULL_ARG"]
+    assert lib.sv_sol_read(A, 16, None, None) == sv.STATUS_CODE["SV_ERR_NULL_ARG"]
+    assert lib.sv_sol_read(vp(4104), 16, A, None) == sv.STATUS_CODE["SV_ERR_MISALIGNED"]
+    assert lib.sv_sol_read(A, 24, A, None) == sv.STATUS_CODE["SV_ERR_MISALIGNED"]
+    assert lib.sv_sol_read_write(A, A, A, 8, 2, None) == sv.STATUS_CODE["SV_ERR_BAD_DTYPE"]
+    assert lib.sv_sol_read_write(A, A, A, -4, 0, None) == sv.STATUS_CODE["SV_ERR_BAD_SHAPE"]
+    assert lib.sv_sol_read_write(None, None, None, 0, 0, None) == 0
+    assert lib.sv_sol_read_write(A, None, A, 8, 0, None) == sv.STATUS_CODE["SV_ERR_NULL_ARG"]
+    assert lib.sv_sol_read_write(A, A, A, 6, 0, None) == sv.STATUS_CODE["SV_ERR_MISALIGNED"]
+    assert lib.sv_sol_read_write(A, A, A, 12, 1, None) == sv.STATUS_CODE["SV_ERR_MISALIGNED"]
+    assert lib.sv_sol_read_write(A, vp(4100), A, 8, 0, None) == sv.STATUS_CODE["SV_ERR_MISALIGNED"]
+
+
 def test_missing_library_raises_and_package_has_no_fallback(monkeypatch, tmp_path):
     """Without the built library the binding raises instead of computing
     anything on the CPU, and no module of the package imports the oracle."""
