@@ -49,7 +49,8 @@ class SVError(RuntimeError):
     def __init__(self, status: int, where: str, lib=None):
         self.status = status
         msg = STATUS.get(status, "status %d" % status)
-        if lib is not None:
+        if lib is not None and hasattr(lib, "sv_status_str"):
+            lib.sv_status_str.restype = ctypes.c_char_p
             msg = lib.sv_status_str(status).decode()
         super().__init__("%s: %s" % (where, msg))
 
@@ -149,17 +150,22 @@ def load_library():
     i32 = ctypes.c_int32
     lib.sv_accept_histogram.restype = ctypes.c_int
     lib.sv_accept_histogram.argtypes = [vp, i32, i32, vp, vp]
-    lib.sv_draft_len_init.restype = ctypes.c_int
-    lib.sv_draft_len_init.argtypes = [ctypes.POINTER(DraftLenCtl), ctypes.POINTER(i32), i32, ctypes.c_float,
-                                      ctypes.c_float, i32]
-    lib.sv_draft_len_update.restype = ctypes.c_int
-    lib.sv_draft_len_update.argtypes = [ctypes.POINTER(DraftLenCtl), ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
+    _bind_control(lib)
     lib.sv_sol_read.restype = ctypes.c_int
     lib.sv_sol_read.argtypes = [vp, sz, vp, vp]
     lib.sv_sol_read_write.restype = ctypes.c_int
     lib.sv_sol_read_write.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int, vp]
     _lib = lib
     return lib
+
+
+def _bind_control(lib) -> None:
+    i32 = ctypes.c_int32
+    lib.sv_draft_len_init.restype = ctypes.c_int
+    lib.sv_draft_len_init.argtypes = [ctypes.POINTER(DraftLenCtl), ctypes.POINTER(i32), i32, ctypes.c_float,
+                                      ctypes.c_float, i32]
+    lib.sv_draft_len_update.restype = ctypes.c_int
+    lib.sv_draft_len_update.argtypes = [ctypes.POINTER(DraftLenCtl), ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
 
 
 def _torch():
@@ -740,10 +746,15 @@ class DraftLengthController:
     """The host-side draft-length rule (sv_draft_len_init / sv_draft_len_update):
     choices ascending (default 5, 7, 9, 11), start at the shortest, move one
     step up or down after `patience` consecutive steps whose block efficiency
-    is at least up_frac*(k+1) or at most down_frac*(k+1)."""
+    is at least up_frac*(k+1) or at most down_frac*(k+1).  `lib`: a ctypes
+    library exporting the two controller symbols (default: libspecverify)."""
 
-    def __init__(self, choices=(5, 7, 9, 11), up_frac: float = 0.9, down_frac: float = 0.5, patience: int = 2):
-        lib = load_library()
+    def __init__(self, choices=(5, 7, 9, 11), up_frac: float = 0.9, down_frac: float = 0.5, patience: int = 2,
+                 lib=None):
+        if lib is None:
+            lib = load_library()
+        else:
+            _bind_control(lib)
         self._lib = lib
         self.ctl = DraftLenCtl()
         arr = (ctypes.c_int32 * len(choices))(*choices)

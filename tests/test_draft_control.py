@@ -4,10 +4,20 @@ rule as that section states it, restated here in plain Python: a fixed set of
 lengths, start at the shortest, move up after two consecutive steps whose
 block efficiency is near the length's limit, down after two consecutive steps
 that are too low, one noisy step moves nothing."""
+import ctypes
+import os
+
 import numpy as np
 import pytest
 
 import speculative_decoding_verification_amd as sv
+
+# A host-only build of the controller (the sanitizer run sets this).
+_LIB = ctypes.CDLL(os.environ["SV_CONTROL_LIB"]) if os.environ.get("SV_CONTROL_LIB") else None
+
+
+def controller(*args, **kw):
+    return sv.DraftLengthController(*args, lib=_LIB, **kw)
 
 
 def hist_for(k, lengths):
@@ -51,7 +61,7 @@ class PlainRule:
 
 
 def test_starts_short_and_climbs_after_two_good_steps():
-    c = sv.DraftLengthController()
+    c = controller()
     assert c.k == 5
     good = hist_for(5, [5] * 9 + [4])      # efficiency 5.9 of 6
     assert c.update(good) == 5             # one step moves nothing
@@ -66,7 +76,7 @@ def test_starts_short_and_climbs_after_two_good_steps():
 
 
 def test_one_noisy_step_moves_nothing_and_low_steps_step_down():
-    c = sv.DraftLengthController()
+    c = controller()
     good = hist_for(5, [5] * 10)
     bad = hist_for(5, [0] * 10)            # efficiency 1 of 6
     c.update(good)
@@ -82,13 +92,13 @@ def test_one_noisy_step_moves_nothing_and_low_steps_step_down():
 def test_efficiency_of_geometric_acceptance():
     """Kept with probability alpha: E[tokens per cycle] = sum_{j=0..k} alpha^j."""
     for alpha in (0.5, 0.9, 0.96):
-        c = sv.DraftLengthController()
+        c = controller()
         c.update(hist_geometric(5, alpha))
         assert c.efficiency == pytest.approx(sum(alpha ** j for j in range(6)), rel=1e-4)
 
 
 def test_invalid_and_timed_out_sequences_are_not_counted():
-    c = sv.DraftLengthController()
+    c = controller()
     h = hist_for(5, [5] * 4)
     h[6] = 100   # invalid tokens
     h[7] = 7     # timed out
@@ -104,7 +114,7 @@ def test_matches_the_plain_rule_on_random_runs():
         down = float(rng.uniform(0.1, up - 0.05))
         pat = int(rng.integers(1, 4))
         choices = sorted(rng.choice(np.arange(2, 20), size=int(rng.integers(1, 6)), replace=False).tolist())
-        c = sv.DraftLengthController(choices, up, down, pat)
+        c = controller(choices, up, down, pat)
         plain = PlainRule(choices, np.float32(up), np.float32(down), pat)
         for step in range(60):
             k = c.k
@@ -116,13 +126,13 @@ def test_matches_the_plain_rule_on_random_runs():
 
 def test_bad_arguments():
     with pytest.raises(sv.SVError):
-        sv.DraftLengthController((5, 5, 7))            # not increasing
+        controller((5, 5, 7))            # not increasing
     with pytest.raises(sv.SVError):
-        sv.DraftLengthController((5, 7), up_frac=0.4, down_frac=0.5)
+        controller((5, 7), up_frac=0.4, down_frac=0.5)
     with pytest.raises(sv.SVError):
-        sv.DraftLengthController((5, 70))              # beyond 64
+        controller((5, 70))              # beyond 64
     with pytest.raises(sv.SVError):
-        sv.DraftLengthController(tuple(range(1, 10)))  # more than 8 choices
-    c = sv.DraftLengthController()
+        controller(tuple(range(1, 10)))  # more than 8 choices
+    c = controller()
     with pytest.raises(ValueError):
         c.update([1, 2])

@@ -20,10 +20,12 @@ DW, DF, RW, RF, BW, BF = range(6)
 
 @pytest.fixture(scope="module")
 def probe(tmp_path_factory):
-    out = str(tmp_path_factory.mktemp("grid") / "libgridprobe.so")
-    subprocess.check_call(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-I", CSRC,
-                           os.path.join(CSRC, "sv_grid.cpp"), os.path.join(ROOT, "tests", "grid_probe.cpp"),
-                           "-o", out])
+    out = os.environ.get("SV_GRID_PROBE_LIB")  # a sanitizer build, when set
+    if not out:
+        out = str(tmp_path_factory.mktemp("grid") / "libgridprobe.so")
+        subprocess.check_call(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-I", CSRC,
+                               os.path.join(CSRC, "sv_grid.cpp"), os.path.join(ROOT, "tests", "grid_probe.cpp"),
+                               "-o", out])
     lib = ctypes.CDLL(out)
     i32, i64, p32 = ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
     lib.probe_plan.argtypes = [i32, i64, i64, i32, i32, i64, i64, i64, i64, p32]
