@@ -26,6 +26,28 @@ LOSS_ATOL = 1e-6
 FLT_MIN = float(np.finfo(np.float32).tiny)
 
 
+def pooled(fn, idx, workers=None):
+    """fn(one-element index array) for every element of idx on a thread pool
+    (the oracle's C calls run without Python's lock), the per-element
+    results (oracle result objects) joined along their first axis."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    idx = np.asarray(idx)
+    workers = workers or max(1, min(16, os.cpu_count() or 1, len(idx)))
+    with ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(lambda i: fn(idx[i:i + 1]), range(len(idx))))
+    if isinstance(parts[0], np.ndarray):
+        return np.concatenate(parts, axis=0)
+    cls = type(parts[0])
+
+    def join(name):
+        vals = [getattr(q, name, None) for q in parts]
+        return None if vals[0] is None else np.concatenate(vals, axis=0)
+
+    return cls(**{name: join(name) for name in cls.__slots__})
+
+
 def to_torch(a, device):
     import torch
 

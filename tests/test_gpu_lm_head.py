@@ -18,6 +18,7 @@ import pytest
 
 import oracle
 import workloads
+from parity import pooled
 from workloads import bf16_bits_to_f32, round_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -144,6 +145,26 @@ def test_lm_head_unplanted_gaussian_logits(dev):
     _compare(h, w, x, got, orc)
 
 
+def test_lm_head_unplanted_full_vocabulary_and_hidden_size(dev):
+    """No planted margin at the workloads' real sizes (V=151936, D=4096): every
+    argmax is the maximum of 151936 Gaussian logits (top-two gaps of a few
+    hundredths and below), summed over 4096 products; every row's argmax and
+    every sequence's decision against the oracle."""
+    rng = np.random.default_rng(83)
+    B, k, V, D = 6, 5, 151936, 4096
+    h = round_to_bf16_bits(rng.standard_normal((B, k + 1, D)).astype(np.float32))
+    w = workloads.lm_head_weight(workloads.LM_CONFIGS["lmhead_selfdraft"])  # z / sqrt(D), [V][D] bf16
+    assert w.shape == (V, D)
+    every = np.arange(B)
+    g = pooled(lambda i: oracle.lm_head_greedy(h[i], w, np.zeros((1, k), np.int32)), every).argmax
+    x = np.where(rng.random((B, k)) < 0.85, g[:, :k], rng.integers(0, V, (B, k))).astype(np.int32)
+    _say("case lm_head unplanted B=%d k=%d V=%d D=%d" % (B, k, V, D))
+    got = _run_gpu(h, w, x, dev)
+    orc = pooled(lambda i: oracle.lm_head_greedy(h[i], w, x[i]), every)
+    amb = _compare(h, w, x, got, orc)
+    _say("  ambiguous positions: %d of %d; smallest top-two gap %.3g" % (amb, B * (k + 1), float(orc.top2_gap.min())))
+
+
 def test_lm_head_integer_ties_lowest_index(dev):
     """Integer inputs: every logit is exact in fp32 and ties are common; the
     lowest index must win, bit for bit."""
@@ -182,17 +203,19 @@ def test_lm_head_repeat_calls_are_bitwise_identical(dev):
         assert np.array_equal(u, v)
 
 
-@pytest.mark.parametrize("name,sample", [("lmhead_selfdraft", (0, 127)), ("lmhead_grpo", (201,))])
-def test_lm_head_full_size_sampled(dev, name, sample):
-    """Full workload on the GPU; every sequence checked for consistency, the
-    sampled sequences against the oracle over the whole vocabulary."""
+@pytest.mark.parametrize("name,seed", [("lmhead_selfdraft", 11), ("lmhead_grpo", 12)])
+def test_lm_head_full_size_sampled(dev, name, seed):
+    """Full workload on the GPU; every sequence checked for consistency, 8
+    sequences (the first, the last and 6 drawn) against the oracle over the
+    whole vocabulary."""
     cfg = workloads.LM_CONFIGS[name]
     _say("case lm_head full %s B=%d k=%d V=%d D=%d" % (name, cfg.B, cfg.k, cfg.V, cfg.D))
     wl = workloads.generate_lm_head(cfg)
     acc, out, am = _run_gpu(wl.hidden, wl.weight, wl.tokens, dev)
     _consistent(acc, out, am, wl.tokens, cfg.V)
-    idx = np.asarray(sample)
-    orc = oracle.lm_head_greedy(wl.hidden[idx], wl.weight, wl.tokens[idx])
+    drawn = np.random.default_rng(seed).choice(np.arange(1, cfg.B - 1), 6, replace=False)
+    idx = np.unique(np.concatenate([[0, cfg.B - 1], drawn]))
+    orc = pooled(lambda i: oracle.lm_head_greedy(wl.hidden[i], wl.weight, wl.tokens[i]), idx)
     _compare(wl.hidden[idx], wl.weight, wl.tokens[idx], (acc[idx], out[idx], am[idx]), orc)
     # the planted margin makes the planted token the choice almost everywhere
     assert np.mean(am == wl.planted) > 0.99

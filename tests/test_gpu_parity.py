@@ -12,8 +12,8 @@ import pytest
 
 import oracle
 import workloads
-from parity import (check_row_stats, compare_vat, compare_vat_loss, compare_verify, run_vat_gpu, run_vat_loss_gpu,
-                    run_verify_gpu, to_torch)
+from parity import (check_row_stats, compare_vat, compare_vat_loss, compare_verify, pooled, run_vat_gpu,
+                    run_vat_loss_gpu, run_verify_gpu, to_torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,8 +46,8 @@ def _verify_case(wl, dev, T=None, onehot=None, seq_index=None):
         rep = compare_verify(gpu, orc, cfg.k, cfg.V, T == 0.0)
     else:
         idx = np.asarray(seq_index)
-        sub_d = wl.draft[idx] if wl.draft is not None else None
-        orc = oracle.verify(wl.target[idx], sub_d, wl.tokens[idx], wl.uniforms[idx], T, onehot=oh)
+        orc = pooled(lambda i: oracle.verify(wl.target[i], wl.draft[i] if wl.draft is not None else None,
+                                             wl.tokens[i], wl.uniforms[i], T, onehot=oh), idx)
         gsub = {k: v[idx] for k, v in gpu.items() if k != "row_stats"}
         rows_per = cfg.k + 1
         st_t = gpu["row_stats"][: wl.n * rows_per].reshape(wl.n, rows_per, 2)[idx].reshape(-1, 2)
@@ -149,7 +149,7 @@ def _compare_grad(g, target, draft, hard, weights, T, hw):
     T = float(np.float32(T))
     hw = float(np.float32(hw))
     w = weights.astype(np.float64)
-    o = oracle.vat_loss_grad(target, draft, hard, w, T, hw)
+    o = pooled(lambda i: oracle.vat_loss_grad(target[i], draft[i], hard[i], w[i], T, hw), np.arange(len(w)))
     p = _softmax_rows(_logits_f64(target), T)
     q = _softmax_rows(_logits_f64(draft), T)
     eh = np.zeros_like(p)
@@ -394,7 +394,7 @@ def test_full_ngram_tail(dev):
 def test_full_grpo_sampled(dev):
     cfg = workloads.get_config("grpo")
     wl = workloads.generate(cfg)
-    idx = np.random.default_rng(1).choice(cfg.B, 40, replace=False)
+    idx = np.random.default_rng(1).choice(cfg.B, 96, replace=False)
     idx.sort()
     _verify_case(wl, dev, seq_index=idx)
 
@@ -424,14 +424,15 @@ def test_full_vat_sampled(dev):
     dec = float(np.float32(cfg.decay))
     want = np.where(i[None, :] < fr[:, None], 1.0, dec ** np.maximum(i[None, :] - fr[:, None], 0))
     assert np.allclose(w, want, rtol=1e-7, atol=0)
-    idx = np.random.default_rng(5).choice(cfg.B, 24, replace=False)
+    idx = np.random.default_rng(5).choice(cfg.B, 64, replace=False)
     idx.sort()
     ti = torch.as_tensor(idx, device=dev)
     tl = t.index_select(0, ti).cpu().numpy()
     dl = d.index_select(0, ti).cpu().numpy()
     xs = x.index_select(0, ti).cpu().numpy()
     us = u.index_select(0, ti).cpu().numpy()
-    orc = oracle.vat_labels(tl, dl, xs, us, cfg.T, float(np.float32(cfg.decay)))
+    dec = float(np.float32(cfg.decay))
+    orc = pooled(lambda i: oracle.vat_labels(tl[i], dl[i], xs[i], us[i], cfg.T, dec), np.arange(len(idx)))
     gpu = {"first_reject": fr[idx], "accept_mask": mask[idx], "weights": w[idx],
            "probs": res.probs.cpu().numpy()[idx]}
     rep = compare_vat(gpu, orc, cfg.k, cfg.decay, False)
@@ -455,14 +456,15 @@ def test_full_vat_loss_sampled(dev):
     fr = res.first_reject.cpu().numpy()
     loss = res.block_loss.cpu().numpy()
     assert np.all((fr >= 0) & (fr <= cfg.k)) and np.all(np.isfinite(loss)) and np.all(loss > 0)
-    idx = np.random.default_rng(6).choice(cfg.B, 16, replace=False)
+    idx = np.random.default_rng(6).choice(cfg.B, 64, replace=False)
     idx.sort()
     ti = torch.as_tensor(idx, device=dev)
     tl, dl = t.index_select(0, ti).cpu().numpy(), d.index_select(0, ti).cpu().numpy()
     xs, us, hs = (a.index_select(0, ti).cpu().numpy() for a in (x, u, h))
     dec = float(np.float32(cfg.decay))
-    orc = oracle.vat_loss(tl, dl, xs, us, hs, cfg.T, dec, 1.0)
-    lab = oracle.vat_labels(tl, dl, xs, us, cfg.T, dec)
+    every = np.arange(len(idx))
+    orc = pooled(lambda i: oracle.vat_loss(tl[i], dl[i], xs[i], us[i], hs[i], cfg.T, dec, 1.0), every)
+    lab = pooled(lambda i: oracle.vat_labels(tl[i], dl[i], xs[i], us[i], cfg.T, dec), every)
     gpu = {"first_reject": fr[idx], "accept_mask": res.accept_mask.cpu().numpy()[idx],
            "weights": res.weights.cpu().numpy()[idx], "soft_ce": res.soft_ce.cpu().numpy()[idx],
            "hard_ce": res.hard_ce.cpu().numpy()[idx], "block_loss": loss[idx]}
@@ -486,7 +488,7 @@ def test_full_vat_loss_grad_sampled(dev):
     rs = g.sum(dim=2, dtype=torch.float64)
     torch.cuda.synchronize()
     assert float(rs.abs().max()) < 1e-4
-    idx = np.random.default_rng(7).choice(cfg.B, 6, replace=False)
+    idx = np.random.default_rng(7).choice(cfg.B, 16, replace=False)
     idx.sort()
     ti = torch.as_tensor(idx, device=dev)
     gs = g.index_select(0, ti).cpu().numpy()
