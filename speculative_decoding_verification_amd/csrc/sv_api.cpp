@@ -162,7 +162,7 @@ bool fill_plan(const Shape& s, float temperature, float decay, bool vec, Plan* p
     const int64_t per_block = kWavesPerBlock * nc;
     const int64_t dec_items = s.loss ? s.k * s.chunks : static_cast<int64_t>(pl->dec_rows) * pl->segs * per_block;
     if (!plan_task_grid(pl->batch, dec_items, s.chunks, has_resid, has_bonus, per_block, per_block,
-                        kWavesPerBlock * pl->nc_res, resident, &pl->grid))
+                        kWavesPerBlock * pl->nc_res, resident, &pl->grid, !s.loss))
         return false;
     // Every decision worker block before every finisher: position-major.
     pl->pos_major = !s.loss && pl->grid.lag_a >= pl->batch;

@@ -9,6 +9,7 @@ namespace {
 
 struct PhaseRoles {
     bool a;  // phase A (decision, residual) or phase B (bonus)
+    bool df;  // phase A holds the decision finishers (not placed first)
     int32_t batch, w_dec, w_res, w_bonus;
     bool has_resid;
     int32_t lag_a, lag_r, lag_f, lag_b;
@@ -19,7 +20,7 @@ struct PhaseRoles {
         int32_t r = 0;
         if (a) {
             if (in(g)) r |= kBitDecWorker;
-            if (in(g - lag_a)) r |= kBitDecFinisher;
+            if (df && in(g - lag_a)) r |= kBitDecFinisher;
             if (has_resid && in(g - lag_a - lag_r)) r |= kBitResWorker;
             if (has_resid && in(g - lag_a - lag_r - lag_f)) r |= kBitResFinisher;
         } else {
@@ -44,8 +45,9 @@ struct PhaseRoles {
 }  // namespace
 
 bool build_task_grid(int32_t batch, int32_t w_dec, int32_t w_res, int32_t w_bonus, bool has_resid, bool has_bonus,
-                     int32_t lag_a, int32_t lag_r, int32_t lag_f, int32_t lag_b, TaskGrid* tg) {
+                     int32_t lag_a, int32_t lag_r, int32_t lag_f, int32_t lag_b, TaskGrid* tg, bool fin_first) {
     *tg = TaskGrid{};
+    tg->fin_first = fin_first ? 1 : 0;
     tg->batch = batch;
     tg->w_dec = w_dec;
     tg->w_res = has_resid ? w_res : 0;
@@ -61,9 +63,19 @@ bool build_task_grid(int32_t batch, int32_t w_dec, int32_t w_res, int32_t w_bonu
 
     int64_t next_block = 0;
     int n = 0;
+    if (fin_first) {
+        // one finisher per group, decoded as sequence g - lag_a = 0 .. B-1
+        Segment& s = tg->seg[n++];
+        s.first_block = 0;
+        s.first_group = tg->lag_a;
+        s.group_blocks = 1;
+        s.roles = kBitDecFinisher;
+        s.inv_group_blocks = 1.0f;
+        next_block = batch;
+    }
     for (int phase = 0; phase < 2; ++phase) {
         if (phase == 1 && !has_bonus) break;
-        const PhaseRoles pr{phase == 0, batch, w_dec, tg->w_res, tg->w_bonus, has_resid,
+        const PhaseRoles pr{phase == 0, !fin_first, batch, w_dec, tg->w_res, tg->w_bonus, has_resid,
                             tg->lag_a, tg->lag_r, tg->lag_f, tg->lag_b};
         const int64_t B = batch;
         std::vector<int64_t> bp;
@@ -115,7 +127,7 @@ bool build_task_grid(int32_t batch, int32_t w_dec, int32_t w_res, int32_t w_bonu
 
 bool plan_task_grid(int32_t batch, int64_t dec_items, int64_t chunks, bool has_resid, bool has_bonus,
                     int64_t per_block_dec, int64_t per_block_bonus, int64_t per_block_res, int64_t resident_blocks,
-                    TaskGrid* tg) {
+                    TaskGrid* tg, bool allow_fin_first) {
     const auto ceil_div = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
     if (batch < 1 || dec_items < 1 || chunks < 1 || per_block_dec < 1 || per_block_bonus < 1 || per_block_res < 1)
         return false;
@@ -134,8 +146,10 @@ bool plan_task_grid(int32_t batch, int64_t dec_items, int64_t chunks, bool has_r
     const int32_t lag_r = 0;
     const int32_t lag_f = has_resid ? lag(resident_blocks / 2, group_a) : 0;
     const int32_t lag_b = has_bonus ? lag(resident_blocks, w_bonus + 1) : 0;
+    const bool fin_first = allow_fin_first && lag_a >= batch && static_cast<int64_t>(batch) * 8 <= resident_blocks;
     return build_task_grid(batch, static_cast<int32_t>(w_dec), static_cast<int32_t>(w_res),
-                           static_cast<int32_t>(w_bonus), has_resid, has_bonus, lag_a, lag_r, lag_f, lag_b, tg);
+                           static_cast<int32_t>(w_bonus), has_resid, has_bonus, lag_a, lag_r, lag_f, lag_b, tg,
+                           fin_first);
 }
 
 }  // namespace sv

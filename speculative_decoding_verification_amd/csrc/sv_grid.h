@@ -10,7 +10,10 @@
 //   bonus workers of sequence h              (w_bonus blocks, if h < B)
 //   the bonus finisher of h - lag_b          (1 block)
 // A role only waits on roles of the same sequence placed before it, so with
-// blocks dispatched in index order every wait ends.  The lags (in groups)
+// blocks dispatched in index order every wait ends; the one exception is a
+// grid of about one residency whose decision finishers are all placed first
+// (fin_first): they wait on workers dispatched after them, which always find
+// a slot since the finishers hold at most an eighth of them.  The lags (in groups)
 // place a finisher about one residency of blocks behind the blocks it waits
 // on, so finishers run while later sequences stream.
 //
@@ -58,7 +61,7 @@ struct Role {
     int32_t index;  // worker index within the sequence
 };
 
-constexpr int kMaxSegments = 12;  // phase A has at most 8, phase B at most 4
+constexpr int kMaxSegments = 13;  // the finishers placed first, phase A at most 8, phase B at most 4
 
 // A run of groups with the same roles.
 struct Segment {
@@ -75,6 +78,7 @@ struct TaskGrid {
     int32_t lag_a, lag_r, lag_f, lag_b;  // in groups
     int32_t n_segments;
     int32_t total_blocks;
+    int32_t fin_first;  // 1: the B decision finishers are blocks 0 .. B-1, before every worker
     Segment seg[kMaxSegments];
 };
 
@@ -133,14 +137,17 @@ SV_HOST_DEVICE inline Role decode_role(const TaskGrid& tg, int32_t blk) {
 // decision rows, `per_block_bonus` chunks of the bonus row and
 // `per_block_res` chunk pairs of the residual; the lags are derived from the
 // number of blocks the device keeps resident.  Returns false if the grid
-// does not fit the limits.
+// does not fit the limits.  With allow_fin_first, a grid whose decision
+// workers all come before its first finisher (one residency) places the
+// decision finishers first when they take at most an eighth of the resident
+// blocks.
 bool plan_task_grid(int32_t batch, int64_t dec_items, int64_t chunks, bool has_resid, bool has_bonus,
                     int64_t per_block_dec, int64_t per_block_bonus, int64_t per_block_res, int64_t resident_blocks,
-                    TaskGrid* tg);
+                    TaskGrid* tg, bool allow_fin_first = false);
 
 // Host: the segments of a grid.  Returns false if the grid does not fit the
 // limits (more than 2^31 - 1 blocks, or lags outside [0, B]).
 bool build_task_grid(int32_t batch, int32_t w_dec, int32_t w_res, int32_t w_bonus, bool has_resid, bool has_bonus,
-                     int32_t lag_a, int32_t lag_r, int32_t lag_f, int32_t lag_b, TaskGrid* tg);
+                     int32_t lag_a, int32_t lag_r, int32_t lag_f, int32_t lag_b, TaskGrid* tg, bool fin_first = false);
 
 }  // namespace sv

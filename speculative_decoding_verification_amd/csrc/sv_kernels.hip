@@ -1567,6 +1567,16 @@ __device__ __forceinline__ void bonus_worker(const Plan& pl, int b, int s, TailS
     if (!pl.row_stats_out && b < pl.eager_bonus_from) {
         if (!collect(decision_word(pl, b), 1, pl.tag, sh.stage, sh.vote, false, kDecisionTimeoutTicks)) return;
         if (static_cast<int>(sh.stage[0]) - 2 != pl.k) return;
+    } else if (!pl.row_stats_out && pl.grid.fin_first) {
+        // Finishers placed first have often decided by now: one look at the
+        // decision word, and no read of a row that a rejection makes useless.
+        if (threadIdx.x == 0) {
+            const uint64_t w = get_word(decision_word(pl, b));
+            sh.stage[0] = static_cast<uint32_t>(w >> 32) == pl.tag ? word_data(w) : 0u;
+        }
+        __syncthreads();
+        const uint32_t d = sh.stage[0];
+        if (d != 0u && static_cast<int>(d) - 2 != pl.k) return;
     }
     stream_segment<EB, VEC, MODE>(pl, b, pl.dec_rows, s, sh);
 }

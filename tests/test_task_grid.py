@@ -28,25 +28,25 @@ def probe(tmp_path_factory):
                                "-o", out])
     lib = ctypes.CDLL(out)
     i32, i64, p32 = ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
-    lib.probe_plan.argtypes = [i32, i64, i64, i32, i32, i64, i64, i64, i64, p32]
+    lib.probe_plan.argtypes = [i32, i64, i64, i32, i32, i64, i64, i64, i64, i32, p32]
     lib.probe_plan.restype = i32
-    lib.probe_decode.argtypes = [i32] * 10 + [p32, p32, p32, i32]
+    lib.probe_decode.argtypes = [i32] * 11 + [p32, p32, p32, i32]
     lib.probe_decode.restype = i32
     return lib
 
 
-def decode(lib, B, w_dec, w_res, w_bonus, has_resid, has_bonus, la, lr, lf, lb, cap=1 << 20):
+def decode(lib, B, w_dec, w_res, w_bonus, has_resid, has_bonus, la, lr, lf, lb, cap=1 << 20, fin_first=False):
     kind = np.empty(cap, np.int32)
     seq = np.empty(cap, np.int32)
     idx = np.empty(cap, np.int32)
     p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    n = lib.probe_decode(B, w_dec, w_res, w_bonus, int(has_resid), int(has_bonus), la, lr, lf, lb, p(kind), p(seq),
-                         p(idx), cap)
+    n = lib.probe_decode(B, w_dec, w_res, w_bonus, int(has_resid), int(has_bonus), la, lr, lf, lb, int(fin_first),
+                         p(kind), p(seq), p(idx), cap)
     assert n > 0, n
     return kind[:n], seq[:n], idx[:n]
 
 
-def check_grid(kind, seq, idx, B, w_dec, w_res, w_bonus, has_resid, has_bonus):
+def check_grid(kind, seq, idx, B, w_dec, w_res, w_bonus, has_resid, has_bonus, fin_first=False):
     where = {}
     for blk, (k, s, i) in enumerate(zip(kind.tolist(), seq.tolist(), idx.tolist())):
         assert 0 <= s < B, (blk, k, s, i)
@@ -55,9 +55,12 @@ def check_grid(kind, seq, idx, B, w_dec, w_res, w_bonus, has_resid, has_bonus):
         where[key] = blk
     want = B * (w_dec + 1 + ((w_res + 1) if has_resid else 0) + ((w_bonus + 1) if has_bonus else 0))
     assert len(where) == want == len(kind)
+    if fin_first:
+        # the finishers first, in sequence order; everything else as usual
+        assert [where[(DF, s, 0)] for s in range(B)] == list(range(B))
     for s in range(B):
         df = where[(DF, s, 0)]
-        assert all(where[(DW, s, w)] < df for w in range(w_dec))
+        assert fin_first or all(where[(DW, s, w)] < df for w in range(w_dec))
         if has_resid:
             rf = where[(RF, s, 0)]
             assert all(df < where[(RW, s, w)] < rf for w in range(w_res))
@@ -77,9 +80,11 @@ def test_every_block_decodes_to_one_role_in_dependency_order(probe):
                                                             (0, B) if has_resid else (0,),
                                                             (0, 1, B) if has_bonus else (0,)):
                         lr, lf, lb = min(lr, B), min(lf, B), min(lb, B)
-                        k, s, i = decode(probe, B, w_dec, w_res, w_bonus, has_resid, has_bonus, la, lr, lf, lb)
-                        check_grid(k, s, i, B, w_dec, w_res, w_bonus, has_resid, has_bonus)
-                        n += 1
+                        for ff in (False, True):
+                            k, s, i = decode(probe, B, w_dec, w_res, w_bonus, has_resid, has_bonus, la, lr, lf, lb,
+                                             fin_first=ff)
+                            check_grid(k, s, i, B, w_dec, w_res, w_bonus, has_resid, has_bonus, ff)
+                            n += 1
     assert n > 500
 
 
@@ -102,22 +107,24 @@ def test_planned_grids_of_the_workloads(probe, name, B, k, V, eb, T, onehot, vat
     dec_rows = k + (k if reads_draft else 0)
     has_resid = (not vat) and T != 0.0 and not onehot
     has_bonus = not vat
-    params = np.zeros(8, np.int32)
+    params = np.zeros(9, np.int32)
     for per_dec, per_bonus, per_res in ((4, 4, 4), (8, 4, 4), (8, 8, 4), (16, 8, 8)):
         n = probe.probe_plan(B, dec_rows * chunks, chunks, int(has_resid), int(has_bonus), per_dec, per_bonus,
-                             per_res, resident, params.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+                             per_res, resident, int(not vat), params.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
         assert n > 0
-        w_dec, w_res, w_bonus, la, lr, lf, lb, nseg = params.tolist()
+        w_dec, w_res, w_bonus, la, lr, lf, lb, nseg, ff = params.tolist()
+        # finishers first only for one-residency grids of few sequences
+        assert ff == int((not vat) and la >= B and 8 * B <= resident)
         # a finisher sits about one residency of blocks behind its workers
         assert la == min(B, -(-resident // (w_dec + 1 + ((w_res + 1) if has_resid else 0))))
         assert w_dec == -(-dec_rows * chunks // per_dec)
         assert w_bonus == (-(-chunks // per_bonus) if has_bonus else 0)
-        assert 1 <= nseg <= 12
+        assert 1 <= nseg <= 13
         assert all(0 <= x <= B for x in (la, lr, lf, lb))
         kind, seq, idx = decode(probe, B, w_dec, w_res, w_bonus, has_resid, has_bonus, la, lr, lf, lb,
-                                cap=1 << 22)
+                                cap=1 << 22, fin_first=bool(ff))
         assert len(kind) == n
-        check_grid(kind, seq, idx, B, w_dec, w_res, w_bonus, has_resid, has_bonus)
+        check_grid(kind, seq, idx, B, w_dec, w_res, w_bonus, has_resid, has_bonus, bool(ff))
 
 
 def test_grid_division_is_exact(probe):
