@@ -222,6 +222,9 @@ def _custom(B, k, V, dtype, T, sigma_t=3.0, sigma_d=0.5, mode="sample", onehot=F
     (6, 4, 1001, "bf16", 1.0, True),      # one-hot draft, unaligned rows
     (20, 4, 2048, "f32", 0.0, False),     # greedy fp32, exactly one chunk
     (9, 3, 1001, "bf16", 0.0, False),     # greedy unaligned
+    (32, 16, 151936, "bf16", 1.0, True),  # one-hot, several residencies: finishers behind their workers
+    (24, 3, 151936, "bf16", 0.7, False),  # sampling in one residency: finishers first, residual roles after
+    (12, 5, 151936, "bf16", 0.0, False),  # greedy in one residency, finishers first
 ])
 def test_edge_shapes(dev, B, k, V, dtype, T, onehot):
     cfg = _custom(B, k, V, dtype, T, onehot=onehot, mode="argmax" if T == 0 else "sample")
