@@ -1426,8 +1426,9 @@ __device__ __forceinline__ void decision_finisher(const Plan& pl, int b, TailSha
         for (int j = threadIdx.x; j < pl.dec_rows; j += kBlock) write_row_stats(pl, global_row(pl, b, j), sh.mz[j]);
     const bool draws = Tr::onehot && r >= 0 && r < k;
     // r for the bonus workers that read the bonus row only after full
-    // acceptance (after the one-hot draw when there is one: see below).
-    if (Tr::bonus && !draws && threadIdx.x == kWave)
+    // acceptance, and for decision workers that skip rows after r (after
+    // the one-hot draw when there is one and no row is skipped: see below).
+    if (Tr::bonus && (!draws || pl.row_skip) && threadIdx.x == kWave)
         put_word(decision_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
     if (threadIdx.x < kWave) {
         const int i = lane;
@@ -1473,7 +1474,7 @@ __device__ __forceinline__ void decision_finisher(const Plan& pl, int b, TailSha
         const DrawRow d = onehot_row<EB>(pl, b, r, PartialSrc{cstaged ? sh.stage : nullptr, cw}, m_r, sh.x_r, sh.l_x);
         const int y = ok ? draw_token<EB, VEC>(d, u_draw, P, V, sh) : -2;
         if (threadIdx.x < kWave) publish_outputs<MODE>(pl, b, r, pr.x, y, sh);
-        if (threadIdx.x == kWave) put_word(decision_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
+        if (threadIdx.x == kWave && !pl.row_skip) put_word(decision_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
     }
 }
 
@@ -1810,6 +1811,16 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCu) void k_verify(Plan pl) {
                     idx = static_cast<int>(t / pl.batch) * pl.segs + s;
                 }
                 const int j = idx / pl.segs;
+                if (pl.row_skip && j >= Tr::halves) {
+                    // a row after a first rejection that is already known
+                    // is never read by anyone: skip it
+                    if (threadIdx.x == 0) {
+                        const uint64_t w = get_word(decision_word(pl, b));
+                        sh.r = static_cast<uint32_t>(w >> 32) == pl.tag ? static_cast<int>(word_data(w)) - 2 : pl.k;
+                    }
+                    __syncthreads();
+                    if (sh.r < j / Tr::halves) return;
+                }
                 stream_segment<EB, VEC, MODE>(pl, b, j, idx - j * pl.segs, sh);
             }
             return;
@@ -1842,7 +1853,8 @@ hipError_t launch_typed(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipE
         e = hipEventRecord(ev0, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_verify<EB, VEC, MODE>), dim3(static_cast<unsigned>(pl.grid.total_blocks)), dim3(kBlock), 0,
+    hipLaunchKernelGGL((k_verify<EB, VEC, MODE>), dim3(static_cast<unsigned>(pl.grid.total_blocks)), dim3(kBlock),
+                       static_cast<uint32_t>(pl.dyn_lds),
                        stream, pl);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1867,21 +1879,21 @@ hipError_t launch_mode(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEv
 }
 
 template <int EB, bool VEC, int MODE>
-int blocks_per_cu_typed() {
+int blocks_per_cu_typed(size_t lds) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_verify<EB, VEC, MODE>, kBlock, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_verify<EB, VEC, MODE>, kBlock, lds) != hipSuccess) return 0;
     return n;
 }
 
 template <int EB, bool VEC>
-int blocks_per_cu_mode(int path) {
+int blocks_per_cu_mode(int path, size_t lds) {
     switch (path) {
-        case kPathSample: return blocks_per_cu_typed<EB, VEC, kPathSample>();
-        case kPathOneHot: return blocks_per_cu_typed<EB, VEC, kPathOneHot>();
-        case kPathGreedy: return blocks_per_cu_typed<EB, VEC, kPathGreedy>();
-        case kPathVat: return blocks_per_cu_typed<EB, VEC, kPathVat>();
-        case kPathVatGreedy: return blocks_per_cu_typed<EB, VEC, kPathVatGreedy>();
-        case kPathVatLoss: return blocks_per_cu_typed<EB, VEC, kPathVatLoss>();
+        case kPathSample: return blocks_per_cu_typed<EB, VEC, kPathSample>(lds);
+        case kPathOneHot: return blocks_per_cu_typed<EB, VEC, kPathOneHot>(lds);
+        case kPathGreedy: return blocks_per_cu_typed<EB, VEC, kPathGreedy>(lds);
+        case kPathVat: return blocks_per_cu_typed<EB, VEC, kPathVat>(lds);
+        case kPathVatGreedy: return blocks_per_cu_typed<EB, VEC, kPathVatGreedy>(lds);
+        case kPathVatLoss: return blocks_per_cu_typed<EB, VEC, kPathVatLoss>(lds);
         default: return 0;
     }
 }
@@ -2061,9 +2073,17 @@ hipError_t launch_accept_hist(const int32_t* acc, int32_t batch, int32_t k, int3
     return hipGetLastError();
 }
 
-int verify_blocks_per_cu(int elem_bytes, bool vec, int path) {
-    if (elem_bytes == 2) return vec ? blocks_per_cu_mode<2, true>(path) : blocks_per_cu_mode<2, false>(path);
-    return vec ? blocks_per_cu_mode<4, true>(path) : blocks_per_cu_mode<4, false>(path);
+int verify_blocks_per_cu_lds(int elem_bytes, bool vec, int path, size_t lds) {
+    if (elem_bytes == 2) return vec ? blocks_per_cu_mode<2, true>(path, lds) : blocks_per_cu_mode<2, false>(path, lds);
+    return vec ? blocks_per_cu_mode<4, true>(path, lds) : blocks_per_cu_mode<4, false>(path, lds);
+}
+
+int verify_blocks_per_cu(int elem_bytes, bool vec, int path) { return verify_blocks_per_cu_lds(elem_bytes, vec, path, 0); }
+
+int verify_lds_for_blocks(int elem_bytes, bool vec, int path, int blocks) {
+    for (int lds = 0; lds <= 65536; lds += 1024)
+        if (verify_blocks_per_cu_lds(elem_bytes, vec, path, static_cast<size_t>(lds)) == blocks) return lds;
+    return -1;
 }
 
 // ------------------------------------------------------------------ built-in scratch

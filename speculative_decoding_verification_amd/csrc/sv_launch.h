@@ -67,6 +67,8 @@ struct Plan {
     int32_t nc_dec, nc_res;   // chunks per worker wavefront
     int32_t eager_bonus_from; // sequences b >= this read their bonus row without deciding first
     int32_t pos_major;        // decision worker blocks ordered position-major over all sequences
+    int32_t row_skip;         // decision workers of a row after a known first rejection read nothing
+    int32_t dyn_lds;          // dynamic LDS bytes per block (only to cap the blocks per compute unit)
     // Flags are 32-bit: a byte-sized field at an unaligned offset of the
     // kernel argument block is read with a vector load (a memory round trip
     // at the start of every block) instead of a scalar one.
@@ -117,6 +119,14 @@ constexpr int kDefaultComputeUnits = 256;
 
 // Blocks of k_verify<EB, VEC, path> one compute unit holds at once (0 on failure).
 int verify_blocks_per_cu(int elem_bytes, bool vec, int path);
+
+// Dynamic LDS bytes per block that hold k_verify to `blocks` blocks per
+// compute unit (-1 if no amount up to 64 KiB does).
+int verify_lds_for_blocks(int elem_bytes, bool vec, int path, int blocks);
+
+// Small one-hot and greedy calls whose rows need not all be read: blocks per
+// compute unit while they stream (see Plan::row_skip).
+constexpr int kRowSkipBlocksPerCu = 3;
 
 // Chunks each worker wavefront streams, one after the other.  Two per wave
 // for large calls: block dispatch (on the order of 150-200 blocks per
