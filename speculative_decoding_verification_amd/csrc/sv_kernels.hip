@@ -8,31 +8,41 @@
 // 的锚点": the same rule on training blocks, labels and first-rejection-
 // anchored weights).
 //
-// One call is one launch of k_verify, a grid of 256-thread blocks, each of
-// which decodes its role from its block index (a "task grid").  The roles:
-//  decision worker   one wavefront per (row, 8 KiB chunk) of the k target rows
-//                    and k draft rows of a sequence: non-temporal 16-byte
-//                    coalesced loads, the chunk's max and sum of
+// One call is one launch of k_verify<EB, VEC, MODE> (one specialisation per
+// path: sampling with draft logits, one-hot drafts, greedy, VAT labels, VAT
+// greedy, VAT loss), a grid of 256-thread blocks, each of which decodes its
+// role from its block index (a "task grid").  The roles:
+//  decision worker   one segment of one row per block: each wavefront streams
+//                    nc 8 KiB chunks of the row (non-temporal 16-byte
+//                    coalesced loads), the chunk's max and sum of
 //                    exp2((l - m) * log2(e)/T) (at T == 0: max and lowest
-//                    index), DPP wave reductions, the partial published as
-//                    tagged words.  Workers never wait.
-//  decision finisher per sequence: waits for that sequence's partials, combines
-//                    them into (m, Z) per row, p(x_i), q(x_i), runs the test
-//                    u*q < p on one lane per position, ballot -> first
-//                    rejection r, accepted prefix or VAT labels and weights,
-//                    and the one-hot residual draw (p_r without x_r) inline.
-//  residual worker   draft logits at T > 0 only: residual mass max(0, p_r - q_r)
-//                    of one chunk of the rejected row pair.
-//  residual finisher the residual draw (chunk prefix scan, then one chunk).
-//  bonus worker      streams the target row at position k (the bonus row).
-//  bonus finisher    its statistics and, after full acceptance, the draw.
+//                    index), DPP wave reductions; one tagged word pair per
+//                    chunk, then one merged pair per segment.  Workers never
+//                    wait (except to skip a row a known rejection has made
+//                    useless, in small one-hot and greedy calls).
+//  decision finisher per sequence: `decide` (shared by every role that needs
+//                    the first rejection r) combines the segment partials
+//                    into (m, Z) per row as the rows complete, gathers
+//                    p(x_i), q(x_i), tests u*q < p position by position and
+//                    stops at the first rejection; then the accepted prefix
+//                    or VAT labels and weights, and the one-hot residual draw
+//                    (p_r without x_r) inline.
+//  residual worker   draft logits at T > 0 only: decides, then the residual
+//                    mass max(0, p_r - q_r) of one chunk pair per wavefront.
+//  residual finisher decides, then the residual draw (chunk prefix scan, then
+//                    one chunk).
+//  bonus worker      streams the target row at position k (the bonus row)
+//                    when it can be needed.
+//  bonus finisher    decides, the bonus row's statistics and, after full
+//                    acceptance, the draw.
 // Blocks run in index order within the grid closely enough that each role only
-// ever waits on blocks with smaller indices, and finishers are placed about one
-// residency (a lag, in sequences) behind the workers they wait on, so that
-// they overlap the streaming of later sequences instead of stalling it.  Every
-// wait is bounded (about a second); a sequence whose wait runs out reports -2.
-// Hand-off words carry a per-call tag in their upper half, so the workspace
-// needs no clearing between calls and no fence is ever issued.
+// ever waits on blocks with smaller indices (small grids place their decision
+// finishers first, where they take few slots), and finishers are placed about
+// one residency behind the workers they wait on, so that they overlap the
+// streaming of later sequences instead of stalling it.  Every wait is bounded
+// (about a second); a sequence whose wait runs out reports -2.  Hand-off words
+// carry a per-call tag in their upper half, so the workspace needs no clearing
+// between calls and no fence is ever issued.
 //
 // Draws: block prefix scan over the chunk masses finds the chunk holding the
 // draw, then an LDS block scan of that one chunk finds the token.  No
@@ -1591,21 +1601,23 @@ __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared
     const int lane = threadIdx.x & (kWave - 1);
     const int k = pl.k;
     const int P = pl.chunks;
-    const int S = pl.segs;
     const int64_t V = pl.vocab;
     PosRegs pr = load_positions<EB, MODE>(pl, b);
     const float u_draw = Tr::greedy ? 0.f : pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k];
     const int r = decide<EB, VEC, MODE>(pl, b, sh, false, pr, kDecisionTimeoutTicks);
     if (r < 0 || (r != k && !pl.row_stats_out)) return;
     int32_t* token = pl.out_tokens + static_cast<int64_t>(b) * (k + 1) + k;
-    const uint64_t* sw = seg_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * S * 2;
-    const bool sstaged = 2 * S <= kStageWords;
-    if (!collect(sw, 2 * S, pl.tag, sstaged ? sh.stage : nullptr, sh.vote, pl.two_deep_polls)) {
+    // The row's chunk partials, combined directly: the draw needs them
+    // anyway, so one wait covers the row's statistics and the draw.
+    const uint64_t* cw = chunk_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * P * 2;
+    const bool cstaged = 2 * P <= kStageWords;
+    const PartialSrc src{cstaged ? sh.stage : nullptr, cw};
+    if (!collect(cw, 2 * P, pl.tag, src.stage ? sh.stage : nullptr, sh.vote, pl.two_deep_polls)) {
         if (r == k && threadIdx.x == 0) *token = -2;
         return;
     }
     if (threadIdx.x < kWave) {
-        const float2 res = combine_row(PartialSrc{sstaged ? sh.stage : nullptr, sw}, 0, S, Tr::greedy, pl.c2);
+        const float2 res = combine_row(src, 0, P, Tr::greedy, pl.c2);
         if (lane == 0) {
             sh.mz[0] = res;
             write_row_stats(pl, global_row(pl, b, pl.dec_rows), res);
@@ -1617,12 +1629,6 @@ __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared
         if (threadIdx.x == 0) *token = __float_as_int(sh.mz[0].y);
     } else {
         const float m_k = sh.mz[0].x;
-        const uint64_t* cw = chunk_words(pl, b) + static_cast<int64_t>(pl.dec_rows) * P * 2;
-        const bool cstaged = 2 * P <= kStageWords;
-        if (!collect(cw, 2 * P, pl.tag, cstaged ? sh.stage : nullptr, sh.vote, false)) {
-            if (threadIdx.x == 0) *token = -2;
-            return;
-        }
         DrawRow d;
         d.mode = kModeBonus;
         d.rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + k, V, EB);
@@ -1643,7 +1649,7 @@ __device__ __forceinline__ void bonus_finisher(const Plan& pl, int b, TailShared
 
 // VAT loss finisher of block b: the pair partials of each position, combined
 // by one wave per position; then on wave 0, one lane per position: the
-// simulated acceptance, labels and weights (as decide_sequence), the soft
+// simulated acceptance, labels and weights (as the decision finisher), the soft
 // and hard terms and the block's weighted loss.
 template <int EB, bool VEC>
 __device__ __forceinline__ void vat_loss_finisher(const Plan& pl, int b, TailShared& sh) {
