@@ -21,15 +21,18 @@ both sides.  Prints ONE JSON line:
                needed (the bonus row only of sequences that kept all k) and
                that fraction; `traffic` = HBM bytes per launch from
                committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters when they
-               were taken on the current kernel source, else null
+               were taken on the current kernel source, else null, and
+               `traffic_gbps` = that over the mean launch
   sol          k_sol_read (sv_sol_read: a plain non-temporal read) over the
                needed bytes, buffers rotated the same way: its mean launch
                duration and sol/k_verify
   call_us      p10 / p50 / p90 of single calls' device time (each between
                its own events), 200 calls after the timed steps
-  accept_rate, mean_accepted_len, full_acceptance, block_efficiency
+  accept_rate, mean_accepted_len, full_acceptance, block_efficiency,
+  accept_histogram
                acceptance of the last call (accept_rate = accepted drafts /
-               tested drafts)
+               tested drafts; the histogram counts accepted lengths 0..k,
+               then invalid, timed out, other)
   parity_sample
                the fp64 oracle on the first 32 sequences next to the GPU's
                outputs for them, outside any timed region: positions whose
@@ -688,8 +691,11 @@ def bench_verify(args) -> int:
                     "p90": float(np.percentile(calls, 90) * 1e3), "calls": len(calls),
                     "how": "device time of single calls, each between its own HIP events, after the timed steps"},
         "accept_histogram_us": hist_us,
+        "accept_histogram": hist.cpu().tolist(),
         "block_efficiency": ctl.efficiency,
     }
+    tr = res["roofline"]["traffic"]
+    res["roofline"]["traffic_gbps"] = tr / (k1_mean * 1e-3) / 1e9 if tr else None
     res.update(acceptance_stats(acc, cfg.k))
     res["parity_sample"] = sample_parity(cfg, run.host, acc[:run.host.n], out[:run.host.n], host_threads())
     del run
