@@ -927,12 +927,19 @@ __device__ __forceinline__ void stream_segment(const Plan& pl, int b, int j, int
         const float2 part = Tr::greedy ? chunk_argmax<EB, VEC>(rp, start, len, lane)
                                        : chunk_stats<EB, VEC>(rp, start, len, lane, pl.c2);
         if (lane == 0) {
-            put_partial(cw, c, part, pl.tag);
+            // one chunk per wave: its word at once; more: after all of the
+            // block's loads (a wave's write-through stores share the memory
+            // counter with its loads, so a store between two chunks would
+            // make the second chunk's wait cover the store's acknowledgement)
+            if (pl.nc_dec == 1) put_partial(cw, c, part, pl.tag);
             sh.segp[c - c0] = part;
         }
     }
     __syncthreads();
+    if (pl.nc_dec > 1 && threadIdx.x > 0 && threadIdx.x < c1 - c0)
+        put_partial(cw, c0 + static_cast<int>(threadIdx.x), sh.segp[threadIdx.x], pl.tag);
     if (threadIdx.x == 0) {
+        if (pl.nc_dec > 1) put_partial(cw, c0, sh.segp[0], pl.tag);
         float2 acc = sh.segp[0];
         for (int q = 1; q < c1 - c0; ++q) acc = merge_partial(acc, sh.segp[q], Tr::greedy, pl.c2);
         put_partial(seg_words(pl, b) + static_cast<int64_t>(j) * pl.segs * 2, s, acc, pl.tag);
@@ -1065,10 +1072,10 @@ __device__ __forceinline__ PairPart lane_pair(int n, Get get, float c2) {
     return p;
 }
 
-// Pair partials of chunk c of target row i and draft row i of block b,
-// published as five tagged words.  Whole wave.
+// Pair partials of chunk c of target row i and draft row i of block b (the
+// wave's merged result; put_pair publishes it).  Whole wave.
 template <int EB, bool VEC>
-__device__ __forceinline__ void stream_pair(const Plan& pl, int b, int i, int c) {
+__device__ __forceinline__ PairPart stream_pair(const Plan& pl, int b, int i, int c) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t V = pl.vocab;
     const char* rt = row_base(pl.target, static_cast<int64_t>(b) * pl.k + i, V, EB);
@@ -1117,15 +1124,17 @@ __device__ __forceinline__ void stream_pair(const Plan& pl, int b, int i, int c)
             acc = pair_merge(acc, lane_pair(kStep, [&](int e) { return make_float2(ft[e], fd[e]); }, c2), c2);
         }
     }
-    acc = wave_merge_pair(acc, c2);
-    if (lane == 0) {
-        uint64_t* w = chunk_words(pl, b) + (static_cast<int64_t>(i) * pl.chunks + c) * kPairWords;
-        put_word(w + 0, __float_as_uint(acc.mt), pl.tag);
-        put_word(w + 1, __float_as_uint(acc.st), pl.tag);
-        put_word(w + 2, __float_as_uint(acc.md), pl.tag);
-        put_word(w + 3, __float_as_uint(acc.sd), pl.tag);
-        put_word(w + 4, __float_as_uint(acc.x), pl.tag);
-    }
+    return wave_merge_pair(acc, c2);
+}
+
+// The five tagged words of a chunk pair's partials (one lane).
+__device__ __forceinline__ void put_pair(const Plan& pl, int b, int li, const PairPart& acc) {
+    uint64_t* w = chunk_words(pl, b) + static_cast<int64_t>(li) * kPairWords;
+    put_word(w + 0, __float_as_uint(acc.mt), pl.tag);
+    put_word(w + 1, __float_as_uint(acc.st), pl.tag);
+    put_word(w + 2, __float_as_uint(acc.md), pl.tag);
+    put_word(w + 3, __float_as_uint(acc.sd), pl.tag);
+    put_word(w + 4, __float_as_uint(acc.x), pl.tag);
 }
 
 // ------------------------------------------------------------------ finishers
@@ -1791,14 +1800,22 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCu) void k_verify(Plan pl) {
     switch (role.kind) {
         case kDecWorker: {
             if constexpr (Tr::loss) {
-                // Step n: the block's waves take chunk pairs base + n*4 + wave.
+                // Step n: the block's waves take chunk pairs base + n*4 + wave
+                // (pair index li = i * P + c); the words go out after both
+                // steps' loads (see stream_segment).
+                static_assert(kChunksPerWave <= 2, "two steps at most");
                 const int items = pl.dec_rows * pl.chunks;
-                const int base = role.index * kWavesPerBlock * pl.nc_dec + static_cast<int>(threadIdx.x / kWave);
-#pragma unroll 1
-                for (int n = 0; n < pl.nc_dec; ++n) {
-                    const int li = base + n * kWavesPerBlock;
-                    if (li >= items) break;
-                    stream_pair<EB, VEC>(pl, b, li / pl.chunks, li % pl.chunks);
+                const int li0 = role.index * kWavesPerBlock * pl.nc_dec + static_cast<int>(threadIdx.x / kWave);
+                const int li1 = li0 + kWavesPerBlock;
+                const bool has1 = pl.nc_dec > 1 && li1 < items;
+                if (li0 < items) {
+                    const PairPart p0 = stream_pair<EB, VEC>(pl, b, li0 / pl.chunks, li0 % pl.chunks);
+                    PairPart p1 = p0;
+                    if (has1) p1 = stream_pair<EB, VEC>(pl, b, li1 / pl.chunks, li1 % pl.chunks);
+                    if ((threadIdx.x & (kWave - 1)) == 0) {
+                        put_pair(pl, b, li0, p0);
+                        if (has1) put_pair(pl, b, li1, p1);
+                    }
                 }
             } else {
                 // Block `index` of sequence b: segment index % S of local
