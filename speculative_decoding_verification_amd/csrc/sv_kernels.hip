@@ -1511,14 +1511,24 @@ __device__ __forceinline__ void residual_worker(const Plan& pl, int b, int w, Ta
     const char* rt = row_base(pl.target, static_cast<int64_t>(b) * pl.target_rows_per_seq + r, V, EB);
     const char* rd = row_base(pl.draft, static_cast<int64_t>(b) * pl.k + r, V, EB);
     const int base = w * kWavesPerBlock * pl.nc_res + static_cast<int>(threadIdx.x / kWave);
-#pragma unroll 1
-    for (int n = 0; n < pl.nc_res; ++n) {
+    // the masses go out after all of the wave's loads (see stream_segment)
+    float mass[kChunksPerWaveResid];
+#pragma unroll
+    for (int n = 0; n < kChunksPerWaveResid; ++n) {
         const int c = base + n * kWavesPerBlock;
-        if (c >= P) break;
-        const int64_t start = static_cast<int64_t>(c) * Chunk<EB>::kElems;
-        const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), V - start));
-        const float s = chunk_resid_mass<EB, VEC>(rt, rd, start, len, lane, wf);
-        if (lane == 0) put_word(resid_words(pl, b) + c, __float_as_uint(s), pl.tag);
+        mass[n] = 0.f;
+        if (n < pl.nc_res && c < P) {
+            const int64_t start = static_cast<int64_t>(c) * Chunk<EB>::kElems;
+            const int len = static_cast<int>(min(static_cast<int64_t>(Chunk<EB>::kElems), V - start));
+            mass[n] = chunk_resid_mass<EB, VEC>(rt, rd, start, len, lane, wf);
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int n = 0; n < kChunksPerWaveResid; ++n) {
+            const int c = base + n * kWavesPerBlock;
+            if (n < pl.nc_res && c < P) put_word(resid_words(pl, b) + c, __float_as_uint(mass[n]), pl.tag);
+        }
     }
 }
 
