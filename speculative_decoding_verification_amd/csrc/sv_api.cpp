@@ -82,22 +82,6 @@ int64_t resident_blocks(const Shape& s, bool vec) {
     return r;
 }
 
-// Dynamic LDS that holds this path's k_verify to kRowSkipBlocksPerCu blocks
-// per compute unit, queried once per device and path (-1: none does).
-int row_skip_lds(const Shape& s, bool vec) {
-    constexpr int kMaxDevices = 64;
-    constexpr int kPaths = kPathVatLoss + 1;
-    static std::atomic<int> cache[kMaxDevices][2][2][kPaths];  // value + 2; 0 = not yet queried
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
-    const int e = s.elem_bytes == 2 ? 1 : 0, v = vec ? 1 : 0, m = s.path();
-    const int c = cache[dev][e][v][m].load(std::memory_order_relaxed);
-    if (c > 0) return c - 2;
-    const int lds = verify_lds_for_blocks(s.elem_bytes, vec, m, kRowSkipBlocksPerCu);
-    cache[dev][e][v][m].store(lds + 2, std::memory_order_relaxed);
-    return lds;
-}
-
 // Shared checks of both entry points.  `draft_kind` is SV_DRAFT_LOGITS for VAT.
 sv_status check_shape(int32_t batch, int32_t k, int32_t vocab, int32_t dtype, int32_t draft_kind,
                       float temperature, bool vat, Shape* s) {
@@ -182,6 +166,19 @@ bool fill_plan(const Shape& s, float temperature, float decay, bool vec, Plan* p
         return false;
     // Every decision worker block before every finisher: position-major.
     pl->pos_major = !s.loss && pl->grid.lag_a >= pl->batch;
+    // Small one-hot and greedy calls whose statistics are not asked for: the
+    // rows after a sequence's first rejection are never used (window mode).
+    // The decision finishers come first and the rows position-major, so a
+    // decision is often known before the blocks of later rows start: those
+    // then read nothing.  When the previous call on this workspace rejected
+    // the first draft token of every sequence (acceptance carries over from
+    // one decoding step to the next), only the rows of the first kRowWindow
+    // positions are read at once, and any other row only once the decision
+    // finisher's accepted prefix comes near it.
+    pl->window = (s.onehot || s.greedy) && !s.vat && !pl->probs_out && !pl->row_stats_out && pl->pos_major &&
+                         pl->grid.fin_first && s.k > kRowWindow
+                     ? kRowWindow
+                     : 0;
     // Short polling sleeps only when (nearly) the whole grid is resident at
     // once: no stream is left for the extra reads to slow down.  A quarter
     // of a residency over is allowed for the finisher and bonus blocks that
@@ -192,22 +189,6 @@ bool fill_plan(const Shape& s, float temperature, float decay, bool vec, Plan* p
     // deciding first, so that reading them is not added to the end of the
     // chain.
     pl->eager_bonus_from = std::max(0, pl->batch - pl->grid.lag_a);
-    // Small one-hot and greedy calls whose statistics are not asked for: the
-    // rows after a sequence's first rejection are never read by anyone.  With
-    // the finishers first and the rows position-major, the stream is held to
-    // fewer blocks per compute unit, so that the rows of early positions are
-    // in (and most decisions taken) while later rows still wait for a slot;
-    // those then skip their read.
-    pl->row_skip = 0;
-    pl->dyn_lds = 0;
-    if ((s.onehot || s.greedy) && !s.vat && !pl->probs_out && !pl->row_stats_out && pl->pos_major &&
-        pl->grid.fin_first) {
-        const int lds = row_skip_lds(s, vec);
-        if (lds >= 0) {
-            pl->row_skip = 1;
-            pl->dyn_lds = lds;
-        }
-    }
     pl->rows_t = s.rows_t;
     pl->rows_d = s.rows_d;
     pl->greedy = s.greedy;
@@ -308,7 +289,7 @@ WorkspaceLayout workspace_layout(int64_t chunk_words, int64_t seg_words, int64_t
     L.segw = off;
     off = align_up(off + static_cast<size_t>(seg_words) * sizeof(uint64_t));
     L.resid = off;
-    off = align_up(off + static_cast<size_t>(batch * (chunks + 1)) * sizeof(uint64_t));
+    off = align_up(off + static_cast<size_t>(batch * (chunks + 3)) * sizeof(uint64_t));
     L.total = off;
     return L;
 }

@@ -18,8 +18,9 @@
 //                    exp2((l - m) * log2(e)/T) (at T == 0: max and lowest
 //                    index), DPP wave reductions; one tagged word pair per
 //                    chunk, then one merged pair per segment.  Workers never
-//                    wait (except to skip a row a known rejection has made
-//                    useless, in small one-hot and greedy calls).
+//                    wait, except in small one-hot and greedy calls (window
+//                    mode), where the rows of later positions are read only
+//                    as the accepted prefix comes near them.
 //  decision finisher per sequence: `decide` (shared by every role that needs
 //                    the first rejection r) combines the segment partials
 //                    into (m, Z) per row as the rows complete, gathers
@@ -530,6 +531,8 @@ struct TailShared {
     int mode;
     int x_r;
     float l_x;
+    int ahead;                     // window mode: last position read without waiting
+    int known;                     // window mode: r from the decision word, k while undecided
 };
 
 // ------------------------------------------------------------------ sampling
@@ -878,13 +881,83 @@ __device__ __forceinline__ uint64_t* seg_words(const Plan& pl, int b) {
     return pl.segw + static_cast<int64_t>(b) * pl.seg_words_per_seq;
 }
 
-// Residual masses of sequence b (one per chunk), then its decision word:
-// r + 2, from the decision finisher, for the bonus workers that wait for it.
+// Residual masses of sequence b (one per chunk), then its decision word
+// (r + 2, from the decision finisher, for the workers that wait for it),
+// its progress word (window mode: the positions accepted so far while no
+// rejection is known) and its history word (window mode: r + 2 of the last
+// call that used the workspace, whatever its tag; 0 before any).
 __device__ __forceinline__ uint64_t* resid_words(const Plan& pl, int b) {
-    return pl.resid + static_cast<int64_t>(b) * (pl.chunks + 1);
+    return pl.resid + static_cast<int64_t>(b) * (pl.chunks + 3);
 }
 
 __device__ __forceinline__ uint64_t* decision_word(const Plan& pl, int b) { return resid_words(pl, b) + pl.chunks; }
+
+__device__ __forceinline__ uint64_t* progress_word(const Plan& pl, int b) {
+    return resid_words(pl, b) + pl.chunks + 1;
+}
+
+__device__ __forceinline__ uint64_t* history_word(const Plan& pl, int b) {
+    return resid_words(pl, b) + pl.chunks + 2;
+}
+
+// Window mode: the last position whose row is read without waiting.  Only
+// kRowWindow - 1 if the previous call on the workspace rejected the first
+// draft token of every sequence (the rows after it were all useless then,
+// and acceptance carries over from one decoding step to the next); else k,
+// every row and the bonus row.  In the same round of loads (wave 1), what
+// sequence b's decision word says: `known` = its r, or k while undecided.
+// Whole block.
+__device__ __forceinline__ int read_ahead(const Plan& pl, int b, TailShared& sh, int& known) {
+    if (threadIdx.x >= kWave && threadIdx.x < 2 * kWave) {
+        const int lane = static_cast<int>(threadIdx.x) - kWave;
+        const uint64_t d = get_word(decision_word(pl, b));
+        bool other = false;
+        for (int i = lane; i < pl.batch; i += kWave) other |= word_data(get_word(history_word(pl, i))) != 2u;
+        const bool any = __ballot(other) != 0ull;
+        if (lane == 0) {
+            sh.ahead = any ? pl.k : pl.window - 1;
+            sh.known = static_cast<uint32_t>(d >> 32) == pl.tag ? static_cast<int>(word_data(d)) - 2 : pl.k;
+        }
+    }
+    __syncthreads();
+    known = sh.known;
+    return sh.ahead;
+}
+
+// Window mode: whether the row of position pos of sequence b is read.  One
+// lane of wave 1 polls the sequence's decision and progress words until the
+// decision is known (read if r >= pos: the bonus row after full acceptance)
+// or the accepted prefix a has pos < window + kWindowGrowth * a.  Returns 0
+// (never used), 1 (read) or 2 (the wait ran out: read anyway).  The wait is
+// a quarter of the decision finisher's, so that a finisher whose rows were
+// held back still receives them before its own wait runs out.  Whole block.
+__device__ __forceinline__ int released(const Plan& pl, int b, int pos, TailShared& sh) {
+    if (threadIdx.x == kWave) {
+        const uint64_t t0 = wall_clock64();
+        int go;
+        for (;;) {
+            const uint64_t d = get_word(decision_word(pl, b));
+            const uint64_t a = get_word(progress_word(pl, b));
+            if (static_cast<uint32_t>(d >> 32) == pl.tag) {
+                go = static_cast<int>(word_data(d)) - 2 >= pos ? 1 : 0;
+                break;
+            }
+            if (static_cast<uint32_t>(a >> 32) == pl.tag &&
+                pos < kWindowGrowth * static_cast<int>(word_data(a)) + pl.window) {
+                go = 1;
+                break;
+            }
+            if (wall_clock64() - t0 > kPollTimeoutTicks / 4) {
+                go = 2;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        sh.r = go;
+    }
+    __syncthreads();
+    return sh.r;
+}
 
 // ------------------------------------------------------------------ workers
 
@@ -906,11 +979,14 @@ __device__ __forceinline__ float2 merge_partial(float2 a, float2 b, bool greedy,
 // c0 + w + 4n (n < nc_dec) of the segment, each handed off as two chunk
 // words; after one barrier, thread 0 merges the segment's chunk partials in
 // chunk order and hands off the segment partial as two segment words.  The
-// finishers poll segment words only (a few per row); the draws read the
-// chunk words of the one row they draw from.  Whole block.
+// decision steps poll segment words only (a few per row); the draws and the
+// bonus finisher read the chunk words of the one row they use.  With more
+// than one chunk per wave, every hand-off store waits for the barrier and
+// comes from wave 0 (see below).  Whole block.
 template <int EB, bool VEC, int MODE>
 __device__ __forceinline__ void stream_segment(const Plan& pl, int b, int j, int s, TailShared& sh) {
     using Tr = PathTraits<MODE>;
+    const bool defer = pl.nc_dec > 1;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int P = pl.chunks;
@@ -931,15 +1007,15 @@ __device__ __forceinline__ void stream_segment(const Plan& pl, int b, int j, int
             // block's loads (a wave's write-through stores share the memory
             // counter with its loads, so a store between two chunks would
             // make the second chunk's wait cover the store's acknowledgement)
-            if (pl.nc_dec == 1) put_partial(cw, c, part, pl.tag);
+            if (!defer) put_partial(cw, c, part, pl.tag);
             sh.segp[c - c0] = part;
         }
     }
     __syncthreads();
-    if (pl.nc_dec > 1 && threadIdx.x > 0 && threadIdx.x < c1 - c0)
+    if (defer && threadIdx.x > 0 && threadIdx.x < c1 - c0)
         put_partial(cw, c0 + static_cast<int>(threadIdx.x), sh.segp[threadIdx.x], pl.tag);
     if (threadIdx.x == 0) {
-        if (pl.nc_dec > 1) put_partial(cw, c0, sh.segp[0], pl.tag);
+        if (defer) put_partial(cw, c0, sh.segp[0], pl.tag);
         float2 acc = sh.segp[0];
         for (int q = 1; q < c1 - c0; ++q) acc = merge_partial(acc, sh.segp[q], Tr::greedy, pl.c2);
         put_partial(seg_words(pl, b) + static_cast<int64_t>(j) * pl.segs * 2, s, acc, pl.tag);
@@ -1334,7 +1410,8 @@ __device__ __forceinline__ bool test_position(const Plan& pl, const TailShared& 
 // out); leaves the combined rows in sh.mz (local row numbering) and the
 // tested positions' p_i(x_i), q_i(x_i) in pr.  Whole block.
 template <int EB, bool VEC, int MODE>
-__device__ __forceinline__ int decide(const Plan& pl, int b, TailShared& sh, bool all, PosRegs& pr, uint64_t timeout) {
+__device__ __forceinline__ int decide(const Plan& pl, int b, TailShared& sh, bool all, PosRegs& pr, uint64_t timeout,
+                                      bool progress = false) {
     using Tr = PathTraits<MODE>;
     constexpr int H = Tr::halves;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1375,6 +1452,10 @@ __device__ __forceinline__ int decide(const Plan& pl, int b, TailShared& sh, boo
             __syncthreads();
             r = sh.r;
             done = f;
+            // window mode: the accepted prefix so far, for the workers of
+            // the next positions
+            if (progress && r == k && done < k && threadIdx.x == kWave)
+                put_word(progress_word(pl, b), static_cast<uint32_t>(done), pl.tag);
         }
         if (done == k || (r < k && !all)) return r;
         // waves read the clock at slightly different times: decide together
@@ -1436,7 +1517,12 @@ __device__ __forceinline__ void decision_finisher(const Plan& pl, int b, TailSha
     PosRegs pr = load_positions<EB, MODE>(pl, b);
     const float u_draw = Tr::onehot ? pl.uniforms[static_cast<int64_t>(b) * (k + 1) + k] : 0.f;
     const bool all = pl.probs_out || pl.row_stats_out;
-    const int r = decide<EB, VEC, MODE>(pl, b, sh, all, pr, kPollTimeoutTicks);
+    // window mode: the accepted prefix is published only while the
+    // read-ahead is limited (a store would delay this wave's next poll)
+    int known;
+    bool limited = false;
+    if constexpr (Tr::bonus && Tr::halves == 1) limited = pl.window && read_ahead(pl, b, sh, known) < pl.k;
+    const int r = decide<EB, VEC, MODE>(pl, b, sh, all, pr, kPollTimeoutTicks, limited);
     if (r == -2) {
         fail_sequence<MODE>(pl, b);
         return;
@@ -1445,10 +1531,12 @@ __device__ __forceinline__ void decision_finisher(const Plan& pl, int b, TailSha
         for (int j = threadIdx.x; j < pl.dec_rows; j += kBlock) write_row_stats(pl, global_row(pl, b, j), sh.mz[j]);
     const bool draws = Tr::onehot && r >= 0 && r < k;
     // r for the bonus workers that read the bonus row only after full
-    // acceptance, and for decision workers that skip rows after r (after
-    // the one-hot draw when there is one and no row is skipped: see below).
-    if (Tr::bonus && (!draws || pl.row_skip) && threadIdx.x == kWave)
+    // acceptance, and for the window's workers (after the one-hot draw when
+    // there is one and no worker waits for it: see below).
+    if (Tr::bonus && (!draws || pl.window) && threadIdx.x == kWave) {
         put_word(decision_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
+        if (pl.window) put_word(history_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
+    }
     if (threadIdx.x < kWave) {
         const int i = lane;
         if (pl.probs_out && pr.active) {
@@ -1493,7 +1581,7 @@ __device__ __forceinline__ void decision_finisher(const Plan& pl, int b, TailSha
         const DrawRow d = onehot_row<EB>(pl, b, r, PartialSrc{cstaged ? sh.stage : nullptr, cw}, m_r, sh.x_r, sh.l_x);
         const int y = ok ? draw_token<EB, VEC>(d, u_draw, P, V, sh) : -2;
         if (threadIdx.x < kWave) publish_outputs<MODE>(pl, b, r, pr.x, y, sh);
-        if (threadIdx.x == kWave && !pl.row_skip) put_word(decision_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
+        if (threadIdx.x == kWave && !pl.window) put_word(decision_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
     }
 }
 
@@ -1594,7 +1682,14 @@ __device__ __forceinline__ void residual_finisher(const Plan& pl, int b, TailSha
 // decision is long taken when they run.
 template <int EB, bool VEC, int MODE>
 __device__ __forceinline__ void bonus_worker(const Plan& pl, int b, int s, TailShared& sh) {
-    if (!pl.row_stats_out && b < pl.eager_bonus_from) {
+    if (pl.window) {
+        // window mode: not after a known rejection; with the read-ahead
+        // limited, once the accepted prefix comes near position k or after
+        // full acceptance
+        int known;
+        const int ahead = read_ahead(pl, b, sh, known);
+        if (known != pl.k || (ahead < pl.k && released(pl, b, pl.k, sh) == 0)) return;
+    } else if (!pl.row_stats_out && b < pl.eager_bonus_from) {
         if (!collect(decision_word(pl, b), 1, pl.tag, sh.stage, sh.vote, false, kDecisionTimeoutTicks)) return;
         if (static_cast<int>(sh.stage[0]) - 2 != pl.k) return;
     } else if (!pl.row_stats_out && pl.grid.fin_first) {
@@ -1844,17 +1939,16 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCu) void k_verify(Plan pl) {
                     idx = static_cast<int>(t / pl.batch) * pl.segs + s;
                 }
                 const int j = idx / pl.segs;
-                if (pl.row_skip && j >= Tr::halves) {
-                    // a row after a first rejection that is already known
-                    // is never read by anyone: skip it
-                    if (threadIdx.x == 0) {
-                        const uint64_t w = get_word(decision_word(pl, b));
-                        sh.r = static_cast<uint32_t>(w >> 32) == pl.tag ? static_cast<int>(word_data(w)) - 2 : pl.k;
-                    }
-                    __syncthreads();
-                    if (sh.r < j / Tr::halves) return;
+                const int s = idx - j * pl.segs;
+                // Window mode: the row of position j >= window is not read
+                // after a known rejection before it, and beyond the
+                // read-ahead only once released.
+                if (Tr::bonus && Tr::halves == 1 && pl.window && j >= pl.window) {
+                    int known;
+                    const int ahead = read_ahead(pl, b, sh, known);
+                    if (known < j || (j > ahead && released(pl, b, j, sh) == 0)) return;
                 }
-                stream_segment<EB, VEC, MODE>(pl, b, j, idx - j * pl.segs, sh);
+                stream_segment<EB, VEC, MODE>(pl, b, j, s, sh);
             }
             return;
         }
@@ -1886,8 +1980,7 @@ hipError_t launch_typed(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipE
         e = hipEventRecord(ev0, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_verify<EB, VEC, MODE>), dim3(static_cast<unsigned>(pl.grid.total_blocks)), dim3(kBlock),
-                       static_cast<uint32_t>(pl.dyn_lds),
+    hipLaunchKernelGGL((k_verify<EB, VEC, MODE>), dim3(static_cast<unsigned>(pl.grid.total_blocks)), dim3(kBlock), 0,
                        stream, pl);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1912,21 +2005,21 @@ hipError_t launch_mode(const Plan& pl, hipStream_t stream, hipEvent_t ev0, hipEv
 }
 
 template <int EB, bool VEC, int MODE>
-int blocks_per_cu_typed(size_t lds) {
+int blocks_per_cu_typed() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_verify<EB, VEC, MODE>, kBlock, lds) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_verify<EB, VEC, MODE>, kBlock, 0) != hipSuccess) return 0;
     return n;
 }
 
 template <int EB, bool VEC>
-int blocks_per_cu_mode(int path, size_t lds) {
+int blocks_per_cu_mode(int path) {
     switch (path) {
-        case kPathSample: return blocks_per_cu_typed<EB, VEC, kPathSample>(lds);
-        case kPathOneHot: return blocks_per_cu_typed<EB, VEC, kPathOneHot>(lds);
-        case kPathGreedy: return blocks_per_cu_typed<EB, VEC, kPathGreedy>(lds);
-        case kPathVat: return blocks_per_cu_typed<EB, VEC, kPathVat>(lds);
-        case kPathVatGreedy: return blocks_per_cu_typed<EB, VEC, kPathVatGreedy>(lds);
-        case kPathVatLoss: return blocks_per_cu_typed<EB, VEC, kPathVatLoss>(lds);
+        case kPathSample: return blocks_per_cu_typed<EB, VEC, kPathSample>();
+        case kPathOneHot: return blocks_per_cu_typed<EB, VEC, kPathOneHot>();
+        case kPathGreedy: return blocks_per_cu_typed<EB, VEC, kPathGreedy>();
+        case kPathVat: return blocks_per_cu_typed<EB, VEC, kPathVat>();
+        case kPathVatGreedy: return blocks_per_cu_typed<EB, VEC, kPathVatGreedy>();
+        case kPathVatLoss: return blocks_per_cu_typed<EB, VEC, kPathVatLoss>();
         default: return 0;
     }
 }
@@ -2106,17 +2199,9 @@ hipError_t launch_accept_hist(const int32_t* acc, int32_t batch, int32_t k, int3
     return hipGetLastError();
 }
 
-int verify_blocks_per_cu_lds(int elem_bytes, bool vec, int path, size_t lds) {
-    if (elem_bytes == 2) return vec ? blocks_per_cu_mode<2, true>(path, lds) : blocks_per_cu_mode<2, false>(path, lds);
-    return vec ? blocks_per_cu_mode<4, true>(path, lds) : blocks_per_cu_mode<4, false>(path, lds);
-}
-
-int verify_blocks_per_cu(int elem_bytes, bool vec, int path) { return verify_blocks_per_cu_lds(elem_bytes, vec, path, 0); }
-
-int verify_lds_for_blocks(int elem_bytes, bool vec, int path, int blocks) {
-    for (int lds = 0; lds <= 65536; lds += 1024)
-        if (verify_blocks_per_cu_lds(elem_bytes, vec, path, static_cast<size_t>(lds)) == blocks) return lds;
-    return -1;
+int verify_blocks_per_cu(int elem_bytes, bool vec, int path) {
+    if (elem_bytes == 2) return vec ? blocks_per_cu_mode<2, true>(path) : blocks_per_cu_mode<2, false>(path);
+    return vec ? blocks_per_cu_mode<4, true>(path) : blocks_per_cu_mode<4, false>(path);
 }
 
 // ------------------------------------------------------------------ built-in scratch

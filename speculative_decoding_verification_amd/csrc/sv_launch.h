@@ -67,8 +67,11 @@ struct Plan {
     int32_t nc_dec, nc_res;   // chunks per worker wavefront
     int32_t eager_bonus_from; // sequences b >= this read their bonus row without deciding first
     int32_t pos_major;        // decision worker blocks ordered position-major over all sequences
-    int32_t row_skip;         // decision workers of a row after a known first rejection read nothing
-    int32_t dyn_lds;          // dynamic LDS bytes per block (only to cap the blocks per compute unit)
+    int32_t window;           // > 0 (window mode): no row after a known rejection is read; unless the
+                              // previous call on the workspace rejected every sequence at position 0,
+                              // every other row is read at once, else the rows of position i >= window
+                              // only once the sequence's accepted prefix a has i < window +
+                              // kWindowGrowth * a
     // Flags are 32-bit: a byte-sized field at an unaligned offset of the
     // kernel argument block is read with a vector load (a memory round trip
     // at the start of every block) instead of a scalar one.
@@ -104,7 +107,9 @@ struct Plan {
     uint64_t* chunkw;         // [B][rows_per_seq][P][2] tagged chunk partials (m, s) or (max, index);
                               // VAT loss: [B][k][P][5] (pair partials)
     uint64_t* segw;           // [B][rows_per_seq][S][2] tagged segment partials (not for the VAT loss)
-    uint64_t* resid;          // [B][P + 1] tagged residual masses, then the decision word (r + 2)
+    uint64_t* resid;          // [B][P + 3] tagged residual masses, then the decision word (r + 2), the
+                              // progress word (window mode: positions accepted while none is rejected)
+                              // and the history word (window mode: r + 2 of the last call, any tag)
 
     TaskGrid grid;            // role of every block of the launch
 };
@@ -120,13 +125,11 @@ constexpr int kDefaultComputeUnits = 256;
 // Blocks of k_verify<EB, VEC, path> one compute unit holds at once (0 on failure).
 int verify_blocks_per_cu(int elem_bytes, bool vec, int path);
 
-// Dynamic LDS bytes per block that hold k_verify to `blocks` blocks per
-// compute unit (-1 if no amount up to 64 KiB does).
-int verify_lds_for_blocks(int elem_bytes, bool vec, int path, int blocks);
-
-// Small one-hot and greedy calls whose rows need not all be read: blocks per
-// compute unit while they stream (see Plan::row_skip).
-constexpr int kRowSkipBlocksPerCu = 3;
+// Small one-hot and greedy calls whose rows need not all be read (see
+// Plan::window): positions whose rows are always read at once, and how fast
+// the read-ahead grows with the accepted prefix.
+constexpr int kRowWindow = 1;
+constexpr int kWindowGrowth = 2;
 
 // Chunks each worker wavefront streams, one after the other.  Two per wave
 // for large calls: block dispatch (on the order of 150-200 blocks per

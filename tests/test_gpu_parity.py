@@ -231,6 +231,60 @@ def test_edge_shapes(dev, B, k, V, dtype, T, onehot):
     _verify_case(workloads.generate(cfg), dev)
 
 
+def _planted_rejections(rej, k, V, T, onehot, seed):
+    """Each row has one planted maximum 40 above the rest, so the draft token
+    is kept (argmax) or rejected (any other token) with certainty; sequence b
+    first rejects at rej[b] (k: full acceptance, the bonus row)."""
+    rng = np.random.default_rng(seed)
+    B = len(rej)
+    t = (2.0 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+    g = rng.integers(0, V, (B, k + 1))
+    t[np.arange(B)[:, None], np.arange(k + 1)[None, :], g] = 40.0
+    bits = workloads.round_to_bf16_bits(t)
+    x = g[:, :k].astype(np.int32).copy()
+    for b, r in enumerate(rej):
+        if r < k:
+            x[b, r] = (g[b, r] + 1 + rng.integers(0, V - 1)) % V
+    u = rng.random((B, k + 1), dtype=np.float32)
+    cfg = _custom(B, k, V, "bf16", T, onehot=onehot, mode="argmax" if T == 0 else "sample")
+    return workloads.Workload(cfg, 0, bits, None, x, u)
+
+
+@pytest.mark.parametrize("T,onehot", [(0.0, False), (1.0, True)])
+@pytest.mark.parametrize("rej", [(0, 2, 3, 5, 8, 13, 15, 16), (16, 16, 16, 16, 4, 6, 7, 12)])
+def test_first_rejection_at_every_depth(dev, T, onehot, rej):
+    """Small one-hot and greedy calls whose statistics are not asked for read
+    every row at once, or, after a call on the same workspace that rejected
+    every sequence's first token, the rows of later positions only as the
+    accepted prefix comes near them.  First rejections at every depth and
+    full acceptance, in both regimes: the call with statistics (every row
+    read) matches the oracle, and the calls without match it bit for bit."""
+    import torch
+
+    import speculative_decoding_verification_amd as sv
+
+    k, V = 16, 151936
+    wl = _planted_rejections(rej, k, V, T, onehot, 81)
+    gpu, _ = _verify_case(wl, dev)
+    assert list(gpu["accepted_len"]) == list(rej)
+    primer = _planted_rejections((0,) * len(rej), k, V, T, onehot, 82)
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device=dev)
+
+    def lean(w):
+        t = to_torch(w.target, dev)
+        return sv.verify(t, None, to_torch(w.tokens, dev), to_torch(w.uniforms, dev), T, onehot=onehot, workspace=ws)
+
+    for first in (primer, wl):  # the second call reads every row: its predecessor accepted tokens
+        out = lean(first)
+        if first is primer:
+            assert np.all(out.accepted_len.cpu().numpy() == 0)
+        out = lean(wl)
+        _say("  after %s:" % ("all-rejecting call" if first is primer else "accepting call"),
+             list(out.accepted_len.cpu().numpy()))
+        assert np.array_equal(out.accepted_len.cpu().numpy(), gpu["accepted_len"])
+        assert np.array_equal(out.out_tokens.cpu().numpy(), gpu["out_tokens"])
+
+
 def test_neg_inf_logits_and_greedy_ties(dev):
     rng = np.random.default_rng(77)
     B, k, V = 12, 4, 9000
