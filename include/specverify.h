@@ -104,9 +104,12 @@
  *    reuse it): they return SV_ERR_CAPTURING while `stream` is capturing.  A
  *    buffer that anything else has written since (the LM-head entry points
  *    included) must be zero-filled again before one of them uses it.  Calls
- *    that use the same workspace must not overlap in time.  The LM-head entry
- *    points and sv_vat_loss_grad hand nothing between blocks through tags and
- *    may be captured.
+ *    that use the same workspace must not overlap in time.  sv_verify also
+ *    keeps each sequence's first rejection in the workspace: small one-hot
+ *    and greedy calls read it back to decide how early they read the rows of
+ *    later positions, which changes their speed, never their results.  The
+ *    LM-head entry points and sv_vat_loss_grad hand nothing between blocks
+ *    through tags and may be captured.
  *  - Determinism: results are bitwise reproducible for identical inputs (no
  *    floating-point atomics; fixed reduction orders).
  */
