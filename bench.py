@@ -82,6 +82,13 @@ every row's fp32 logits); the step also holds the decisions and the draws.
 runs K plain device-to-device copies of 1 GiB (torch's copy kernel) and
 nothing else: the known-size reference that scales rocprofv3's FETCH_SIZE and
 WRITE_SIZE counters to bytes.
+
+    python bench.py --blas-probe [--steps K]
+
+times the library GEMM (torch.matmul, hipBLASLt) on the LM-head operands of
+lmhead_selfdraft and lmhead_grpo, writing the bf16 logits instead of reducing
+them: the reference for the LM-head GEMM's MFMA rate (one JSON line per
+shape; a kernel trace names the kernel the library picks).
 """
 from __future__ import annotations
 
@@ -737,6 +744,40 @@ def _launchers(cfg, sets, sv, n, loss=False):
     return out
 
 
+def blas_probe(steps: int) -> int:
+    """torch.matmul (hipBLASLt) of the LM-head workloads' hidden states by
+    their output layer's transpose, bf16 in and out, synthetic operands of
+    the same shapes."""
+    import torch
+
+    import workloads
+
+    dev = torch.device("cuda:0")
+    for name in ("lmhead_selfdraft", "lmhead_grpo"):
+        cfg = workloads.LM_CONFIGS[name]
+        gen = torch.Generator(device=dev).manual_seed(cfg.seed)
+        h = (torch.randn(cfg.rows, cfg.D, generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+        w = (torch.randn(cfg.V, cfg.D, generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+        wt = w.t()
+        for _ in range(5):
+            y = torch.matmul(h, wt)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            y = torch.matmul(h, wt)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        tflops = cfg.flops() / (ms * 1e-3) / 1e12
+        print(json.dumps({"blas_probe": name, "rows": cfg.rows, "hidden": cfg.D, "vocab": cfg.V, "steps": steps,
+                          "mean_us": ms * 1e3, "tflops": tflops, "frac_of_bf16_peak": tflops / MFMA_BF16_PEAK_TFLOPS,
+                          "output": "bf16 logits written"}), flush=True)
+        del h, w, wt, y
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -748,6 +789,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--blas-probe", action="store_true")
     ap.add_argument("--no-side", action="store_true",
                     help="time only --workload (no ngram_tail / grpo / grpo_greedy side figures)")
     args = ap.parse_args(argv)
@@ -764,6 +806,8 @@ def main(argv=None):
         return 1
     if args.copy_probe:
         return copy_probe(args.steps)
+    if args.blas_probe:
+        return blas_probe(args.steps)
 
     if args.workload.startswith("lmhead_"):
         return bench_lm_head(args)
