@@ -1408,10 +1408,13 @@ __device__ __forceinline__ bool test_position(const Plan& pl, const TailShared& 
 // (`all`: row statistics or probabilities of every position).  Returns r in
 // [0, k] (k: all kept), -1 (a token outside [0, V)) or -2 (the wait ran
 // out); leaves the combined rows in sh.mz (local row numbering) and the
-// tested positions' p_i(x_i), q_i(x_i) in pr.  Whole block.
+// tested positions' p_i(x_i), q_i(x_i) in pr.  With `row0_chunks` (one-hot
+// window mode) position 0 is decided from row 0's chunk words instead of its
+// segment words, staged in sh.stage after the segment words for a draw at
+// r = 0.  Whole block.
 template <int EB, bool VEC, int MODE>
 __device__ __forceinline__ int decide(const Plan& pl, int b, TailShared& sh, bool all, PosRegs& pr, uint64_t timeout,
-                                      bool progress = false) {
+                                      bool progress = false, bool row0_chunks = false) {
     using Tr = PathTraits<MODE>;
     constexpr int H = Tr::halves;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1431,6 +1434,27 @@ __device__ __forceinline__ int decide(const Plan& pl, int b, TailShared& sh, boo
     if (r < 0) return -1;
     int done = 0;
     const uint64_t t0 = wall_clock64();
+    if (row0_chunks) {
+        // One poll of the row's chunk words (one per chunk) rather than of
+        // its segment words: the same arrival, and a rejection at 0 then
+        // draws from words already staged.
+        const int P = pl.chunks;
+        uint32_t* cst = sh.stage + n_words;
+        if (!collect(chunk_words(pl, b), 2 * P, pl.tag, cst, sh.vote, false, timeout)) return -2;
+        combine_rows(PartialSrc{cst, nullptr}, 0, 1, P, Tr::greedy, pl.c2, sh.mz);
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            bool keep = true;
+            if (lane == 0) keep = test_position<MODE>(pl, sh, pr, 0);
+            if (lane == 0 && !keep) sh.r = 0;
+        }
+        __syncthreads();
+        r = sh.r;
+        done = 1;
+        if (progress && r == k && done < k && threadIdx.x == kWave)
+            put_word(progress_word(pl, b), static_cast<uint32_t>(done), pl.tag);
+        if (done == k || (r < k && !all)) return r;
+    }
     for (;;) {
         int miss = k;  // first position with a segment word not yet there
         for (int w = done * per_pos + static_cast<int>(threadIdx.x); w < n_words; w += kBlock) {
@@ -1522,7 +1546,11 @@ __device__ __forceinline__ void decision_finisher(const Plan& pl, int b, TailSha
     int known;
     bool limited = false;
     if constexpr (Tr::bonus && Tr::halves == 1) limited = pl.window && read_ahead(pl, b, sh, known) < pl.k;
-    const int r = decide<EB, VEC, MODE>(pl, b, sh, all, pr, kPollTimeoutTicks, limited);
+    // One-hot window mode: position 0 from row 0's chunk words (staged after
+    // the segment words, if they fit)
+    const int seg_n = k * 2 * pl.segs;
+    const bool row0 = Tr::onehot && pl.window && !all && seg_n + 2 * P <= kStageWords;
+    const int r = decide<EB, VEC, MODE>(pl, b, sh, all, pr, kPollTimeoutTicks, limited, row0);
     if (r == -2) {
         fail_sequence<MODE>(pl, b);
         return;
@@ -1575,10 +1603,15 @@ __device__ __forceinline__ void decision_finisher(const Plan& pl, int b, TailSha
         if (!draws) return;
         // chunk partials of target row r (local row r), tags checked
         const uint64_t* cw = chunk_words(pl, b) + static_cast<int64_t>(r) * P * 2;
-        const bool cstaged = 2 * P <= kStageWords;
         const float m_r = sh.mz[r].x;
-        const bool ok = collect(cw, 2 * P, pl.tag, cstaged ? sh.stage : nullptr, sh.vote, false);
-        const DrawRow d = onehot_row<EB>(pl, b, r, PartialSrc{cstaged ? sh.stage : nullptr, cw}, m_r, sh.x_r, sh.l_x);
+        bool ok = true;
+        PartialSrc src{sh.stage + seg_n, cw};  // a rejection at 0 in window mode: staged by decide
+        if (!(row0 && r == 0)) {
+            const bool cstaged = 2 * P <= kStageWords;
+            ok = collect(cw, 2 * P, pl.tag, cstaged ? sh.stage : nullptr, sh.vote, false);
+            src = PartialSrc{cstaged ? sh.stage : nullptr, cw};
+        }
+        const DrawRow d = onehot_row<EB>(pl, b, r, src, m_r, sh.x_r, sh.l_x);
         const int y = ok ? draw_token<EB, VEC>(d, u_draw, P, V, sh) : -2;
         if (threadIdx.x < kWave) publish_outputs<MODE>(pl, b, r, pr.x, y, sh);
         if (threadIdx.x == kWave && !pl.window) put_word(decision_word(pl, b), static_cast<uint32_t>(r + 2), pl.tag);
