@@ -1610,6 +1610,8 @@ __device__ __forceinline__ void decision_finisher(const Plan& pl, int b, TailSha
             const bool cstaged = 2 * P <= kStageWords;
             ok = collect(cw, 2 * P, pl.tag, cstaged ? sh.stage : nullptr, sh.vote, false);
             src = PartialSrc{cstaged ? sh.stage : nullptr, cw};
+        } else {
+            __syncthreads();  // sh.x_r and sh.l_x, written by wave 0, for every wave (collect's barrier otherwise)
         }
         const DrawRow d = onehot_row<EB>(pl, b, r, src, m_r, sh.x_r, sh.l_x);
         const int y = ok ? draw_token<EB, VEC>(d, u_draw, P, V, sh) : -2;
