@@ -223,6 +223,8 @@ def _custom(B, k, V, dtype, T, sigma_t=3.0, sigma_d=0.5, mode="sample", onehot=F
     (20, 4, 2048, "f32", 0.0, False),     # greedy fp32, exactly one chunk
     (9, 3, 1001, "bf16", 0.0, False),     # greedy unaligned
     (32, 16, 151936, "bf16", 1.0, True),  # one-hot, several residencies: finishers behind their workers
+    (2, 64, 151936, "bf16", 1.0, True),   # one-hot window mode, k = 64: position 0 from row 0's chunk words
+    (1, 16, 600000, "f32", 1.0, True),    # one-hot window mode, 293 chunks staged beside the segment words
     (24, 3, 151936, "bf16", 0.7, False),  # sampling in one residency: finishers first, residual roles after
     (12, 5, 151936, "bf16", 0.0, False),  # greedy in one residency, finishers first
 ])
